@@ -1,0 +1,361 @@
+"""Pins for the CPU oracle: each test ties it to something other than itself
+(hand-derived bytes, library routines, closed forms, exact rational brute
+force, invariants, figures printed by the pages)."""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+from ternary_weight_only_tern_amd import synth
+
+
+def _word_trits(case):
+    t = np.zeros(16, dtype=np.int8)
+    if "all" in case:
+        t[:] = case["all"]
+    else:
+        for off, v in case["nonzero"].items():
+            t[int(off)] = v
+    return t
+
+
+# ---------------------------------------------------------------- 2-bit bytes
+def test_2bit_hand_vectors(golden_dir):
+    cases = json.load(open(os.path.join(golden_dir, "pack_2bit_vectors.json")))["cases"]
+    for case in cases:
+        t = _word_trits(case)
+        got = O.pack_2bit(t[None, :])[0]
+        assert list(got) == case["bytes"], case
+        assert int.from_bytes(bytes(got), "little") == int(case["word"], 16)
+        assert list(O.pack_2bit_row(t)) == case["bytes"]
+        assert np.array_equal(O.unpack_2bit(got[None, :], 16)[0], t)
+
+
+def _fp16_pair_decode(words):
+    """Independent decoder: shifting pair i to bits 14/15 and 30/31 and masking
+    yields the fp16 values +-2.0 / 0 of trits (2i, 2i+1) of the word."""
+    out = np.zeros(words.shape + (16,))
+    for i in range(8):
+        m = ((words.astype(np.uint64) << np.uint64(14 - 2 * i)) & np.uint64(0xC000C000)).astype(np.uint32)
+        lo = (m & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64)
+        hi = (m >> 16).astype(np.uint16).view(np.float16).astype(np.float64)
+        out[..., 2 * i] = lo / 2
+        out[..., 2 * i + 1] = hi / 2
+    return out
+
+
+def test_2bit_layout_against_fp16_bit_decoder():
+    rng = np.random.default_rng(11)
+    t = synth.draw_trits(rng, (7, 256))
+    words = O.pack_2bit(t).view("<u4")
+    dec = _fp16_pair_decode(words).reshape(7, 256)
+    assert np.array_equal(dec, t.astype(np.float64))
+
+
+def test_2bit_every_single_trit_position_and_value():
+    """3 values x 16 positions, checked against the bit-position closed form."""
+    for o in range(16):
+        for v in (-1, 1):
+            t = np.zeros((1, 16), dtype=np.int8)
+            t[0, o] = v
+            word = int.from_bytes(bytes(O.pack_2bit(t)[0]), "little")
+            b = 16 * (o % 2) + 2 * (o // 2)
+            assert word == (1 if v == 1 else 3) << b
+
+
+def test_2bit_code_10_rejected():
+    bad = np.array([[2, 0, 0, 0]], dtype=np.uint8)  # offset 0 holds code 10
+    with pytest.raises(O.CorruptError):
+        O.unpack_2bit(bad, 16)
+
+
+# ---------------------------------------------------------------- base-3 bytes
+def test_b3_hand_vectors(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "pack_b3_vectors.json")))
+    for case in g["cases"]:
+        assert O.pack_b3_group(case["trits"]) == bytes([case["byte"]])
+    tail = np.zeros(128, dtype=np.int8)
+    tail[125:] = g["group_tail"]["tail_trits"]
+    packed = O.pack_b3_group(tail)
+    assert len(packed) == 26 and packed[25] == g["group_tail"]["byte"]
+    assert packed[:25] == bytes([121] * 25)
+
+
+def test_b3_all_243_patterns_against_python_base3():
+    seen = set()
+    for digs in itertools.product((-1, 0, 1), repeat=5):
+        b = O.pack_b3_group(list(digs))[0]
+        # int(str, 3) reads the most significant digit first
+        assert b == int("".join(str(d + 1) for d in reversed(digs)), 3)
+        seen.add(b)
+    assert seen == set(range(243))
+
+
+def test_b3_row_layout_and_padding():
+    rng = np.random.default_rng(3)
+    for k, g in [(2560, 128), (4096, 128), (9728, 128), (12288, 128), (256, 64), (640, 64)]:
+        t = synth.draw_trits(rng, (3, k))
+        p = O.pack_b3(t, g)
+        nb = (g + 4) // 5
+        assert p.shape[1] == O.row_stride(k, g, O.FMT_B3)
+        assert p.shape[1] % 16 == 0 and p.shape[1] - (k // g) * nb < 16
+        assert (p[:, (k // g) * nb:] == 0).all()
+        for r in range(3):
+            for gi in (0, k // g - 1):
+                assert bytes(p[r, gi * nb:(gi + 1) * nb]) == O.pack_b3_group(t[r, gi * g:(gi + 1) * g])
+        assert np.array_equal(O.unpack_b3(p, k, g), t)
+
+
+def test_b3_corrupt_rejected():
+    t = np.zeros((1, 128), dtype=np.int8)
+    p = O.pack_b3(t, 128)
+    bad = p.copy()
+    bad[0, 3] = 243
+    with pytest.raises(O.CorruptError):
+        O.unpack_b3(bad, 128, 128)
+    bad = p.copy()
+    bad[0, 25] = 121 - 81  # last byte of group with a -1 padding trit
+    with pytest.raises(O.CorruptError):
+        O.unpack_b3(bad, 128, 128)
+
+
+# ---------------------------------------------------------------- residual planes / masks
+def test_mask_bits_hand_vector():
+    bits = np.array([[0x00000001, 0x00000002]], dtype=np.uint32)  # groups 0 and 33
+    m = O.mask_bool(bits, 40)
+    assert m[0].nonzero()[0].tolist() == [0, 33]
+
+
+def test_residual_roundtrip_and_order():
+    rng = np.random.default_rng(5)
+    mat = synth.make_matrix(6, 512, 128, 2, 0.4, rng=rng)
+    rp, bl, rs = O.pack_residual(mat["trits"][1], mat["scales"][1], mat["mask_bits"][0], 128)
+    sel = mat["masks"][0]
+    assert rp[0] == 0 and np.array_equal(np.diff(rp.astype(np.int64)), sel.sum(axis=1))
+    rows, groups = np.nonzero(sel)
+    for i, (r, g) in enumerate(zip(rows, groups)):
+        assert np.array_equal(bl[i], O.pack_2bit(mat["trits"][1][r:r + 1, g * 128:(g + 1) * 128])[0])
+        assert rs[i] == mat["scales"][1][r, g]
+    back = O.unpack_residual(rp, bl, mat["mask_bits"][0], 6, 512, 128)
+    assert np.array_equal(back, mat["trits"][1])
+
+
+def test_residual_errors():
+    t = np.zeros((2, 256), dtype=np.int8)
+    t[1, 5] = 1
+    bits = np.zeros((2, 1), dtype=np.uint32)  # no group masked
+    with pytest.raises(O.PackError):
+        O.pack_residual(t, np.ones((2, 2), np.float16), bits, 128)
+    bits[1, 0] = 1
+    rp, bl, _ = O.pack_residual(t, np.ones((2, 2), np.float16), bits, 128)
+    with pytest.raises(O.CorruptError):
+        O.unpack_residual(np.array([0, 0, 2], np.uint32), bl, bits, 2, 256, 128)
+    with pytest.raises(O.PackError):
+        O.pack_2bit(np.full((1, 16), 2, dtype=np.int8))
+
+
+def test_full_pack_unpack_roundtrip_all_configs_small():
+    for cfg, fmt in [(1, O.FMT_2BIT), (5, O.FMT_2BIT), (5, O.FMT_B3), (3, O.FMT_B3)]:
+        c = synth.CONFIGS[cfg]
+        rng = np.random.default_rng(cfg)
+        mat = synth.make_matrix(8, 1280 if cfg != 1 else 256, c["group"], c["planes"],
+                                c["res_frac"] or 0.0, rng=rng, scale_law=c["scale_law"],
+                                offset_mode=c["offset_mode"], shared_mask=c.get("shared_mask", False))
+        pk = O.pack(mat["trits"], mat["scales"], mat["mask_bits"], mat["offset"], c["group"], fmt)
+        trits, rdense = O.unpack(pk)
+        assert np.array_equal(trits, mat["trits"])
+        for p in range(1, c["planes"]):
+            m = mat["masks"][p - 1]
+            assert np.array_equal(rdense[p - 1][m], mat["scales"][p][m])
+
+
+# ---------------------------------------------------------------- products
+def _exact(trits, scales, masks, offset, mode, x, group):
+    """Brute force in exact rationals with plain loops (tiny sizes only)."""
+    P, N, K = trits.shape
+    M = x.shape[0]
+    y = [[Fraction(0)] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                g = k // group
+                w = Fraction(0)
+                if mode == O.OFF_ROW:
+                    w += Fraction(float(offset[n]))
+                elif mode == O.OFF_GROUP:
+                    w += Fraction(float(offset[n, g]))
+                for p in range(P):
+                    if p == 0 or masks[p - 1][n, g]:
+                        w += Fraction(float(scales[p][n, g])) * int(trits[p, n, k])
+                acc += w * Fraction(float(x[m, k]))
+            y[m][n] = acc
+    return y
+
+
+@pytest.mark.parametrize("mode", [O.OFF_NONE, O.OFF_ROW, O.OFF_GROUP])
+def test_gemv_exact_brute_force(mode):
+    rng = np.random.default_rng(21 + mode)
+    mat = synth.make_matrix(3, 16, 8, 3, 0.5, rng=rng, scale_law="lognormal", offset_mode=mode)
+    x = synth.draw_x(rng, 2, 16, "student_t3")
+    y = O.gemv(mat["trits"], mat["scales"], mat["masks"], mat["offset"], mode, x, 8)
+    ex = _exact(mat["trits"], mat["scales"], mat["masks"], mat["offset"], mode, x, 8)
+    for m in range(2):
+        for n in range(3):
+            assert abs(Fraction(y[m, n]) - ex[m][n]) <= abs(ex[m][n]) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 80)
+
+
+def test_gemv_all_3pow5_patterns_equal_base3_byte():
+    """With x_i = 3**i, s = 1 and G = K = 5, y = sum t_i 3**i = byte - 121."""
+    pats = np.array(list(itertools.product((-1, 0, 1), repeat=5)), dtype=np.int8)  # 243 rows
+    x = np.array([[1, 3, 9, 27, 81]], dtype=np.float16)
+    y = O.gemv(pats[None], np.ones((1, 243, 1), np.float16), None, None, O.OFF_NONE, x, 5)
+    for r in range(243):
+        assert y[0, r] == O.pack_b3_group(pats[r])[0] - 121
+
+
+def test_gemv_2bit_word_closed_form():
+    """x_k = 2**b(k) gives y = word - 4 * sum_{t_k<0} 2**b(k) for a 16-trit row."""
+    rng = np.random.default_rng(8)
+    t = synth.draw_trits(rng, (50, 16))
+    b = np.array([16 * (o % 2) + 2 * (o // 2) for o in range(16)])
+    x = (2.0 ** b).astype(np.float64)
+    y = O.gemv(t[None], np.ones((1, 50, 1), np.float16), None, None, O.OFF_NONE,
+               x[None, :].astype(np.float64), 16)
+    words = O.pack_2bit(t).view("<u4")[:, 0].astype(np.int64)
+    neg = ((t < 0) * (4 * 2 ** b)).sum(axis=1)
+    assert np.array_equal(y[0].astype(np.int64), words - neg)
+
+
+def test_gemv_textbook_special_case_matmul():
+    rng = np.random.default_rng(9)
+    t = synth.draw_trits(rng, (1, 40, 256))
+    x = synth.draw_x(rng, 3, 256, "normal")
+    y = O.gemv(t, np.ones((1, 40, 1), np.float16), None, None, O.OFF_NONE, x, 256)
+    assert np.allclose(y, x.astype(np.float64) @ t[0].T.astype(np.float64), rtol=1e-12, atol=1e-12)
+
+
+def test_gemv_equals_dense_dequant_matmul():
+    for mode in (O.OFF_NONE, O.OFF_ROW, O.OFF_GROUP):
+        rng = np.random.default_rng(30 + mode)
+        mat = synth.make_matrix(24, 640, 64, 3, 0.3, rng=rng, scale_law="lognormal", offset_mode=mode)
+        x = synth.draw_x(rng, 4, 640, "student_t3")
+        y = O.gemv(mat["trits"], mat["scales"], mat["masks"], mat["offset"], mode, x, 64)
+        w = O.dequant(mat["trits"], mat["scales"], mat["masks"], mat["offset"], mode, 64)
+        yd = x.astype(np.float64) @ w.T
+        b = O.bound(mat["trits"], mat["scales"], mat["masks"], mat["offset"], mode, x, 64)
+        assert (np.abs(y - yd) <= 1e-12 * b + 1e-300).all()
+
+
+def test_gemv_invariants():
+    rng = np.random.default_rng(41)
+    mat = synth.make_matrix(16, 512, 128, 2, 0.25, rng=rng, offset_mode=O.OFF_ROW)
+    x = synth.draw_x(rng, 2, 512, "normal")
+    args = (mat["scales"], mat["masks"])
+    y = O.gemv(mat["trits"], *args, mat["offset"], O.OFF_ROW, x, 128)
+    # zero trits, no offset -> exactly zero
+    z = O.gemv(np.zeros_like(mat["trits"]), *args, None, O.OFF_NONE, x, 128)
+    assert (z == 0).all()
+    # (T, mu) -> (-T, -mu) gives -y bitwise
+    yn = O.gemv(-mat["trits"], *args, -mat["offset"], O.OFF_ROW, x, 128)
+    assert np.array_equal(yn, -y)
+    # doubling all scales and the offset doubles y exactly
+    y2 = O.gemv(mat["trits"], mat["scales"] * np.float16(2), mat["masks"],
+                mat["offset"] * np.float16(2), O.OFF_ROW, x, 128)
+    assert np.array_equal(y2, 2 * y)
+    # planes add up
+    parts = O.gemv(mat["trits"][:1], mat["scales"][:1], None, mat["offset"], O.OFF_ROW, x, 128)
+    t1 = mat["trits"].copy()
+    t1[0] = 0
+    parts = parts + O.gemv(t1, *args, None, O.OFF_NONE, x, 128)
+    assert np.allclose(parts, y, rtol=1e-13, atol=1e-13)
+    # linear in x
+    y3 = O.gemv(mat["trits"], *args, mat["offset"], O.OFF_ROW, (x.astype(np.float64) * 4), 128)
+    assert np.array_equal(y3, 4 * y)
+
+
+def test_gemv_closed_forms():
+    rng = np.random.default_rng(42)
+    x = synth.draw_x(rng, 1, 256, "normal")
+    s = np.full((1, 1, 2), 0.0625, np.float16)
+    t = np.zeros((1, 1, 256), np.int8)
+    t[0, 0, 128:] = 1                       # all +1 in group 1 -> s * sum(x over group 1)
+    y = O.gemv(t, s, None, None, O.OFF_NONE, x, 128)
+    assert y[0, 0] == 0.0625 * x[0, 128:].astype(np.float64).sum()
+    t[:] = 0
+    t[0, 0, 7] = -1                         # one trit -> -s * x_7 exactly
+    y = O.gemv(t, s, None, None, O.OFF_NONE, x, 128)
+    assert y[0, 0] == -0.0625 * float(x[0, 7])
+
+
+def test_bound_dominates_and_zero_case():
+    rng = np.random.default_rng(43)
+    mat = synth.make_matrix(10, 256, 64, 3, 0.5, rng=rng, scale_law="lognormal", offset_mode=O.OFF_GROUP)
+    x = synth.draw_x(rng, 3, 256, "student_t3")
+    y = O.gemv(mat["trits"], mat["scales"], mat["masks"], mat["offset"], O.OFF_GROUP, x, 64)
+    b = O.bound(mat["trits"], mat["scales"], mat["masks"], mat["offset"], O.OFF_GROUP, x, 64)
+    assert (b >= np.abs(y) * (1 - 1e-12)).all()
+    assert not O.accept(y * (1 + 3e-3), y, np.abs(y)).all()
+    assert O.accept(y, y, b).all()
+    zb = O.bound(np.zeros_like(mat["trits"]), mat["scales"], mat["masks"], None, O.OFF_NONE, x, 64)
+    assert (zb == 0).all()
+    assert not O.accept(np.full_like(zb, 1e-30), np.zeros_like(zb), zb).any()
+
+
+def test_gemv_packed_equals_gemv():
+    mat = synth.config_matrix(5)
+    # shrink the stress layer to a few rows to keep the CPU suite fast
+    for key in ("trits",):
+        mat[key] = mat[key][:, :6]
+    mat["scales"] = mat["scales"][:, :6]
+    mat["masks"] = [m[:6] for m in mat["masks"]]
+    mat["mask_bits"] = [m[:6] for m in mat["mask_bits"]]
+    mat["offset"] = mat["offset"][:6]
+    x = synth.config_x(5, 2)
+    for fmt in (O.FMT_2BIT, O.FMT_B3):
+        pk = O.pack(mat["trits"], mat["scales"], mat["mask_bits"], mat["offset"], 128, fmt)
+        yp = O.gemv_packed(pk, x)
+        y = O.gemv(mat["trits"], mat["scales"], mat["masks"], mat["offset"], O.OFF_ROW, x, 128)
+        assert np.array_equal(yp, y)
+
+
+# ---------------------------------------------------------------- bits per weight
+def test_bits_against_page_figures(golden_dir):
+    f = json.load(open(os.path.join(golden_dir, "page_figures.json")))
+    assert round(O.info_bits(0.0), 3) == f["ideal_bits_per_trit"]["value"]
+    # 1.641 is reproduced by a second-plane fraction of about 3.54 %
+    assert round(O.info_bits(0.0354), 3) == f["effective_bits"]["value"]
+    cov = f["mask_coverages_percent"]["values"]
+    assert math.isclose(cov[0] + cov[1], f["mask_coverages_percent"]["two_plane_percent"])
+    assert math.isclose(cov[2] + cov[3], f["mask_coverages_percent"]["one_plane_percent"])
+    assert round(O.info_bits(0.036), 3) == 1.642  # the rounded 3.6 % overshoots by 0.001
+
+
+def test_bits_of_packed_matrices():
+    rng = np.random.default_rng(50)
+    mat = synth.make_matrix(64, 4096, 128, 2, 0.08, rng=rng)
+    pk2 = O.pack(mat["trits"], mat["scales"], mat["mask_bits"], None, 128, O.FMT_2BIT)
+    pk3 = O.pack(mat["trits"], mat["scales"], mat["mask_bits"], None, 128, O.FMT_B3)
+    b2, b3 = O.bits(pk2), O.bits(pk3)
+    f = 0.08
+    assert math.isclose(b2["info"], math.log2(3) * (1 + f), rel_tol=1e-3)
+    assert math.isclose(b2["plane"], 2.0 * (1 + f), rel_tol=1e-3)
+    assert math.isclose(b3["plane"], 26 * 8 / 128 + 2.0 * f, rel_tol=1e-3)
+    # storage adds fp16 scales per group: 16/128 bits, plus residual metadata
+    assert b2["storage"] > b2["plane"] + 16 / 128
+
+
+def test_bound_equals_y_when_every_term_is_nonnegative():
+    """With |T|, |s|, |off| and |x| in place of the signed values, B = y."""
+    rng = np.random.default_rng(44)
+    mat = synth.make_matrix(12, 512, 64, 3, 0.4, rng=rng, scale_law="lognormal", offset_mode=O.OFF_GROUP)
+    x = synth.draw_x(rng, 2, 512, "student_t3")
+    at, asc, aoff, ax = (np.abs(mat["trits"]), np.abs(mat["scales"]), np.abs(mat["offset"]), np.abs(x))
+    b = O.bound(mat["trits"], mat["scales"], mat["masks"], mat["offset"], O.OFF_GROUP, x, 64)
+    y = O.gemv(at, asc, mat["masks"], aoff, O.OFF_GROUP, ax, 64)
+    assert np.allclose(b, y, rtol=1e-13, atol=0)
