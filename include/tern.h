@@ -1,0 +1,201 @@
+/*
+ * tern.h -- C ABI of libtern, packed ternary (W1.58A16) linear layers on AMD
+ * MI355X (gfx950).
+ *
+ * The operation.  A quantized linear weight W (N output rows x K inputs) is a
+ * stack of trit planes T_p in {-1,0,+1}^{N x K} with one FP16 scale per
+ * (row, group of G inputs), an optional FP16 offset, and residual planes that
+ * exist only on salience-selected groups:
+ *     W[n,k] = off(n,g) + sum_p m_p[n,g] * s_p[n,g] * T_p[n,k],  g = k / G,
+ * and the library computes y[m,n] = sum_k W[n,k] * x[m,k] for FP16
+ * activations x.  Sources: "Post-Training Ternarization of Qwen3-4B"
+ * (arXiv 2609.01962v1 summary) §4.3 (offset plus ternary planes with
+ * scales), §4.4 (salience masks select which weights get a second plane),
+ * §4.5 (group size 128), §9.1 and §15 (persist the discrete planes and run a
+ * lossless native kernel); arXiv 2609.09240 (Qwen3-8B scale-up),
+ * representation, packing and direct-execution paragraphs.  The pages drop
+ * the displayed reconstruction equation; the additive reading above is the
+ * one this library implements.
+ *
+ * Packed layout (this library's definition; the pages print none):
+ *   plane 0, TERN_FMT_2BIT: code(t) = t mod 4 (00 = 0, 01 = +1, 11 = -1; 10
+ *     invalid).  Each little-endian uint32 holds 16 consecutive trits of a
+ *     row; the trit at offset o occupies bits 16*(o%2) + 2*(o/2) .. +1 (even
+ *     offsets in the low half-word, odd offsets in the high half-word).  Row
+ *     stride K/4 bytes.
+ *   plane 0, TERN_FMT_B3: every group of G trits takes ceil(G/5) bytes; byte
+ *     j of a group is sum_i (t[5j+i]+1)*3^i, i = 0..4 (positions past the end
+ *     of the group are zero trits).  Groups are consecutive; each row is
+ *     zero-padded to a multiple of 16 bytes (tern_row_stride).
+ *   residual plane p (1 or 2): mask[p-1] is a uint32 bitmap [N][ceil((K/G)/32)]
+ *     (bit g%32 of word g/32 set when group g of row n carries plane p);
+ *     rowptr[p-1] is [N+1] uint32, the exclusive prefix sum of the per-row
+ *     popcounts; blocks[p-1] is [nnz][G/4] bytes, the 2-bit encoding of the G
+ *     trits of each masked group in (row, group) order; rscale[p-1] is FP16
+ *     [nnz] in the same order.
+ *   scale0: FP16 [N][K/G].  offset: FP16 [N] (TERN_OFF_ROW) or [N][K/G]
+ *     (TERN_OFF_GROUP), NULL for TERN_OFF_NONE.
+ *
+ * Conventions.
+ *   - Every array argument is caller-owned device memory (e.g. from torch);
+ *     the library allocates no device memory and keeps none between calls.
+ *     Host-side descriptors (tern_matrix, arrays of them) are read during the
+ *     call only.
+ *   - Alignment (TERN_E_ALIGN otherwise): plane0, blocks, trits, x and
+ *     workspaces 16 bytes (they are read with 16-byte vector loads); every
+ *     other array its element size.
+ *   - Supported shapes: n >= 0, k >= 0, k % 64 == 0, group % 64 == 0,
+ *     group <= 1024, k % group == 0, 1 <= planes <= 3 (TERN_E_UNSUPPORTED
+ *     otherwise).  n == 0 or m == 0 is an empty product and returns TERN_OK
+ *     without touching memory; k == 0 writes y = 0.
+ *   - x is [m][k] FP16, row-major; y is [m][n], row-major, FP16 (rounded to
+ *     nearest even from an FP32 accumulator) or FP32.  y is overwritten.
+ *   - stream is a hipStream_t (NULL = the null stream).  Products run
+ *     asynchronously on it; launch failures return TERN_E_HIP and device
+ *     faults surface at the caller's next synchronisation.  tern_pack and
+ *     tern_unpack synchronise the stream so they can return validation
+ *     results.
+ *   - Products trust their packed input (no validation of codes); use
+ *     tern_unpack to validate an artifact.
+ *   - Errors are status codes; nothing throws across the ABI.
+ *     tern_last_error() returns a message for the calling thread's last
+ *     failure.
+ */
+#ifndef TERN_H
+#define TERN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tern_status {
+  TERN_OK = 0,
+  TERN_E_INVAL = -1,        /* bad argument value, bad trit, trit outside mask */
+  TERN_E_ALIGN = -2,        /* a device pointer is not 16-byte aligned */
+  TERN_E_UNSUPPORTED = -3,  /* shape or mode outside the supported set */
+  TERN_E_CORRUPT = -4,      /* packed bytes are not a valid encoding */
+  TERN_E_WORKSPACE = -5,    /* workspace missing or too small */
+  TERN_E_HIP = -6           /* a HIP runtime call failed */
+} tern_status;
+
+typedef enum tern_format { TERN_FMT_2BIT = 0, TERN_FMT_B3 = 1 } tern_format;
+typedef enum tern_offset_mode { TERN_OFF_NONE = 0, TERN_OFF_ROW = 1, TERN_OFF_GROUP = 2 } tern_offset_mode;
+typedef enum tern_dtype { TERN_F16 = 0, TERN_F32 = 1 } tern_dtype;
+
+/* Indices of tern_packed_sizes' output array. */
+typedef enum tern_buffer {
+  TERN_BUF_PLANE0 = 0, TERN_BUF_SCALE0 = 1, TERN_BUF_OFFSET = 2, TERN_BUF_MASK = 3,
+  TERN_BUF_ROWPTR = 4, TERN_BUF_BLOCKS1 = 5, TERN_BUF_BLOCKS2 = 6, TERN_BUF_RSCALE1 = 7,
+  TERN_BUF_RSCALE2 = 8, TERN_NBUF = 9
+} tern_buffer;
+
+/* Host struct of caller-owned device pointers describing one packed matrix.
+ * Members for absent residual planes and offsets are ignored (may be NULL). */
+typedef struct tern_matrix {
+  int32_t n, k, group, planes;   /* planes = 1 + number of residual planes */
+  int32_t format;                /* tern_format of plane 0 */
+  int32_t offset_mode;           /* tern_offset_mode */
+  uint8_t  *plane0;              /* [n][tern_row_stride(k, group, format)] */
+  uint16_t *scale0;              /* fp16 [n][k/group] */
+  uint32_t *mask[2];             /* residual plane p: bitmap [n][ceil(k/group/32)] */
+  uint32_t *rowptr[2];           /* [n+1] */
+  uint8_t  *blocks[2];           /* [nnz[p-1]][group/4] */
+  uint16_t *rscale[2];           /* fp16 [nnz[p-1]] */
+  uint16_t *offset;              /* fp16 [n] or [n][k/group]; NULL for TERN_OFF_NONE */
+  uint32_t nnz[2];               /* masked groups of residual planes 1 and 2 */
+} tern_matrix;
+
+/* Bytes per packed plane-0 row; 0 if (k, group, format) is unsupported. */
+size_t tern_row_stride(int32_t k, int32_t group, int32_t format);
+
+/* Host-only check of a descriptor (shapes, modes, NULL and alignment of the
+ * pointers the product reads).  Makes no HIP call. */
+tern_status tern_check(const tern_matrix *w);
+
+/* Byte sizes of every buffer of a packed matrix, indexed by tern_buffer.
+ * nnz may be NULL when planes == 1. */
+tern_status tern_packed_sizes(int32_t n, int32_t k, int32_t group, int32_t format,
+                              int32_t planes, const uint32_t *nnz, int32_t offset_mode,
+                              size_t out_bytes[TERN_NBUF]);
+
+/* Device workspace needed by tern_pack / tern_unpack / tern_gemv / tern_gemm
+ * on this matrix with m activation rows (the maximum over the four). */
+size_t tern_workspace_bytes(const tern_matrix *w, int32_t m);
+
+/* Pack trit planes (lossless serialisation: 2609.01962 §9.1, §15).
+ *   trits        device int8 [planes][n][k]
+ *   rscale_dense device fp16 [planes-1][n][k/group]: residual scales per group;
+ *                entries outside the mask are ignored.  NULL if planes == 1.
+ *   dst          descriptor whose shape, format, mask[] and nnz[] are inputs
+ *                and whose plane0, rowptr[], blocks[] and rscale[] buffers
+ *                are written (scale0 and offset are not touched).
+ *   ws           device workspace of tern_workspace_bytes(dst, 1) bytes.
+ * Synchronises stream.  TERN_E_INVAL if a trit is outside {-1,0,1}, a
+ * residual trit is non-zero outside its mask, or nnz disagrees with the mask. */
+tern_status tern_pack(const int8_t *trits, const uint16_t *rscale_dense, const tern_matrix *dst,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* Unpack to device int8 [planes][n][k] (zeros outside the residual masks) and
+ * validate the artifact.  Synchronises stream.  TERN_E_CORRUPT on a 2-bit
+ * code 10, a base-3 byte above 242, a non-zero base-3 padding trit or a
+ * rowptr that disagrees with the mask popcounts. */
+tern_status tern_unpack(const tern_matrix *src, int8_t *trits, void *ws, size_t ws_bytes,
+                        void *stream);
+
+/* y = x W^T for 1 <= m <= 63 (decode path; the direct ternary product of
+ * "Can ternary LLMs hit 1.58 bits per weight", How It Works, and 2609.09240's
+ * direct packed execution).  m == 0 is a no-op; m >= 64 is
+ * TERN_E_UNSUPPORTED (use tern_gemm).  ws: tern_workspace_bytes(w, m). */
+tern_status tern_gemv(const tern_matrix *w, const uint16_t *x, int32_t m, void *y,
+                      int32_t y_dtype, void *ws, size_t ws_bytes, void *stream);
+
+/* y = x W^T for any m >= 0 through FP16 MFMA on tiles decoded into LDS
+ * (tuned for m >= 64).  Supports group in {64, 128}; other groups return
+ * TERN_E_UNSUPPORTED.  ws: tern_workspace_bytes(w, m). */
+tern_status tern_gemm(const tern_matrix *w, const uint16_t *x, int32_t m, void *y,
+                      int32_t y_dtype, void *ws, size_t ws_bytes, void *stream);
+
+/* Grouped decode: count independent products y[i] = x[i] W[i]^T with the same
+ * m (1..63), format and output dtype, in one launch.
+ *   w  host array [count] of descriptors
+ *   x  host array [count] of device pointers, y likewise
+ *   ws device workspace of tern_batch_workspace_bytes(w, count, m) bytes; the
+ *      descriptor table is copied into it (hipMemcpyAsync on stream) on every
+ *      call.  For repeated launches use tern_plan_create / tern_plan_run. */
+size_t tern_batch_workspace_bytes(const tern_matrix *w, int32_t count, int32_t m);
+tern_status tern_gemv_batched(const tern_matrix *w, const uint16_t *const *x, void *const *y,
+                              int32_t count, int32_t m, int32_t y_dtype, void *ws,
+                              size_t ws_bytes, void *stream);
+
+/* A prepared grouped decode.  tern_plan_create copies the descriptor table
+ * into the caller's device buffer `ws` (synchronously) and returns a host
+ * handle (malloc'ed; free it with tern_plan_destroy).  tern_plan_run
+ * launches the whole batch on stream; it may be called any number of times
+ * and captured in a HIP graph.  The buffers named in the plan must stay
+ * valid while the plan is used. */
+typedef struct tern_plan tern_plan;
+tern_status tern_plan_create(const tern_matrix *w, const uint16_t *const *x, void *const *y,
+                             int32_t count, int32_t m, int32_t y_dtype, void *ws,
+                             size_t ws_bytes, tern_plan **out);
+tern_status tern_plan_run(const tern_plan *plan, void *stream);
+void tern_plan_destroy(tern_plan *plan);
+
+/* Bits per weight of a packed matrix (2609.01962 §3.2, §7.1: effective bits
+ * count log2(3) per stored trit over the planes actually present):
+ *   info    = log2(3) * (n*k + group * sum nnz) / (n*k)
+ *   plane   = 8 * (plane-0 bytes + residual block bytes) / (n*k)
+ *   storage = 8 * (every byte of the representation) / (n*k)
+ * Any output pointer may be NULL.  Host-only. */
+tern_status tern_bits(const tern_matrix *w, double *info, double *plane, double *storage);
+
+const char *tern_status_str(tern_status s);
+const char *tern_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TERN_H */

@@ -1,0 +1,83 @@
+// Internal declarations shared by the host API (tern_api.cpp) and the HIP
+// kernel sources.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tern {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kGemvRows = 64;      // rows per decode work item: one row per lane
+constexpr int kMaxMT = 8;          // activation rows per decode pass
+
+// Device-side description of one product (one matrix, one activation block).
+struct GemvDesc {
+  const uint8_t* plane0;
+  const uint16_t* scale0;
+  const uint32_t* mask[2];
+  const uint32_t* rowptr[2];
+  const uint8_t* blocks[2];
+  const uint16_t* rscale[2];
+  const uint16_t* offset;
+  const uint16_t* x;      // [m][k]
+  void* y;                // [m][n]
+  float* partial;         // [splits][m][n] fp32 when splits > 1
+  int32_t n, k, group, planes, offset_mode;
+  int32_t m;              // activation rows handled by this descriptor (<= MT)
+  int32_t stride;         // plane-0 row stride in bytes
+  int32_t ng;             // groups per row
+  int32_t mwords;         // mask words per row
+  int32_t splits;         // K splits (work items along K)
+  int32_t gps;            // groups per split
+  int32_t row_blocks;     // ceil(n / kGemvRows)
+  int32_t tile_begin;     // first work-item index of this descriptor in the grid
+  int32_t y_f32;          // 1: y is fp32, 0: fp16
+};
+
+// ---- decode products (gemv.hip)
+// Launches the lane-per-row decode kernel over `ndesc` descriptors stored in
+// device memory (`descs`), or over the single descriptor `one` when ndesc == 0.
+// total_items = sum over descriptors of splits * row_blocks.
+hipError_t launch_gemv(int format, int group, int mt, const GemvDesc* descs, int ndesc,
+                       const GemvDesc& one, int total_items, int max_stage_bytes,
+                       hipStream_t stream);
+// y[m][n] = sum_s partial[s][m][n] in split order.
+hipError_t launch_splitk_reduce(const float* partial, int splits, int m, int n, void* y,
+                                int y_f32, hipStream_t stream);
+// Bytes of dynamic LDS the decode kernel uses for a given format / group.
+int gemv_stage_bytes(int format, int group);
+
+// ---- MFMA product (gemm.hip)
+hipError_t launch_gemm(const GemvDesc& d, int format, hipStream_t stream);
+
+// ---- packing (pack.hip)
+hipError_t launch_pack_plane0(int format, const int8_t* trits, int n, int k, int group,
+                              int stride, uint8_t* plane0, uint32_t* flag, hipStream_t stream);
+hipError_t launch_unpack_plane0(int format, const uint8_t* plane0, int n, int k, int group,
+                                int stride, int8_t* trits, uint32_t* flag, hipStream_t stream);
+// rowptr[0] = 0, rowptr[r+1] = popcount(mask row r); flags bits past ng.
+hipError_t launch_mask_counts(const uint32_t* mask, int n, int ng, int mwords, uint32_t* rowptr,
+                              uint32_t* flag, hipStream_t stream);
+// In-place inclusive scan of rowptr[1..n] (single workgroup).
+hipError_t launch_rowptr_scan(uint32_t* rowptr, int n, hipStream_t stream);
+hipError_t launch_pack_residual(const int8_t* trits_p, const uint16_t* rscale_dense,
+                                const uint32_t* mask, const uint32_t* rowptr, int n, int k,
+                                int group, int mwords, uint8_t* blocks, uint16_t* rscale,
+                                uint32_t* flag, hipStream_t stream);
+hipError_t launch_unpack_residual(const uint8_t* blocks, const uint32_t* mask,
+                                  const uint32_t* rowptr, int n, int k, int group, int mwords,
+                                  int8_t* trits_p, uint32_t* flag, hipStream_t stream);
+// flag |= bit if a[i] != b[i] for some i < count.
+hipError_t launch_compare_u32(const uint32_t* a, const uint32_t* b, int count, uint32_t bit,
+                              uint32_t* flag, hipStream_t stream);
+
+// Validation flag bits written by the packing kernels.
+constexpr uint32_t kFlagBadTrit = 1u;        // trit outside {-1,0,1}
+constexpr uint32_t kFlagOutsideMask = 2u;    // residual trit set outside its mask
+constexpr uint32_t kFlagMaskBits = 4u;       // mask bit set past the last group
+constexpr uint32_t kFlagBadCode = 8u;        // invalid 2-bit code / base-3 byte / pad trit
+constexpr uint32_t kFlagRowptr = 16u;        // rowptr disagrees with the mask
+
+}  // namespace tern

@@ -1,0 +1,486 @@
+// Host half of the C ABI declared in include/tern.h: argument and alignment
+// checks, buffer and workspace sizing, work decomposition and launches.
+#include "tern.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "internal.h"
+
+using tern::GemvDesc;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+tern_status fail(tern_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+tern_status hip_fail(hipError_t e, const char* what) {
+  return fail(TERN_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define TERN_HIP(call)                                  \
+  do {                                                  \
+    hipError_t e_ = (call);                             \
+    if (e_ != hipSuccess) return hip_fail(e_, #call);   \
+  } while (0)
+
+#define TERN_TRY(expr)                   \
+  do {                                   \
+    tern_status s_ = (expr);             \
+    if (s_ != TERN_OK) return s_;        \
+  } while (0)
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr size_t kFlagBytes = 256;
+constexpr int kTargetItems = 2048;  // decode work items that keep 256 CUs busy
+
+tern_status check_shape(int32_t n, int32_t k, int32_t group, int32_t planes, int32_t format,
+                        int32_t offset_mode) {
+  if (n < 0 || k < 0) return fail(TERN_E_INVAL, "negative shape n=%d k=%d", n, k);
+  if (group <= 0 || group % 64 || group > 1024)
+    return fail(TERN_E_UNSUPPORTED, "group %d must be a positive multiple of 64 up to 1024", group);
+  if (k % 64 || k % group) return fail(TERN_E_UNSUPPORTED, "k=%d must be a multiple of 64 and of group %d", k, group);
+  if (planes < 1 || planes > 3) return fail(TERN_E_UNSUPPORTED, "planes=%d outside 1..3", planes);
+  if (format != TERN_FMT_2BIT && format != TERN_FMT_B3) return fail(TERN_E_UNSUPPORTED, "unknown format %d", format);
+  if (offset_mode < TERN_OFF_NONE || offset_mode > TERN_OFF_GROUP)
+    return fail(TERN_E_UNSUPPORTED, "unknown offset mode %d", offset_mode);
+  return TERN_OK;
+}
+
+// Arrays read with 16-byte vector loads (plane0, blocks, trits, x, workspace)
+// need 16-byte alignment; the others need their element size.
+tern_status check_dev(const void* p, bool needed, const char* name, size_t align = 16) {
+  if (!p) return needed ? fail(TERN_E_INVAL, "%s is NULL", name) : TERN_OK;
+  if (!aligned_to(p, align)) return fail(TERN_E_ALIGN, "%s is not %zu-byte aligned", name, align);
+  return TERN_OK;
+}
+
+int mask_words(int k, int group) { return (k / group + 31) / 32; }
+
+// Descriptor pointers that a product reads.
+tern_status check_matrix(const tern_matrix* w) {
+  if (!w) return fail(TERN_E_INVAL, "matrix descriptor is NULL");
+  TERN_TRY(check_shape(w->n, w->k, w->group, w->planes, w->format, w->offset_mode));
+  const bool body = w->n > 0 && w->k > 0;
+  TERN_TRY(check_dev(w->plane0, body, "plane0"));
+  TERN_TRY(check_dev(w->scale0, body, "scale0", 2));
+  for (int p = 0; p < w->planes - 1; ++p) {
+    TERN_TRY(check_dev(w->mask[p], body, "mask", 4));
+    TERN_TRY(check_dev(w->rowptr[p], w->n > 0, "rowptr", 4));
+    TERN_TRY(check_dev(w->blocks[p], body && w->nnz[p] > 0, "blocks"));
+    TERN_TRY(check_dev(w->rscale[p], body && w->nnz[p] > 0, "rscale", 2));
+    if ((uint64_t)w->nnz[p] > (uint64_t)w->n * (uint64_t)(w->k / w->group))
+      return fail(TERN_E_INVAL, "nnz[%d]=%u exceeds the number of groups", p, w->nnz[p]);
+  }
+  TERN_TRY(check_dev(w->offset, body && w->offset_mode != TERN_OFF_NONE, "offset", 2));
+  return TERN_OK;
+}
+
+// Split of K for a single decode product: enough work items to fill the GPU,
+// split boundaries on stage multiples.
+void choose_splits(const tern_matrix* w, int* splits, int* gps) {
+  const int ng = w->k / w->group;
+  const int sg = tern::gemv_stage_bytes(w->format, w->group);
+  const int rb = (w->n + tern::kGemvRows - 1) / tern::kGemvRows;
+  const int max_splits = std::max(1, (ng + sg - 1) / sg);
+  int s = std::min(max_splits, std::max(1, (kTargetItems + rb - 1) / std::max(rb, 1)));
+  int g = (ng + s - 1) / s;
+  g = (g + sg - 1) / sg * sg;
+  g = std::max(g, sg);
+  *gps = g;
+  *splits = std::max(1, (ng + g - 1) / g);
+}
+
+bool product_group_ok(int group) { return group == 64 || group == 128; }
+
+int pick_mt(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8; }
+
+void fill_desc(GemvDesc& d, const tern_matrix* w, const uint16_t* x, int m, void* y, int y_f32) {
+  std::memset(&d, 0, sizeof(d));
+  d.plane0 = w->plane0;
+  d.scale0 = w->scale0;
+  for (int p = 0; p < 2; ++p) {
+    const bool on = p < w->planes - 1;
+    d.mask[p] = on ? w->mask[p] : nullptr;
+    d.rowptr[p] = on ? w->rowptr[p] : nullptr;
+    d.blocks[p] = on ? w->blocks[p] : nullptr;
+    d.rscale[p] = on ? w->rscale[p] : nullptr;
+  }
+  d.offset = w->offset_mode != TERN_OFF_NONE ? w->offset : nullptr;
+  d.x = x;
+  d.y = y;
+  d.n = w->n;
+  d.k = w->k;
+  d.group = w->group;
+  d.planes = w->planes;
+  d.offset_mode = w->offset_mode;
+  d.m = m;
+  d.stride = (int32_t)tern_row_stride(w->k, w->group, w->format);
+  d.ng = w->group ? w->k / w->group : 0;
+  d.mwords = mask_words(w->k, w->group);
+  d.splits = 1;
+  d.gps = d.ng;
+  d.row_blocks = (w->n + tern::kGemvRows - 1) / tern::kGemvRows;
+  d.y_f32 = y_f32;
+}
+
+size_t gemv_ws_bytes(const tern_matrix* w, int m) {
+  if (m <= 0 || w->n <= 0 || w->k <= 0 || !product_group_ok(w->group)) return 0;
+  int splits, gps;
+  choose_splits(w, &splits, &gps);
+  if (splits <= 1) return 0;
+  return round_up((size_t)splits * std::min(m, tern::kMaxMT) * w->n * sizeof(float), 256);
+}
+
+tern_status flag_status(uint32_t flag, bool unpacking) {
+  if (!flag) return TERN_OK;
+  if (unpacking) {
+    if (flag & tern::kFlagBadCode) return fail(TERN_E_CORRUPT, "invalid packed code (2-bit 10, base-3 byte > 242 or non-zero pad trit)");
+    if (flag & tern::kFlagRowptr) return fail(TERN_E_CORRUPT, "rowptr disagrees with the mask popcounts");
+    if (flag & tern::kFlagMaskBits) return fail(TERN_E_CORRUPT, "mask has bits past the last group");
+  }
+  if (flag & tern::kFlagBadTrit) return fail(TERN_E_INVAL, "trit outside {-1, 0, 1}");
+  if (flag & tern::kFlagOutsideMask) return fail(TERN_E_INVAL, "non-zero residual trit outside its mask");
+  if (flag & tern::kFlagMaskBits) return fail(TERN_E_INVAL, "mask has bits past the last group");
+  return fail(TERN_E_INVAL, "validation flag 0x%x", flag);
+}
+
+tern_status check_xy(const uint16_t* x, void* y, int y_dtype) {
+  if (y_dtype != TERN_F16 && y_dtype != TERN_F32) return fail(TERN_E_UNSUPPORTED, "unknown y dtype %d", y_dtype);
+  TERN_TRY(check_dev(x, true, "x"));
+  TERN_TRY(check_dev(y, true, "y", y_dtype == TERN_F32 ? 4 : 2));
+  return TERN_OK;
+}
+
+}  // namespace
+
+struct tern_plan {
+  const GemvDesc* dev;
+  int ndesc;
+  int total_items;
+  int format, group, mt;
+};
+
+extern "C" {
+
+size_t tern_row_stride(int32_t k, int32_t group, int32_t format) {
+  if (k < 0 || group <= 0 || k % 64 || group % 64 || group > 1024 || k % group) return 0;
+  if (format == TERN_FMT_2BIT) return (size_t)k / 4;
+  if (format == TERN_FMT_B3) return round_up((size_t)(k / group) * ((group + 4) / 5), 16);
+  return 0;
+}
+
+tern_status tern_check(const tern_matrix* w) { return check_matrix(w); }
+
+tern_status tern_packed_sizes(int32_t n, int32_t k, int32_t group, int32_t format, int32_t planes,
+                              const uint32_t* nnz, int32_t offset_mode, size_t out[TERN_NBUF]) {
+  if (!out) return fail(TERN_E_INVAL, "out_bytes is NULL");
+  TERN_TRY(check_shape(n, k, group, planes, format, offset_mode));
+  if (planes > 1 && !nnz) return fail(TERN_E_INVAL, "nnz is NULL with residual planes");
+  const size_t ng = (size_t)(k / group);
+  for (int i = 0; i < TERN_NBUF; ++i) out[i] = 0;
+  out[TERN_BUF_PLANE0] = (size_t)n * tern_row_stride(k, group, format);
+  out[TERN_BUF_SCALE0] = (size_t)n * ng * 2;
+  out[TERN_BUF_OFFSET] = offset_mode == TERN_OFF_ROW ? (size_t)n * 2 : offset_mode == TERN_OFF_GROUP ? (size_t)n * ng * 2 : 0;
+  if (planes > 1) {
+    out[TERN_BUF_MASK] = (size_t)n * mask_words(k, group) * 4;
+    out[TERN_BUF_ROWPTR] = ((size_t)n + 1) * 4;
+    for (int p = 0; p < planes - 1; ++p) {
+      out[TERN_BUF_BLOCKS1 + p] = (size_t)nnz[p] * (group / 4);
+      out[TERN_BUF_RSCALE1 + p] = (size_t)nnz[p] * 2;
+    }
+  }
+  return TERN_OK;
+}
+
+size_t tern_workspace_bytes(const tern_matrix* w, int32_t m) {
+  if (!w || check_shape(w->n, w->k, w->group, w->planes, w->format, w->offset_mode) != TERN_OK) return 0;
+  const size_t packing = kFlagBytes + round_up(((size_t)w->n + 1) * 4, 256);
+  return std::max(packing, gemv_ws_bytes(w, m));
+}
+
+tern_status tern_pack(const int8_t* trits, const uint16_t* rscale_dense, const tern_matrix* dst,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (!dst) return fail(TERN_E_INVAL, "dst is NULL");
+  TERN_TRY(check_shape(dst->n, dst->k, dst->group, dst->planes, dst->format, dst->offset_mode));
+  const int n = dst->n, k = dst->k, group = dst->group;
+  if (n == 0 || k == 0) return TERN_OK;
+  TERN_TRY(check_dev(trits, true, "trits"));
+  TERN_TRY(check_dev(dst->plane0, true, "plane0"));
+  if (dst->planes > 1) TERN_TRY(check_dev(rscale_dense, true, "rscale_dense", 2));
+  for (int p = 0; p < dst->planes - 1; ++p) {
+    TERN_TRY(check_dev(dst->mask[p], true, "mask", 4));
+    TERN_TRY(check_dev(dst->rowptr[p], true, "rowptr", 4));
+    TERN_TRY(check_dev(dst->blocks[p], dst->nnz[p] > 0, "blocks"));
+    TERN_TRY(check_dev(dst->rscale[p], dst->nnz[p] > 0, "rscale", 2));
+  }
+  if (!ws || ws_bytes < kFlagBytes) return fail(TERN_E_WORKSPACE, "pack needs %zu workspace bytes", kFlagBytes);
+  TERN_TRY(check_dev(ws, true, "ws"));
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* flag = static_cast<uint32_t*>(ws);
+  const int stride = (int)tern_row_stride(k, group, dst->format);
+  const int ng = k / group, mw = mask_words(k, group);
+  TERN_HIP(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
+  TERN_HIP(tern::launch_pack_plane0(dst->format, trits, n, k, group, stride, dst->plane0, flag, s));
+  for (int p = 0; p < dst->planes - 1; ++p) {
+    const int8_t* tp = trits + (size_t)(p + 1) * n * k;
+    TERN_HIP(tern::launch_mask_counts(dst->mask[p], n, ng, mw, dst->rowptr[p], flag, s));
+    TERN_HIP(tern::launch_rowptr_scan(dst->rowptr[p], n, s));
+    uint32_t total = 0, fl = 0;
+    TERN_HIP(hipMemcpyAsync(&total, dst->rowptr[p] + n, sizeof(total), hipMemcpyDeviceToHost, s));
+    TERN_HIP(hipMemcpyAsync(&fl, flag, sizeof(fl), hipMemcpyDeviceToHost, s));
+    TERN_HIP(hipStreamSynchronize(s));
+    if (fl) return flag_status(fl, false);
+    if (total != dst->nnz[p])
+      return fail(TERN_E_INVAL, "residual plane %d: mask has %u groups but nnz is %u", p + 1, total, dst->nnz[p]);
+    TERN_HIP(tern::launch_pack_residual(tp, rscale_dense + (size_t)p * n * ng, dst->mask[p], dst->rowptr[p],
+                                        n, k, group, mw, dst->blocks[p], dst->rscale[p], flag, s));
+  }
+  uint32_t fl = 0;
+  TERN_HIP(hipMemcpyAsync(&fl, flag, sizeof(fl), hipMemcpyDeviceToHost, s));
+  TERN_HIP(hipStreamSynchronize(s));
+  return flag_status(fl, false);
+}
+
+tern_status tern_unpack(const tern_matrix* src, int8_t* trits, void* ws, size_t ws_bytes, void* stream) {
+  TERN_TRY(check_matrix(src));
+  const int n = src->n, k = src->k, group = src->group;
+  if (n == 0 || k == 0) return TERN_OK;
+  TERN_TRY(check_dev(trits, true, "trits"));
+  const size_t need = kFlagBytes + round_up(((size_t)n + 1) * 4, 256);
+  if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "unpack needs %zu workspace bytes", need);
+  TERN_TRY(check_dev(ws, true, "ws"));
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* flag = static_cast<uint32_t*>(ws);
+  uint32_t* expect = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kFlagBytes);
+  const int stride = (int)tern_row_stride(k, group, src->format);
+  const int ng = k / group, mw = mask_words(k, group);
+  TERN_HIP(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
+  TERN_HIP(tern::launch_unpack_plane0(src->format, src->plane0, n, k, group, stride, trits, flag, s));
+  for (int p = 0; p < src->planes - 1; ++p) {
+    TERN_HIP(tern::launch_mask_counts(src->mask[p], n, ng, mw, expect, flag, s));
+    TERN_HIP(tern::launch_rowptr_scan(expect, n, s));
+    TERN_HIP(tern::launch_compare_u32(expect, src->rowptr[p], n + 1, tern::kFlagRowptr, flag, s));
+    uint32_t total = 0, fl = 0;
+    TERN_HIP(hipMemcpyAsync(&total, expect + n, sizeof(total), hipMemcpyDeviceToHost, s));
+    TERN_HIP(hipMemcpyAsync(&fl, flag, sizeof(fl), hipMemcpyDeviceToHost, s));
+    TERN_HIP(hipStreamSynchronize(s));
+    if (fl & (tern::kFlagRowptr | tern::kFlagMaskBits)) return flag_status(fl, true);
+    if (total != src->nnz[p])
+      return fail(TERN_E_CORRUPT, "residual plane %d: mask has %u groups but nnz is %u", p + 1, total, src->nnz[p]);
+    TERN_HIP(tern::launch_unpack_residual(src->blocks[p], src->mask[p], src->rowptr[p], n, k, group, mw,
+                                          trits + (size_t)(p + 1) * n * k, flag, s));
+  }
+  uint32_t fl = 0;
+  TERN_HIP(hipMemcpyAsync(&fl, flag, sizeof(fl), hipMemcpyDeviceToHost, s));
+  TERN_HIP(hipStreamSynchronize(s));
+  return flag_status(fl, true);
+}
+
+tern_status tern_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* y, int32_t y_dtype,
+                      void* ws, size_t ws_bytes, void* stream) {
+  TERN_TRY(check_matrix(w));
+  if (m < 0) return fail(TERN_E_INVAL, "m=%d is negative", m);
+  if (m >= 64) return fail(TERN_E_UNSUPPORTED, "tern_gemv takes m <= 63 (got %d); use tern_gemm", m);
+  if (m == 0 || w->n == 0) return TERN_OK;
+  TERN_TRY(check_xy(x, y, y_dtype));
+  if (!product_group_ok(w->group)) return fail(TERN_E_UNSUPPORTED, "products support group 64 or 128 (got %d)", w->group);
+  hipStream_t s = (hipStream_t)stream;
+  const int y_f32 = y_dtype == TERN_F32;
+  GemvDesc d;
+  fill_desc(d, w, x, m, y, y_f32);
+  if (w->k == 0) {
+    TERN_HIP(tern::launch_gemm(d, w->format, s));  // ng == 0: zero fill
+    return TERN_OK;
+  }
+  int splits, gps;
+  choose_splits(w, &splits, &gps);
+  const size_t need = gemv_ws_bytes(w, m);
+  if (need && (!ws || ws_bytes < need)) return fail(TERN_E_WORKSPACE, "tern_gemv needs %zu workspace bytes", need);
+  if (need) TERN_TRY(check_dev(ws, true, "ws"));
+  const size_t esz = y_f32 ? 4 : 2;
+  for (int c0 = 0; c0 < m; c0 += tern::kMaxMT) {
+    const int mc = std::min(tern::kMaxMT, m - c0);
+    GemvDesc dc = d;
+    dc.x = x + (size_t)c0 * w->k;
+    dc.y = static_cast<char*>(y) + (size_t)c0 * w->n * esz;
+    dc.m = mc;
+    dc.splits = splits;
+    dc.gps = gps;
+    dc.partial = splits > 1 ? static_cast<float*>(ws) : nullptr;
+    dc.tile_begin = 0;
+    const int items = splits * dc.row_blocks;
+    TERN_HIP(tern::launch_gemv(w->format, w->group, pick_mt(mc), nullptr, 0, dc, items, 0, s));
+    if (splits > 1) TERN_HIP(tern::launch_splitk_reduce(dc.partial, splits, mc, w->n, dc.y, y_f32, s));
+  }
+  return TERN_OK;
+}
+
+tern_status tern_gemm(const tern_matrix* w, const uint16_t* x, int32_t m, void* y, int32_t y_dtype,
+                      void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  TERN_TRY(check_matrix(w));
+  if (m < 0) return fail(TERN_E_INVAL, "m=%d is negative", m);
+  if (m == 0 || w->n == 0) return TERN_OK;
+  TERN_TRY(check_xy(x, y, y_dtype));
+  if (!product_group_ok(w->group)) return fail(TERN_E_UNSUPPORTED, "products support group 64 or 128 (got %d)", w->group);
+  GemvDesc d;
+  fill_desc(d, w, x, m, y, y_dtype == TERN_F32);
+  TERN_HIP(tern::launch_gemm(d, w->format, (hipStream_t)stream));
+  return TERN_OK;
+}
+
+// ---- grouped decode
+static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y,
+                               int32_t count, int32_t m, int32_t y_dtype,
+                               std::vector<GemvDesc>* out, int* total, int* mt) {
+  if (count < 0) return fail(TERN_E_INVAL, "count=%d is negative", count);
+  if (count > 0 && (!w || !x || !y)) return fail(TERN_E_INVAL, "NULL descriptor arrays");
+  if (m < 0) return fail(TERN_E_INVAL, "m=%d is negative", m);
+  if (m >= 64) return fail(TERN_E_UNSUPPORTED, "batched decode takes m <= 63 (got %d)", m);
+  if (y_dtype != TERN_F16 && y_dtype != TERN_F32) return fail(TERN_E_UNSUPPORTED, "unknown y dtype %d", y_dtype);
+  out->clear();
+  *total = 0;
+  *mt = pick_mt(std::min(m, tern::kMaxMT));
+  std::vector<int> order;
+  for (int i = 0; i < count; ++i) {
+    TERN_TRY(check_matrix(&w[i]));
+    if (w[i].format != w[0].format || w[i].group != w[0].group)
+      return fail(TERN_E_UNSUPPORTED, "batched products must share format and group");
+    if (!product_group_ok(w[i].group)) return fail(TERN_E_UNSUPPORTED, "products support group 64 or 128");
+    if (w[i].n == 0 || m == 0) continue;
+    if (w[i].k == 0) return fail(TERN_E_UNSUPPORTED, "batched decode needs k > 0");
+    TERN_TRY(check_xy(x[i], y[i], y_dtype));
+    order.push_back(i);
+  }
+  // longest work items first
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return w[a].k > w[b].k; });
+  const size_t esz = y_dtype == TERN_F32 ? 4 : 2;
+  for (int i : order) {
+    for (int c0 = 0; c0 < m; c0 += tern::kMaxMT) {
+      GemvDesc d;
+      fill_desc(d, &w[i], x[i] + (size_t)c0 * w[i].k, std::min(tern::kMaxMT, m - c0),
+                static_cast<char*>(y[i]) + (size_t)c0 * w[i].n * esz, y_dtype == TERN_F32);
+      d.tile_begin = *total;
+      *total += d.row_blocks;
+      out->push_back(d);
+    }
+  }
+  return TERN_OK;
+}
+
+size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m) {
+  (void)w;
+  if (count <= 0) return 0;
+  const int chunks = std::max(1, (m + tern::kMaxMT - 1) / tern::kMaxMT);
+  return round_up((size_t)count * chunks * sizeof(GemvDesc), 256);
+}
+
+tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, void* const* y,
+                              int32_t count, int32_t m, int32_t y_dtype, void* ws, size_t ws_bytes,
+                              void* stream) {
+  std::vector<GemvDesc> descs;
+  int total = 0, mt = 1;
+  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &descs, &total, &mt));
+  if (descs.empty()) return TERN_OK;
+  const size_t need = descs.size() * sizeof(GemvDesc);
+  if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "batched decode needs %zu workspace bytes", need);
+  TERN_TRY(check_dev(ws, true, "ws"));
+  hipStream_t s = (hipStream_t)stream;
+  TERN_HIP(hipMemcpyAsync(ws, descs.data(), need, hipMemcpyHostToDevice, s));
+  TERN_HIP(tern::launch_gemv(w[0].format, w[0].group, mt, static_cast<const GemvDesc*>(ws),
+                             (int)descs.size(), descs[0], total, 0, s));
+  return TERN_OK;
+}
+
+tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, void* const* y,
+                             int32_t count, int32_t m, int32_t y_dtype, void* ws, size_t ws_bytes,
+                             tern_plan** out) {
+  if (!out) return fail(TERN_E_INVAL, "out is NULL");
+  *out = nullptr;
+  std::vector<GemvDesc> descs;
+  int total = 0, mt = 1;
+  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &descs, &total, &mt));
+  const size_t need = descs.size() * sizeof(GemvDesc);
+  if (need) {
+    if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "plan needs %zu workspace bytes", need);
+    TERN_TRY(check_dev(ws, true, "ws"));
+    TERN_HIP(hipMemcpy(ws, descs.data(), need, hipMemcpyHostToDevice));
+  }
+  tern_plan* p = static_cast<tern_plan*>(std::malloc(sizeof(tern_plan)));
+  if (!p) return fail(TERN_E_INVAL, "out of host memory");
+  p->dev = static_cast<const GemvDesc*>(ws);
+  p->ndesc = (int)descs.size();
+  p->total_items = total;
+  p->format = count > 0 ? w[0].format : 0;
+  p->group = count > 0 ? w[0].group : 128;
+  p->mt = mt;
+  *out = p;
+  return TERN_OK;
+}
+
+tern_status tern_plan_run(const tern_plan* plan, void* stream) {
+  if (!plan) return fail(TERN_E_INVAL, "plan is NULL");
+  if (plan->ndesc == 0) return TERN_OK;
+  GemvDesc dummy;
+  std::memset(&dummy, 0, sizeof(dummy));
+  TERN_HIP(tern::launch_gemv(plan->format, plan->group, plan->mt, plan->dev, plan->ndesc, dummy,
+                             plan->total_items, 0, (hipStream_t)stream));
+  return TERN_OK;
+}
+
+void tern_plan_destroy(tern_plan* plan) { std::free(plan); }
+
+tern_status tern_bits(const tern_matrix* w, double* info, double* plane, double* storage) {
+  if (!w) return fail(TERN_E_INVAL, "matrix descriptor is NULL");
+  TERN_TRY(check_shape(w->n, w->k, w->group, w->planes, w->format, w->offset_mode));
+  const double weights = (double)w->n * (double)w->k;
+  if (weights == 0) return fail(TERN_E_INVAL, "empty matrix");
+  size_t sz[TERN_NBUF];
+  TERN_TRY(tern_packed_sizes(w->n, w->k, w->group, w->format, w->planes, w->nnz, w->offset_mode, sz));
+  double trits = weights, planeb = (double)sz[TERN_BUF_PLANE0], total = 0;
+  for (int p = 0; p < w->planes - 1; ++p) {
+    trits += (double)w->nnz[p] * w->group;
+    planeb += (double)sz[TERN_BUF_BLOCKS1 + p];
+  }
+  for (int i = 0; i < TERN_NBUF; ++i) total += (double)sz[i];
+  if (w->planes > 1) total += (double)(w->planes - 2) * (sz[TERN_BUF_MASK] + sz[TERN_BUF_ROWPTR]);
+  if (info) *info = std::log2(3.0) * trits / weights;
+  if (plane) *plane = 8.0 * planeb / weights;
+  if (storage) *storage = 8.0 * total / weights;
+  return TERN_OK;
+}
+
+const char* tern_status_str(tern_status s) {
+  switch (s) {
+    case TERN_OK: return "TERN_OK";
+    case TERN_E_INVAL: return "TERN_E_INVAL";
+    case TERN_E_ALIGN: return "TERN_E_ALIGN";
+    case TERN_E_UNSUPPORTED: return "TERN_E_UNSUPPORTED";
+    case TERN_E_CORRUPT: return "TERN_E_CORRUPT";
+    case TERN_E_WORKSPACE: return "TERN_E_WORKSPACE";
+    case TERN_E_HIP: return "TERN_E_HIP";
+  }
+  return "TERN_E_UNKNOWN";
+}
+
+const char* tern_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,274 @@
+"""ctypes binding of libtern (include/tern.h), with the same names.
+
+Argument marshalling only: torch supplies device memory and streams, every
+step of packing and of the products runs in the HIP kernels behind the C ABI.
+There is no CPU fallback: importing this module on a machine without the
+built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_double, c_int32, c_size_t, c_uint32, c_void_p
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libtern.so")
+
+TERN_OK = 0
+TERN_E_INVAL = -1
+TERN_E_ALIGN = -2
+TERN_E_UNSUPPORTED = -3
+TERN_E_CORRUPT = -4
+TERN_E_WORKSPACE = -5
+TERN_E_HIP = -6
+
+TERN_FMT_2BIT = 0
+TERN_FMT_B3 = 1
+TERN_OFF_NONE = 0
+TERN_OFF_ROW = 1
+TERN_OFF_GROUP = 2
+TERN_F16 = 0
+TERN_F32 = 1
+
+(TERN_BUF_PLANE0, TERN_BUF_SCALE0, TERN_BUF_OFFSET, TERN_BUF_MASK, TERN_BUF_ROWPTR,
+ TERN_BUF_BLOCKS1, TERN_BUF_BLOCKS2, TERN_BUF_RSCALE1, TERN_BUF_RSCALE2, TERN_NBUF) = range(10)
+
+SYMBOLS = ["tern_row_stride", "tern_check", "tern_packed_sizes", "tern_workspace_bytes",
+           "tern_pack", "tern_unpack", "tern_gemv", "tern_gemm", "tern_batch_workspace_bytes",
+           "tern_gemv_batched", "tern_plan_create", "tern_plan_run", "tern_plan_destroy",
+           "tern_bits", "tern_status_str", "tern_last_error"]
+
+
+class tern_matrix(ctypes.Structure):
+    _fields_ = [("n", c_int32), ("k", c_int32), ("group", c_int32), ("planes", c_int32),
+                ("format", c_int32), ("offset_mode", c_int32),
+                ("plane0", c_void_p), ("scale0", c_void_p),
+                ("mask", c_void_p * 2), ("rowptr", c_void_p * 2), ("blocks", c_void_p * 2),
+                ("rscale", c_void_p * 2), ("offset", c_void_p), ("nnz", c_uint32 * 2)]
+
+
+class TernError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_str(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libtern.so (built in-tree by ternary_weight_only_tern_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m ternary_weight_only_tern_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = POINTER(tern_matrix)
+    sig = {
+        "tern_row_stride": (c_size_t, [c_int32, c_int32, c_int32]),
+        "tern_check": (c_int32, [P]),
+        "tern_packed_sizes": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, POINTER(c_uint32), c_int32, POINTER(c_size_t)]),
+        "tern_workspace_bytes": (c_size_t, [P, c_int32]),
+        "tern_pack": (c_int32, [c_void_p, c_void_p, P, c_void_p, c_size_t, c_void_p]),
+        "tern_unpack": (c_int32, [P, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "tern_gemv": (c_int32, [P, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_size_t, c_void_p]),
+        "tern_gemm": (c_int32, [P, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_size_t, c_void_p]),
+        "tern_batch_workspace_bytes": (c_size_t, [P, c_int32, c_int32]),
+        "tern_gemv_batched": (c_int32, [P, POINTER(c_void_p), POINTER(c_void_p), c_int32, c_int32, c_int32, c_void_p, c_size_t, c_void_p]),
+        "tern_plan_create": (c_int32, [P, POINTER(c_void_p), POINTER(c_void_p), c_int32, c_int32, c_int32, c_void_p, c_size_t, POINTER(c_void_p)]),
+        "tern_plan_run": (c_int32, [c_void_p, c_void_p]),
+        "tern_plan_destroy": (None, [c_void_p]),
+        "tern_bits": (c_int32, [P, POINTER(c_double), POINTER(c_double), POINTER(c_double)]),
+        "tern_status_str": (ctypes.c_char_p, [c_int32]),
+        "tern_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().tern_status_str(status).decode()
+
+
+def last_error() -> str:
+    return load().tern_last_error().decode()
+
+
+def check(status: int) -> None:
+    if status != TERN_OK:
+        raise TernError(status, last_error())
+
+
+# ---------------------------------------------------------------- thin wrappers
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def tern_row_stride(k: int, group: int, fmt: int) -> int:
+    return load().tern_row_stride(k, group, fmt)
+
+
+def tern_packed_sizes(n, k, group, fmt, planes, nnz, offset_mode) -> list:
+    out = (c_size_t * TERN_NBUF)()
+    nz = (c_uint32 * 2)(*(list(nnz) + [0, 0])[:2])
+    check(load().tern_packed_sizes(n, k, group, fmt, planes, nz, offset_mode, out))
+    return list(out)
+
+
+class PackedMatrix:
+    """Device buffers of one packed matrix (torch tensors) and its descriptor."""
+
+    def __init__(self, n, k, group, planes, fmt, offset_mode, nnz, device="cuda"):
+        import torch
+        self.n, self.k, self.group, self.planes, self.fmt = n, k, group, planes, fmt
+        self.offset_mode = offset_mode
+        self.nnz = [int(v) for v in (list(nnz) + [0, 0])[:2]]
+        sz = tern_packed_sizes(n, k, group, fmt, planes, self.nnz, offset_mode)
+        u8 = dict(dtype=torch.uint8, device=device)
+        ng = k // group if group else 0
+        self.plane0 = torch.zeros(max(sz[TERN_BUF_PLANE0], 1), **u8)
+        self.scale0 = torch.zeros((n, ng), dtype=torch.float16, device=device)
+        self.mask, self.rowptr, self.blocks, self.rscale = [], [], [], []
+        for p in range(planes - 1):
+            self.mask.append(torch.zeros((n, (ng + 31) // 32), dtype=torch.int32, device=device))
+            self.rowptr.append(torch.zeros(n + 1, dtype=torch.int32, device=device))
+            self.blocks.append(torch.zeros(max(sz[TERN_BUF_BLOCKS1 + p], 1), **u8))
+            self.rscale.append(torch.zeros(max(self.nnz[p], 1), dtype=torch.float16, device=device))
+        shape = (n,) if offset_mode == TERN_OFF_ROW else (n, ng)
+        self.offset = (torch.zeros(shape, dtype=torch.float16, device=device)
+                       if offset_mode != TERN_OFF_NONE else None)
+
+    def desc(self) -> tern_matrix:
+        d = tern_matrix()
+        d.n, d.k, d.group, d.planes = self.n, self.k, self.group, self.planes
+        d.format, d.offset_mode = self.fmt, self.offset_mode
+        d.plane0, d.scale0 = _ptr(self.plane0), _ptr(self.scale0)
+        for p in range(self.planes - 1):
+            d.mask[p] = _ptr(self.mask[p])
+            d.rowptr[p] = _ptr(self.rowptr[p])
+            d.blocks[p] = _ptr(self.blocks[p])
+            d.rscale[p] = _ptr(self.rscale[p])
+            d.nnz[p] = self.nnz[p]
+        d.offset = _ptr(self.offset)
+        return d
+
+    def nbytes(self) -> int:
+        """Bytes of the representation a product reads (every buffer)."""
+        sz = tern_packed_sizes(self.n, self.k, self.group, self.fmt, self.planes, self.nnz,
+                               self.offset_mode)
+        extra = max(self.planes - 2, 0) * (sz[TERN_BUF_MASK] + sz[TERN_BUF_ROWPTR])
+        return sum(sz) + extra
+
+
+def _workspace(desc: tern_matrix, m: int, device="cuda"):
+    import torch
+    nbytes = load().tern_workspace_bytes(ctypes.byref(desc), m)
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def tern_pack(pm: PackedMatrix, trits, scales, mask_bits, offset=None, stream=None, ws=None):
+    """Fill pm from device trits [P][N][K] int8, scales [P][N][K/G] fp16 and
+    mask_bits [P-1][N][W] int32 (copied into pm.mask); plane-0 scales and the
+    offset are copied into pm as given."""
+    pm.scale0.copy_(scales[0])
+    for p in range(pm.planes - 1):
+        pm.mask[p].copy_(mask_bits[p])
+    if pm.offset is not None:
+        pm.offset.copy_(offset)
+    d = pm.desc()
+    ws = ws if ws is not None else _workspace(d, 1, pm.plane0.device)
+    rs = scales[1:].contiguous() if pm.planes > 1 else None
+    check(load().tern_pack(_ptr(trits), _ptr(rs), ctypes.byref(d), _ptr(ws), ws.numel(), _stream(stream)))
+    return pm
+
+
+def tern_unpack(pm: PackedMatrix, out=None, stream=None, ws=None):
+    import torch
+    d = pm.desc()
+    if out is None:
+        out = torch.empty((pm.planes, pm.n, pm.k), dtype=torch.int8, device=pm.plane0.device)
+    ws = ws if ws is not None else _workspace(d, 1, pm.plane0.device)
+    check(load().tern_unpack(ctypes.byref(d), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def _product(fn, pm, x, y_dtype, out, stream, ws):
+    import torch
+    m = x.shape[0]
+    if out is None:
+        dt = torch.float32 if y_dtype == TERN_F32 else torch.float16
+        out = torch.empty((m, pm.n), dtype=dt, device=x.device)
+    d = pm.desc()
+    ws = ws if ws is not None else _workspace(d, m, x.device)
+    check(fn(ctypes.byref(d), _ptr(x), m, _ptr(out), y_dtype, _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def tern_gemv(pm, x, y_dtype=TERN_F16, out=None, stream=None, ws=None):
+    return _product(load().tern_gemv, pm, x, y_dtype, out, stream, ws)
+
+
+def tern_gemm(pm, x, y_dtype=TERN_F16, out=None, stream=None, ws=None):
+    return _product(load().tern_gemm, pm, x, y_dtype, out, stream, ws)
+
+
+def _arrays(mats, xs, ys):
+    n = len(mats)
+    descs = (tern_matrix * max(n, 1))(*[m.desc() for m in mats])
+    xp = (c_void_p * max(n, 1))(*[x.data_ptr() for x in xs])
+    yp = (c_void_p * max(n, 1))(*[y.data_ptr() for y in ys])
+    return descs, xp, yp
+
+
+def tern_gemv_batched(mats, xs, ys, y_dtype=TERN_F16, stream=None, ws=None):
+    import torch
+    m = xs[0].shape[0] if xs else 0
+    descs, xp, yp = _arrays(mats, xs, ys)
+    if ws is None:
+        nbytes = load().tern_batch_workspace_bytes(descs, len(mats), m)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=xs[0].device)
+    check(load().tern_gemv_batched(descs, xp, yp, len(mats), m, y_dtype, _ptr(ws), ws.numel(), _stream(stream)))
+    return ys
+
+
+class Plan:
+    """tern_plan_create / tern_plan_run / tern_plan_destroy."""
+
+    def __init__(self, mats, xs, ys, y_dtype=TERN_F16):
+        import torch
+        self.m = xs[0].shape[0] if xs else 0
+        descs, xp, yp = _arrays(mats, xs, ys)
+        nbytes = load().tern_batch_workspace_bytes(descs, len(mats), self.m)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=xs[0].device)
+        self._keep = (mats, xs, ys)
+        handle = c_void_p()
+        check(load().tern_plan_create(descs, xp, yp, len(mats), self.m, y_dtype, _ptr(self.ws),
+                                      self.ws.numel(), ctypes.byref(handle)))
+        self.handle = handle
+
+    def run(self, stream=None):
+        check(load().tern_plan_run(self.handle, _stream(stream)))
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.tern_plan_destroy(self.handle)
+            self.handle = None
+
+
+def tern_bits(pm: PackedMatrix) -> dict:
+    d = pm.desc()
+    info, plane, storage = c_double(), c_double(), c_double()
+    check(load().tern_bits(ctypes.byref(d), ctypes.byref(info), ctypes.byref(plane), ctypes.byref(storage)))
+    return dict(info=info.value, plane=plane.value, storage=storage.value)

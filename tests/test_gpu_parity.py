@@ -1,0 +1,286 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Packing must be byte-identical to the oracle's encoding; products must meet
+|y - y_ref| <= 2e-3 * sum_k (|off| + sum_p m_p |s_p T_p|) |x| per element
+(the tolerance the project fixes for FP32 accumulation on FP16 inputs), with
+y == 0 exactly where that bound is 0.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from ternary_weight_only_tern_amd import lib as L
+from ternary_weight_only_tern_amd import synth
+
+from gpu_util import (assert_bytes_equal, check_y, oracle_pack, oracle_y, say, small_matrix,
+                       to_dev, upload_pack)
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [O.FMT_2BIT, O.FMT_B3]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    L.load()
+    yield
+
+
+def _ydt(f32):
+    return L.TERN_F32 if f32 else L.TERN_F16
+
+
+# ----------------------------------------------------------------- packing
+SMALL_SHAPES = [  # n, k, group, planes, frac, offset_mode
+    (128, 256, 64, 1, 0.0, O.OFF_NONE),
+    (65, 640, 64, 2, 0.3, O.OFF_GROUP),
+    (130, 1280, 128, 3, 0.2, O.OFF_ROW),
+    (7, 2560, 128, 2, 0.1, O.OFF_NONE),
+    (64, 128, 128, 2, 1.0, O.OFF_NONE),
+]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", SMALL_SHAPES)
+def test_pack_bytes_small(shape, fmt):
+    n, k, g, planes, frac, off = shape
+    say("pack", shape, fmt)
+    mat, _ = small_matrix(n, k, g, planes, frac, seed=n + k, offset_mode=off)
+    pm = upload_pack(mat, fmt)
+    assert_bytes_equal(pm, oracle_pack(mat, fmt))
+
+
+@pytest.mark.parametrize("cfg,proj,fmt", [(1, 0, O.FMT_2BIT), (2, 0, O.FMT_2BIT), (2, 6, O.FMT_B3),
+                                          (3, 4, O.FMT_B3), (3, 6, O.FMT_B3), (5, 0, O.FMT_2BIT),
+                                          (5, 0, O.FMT_B3)])
+def test_pack_bytes_config(cfg, proj, fmt):
+    say("pack config", cfg, proj, fmt)
+    mat = synth.config_matrix(cfg, proj)
+    pm = upload_pack(mat, fmt)
+    assert_bytes_equal(pm, oracle_pack(mat, fmt))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_unpack_roundtrip_and_corruption(fmt):
+    import torch
+    say("unpack", fmt)
+    mat, _ = small_matrix(96, 1280, 128, 3, 0.25, seed=3, offset_mode=O.OFF_ROW)
+    pm = upload_pack(mat, fmt)
+    back = L.tern_unpack(pm).cpu().numpy()
+    assert np.array_equal(back, mat["trits"])
+    # invalid plane-0 code
+    saved = pm.plane0.clone()
+    if fmt == O.FMT_2BIT:
+        pm.plane0[5] = 0x02          # offset-0 trit with code 10
+    else:
+        pm.plane0[5] = 250           # base-3 byte above 242
+    with pytest.raises(L.TernError) as e:
+        L.tern_unpack(pm)
+    assert e.value.status == L.TERN_E_CORRUPT
+    pm.plane0.copy_(saved)
+    if fmt == O.FMT_B3:
+        pm.plane0[25] = 121 - 81      # last byte of group 0 with a -1 padding trit
+        with pytest.raises(L.TernError) as e:
+            L.tern_unpack(pm)
+        assert e.value.status == L.TERN_E_CORRUPT
+        pm.plane0.copy_(saved)
+    # corrupt residual block code and rowptr
+    sb = pm.blocks[0].clone()
+    pm.blocks[0][0] = 0x02
+    with pytest.raises(L.TernError) as e:
+        L.tern_unpack(pm)
+    assert e.value.status == L.TERN_E_CORRUPT
+    pm.blocks[0].copy_(sb)
+    pm.rowptr[1][3] += 1
+    with pytest.raises(L.TernError) as e:
+        L.tern_unpack(pm)
+    assert e.value.status == L.TERN_E_CORRUPT
+    pm.rowptr[1][3] -= 1
+    assert np.array_equal(L.tern_unpack(pm).cpu().numpy(), mat["trits"])
+    torch.cuda.synchronize()
+
+
+def test_pack_rejects_invalid_input():
+    say("pack invalid")
+    mat, _ = small_matrix(64, 256, 64, 2, 0.25, seed=4)
+    bad = dict(mat)
+    bad["trits"] = mat["trits"].copy()
+    bad["trits"][0, 3, 7] = 2
+    with pytest.raises(L.TernError) as e:
+        upload_pack(bad, O.FMT_2BIT)
+    assert e.value.status == L.TERN_E_INVAL
+    bad["trits"] = mat["trits"].copy()
+    rows, groups = np.nonzero(~mat["masks"][0])
+    bad["trits"][1, rows[0], groups[0] * 64 + 5] = 1     # residual trit outside the mask
+    with pytest.raises(L.TernError) as e:
+        upload_pack(bad, O.FMT_B3)
+    assert e.value.status == L.TERN_E_INVAL
+
+
+# ----------------------------------------------------------------- decode products
+def _gemv_case(mat, fmt, m, x_law="normal", f32=False, seed=0, batched=False):
+    import torch
+    rng = np.random.default_rng(seed)
+    x = synth.draw_x(rng, m, mat["k"], x_law)
+    pm = upload_pack(mat, fmt)
+    xd = to_dev(x.view(np.uint16)).view(torch.float16)
+    y = L.tern_gemv(pm, xd, _ydt(f32))
+    torch.cuda.synchronize()
+    y_ref, b = oracle_y(mat, x)
+    return check_y(y, y_ref, b, f"gemv n={mat['n']} k={mat['k']} fmt={fmt} m={m}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", SMALL_SHAPES)
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_gemv_small(shape, fmt, m):
+    n, k, g, planes, frac, off = shape
+    say("gemv small", shape, fmt, m)
+    mat, _ = small_matrix(n, k, g, planes, frac, seed=7 * n + k, offset_mode=off, scale_law="lognormal")
+    _gemv_case(mat, fmt, m, x_law="student_t3", seed=m)
+
+
+@pytest.mark.parametrize("m", [9, 17, 63])
+def test_gemv_m_chunks(m):
+    say("gemv chunks", m)
+    mat, _ = small_matrix(100, 1024, 128, 2, 0.1, seed=m)
+    _gemv_case(mat, O.FMT_2BIT, m, f32=True, seed=m)
+    _gemv_case(mat, O.FMT_B3, m, seed=m)
+
+
+def test_gemv_config1():
+    say("gemv config 1")
+    mat = synth.config_matrix(1)
+    _gemv_case(mat, O.FMT_2BIT, 1, seed=0)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_config2_layer(fmt):
+    for proj in range(7):
+        say("gemv config 2", proj, fmt)
+        mat = synth.config_matrix(2, proj)
+        rel = _gemv_case(mat, fmt, 1, seed=proj)
+        say("  max |err|/B", rel)
+
+
+@pytest.mark.parametrize("fmt,m,f32", [(O.FMT_2BIT, 1, False), (O.FMT_2BIT, 8, True),
+                                       (O.FMT_B3, 1, True), (O.FMT_B3, 8, False)])
+def test_gemv_config5_stress(fmt, m, f32):
+    say("gemv config 5", fmt, m, f32)
+    mat = synth.config_matrix(5)
+    _gemv_case(mat, fmt, m, x_law="student_t3", f32=f32, seed=5)
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_gemv_config4_layer(m):
+    for proj in range(7):
+        say("gemv config 4", proj, m)
+        mat = synth.config_matrix(4, proj)
+        _gemv_case(mat, O.FMT_B3, m, seed=10 * m + proj)
+
+
+def test_gemv_zero_and_sign_invariants():
+    import torch
+    say("gemv invariants")
+    mat, rng = small_matrix(200, 1280, 128, 3, 0.2, seed=12, offset_mode=O.OFF_ROW)
+    x = synth.draw_x(rng, 2, 1280, "normal")
+    xd = to_dev(x.view(np.uint16)).view(torch.float16)
+    for fmt in FMTS:
+        pm = upload_pack(mat, fmt)
+        y1 = L.tern_gemv(pm, xd, L.TERN_F32)
+        y2 = L.tern_gemv(pm, xd, L.TERN_F32)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2), "run-to-run results differ"
+        neg = dict(mat, trits=-mat["trits"], offset=-mat["offset"])
+        yn = L.tern_gemv(upload_pack(neg, fmt), xd, L.TERN_F32)
+        assert torch.equal(yn, -y1), "sign flip is not exact"
+        zero = dict(mat, trits=np.zeros_like(mat["trits"]), offset=None, offset_mode=O.OFF_NONE)
+        yz = L.tern_gemv(upload_pack(zero, fmt), xd, L.TERN_F16)
+        assert not yz.any(), "all-zero trits must give exactly zero"
+
+
+def test_gemv_degenerate_shapes():
+    import torch
+    say("gemv degenerate")
+    for (n, k) in [(1, 64), (0, 128), (5, 0)]:
+        mat, rng = small_matrix(n, k, 64, 1, 0.0, seed=n + k)
+        pm = upload_pack(mat, O.FMT_2BIT)
+        x = synth.draw_x(rng, 2, k, "normal")
+        xd = to_dev(x.view(np.uint16)).view(torch.float16) if k else torch.zeros((2, 64), dtype=torch.float16, device="cuda")
+        y = torch.full((2, max(n, 1)), 7.0, dtype=torch.float32, device="cuda")
+        L.tern_gemv(pm, xd, L.TERN_F32, out=y)
+        torch.cuda.synchronize()
+        if n == 0:
+            assert (y == 7.0).all()
+        elif k == 0:
+            assert not y.any()
+        else:
+            y_ref, b = oracle_y(mat, x)
+            check_y(y, y_ref, b, "n=1")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_batched_and_plan_match_oracle(fmt):
+    import torch
+    say("batched", fmt)
+    mats, pms, xs, ys, refs = [], [], [], [], []
+    for proj in range(7):
+        mat = synth.config_matrix(2, proj)
+        x = synth.config_x(2, 1, proj)
+        mats.append(mat)
+        pms.append(upload_pack(mat, fmt))
+        xs.append(to_dev(x.view(np.uint16)).view(torch.float16))
+        ys.append(torch.empty((1, mat["n"]), dtype=torch.float16, device="cuda"))
+        refs.append(oracle_y(mat, x))
+    L.tern_gemv_batched(pms, xs, ys)
+    torch.cuda.synchronize()
+    for y, (y_ref, b) in zip(ys, refs):
+        check_y(y, y_ref, b, "batched")
+    first = [y.clone() for y in ys]
+    plan = L.Plan(pms, xs, ys)
+    for _ in range(3):
+        for y in ys:
+            y.zero_()
+        plan.run()
+        torch.cuda.synchronize()
+        for y, f in zip(ys, first):
+            assert torch.equal(y, f), "plan run differs from the batched call"
+
+
+# ----------------------------------------------------------------- MFMA product
+def _gemm_case(mat, fmt, m, x_law="normal", f32=False, seed=0):
+    import torch
+    rng = np.random.default_rng(seed)
+    x = synth.draw_x(rng, m, mat["k"], x_law)
+    pm = upload_pack(mat, fmt)
+    xd = to_dev(x.view(np.uint16)).view(torch.float16)
+    y = L.tern_gemm(pm, xd, _ydt(f32))
+    torch.cuda.synchronize()
+    y_ref, b = oracle_y(mat, x)
+    return check_y(y, y_ref, b, f"gemm n={mat['n']} k={mat['k']} fmt={fmt} m={m}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", SMALL_SHAPES)
+@pytest.mark.parametrize("m", [1, 64, 130])
+def test_gemm_small(shape, fmt, m):
+    n, k, g, planes, frac, off = shape
+    say("gemm small", shape, fmt, m)
+    mat, _ = small_matrix(n, k, g, planes, frac, seed=11 * n + k, offset_mode=off, scale_law="lognormal")
+    _gemm_case(mat, fmt, m, x_law="student_t3", seed=m, f32=(m == 130))
+
+
+@pytest.mark.parametrize("m", [64, 512])
+def test_gemm_config4_layer(m):
+    for proj in range(7):
+        say("gemm config 4", proj, m)
+        mat = synth.config_matrix(4, proj)
+        _gemm_case(mat, O.FMT_B3, m, seed=100 * m + proj)
+
+
+def test_gemm_config5():
+    say("gemm config 5")
+    mat = synth.config_matrix(5)
+    _gemm_case(mat, O.FMT_2BIT, 8, x_law="student_t3", f32=True, seed=55)
