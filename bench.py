@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Throughput of the packed ternary decode product (W1.58A16) on one MI355X.
+
+Headline workload: the Qwen3-4B-class decoder layer at M=1 (q 2560->4096,
+k/v 2560->1024, o 4096->2560, gate/up 2560->9728, down 9728->2560; group
+128; a residual plane on 10 % of groups; 2-bit planes).  One step is one
+decode token through one layer: the seven products in one grouped launch.
+The model has 36 layers (arXiv 2609.01962 §3.1), so the timed steps walk 36
+distinct, HBM-resident layer copies (1.07 GB; more than the 256 MB Infinity
+Cache) the way a decode does; steps are replayed from a HIP graph.
+
+value = packed-weight bytes of the step (every byte of the representation:
+planes, scales, residual blocks and metadata; activations excluded) divided
+by the step time.  Extra measurements on the same line: the Qwen3-8B-class
+36 x 7 base-3 stack at M=1 (tokens/s-equivalent) and the 8B-class layer at
+M=512 through the MFMA path (TFLOP/s).  The CPU baseline is the oracle's
+plain unpack-and-dot on one thread over a bounded sample of the workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+F16_MFMA_PEAK_TFS = 2500.0   # MI355X dense FP16 MFMA, TFLOP/s
+LAYERS = 36
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def clone_packed(pm):
+    from ternary_weight_only_tern_amd import lib as L
+    c = L.PackedMatrix.__new__(L.PackedMatrix)
+    c.__dict__.update(pm.__dict__)
+    c.plane0 = pm.plane0.clone()
+    c.scale0 = pm.scale0.clone()
+    c.mask = [t.clone() for t in pm.mask]
+    c.rowptr = [t.clone() for t in pm.rowptr]
+    c.blocks = [t.clone() for t in pm.blocks]
+    c.rscale = [t.clone() for t in pm.rscale]
+    c.offset = None if pm.offset is None else pm.offset.clone()
+    return c
+
+
+def pack_config(cfg: int, fmt: int, proj: int, layer: int = 0):
+    import torch
+    from ternary_weight_only_tern_amd import lib as L
+    from ternary_weight_only_tern_amd import synth
+    mat = synth.config_matrix(cfg, proj, layer)
+    nnz = [int(m.sum()) for m in mat["masks"]]
+    pm = L.PackedMatrix(mat["n"], mat["k"], mat["group"], mat["planes"], fmt, mat["offset_mode"], nnz)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    masks = dev(np.stack(mat["mask_bits"]).view(np.int32)) if mat["planes"] > 1 else None
+    off = dev(mat["offset"]) if mat["offset"] is not None else None
+    L.tern_pack(pm, dev(mat["trits"]), dev(mat["scales"]), masks, off)
+    return pm, mat
+
+
+def x_for(cfg, proj, m, layer=0):
+    import torch
+    from ternary_weight_only_tern_amd import synth
+    x = synth.config_x(cfg, m, proj, layer)
+    return torch.from_numpy(x.view(np.uint16)).cuda().view(torch.float16), x
+
+
+def time_graph(step_fns, steps, warmup, stream):
+    """Capture one call of every step function into a HIP graph, replay it so
+    that exactly `steps` steps run; returns (total seconds, per-step seconds
+    from events around each replayed step group)."""
+    import torch
+    per = len(step_fns)
+    assert steps % per == 0, "steps must be a multiple of the rotation length"
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        for f in step_fns:  # eager warm-up before capture
+            f()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for f in step_fns:
+                f()
+    torch.cuda.synchronize()
+    reps_w = max(1, warmup // per)
+    reps = steps // per
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    with torch.cuda.stream(stream):  # replay on the stream the events are recorded on
+        for _ in range(reps_w):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s, e in evs:
+            s.record(stream)
+            g.replay()
+            e.record(stream)
+        torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu = sum(s.elapsed_time(e) for s, e in evs) / 1e3
+    return wall, gpu, g
+
+
+def bench_layer4b(args, stream):
+    """Qwen3-4B-class layer, M=1, 36 distinct layer copies."""
+    import torch
+    from ternary_weight_only_tern_amd import lib as L
+    from ternary_weight_only_tern_amd import synth
+    fmt = 0 if args.fmt == "2bit" else 1
+    base, xs, ys, mats = [], [], [], []
+    for proj in range(len(synth.QWEN3_4B_LAYER)):
+        pm, mat = pack_config(2, fmt, proj)
+        base.append(pm)
+        mats.append(mat)
+        xd, _ = x_for(2, proj, 1)
+        xs.append(xd)
+        ys.append(torch.empty((1, pm.n), dtype=torch.float16, device="cuda"))
+    layer_bytes = sum(pm.nbytes() for pm in base)
+    layers = [base] + [[clone_packed(pm) for pm in base] for _ in range(LAYERS - 1)]
+    plans = [L.Plan(layer, xs, ys) for layer in layers]
+    torch.cuda.synchronize()
+    steps = max(LAYERS, (args.steps + LAYERS - 1) // LAYERS * LAYERS)
+    fns = [(lambda p=p: p.run(stream.cuda_stream)) for p in plans]
+    wall, gpu, _ = time_graph(fns, steps, args.warmup, stream)
+    step_s = gpu / steps
+    # one kernel launch per step: the average launch duration over the timed
+    # region is the step time
+    launch_s = step_s
+    return dict(layer_bytes=layer_bytes, steps=steps, wall_s=wall, gpu_s=gpu, step_s=step_s,
+                gbs=layer_bytes / step_s / 1e9, launch_s=launch_s, launch_gbs=layer_bytes / launch_s / 1e9,
+                mats=mats, base=base, xs=xs, weights=sum(pm.n * pm.k for pm in base))
+
+
+def bench_stack8b(args, stream):
+    """Qwen3-8B-class 36 x 7 stack, base-3, M=1: one grouped launch per token."""
+    import torch
+    from ternary_weight_only_tern_amd import lib as L
+    from ternary_weight_only_tern_amd import synth
+    base, xs = [], []
+    for proj in range(len(synth.QWEN3_8B_LAYER)):
+        pm, _ = pack_config(3, 1, proj)
+        base.append(pm)
+        xd, _ = x_for(3, proj, 1)
+        xs.append(xd)
+    mats, xl, yl = [], [], []
+    for layer in range(LAYERS):
+        for proj, pm in enumerate(base):
+            mats.append(pm if layer == 0 else clone_packed(pm))
+            xl.append(xs[proj])
+            yl.append(torch.empty((1, pm.n), dtype=torch.float16, device="cuda"))
+    stack_bytes = sum(pm.nbytes() for pm in mats)
+    plan = L.Plan(mats, xl, yl)
+    torch.cuda.synchronize()
+    steps = max(2, args.steps // 20)
+    wall, gpu, _ = time_graph([lambda: plan.run(stream.cuda_stream)], steps, max(2, args.warmup // 10), stream)
+    step_s = gpu / steps
+    return dict(stack_bytes=stack_bytes, steps=steps, step_s=step_s, gbs=stack_bytes / step_s / 1e9,
+                tok_s=1.0 / step_s)
+
+
+def bench_gemm512(args, stream):
+    """Qwen3-8B-class layer at M=512 through the MFMA product (base-3)."""
+    import torch
+    from ternary_weight_only_tern_amd import lib as L
+    from ternary_weight_only_tern_amd import synth
+    m = 512
+    items = []
+    for proj in range(len(synth.QWEN3_8B_LAYER)):
+        pm, _ = pack_config(4, 1, proj)
+        xd, _ = x_for(4, proj, m)
+        y = torch.empty((m, pm.n), dtype=torch.float16, device="cuda")
+        items.append((pm, xd, y))
+    flops = sum(2.0 * m * pm.n * pm.k for pm, _, _ in items)
+    fns = [(lambda pm=pm, xd=xd, y=y: L.tern_gemm(pm, xd, L.TERN_F16, out=y, stream=stream.cuda_stream))
+           for pm, xd, y in items]
+    step = lambda: [f() for f in fns]
+    steps = max(2, args.steps // 20)
+    wall, gpu, _ = time_graph([step], steps, 2, stream)
+    step_s = gpu / steps
+    return dict(flops=flops, steps=steps, step_s=step_s, tflops=flops / step_s / 1e12)
+
+
+def cpu_baseline(mats, fmt, budget_s=12.0):
+    """The oracle's unpack-and-dot on one thread, over whole layers of the
+    same workload until about budget_s seconds of CPU work."""
+    from threadpoolctl import threadpool_limits
+    import oracle as O
+    from ternary_weight_only_tern_amd import synth
+    packed = [O.pack(m["trits"], m["scales"], m["mask_bits"], m["offset"], m["group"], fmt) for m in mats]
+    xs = [synth.config_x(2, 1, p) for p in range(len(mats))]
+    nbytes = 0
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            for pk, x in zip(packed, xs):
+                O.gemv_packed(pk, x)
+                nbytes += O.bits(pk)["total_bytes"]
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return dict(value=nbytes / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
+                sample=f"{done} pass(es) over the 7 projections of one Qwen3-4B-class layer "
+                       f"({'2-bit' if fmt == 0 else 'base-3'}, M=1), fp64 unpack-and-dot, 1 thread, {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1080, help="timed steps (rounded up to a multiple of 36)")
+    ap.add_argument("--warmup", type=int, default=72)
+    ap.add_argument("--fmt", choices=["2bit", "b3"], default="2bit")
+    ap.add_argument("--skip-extra", action="store_true", help="only the headline measurement")
+    ap.add_argument("--skip-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the product shards by output rows with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from ternary_weight_only_tern_amd import lib as L
+    L.load()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+
+    log("bench: packing the 4B-class layer")
+    r = bench_layer4b(args, stream)
+    log(f"bench: layer {r['layer_bytes']} B, {r['step_s']*1e6:.2f} us/step, {r['gbs']:.1f} GB/s; "
+        f"single launch {r['launch_s']*1e6:.2f} us = {r['launch_gbs']:.1f} GB/s")
+    extra = {}
+    if not args.skip_extra:
+        log("bench: 8B-class stack")
+        s8 = bench_stack8b(args, stream)
+        extra["qwen3_8b_stack_m1_b3"] = dict(bytes=s8["stack_bytes"], us_per_token=s8["step_s"] * 1e6,
+                                             gbs=s8["gbs"], hbm_frac=s8["gbs"] / HBM_PEAK_GBS,
+                                             tokens_per_s_equiv=s8["tok_s"], steps=s8["steps"])
+        log(f"bench: stack {s8['gbs']:.1f} GB/s, {s8['tok_s']:.0f} tok/s-eq")
+        log("bench: M=512 MFMA layer")
+        g = bench_gemm512(args, stream)
+        extra["qwen3_8b_layer_m512_b3"] = dict(tflops=g["tflops"], mfma_frac=g["tflops"] / F16_MFMA_PEAK_TFS,
+                                               us_per_layer=g["step_s"] * 1e6, steps=g["steps"])
+        log(f"bench: M=512 {g['tflops']:.1f} TFLOP/s")
+    cpu = None
+    if not args.skip_cpu:
+        log("bench: cpu baseline (oracle)")
+        cpu = cpu_baseline(r["mats"], 0 if args.fmt == "2bit" else 1)
+        log(f"bench: cpu {cpu['value']:.4f} GB/s")
+
+    out = {
+        "metric": "ternary GEMV packed-weight GB/s (% HBM peak) at M=1; TFLOP/s at M=512",
+        "value": round(r["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": r["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": r["step_s"] * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 x, 2-bit trits" if args.fmt == "2bit" else "fp16 x, base-3 trits",
+        "data": "synthetic (seeded; Qwen3-4B-class shapes, random trits/scales/masks)",
+        "config": {"workload": "qwen3-4b-class decoder layer, M=1, 7 projections in one grouped launch, "
+                               "36 distinct layer copies rotated",
+                   "format": args.fmt, "group": 128, "residual_frac": 0.10, "layer_bytes": r["layer_bytes"],
+                   "weights_per_step": r["weights"]},
+        "roofline": {"bound": "hbm", "achieved": round(r["launch_gbs"], 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(r["launch_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemv_kernel (2-bit, G=128, MT=1): one grouped launch per layer",
+                     "launch_us": round(r["launch_s"] * 1e6, 3),
+                     "bytes_per_launch": r["layer_bytes"]},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -122,7 +122,10 @@ tern_status tern_packed_sizes(int32_t n, int32_t k, int32_t group, int32_t forma
                               size_t out_bytes[TERN_NBUF]);
 
 /* Device workspace needed by tern_pack / tern_unpack / tern_gemv / tern_gemm
- * on this matrix with m activation rows (the maximum over the four). */
+ * on this matrix with m activation rows (the maximum over the four).  A
+ * decode product that is split along K keeps FP32 partials there and sums
+ * them in split order with a second kernel.  Calls that overlap in time must
+ * not share a workspace. */
 size_t tern_workspace_bytes(const tern_matrix *w, int32_t m);
 
 /* Pack trit planes (lossless serialisation: 2609.01962 §9.1, §15).
@@ -171,7 +174,8 @@ tern_status tern_gemv_batched(const tern_matrix *w, const uint16_t *const *x, vo
                               size_t ws_bytes, void *stream);
 
 /* A prepared grouped decode.  tern_plan_create copies the descriptor table
- * into the caller's device buffer `ws` (synchronously) and returns a host
+ * into the caller's device buffer `ws` of tern_batch_workspace_bytes bytes
+ * (synchronously) and returns a host
  * handle (malloc'ed; free it with tern_plan_destroy).  tern_plan_run
  * launches the whole batch on stream; it may be called any number of times
  * and captured in a HIP graph.  The buffers named in the plan must stay

@@ -3,12 +3,11 @@
 // 1.58 bits per weight", How It Works: matrix products become additions and
 // subtractions; arXiv 2609.09240: the packed weights are consumed directly).
 //
-// Work item = 64 output rows x one K split; one wavefront per work item, one
-// row per lane.  Packed rows are staged through LDS with coalesced 16-byte
+// One row per lane: a wavefront covers 64 output rows.  Packed rows are staged through LDS with coalesced 16-byte
 // loads (8 or 13 lanes cover 128 or 208 contiguous bytes of a row), then each
 // lane decodes its own row.  All lanes sit at the same K position, so the
-// activations are wave-uniform and live in SGPRs (scalar loads), which leaves
-// the VALU for decode and multiply-accumulate only.
+// activations are wave-uniform and are read with scalar loads into SGPRs,
+// which leaves the VALU for decode and multiply-accumulate only.
 //
 // Decode.  A 2-bit word holds 16 trits, even offsets in the low half-word and
 // odd offsets in the high half-word, each as a 2-bit two's-complement code.
@@ -21,12 +20,25 @@
 // Per group the FP32 partial is scaled by 0.5*s (exact) and added to the row
 // accumulator.  Residual planes are walked per lane over the row's compact
 // blocks (divergent loop), and offsets add off * sum(x) per group.
+//
+// Work item = 64 rows x one K split, run by a workgroup of 4 wavefronts that
+// split the item's groups between them; their FP32 accumulators are summed
+// in wave order through LDS (deterministic, no global memory fences: on this
+// multi-XCD part a device-scope fence writes back and invalidates the L2).
+// When a row block is additionally split along K across workgroups, each
+// split writes FP32 partials and a second kernel sums them in split order.
 #include "internal.h"
+
+#define GLOBAL __attribute__((address_space(1)))
 
 namespace tern {
 namespace {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ const GLOBAL T* gp(const T* p) { return (const GLOBAL T*)p; }
 
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, w), __builtin_bit_cast(h2_t, x), c, false);
@@ -52,6 +64,9 @@ struct Geo {
   static constexpr int CPR = SGB / 16;                          // 16-byte chunks per row
   static constexpr int PITCH = FMT == 0 ? 144 : 208;            // LDS row pitch (bytes)
   static constexpr int CHUNKS = kGemvRows * CPR / kWave;        // chunks per lane per stage
+  static constexpr int XDW = SG * G / 2;                        // activation dwords per stage per row of x
+  static constexpr int XCH = XDW / 4 / kWave;                   // 16-byte x chunks per lane per stage
+  static constexpr int WBYTES = kGemvRows * PITCH;              // weight part of the LDS stage
   static_assert(SG * GB == SGB, "stage must hold whole groups");
   static_assert((PITCH / 16) % 2 == 1, "odd 16-byte pitch keeps b128 reads conflict-free");
 };
@@ -59,8 +74,8 @@ struct Geo {
 // Base-3 byte -> 2-bit codes.  For a byte pair (A, B) holding trits t0..t4 and
 // t5..t9, pair i = (t[2i], t[2i+1]) must sit at bits 6+2i (low) and 22+2i
 // (high) of lutA[A] | lutB[B]; then pair i decodes with shift 8-2i.
-__device__ void build_b3_luts(uint32_t* lutA, uint32_t* lutB) {
-  for (int v = threadIdx.x; v < 256; v += kWave) {
+__device__ void build_b3_entry(int v, uint32_t* lutA, uint32_t* lutB) {
+  {
     uint32_t a = 0, b = 0;
     if (v < 243) {
       int r = v;
@@ -79,7 +94,7 @@ __device__ void build_b3_luts(uint32_t* lutA, uint32_t* lutB) {
   }
 }
 
-__device__ __forceinline__ int find_desc(const GemvDesc* descs, int ndesc, int item) {
+__device__ __forceinline__ int find_desc(const GemvDesc* __restrict__ descs, int ndesc, int item) {
   int lo = 0, hi = ndesc - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -88,108 +103,189 @@ __device__ __forceinline__ int find_desc(const GemvDesc* descs, int ndesc, int i
   return lo;
 }
 
-// Multiply-accumulate the 2-bit word w (16 trits starting at activation
-// dword xd) against MT activation rows.
-template <int MT>
-__device__ __forceinline__ void mac_word(uint32_t w, const uint32_t* const (&xr)[MT], int xd,
-                                         float (&acc)[MT]) {
+// Residual blocks of this lane's row in groups [g0, g1) of plane p.
+template <int G, int MT>
+__device__ __forceinline__ void residual_plane(const GemvDesc& d, int p, int row, int g0, int g1,
+                                               const GLOBAL uint32_t* const (&xr)[MT],
+                                               float (&acc)[MT]) {
+  const GLOBAL uint32_t* rm = gp(d.mask[p]) + (size_t)row * d.mwords;
+  uint32_t b = gp(d.rowptr[p])[row];
+  for (int w = 0; w < (g0 >> 5); ++w) b += __popc(rm[w]);
+  if (g0 & 31) b += __popc(rm[g0 >> 5] & ((1u << (g0 & 31)) - 1u));
+  const GLOBAL uint8_t* blocks = gp(d.blocks[p]);
+  const GLOBAL uint16_t* rscale = gp(d.rscale[p]);
+  for (int w = g0 >> 5; w <= ((g1 - 1) >> 5); ++w) {
+    uint32_t bits = rm[w];
+    const int lo = max(g0 - (w << 5), 0), hi = min(g1 - (w << 5), 32);
+    bits &= (lo > 0 ? ~((1u << lo) - 1u) : ~0u) & (hi < 32 ? ((1u << hi) - 1u) : ~0u);
+    while (bits) {
+      const int g = (w << 5) + __builtin_ctz(bits);
+      bits &= bits - 1u;
+      const GLOBAL u4_t* blk = reinterpret_cast<const GLOBAL u4_t*>(blocks + (size_t)b * (G / 4));
+      float part[MT];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t p = pair_of(w, 14 - 2 * i);
+      for (int m = 0; m < MT; ++m) part[m] = 0.f;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = dot2(p, xr[m][xd + i], acc[m]);
+      for (int q = 0; q < G / 64; ++q) {
+        const u4_t v = blk[q];
+        const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int xd = g * (G / 2) + q * 32 + u * 8;
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const GLOBAL u4_t* xv = reinterpret_cast<const GLOBAL u4_t*>(xr[m] + xd);
+            const u4_t x0 = xv[0], x1 = xv[1];
+            const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) part[m] = dot2(pair_of(ws[u], 14 - 2 * i), xs[i], part[m]);
+          }
+        }
+      }
+      const float rs = 0.5f * h2f(rscale[b]);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[m] = fmaf(rs, part[m], acc[m]);
+      ++b;
+    }
   }
 }
 
+constexpr int kWaves = 4;  // wavefronts per workgroup, splitting K
+
+__device__ __forceinline__ void wave_sync() {
+  // LDS traffic of one wavefront is processed in order; this keeps the
+  // compiler from moving LDS accesses across the hand-off point.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int FMT, int G, int MT>
-__global__ __launch_bounds__(kWave) void gemv_kernel(const GemvDesc* __restrict__ descs, int ndesc,
-                                                     GemvDesc one) {
+__global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __restrict__ descs,
+                                                              int ndesc, GemvDesc one) {
   using Gm = Geo<FMT, G>;
-  extern __shared__ uint4 stage[];  // [64 rows][PITCH bytes]
+  extern __shared__ uint4 stage_all[];  // per wave: [64 rows][PITCH] + activations of a stage
   __shared__ uint32_t lutA[FMT == 1 ? 256 : 1];
   __shared__ uint32_t lutB[FMT == 1 ? 256 : 1];
 
   const int item_g = blockIdx.x;
-  const GemvDesc& d = ndesc ? descs[find_desc(descs, ndesc, item_g)] : one;
+  GemvDesc d;
+  if (ndesc > 0) d = descs[find_desc(descs, ndesc, item_g)];
+  else d = one;
   const int item = item_g - d.tile_begin;
   const int rb = item % d.row_blocks;
   const int split = item / d.row_blocks;
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
   const int row = rb * kGemvRows + lane;
   const bool row_ok = row < d.n;
-  const int g0 = split * d.gps;
-  const int g1 = min(d.ng, g0 + d.gps);
+  // this wave's share of the item's groups, on stage boundaries
+  const int ga = split * d.gps;
+  const int gb = min(d.ng, ga + d.gps);
+  const int q = ((gb - ga + kWaves - 1) / kWaves + Gm::SG - 1) / Gm::SG * Gm::SG;
+  const int g0 = min(gb, ga + wave * q);
+  const int g1 = min(gb, g0 + q);
   const int nstages = (g1 - g0 + Gm::SG - 1) / Gm::SG;
 
   if (FMT == 1) {
-    build_b3_luts(lutA, lutB);
+    for (int v = threadIdx.x; v < 256; v += kWave * kWaves) build_b3_entry(v, lutA, lutB);
+    __syncthreads();
   }
 
-  const uint32_t* xr[MT];
+  const GLOBAL uint32_t* xr[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
-    xr[m] = reinterpret_cast<const uint32_t*>(d.x + (size_t)min(m, d.m - 1) * d.k);
+    xr[m] = reinterpret_cast<const GLOBAL uint32_t*>(gp(d.x) + (size_t)min(m, d.m - 1) * d.k);
 
   float acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0.f;
 
-  const uint8_t* prow0 = d.plane0 + (size_t)rb * kGemvRows * d.stride;
+  const GLOBAL uint8_t* prow0 = gp(d.plane0) + (size_t)rb * kGemvRows * d.stride;
+  const GLOBAL uint16_t* srow = gp(d.scale0) + (size_t)(row_ok ? row : 0) * d.ng;
   const int rows_here = min(kGemvRows, d.n - rb * kGemvRows);
-  uint8_t* lds = reinterpret_cast<uint8_t*>(stage);
+  uint8_t* lds = reinterpret_cast<uint8_t*>(stage_all) + (size_t)wave * (Gm::WBYTES + MT * Gm::XDW * 4);
 
-  uint4 pre[Gm::CHUNKS];
+  // prefetch registers for the next stage: packed rows, scales, activations
+  u4_t pre[Gm::CHUNKS];
   uint16_t spre[Gm::SG];
-  auto load_stage = [&](int s) {
-    const int gs = g0 + s * Gm::SG;
-    const int bytes = min(Gm::SG, g1 - gs) * Gm::GB;
-    const uint8_t* base = prow0 + (size_t)gs * Gm::GB;
+  u4_t xpre[MT][Gm::XCH];
+  const GLOBAL u4_t* xq[MT];
 #pragma unroll
-    for (int i = 0; i < Gm::CHUNKS; ++i) {
-      const int c = i * kWave + lane;
-      const int r = c / Gm::CPR, col = c % Gm::CPR;
-      if (r < rows_here && col * 16 < bytes)
-        pre[i] = *reinterpret_cast<const uint4*>(base + (size_t)r * d.stride + col * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < Gm::SG; ++j)
-      spre[j] = (row_ok && gs + j < g1) ? d.scale0[(size_t)row * d.ng + gs + j] : (uint16_t)0;
-  };
+  for (int m = 0; m < MT; ++m) xq[m] = reinterpret_cast<const GLOBAL u4_t*>(xr[m]);
+#define TERN_LOAD_STAGE(s_)                                                                 \
+  do {                                                                                      \
+    const int gs_ = g0 + (s_) * Gm::SG;                                                     \
+    const int bytes_ = min(Gm::SG, g1 - gs_) * Gm::GB;                                      \
+    const GLOBAL uint8_t* base_ = prow0 + (size_t)gs_ * Gm::GB;                             \
+    _Pragma("unroll") for (int i = 0; i < Gm::CHUNKS; ++i) {                                \
+      const int c = i * kWave + lane;                                                       \
+      const int r = c / Gm::CPR, col = c % Gm::CPR;                                         \
+      if (r < rows_here && col * 16 < bytes_)                                               \
+        pre[i] = *reinterpret_cast<const GLOBAL u4_t*>(base_ + (size_t)r * d.stride + col * 16); \
+    }                                                                                       \
+    _Pragma("unroll") for (int j = 0; j < Gm::SG; ++j)                                      \
+      spre[j] = (row_ok && gs_ + j < g1) ? srow[gs_ + j] : (uint16_t)0;                     \
+    _Pragma("unroll") for (int m = 0; m < MT; ++m)                                          \
+      _Pragma("unroll") for (int i = 0; i < Gm::XCH; ++i) {                                 \
+        const int xc_ = gs_ * (G / 8) + i * kWave + lane;                                   \
+        if (xc_ < g1 * (G / 8)) xpre[m][i] = xq[m][xc_];                                    \
+      }                                                                                     \
+  } while (0)
 
-  if (nstages > 0) load_stage(0);
+  if (nstages > 0) TERN_LOAD_STAGE(0);
   for (int s = 0; s < nstages; ++s) {
     const int gs = g0 + s * Gm::SG;
     const int ngs = min(Gm::SG, g1 - gs);
-    __syncthreads();  // previous stage fully consumed (and LUTs built)
+    wave_sync();  // previous stage consumed
 #pragma unroll
     for (int i = 0; i < Gm::CHUNKS; ++i) {
       const int c = i * kWave + lane;
       const int r = c / Gm::CPR, col = c % Gm::CPR;
-      *reinterpret_cast<uint4*>(lds + r * Gm::PITCH + col * 16) = pre[i];
+      *reinterpret_cast<u4_t*>(lds + r * Gm::PITCH + col * 16) = pre[i];
     }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < Gm::XCH; ++i)
+        *reinterpret_cast<u4_t*>(lds + Gm::WBYTES + (m * Gm::XDW + (i * kWave + lane) * 4) * 4) = xpre[m][i];
     float sc[Gm::SG];
 #pragma unroll
     for (int j = 0; j < Gm::SG; ++j) sc[j] = 0.5f * h2f(spre[j]);
-    __syncthreads();
-    if (s + 1 < nstages) load_stage(s + 1);
+    wave_sync();
+    if (s + 1 < nstages) TERN_LOAD_STAGE(s + 1);
 
     const uint8_t* my = lds + lane * Gm::PITCH;
+    // wave-uniform activation chunks of this stage (broadcast LDS reads)
+    const u4_t* xs4 = reinterpret_cast<const u4_t*>(lds + Gm::WBYTES);
 #pragma unroll
     for (int j = 0; j < Gm::SG; ++j) {
       if (j < ngs) {
         const int g = gs + j;
-        const int xg = g * (G / 2);  // activation dword index of the group start
         float part[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) part[m] = 0.f;
         if (FMT == 0) {
 #pragma unroll
           for (int q = 0; q < G / 64; ++q) {
-            const uint4 v = *reinterpret_cast<const uint4*>(my + j * Gm::GB + q * 16);
-            mac_word<MT>(v.x, xr, xg + q * 32 + 0, part);
-            mac_word<MT>(v.y, xr, xg + q * 32 + 8, part);
-            mac_word<MT>(v.z, xr, xg + q * 32 + 16, part);
-            mac_word<MT>(v.w, xr, xg + q * 32 + 24, part);
+            const u4_t v = *reinterpret_cast<const u4_t*>(my + j * Gm::GB + q * 16);
+            const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              u4_t xa[MT], xb[MT];
+#pragma unroll
+              for (int m = 0; m < MT; ++m) {
+                const int c = (m * Gm::XDW + j * (G / 2) + q * 32 + u * 8) / 4;
+                xa[m] = xs4[c];
+                xb[m] = xs4[c + 1];
+              }
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                const uint32_t p = pair_of(ws[u], 14 - 2 * i);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) part[m] = dot2(p, i < 4 ? xa[m][i] : xb[m][i - 4], part[m]);
+              }
+            }
           }
         } else {
           constexpr int GB = Gm::GB;
@@ -199,15 +295,23 @@ __global__ __launch_bounds__(kWave) void gemv_kernel(const GemvDesc* __restrict_
 #pragma unroll
           for (int q = 0; q < 3; ++q) {
             if (((off + GB - 1) >> 4) >= c0 + q) {
-              const uint4 v = *reinterpret_cast<const uint4*>(my + (c0 + q) * 16);
+              const u4_t v = *reinterpret_cast<const u4_t*>(my + (c0 + q) * 16);
               dw[4 * q + 0] = v.x; dw[4 * q + 1] = v.y; dw[4 * q + 2] = v.z; dw[4 * q + 3] = v.w;
             } else {
               dw[4 * q + 0] = dw[4 * q + 1] = dw[4 * q + 2] = dw[4 * q + 3] = 0u;
             }
           }
           const int sh = off - c0 * 16;
+          u4_t xc[MT][5];
 #pragma unroll
           for (int bp = 0; bp < (GB + 1) / 2; ++bp) {
+            if (bp % 4 == 0) {  // activation pairs 5*bp .. 5*bp+19 of the group
+#pragma unroll
+              for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int c = 0; c < 5; ++c)
+                  if (4 * (5 * bp / 4 + c) < G / 2) xc[m][c] = xs4[(m * Gm::XDW + j * (G / 2)) / 4 + 5 * bp / 4 + c];
+            }
             const int ia = sh + 2 * bp, ib = ia + 1;
             const uint32_t ba = (dw[ia >> 2] >> ((ia & 3) * 8)) & 0xFFu;
             uint32_t code = lutA[ba];
@@ -219,8 +323,9 @@ __global__ __launch_bounds__(kWave) void gemv_kernel(const GemvDesc* __restrict_
             for (int i = 0; i < 5; ++i) {
               if (10 * bp + 2 * i < G) {
                 const uint32_t p = pair_of(code, 8 - 2 * i);
+                const int xi = 5 * bp + i - 4 * (5 * (bp / 4 * 4) / 4);  // index within the 5 chunks
 #pragma unroll
-                for (int m = 0; m < MT; ++m) part[m] = dot2(p, xr[m][xg + 5 * bp + i], part[m]);
+                for (int m = 0; m < MT; ++m) part[m] = dot2(p, xc[m][xi / 4][xi % 4], part[m]);
               }
             }
           }
@@ -230,51 +335,17 @@ __global__ __launch_bounds__(kWave) void gemv_kernel(const GemvDesc* __restrict_
       }
     }
   }
+#undef TERN_LOAD_STAGE
 
   // ---- residual planes: each lane walks its row's compact blocks in [g0, g1)
-  if (d.planes > 1 && row_ok) {
-    for (int p = 0; p < d.planes - 1; ++p) {
-      const uint32_t* rm = d.mask[p] + (size_t)row * d.mwords;
-      uint32_t b = d.rowptr[p][row];
-      for (int w = 0; w < (g0 >> 5); ++w) b += __popc(rm[w]);
-      if (g0 & 31) b += __popc(rm[g0 >> 5] & ((1u << (g0 & 31)) - 1u));
-      for (int w = g0 >> 5; w <= ((g1 - 1) >> 5) && g1 > g0; ++w) {
-        uint32_t bits = rm[w];
-        const int lo = max(g0 - (w << 5), 0), hi = min(g1 - (w << 5), 32);
-        bits &= (lo > 0 ? ~((1u << lo) - 1u) : ~0u) & (hi < 32 ? ((1u << hi) - 1u) : ~0u);
-        while (bits) {
-          const int g = (w << 5) + __builtin_ctz(bits);
-          bits &= bits - 1u;
-          const uint4* blk = reinterpret_cast<const uint4*>(d.blocks[p] + (size_t)b * (G / 4));
-          float part[MT];
-#pragma unroll
-          for (int m = 0; m < MT; ++m) part[m] = 0.f;
-#pragma unroll
-          for (int q = 0; q < G / 64; ++q) {
-            const uint4 v = blk[q];
-            const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const int xd = g * (G / 2) + q * 32 + u * 8;
-#pragma unroll
-              for (int i = 0; i < 8; ++i) {
-                const uint32_t pr = pair_of(ws[u], 14 - 2 * i);
-#pragma unroll
-                for (int m = 0; m < MT; ++m) part[m] = dot2(pr, xr[m][xd + i], part[m]);
-              }
-            }
-          }
-          const float rs = 0.5f * h2f(d.rscale[p][b]);
-#pragma unroll
-          for (int m = 0; m < MT; ++m) acc[m] = fmaf(rs, part[m], acc[m]);
-          ++b;
-        }
-      }
-    }
+  if (row_ok && g1 > g0) {
+    if (d.planes > 1) residual_plane<G, MT>(d, 0, row, g0, g1, xr, acc);
+    if (d.planes > 2) residual_plane<G, MT>(d, 1, row, g0, g1, xr, acc);
   }
 
   // ---- offsets: off(n,g) * sum of the group's activations
   if (d.offset_mode != 0) {
+    const GLOBAL uint16_t* off = gp(d.offset);
     for (int g = g0; g < g1; ++g) {
       float xs[MT];
 #pragma unroll
@@ -284,24 +355,36 @@ __global__ __launch_bounds__(kWave) void gemv_kernel(const GemvDesc* __restrict_
         xs[m] = wave_sum(v);
       }
       if (row_ok) {
-        const float o = h2f(d.offset_mode == 1 ? d.offset[row] : d.offset[(size_t)row * d.ng + g]);
+        const float o = h2f(d.offset_mode == 1 ? off[row] : off[(size_t)row * d.ng + g]);
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[m] = fmaf(o, xs[m], acc[m]);
       }
     }
   }
 
-  if (!row_ok) return;
+  // ---- combine the wavefronts' accumulators in wave order
+  __syncthreads();  // every wave is done with its stage buffers
+  float* red = reinterpret_cast<float*>(stage_all);
+#pragma unroll
+  for (int m = 0; m < MT; ++m) red[(wave * MT + m) * kWave + lane] = acc[m];
+  __syncthreads();
+  if (wave != 0 || !row_ok) return;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    float v = red[m * kWave + lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) v += red[(w * MT + m) * kWave + lane];
+    acc[m] = v;
+  }
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     if (m < d.m) {
-      if (d.splits > 1) {
+      if (d.splits > 1)
         d.partial[((size_t)split * d.m + m) * d.n + row] = acc[m];
-      } else if (d.y_f32) {
+      else if (d.y_f32)
         reinterpret_cast<float*>(d.y)[(size_t)m * d.n + row] = acc[m];
-      } else {
+      else
         reinterpret_cast<_Float16*>(d.y)[(size_t)m * d.n + row] = (_Float16)acc[m];
-      }
     }
   }
 }
@@ -311,23 +394,22 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ partial, int spli
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t total = (size_t)m * n;
   if (i >= total) return;
-  float s = 0.f;
-  for (int p = 0; p < splits; ++p) s += partial[(size_t)p * total + i];
-  if (y_f32)
-    reinterpret_cast<float*>(y)[i] = s;
-  else
-    reinterpret_cast<_Float16*>(y)[i] = (_Float16)s;
+  float v = 0.f;
+  for (int s = 0; s < splits; ++s) v += partial[(size_t)s * total + i];
+  if (y_f32) reinterpret_cast<float*>(y)[i] = v;
+  else reinterpret_cast<_Float16*>(y)[i] = (_Float16)v;
 }
 
 template <int FMT, int G>
 hipError_t launch_fmt_g(int mt, const GemvDesc* descs, int ndesc, const GemvDesc& one, int items,
                         hipStream_t s) {
-  const size_t lds = (size_t)kGemvRows * Geo<FMT, G>::PITCH;
+  const size_t lds = (size_t)kWaves * (Geo<FMT, G>::WBYTES + (size_t)mt * Geo<FMT, G>::XDW * 4);
+  const dim3 block(kWave * kWaves);
   switch (mt) {
-    case 1: hipLaunchKernelGGL((gemv_kernel<FMT, G, 1>), dim3(items), dim3(kWave), lds, s, descs, ndesc, one); break;
-    case 2: hipLaunchKernelGGL((gemv_kernel<FMT, G, 2>), dim3(items), dim3(kWave), lds, s, descs, ndesc, one); break;
-    case 4: hipLaunchKernelGGL((gemv_kernel<FMT, G, 4>), dim3(items), dim3(kWave), lds, s, descs, ndesc, one); break;
-    case 8: hipLaunchKernelGGL((gemv_kernel<FMT, G, 8>), dim3(items), dim3(kWave), lds, s, descs, ndesc, one); break;
+    case 1: hipLaunchKernelGGL((gemv_kernel<FMT, G, 1>), dim3(items), block, lds, s, descs, ndesc, one); break;
+    case 2: hipLaunchKernelGGL((gemv_kernel<FMT, G, 2>), dim3(items), block, lds, s, descs, ndesc, one); break;
+    case 4: hipLaunchKernelGGL((gemv_kernel<FMT, G, 4>), dim3(items), block, lds, s, descs, ndesc, one); break;
+    case 8: hipLaunchKernelGGL((gemv_kernel<FMT, G, 8>), dim3(items), block, lds, s, descs, ndesc, one); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -335,21 +417,10 @@ hipError_t launch_fmt_g(int mt, const GemvDesc* descs, int ndesc, const GemvDesc
 
 }  // namespace
 
-int gemv_stage_bytes(int format, int group) {
+int gemv_stage_groups(int format, int group) {
   // groups per stage; split boundaries must be multiples of this
   if (format == 0) return group == 64 ? Geo<0, 64>::SG : Geo<0, 128>::SG;
   return group == 64 ? Geo<1, 64>::SG : Geo<1, 128>::SG;
-}
-
-hipError_t launch_gemv(int format, int group, int mt, const GemvDesc* descs, int ndesc,
-                       const GemvDesc& one, int total_items, int /*max_stage_bytes*/,
-                       hipStream_t s) {
-  if (total_items <= 0) return hipSuccess;
-  if (format == 0 && group == 64) return launch_fmt_g<0, 64>(mt, descs, ndesc, one, total_items, s);
-  if (format == 0 && group == 128) return launch_fmt_g<0, 128>(mt, descs, ndesc, one, total_items, s);
-  if (format == 1 && group == 64) return launch_fmt_g<1, 64>(mt, descs, ndesc, one, total_items, s);
-  if (format == 1 && group == 128) return launch_fmt_g<1, 128>(mt, descs, ndesc, one, total_items, s);
-  return hipErrorInvalidValue;
 }
 
 hipError_t launch_splitk_reduce(const float* partial, int splits, int m, int n, void* y, int y_f32,
@@ -359,6 +430,16 @@ hipError_t launch_splitk_reduce(const float* partial, int splits, int m, int n, 
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                      partial, splits, m, n, y, y_f32);
   return hipGetLastError();
+}
+
+hipError_t launch_gemv(int format, int group, int mt, const GemvDesc* descs, int ndesc,
+                       const GemvDesc& one, int total_items, hipStream_t s) {
+  if (total_items <= 0) return hipSuccess;
+  if (format == 0 && group == 64) return launch_fmt_g<0, 64>(mt, descs, ndesc, one, total_items, s);
+  if (format == 0 && group == 128) return launch_fmt_g<0, 128>(mt, descs, ndesc, one, total_items, s);
+  if (format == 1 && group == 64) return launch_fmt_g<1, 64>(mt, descs, ndesc, one, total_items, s);
+  if (format == 1 && group == 128) return launch_fmt_g<1, 128>(mt, descs, ndesc, one, total_items, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tern

@@ -39,15 +39,15 @@ struct GemvDesc {
 // ---- decode products (gemv.hip)
 // Launches the lane-per-row decode kernel over `ndesc` descriptors stored in
 // device memory (`descs`), or over the single descriptor `one` when ndesc == 0.
-// total_items = sum over descriptors of splits * row_blocks.
+// total_items = sum over descriptors of splits * row_blocks.  Descriptors
+// with splits > 1 write FP32 partials; launch_splitk_reduce then sums them.
 hipError_t launch_gemv(int format, int group, int mt, const GemvDesc* descs, int ndesc,
-                       const GemvDesc& one, int total_items, int max_stage_bytes,
-                       hipStream_t stream);
+                       const GemvDesc& one, int total_items, hipStream_t stream);
 // y[m][n] = sum_s partial[s][m][n] in split order.
 hipError_t launch_splitk_reduce(const float* partial, int splits, int m, int n, void* y,
                                 int y_f32, hipStream_t stream);
-// Bytes of dynamic LDS the decode kernel uses for a given format / group.
-int gemv_stage_bytes(int format, int group);
+// Groups per LDS stage of the decode kernel; K splits start on multiples of it.
+int gemv_stage_groups(int format, int group);
 
 // ---- MFMA product (gemm.hip)
 hipError_t launch_gemm(const GemvDesc& d, int format, hipStream_t stream);

@@ -48,7 +48,7 @@ inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 constexpr size_t kFlagBytes = 256;
-constexpr int kTargetItems = 2048;  // decode work items that keep 256 CUs busy
+constexpr int kTargetItems = 512;   // decode workgroups (4 wavefronts each) that keep 256 CUs busy
 
 tern_status check_shape(int32_t n, int32_t k, int32_t group, int32_t planes, int32_t format,
                         int32_t offset_mode) {
@@ -92,19 +92,30 @@ tern_status check_matrix(const tern_matrix* w) {
   return TERN_OK;
 }
 
-// Split of K for a single decode product: enough work items to fill the GPU,
-// split boundaries on stage multiples.
-void choose_splits(const tern_matrix* w, int* splits, int* gps) {
+// Split of K into `want` parts (at most one per LDS stage of groups); split
+// boundaries fall on stage multiples.
+void split_k(const tern_matrix* w, int want, int* splits, int* gps) {
   const int ng = w->k / w->group;
-  const int sg = tern::gemv_stage_bytes(w->format, w->group);
-  const int rb = (w->n + tern::kGemvRows - 1) / tern::kGemvRows;
+  const int sg = tern::gemv_stage_groups(w->format, w->group);
   const int max_splits = std::max(1, (ng + sg - 1) / sg);
-  int s = std::min(max_splits, std::max(1, (kTargetItems + rb - 1) / std::max(rb, 1)));
+  const int s = std::min(max_splits, std::max(1, want));
   int g = (ng + s - 1) / s;
   g = (g + sg - 1) / sg * sg;
   g = std::max(g, sg);
   *gps = g;
   *splits = std::max(1, (ng + g - 1) / g);
+}
+
+// Single decode product: enough work items (row blocks x splits) to fill the GPU.
+void choose_splits(const tern_matrix* w, int* splits, int* gps) {
+  const int rb = std::max(1, (w->n + tern::kGemvRows - 1) / tern::kGemvRows);
+  split_k(w, (kTargetItems + rb - 1) / rb, splits, gps);
+}
+
+// Workspace of one split product: FP32 partials [splits][m][n].
+size_t split_ws_bytes(int splits, int m, int n) {
+  if (splits <= 1) return 0;
+  return round_up((size_t)splits * m * n * sizeof(float), 256);
 }
 
 bool product_group_ok(int group) { return group == 64 || group == 128; }
@@ -144,8 +155,7 @@ size_t gemv_ws_bytes(const tern_matrix* w, int m) {
   if (m <= 0 || w->n <= 0 || w->k <= 0 || !product_group_ok(w->group)) return 0;
   int splits, gps;
   choose_splits(w, &splits, &gps);
-  if (splits <= 1) return 0;
-  return round_up((size_t)splits * std::min(m, tern::kMaxMT) * w->n * sizeof(float), 256);
+  return split_ws_bytes(splits, std::min(m, tern::kMaxMT), w->n);
 }
 
 tern_status flag_status(uint32_t flag, bool unpacking) {
@@ -323,10 +333,10 @@ tern_status tern_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* 
     dc.m = mc;
     dc.splits = splits;
     dc.gps = gps;
-    dc.partial = splits > 1 ? static_cast<float*>(ws) : nullptr;
+    if (splits > 1) dc.partial = static_cast<float*>(ws);
     dc.tile_begin = 0;
     const int items = splits * dc.row_blocks;
-    TERN_HIP(tern::launch_gemv(w->format, w->group, pick_mt(mc), nullptr, 0, dc, items, 0, s));
+    TERN_HIP(tern::launch_gemv(w->format, w->group, pick_mt(mc), nullptr, 0, dc, items, s));
     if (splits > 1) TERN_HIP(tern::launch_splitk_reduce(dc.partial, splits, mc, w->n, dc.y, y_f32, s));
   }
   return TERN_OK;
@@ -348,6 +358,9 @@ tern_status tern_gemm(const tern_matrix* w, const uint16_t* x, int32_t m, void* 
 }
 
 // ---- grouped decode
+// Descriptors of a batch: one per (matrix, block of <= 8 activation rows),
+// longest K first; every descriptor covers its whole K (the four wavefronts
+// of a workgroup split it).  `ws` holds the descriptor table.
 static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y,
                                int32_t count, int32_t m, int32_t y_dtype,
                                std::vector<GemvDesc>* out, int* total, int* mt) {
@@ -370,7 +383,6 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
     TERN_TRY(check_xy(x[i], y[i], y_dtype));
     order.push_back(i);
   }
-  // longest work items first
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return w[a].k > w[b].k; });
   const size_t esz = y_dtype == TERN_F32 ? 4 : 2;
   for (int i : order) {
@@ -388,8 +400,8 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
 
 size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m) {
   (void)w;
-  if (count <= 0) return 0;
-  const int chunks = std::max(1, (m + tern::kMaxMT - 1) / tern::kMaxMT);
+  if (count <= 0 || m <= 0) return 0;
+  const size_t chunks = (size_t)(m + tern::kMaxMT - 1) / tern::kMaxMT;
   return round_up((size_t)count * chunks * sizeof(GemvDesc), 256);
 }
 
@@ -406,7 +418,7 @@ tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, vo
   hipStream_t s = (hipStream_t)stream;
   TERN_HIP(hipMemcpyAsync(ws, descs.data(), need, hipMemcpyHostToDevice, s));
   TERN_HIP(tern::launch_gemv(w[0].format, w[0].group, mt, static_cast<const GemvDesc*>(ws),
-                             (int)descs.size(), descs[0], total, 0, s));
+                             (int)descs.size(), descs[0], total, s));
   return TERN_OK;
 }
 
@@ -442,7 +454,7 @@ tern_status tern_plan_run(const tern_plan* plan, void* stream) {
   GemvDesc dummy;
   std::memset(&dummy, 0, sizeof(dummy));
   TERN_HIP(tern::launch_gemv(plan->format, plan->group, plan->mt, plan->dev, plan->ndesc, dummy,
-                             plan->total_items, 0, (hipStream_t)stream));
+                             plan->total_items, (hipStream_t)stream));
   return TERN_OK;
 }
 

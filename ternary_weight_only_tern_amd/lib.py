@@ -175,7 +175,7 @@ class PackedMatrix:
 def _workspace(desc: tern_matrix, m: int, device="cuda"):
     import torch
     nbytes = load().tern_workspace_bytes(ctypes.byref(desc), m)
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 def tern_pack(pm: PackedMatrix, trits, scales, mask_bits, offset=None, stream=None, ws=None):
@@ -238,7 +238,7 @@ def tern_gemv_batched(mats, xs, ys, y_dtype=TERN_F16, stream=None, ws=None):
     descs, xp, yp = _arrays(mats, xs, ys)
     if ws is None:
         nbytes = load().tern_batch_workspace_bytes(descs, len(mats), m)
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=xs[0].device)
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=xs[0].device)
     check(load().tern_gemv_batched(descs, xp, yp, len(mats), m, y_dtype, _ptr(ws), ws.numel(), _stream(stream)))
     return ys
 
@@ -251,7 +251,7 @@ class Plan:
         self.m = xs[0].shape[0] if xs else 0
         descs, xp, yp = _arrays(mats, xs, ys)
         nbytes = load().tern_batch_workspace_bytes(descs, len(mats), self.m)
-        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=xs[0].device)
+        self.ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=xs[0].device)
         self._keep = (mats, xs, ys)
         handle = c_void_p()
         check(load().tern_plan_create(descs, xp, yp, len(mats), self.m, y_dtype, _ptr(self.ws),
