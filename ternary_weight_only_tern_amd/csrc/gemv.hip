@@ -3,11 +3,21 @@
 // 1.58 bits per weight", How It Works: matrix products become additions and
 // subtractions; arXiv 2609.09240: the packed weights are consumed directly).
 //
-// One row per lane: a wavefront covers 64 output rows.  Packed rows are staged through LDS with coalesced 16-byte
-// loads (8 or 13 lanes cover 128 or 208 contiguous bytes of a row), then each
-// lane decodes its own row.  All lanes sit at the same K position, so the
-// activations are wave-uniform and are read with scalar loads into SGPRs,
-// which leaves the VALU for decode and multiply-accumulate only.
+// One row per lane: a wavefront covers 64 output rows.  A work item (64 rows
+// x one K split) runs on a workgroup of 4 wavefronts that take the item's
+// LDS stages in turn (stage s goes to wave s % 4); their FP32 accumulators
+// are summed in wave order through LDS at the end (deterministic, and no
+// global memory fence: on this multi-XCD part a device-scope fence writes
+// back and invalidates the L2).  When a row block is also split along K
+// across workgroups, each split writes FP32 partials and a second kernel sums
+// them in split order.
+//
+// Stage.  A stage is 128 (2-bit) or 208 (base-3) bytes of each of the 64
+// rows, i.e. whole groups.  Its packed rows are loaded with coalesced 16-byte
+// loads (8 or 13 lanes per row), two stages ahead, and written to the wave's
+// LDS area together with the stage's activations; each lane then decodes its
+// own row.  All lanes sit at the same K position, so activations are read
+// with wave-uniform (broadcast) LDS reads.
 //
 // Decode.  A 2-bit word holds 16 trits, even offsets in the low half-word and
 // odd offsets in the high half-word, each as a 2-bit two's-complement code.
@@ -18,15 +28,13 @@
 // are first mapped through a 256-entry LDS table to the same 2-bit codes
 // (two tables place the five trits of the first / second byte of a pair).
 // Per group the FP32 partial is scaled by 0.5*s (exact) and added to the row
-// accumulator.  Residual planes are walked per lane over the row's compact
-// blocks (divergent loop), and offsets add off * sum(x) per group.
+// accumulator.
 //
-// Work item = 64 rows x one K split, run by a workgroup of 4 wavefronts that
-// split the item's groups between them; their FP32 accumulators are summed
-// in wave order through LDS (deterministic, no global memory fences: on this
-// multi-XCD part a device-scope fence writes back and invalidates the L2).
-// When a row block is additionally split along K across workgroups, each
-// split writes FP32 partials and a second kernel sums them in split order.
+// Residual planes are sparse, so they are processed compacted: each wave
+// lists the residual blocks of its 64 rows in its share of the groups in LDS
+// (a wave prefix sum over the per-row counts places each row's entries), one
+// lane per block decodes it against the group's activations, and each lane
+// then sums the values of its own row's entries in order.
 #include "internal.h"
 
 #define GLOBAL __attribute__((address_space(1)))
@@ -36,6 +44,8 @@ namespace {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;  // wavefronts per workgroup, sharing one work item
 
 template <typename T>
 __device__ __forceinline__ const GLOBAL T* gp(const T* p) { return (const GLOBAL T*)p; }
@@ -56,6 +66,14 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+__device__ __forceinline__ void wave_sync() {
+  // One wavefront's LDS accesses are processed in order; this keeps the
+  // compiler from moving LDS accesses across the hand-off between lanes.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int FMT, int G>
 struct Geo {
   static constexpr int GB = FMT == 0 ? G / 4 : (G + 4) / 5;   // bytes per group
@@ -64,63 +82,185 @@ struct Geo {
   static constexpr int CPR = SGB / 16;                          // 16-byte chunks per row
   static constexpr int PITCH = FMT == 0 ? 144 : 208;            // LDS row pitch (bytes)
   static constexpr int CHUNKS = kGemvRows * CPR / kWave;        // chunks per lane per stage
-  static constexpr int XDW = SG * G / 2;                        // activation dwords per stage per row of x
+  static constexpr int XDW = SG * G / 2;                        // activation dwords per stage per x row
   static constexpr int XCH = XDW / 4 / kWave;                   // 16-byte x chunks per lane per stage
   static constexpr int WBYTES = kGemvRows * PITCH;              // weight part of the LDS stage
   static_assert(SG * GB == SGB, "stage must hold whole groups");
   static_assert((PITCH / 16) % 2 == 1, "odd 16-byte pitch keeps b128 reads conflict-free");
 };
 
+template <int FMT, int G, int MT>
+constexpr int wave_lds_bytes() { return Geo<FMT, G>::WBYTES + MT * Geo<FMT, G>::XDW * 4; }
+
 // Base-3 byte -> 2-bit codes.  For a byte pair (A, B) holding trits t0..t4 and
 // t5..t9, pair i = (t[2i], t[2i+1]) must sit at bits 6+2i (low) and 22+2i
 // (high) of lutA[A] | lutB[B]; then pair i decodes with shift 8-2i.
 __device__ void build_b3_entry(int v, uint32_t* lutA, uint32_t* lutB) {
-  {
-    uint32_t a = 0, b = 0;
-    if (v < 243) {
-      int r = v;
-      uint32_t c[5];
-      for (int i = 0; i < 5; ++i) {
-        c[i] = (uint32_t)((r % 3) - 1) & 3u;
-        r /= 3;
-      }
-      // first byte of a pair: t0 t1 t2 t3 t4 -> pair0 lo/hi, pair1 lo/hi, pair2 lo
-      a = (c[0] << 6) | (c[1] << 22) | (c[2] << 8) | (c[3] << 24) | (c[4] << 10);
-      // second byte: t5 t6 t7 t8 t9 -> pair2 hi, pair3 lo/hi, pair4 lo/hi
-      b = (c[0] << 26) | (c[1] << 12) | (c[2] << 28) | (c[3] << 14) | (c[4] << 30);
+  uint32_t a = 0, b = 0;
+  if (v < 243) {
+    int r = v;
+    uint32_t c[5];
+    for (int i = 0; i < 5; ++i) {
+      c[i] = (uint32_t)((r % 3) - 1) & 3u;
+      r /= 3;
     }
-    lutA[v] = a;
-    lutB[v] = b;
+    // first byte of a pair: t0 t1 t2 t3 t4 -> pair0 lo/hi, pair1 lo/hi, pair2 lo
+    a = (c[0] << 6) | (c[1] << 22) | (c[2] << 8) | (c[3] << 24) | (c[4] << 10);
+    // second byte: t5 t6 t7 t8 t9 -> pair2 hi, pair3 lo/hi, pair4 lo/hi
+    b = (c[0] << 26) | (c[1] << 12) | (c[2] << 28) | (c[3] << 14) | (c[4] << 30);
+  }
+  lutA[v] = a;
+  lutB[v] = b;
+}
+
+// Decode and multiply one LDS stage: groups 0..ngs-1 of the stage, this
+// lane's row at `my`, activations at `xs4` ([MT][XDW] dwords).
+template <int FMT, int G, int MT>
+__device__ __forceinline__ void stage_compute(const uint8_t* my, const u4_t* xs4, int ngs,
+                                              const float* sc, const uint32_t* lutA,
+                                              const uint32_t* lutB, float (&acc)[MT]) {
+  using Gm = Geo<FMT, G>;
+#pragma unroll
+  for (int j = 0; j < Gm::SG; ++j) {
+    if (j < ngs) {
+      float part[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) part[m] = 0.f;
+      if (FMT == 0) {
+#pragma unroll
+        for (int q = 0; q < G / 64; ++q) {
+          const u4_t v = *reinterpret_cast<const u4_t*>(my + j * Gm::GB + q * 16);
+          const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            u4_t xa[MT], xb[MT];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              const int c = (m * Gm::XDW + j * (G / 2) + q * 32 + u * 8) / 4;
+              xa[m] = xs4[c];
+              xb[m] = xs4[c + 1];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const uint32_t p = pair_of(ws[u], 14 - 2 * i);
+#pragma unroll
+              for (int m = 0; m < MT; ++m) part[m] = dot2(p, i < 4 ? xa[m][i] : xb[m][i - 4], part[m]);
+            }
+          }
+        }
+      } else {
+        constexpr int GB = Gm::GB;
+        const int off = j * GB;  // compile-time after unrolling
+        const int c0 = off >> 4;
+        uint32_t dw[12];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          if (((off + GB - 1) >> 4) >= c0 + q) {
+            const u4_t v = *reinterpret_cast<const u4_t*>(my + (c0 + q) * 16);
+            dw[4 * q + 0] = v.x; dw[4 * q + 1] = v.y; dw[4 * q + 2] = v.z; dw[4 * q + 3] = v.w;
+          } else {
+            dw[4 * q + 0] = dw[4 * q + 1] = dw[4 * q + 2] = dw[4 * q + 3] = 0u;
+          }
+        }
+        const int sh = off - c0 * 16;
+        u4_t xc[MT][5];
+#pragma unroll
+        for (int bp = 0; bp < (GB + 1) / 2; ++bp) {
+          if (bp % 4 == 0) {  // activation pairs 5*bp .. 5*bp+19 of the group
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+              for (int c = 0; c < 5; ++c)
+                if (4 * (5 * bp / 4 + c) < G / 2) xc[m][c] = xs4[(m * Gm::XDW + j * (G / 2)) / 4 + 5 * bp / 4 + c];
+          }
+          const int ia = sh + 2 * bp, ib = ia + 1;
+          const uint32_t ba = (dw[ia >> 2] >> ((ia & 3) * 8)) & 0xFFu;
+          uint32_t code = lutA[ba];
+          if (2 * bp + 1 < GB) {
+            const uint32_t bb = (dw[ib >> 2] >> ((ib & 3) * 8)) & 0xFFu;
+            code |= lutB[bb];
+          }
+#pragma unroll
+          for (int i = 0; i < 5; ++i) {
+            if (10 * bp + 2 * i < G) {
+              const uint32_t p = pair_of(code, 8 - 2 * i);
+              const int xi = 5 * bp + i - 20 * (bp / 4);  // index within the 5 chunks
+#pragma unroll
+              for (int m = 0; m < MT; ++m) part[m] = dot2(p, xc[m][xi / 4][xi % 4], part[m]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[m] = fmaf(sc[j], part[m], acc[m]);
+    }
   }
 }
 
-__device__ __forceinline__ int find_desc(const GemvDesc* __restrict__ descs, int ndesc, int item) {
-  int lo = 0, hi = ndesc - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (descs[mid].tile_begin <= item) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-// Residual blocks of this lane's row in groups [g0, g1) of plane p.
+// Residual plane p, groups [ra, rz) of the 64 rows of this wave, processed
+// compacted through the wave's LDS area `buf` (`cap` bytes).
 template <int G, int MT>
-__device__ __forceinline__ void residual_plane(const GemvDesc& d, int p, int row, int g0, int g1,
-                                               const GLOBAL uint32_t* const (&xr)[MT],
-                                               float (&acc)[MT]) {
-  const GLOBAL uint32_t* rm = gp(d.mask[p]) + (size_t)row * d.mwords;
-  uint32_t b = gp(d.rowptr[p])[row];
-  for (int w = 0; w < (g0 >> 5); ++w) b += __popc(rm[w]);
-  if (g0 & 31) b += __popc(rm[g0 >> 5] & ((1u << (g0 & 31)) - 1u));
+__device__ __forceinline__ void residual_compact(const GemvDesc& d, int p, int row, bool row_ok,
+                                                 int ra, int rz, const GLOBAL uint32_t* const (&xr)[MT],
+                                                 uint8_t* buf, int cap, float (&acc)[MT]) {
+  const int lane = threadIdx.x % kWave;
+  // this row's blocks in [ra, rz): count, first block index
+  uint32_t cnt = 0, base = 0;
+  const GLOBAL uint32_t* rm = gp(d.mask[p]) + (size_t)(row_ok ? row : 0) * d.mwords;
+  if (row_ok) {
+    base = gp(d.rowptr[p])[row];
+    for (int w = 0; w < (ra >> 5); ++w) base += __popc(rm[w]);
+    if (ra & 31) base += __popc(rm[ra >> 5] & ((1u << (ra & 31)) - 1u));
+    for (int w = ra >> 5; w <= ((rz - 1) >> 5); ++w) {
+      const int lo = max(ra - (w << 5), 0), hi = min(rz - (w << 5), 32);
+      const uint32_t keep = (lo > 0 ? ~((1u << lo) - 1u) : ~0u) & (hi < 32 ? ((1u << hi) - 1u) : ~0u);
+      cnt += __popc(rm[w] & keep);
+    }
+  }
+  // exclusive prefix of the counts over the wave
+  uint32_t incl = cnt;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t v = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += v;
+  }
+  const uint32_t off = incl - cnt;
+  const uint32_t total = __shfl(incl, kWave - 1, kWave);
+  if (total == 0) return;
+
+  // window of entries held in LDS: [block index, (row lane << 16) | group], then MT values
+  constexpr int ESZ = 8 + 4 * MT;
+  const int win = (cap / ESZ) / kWave * kWave;
+  uint32_t* ent = reinterpret_cast<uint32_t*>(buf);
+  float* val = reinterpret_cast<float*>(buf + (size_t)win * 8);
   const GLOBAL uint8_t* blocks = gp(d.blocks[p]);
   const GLOBAL uint16_t* rscale = gp(d.rscale[p]);
-  for (int w = g0 >> 5; w <= ((g1 - 1) >> 5); ++w) {
-    uint32_t bits = rm[w];
-    const int lo = max(g0 - (w << 5), 0), hi = min(g1 - (w << 5), 32);
-    bits &= (lo > 0 ? ~((1u << lo) - 1u) : ~0u) & (hi < 32 ? ((1u << hi) - 1u) : ~0u);
-    while (bits) {
-      const int g = (w << 5) + __builtin_ctz(bits);
-      bits &= bits - 1u;
+
+  for (uint32_t w0 = 0; w0 < total; w0 += win) {
+    const uint32_t wn = min((uint32_t)win, total - w0);
+    wave_sync();
+    // each lane lists its own entries that fall in this window
+    if (cnt && off < w0 + wn && off + cnt > w0) {
+      uint32_t e = off;
+      for (int w = ra >> 5; w <= ((rz - 1) >> 5); ++w) {
+        const int lo = max(ra - (w << 5), 0), hi = min(rz - (w << 5), 32);
+        uint32_t bits = rm[w] & (lo > 0 ? ~((1u << lo) - 1u) : ~0u) & (hi < 32 ? ((1u << hi) - 1u) : ~0u);
+        while (bits) {
+          const int g = (w << 5) + __builtin_ctz(bits);
+          bits &= bits - 1u;
+          if (e >= w0 && e < w0 + wn) {
+            ent[2 * (e - w0)] = base + (e - off);
+            ent[2 * (e - w0) + 1] = ((uint32_t)lane << 16) | (uint32_t)g;
+          }
+          ++e;
+        }
+      }
+    }
+    wave_sync();
+    // one lane per block
+    for (uint32_t t = lane; t < wn; t += kWave) {
+      const uint32_t b = ent[2 * t];
+      const int g = (int)(ent[2 * t + 1] & 0xFFFFu);
       const GLOBAL u4_t* blk = reinterpret_cast<const GLOBAL u4_t*>(blocks + (size_t)b * (G / 4));
       float part[MT];
 #pragma unroll
@@ -144,48 +284,43 @@ __device__ __forceinline__ void residual_plane(const GemvDesc& d, int p, int row
       }
       const float rs = 0.5f * h2f(rscale[b]);
 #pragma unroll
-      for (int m = 0; m < MT; ++m) acc[m] = fmaf(rs, part[m], acc[m]);
-      ++b;
+      for (int m = 0; m < MT; ++m) val[t * MT + m] = rs * part[m];
+    }
+    wave_sync();
+    // each lane adds the values of its own entries, in order
+    if (cnt) {
+      const uint32_t lo = max(off, w0), hi = min(off + cnt, w0 + wn);
+      for (uint32_t e = lo; e < hi; ++e)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m] += val[(e - w0) * MT + m];
     }
   }
 }
 
-constexpr int kWaves = 4;  // wavefronts per workgroup, splitting K
-
-__device__ __forceinline__ void wave_sync() {
-  // LDS traffic of one wavefront is processed in order; this keeps the
-  // compiler from moving LDS accesses across the hand-off point.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 template <int FMT, int G, int MT>
 __global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __restrict__ descs,
+                                                              const uint16_t* __restrict__ tile_desc,
                                                               int ndesc, GemvDesc one) {
   using Gm = Geo<FMT, G>;
+  constexpr int WL = wave_lds_bytes<FMT, G, MT>();
   extern __shared__ uint4 stage_all[];  // per wave: [64 rows][PITCH] + activations of a stage
   __shared__ uint32_t lutA[FMT == 1 ? 256 : 1];
   __shared__ uint32_t lutB[FMT == 1 ? 256 : 1];
 
-  const int item_g = blockIdx.x;
   GemvDesc d;
-  if (ndesc > 0) d = descs[find_desc(descs, ndesc, item_g)];
+  if (ndesc > 0) d = descs[tile_desc[blockIdx.x]];
   else d = one;
-  const int item = item_g - d.tile_begin;
+  const int item = (int)blockIdx.x - d.tile_begin;
   const int rb = item % d.row_blocks;
   const int split = item / d.row_blocks;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int row = rb * kGemvRows + lane;
   const bool row_ok = row < d.n;
-  // this wave's share of the item's groups, on stage boundaries
-  const int ga = split * d.gps;
+  const int ga = split * d.gps;                // the item's groups [ga, gb)
   const int gb = min(d.ng, ga + d.gps);
-  const int q = ((gb - ga + kWaves - 1) / kWaves + Gm::SG - 1) / Gm::SG * Gm::SG;
-  const int g0 = min(gb, ga + wave * q);
-  const int g1 = min(gb, g0 + q);
-  const int nstages = (g1 - g0 + Gm::SG - 1) / Gm::SG;
+  const int nstages = (gb - ga + Gm::SG - 1) / Gm::SG;
+  const int nmine = nstages > wave ? (nstages - wave + kWaves - 1) / kWaves : 0;
 
   if (FMT == 1) {
     for (int v = threadIdx.x; v < 256; v += kWave * kWaves) build_b3_entry(v, lutA, lutB);
@@ -193,9 +328,12 @@ __global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __
   }
 
   const GLOBAL uint32_t* xr[MT];
+  const GLOBAL u4_t* xq[MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+  for (int m = 0; m < MT; ++m) {
     xr[m] = reinterpret_cast<const GLOBAL uint32_t*>(gp(d.x) + (size_t)min(m, d.m - 1) * d.k);
+    xq[m] = reinterpret_cast<const GLOBAL u4_t*>(xr[m]);
+  }
 
   float acc[MT];
 #pragma unroll
@@ -204,166 +342,91 @@ __global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __
   const GLOBAL uint8_t* prow0 = gp(d.plane0) + (size_t)rb * kGemvRows * d.stride;
   const GLOBAL uint16_t* srow = gp(d.scale0) + (size_t)(row_ok ? row : 0) * d.ng;
   const int rows_here = min(kGemvRows, d.n - rb * kGemvRows);
-  uint8_t* lds = reinterpret_cast<uint8_t*>(stage_all) + (size_t)wave * (Gm::WBYTES + MT * Gm::XDW * 4);
+  uint8_t* lds = reinterpret_cast<uint8_t*>(stage_all) + (size_t)wave * WL;
+  const u4_t* xs4 = reinterpret_cast<const u4_t*>(lds + Gm::WBYTES);
+  const uint8_t* my = lds + lane * Gm::PITCH;
 
-  // prefetch registers for the next stage: packed rows, scales, activations
-  u4_t pre[Gm::CHUNKS];
-  uint16_t spre[Gm::SG];
-  u4_t xpre[MT][Gm::XCH];
-  const GLOBAL u4_t* xq[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) xq[m] = reinterpret_cast<const GLOBAL u4_t*>(xr[m]);
-#define TERN_LOAD_STAGE(s_)                                                                 \
-  do {                                                                                      \
-    const int gs_ = g0 + (s_) * Gm::SG;                                                     \
-    const int bytes_ = min(Gm::SG, g1 - gs_) * Gm::GB;                                      \
-    const GLOBAL uint8_t* base_ = prow0 + (size_t)gs_ * Gm::GB;                             \
-    _Pragma("unroll") for (int i = 0; i < Gm::CHUNKS; ++i) {                                \
-      const int c = i * kWave + lane;                                                       \
-      const int r = c / Gm::CPR, col = c % Gm::CPR;                                         \
-      if (r < rows_here && col * 16 < bytes_)                                               \
-        pre[i] = *reinterpret_cast<const GLOBAL u4_t*>(base_ + (size_t)r * d.stride + col * 16); \
-    }                                                                                       \
-    _Pragma("unroll") for (int j = 0; j < Gm::SG; ++j)                                      \
-      spre[j] = (row_ok && gs_ + j < g1) ? srow[gs_ + j] : (uint16_t)0;                     \
-    _Pragma("unroll") for (int m = 0; m < MT; ++m)                                          \
-      _Pragma("unroll") for (int i = 0; i < Gm::XCH; ++i) {                                 \
-        const int xc_ = gs_ * (G / 8) + i * kWave + lane;                                   \
-        if (xc_ < g1 * (G / 8)) xpre[m][i] = xq[m][xc_];                                    \
-      }                                                                                     \
+  // two register sets of prefetched stages: packed rows, scales, activations
+  u4_t preA[Gm::CHUNKS], preB[Gm::CHUNKS];
+  uint16_t spA[Gm::SG], spB[Gm::SG];
+  u4_t xpA[MT][Gm::XCH], xpB[MT][Gm::XCH];
+
+#define TERN_LOAD(P, SP, XP, i_)                                                             \
+  do {                                                                                       \
+    const int gs_ = ga + (wave + kWaves * (i_)) * Gm::SG;                                    \
+    const int bytes_ = min(Gm::SG, gb - gs_) * Gm::GB;                                       \
+    const GLOBAL uint8_t* base_ = prow0 + (size_t)gs_ * Gm::GB;                              \
+    _Pragma("unroll") for (int i = 0; i < Gm::CHUNKS; ++i) {                                 \
+      const int c = i * kWave + lane;                                                        \
+      const int r = c / Gm::CPR, col = c % Gm::CPR;                                          \
+      if (r < rows_here && col * 16 < bytes_)                                                \
+        P[i] = *reinterpret_cast<const GLOBAL u4_t*>(base_ + (size_t)r * d.stride + col * 16); \
+    }                                                                                        \
+    _Pragma("unroll") for (int j = 0; j < Gm::SG; ++j)                                       \
+      SP[j] = (row_ok && gs_ + j < gb) ? srow[gs_ + j] : (uint16_t)0;                        \
+    _Pragma("unroll") for (int m = 0; m < MT; ++m)                                           \
+      _Pragma("unroll") for (int i = 0; i < Gm::XCH; ++i) {                                  \
+        const int xc_ = gs_ * (G / 8) + i * kWave + lane;                                    \
+        if (xc_ < gb * (G / 8)) XP[m][i] = xq[m][xc_];                                       \
+      }                                                                                      \
   } while (0)
 
-  if (nstages > 0) TERN_LOAD_STAGE(0);
-  for (int s = 0; s < nstages; ++s) {
-    const int gs = g0 + s * Gm::SG;
-    const int ngs = min(Gm::SG, g1 - gs);
-    wave_sync();  // previous stage consumed
-#pragma unroll
-    for (int i = 0; i < Gm::CHUNKS; ++i) {
-      const int c = i * kWave + lane;
-      const int r = c / Gm::CPR, col = c % Gm::CPR;
-      *reinterpret_cast<u4_t*>(lds + r * Gm::PITCH + col * 16) = pre[i];
-    }
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int i = 0; i < Gm::XCH; ++i)
-        *reinterpret_cast<u4_t*>(lds + Gm::WBYTES + (m * Gm::XDW + (i * kWave + lane) * 4) * 4) = xpre[m][i];
-    float sc[Gm::SG];
-#pragma unroll
-    for (int j = 0; j < Gm::SG; ++j) sc[j] = 0.5f * h2f(spre[j]);
-    wave_sync();
-    if (s + 1 < nstages) TERN_LOAD_STAGE(s + 1);
+#define TERN_CONSUME(P, SP, XP, i_)                                                          \
+  do {                                                                                       \
+    const int gs_ = ga + (wave + kWaves * (i_)) * Gm::SG;                                    \
+    const int ngs_ = min(Gm::SG, gb - gs_);                                                  \
+    wave_sync(); /* the previous stage has been read */                                      \
+    _Pragma("unroll") for (int i = 0; i < Gm::CHUNKS; ++i) {                                 \
+      const int c = i * kWave + lane;                                                        \
+      const int r = c / Gm::CPR, col = c % Gm::CPR;                                          \
+      *reinterpret_cast<u4_t*>(lds + r * Gm::PITCH + col * 16) = P[i];                       \
+    }                                                                                        \
+    _Pragma("unroll") for (int m = 0; m < MT; ++m)                                           \
+      _Pragma("unroll") for (int i = 0; i < Gm::XCH; ++i)                                    \
+        *reinterpret_cast<u4_t*>(lds + Gm::WBYTES + (m * Gm::XDW + (i * kWave + lane) * 4) * 4) = XP[m][i]; \
+    float sc_[Gm::SG];                                                                       \
+    _Pragma("unroll") for (int j = 0; j < Gm::SG; ++j) sc_[j] = 0.5f * h2f(SP[j]);          \
+    wave_sync();                                                                             \
+    if ((i_) + 2 < nmine) TERN_LOAD(P, SP, XP, (i_) + 2);                                    \
+    stage_compute<FMT, G, MT>(my, xs4, ngs_, sc_, lutA, lutB, acc);                          \
+  } while (0)
 
-    const uint8_t* my = lds + lane * Gm::PITCH;
-    // wave-uniform activation chunks of this stage (broadcast LDS reads)
-    const u4_t* xs4 = reinterpret_cast<const u4_t*>(lds + Gm::WBYTES);
+  if (nmine > 0) TERN_LOAD(preA, spA, xpA, 0);
+  if (nmine > 1) TERN_LOAD(preB, spB, xpB, 1);
+  for (int i = 0; i < nmine; i += 2) {
+    TERN_CONSUME(preA, spA, xpA, i);
+    if (i + 1 < nmine) TERN_CONSUME(preB, spB, xpB, i + 1);
+  }
+#undef TERN_CONSUME
+#undef TERN_LOAD
+
+  // ---- residual planes and offsets over this wave's share [ra, rz) of the groups
+  const int rq = (gb - ga + kWaves - 1) / kWaves;
+  const int ra = min(gb, ga + wave * rq), rz = min(gb, ra + rq);
+  if (rz > ra) {
+    if (d.planes > 1) residual_compact<G, MT>(d, 0, row, row_ok, ra, rz, xr, lds, WL, acc);
+    if (d.planes > 2) residual_compact<G, MT>(d, 1, row, row_ok, ra, rz, xr, lds, WL, acc);
+    if (d.offset_mode != 0) {
+      const GLOBAL uint16_t* off = gp(d.offset);
+      for (int g = ra; g < rz; ++g) {
+        float xs[MT];
 #pragma unroll
-    for (int j = 0; j < Gm::SG; ++j) {
-      if (j < ngs) {
-        const int g = gs + j;
-        float part[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) part[m] = 0.f;
-        if (FMT == 0) {
-#pragma unroll
-          for (int q = 0; q < G / 64; ++q) {
-            const u4_t v = *reinterpret_cast<const u4_t*>(my + j * Gm::GB + q * 16);
-            const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              u4_t xa[MT], xb[MT];
-#pragma unroll
-              for (int m = 0; m < MT; ++m) {
-                const int c = (m * Gm::XDW + j * (G / 2) + q * 32 + u * 8) / 4;
-                xa[m] = xs4[c];
-                xb[m] = xs4[c + 1];
-              }
-#pragma unroll
-              for (int i = 0; i < 8; ++i) {
-                const uint32_t p = pair_of(ws[u], 14 - 2 * i);
-#pragma unroll
-                for (int m = 0; m < MT; ++m) part[m] = dot2(p, i < 4 ? xa[m][i] : xb[m][i - 4], part[m]);
-              }
-            }
-          }
-        } else {
-          constexpr int GB = Gm::GB;
-          const int off = j * GB;               // compile-time after unrolling
-          const int c0 = off >> 4;
-          uint32_t dw[12];
-#pragma unroll
-          for (int q = 0; q < 3; ++q) {
-            if (((off + GB - 1) >> 4) >= c0 + q) {
-              const u4_t v = *reinterpret_cast<const u4_t*>(my + (c0 + q) * 16);
-              dw[4 * q + 0] = v.x; dw[4 * q + 1] = v.y; dw[4 * q + 2] = v.z; dw[4 * q + 3] = v.w;
-            } else {
-              dw[4 * q + 0] = dw[4 * q + 1] = dw[4 * q + 2] = dw[4 * q + 3] = 0u;
-            }
-          }
-          const int sh = off - c0 * 16;
-          u4_t xc[MT][5];
-#pragma unroll
-          for (int bp = 0; bp < (GB + 1) / 2; ++bp) {
-            if (bp % 4 == 0) {  // activation pairs 5*bp .. 5*bp+19 of the group
-#pragma unroll
-              for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int c = 0; c < 5; ++c)
-                  if (4 * (5 * bp / 4 + c) < G / 2) xc[m][c] = xs4[(m * Gm::XDW + j * (G / 2)) / 4 + 5 * bp / 4 + c];
-            }
-            const int ia = sh + 2 * bp, ib = ia + 1;
-            const uint32_t ba = (dw[ia >> 2] >> ((ia & 3) * 8)) & 0xFFu;
-            uint32_t code = lutA[ba];
-            if (2 * bp + 1 < GB) {
-              const uint32_t bb = (dw[ib >> 2] >> ((ib & 3) * 8)) & 0xFFu;
-              code |= lutB[bb];
-            }
-#pragma unroll
-            for (int i = 0; i < 5; ++i) {
-              if (10 * bp + 2 * i < G) {
-                const uint32_t p = pair_of(code, 8 - 2 * i);
-                const int xi = 5 * bp + i - 4 * (5 * (bp / 4 * 4) / 4);  // index within the 5 chunks
-#pragma unroll
-                for (int m = 0; m < MT; ++m) part[m] = dot2(p, xc[m][xi / 4][xi % 4], part[m]);
-              }
-            }
-          }
+        for (int m = 0; m < MT; ++m) {
+          float v = 0.f;
+          for (int pi = lane; pi < G / 2; pi += kWave) v = dot2(xr[m][g * (G / 2) + pi], 0x3C003C00u, v);
+          xs[m] = wave_sum(v);
         }
+        if (row_ok) {
+          const float o = h2f(d.offset_mode == 1 ? off[row] : off[(size_t)row * d.ng + g]);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m] = fmaf(sc[j], part[m], acc[m]);
-      }
-    }
-  }
-#undef TERN_LOAD_STAGE
-
-  // ---- residual planes: each lane walks its row's compact blocks in [g0, g1)
-  if (row_ok && g1 > g0) {
-    if (d.planes > 1) residual_plane<G, MT>(d, 0, row, g0, g1, xr, acc);
-    if (d.planes > 2) residual_plane<G, MT>(d, 1, row, g0, g1, xr, acc);
-  }
-
-  // ---- offsets: off(n,g) * sum of the group's activations
-  if (d.offset_mode != 0) {
-    const GLOBAL uint16_t* off = gp(d.offset);
-    for (int g = g0; g < g1; ++g) {
-      float xs[MT];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        float v = 0.f;
-        for (int pi = lane; pi < G / 2; pi += kWave) v = dot2(xr[m][g * (G / 2) + pi], 0x3C003C00u, v);
-        xs[m] = wave_sum(v);
-      }
-      if (row_ok) {
-        const float o = h2f(d.offset_mode == 1 ? off[row] : off[(size_t)row * d.ng + g]);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m] = fmaf(o, xs[m], acc[m]);
+          for (int m = 0; m < MT; ++m) acc[m] = fmaf(o, xs[m], acc[m]);
+        }
       }
     }
   }
 
   // ---- combine the wavefronts' accumulators in wave order
-  __syncthreads();  // every wave is done with its stage buffers
+  __syncthreads();  // every wave is done with its LDS area
   float* red = reinterpret_cast<float*>(stage_all);
 #pragma unroll
   for (int m = 0; m < MT; ++m) red[(wave * MT + m) * kWave + lane] = acc[m];
@@ -400,19 +463,25 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ partial, int spli
   else reinterpret_cast<_Float16*>(y)[i] = (_Float16)v;
 }
 
+template <int FMT, int G, int MT>
+hipError_t launch_one(const GemvDesc* descs, const uint16_t* tile_desc, int ndesc, const GemvDesc& one,
+                      int items, hipStream_t s) {
+  const size_t lds = (size_t)kWaves * wave_lds_bytes<FMT, G, MT>();
+  hipLaunchKernelGGL((gemv_kernel<FMT, G, MT>), dim3(items), dim3(kWave * kWaves), lds, s, descs,
+                     tile_desc, ndesc, one);
+  return hipGetLastError();
+}
+
 template <int FMT, int G>
-hipError_t launch_fmt_g(int mt, const GemvDesc* descs, int ndesc, const GemvDesc& one, int items,
-                        hipStream_t s) {
-  const size_t lds = (size_t)kWaves * (Geo<FMT, G>::WBYTES + (size_t)mt * Geo<FMT, G>::XDW * 4);
-  const dim3 block(kWave * kWaves);
+hipError_t launch_fmt_g(int mt, const GemvDesc* descs, const uint16_t* tile_desc, int ndesc,
+                        const GemvDesc& one, int items, hipStream_t s) {
   switch (mt) {
-    case 1: hipLaunchKernelGGL((gemv_kernel<FMT, G, 1>), dim3(items), block, lds, s, descs, ndesc, one); break;
-    case 2: hipLaunchKernelGGL((gemv_kernel<FMT, G, 2>), dim3(items), block, lds, s, descs, ndesc, one); break;
-    case 4: hipLaunchKernelGGL((gemv_kernel<FMT, G, 4>), dim3(items), block, lds, s, descs, ndesc, one); break;
-    case 8: hipLaunchKernelGGL((gemv_kernel<FMT, G, 8>), dim3(items), block, lds, s, descs, ndesc, one); break;
+    case 1: return launch_one<FMT, G, 1>(descs, tile_desc, ndesc, one, items, s);
+    case 2: return launch_one<FMT, G, 2>(descs, tile_desc, ndesc, one, items, s);
+    case 4: return launch_one<FMT, G, 4>(descs, tile_desc, ndesc, one, items, s);
+    case 8: return launch_one<FMT, G, 8>(descs, tile_desc, ndesc, one, items, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -432,13 +501,13 @@ hipError_t launch_splitk_reduce(const float* partial, int splits, int m, int n, 
   return hipGetLastError();
 }
 
-hipError_t launch_gemv(int format, int group, int mt, const GemvDesc* descs, int ndesc,
-                       const GemvDesc& one, int total_items, hipStream_t s) {
+hipError_t launch_gemv(int format, int group, int mt, const GemvDesc* descs, const uint16_t* tile_desc,
+                       int ndesc, const GemvDesc& one, int total_items, hipStream_t s) {
   if (total_items <= 0) return hipSuccess;
-  if (format == 0 && group == 64) return launch_fmt_g<0, 64>(mt, descs, ndesc, one, total_items, s);
-  if (format == 0 && group == 128) return launch_fmt_g<0, 128>(mt, descs, ndesc, one, total_items, s);
-  if (format == 1 && group == 64) return launch_fmt_g<1, 64>(mt, descs, ndesc, one, total_items, s);
-  if (format == 1 && group == 128) return launch_fmt_g<1, 128>(mt, descs, ndesc, one, total_items, s);
+  if (format == 0 && group == 64) return launch_fmt_g<0, 64>(mt, descs, tile_desc, ndesc, one, total_items, s);
+  if (format == 0 && group == 128) return launch_fmt_g<0, 128>(mt, descs, tile_desc, ndesc, one, total_items, s);
+  if (format == 1 && group == 64) return launch_fmt_g<1, 64>(mt, descs, tile_desc, ndesc, one, total_items, s);
+  if (format == 1 && group == 128) return launch_fmt_g<1, 128>(mt, descs, tile_desc, ndesc, one, total_items, s);
   return hipErrorInvalidValue;
 }
 

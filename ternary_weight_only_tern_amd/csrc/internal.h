@@ -41,8 +41,10 @@ struct GemvDesc {
 // device memory (`descs`), or over the single descriptor `one` when ndesc == 0.
 // total_items = sum over descriptors of splits * row_blocks.  Descriptors
 // with splits > 1 write FP32 partials; launch_splitk_reduce then sums them.
-hipError_t launch_gemv(int format, int group, int mt, const GemvDesc* descs, int ndesc,
-                       const GemvDesc& one, int total_items, hipStream_t stream);
+// tile_desc[i] is the descriptor index of work item i (device, used when ndesc > 0).
+hipError_t launch_gemv(int format, int group, int mt, const GemvDesc* descs,
+                       const uint16_t* tile_desc, int ndesc, const GemvDesc& one, int total_items,
+                       hipStream_t stream);
 // y[m][n] = sum_s partial[s][m][n] in split order.
 hipError_t launch_splitk_reduce(const float* partial, int splits, int m, int n, void* y,
                                 int y_f32, hipStream_t stream);

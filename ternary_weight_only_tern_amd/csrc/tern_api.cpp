@@ -182,6 +182,7 @@ tern_status check_xy(const uint16_t* x, void* y, int y_dtype) {
 
 struct tern_plan {
   const GemvDesc* dev;
+  const uint16_t* tiles;
   int ndesc;
   int total_items;
   int format, group, mt;
@@ -336,7 +337,7 @@ tern_status tern_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* 
     if (splits > 1) dc.partial = static_cast<float*>(ws);
     dc.tile_begin = 0;
     const int items = splits * dc.row_blocks;
-    TERN_HIP(tern::launch_gemv(w->format, w->group, pick_mt(mc), nullptr, 0, dc, items, s));
+    TERN_HIP(tern::launch_gemv(w->format, w->group, pick_mt(mc), nullptr, nullptr, 0, dc, items, s));
     if (splits > 1) TERN_HIP(tern::launch_splitk_reduce(dc.partial, splits, mc, w->n, dc.y, y_f32, s));
   }
   return TERN_OK;
@@ -363,13 +364,15 @@ tern_status tern_gemm(const tern_matrix* w, const uint16_t* x, int32_t m, void* 
 // of a workgroup split it).  `ws` holds the descriptor table.
 static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y,
                                int32_t count, int32_t m, int32_t y_dtype,
-                               std::vector<GemvDesc>* out, int* total, int* mt) {
+                               std::vector<GemvDesc>* out, std::vector<uint16_t>* tiles, int* total,
+                               int* mt) {
   if (count < 0) return fail(TERN_E_INVAL, "count=%d is negative", count);
   if (count > 0 && (!w || !x || !y)) return fail(TERN_E_INVAL, "NULL descriptor arrays");
   if (m < 0) return fail(TERN_E_INVAL, "m=%d is negative", m);
   if (m >= 64) return fail(TERN_E_UNSUPPORTED, "batched decode takes m <= 63 (got %d)", m);
   if (y_dtype != TERN_F16 && y_dtype != TERN_F32) return fail(TERN_E_UNSUPPORTED, "unknown y dtype %d", y_dtype);
   out->clear();
+  tiles->clear();
   *total = 0;
   *mt = pick_mt(std::min(m, tern::kMaxMT));
   std::vector<int> order;
@@ -392,33 +395,44 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
                 static_cast<char*>(y[i]) + (size_t)c0 * w[i].n * esz, y_dtype == TERN_F32);
       d.tile_begin = *total;
       *total += d.row_blocks;
+      if (out->size() >= 65535) return fail(TERN_E_UNSUPPORTED, "batch has more than 65535 descriptors");
+      tiles->insert(tiles->end(), (size_t)d.row_blocks, (uint16_t)out->size());
       out->push_back(d);
     }
   }
   return TERN_OK;
 }
 
+// Workspace layout of a batch: [descriptor table][work item -> descriptor index].
+static size_t batch_tiles_offset(size_t ndesc) { return round_up(ndesc * sizeof(GemvDesc), 256); }
+
 size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m) {
-  (void)w;
-  if (count <= 0 || m <= 0) return 0;
+  if (count <= 0 || m <= 0 || !w) return 0;
   const size_t chunks = (size_t)(m + tern::kMaxMT - 1) / tern::kMaxMT;
-  return round_up((size_t)count * chunks * sizeof(GemvDesc), 256);
+  size_t tiles = 0;
+  for (int i = 0; i < count; ++i) tiles += (size_t)std::max(0, (w[i].n + tern::kGemvRows - 1) / tern::kGemvRows) * chunks;
+  return batch_tiles_offset((size_t)count * chunks) + round_up(tiles * sizeof(uint16_t), 256);
 }
 
 tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, void* const* y,
                               int32_t count, int32_t m, int32_t y_dtype, void* ws, size_t ws_bytes,
                               void* stream) {
   std::vector<GemvDesc> descs;
+  std::vector<uint16_t> tiles;
   int total = 0, mt = 1;
-  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &descs, &total, &mt));
+  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &descs, &tiles, &total, &mt));
   if (descs.empty()) return TERN_OK;
-  const size_t need = descs.size() * sizeof(GemvDesc);
+  const size_t toff = batch_tiles_offset(descs.size());
+  const size_t need = toff + tiles.size() * sizeof(uint16_t);
   if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "batched decode needs %zu workspace bytes", need);
   TERN_TRY(check_dev(ws, true, "ws"));
   hipStream_t s = (hipStream_t)stream;
-  TERN_HIP(hipMemcpyAsync(ws, descs.data(), need, hipMemcpyHostToDevice, s));
-  TERN_HIP(tern::launch_gemv(w[0].format, w[0].group, mt, static_cast<const GemvDesc*>(ws),
-                             (int)descs.size(), descs[0], total, s));
+  char* base = static_cast<char*>(ws);
+  TERN_HIP(hipMemcpyAsync(base, descs.data(), descs.size() * sizeof(GemvDesc), hipMemcpyHostToDevice, s));
+  TERN_HIP(hipMemcpyAsync(base + toff, tiles.data(), tiles.size() * sizeof(uint16_t), hipMemcpyHostToDevice, s));
+  TERN_HIP(tern::launch_gemv(w[0].format, w[0].group, mt, reinterpret_cast<const GemvDesc*>(base),
+                             reinterpret_cast<const uint16_t*>(base + toff), (int)descs.size(), descs[0],
+                             total, s));
   return TERN_OK;
 }
 
@@ -428,17 +442,22 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
   if (!out) return fail(TERN_E_INVAL, "out is NULL");
   *out = nullptr;
   std::vector<GemvDesc> descs;
+  std::vector<uint16_t> tiles;
   int total = 0, mt = 1;
-  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &descs, &total, &mt));
-  const size_t need = descs.size() * sizeof(GemvDesc);
-  if (need) {
+  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &descs, &tiles, &total, &mt));
+  const size_t toff = batch_tiles_offset(descs.size());
+  if (!descs.empty()) {
+    const size_t need = toff + tiles.size() * sizeof(uint16_t);
     if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "plan needs %zu workspace bytes", need);
     TERN_TRY(check_dev(ws, true, "ws"));
-    TERN_HIP(hipMemcpy(ws, descs.data(), need, hipMemcpyHostToDevice));
+    char* base = static_cast<char*>(ws);
+    TERN_HIP(hipMemcpy(base, descs.data(), descs.size() * sizeof(GemvDesc), hipMemcpyHostToDevice));
+    TERN_HIP(hipMemcpy(base + toff, tiles.data(), tiles.size() * sizeof(uint16_t), hipMemcpyHostToDevice));
   }
   tern_plan* p = static_cast<tern_plan*>(std::malloc(sizeof(tern_plan)));
   if (!p) return fail(TERN_E_INVAL, "out of host memory");
   p->dev = static_cast<const GemvDesc*>(ws);
+  p->tiles = reinterpret_cast<const uint16_t*>(static_cast<const char*>(ws) + toff);
   p->ndesc = (int)descs.size();
   p->total_items = total;
   p->format = count > 0 ? w[0].format : 0;
@@ -453,8 +472,8 @@ tern_status tern_plan_run(const tern_plan* plan, void* stream) {
   if (plan->ndesc == 0) return TERN_OK;
   GemvDesc dummy;
   std::memset(&dummy, 0, sizeof(dummy));
-  TERN_HIP(tern::launch_gemv(plan->format, plan->group, plan->mt, plan->dev, plan->ndesc, dummy,
-                             plan->total_items, (hipStream_t)stream));
+  TERN_HIP(tern::launch_gemv(plan->format, plan->group, plan->mt, plan->dev, plan->tiles, plan->ndesc,
+                             dummy, plan->total_items, (hipStream_t)stream));
   return TERN_OK;
 }
 
