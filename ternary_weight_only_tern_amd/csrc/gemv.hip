@@ -14,7 +14,8 @@
 //
 // Stage.  A stage is 128 (2-bit) or 208 (base-3) bytes of each of the 64
 // rows, i.e. whole groups.  Its packed rows are loaded with coalesced 16-byte
-// loads (8 or 13 lanes per row), two stages ahead, and written to the wave's
+// loads (8 or 13 lanes per row), two (2-bit) or one (base-3) stages ahead,
+// and written to the wave's
 // LDS area together with the stage's activations; each lane then decodes its
 // own row.  All lanes sit at the same K position, so activations are read
 // with wave-uniform (broadcast) LDS reads.
@@ -25,8 +26,8 @@
 // the FP16 pair (2*t[2i], 2*t[2i+1]) exactly (bit 15 = sign, bit 14 = the top
 // exponent bit: 0x4000 = 2.0), so one v_dot2_f32_f16 against the natural
 // activation pair (x[2i], x[2i+1]) accumulates 2*(t.x) in FP32.  Base-3 bytes
-// are first mapped through a 256-entry LDS table to the same 2-bit codes
-// (two tables place the five trits of the first / second byte of a pair).
+// are mapped through two 256-entry LDS tables straight to such pair words
+// (see build_b3_entry); the activations are staged in the matching order.
 // Per group the FP32 partial is scaled by 0.5*s (exact) and added to the row
 // accumulator.
 //
@@ -82,21 +83,38 @@ struct Geo {
   static constexpr int CPR = SGB / 16;                          // 16-byte chunks per row
   static constexpr int PITCH = FMT == 0 ? 144 : 208;            // LDS row pitch (bytes)
   static constexpr int CHUNKS = kGemvRows * CPR / kWave;        // chunks per lane per stage
-  static constexpr int XDW = SG * G / 2;                        // activation dwords per stage per x row
-  static constexpr int XCH = XDW / 4 / kWave;                   // 16-byte x chunks per lane per stage
+  // activation dwords per group in the LDS stage: natural pairs for 2-bit;
+  // for base-3 five permuted pairs per byte pair, padded to a 16-byte multiple
+  static constexpr int XGD = FMT == 0 ? G / 2 : ((GB + 1) / 2 * 5 + 3) / 4 * 4;
+  static constexpr int XDW = SG * XGD;                          // activation dwords per stage per x row
+  static constexpr int XNAT = SG * G / 2;                       // natural activation dwords per stage
+  static constexpr int XCH = XNAT / 4 / kWave;                  // 16-byte x chunks per lane per stage
+  static constexpr int XBP = FMT == 1 ? SG * ((GB + 1) / 2) : 0; // byte pairs per stage (base-3)
+  static constexpr int XBL = (XBP + kWave - 1) / kWave;         // byte pairs per lane (base-3)
+  static_assert(XNAT % (4 * kWave) == 0, "activation chunks must split evenly over the lanes");
   static constexpr int WBYTES = kGemvRows * PITCH;              // weight part of the LDS stage
   static_assert(SG * GB == SGB, "stage must hold whole groups");
   static_assert((PITCH / 16) % 2 == 1, "odd 16-byte pitch keeps b128 reads conflict-free");
 };
 
+// Per-wave LDS: packed rows, the stage's activations in decode order, and for
+// base-3 a natural-order copy the permuted one is built from.
 template <int FMT, int G, int MT>
-constexpr int wave_lds_bytes() { return Geo<FMT, G>::WBYTES + MT * Geo<FMT, G>::XDW * 4; }
+constexpr int wave_lds_bytes() {
+  return Geo<FMT, G>::WBYTES + MT * Geo<FMT, G>::XDW * 4 + (FMT == 1 ? MT * Geo<FMT, G>::XNAT * 4 : 0);
+}
 
-// Base-3 byte -> 2-bit codes.  For a byte pair (A, B) holding trits t0..t4 and
-// t5..t9, pair i = (t[2i], t[2i+1]) must sit at bits 6+2i (low) and 22+2i
-// (high) of lutA[A] | lutB[B]; then pair i decodes with shift 8-2i.
-__device__ void build_b3_entry(int v, uint32_t* lutA, uint32_t* lutB) {
-  uint32_t a = 0, b = 0;
+// Base-3 byte -> FP16 pair words.  For a byte pair (A, B) holding trits
+// t0..t4 and t5..t9, the decode forms five pair words, each bit 15 / 14 (and
+// 31 / 30) being the 2-bit code of a trit, i.e. the FP16 value 2t:
+//   W0 = lutA[A].x & 0xC000C000 = (t0, t1)    W1 = lutA[A].y = (t2, t3)
+//   W3 = lutB[B].x & 0xC000C000 = (t5, t6)    W4 = lutB[B].y = (t7, t8)
+//   W2 = perm(byte 0 of lutA[A].x, byte 2 of lutB[B].x) = (t4, t9)
+// (t4's code sits at bits 6..7 of lutA.x, t9's at bits 22..23 of lutB.x).
+// The activations of a byte pair are staged in the matching order
+// (x0,x1) (x2,x3) (x4,x9) (x5,x6) (x7,x8).
+__device__ void build_b3_entry(int v, uint2* lutA, uint2* lutB) {
+  uint2 a = make_uint2(0u, 0u), b = make_uint2(0u, 0u);
   if (v < 243) {
     int r = v;
     uint32_t c[5];
@@ -104,10 +122,10 @@ __device__ void build_b3_entry(int v, uint32_t* lutA, uint32_t* lutB) {
       c[i] = (uint32_t)((r % 3) - 1) & 3u;
       r /= 3;
     }
-    // first byte of a pair: t0 t1 t2 t3 t4 -> pair0 lo/hi, pair1 lo/hi, pair2 lo
-    a = (c[0] << 6) | (c[1] << 22) | (c[2] << 8) | (c[3] << 24) | (c[4] << 10);
-    // second byte: t5 t6 t7 t8 t9 -> pair2 hi, pair3 lo/hi, pair4 lo/hi
-    b = (c[0] << 26) | (c[1] << 12) | (c[2] << 28) | (c[3] << 14) | (c[4] << 30);
+    a.x = (c[0] << 14) | (c[1] << 30) | (c[4] << 6);
+    a.y = (c[2] << 14) | (c[3] << 30);
+    b.x = (c[0] << 14) | (c[1] << 30) | (c[4] << 22);
+    b.y = (c[2] << 14) | (c[3] << 30);
   }
   lutA[v] = a;
   lutB[v] = b;
@@ -117,8 +135,8 @@ __device__ void build_b3_entry(int v, uint32_t* lutA, uint32_t* lutB) {
 // lane's row at `my`, activations at `xs4` ([MT][XDW] dwords).
 template <int FMT, int G, int MT>
 __device__ __forceinline__ void stage_compute(const uint8_t* my, const u4_t* xs4, int ngs,
-                                              const float* sc, const uint32_t* lutA,
-                                              const uint32_t* lutB, float (&acc)[MT]) {
+                                              const float* sc, const uint2* lutA,
+                                              const uint2* lutB, float (&acc)[MT]) {
   using Gm = Geo<FMT, G>;
 #pragma unroll
   for (int j = 0; j < Gm::SG; ++j) {
@@ -166,27 +184,31 @@ __device__ __forceinline__ void stage_compute(const uint8_t* my, const u4_t* xs4
         u4_t xc[MT][5];
 #pragma unroll
         for (int bp = 0; bp < (GB + 1) / 2; ++bp) {
-          if (bp % 4 == 0) {  // activation pairs 5*bp .. 5*bp+19 of the group
+          if (bp % 4 == 0) {  // permuted activation dwords 5*bp .. 5*bp+19 of the group
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
               for (int c = 0; c < 5; ++c)
-                if (4 * (5 * bp / 4 + c) < G / 2) xc[m][c] = xs4[(m * Gm::XDW + j * (G / 2)) / 4 + 5 * bp / 4 + c];
+                if (4 * (5 * bp / 4 + c) < Gm::XGD) xc[m][c] = xs4[(m * Gm::XDW + j * Gm::XGD) / 4 + 5 * bp / 4 + c];
           }
           const int ia = sh + 2 * bp, ib = ia + 1;
-          const uint32_t ba = (dw[ia >> 2] >> ((ia & 3) * 8)) & 0xFFu;
-          uint32_t code = lutA[ba];
-          if (2 * bp + 1 < GB) {
-            const uint32_t bb = (dw[ib >> 2] >> ((ib & 3) * 8)) & 0xFFu;
-            code |= lutB[bb];
-          }
+          const uint2 wa = lutA[(dw[ia >> 2] >> ((ia & 3) * 8)) & 0xFFu];
+          uint2 wb = make_uint2(0u, 0u);
+          if (2 * bp + 1 < GB) wb = lutB[(dw[ib >> 2] >> ((ib & 3) * 8)) & 0xFFu];
+          uint32_t wv[5];
+          wv[0] = wa.x & 0xC000C000u;
+          wv[1] = wa.y;
+          wv[2] = __builtin_amdgcn_perm(wb.x, wa.x, 0x060C000Cu);
+          wv[3] = wb.x & 0xC000C000u;
+          wv[4] = wb.y;
+          // trit positions of the five words: (0,1) (2,3) (4,9) (5,6) (7,8)
+          constexpr int first[5] = {0, 2, 4, 5, 7};
 #pragma unroll
           for (int i = 0; i < 5; ++i) {
-            if (10 * bp + 2 * i < G) {
-              const uint32_t p = pair_of(code, 8 - 2 * i);
+            if (10 * bp + first[i] < G) {
               const int xi = 5 * bp + i - 20 * (bp / 4);  // index within the 5 chunks
 #pragma unroll
-              for (int m = 0; m < MT; ++m) part[m] = dot2(p, xc[m][xi / 4][xi % 4], part[m]);
+              for (int m = 0; m < MT; ++m) part[m] = dot2(wv[i], xc[m][xi / 4][xi % 4], part[m]);
             }
           }
         }
@@ -304,8 +326,8 @@ __global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __
   using Gm = Geo<FMT, G>;
   constexpr int WL = wave_lds_bytes<FMT, G, MT>();
   extern __shared__ uint4 stage_all[];  // per wave: [64 rows][PITCH] + activations of a stage
-  __shared__ uint32_t lutA[FMT == 1 ? 256 : 1];
-  __shared__ uint32_t lutB[FMT == 1 ? 256 : 1];
+  __shared__ uint2 lutA[FMT == 1 ? 256 : 1];
+  __shared__ uint2 lutB[FMT == 1 ? 256 : 1];
 
   GemvDesc d;
   if (ndesc > 0) d = descs[tile_desc[blockIdx.x]];
@@ -344,9 +366,13 @@ __global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __
   const int rows_here = min(kGemvRows, d.n - rb * kGemvRows);
   uint8_t* lds = reinterpret_cast<uint8_t*>(stage_all) + (size_t)wave * WL;
   const u4_t* xs4 = reinterpret_cast<const u4_t*>(lds + Gm::WBYTES);
+  uint32_t* xperm = reinterpret_cast<uint32_t*>(lds + Gm::WBYTES);
+  uint32_t* xnat = xperm + MT * Gm::XDW;  // base-3 only
   const uint8_t* my = lds + lane * Gm::PITCH;
 
-  // two register sets of prefetched stages: packed rows, scales, activations
+  // register sets of prefetched stages (packed rows, scales, activations):
+  // two stages in flight for 2-bit, one for base-3 (whose stages are larger)
+  constexpr int kDepth = FMT == 0 ? 2 : 1;
   u4_t preA[Gm::CHUNKS], preB[Gm::CHUNKS];
   uint16_t spA[Gm::SG], spB[Gm::SG];
   u4_t xpA[MT][Gm::XCH], xpB[MT][Gm::XCH];
@@ -371,6 +397,32 @@ __global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __
       }                                                                                      \
   } while (0)
 
+  // base-3: rebuild the stage's activations in byte-pair order (see the
+  // table above) from the natural-order copy at xnat
+#define TERN_STAGE_X_B3()                                                                    \
+  do {                                                                                       \
+    constexpr int NBP = (Gm::GB + 1) / 2;                                                    \
+    _Pragma("unroll") for (int r_ = 0; r_ < Gm::XBL; ++r_) {                                 \
+      const int t_ = r_ * kWave + lane;                                                      \
+      if (t_ < Gm::XBP) {                                                                    \
+        const int j_ = t_ / NBP, bp_ = t_ % NBP;                                             \
+        _Pragma("unroll") for (int m = 0; m < MT; ++m) {                                     \
+          uint32_t n_[5];                                                                    \
+          _Pragma("unroll") for (int c = 0; c < 5; ++c) {                                    \
+            const int k2_ = 5 * bp_ + c; /* natural dword within the group */                 \
+            n_[c] = k2_ < G / 2 ? xnat[m * Gm::XNAT + j_ * (G / 2) + k2_] : 0u;              \
+          }                                                                                  \
+          uint32_t* o_ = xperm + m * Gm::XDW + j_ * Gm::XGD + 5 * bp_;                       \
+          o_[0] = n_[0];                                                                     \
+          o_[1] = n_[1];                                                                     \
+          o_[2] = __builtin_amdgcn_perm(n_[4], n_[2], 0x07060100u); /* (x4, x9) */           \
+          o_[3] = __builtin_amdgcn_perm(n_[3], n_[2], 0x05040302u); /* (x5, x6) */           \
+          o_[4] = __builtin_amdgcn_perm(n_[4], n_[3], 0x05040302u); /* (x7, x8) */           \
+        }                                                                                    \
+      }                                                                                      \
+    }                                                                                        \
+  } while (0)
+
 #define TERN_CONSUME(P, SP, XP, i_)                                                          \
   do {                                                                                       \
     const int gs_ = ga + (wave + kWaves * (i_)) * Gm::SG;                                    \
@@ -383,22 +435,28 @@ __global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __
     }                                                                                        \
     _Pragma("unroll") for (int m = 0; m < MT; ++m)                                           \
       _Pragma("unroll") for (int i = 0; i < Gm::XCH; ++i)                                    \
-        *reinterpret_cast<u4_t*>(lds + Gm::WBYTES + (m * Gm::XDW + (i * kWave + lane) * 4) * 4) = XP[m][i]; \
+        *reinterpret_cast<u4_t*>((FMT == 1 ? xnat + m * Gm::XNAT : xperm + m * Gm::XDW) +     \
+                                 (i * kWave + lane) * 4) = XP[m][i];                         \
+    if (FMT == 1) {                                                                          \
+      wave_sync();                                                                           \
+      TERN_STAGE_X_B3();                                                                     \
+    }                                                                                        \
     float sc_[Gm::SG];                                                                       \
     _Pragma("unroll") for (int j = 0; j < Gm::SG; ++j) sc_[j] = 0.5f * h2f(SP[j]);          \
     wave_sync();                                                                             \
-    if ((i_) + 2 < nmine) TERN_LOAD(P, SP, XP, (i_) + 2);                                    \
+    if ((i_) + kDepth < nmine) TERN_LOAD(P, SP, XP, (i_) + kDepth);                          \
     stage_compute<FMT, G, MT>(my, xs4, ngs_, sc_, lutA, lutB, acc);                          \
   } while (0)
 
   if (nmine > 0) TERN_LOAD(preA, spA, xpA, 0);
-  if (nmine > 1) TERN_LOAD(preB, spB, xpB, 1);
-  for (int i = 0; i < nmine; i += 2) {
+  if (kDepth == 2 && nmine > 1) TERN_LOAD(preB, spB, xpB, 1);
+  for (int i = 0; i < nmine; i += kDepth) {
     TERN_CONSUME(preA, spA, xpA, i);
-    if (i + 1 < nmine) TERN_CONSUME(preB, spB, xpB, i + 1);
+    if (kDepth == 2 && i + 1 < nmine) TERN_CONSUME(preB, spB, xpB, i + 1);
   }
 #undef TERN_CONSUME
 #undef TERN_LOAD
+#undef TERN_STAGE_X_B3
 
   // ---- residual planes and offsets over this wave's share [ra, rz) of the groups
   const int rq = (gb - ga + kWaves - 1) / kWaves;

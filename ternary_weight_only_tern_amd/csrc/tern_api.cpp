@@ -122,6 +122,10 @@ bool product_group_ok(int group) { return group == 64 || group == 128; }
 
 int pick_mt(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8; }
 
+// Activation rows per decode pass: 8 for 2-bit, 4 for base-3 (whose LDS stage
+// would not fit four wavefronts at 8 rows).
+int max_mt(int format) { return format == TERN_FMT_B3 ? 4 : tern::kMaxMT; }
+
 void fill_desc(GemvDesc& d, const tern_matrix* w, const uint16_t* x, int m, void* y, int y_f32) {
   std::memset(&d, 0, sizeof(d));
   d.plane0 = w->plane0;
@@ -155,7 +159,7 @@ size_t gemv_ws_bytes(const tern_matrix* w, int m) {
   if (m <= 0 || w->n <= 0 || w->k <= 0 || !product_group_ok(w->group)) return 0;
   int splits, gps;
   choose_splits(w, &splits, &gps);
-  return split_ws_bytes(splits, std::min(m, tern::kMaxMT), w->n);
+  return split_ws_bytes(splits, std::min(m, max_mt(w->format)), w->n);
 }
 
 tern_status flag_status(uint32_t flag, bool unpacking) {
@@ -326,8 +330,9 @@ tern_status tern_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* 
   if (need && (!ws || ws_bytes < need)) return fail(TERN_E_WORKSPACE, "tern_gemv needs %zu workspace bytes", need);
   if (need) TERN_TRY(check_dev(ws, true, "ws"));
   const size_t esz = y_f32 ? 4 : 2;
-  for (int c0 = 0; c0 < m; c0 += tern::kMaxMT) {
-    const int mc = std::min(tern::kMaxMT, m - c0);
+  const int cmax = max_mt(w->format);
+  for (int c0 = 0; c0 < m; c0 += cmax) {
+    const int mc = std::min(cmax, m - c0);
     GemvDesc dc = d;
     dc.x = x + (size_t)c0 * w->k;
     dc.y = static_cast<char*>(y) + (size_t)c0 * w->n * esz;
@@ -374,7 +379,8 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
   out->clear();
   tiles->clear();
   *total = 0;
-  *mt = pick_mt(std::min(m, tern::kMaxMT));
+  const int cmax = count > 0 ? max_mt(w[0].format) : tern::kMaxMT;
+  *mt = pick_mt(std::min(m, cmax));
   std::vector<int> order;
   for (int i = 0; i < count; ++i) {
     TERN_TRY(check_matrix(&w[i]));
@@ -389,9 +395,9 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return w[a].k > w[b].k; });
   const size_t esz = y_dtype == TERN_F32 ? 4 : 2;
   for (int i : order) {
-    for (int c0 = 0; c0 < m; c0 += tern::kMaxMT) {
+    for (int c0 = 0; c0 < m; c0 += cmax) {
       GemvDesc d;
-      fill_desc(d, &w[i], x[i] + (size_t)c0 * w[i].k, std::min(tern::kMaxMT, m - c0),
+      fill_desc(d, &w[i], x[i] + (size_t)c0 * w[i].k, std::min(cmax, m - c0),
                 static_cast<char*>(y[i]) + (size_t)c0 * w[i].n * esz, y_dtype == TERN_F32);
       d.tile_begin = *total;
       *total += d.row_blocks;
@@ -408,7 +414,8 @@ static size_t batch_tiles_offset(size_t ndesc) { return round_up(ndesc * sizeof(
 
 size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m) {
   if (count <= 0 || m <= 0 || !w) return 0;
-  const size_t chunks = (size_t)(m + tern::kMaxMT - 1) / tern::kMaxMT;
+  const int cmax = max_mt(w[0].format);
+  const size_t chunks = (size_t)(m + cmax - 1) / cmax;
   size_t tiles = 0;
   for (int i = 0; i < count; ++i) tiles += (size_t)std::max(0, (w[i].n + tern::kGemvRows - 1) / tern::kGemvRows) * chunks;
   return batch_tiles_offset((size_t)count * chunks) + round_up(tiles * sizeof(uint16_t), 256);
