@@ -274,7 +274,7 @@ def main():
                    "weights_per_step": r["weights"]},
         "roofline": {"bound": "hbm", "achieved": round(r["launch_gbs"], 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(r["launch_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gemv_kernel (2-bit, G=128, MT=1): one grouped launch per layer",
+                     "kernel": "gemv_mfma_kernel<128,1> (2-bit, G=128, M=1): one grouped launch per layer",
                      "launch_us": round(r["launch_s"] * 1e6, 3),
                      "bytes_per_launch": r["layer_bytes"]},
         "cpu_baseline": cpu,

@@ -320,9 +320,8 @@ __device__ __forceinline__ void residual_compact(const GemvDesc& d, int p, int r
 }
 
 template <int FMT, int G, int MT>
-__global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __restrict__ descs,
-                                                              const uint16_t* __restrict__ tile_desc,
-                                                              int ndesc, GemvDesc one) {
+__global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __restrict__ descs, int ndesc,
+                                                              GemvDesc one) {
   using Gm = Geo<FMT, G>;
   constexpr int WL = wave_lds_bytes<FMT, G, MT>();
   extern __shared__ uint4 stage_all[];  // per wave: [64 rows][PITCH] + activations of a stage
@@ -330,7 +329,7 @@ __global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __
   __shared__ uint2 lutB[FMT == 1 ? 256 : 1];
 
   GemvDesc d;
-  if (ndesc > 0) d = descs[tile_desc[blockIdx.x]];
+  if (ndesc > 0) d = descs[blockIdx.x];
   else d = one;
   const int item = (int)blockIdx.x - d.tile_begin;
   const int rb = item % d.row_blocks;
@@ -522,22 +521,20 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ partial, int spli
 }
 
 template <int FMT, int G, int MT>
-hipError_t launch_one(const GemvDesc* descs, const uint16_t* tile_desc, int ndesc, const GemvDesc& one,
-                      int items, hipStream_t s) {
+hipError_t launch_one(const GemvDesc* descs, int ndesc, const GemvDesc& one, int items, hipStream_t s) {
   const size_t lds = (size_t)kWaves * wave_lds_bytes<FMT, G, MT>();
-  hipLaunchKernelGGL((gemv_kernel<FMT, G, MT>), dim3(items), dim3(kWave * kWaves), lds, s, descs,
-                     tile_desc, ndesc, one);
+  hipLaunchKernelGGL((gemv_kernel<FMT, G, MT>), dim3(items), dim3(kWave * kWaves), lds, s, descs, ndesc, one);
   return hipGetLastError();
 }
 
 template <int FMT, int G>
-hipError_t launch_fmt_g(int mt, const GemvDesc* descs, const uint16_t* tile_desc, int ndesc,
-                        const GemvDesc& one, int items, hipStream_t s) {
+hipError_t launch_fmt_g(int mt, const GemvDesc* descs, int ndesc, const GemvDesc& one, int items,
+                        hipStream_t s) {
   switch (mt) {
-    case 1: return launch_one<FMT, G, 1>(descs, tile_desc, ndesc, one, items, s);
-    case 2: return launch_one<FMT, G, 2>(descs, tile_desc, ndesc, one, items, s);
-    case 4: return launch_one<FMT, G, 4>(descs, tile_desc, ndesc, one, items, s);
-    case 8: return launch_one<FMT, G, 8>(descs, tile_desc, ndesc, one, items, s);
+    case 1: return launch_one<FMT, G, 1>(descs, ndesc, one, items, s);
+    case 2: return launch_one<FMT, G, 2>(descs, ndesc, one, items, s);
+    case 4: return launch_one<FMT, G, 4>(descs, ndesc, one, items, s);
+    case 8: return launch_one<FMT, G, 8>(descs, ndesc, one, items, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -559,13 +556,13 @@ hipError_t launch_splitk_reduce(const float* partial, int splits, int m, int n, 
   return hipGetLastError();
 }
 
-hipError_t launch_gemv(int format, int group, int mt, const GemvDesc* descs, const uint16_t* tile_desc,
-                       int ndesc, const GemvDesc& one, int total_items, hipStream_t s) {
+hipError_t launch_gemv(int format, int group, int mt, const GemvDesc* descs, int ndesc, const GemvDesc& one,
+                       int total_items, hipStream_t s) {
   if (total_items <= 0) return hipSuccess;
-  if (format == 0 && group == 64) return launch_fmt_g<0, 64>(mt, descs, tile_desc, ndesc, one, total_items, s);
-  if (format == 0 && group == 128) return launch_fmt_g<0, 128>(mt, descs, tile_desc, ndesc, one, total_items, s);
-  if (format == 1 && group == 64) return launch_fmt_g<1, 64>(mt, descs, tile_desc, ndesc, one, total_items, s);
-  if (format == 1 && group == 128) return launch_fmt_g<1, 128>(mt, descs, tile_desc, ndesc, one, total_items, s);
+  if (format == 0 && group == 64) return launch_fmt_g<0, 64>(mt, descs, ndesc, one, total_items, s);
+  if (format == 0 && group == 128) return launch_fmt_g<0, 128>(mt, descs, ndesc, one, total_items, s);
+  if (format == 1 && group == 64) return launch_fmt_g<1, 64>(mt, descs, ndesc, one, total_items, s);
+  if (format == 1 && group == 128) return launch_fmt_g<1, 128>(mt, descs, ndesc, one, total_items, s);
   return hipErrorInvalidValue;
 }
 

@@ -31,25 +31,36 @@ struct GemvDesc {
   int32_t mwords;         // mask words per row
   int32_t splits;         // K splits (work items along K)
   int32_t gps;            // groups per split
-  int32_t row_blocks;     // ceil(n / kGemvRows)
+  int32_t row_blocks;     // work items along the rows: ceil(n / rows per item)
   int32_t tile_begin;     // first work-item index of this descriptor in the grid
   int32_t y_f32;          // 1: y is fp32, 0: fp16
+  int32_t kwaves;         // matrix-core kernel: wavefronts sharing one 16-row tile's K (1, 2, 4)
 };
 
 // ---- decode products (gemv.hip)
-// Launches the lane-per-row decode kernel over `ndesc` descriptors stored in
-// device memory (`descs`), or over the single descriptor `one` when ndesc == 0.
-// total_items = sum over descriptors of splits * row_blocks.  Descriptors
+// Launches the lane-per-row decode kernel over total_items work items: with
+// ndesc > 0, descs (device memory) holds one descriptor per work item (the
+// descriptor of the matrix the item belongs to, whose tile_begin is the
+// matrix's first item); with ndesc == 0 every item uses `one`.  Descriptors
 // with splits > 1 write FP32 partials; launch_splitk_reduce then sums them.
-// tile_desc[i] is the descriptor index of work item i (device, used when ndesc > 0).
-hipError_t launch_gemv(int format, int group, int mt, const GemvDesc* descs,
-                       const uint16_t* tile_desc, int ndesc, const GemvDesc& one, int total_items,
-                       hipStream_t stream);
+hipError_t launch_gemv(int format, int group, int mt, const GemvDesc* descs, int ndesc, const GemvDesc& one,
+                       int total_items, hipStream_t stream);
 // y[m][n] = sum_s partial[s][m][n] in split order.
 hipError_t launch_splitk_reduce(const float* partial, int splits, int m, int n, void* y,
                                 int y_f32, hipStream_t stream);
 // Groups per LDS stage of the decode kernel; K splits start on multiples of it.
 int gemv_stage_groups(int format, int group);
+
+// ---- matrix-core decode product for 2-bit planes (gemv_mfma.hip)
+// Activation rows per pass (8 for group 128, 4 for group 64) and the longest
+// K range (trits) one work item stages, for `mp` padded activation rows.
+int gemv_mfma_max_rows(int group);
+int gemv_mfma_max_range(int mp);
+// Same descriptors and work items as launch_gemv; a work item is 64 / kwaves
+// rows; K splits start on 256-trit blocks.  max_krp = the longest range of
+// any descriptor rounded up to 256; offsets = some descriptor has an offset.
+hipError_t launch_gemv_mfma(int group, int mp, const GemvDesc* descs, int ndesc, const GemvDesc& one,
+                            int total_items, int max_krp, bool offsets, hipStream_t stream);
 
 // ---- MFMA product (gemm.hip)
 hipError_t launch_gemm(const GemvDesc& d, int format, hipStream_t stream);

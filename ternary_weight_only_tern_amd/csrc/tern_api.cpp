@@ -92,24 +92,58 @@ tern_status check_matrix(const tern_matrix* w) {
   return TERN_OK;
 }
 
-// Split of K into `want` parts (at most one per LDS stage of groups); split
-// boundaries fall on stage multiples.
-void split_k(const tern_matrix* w, int want, int* splits, int* gps) {
+// 2-bit products run on the matrix-core kernel, base-3 on the lane-per-row one.
+bool use_mfma(int format) { return format == TERN_FMT_2BIT; }
+
+int pick_mt(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8; }
+
+// Activation rows per decode pass: 2-bit 8 (group 128) or 4 (group 64);
+// base-3 4 (its LDS stage would not fit four wavefronts at 8 rows).
+int max_mt(int format, int group) {
+  return use_mfma(format) ? tern::gemv_mfma_max_rows(group) : 4;
+}
+
+// Groups on which K splits may start.
+int split_quantum(int format, int group) {
+  return use_mfma(format) ? std::max(1, 256 / group) : tern::gemv_stage_groups(format, group);
+}
+
+// Split of K into about `want` parts whose boundaries fall on split quanta;
+// on the matrix-core kernel no part is longer than its activation stage.
+void split_k(const tern_matrix* w, int want, int mp, int* splits, int* gps) {
   const int ng = w->k / w->group;
-  const int sg = tern::gemv_stage_groups(w->format, w->group);
+  const int sg = split_quantum(w->format, w->group);
   const int max_splits = std::max(1, (ng + sg - 1) / sg);
   const int s = std::min(max_splits, std::max(1, want));
   int g = (ng + s - 1) / s;
   g = (g + sg - 1) / sg * sg;
   g = std::max(g, sg);
+  if (use_mfma(w->format)) {
+    const int cap = std::max(sg, tern::gemv_mfma_max_range(mp) / w->group / sg * sg);
+    g = std::min(g, cap);
+  }
   *gps = g;
   *splits = std::max(1, (ng + g - 1) / g);
 }
 
+// Wavefronts sharing one 16-row tile's K on the matrix-core kernel: the
+// fewest (1, 2 or 4) that keep each one's 256-trit blocks near `ref`, so that
+// long-K matrices of a batch finish with the short ones.
+int choose_kwaves(int format, int k, int ref) {
+  if (!use_mfma(format)) return 1;
+  const int nblk = (k + 255) / 256, cap = std::max(ref, 12);
+  int kw = 1;
+  while (kw < 4 && (nblk + kw - 1) / kw > cap) kw *= 2;
+  return kw;
+}
+
+int rows_per_item(int kwaves) { return tern::kGemvRows / kwaves; }
+
 // Single decode product: enough work items (row blocks x splits) to fill the GPU.
-void choose_splits(const tern_matrix* w, int* splits, int* gps) {
-  const int rb = std::max(1, (w->n + tern::kGemvRows - 1) / tern::kGemvRows);
-  split_k(w, (kTargetItems + rb - 1) / rb, splits, gps);
+void choose_splits(const tern_matrix* w, int mp, int* splits, int* gps) {
+  const int rpi = rows_per_item(choose_kwaves(w->format, w->k, 12));
+  const int rb = std::max(1, (w->n + rpi - 1) / rpi);
+  split_k(w, (kTargetItems + rb - 1) / rb, mp, splits, gps);
 }
 
 // Workspace of one split product: FP32 partials [splits][m][n].
@@ -120,11 +154,14 @@ size_t split_ws_bytes(int splits, int m, int n) {
 
 bool product_group_ok(int group) { return group == 64 || group == 128; }
 
-int pick_mt(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8; }
+int round256(int v) { return (v + 255) / 256 * 256; }
 
-// Activation rows per decode pass: 8 for 2-bit, 4 for base-3 (whose LDS stage
-// would not fit four wavefronts at 8 rows).
-int max_mt(int format) { return format == TERN_FMT_B3 ? 4 : tern::kMaxMT; }
+// Decode launch over descriptors (device table) or the single descriptor `one`.
+hipError_t launch_decode(int format, int group, int mt, const GemvDesc* descs, int ndesc, const GemvDesc& one,
+                         int items, int max_krp, bool offsets, hipStream_t s) {
+  if (use_mfma(format)) return tern::launch_gemv_mfma(group, mt, descs, ndesc, one, items, max_krp, offsets, s);
+  return tern::launch_gemv(format, group, mt, descs, ndesc, one, items, s);
+}
 
 void fill_desc(GemvDesc& d, const tern_matrix* w, const uint16_t* x, int m, void* y, int y_f32) {
   std::memset(&d, 0, sizeof(d));
@@ -153,13 +190,20 @@ void fill_desc(GemvDesc& d, const tern_matrix* w, const uint16_t* x, int m, void
   d.gps = d.ng;
   d.row_blocks = (w->n + tern::kGemvRows - 1) / tern::kGemvRows;
   d.y_f32 = y_f32;
+  d.kwaves = 1;
+}
+
+void set_kwaves(GemvDesc& d, int kw) {
+  d.kwaves = kw;
+  d.row_blocks = (d.n + rows_per_item(kw) - 1) / rows_per_item(kw);
 }
 
 size_t gemv_ws_bytes(const tern_matrix* w, int m) {
   if (m <= 0 || w->n <= 0 || w->k <= 0 || !product_group_ok(w->group)) return 0;
+  const int mc = std::min(m, max_mt(w->format, w->group));
   int splits, gps;
-  choose_splits(w, &splits, &gps);
-  return split_ws_bytes(splits, std::min(m, max_mt(w->format)), w->n);
+  choose_splits(w, pick_mt(mc), &splits, &gps);
+  return split_ws_bytes(splits, mc, w->n);
 }
 
 tern_status flag_status(uint32_t flag, bool unpacking) {
@@ -185,11 +229,11 @@ tern_status check_xy(const uint16_t* x, void* y, int y_dtype) {
 }  // namespace
 
 struct tern_plan {
-  const GemvDesc* dev;
-  const uint16_t* tiles;
-  int ndesc;
+  const GemvDesc* dev;    // one descriptor per work item
   int total_items;
   int format, group, mt;
+  int max_krp;
+  bool offsets;
 };
 
 extern "C" {
@@ -324,13 +368,14 @@ tern_status tern_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* 
     TERN_HIP(tern::launch_gemm(d, w->format, s));  // ng == 0: zero fill
     return TERN_OK;
   }
+  const int cmax = max_mt(w->format, w->group);
   int splits, gps;
-  choose_splits(w, &splits, &gps);
+  choose_splits(w, pick_mt(std::min(m, cmax)), &splits, &gps);
   const size_t need = gemv_ws_bytes(w, m);
   if (need && (!ws || ws_bytes < need)) return fail(TERN_E_WORKSPACE, "tern_gemv needs %zu workspace bytes", need);
   if (need) TERN_TRY(check_dev(ws, true, "ws"));
   const size_t esz = y_f32 ? 4 : 2;
-  const int cmax = max_mt(w->format);
+  set_kwaves(d, choose_kwaves(w->format, w->k, 12));
   for (int c0 = 0; c0 < m; c0 += cmax) {
     const int mc = std::min(cmax, m - c0);
     GemvDesc dc = d;
@@ -342,7 +387,8 @@ tern_status tern_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* 
     if (splits > 1) dc.partial = static_cast<float*>(ws);
     dc.tile_begin = 0;
     const int items = splits * dc.row_blocks;
-    TERN_HIP(tern::launch_gemv(w->format, w->group, pick_mt(mc), nullptr, nullptr, 0, dc, items, s));
+    TERN_HIP(launch_decode(w->format, w->group, pick_mt(std::min(m, cmax)), nullptr, 0, dc, items,
+                           round256(gps * w->group), w->offset_mode != TERN_OFF_NONE, s));
     if (splits > 1) TERN_HIP(tern::launch_splitk_reduce(dc.partial, splits, mc, w->n, dc.y, y_f32, s));
   }
   return TERN_OK;
@@ -364,24 +410,22 @@ tern_status tern_gemm(const tern_matrix* w, const uint16_t* x, int32_t m, void* 
 }
 
 // ---- grouped decode
-// Descriptors of a batch: one per (matrix, block of <= 8 activation rows),
-// longest K first; every descriptor covers its whole K (the four wavefronts
-// of a workgroup split it).  `ws` holds the descriptor table.
+// A batch launch reads one descriptor per work item: the descriptor of the
+// (matrix, block of activation rows) the item belongs to, longest K first.
+// Every descriptor covers its whole K (no split across workgroups).
 static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y,
-                               int32_t count, int32_t m, int32_t y_dtype,
-                               std::vector<GemvDesc>* out, std::vector<uint16_t>* tiles, int* total,
-                               int* mt) {
+                               int32_t count, int32_t m, int32_t y_dtype, std::vector<GemvDesc>* items,
+                               int* mt, int* max_krp, bool* offsets) {
   if (count < 0) return fail(TERN_E_INVAL, "count=%d is negative", count);
   if (count > 0 && (!w || !x || !y)) return fail(TERN_E_INVAL, "NULL descriptor arrays");
   if (m < 0) return fail(TERN_E_INVAL, "m=%d is negative", m);
   if (m >= 64) return fail(TERN_E_UNSUPPORTED, "batched decode takes m <= 63 (got %d)", m);
   if (y_dtype != TERN_F16 && y_dtype != TERN_F32) return fail(TERN_E_UNSUPPORTED, "unknown y dtype %d", y_dtype);
-  out->clear();
-  tiles->clear();
-  *total = 0;
-  const int cmax = count > 0 ? max_mt(w[0].format) : tern::kMaxMT;
-  *mt = pick_mt(std::min(m, cmax));
+  items->clear();
+  *max_krp = 0;
+  *offsets = false;
   std::vector<int> order;
+  int kmax = 0, nblk_min = 1 << 30;
   for (int i = 0; i < count; ++i) {
     TERN_TRY(check_matrix(&w[i]));
     if (w[i].format != w[0].format || w[i].group != w[0].group)
@@ -391,7 +435,17 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
     if (w[i].k == 0) return fail(TERN_E_UNSUPPORTED, "batched decode needs k > 0");
     TERN_TRY(check_xy(x[i], y[i], y_dtype));
     order.push_back(i);
+    kmax = std::max(kmax, w[i].k);
+    nblk_min = std::min(nblk_min, (w[i].k + 255) / 256);
   }
+  int cmax = count > 0 ? max_mt(w[0].format, w[0].group) : 1;
+  if (count > 0 && use_mfma(w[0].format)) {
+    // every descriptor covers its whole K, which the activation stage must hold
+    if (round256(kmax) > tern::gemv_mfma_max_range(1))
+      return fail(TERN_E_UNSUPPORTED, "batched 2-bit decode takes k <= %d (got %d)", tern::gemv_mfma_max_range(1), kmax);
+    while (cmax > 1 && round256(kmax) > tern::gemv_mfma_max_range(cmax)) cmax /= 2;
+  }
+  *mt = pick_mt(std::min(std::max(m, 1), cmax));
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return w[a].k > w[b].k; });
   const size_t esz = y_dtype == TERN_F32 ? 4 : 2;
   for (int i : order) {
@@ -399,47 +453,52 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
       GemvDesc d;
       fill_desc(d, &w[i], x[i] + (size_t)c0 * w[i].k, std::min(cmax, m - c0),
                 static_cast<char*>(y[i]) + (size_t)c0 * w[i].n * esz, y_dtype == TERN_F32);
-      d.tile_begin = *total;
-      *total += d.row_blocks;
-      if (out->size() >= 65535) return fail(TERN_E_UNSUPPORTED, "batch has more than 65535 descriptors");
-      tiles->insert(tiles->end(), (size_t)d.row_blocks, (uint16_t)out->size());
-      out->push_back(d);
+      set_kwaves(d, choose_kwaves(w[i].format, w[i].k, nblk_min));
+      d.tile_begin = (int)items->size();
+      if ((size_t)d.tile_begin + d.row_blocks > (size_t)INT32_MAX) return fail(TERN_E_UNSUPPORTED, "batch too large");
+      items->insert(items->end(), (size_t)d.row_blocks, d);
+      *max_krp = std::max(*max_krp, round256(w[i].k));
+      *offsets = *offsets || w[i].offset_mode != TERN_OFF_NONE;
     }
   }
   return TERN_OK;
 }
 
-// Workspace layout of a batch: [descriptor table][work item -> descriptor index].
-static size_t batch_tiles_offset(size_t ndesc) { return round_up(ndesc * sizeof(GemvDesc), 256); }
-
 size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m) {
   if (count <= 0 || m <= 0 || !w) return 0;
-  const int cmax = max_mt(w[0].format);
+  int cmax = max_mt(w[0].format, w[0].group), kmax = 0, nblk_min = 1 << 30;
+  for (int i = 0; i < count; ++i) {
+    if (w[i].n <= 0 || w[i].k <= 0) continue;
+    kmax = std::max(kmax, w[i].k);
+    nblk_min = std::min(nblk_min, (w[i].k + 255) / 256);
+  }
+  if (use_mfma(w[0].format))
+    while (cmax > 1 && round256(kmax) > tern::gemv_mfma_max_range(cmax)) cmax /= 2;
   const size_t chunks = (size_t)(m + cmax - 1) / cmax;
-  size_t tiles = 0;
-  for (int i = 0; i < count; ++i) tiles += (size_t)std::max(0, (w[i].n + tern::kGemvRows - 1) / tern::kGemvRows) * chunks;
-  return batch_tiles_offset((size_t)count * chunks) + round_up(tiles * sizeof(uint16_t), 256);
+  size_t items = 0;
+  for (int i = 0; i < count; ++i) {
+    if (w[i].n <= 0 || w[i].k <= 0) continue;
+    const int rpi = rows_per_item(choose_kwaves(w[i].format, w[i].k, nblk_min));
+    items += (size_t)((w[i].n + rpi - 1) / rpi) * chunks;
+  }
+  return round_up(items * sizeof(GemvDesc), 256);
 }
 
 tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, void* const* y,
                               int32_t count, int32_t m, int32_t y_dtype, void* ws, size_t ws_bytes,
                               void* stream) {
-  std::vector<GemvDesc> descs;
-  std::vector<uint16_t> tiles;
-  int total = 0, mt = 1;
-  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &descs, &tiles, &total, &mt));
-  if (descs.empty()) return TERN_OK;
-  const size_t toff = batch_tiles_offset(descs.size());
-  const size_t need = toff + tiles.size() * sizeof(uint16_t);
+  std::vector<GemvDesc> items;
+  int mt = 1, max_krp = 0;
+  bool offsets = false;
+  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets));
+  if (items.empty()) return TERN_OK;
+  const size_t need = items.size() * sizeof(GemvDesc);
   if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "batched decode needs %zu workspace bytes", need);
   TERN_TRY(check_dev(ws, true, "ws"));
   hipStream_t s = (hipStream_t)stream;
-  char* base = static_cast<char*>(ws);
-  TERN_HIP(hipMemcpyAsync(base, descs.data(), descs.size() * sizeof(GemvDesc), hipMemcpyHostToDevice, s));
-  TERN_HIP(hipMemcpyAsync(base + toff, tiles.data(), tiles.size() * sizeof(uint16_t), hipMemcpyHostToDevice, s));
-  TERN_HIP(tern::launch_gemv(w[0].format, w[0].group, mt, reinterpret_cast<const GemvDesc*>(base),
-                             reinterpret_cast<const uint16_t*>(base + toff), (int)descs.size(), descs[0],
-                             total, s));
+  TERN_HIP(hipMemcpyAsync(ws, items.data(), need, hipMemcpyHostToDevice, s));
+  TERN_HIP(launch_decode(w[0].format, w[0].group, mt, static_cast<const GemvDesc*>(ws), (int)items.size(),
+                         items[0], (int)items.size(), max_krp, offsets, s));
   return TERN_OK;
 }
 
@@ -448,39 +507,36 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
                              tern_plan** out) {
   if (!out) return fail(TERN_E_INVAL, "out is NULL");
   *out = nullptr;
-  std::vector<GemvDesc> descs;
-  std::vector<uint16_t> tiles;
-  int total = 0, mt = 1;
-  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &descs, &tiles, &total, &mt));
-  const size_t toff = batch_tiles_offset(descs.size());
-  if (!descs.empty()) {
-    const size_t need = toff + tiles.size() * sizeof(uint16_t);
+  std::vector<GemvDesc> items;
+  int mt = 1, max_krp = 0;
+  bool offsets = false;
+  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets));
+  if (!items.empty()) {
+    const size_t need = items.size() * sizeof(GemvDesc);
     if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "plan needs %zu workspace bytes", need);
     TERN_TRY(check_dev(ws, true, "ws"));
-    char* base = static_cast<char*>(ws);
-    TERN_HIP(hipMemcpy(base, descs.data(), descs.size() * sizeof(GemvDesc), hipMemcpyHostToDevice));
-    TERN_HIP(hipMemcpy(base + toff, tiles.data(), tiles.size() * sizeof(uint16_t), hipMemcpyHostToDevice));
+    TERN_HIP(hipMemcpy(ws, items.data(), need, hipMemcpyHostToDevice));
   }
   tern_plan* p = static_cast<tern_plan*>(std::malloc(sizeof(tern_plan)));
   if (!p) return fail(TERN_E_INVAL, "out of host memory");
   p->dev = static_cast<const GemvDesc*>(ws);
-  p->tiles = reinterpret_cast<const uint16_t*>(static_cast<const char*>(ws) + toff);
-  p->ndesc = (int)descs.size();
-  p->total_items = total;
+  p->total_items = (int)items.size();
   p->format = count > 0 ? w[0].format : 0;
   p->group = count > 0 ? w[0].group : 128;
   p->mt = mt;
+  p->max_krp = max_krp;
+  p->offsets = offsets;
   *out = p;
   return TERN_OK;
 }
 
 tern_status tern_plan_run(const tern_plan* plan, void* stream) {
   if (!plan) return fail(TERN_E_INVAL, "plan is NULL");
-  if (plan->ndesc == 0) return TERN_OK;
+  if (plan->total_items == 0) return TERN_OK;
   GemvDesc dummy;
   std::memset(&dummy, 0, sizeof(dummy));
-  TERN_HIP(tern::launch_gemv(plan->format, plan->group, plan->mt, plan->dev, plan->tiles, plan->ndesc,
-                             dummy, plan->total_items, (hipStream_t)stream));
+  TERN_HIP(launch_decode(plan->format, plan->group, plan->mt, plan->dev, plan->total_items, dummy,
+                         plan->total_items, plan->max_krp, plan->offsets, (hipStream_t)stream));
   return TERN_OK;
 }
 
