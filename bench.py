@@ -38,6 +38,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+PROFILE = os.path.join(ROOT, "profiles", "gemv_mfma_2bit_qwen3_4b_layer_m1.txt")
+
+
+def profiled_traffic(path=PROFILE):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the
+    summary is missing or was taken on a different kernel source."""
+    import hashlib
+    try:
+        fields = dict(l.split(":", 1) for l in open(path) if ":" in l and not l.startswith(" "))
+        sha, src = fields["kernel_source_sha256"].split()[0], fields["kernel_source_sha256"].split("(")[1].rstrip(")\n ")
+        if hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest() != sha:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, IndexError, ValueError):
+        return None
+
+
 def clone_packed(pm):
     from ternary_weight_only_tern_amd import lib as L
     c = L.PackedMatrix.__new__(L.PackedMatrix)
@@ -73,11 +91,33 @@ def x_for(cfg, proj, m, layer=0):
     return torch.from_numpy(x.view(np.uint16)).cuda().view(torch.float16), x
 
 
+EAGER = False  # --eager: launch the steps directly instead of replaying a graph
+
+
+def time_eager(step_fns, steps, warmup, stream):
+    import torch
+    per = len(step_fns)
+    with torch.cuda.stream(stream):
+        for i in range(max(warmup, per)):
+            step_fns[i % per]()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        s.record(stream)
+        for i in range(steps):
+            step_fns[i % per]()
+        e.record(stream)
+        torch.cuda.synchronize()
+    return time.perf_counter() - t0, s.elapsed_time(e) / 1e3, None
+
+
 def time_graph(step_fns, steps, warmup, stream):
     """Capture one call of every step function into a HIP graph, replay it so
     that exactly `steps` steps run; returns (total seconds, per-step seconds
     from events around each replayed step group)."""
     import torch
+    if EAGER:
+        return time_eager(step_fns, steps, warmup, stream)
     per = len(step_fns)
     assert steps % per == 0, "steps must be a multiple of the rotation length"
     g = torch.cuda.CUDAGraph()
@@ -219,6 +259,9 @@ def main():
     ap.add_argument("--fmt", choices=["2bit", "b3"], default="2bit")
     ap.add_argument("--skip-extra", action="store_true", help="only the headline measurement")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="direct launches instead of graph replay (profiling)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device copy 8 times (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -227,6 +270,16 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("bench: copied 8 x 256 MiB")
+        return
+    global EAGER
+    EAGER = args.eager
     from ternary_weight_only_tern_amd import lib as L
     L.load()
     torch.cuda.set_device(0)
@@ -273,7 +326,7 @@ def main():
                    "format": args.fmt, "group": 128, "residual_frac": 0.10, "layer_bytes": r["layer_bytes"],
                    "weights_per_step": r["weights"]},
         "roofline": {"bound": "hbm", "achieved": round(r["launch_gbs"], 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(r["launch_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(r["launch_gbs"] / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(),
                      "kernel": "gemv_mfma_kernel<128,1> (2-bit, G=128, M=1): one grouped launch per layer",
                      "launch_us": round(r["launch_s"] * 1e6, 3),
                      "bytes_per_launch": r["layer_bytes"]},
