@@ -53,7 +53,7 @@ constexpr int kRowsWave = 16;      // output rows per wavefront (MFMA N)
 constexpr int kBlockTrits = 256;   // trits per block: 4 lanes x 64 trits of one row
 constexpr int kDepth = 8;          // blocks in flight per lane
 constexpr int kZeroBytes = 128;    // zero A operands for inactive slots
-constexpr int kResCap = 128;       // residual entries listed per pass and wavefront
+constexpr int kResCap = 64;        // residual entries listed per pass and wavefront
 
 template <typename T>
 __device__ __forceinline__ const GLOBAL T* gp(const T* p) { return (const GLOBAL T*)p; }
@@ -175,7 +175,7 @@ template <int MP>
 constexpr int res_wave_bytes() { return kResCap * 8 + kResCap * MP * 4; }
 
 template <int G, int MP>
-__global__ __launch_bounds__(kWave * kWaves) __attribute__((amdgpu_waves_per_eu(MP == 1 || MP == 8 ? 2 : 3, 8)))
+__global__ __launch_bounds__(kWave * kWaves) __attribute__((amdgpu_waves_per_eu(MP == 8 || (G == 64 && MP == 4) ? 2 : 3, 8)))
 void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc one) {
   constexpr int GW = Win<MP>::GW;
   constexpr int NACC = Win<MP>::NACC;
@@ -372,7 +372,7 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
   float acc[NACC];
 #pragma unroll
   for (int i = 0; i < NACC; ++i) acc[i] = 0.f;
-  f4_t D = {0.f, 0.f, 0.f, 0.f};
+  f4_t D = {0.f, 0.f, 0.f, 0.f}, E = {0.f, 0.f, 0.f, 0.f};  // even / odd MFMAs of a block
   // this row's scales from the part's first group on
   const uint16_t* my_sc = reinterpret_cast<const uint16_t*>(lds + scoff) + (sflat ? sshift : 0) +
                           (tile * kRowsWave + r) * spitch + (pga - (sflat ? 0 : ga));
@@ -389,8 +389,11 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
     h8_t b_[8];                                                                               \
     decode_two((V).x, (V).y, &b_[0]);                                                         \
     decode_two((V).z, (V).w, &b_[4]);                                                         \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                             \
+    _Pragma("unroll") for (int j = 0; j < 8; j += 2) {                                        \
       D = __builtin_amdgcn_mfma_f32_16x16x32_f16(lds_h8(lds, aoff_ + 16u * j), b_[j], D, 0, 0, 0); \
+      E = __builtin_amdgcn_mfma_f32_16x16x32_f16(lds_h8(lds, aoff_ + 16u * (j + 1)), b_[j + 1], E, 0, 0, 0); \
+    }                                                                                         \
+    __builtin_amdgcn_sched_barrier(0); /* one block's operands live at a time */              \
   } while (0)
   // close window wi: scale the slot sums, start the next window
 #define TERN_CLOSE(WI)                                                                        \
@@ -398,8 +401,9 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
     float sc_[4];                                                                             \
     window_scales<GW>(my_sc, (WI) * GW, ngp, dm, row_ok, q, sc_);                             \
     _Pragma("unroll") for (int v = 0; v < 4; ++v)                                             \
-      acc[NACC == 2 ? v / 2 : 0] = fmaf(sc_[v], D[v], acc[NACC == 2 ? v / 2 : 0]);            \
+      acc[NACC == 2 ? v / 2 : 0] = fmaf(sc_[v], D[v] + E[v], acc[NACC == 2 ? v / 2 : 0]);     \
     D = f4_t{0.f, 0.f, 0.f, 0.f};                                                             \
+    E = f4_t{0.f, 0.f, 0.f, 0.f};                                                             \
   } while (0)
 
   // Blocks in groups of kDepth: the next group's loads are issued before the
