@@ -35,6 +35,8 @@
 // sum.  Rows add their entries' scaled values in entry order.  Offsets use
 // per-group activation sums computed once per workgroup.  All sums are in a
 // fixed order, so results are bitwise reproducible.
+#include <algorithm>
+
 #include "internal.h"
 
 #define GLOBAL __attribute__((address_space(1)))
@@ -51,9 +53,10 @@ typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;          // wavefronts per workgroup
 constexpr int kRowsWave = 16;      // output rows per wavefront (MFMA N)
 constexpr int kBlockTrits = 256;   // trits per block: 4 lanes x 64 trits of one row
-constexpr int kDepth = 8;          // blocks in flight per lane
+constexpr int kMaxBlocks = 12;     // blocks per wavefront (all in flight at once)
 constexpr int kZeroBytes = 128;    // zero A operands for inactive slots
 constexpr int kResCap = 64;        // residual entries listed per pass and wavefront
+constexpr int kResStage = 256;     // residual entries a workgroup stages in LDS (plan index)
 
 template <typename T>
 __device__ __forceinline__ const GLOBAL T* gp(const T* p) { return (const GLOBAL T*)p; }
@@ -159,6 +162,43 @@ __device__ __forceinline__ void decode_quarter(uint32_t v, h8_t* bb) {
   bb[1] = t[1];
 }
 
+// LDS staging of a work item once its small operands have arrived: scales
+// (flat 16-byte chunks, or per row for a K split), activations (zero past
+// the range) and the zero area.
+template <int MP, int KSF>
+__device__ __forceinline__ void stage_lds(uint8_t* lds, uint32_t scoff, uint32_t xoff, bool sflat, int nsch,
+                                          const u4_t (&sv)[KSF], const GLOBAL uint16_t* s0, uintptr_t send,
+                                          uintptr_t sa0, int ngr, int rw, int spitch, int row0, int n, int ng,
+                                          int ga, int nx, int cpr, int krp, int kr, const u4_t (&xv)[8], int tid) {
+  uint16_t* ssm = reinterpret_cast<uint16_t*>(lds + scoff);
+  if (sflat) {
+#pragma unroll
+    for (int u = 0; u < KSF; ++u)
+      if (u * kThreads + tid < nsch) *reinterpret_cast<u4_t*>(lds + scoff + (u * kThreads + tid) * 16) = sv[u];
+    for (int c = KSF * kThreads + tid; c < nsch; c += kThreads)  // long ranges
+      *reinterpret_cast<u4_t*>(lds + scoff + c * 16) = scale_chunk(s0, send, sa0 + (size_t)c * 16);
+  } else {
+    // K split: the item's groups of each row (thread -> groups 32c + sgl, rows srr + 8u)
+    const int sgl = tid % 32, srr = tid / 32;
+    for (int c = 0; c * 32 < ngr; ++c) {
+      const int g = c * 32 + sgl;
+      if (g < ngr)
+        for (int u = 0; u < rw / 8; ++u)
+          ssm[(srr + 8 * u) * spitch + g] = s0[(size_t)min(row0 + srr + 8 * u, n - 1) * ng + ga + g];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int id = u * kThreads + tid;
+    if (u * kThreads < nx && id < nx) {
+      const int m = xrow_of<MP>(id, cpr);
+      const int kk = (id - m * cpr) * 8;
+      *reinterpret_cast<u4_t*>(lds + xoff + (size_t)m * krp * 2 + kk * 2) = kk < kr ? xv[u] : u4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  if (tid < kZeroBytes / 16) *reinterpret_cast<u4_t*>(lds + tid * 16) = u4_t{0u, 0u, 0u, 0u};
+}
+
 template <int MP>
 struct Win {
   static constexpr int GW = 16 / MP;                        // groups per window
@@ -171,8 +211,12 @@ struct Win {
 //   then                           scales of the 64 rows (see stage 2)
 //   then per wavefront             residual entries (kResCap x 8 B) and values
 //   then                           per-group activation sums (offsets only)
+static_assert(kWaves * kResCap >= kResStage, "the value area holds every staged entry");
 template <int MP>
 constexpr int res_wave_bytes() { return kResCap * 8 + kResCap * MP * 4; }
+// staged residual entries: blocks (G/4 bytes each), then index chunks
+template <int G>
+constexpr int res_stage_bytes() { return kResStage * (G / 4) + (kResStage / 4 + 1) * 16; }
 
 template <int G, int MP>
 __global__ __launch_bounds__(kWave * kWaves) __attribute__((amdgpu_waves_per_eu(MP == 8 || (G == 64 && MP == 4) ? 2 : 3, 8)))
@@ -225,8 +269,12 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
   const uint32_t xoff = kZeroBytes;                                            // activations
   const uint32_t scoff = xoff + (uint32_t)dm * krp * 2;                        // scales
   const uint32_t scbytes = ((uint32_t)kGemvRows * spitch * 2 + 32 + 15) / 16 * 16;  // + chunk slack
-  const uint32_t roff = scoff + scbytes + (uint32_t)wave * res_wave_bytes<MP>();
-  const uint32_t redoff = scoff + scbytes + kWaves * res_wave_bytes<MP>();    // part sums
+  // residual values [4 waves][kResCap][MP] (a tile's kw waves are adjacent,
+  // so a tile owns kw * kResCap consecutive entries), then entry lists
+  const uint32_t valoff = scoff + scbytes;
+  const uint32_t entoff = valoff + kWaves * kResCap * MP * 4 + (uint32_t)wave * kResCap * 8;
+  const uint32_t rstoff = valoff + kWaves * res_wave_bytes<MP>();              // staged residual data
+  const uint32_t redoff = rstoff + res_stage_bytes<G>();                       // part sums
   const uint32_t soff = redoff + kWaves * MP * kRowsWave * 4;                  // group sums of x
 
   // bytes of this wavefront's part in one row (an empty part reads, and
@@ -234,7 +282,6 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
   const int rbytes = max((pgb - pga) * G / 4, 16);
   const GLOBAL uint8_t* wrow = gp(d.plane0) + (size_t)rowc * d.stride + (k0 + pb0 * kBlockTrits) / 4;
   const GLOBAL uint16_t* s0 = gp(d.scale0);
-  uint16_t* ssm = reinterpret_cast<uint16_t*>(lds + scoff);
   const int cpr = krp / 8;   // 16-byte activation chunks per activation row
   const int nx = dm * cpr;   // at most 2048: MP * krp <= 16384
 
@@ -263,108 +310,47 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
       xv[u] = *reinterpret_cast<const GLOBAL u4_t*>(gp(d.x) + (size_t)m * d.k + k0 + kk);
     }
   }
-  // first residual plane: mask word q of this row (words 0..3 cover the first
-  // 128 groups) and its rowptr
-  const bool res_fast = d.planes > 1 && pgb > pga && ((pgb - 1) >> 5) < 4;
-  uint32_t mword = 0, rp = 0;
-  if (res_fast) {
-    mword = q < d.mwords ? gp(d.mask[0])[(size_t)rowc * d.mwords + min(q, d.mwords - 1)] : 0u;
-    rp = gp(d.rowptr[0])[rowc];
+  // first residual plane, when the plan indexed it and the item covers the
+  // whole row: the workgroup's entries [e0, e1) (its rows are contiguous) are
+  // staged in LDS with the other small operands -- their blocks as raw
+  // 16-byte chunks and their index words (group | scale bits << 16)
+  uint32_t e0 = 0, e1 = 0;
+  if (d.gidx[0] != nullptr && sflat && d.planes == 2) {
+    const int nt = rw / kRowsWave;
+    e0 = d.tile_e[0][0];
+    e1 = nt == 1 ? d.tile_e[0][1] : nt == 2 ? d.tile_e[0][2] : d.tile_e[0][4];
   }
-  // the first kDepth weight blocks of this wavefront's part
-  u4_t cur[kDepth], nxt[kDepth];
+  const bool res_idx = e1 > e0 && e1 - e0 <= (uint32_t)kResStage;
+  const uint32_t nres = res_idx ? e1 - e0 : 0u;
+  constexpr int kBQ = G / 4 / 16;                          // 16-byte chunks per block
+  const GLOBAL uint32_t* gix = gp(d.gidx[0]);
+  const uintptr_t gfirst = (uintptr_t)(gix + e0), ga0 = gfirst & ~(uintptr_t)15;
+  const int gshift = (int)(gfirst - ga0) / 4;
+  const int nbch = (int)nres * kBQ;                        // block chunks
+  const int ngch = res_idx ? (int)(((uintptr_t)(gix + e1) - ga0 + 15) / 16) : 0;  // index chunks
+  constexpr int kRS = (kResStage * kBQ + kResStage / 4 + 1 + kThreads - 1) / kThreads;
+  u4_t rv[kRS];
 #pragma unroll
-  for (int i = 0; i < kDepth; ++i) cur[i] = wload(nblk > 0 ? wrow : wrow - (pb0 * kBlockTrits) / 4, min(i, max(nblk - 1, 0)), q, rbytes);
+  for (int u = 0; u < kRS; ++u) {
+    if (u * kThreads < nbch + ngch) {
+      const int c = min(u * kThreads + tid, nbch + ngch - 1);
+      if (c < nbch)
+        rv[u] = *reinterpret_cast<const GLOBAL u4_t*>(gp(d.blocks[0]) + ((size_t)e0 * kBQ + c) * 16);
+      else
+        rv[u] = *reinterpret_cast<const GLOBAL u4_t*>(ga0 + (size_t)(c - nbch) * 16);
+    }
+  }
+  // this row's entries, for the sums
+  uint32_t rp0 = 0, rp1 = 0;
+  if (res_idx) {
+    rp0 = gp(d.rowptr[0])[rowc];
+    rp1 = gp(d.rowptr[0])[rowc + 1];
+  }
 
-  // ---- 2. LDS: scales, activations, zero area
-  if (sflat) {
-#pragma unroll
-    for (int u = 0; u < kSF; ++u)
-      if (u * kThreads + tid < nsch) *reinterpret_cast<u4_t*>(lds + scoff + (u * kThreads + tid) * 16) = sv[u];
-    for (int c = kSF * kThreads + tid; c < nsch; c += kThreads)  // long ranges
-      *reinterpret_cast<u4_t*>(lds + scoff + c * 16) = scale_chunk(s0, send, sa0 + (size_t)c * 16);
-  } else {
-    // K split: the item's groups of each row (thread -> groups 32c + sgl, rows srr + 8u)
-    const int sgl = tid % 32, srr = tid / 32;
-    for (int c = 0; c * 32 < ngr; ++c) {
-      const int g = c * 32 + sgl;
-      if (g < ngr)
-        for (int u = 0; u < rw / 8; ++u)
-          ssm[(srr + 8 * u) * spitch + g] = s0[(size_t)min(row0 + srr + 8 * u, d.n - 1) * d.ng + ga + g];
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int id = u * kThreads + tid;
-    if (u * kThreads < nx && id < nx) {
-      const int m = xrow_of<MP>(id, cpr);
-      const int kk = (id - m * cpr) * 8;
-      *reinterpret_cast<u4_t*>(lds + xoff + (size_t)m * krp * 2 + kk * 2) = kk < kr ? xv[u] : u4_t{0u, 0u, 0u, 0u};
-    }
-  }
-  if (tid < kZeroBytes / 16) *reinterpret_cast<u4_t*>(lds + tid * 16) = u4_t{0u, 0u, 0u, 0u};
+  float* valw = reinterpret_cast<float*>(lds + valoff) + (size_t)wave * kResCap * MP;  // this wave's
+  float* valr = reinterpret_cast<float*>(lds + valoff);  // staged entries' values [entry][m]
+  uint32_t* ent = reinterpret_cast<uint32_t*>(lds + entoff);
 
-  // ---- 3. first residual plane: list this wavefront's first kResCap entries
-  // in [pga, pgb) (row-major) and prefetch their blocks and scales, one
-  // 16-entry batch per register: lane (q, r) holds quarter q of entry 16bt + r
-  uint32_t* ent = reinterpret_cast<uint32_t*>(lds + roff);
-  float* val = reinterpret_cast<float*>(lds + roff + kResCap * 8);
-  uint32_t r1_cnt = 0, r1_pre = 0, r1_total = 0;
-  RB pre[kResCap / 16];
-  uint16_t prs[kResCap / 16];
-  if (res_fast) {
-    const int wb = q << 5;  // first group of this lane's mask word
-    uint32_t bits = row_ok ? mword & range_bits(pga - wb, pgb - wb) : 0u;
-    uint32_t before = row_ok ? (uint32_t)__popc(mword & range_bits(0, pga - wb)) : 0u;
-    before += __shfl_xor(before, 16, kWave);
-    before += __shfl_xor(before, 32, kWave);
-    const uint32_t base = rp + before;  // block index of the row's first entry in the part
-    // this word's entries: offset within the row, then the row's offset in the wave
-    const uint32_t c1 = __popc(bits);
-    uint32_t inc = c1;
-    {
-      uint32_t t = __shfl_up(inc, 16, kWave);
-      if (q >= 1) inc += t;
-      t = __shfl_up(inc, 32, kWave);
-      if (q >= 2) inc += t;
-    }
-    const uint32_t qoff = inc - c1;
-    r1_cnt = __shfl(inc, 48 + r, kWave);  // the row's count (quarter 3 holds the total)
-    uint32_t incl = r1_cnt;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const uint32_t t = __shfl_up(incl, o, 16);
-      if (r >= o) incl += t;
-    }
-    r1_pre = incl - r1_cnt;
-    r1_total = __shfl(incl, 15, kWave);
-    uint32_t e = r1_pre + qoff;
-    while (bits) {
-      const int g = wb + __builtin_ctz(bits);
-      bits &= bits - 1u;
-      if (e < (uint32_t)kResCap) {
-        ent[2 * e] = base + (e - r1_pre);
-        ent[2 * e + 1] = (uint32_t)(g - ga);
-      }
-      ++e;
-    }
-    wave_sync();
-    const uint32_t ncap = min(r1_total, (uint32_t)kResCap);
-    const GLOBAL uint8_t* blocks = gp(d.blocks[0]);
-    const GLOBAL uint16_t* rscale = gp(d.rscale[0]);
-#pragma unroll
-    for (int bt = 0; bt < kResCap / 16; ++bt) {
-      if ((uint32_t)(bt * 16) < ncap) {
-        const uint32_t t = bt * 16 + r;
-        const uint32_t blk = t < ncap ? ent[2 * t] : 0u;
-        pre[bt] = *reinterpret_cast<const GLOBAL RB*>(blocks + (size_t)blk * (G / 4) + q * sizeof(RB));
-        prs[bt] = rscale[blk];
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- plane 0
   // this lane's slot: activation row m_a = r / GW, group offset r % GW in the window
   const int m_a = r / GW;
   const bool a_row = m_a < dm;
@@ -377,9 +363,40 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
   const uint16_t* my_sc = reinterpret_cast<const uint16_t*>(lds + scoff) + (sflat ? sshift : 0) +
                           (tile * kRowsWave + r) * spitch + (pga - (sflat ? 0 : ga));
   const int ngp = pgb - pga;
+  // an empty part reads, and ignores, the item's first 16 bytes
+  const GLOBAL uint8_t* wr = nblk > 0 ? wrow : wrow - (pb0 * kBlockTrits) / 4;
+
+  // One 16-entry batch: entry t = b0 + r (t < wn) has block quarter BLKQ and
+  // group GRR (relative to the item's range); its scaled partial sums go to
+  // val[t][m].
+#define TERN_RES_BATCH(VAL, B0, WN, BLKQ, GRR, RSV)                                           \
+  do {                                                                                        \
+    const uint32_t t_ = (B0) + r;                                                             \
+    const bool ok_ = t_ < (WN);                                                               \
+    h8_t bb_[4];                                                                              \
+    decode_quarter(ok_ ? (BLKQ) : RB{}, bb_);                                                 \
+    _Pragma("unroll") for (int m = 0; m < MP; ++m) {                                          \
+      if (m < dm) {                                                                           \
+        f4_t R_ = {0.f, 0.f, 0.f, 0.f};                                                       \
+        const uint32_t ab_ = ok_ ? xoff + (uint32_t)(m * krp + (GRR) * G + q * (G / 4)) * 2 : 0u; \
+        _Pragma("unroll") for (int j = 0; j < G / 32; ++j)                                    \
+          R_ = __builtin_amdgcn_mfma_f32_16x16x32_f16(lds_h8(lds, ab_ + 16u * j), bb_[j], R_, 0, 0, 0); \
+        /* diagonal: entry r sits in lane 16 * (r / 4) + r, element r % 4 */                  \
+        if (q == r / 4 && ok_) (VAL)[t_ * MP + m] = (RSV) * R_[r % 4];                        \
+      }                                                                                       \
+    }                                                                                         \
+  } while (0)
+  // each owner adds its row's entries of the window [W0, W0 + WN) in order
+#define TERN_RES_SUM(PRE, CNT, W0, WN)                                                        \
+  do {                                                                                        \
+    const uint32_t lo_ = max((PRE), (W0)), hi_ = min((PRE) + (CNT), (W0) + (WN));             \
+    _Pragma("unroll") for (int i = 0; i < NACC; ++i)                                          \
+      if (owner && m_of[i] < dm)                                                              \
+        for (uint32_t e = lo_; e < hi_; ++e) acc[i] += valw[(e - (W0)) * MP + m_of[i]];       \
+  } while (0)
 
   // One block: decode, 8 MFMAs.  Window boundaries are static in the
-  // unrolled body because BW divides kDepth.
+  // unrolled body because BW divides 8.
 #define TERN_BLOCK(V, C, I)                                                                   \
   do {                                                                                        \
     const int wc_ = (I) % BW;                                                                 \
@@ -406,31 +423,44 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
     E = f4_t{0.f, 0.f, 0.f, 0.f};                                                             \
   } while (0)
 
-  // Blocks in groups of kDepth: the next group's loads are issued before the
-  // current group is computed, so each load has a whole group of work to land.
-  const int nfull = nblk / kDepth * kDepth;
-  for (int c0 = 0; c0 < nfull; c0 += kDepth) {
-#pragma unroll
-    for (int i = 0; i < kDepth; ++i) nxt[i] = wload(wrow, min(c0 + kDepth + i, nblk - 1), q, rbytes);
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the group
-#pragma unroll
-    for (int i = 0; i < kDepth; ++i) {
-      TERN_BLOCK(cur[i], c0 + i, i);
-      if (i % BW == BW - 1) TERN_CLOSE((c0 + i) / BW);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // the copies wait for the loads: keep them last
-#pragma unroll
-    for (int i = 0; i < kDepth; ++i) cur[i] = nxt[i];
-  }
-  const int rem = nblk - nfull;
-#pragma unroll
-  for (int i = 0; i < kDepth; ++i) {
-    if (i < rem) {
-      TERN_BLOCK(cur[i], nfull + i, i);
-      if (i % BW == BW - 1) TERN_CLOSE((nfull + i) / BW);
-    }
-  }
-  if (rem % BW != 0) TERN_CLOSE((nblk - 1) / BW);
+  // ---- 2..5 with NB weight loads in flight.  Every wavefront's blocks (at
+  // most bpp <= kMaxBlocks: the host chooses kwaves and splits so) are requested at once, right
+  // after the small operands; loads past a wavefront's blocks repeat its last
+  // block.  NB is uniform over the workgroup (bpp), so every wavefront meets
+  // the same barrier.
+#define TERN_BODY(NB)                                                                         \
+  do {                                                                                        \
+    u4_t w_[NB];                                                                              \
+    stage_lds<MP, kSF>(lds, scoff, xoff, sflat, nsch, sv, s0, send, sa0, ngr, rw, spitch, row0,         \
+              d.n, d.ng, ga, nx, cpr, krp, kr, xv, tid);                                      \
+    _Pragma("unroll") for (int u = 0; u < kRS; ++u) {                                         \
+      const int c_ = u * kThreads + tid;                                                      \
+      if (u * kThreads < nbch + ngch && c_ < nbch + ngch)                                     \
+        *reinterpret_cast<u4_t*>(lds + rstoff + (c_ < nbch ? c_ * 16 : kResStage * (G / 4) + (c_ - nbch) * 16)) = rv[u]; \
+    }                                                                                         \
+    __syncthreads();                                                                          \
+    /* the weights, once the small operands have landed (issued earlier they */               \
+    /* would queue the small operands behind every wavefront's weights) */                    \
+    _Pragma("unroll") for (int i = 0; i < NB; ++i) w_[i] = wload(wr, min(i, max(nblk - 1, 0)), q, rbytes); \
+    /* residual batches of the staged entries, spread over the wavefronts */                 \
+    for (uint32_t b0_ = 16u * wave; b0_ < nres; b0_ += 16u * kWaves) {                         \
+      const uint32_t t_ = min(b0_ + r, nres - 1);                                             \
+      const RB bq_ = *reinterpret_cast<const RB*>(lds + rstoff + t_ * (G / 4) + q * sizeof(RB)); \
+      const uint32_t gi_ = *reinterpret_cast<const uint32_t*>(lds + rstoff + kResStage * (G / 4) + (gshift + t_) * 4); \
+      TERN_RES_BATCH(valr, b0_, nres, bq_, (int)(gi_ & 0xFFFFu), 0.5f * h2f((uint16_t)(gi_ >> 16))); \
+    }                                                                                         \
+    /* plane 0 */                                                                             \
+    _Pragma("unroll") for (int i = 0; i < NB; ++i) {                                          \
+      if (i < nblk) {                                                                         \
+        TERN_BLOCK(w_[i], i, i);                                                              \
+        if (i % BW == BW - 1) TERN_CLOSE(i / BW);                                             \
+      }                                                                                       \
+    }                                                                                         \
+    if (nblk > 0 && nblk % BW != 0) TERN_CLOSE((nblk - 1) / BW);                              \
+  } while (0)
+  if (bpp > 8) TERN_BODY(kMaxBlocks);
+  else TERN_BODY(8);
+#undef TERN_BODY
 #undef TERN_BLOCK
 #undef TERN_CLOSE
 
@@ -446,56 +476,11 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
   else { m_of[0] = 2 * q; m_of[NACC - 1] = 2 * q + 1; owner = true; }
 
   // ---- residual planes over [pga, pgb)
-  // One 16-entry batch: entry t = b0 + r (t < wn) has block quarter BLKQ and
-  // group GRR (relative to the item's range); its scaled partial sums go to
-  // val[t][m].
-#define TERN_RES_BATCH(B0, WN, BLKQ, GRR, RSV)                                                \
-  do {                                                                                        \
-    const uint32_t t_ = (B0) + r;                                                             \
-    const bool ok_ = t_ < (WN);                                                               \
-    h8_t bb_[4];                                                                              \
-    decode_quarter(ok_ ? (BLKQ) : RB{}, bb_);                                                 \
-    _Pragma("unroll") for (int m = 0; m < MP; ++m) {                                          \
-      if (m < dm) {                                                                           \
-        f4_t R_ = {0.f, 0.f, 0.f, 0.f};                                                       \
-        const uint32_t ab_ = ok_ ? xoff + (uint32_t)(m * krp + (GRR) * G + q * (G / 4)) * 2 : 0u; \
-        _Pragma("unroll") for (int j = 0; j < G / 32; ++j)                                    \
-          R_ = __builtin_amdgcn_mfma_f32_16x16x32_f16(lds_h8(lds, ab_ + 16u * j), bb_[j], R_, 0, 0, 0); \
-        /* diagonal: entry r sits in lane 16 * (r / 4) + r, element r % 4 */                  \
-        if (q == r / 4 && ok_) val[t_ * MP + m] = (RSV) * R_[r % 4];                          \
-      }                                                                                       \
-    }                                                                                         \
-  } while (0)
-  // each owner adds its row's entries of the window [W0, W0 + WN) in order
-#define TERN_RES_SUM(PRE, CNT, W0, WN)                                                        \
-  do {                                                                                        \
-    const uint32_t lo_ = max((PRE), (W0)), hi_ = min((PRE) + (CNT), (W0) + (WN));             \
-    _Pragma("unroll") for (int i = 0; i < NACC; ++i)                                          \
-      if (owner && m_of[i] < dm)                                                              \
-        for (uint32_t e = lo_; e < hi_; ++e) acc[i] += val[(e - (W0)) * MP + m_of[i]];        \
-  } while (0)
-
   for (int p = 0; p + 1 < d.planes && pgb > pga; ++p) {
     const GLOBAL uint8_t* blocks = gp(p == 0 ? d.blocks[0] : d.blocks[1]);
     const GLOBAL uint16_t* rscale = gp(p == 0 ? d.rscale[0] : d.rscale[1]);
-    uint32_t w_begin = 0;
-    if (p == 0 && res_fast) {
-      // entries [0, min(total, kResCap)) are listed and their blocks are in `pre`
-      const uint32_t wn = min(r1_total, (uint32_t)kResCap);
-#pragma unroll
-      for (int bt = 0; bt < kResCap / 16; ++bt) {
-        if ((uint32_t)(bt * 16) < wn) {
-          const uint32_t t = bt * 16 + r;
-          const int grr = t < wn ? (int)ent[2 * t + 1] : 0;
-          const float rs = t < wn ? 0.5f * h2f(prs[bt]) : 0.f;
-          TERN_RES_BATCH((uint32_t)(bt * 16), wn, pre[bt], grr, rs);
-        }
-      }
-      wave_sync();
-      if (r1_cnt) TERN_RES_SUM(r1_pre, r1_cnt, 0u, wn);
-      if (r1_total <= (uint32_t)kResCap) continue;
-      w_begin = kResCap;
-    }
+    const uint32_t w_begin = 0;
+    if (p == 0 && res_idx) continue;  // done before plane 0
     // general path: list from the mask in global memory, window by window
     const int wlo = pga >> 5, whi = (pgb - 1) >> 5;
     const GLOBAL uint32_t* mrow = gp(p == 0 ? d.mask[0] : d.mask[1]) + (size_t)rowc * d.mwords;
@@ -539,7 +524,7 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
         const int grr = t < wn ? (int)ent[2 * t + 1] : 0;
         const RB bq = *reinterpret_cast<const GLOBAL RB*>(blocks + (size_t)blk * (G / 4) + q * sizeof(RB));
         const float rs = t < wn ? 0.5f * h2f(rscale[blk]) : 0.f;
-        TERN_RES_BATCH(b0, wn, bq, grr, rs);
+        TERN_RES_BATCH(valw, b0, wn, bq, grr, rs);
       }
       wave_sync();
       if (cnt) TERN_RES_SUM(pre_r, cnt, w0, wn);
@@ -567,7 +552,7 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
     for (int i = 0; i < NACC; ++i)
       if (owner && m_of[i] < dm) red[(wave * MP + m_of[i]) * kRowsWave + r] = acc[i];
   }
-  if (kw > 1 || d.offset_mode != 0) __syncthreads();
+  if (kw > 1 || d.offset_mode != 0 || res_idx) __syncthreads();
   if (kp != 0) return;
   if (kw > 1) {
 #pragma unroll
@@ -578,6 +563,30 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
         acc[i] = v;
       }
     }
+  }
+  // staged residual entries of this row: the row's four lanes take every
+  // fourth entry, then the quarters are added (fixed order)
+  if (res_idx) {
+    float rsum[MP];
+#pragma unroll
+    for (int m = 0; m < MP; ++m) rsum[m] = 0.f;
+    if (row_ok)
+      for (uint32_t e = rp0 + q; e < rp1; e += 4)
+#pragma unroll
+        for (int m = 0; m < MP; ++m) rsum[m] += valr[(e - e0) * MP + m];
+#pragma unroll
+    for (int m = 0; m < MP; ++m) {
+      rsum[m] += __shfl_xor(rsum[m], 16, kWave);
+      rsum[m] += __shfl_xor(rsum[m], 32, kWave);
+    }
+#pragma unroll
+    for (int i = 0; i < NACC; ++i)
+      if (owner && m_of[i] < dm) {
+        float v = 0.f;
+#pragma unroll
+        for (int m = 0; m < MP; ++m) v = m == m_of[i] ? rsum[m] : v;
+        acc[i] += v;
+      }
   }
   // ---- offsets over the item's range
   if (d.offset_mode != 0) {
@@ -619,7 +628,7 @@ hipError_t launch_mfma(const GemvDesc* descs, int ndesc, const GemvDesc& one, in
                        hipStream_t s) {
   const int ngr = max_krp / G;
   size_t lds = kZeroBytes + (size_t)MP * max_krp * 2 + ((size_t)kGemvRows * ngr * 2 + 32 + 15) / 16 * 16 +
-               (size_t)kWaves * res_wave_bytes<MP>() + (size_t)kWaves * MP * kRowsWave * 4;
+               (size_t)kWaves * res_wave_bytes<MP>() + res_stage_bytes<G>() + (size_t)kWaves * MP * kRowsWave * 4;
   if (offsets) lds += (size_t)MP * (max_krp / G) * 4;
   hipLaunchKernelGGL((gemv_mfma_kernel<G, MP>), dim3(items), dim3(kWave * kWaves), lds, s, descs, ndesc, one);
   return hipGetLastError();
@@ -639,11 +648,53 @@ hipError_t launch_mfma_g(int mp, const GemvDesc* descs, int ndesc, const GemvDes
   }
 }
 
+__global__ void res_index_kernel(const uint32_t* __restrict__ mask, const uint32_t* __restrict__ rowptr,
+                                 const uint16_t* __restrict__ rscale, int n, int mwords,
+                                 uint32_t* __restrict__ gidx) {
+  const int row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= n) return;
+  uint32_t e = rowptr[row];
+  for (int w = 0; w < mwords; ++w) {
+    uint32_t bits = mask[(size_t)row * mwords + w];
+    while (bits) {
+      gidx[e] = (uint32_t)(32 * w + __builtin_ctz(bits)) | ((uint32_t)rscale[e] << 16);
+      ++e;
+      bits &= bits - 1u;
+    }
+  }
+}
+
+__global__ void tile_bounds_kernel(GemvDesc* items, int count) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  GemvDesc* d = items + i;
+  const int item = i - d->tile_begin;
+  const int row0 = (item % d->row_blocks) * kRowsWave * (kWaves / d->kwaves);
+  for (int p = 0; p < 2; ++p) {
+    if (!d->gidx[p]) continue;
+    for (int t = 0; t < 5; ++t) d->tile_e[p][t] = d->rowptr[p][min(row0 + kRowsWave * t, d->n)];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_res_index(const uint32_t* mask, const uint32_t* rowptr, const uint16_t* rscale, int n,
+                            int mwords, uint32_t* gidx, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(res_index_kernel, dim3((n + 255) / 256), dim3(256), 0, s, mask, rowptr, rscale, n, mwords,
+                     gidx);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_bounds(GemvDesc* items, int count, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(tile_bounds_kernel, dim3((count + 255) / 256), dim3(256), 0, s, items, count);
+  return hipGetLastError();
+}
 
 int gemv_mfma_max_rows(int group) { return group == 128 ? 8 : 4; }
 
-int gemv_mfma_max_range(int mp) { return 16384 / mp; }
+int gemv_mfma_max_range(int mp) { return std::min(16384 / mp, kMaxBlocks * kBlockTrits * kWaves); }
 
 hipError_t launch_gemv_mfma(int group, int mp, const GemvDesc* descs, int ndesc, const GemvDesc& one,
                             int total_items, int max_krp, bool offsets, hipStream_t s) {

@@ -35,6 +35,11 @@ struct GemvDesc {
   int32_t tile_begin;     // first work-item index of this descriptor in the grid
   int32_t y_f32;          // 1: y is fp32, 0: fp16
   int32_t kwaves;         // matrix-core kernel: wavefronts sharing one 16-row tile's K (1, 2, 4)
+  // Residual index prepared with a plan (matrix-core kernel; NULL otherwise):
+  // per residual entry (group | FP16 scale bits << 16), and per work item the
+  // entry index (rowptr value) at each 16-row tile boundary of the item.
+  const uint32_t* gidx[2];
+  uint32_t tile_e[2][5];
 };
 
 // ---- decode products (gemv.hip)
@@ -61,6 +66,15 @@ int gemv_mfma_max_range(int mp);
 // any descriptor rounded up to 256; offsets = some descriptor has an offset.
 hipError_t launch_gemv_mfma(int group, int mp, const GemvDesc* descs, int ndesc, const GemvDesc& one,
                             int total_items, int max_krp, bool offsets, hipStream_t stream);
+
+// Residual index of a plan: for row n's j-th masked group g, entry
+// e = rowptr[n] + j gets gidx[e] = g | rscale[e] << 16 (one thread per row).
+hipError_t launch_res_index(const uint32_t* mask, const uint32_t* rowptr, const uint16_t* rscale, int n,
+                            int mwords, uint32_t* gidx, hipStream_t stream);
+// For each of `count` work-item descriptors in device memory whose gidx[p]
+// is set: tile_e[p][t] = rowptr[p][min(row0 + 16 t, n)], t = 0..4, where
+// row0 is the item's first row.
+hipError_t launch_tile_bounds(GemvDesc* items, int count, hipStream_t stream);
 
 // ---- MFMA product (gemm.hip)
 hipError_t launch_gemm(const GemvDesc& d, int format, hipStream_t stream);

@@ -127,11 +127,12 @@ void split_k(const tern_matrix* w, int want, int mp, int* splits, int* gps) {
 }
 
 // Wavefronts sharing one 16-row tile's K on the matrix-core kernel: the
-// fewest (1, 2 or 4) that keep each one's 256-trit blocks near `ref`, so that
-// long-K matrices of a batch finish with the short ones.
+// fewest (1, 2 or 4) that keep each one's 256-trit blocks within 12 (all in
+// flight at once) and near `ref`, so that long-K matrices of a batch finish
+// with the short ones.
 int choose_kwaves(int format, int k, int ref) {
   if (!use_mfma(format)) return 1;
-  const int nblk = (k + 255) / 256, cap = std::max(ref, 12);
+  const int nblk = (k + 255) / 256, cap = std::min(std::max(ref, 8), 12);
   int kw = 1;
   while (kw < 4 && (nblk + kw - 1) / kw > cap) kw *= 2;
   return kw;
@@ -415,13 +416,14 @@ tern_status tern_gemm(const tern_matrix* w, const uint16_t* x, int32_t m, void* 
 // Every descriptor covers its whole K (no split across workgroups).
 static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y,
                                int32_t count, int32_t m, int32_t y_dtype, std::vector<GemvDesc>* items,
-                               int* mt, int* max_krp, bool* offsets) {
+                               int* mt, int* max_krp, bool* offsets, std::vector<int>* mat = nullptr) {
   if (count < 0) return fail(TERN_E_INVAL, "count=%d is negative", count);
   if (count > 0 && (!w || !x || !y)) return fail(TERN_E_INVAL, "NULL descriptor arrays");
   if (m < 0) return fail(TERN_E_INVAL, "m=%d is negative", m);
   if (m >= 64) return fail(TERN_E_UNSUPPORTED, "batched decode takes m <= 63 (got %d)", m);
   if (y_dtype != TERN_F16 && y_dtype != TERN_F32) return fail(TERN_E_UNSUPPORTED, "unknown y dtype %d", y_dtype);
   items->clear();
+  if (mat) mat->clear();
   *max_krp = 0;
   *offsets = false;
   std::vector<int> order;
@@ -457,12 +459,20 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
       d.tile_begin = (int)items->size();
       if ((size_t)d.tile_begin + d.row_blocks > (size_t)INT32_MAX) return fail(TERN_E_UNSUPPORTED, "batch too large");
       items->insert(items->end(), (size_t)d.row_blocks, d);
+      if (mat) mat->insert(mat->end(), (size_t)d.row_blocks, i);
       *max_krp = std::max(*max_krp, round256(w[i].k));
       *offsets = *offsets || w[i].offset_mode != TERN_OFF_NONE;
     }
   }
   return TERN_OK;
 }
+
+// Plans of 2-bit products also keep a residual index after the descriptor
+// table: per entry of the first residual plane, its group and scale (u32).
+static bool plan_indexes(const tern_matrix* w) {
+  return use_mfma(w->format) && w->planes == 2 && w->nnz[0] > 0 && w->n > 0 && w->k > 0;
+}
+static size_t index_bytes(const tern_matrix* w) { return plan_indexes(w) ? round_up((size_t)w->nnz[0] * 4, 256) : 0; }
 
 size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m) {
   if (count <= 0 || m <= 0 || !w) return 0;
@@ -481,7 +491,9 @@ size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m
     const int rpi = rows_per_item(choose_kwaves(w[i].format, w[i].k, nblk_min));
     items += (size_t)((w[i].n + rpi - 1) / rpi) * chunks;
   }
-  return round_up(items * sizeof(GemvDesc), 256);
+  size_t idx = 0;
+  for (int i = 0; i < count; ++i) idx += index_bytes(&w[i]);
+  return round_up(items * sizeof(GemvDesc), 256) + idx;
 }
 
 tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, void* const* y,
@@ -508,14 +520,32 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
   if (!out) return fail(TERN_E_INVAL, "out is NULL");
   *out = nullptr;
   std::vector<GemvDesc> items;
+  std::vector<int> mat;
   int mt = 1, max_krp = 0;
   bool offsets = false;
-  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets));
+  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets, &mat));
   if (!items.empty()) {
-    const size_t need = items.size() * sizeof(GemvDesc);
+    // workspace: [descriptor per work item][residual index of each matrix]
+    const size_t dbytes = round_up(items.size() * sizeof(GemvDesc), 256);
+    std::vector<size_t> ioff(count, 0);
+    size_t need = dbytes;
+    for (int i = 0; i < count; ++i) {
+      ioff[i] = need;
+      need += index_bytes(&w[i]);
+    }
     if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "plan needs %zu workspace bytes", need);
     TERN_TRY(check_dev(ws, true, "ws"));
-    TERN_HIP(hipMemcpy(ws, items.data(), need, hipMemcpyHostToDevice));
+    char* base = static_cast<char*>(ws);
+    for (size_t t = 0; t < items.size(); ++t)
+      if (plan_indexes(&w[mat[t]])) items[t].gidx[0] = reinterpret_cast<const uint32_t*>(base + ioff[mat[t]]);
+    TERN_HIP(hipMemcpy(ws, items.data(), items.size() * sizeof(GemvDesc), hipMemcpyHostToDevice));
+    for (int i = 0; i < count; ++i)
+      if (plan_indexes(&w[i]))
+        TERN_HIP(tern::launch_res_index(w[i].mask[0], w[i].rowptr[0], w[i].rscale[0], w[i].n,
+                                        mask_words(w[i].k, w[i].group),
+                                        reinterpret_cast<uint32_t*>(base + ioff[i]), nullptr));
+    TERN_HIP(tern::launch_tile_bounds(static_cast<GemvDesc*>(ws), (int)items.size(), nullptr));
+    TERN_HIP(hipDeviceSynchronize());
   }
   tern_plan* p = static_cast<tern_plan*>(std::malloc(sizeof(tern_plan)));
   if (!p) return fail(TERN_E_INVAL, "out of host memory");

@@ -223,6 +223,10 @@ def test_gemv_degenerate_shapes():
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_batched_and_plan_match_oracle(fmt):
+    """The 4B-class layer through one grouped launch and through a plan (whose
+    2-bit residual entries come from a plan-time index and are added in entry
+    order after the K parts are combined, so its rounding may differ from the
+    batched call): both within the bound; a plan is bitwise reproducible."""
     import torch
     say("batched", fmt)
     mats, pms, xs, ys, refs = [], [], [], [], []
@@ -238,15 +242,41 @@ def test_batched_and_plan_match_oracle(fmt):
     torch.cuda.synchronize()
     for y, (y_ref, b) in zip(ys, refs):
         check_y(y, y_ref, b, "batched")
-    first = [y.clone() for y in ys]
     plan = L.Plan(pms, xs, ys)
+    first = None
     for _ in range(3):
         for y in ys:
             y.zero_()
         plan.run()
         torch.cuda.synchronize()
-        for y, f in zip(ys, first):
-            assert torch.equal(y, f), "plan run differs from the batched call"
+        if first is None:
+            first = [y.clone() for y in ys]
+            for y, (y_ref, b) in zip(ys, refs):
+                check_y(y, y_ref, b, "plan")
+        else:
+            for y, f in zip(ys, first):
+                assert torch.equal(y, f), "plan runs differ"
+
+
+@pytest.mark.parametrize("n,k,frac,m", [(40, 1024, 1.0, 1), (200, 4096, 0.5, 1), (33, 9728, 0.1, 2),
+                                         (130, 2560, 0.1, 8)])
+def test_plan_residual_index_edges(n, k, frac, m):
+    """Plans on ragged row counts, tiles whose entries exceed the plan index's
+    capacity (every group residual), K shared by 2 and 4 wavefronts, and
+    several activation rows, against the oracle."""
+    import torch
+    rng = np.random.default_rng(n * 7 + k)
+    mat = synth.make_matrix(n, k, 128, 2, frac, rng=rng)
+    x = synth.draw_x(rng, m, k, "normal")
+    pm = upload_pack(mat, O.FMT_2BIT)
+    xd = to_dev(x.view(np.uint16)).view(torch.float16)
+    y = torch.empty((m, n), dtype=torch.float16, device="cuda")
+    say("plan edges", n, k, frac, m)
+    plan = L.Plan([pm], [xd], [y])
+    plan.run()
+    torch.cuda.synchronize()
+    y_ref, b = oracle_y(mat, x)
+    check_y(y, y_ref, b, f"plan n={n} k={k} frac={frac} m={m}")
 
 
 # ----------------------------------------------------------------- MFMA product
