@@ -1,16 +1,21 @@
 // Batched product y = x W^T for many activation rows (tuned for M >= 64):
-// the packed weights of one group are decoded into an FP16 tile in LDS
-// (W~[n,k] = off + s0*t0 + m1*s1*t1 + m2*s2*t2), and the tile product runs on
-// the matrix cores (v_mfma_f32_16x16x32_f16, FP32 accumulation).  This is
-// the batched-execution direction named by arXiv 2609.09240 (kernel
-// optimisation across shapes and batch sizes); at M >= 64 the product is a
-// dense contraction, so MFMA is the right unit.
+// packed weights are decoded into an FP16 tile in LDS
+// (W~[n,k] = off + s0*t0 + m1*s1*t1 + m2*s2*t2, stored doubled), and the tile
+// product runs on the matrix cores (v_mfma_f32_32x32x16_f16, FP32
+// accumulation).  This is the batched-execution direction named by arXiv
+// 2609.09240 (kernel optimisation across shapes and batch sizes); at M >= 64
+// the product is a dense contraction, so MFMA is the right unit.
 //
-// Tile: 128 activation rows x 128 weight rows x one group (BK = G) per step;
-// 256 threads = 4 waves in a 2 x 2 arrangement, each wave owning a 64 x 64
-// output block of 4 x 4 MFMA tiles.  Operand layout of the 16x16x32 f16 MFMA:
-// lane l supplies A[l%16][8*(l/16) .. +7] and B[8*(l/16) .. +7][l%16] and
-// receives D[4*(l/16) + v][l%16], v = 0..3.
+// Tile: BM activation rows (256, or 128 for small M) x 128 weight rows, K in
+// steps of 64.  256 threads = 4 waves in a 2 x 2 arrangement; a wave owns
+// BM/2 x 64 outputs as (BM/64) x 2 MFMA tiles of 32 x 32.  Each step stages
+// the activation tile (copied) and the weight tile (decoded: thread = one
+// weight row and 32 of the step's 64 trits) in one of two LDS buffers, so one
+// barrier per step separates staging from the products, and the next step's
+// global loads are in flight while this step's products run.
+// Operand layout of the 32x32x16 f16 MFMA: lane l supplies A[l%32][8*(l/32)
+// .. +7] and B[8*(l/32) .. +7][l%32] and receives D[8*(v/4) + 4*(l/32) +
+// v%4][l%32], v = 0..15.
 #include "internal.h"
 
 namespace tern {
@@ -18,11 +23,12 @@ namespace {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef float f16v_t __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, NT = 256;
-
-__device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+constexpr int NT = 256;     // threads per workgroup
+constexpr int BN = 128;     // weight rows per tile
+constexpr int BK = 64;      // K per step
+constexpr int PH = BK + 8;  // LDS row pitch in halves: 144 B keeps 16-lane 16-byte accesses conflict-free
 
 // FP16 pair (2*t[2i], 2*t[2i+1]) of 2-bit word w (see the decode kernel).
 __device__ __forceinline__ uint32_t pair_of(uint32_t w, int shift) { return (w << shift) & 0xC000C000u; }
@@ -34,7 +40,10 @@ __device__ __forceinline__ uint32_t pk_fma(uint32_t a, uint32_t b, uint32_t c) {
   const h2_t r = __builtin_bit_cast(h2_t, a) * __builtin_bit_cast(h2_t, b) + __builtin_bit_cast(h2_t, c);
   return __builtin_bit_cast(uint32_t, r);
 }
-__device__ __forceinline__ uint32_t splat(uint16_t h) { return (uint32_t)h * 0x10001u; }
+__device__ __forceinline__ uint32_t pk_add(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, a) + __builtin_bit_cast(h2_t, b));
+}
+__device__ __forceinline__ uint32_t splat(uint32_t h) { return (h & 0xFFFFu) * 0x10001u; }
 
 // Base-3 byte -> five 2-bit codes at bits 0..9 (trit i at bits 2i..2i+1).
 __device__ __forceinline__ uint32_t b3_codes(uint32_t v) {
@@ -47,167 +56,415 @@ __device__ __forceinline__ uint32_t b3_codes(uint32_t v) {
   return c;
 }
 
-// Writes FP16 values 2*W~[row, g*G + H*G/2 + i], i < G/2, to dst (LDS).
-template <int FMT, int G, int H>
-__device__ __forceinline__ void decode_half(const GemvDesc& d, int g, int wrow, bool ok,
-                                            const uint32_t* lut, _Float16* dst_h) {
-  constexpr int HT = G / 2;  // trits per thread
-  uint32_t out[HT / 2];      // FP16 pairs, natural order
-#pragma unroll
-  for (int i = 0; i < HT / 2; ++i) out[i] = 0u;
-  if (ok) {
-    const uint8_t* prow = d.plane0 + (size_t)wrow * d.stride;
-    const uint32_t s0 = splat(d.scale0[(size_t)wrow * d.ng + g]);
-    if (FMT == 0) {
-      const uint4* wp = reinterpret_cast<const uint4*>(prow + (size_t)g * (G / 4) + H * (G / 8));
-#pragma unroll
-      for (int q = 0; q < HT / 64; ++q) {
-        const uint4 v = wp[q];
-        const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) out[q * 32 + u * 8 + i] = pk_mul(pair_of(ws[u], 14 - 2 * i), s0);
-      }
-      if (HT % 64) {  // G = 64: 32 trits = two words
-        const uint32_t* wq = reinterpret_cast<const uint32_t*>(prow + (size_t)g * (G / 4) + H * (G / 8));
-#pragma unroll
-        for (int u = 0; u < (HT % 64) / 16; ++u)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) out[(HT / 64) * 32 + u * 8 + i] = pk_mul(pair_of(wq[(HT / 64) * 4 + u], 14 - 2 * i), s0);
-      }
-    } else {
-      constexpr int GB = (G + 4) / 5;
-      constexpr int B0 = (H * HT) / 5, B1 = (H * HT + HT - 1) / 5, NB = B1 - B0 + 1;
-      const uint8_t* gp = prow + (size_t)g * GB;
-      uint32_t cw[NB];
-#pragma unroll
-      for (int j = 0; j < NB; ++j) cw[j] = lut[gp[B0 + j]];
-#pragma unroll
-      for (int i = 0; i < HT / 2; ++i) {
-        const int ta = H * HT + 2 * i, tb = ta + 1;
-        const uint32_t ca = (cw[ta / 5 - B0] >> (2 * (ta % 5))) & 3u;
-        const uint32_t cb = (cw[tb / 5 - B0] >> (2 * (tb % 5))) & 3u;
-        out[i] = pk_mul((ca << 14) | (cb << 30), s0);
-      }
-    }
-    for (int p = 0; p < d.planes - 1; ++p) {
-      const uint32_t* rm = d.mask[p] + (size_t)wrow * d.mwords;
-      if ((rm[g >> 5] >> (g & 31)) & 1u) {
-        uint32_t b = d.rowptr[p][wrow];
-        for (int w = 0; w < (g >> 5); ++w) b += __popc(rm[w]);
-        if (g & 31) b += __popc(rm[g >> 5] & ((1u << (g & 31)) - 1u));
-        const uint32_t s1 = splat(d.rscale[p][b]);
-        const uint32_t* bp = reinterpret_cast<const uint32_t*>(d.blocks[p] + (size_t)b * (G / 4) + H * (G / 8));
-#pragma unroll
-        for (int q = 0; q < HT / 16; ++q) {
-          const uint32_t w = bp[q];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) out[q * 8 + i] = pk_fma(pair_of(w, 14 - 2 * i), s1, out[q * 8 + i]);
-        }
-      }
-    }
-    if (d.offset_mode != 0) {
-      const uint16_t o = d.offset_mode == 1 ? d.offset[wrow] : d.offset[(size_t)wrow * d.ng + g];
-      const h2_t ov = __builtin_bit_cast(h2_t, splat(o)) * (h2_t){(_Float16)2.0f, (_Float16)2.0f};
-#pragma unroll
-      for (int i = 0; i < HT / 2; ++i)
-        out[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, out[i]) + ov);
-    }
-  }
-  uint32_t* dst = reinterpret_cast<uint32_t*>(dst_h);
-#pragma unroll
-  for (int i = 0; i < HT / 2; i += 4)
-    *reinterpret_cast<uint4*>(dst + i) = make_uint4(out[i], out[i + 1], out[i + 2], out[i + 3]);
+// Buffer resource over `bytes` bytes at p: loads at or past the end return 0,
+// which zeroes the operands of rows past n or m without a branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int FMT, int G>
-__global__ __launch_bounds__(NT) void gemm_kernel(GemvDesc d) {
-  constexpr int BK = G;
-  constexpr int XP = BK + 8;  // LDS row pitch in halves (16-byte pad)
-  __shared__ _Float16 xs[BM * XP];
-  __shared__ _Float16 wt[BN * XP];
-  __shared__ uint32_t lut[256];
+// Buffer resources and per-thread offsets of one matrix.
+struct Src {
+  __amdgpu_buffer_rsrc_t p0, sc, offg, mask[2], blk[2], rsc[2];
+  uint32_t sc_v, offg_v, mask_v;  // row-dependent byte offsets of the decoding thread's row
+};
 
+// Packed plane-0 bytes reach LDS in windows of WSTEPS steps: every row of the
+// tile loads WB bytes with coalesced 16-byte loads (2-bit: 4 steps = 64 B;
+// base-3: 4 steps = 52 B from a dword boundary, read as 64).  Three window
+// buffers let each pair of steps load and store one chunk per thread.
+constexpr int WSTEPS = 4;
+constexpr int WB = 64;
+constexpr int WP = WB + 16;             // LDS pitch of a window row
+constexpr int NWIN = 3;
+constexpr int WCH = BN * WB / 16 / NT;  // 16-byte window chunks per thread and window (2)
+constexpr uint32_t kOOB = 0x7FFFFFF0u;  // offset past every buffer: the load returns zero
+
+template <int FMT>
+__device__ __forceinline__ int win_start(int w) { return FMT == 0 ? WB * w : 52 * w; }
+
+// Per-step operands of one thread (scale, per-group offset, residual), loaded
+// a step ahead of their decode.  Residual loads of lanes whose row has no
+// block at the group use an out-of-range offset, so every step issues the
+// same loads.
+template <int NP>
+struct Pre {
+  uint32_t s0;                       // plane-0 scale (FP16 bits; 0 past row n)
+  uint32_t off;                      // per-group offset (FP16 bits; 0 unless per-group offsets)
+  uint32_t has;                      // bit p: residual plane p+1 present at the group
+  uint32_t rw[NP > 0 ? NP : 1][2];   // residual 2-bit words of the thread's 32 trits
+  uint32_t rs[NP > 0 ? NP : 1];      // residual scales
+};
+
+// Residual walk of the decoding thread's row, kept at the group of the last
+// issued step loads: e[p] = entry index of that group's block (if present),
+// mwl[p] = the mask word holding that group, mwn[p] = the next mask word
+// (reloaded every other step).
+template <int NP>
+struct Walk {
+  uint32_t e[NP > 0 ? NP : 1], mwl[NP > 0 ? NP : 1], mwn[NP > 0 ? NP : 1];
+};
+
+// gc = g clamped to the last group (steps past the end reload it).
+template <int G, int NP, int A>
+__device__ __forceinline__ void load_step(const Src& S, int g, int gc, const Walk<NP>& W, Pre<NP>& P) {
+  P.s0 = __builtin_amdgcn_raw_buffer_load_b16(S.sc, S.sc_v, 2 * gc, 0);
+  P.off = __builtin_amdgcn_raw_buffer_load_b16(S.offg, S.offg_v, 2 * gc, 0);
+  P.has = 0;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const uint32_t pr = (W.mwl[p] >> (g & 31)) & 1u;
+    P.has |= pr << p;
+    P.rs[p] = __builtin_amdgcn_raw_buffer_load_b16(S.rsc[p], pr ? 2 * W.e[p] : kOOB, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(S.blk[p], pr ? W.e[p] * (G / 4) + A / 4 : kOOB, 0, 0);
+    P.rw[p][0] = v[0];
+    P.rw[p][1] = v[1];
+  }
+}
+
+// Moves the walk from group g to group g + 1.
+template <int NP>
+__device__ __forceinline__ void walk_next(int g, Walk<NP>& W) {
+#pragma unroll
+  for (int p = 0; p < NP; ++p) W.e[p] += (W.mwl[p] >> (g & 31)) & 1u;
+  if (((g + 1) & 31) == 0) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) W.mwl[p] = W.mwn[p];
+  }
+}
+
+// 2*W~ for the thread's 32 trits as 16 FP16 pairs in K order:
+// 2*(s0*t0 + m1*s1*t1 + m2*s2*t2 + off) with FP16 fused multiply-adds.  prep()
+// reads the packed bytes from the LDS window and takes the scales, pair(i)
+// forms pair i, store() writes four pairs to LDS; the product loop calls them
+// one piece at a time between its MFMAs.
+template <int FMT, int G, int NP, int A>
+struct Dec {
+  static constexpr int B0 = A / 5, NB = (A + 31) / 5 - B0 + 1;
+  uint32_t out[16];
+  uint32_t s0, o2, s1[NP > 0 ? NP : 1];
+  uint32_t w[FMT == 0 ? 2 : NB];  // 2-bit words, or base-3 code words
+  uint32_t rw[NP > 0 ? NP : 1][2];
+
+  // win: this thread's row in the LDS window holding step s; u = s % WSTEPS;
+  // g = group of step s; wstart = first row byte of the window; ro = row
+  // offset (FP16 bits; 0 unless per-row offsets)
+  __device__ __forceinline__ void prep(int g, int u, int wstart, const uint8_t* win, const Pre<NP>& P,
+                                       uint32_t ro, const uint32_t* lut) {
+    s0 = splat(P.s0);
+    const uint32_t o = splat(ro | P.off);  // at most one of them is non-zero
+    o2 = pk_add(o, o);
+    if constexpr (FMT == 0) {
+      const uint2 v = *reinterpret_cast<const uint2*>(win + 16 * u + 8 * ((A / 32) & 1));
+      w[0] = v.x;
+      w[1] = v.y;
+    } else {
+      // bytes of trits [A, A + 32) of group g: at most 8 from byte b of the window
+      constexpr int GB = (G + 4) / 5;
+      const int b = g * GB + A / 5 - wstart;
+      const uint32_t* wp = reinterpret_cast<const uint32_t*>(win + (b & ~3));
+      const uint32_t w0 = wp[0], w1 = wp[1], w2 = wp[2];
+      const uint32_t bsh = (uint32_t)(b & 3);
+      const uint32_t lo = __builtin_amdgcn_alignbyte(w1, w0, bsh), hi = __builtin_amdgcn_alignbyte(w2, w1, bsh);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) w[j] = lut[((j < 4 ? lo : hi) >> (8 * (j & 3))) & 0xFFu];
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      s1[p] = ((P.has >> p) & 1u) ? splat(P.rs[p]) : 0u;
+      rw[p][0] = P.rw[p][0];
+      rw[p][1] = P.rw[p][1];
+    }
+  }
+
+  __device__ __forceinline__ void pair(int i) {
+    uint32_t v;
+    if constexpr (FMT == 0) {
+      v = pk_fma(pair_of(w[i >> 3], 14 - 2 * (i & 7)), s0, o2);
+    } else {
+      const int ta = A + 2 * i, tb = ta + 1;
+      const uint32_t ca = (w[ta / 5 - B0] >> (2 * (ta % 5))) & 3u;
+      const uint32_t cb = (w[tb / 5 - B0] >> (2 * (tb % 5))) & 3u;
+      v = pk_fma((ca << 14) | (cb << 30), s0, o2);
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) v = pk_fma(pair_of(rw[p][i >> 3], 14 - 2 * (i & 7)), s1[p], v);
+    out[i] = v;
+  }
+
+  __device__ __forceinline__ void store(int q, _Float16* dst_h) const {
+    reinterpret_cast<uint4*>(dst_h)[q] = make_uint4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
+  }
+};
+
+// y = 0.5 * acc for one tile, staged through LDS (the activation buffers) so
+// that rows leave in 16-byte chunks; FP32 tiles of 256 rows go in two halves.
+template <typename T, int AW>
+__device__ __forceinline__ void epilogue(const GemvDesc& d, int m0, int n0, const f16v_t (&acc)[AW][2], char* tile) {
+  constexpr int BM = 64 * AW;
+  constexpr int HALVES = (sizeof(T) == 4 && AW == 4) ? 2 : 1;
+  constexpr int ROWS = BM / HALVES;
+  constexpr int TP = BN * (int)sizeof(T) + 16;  // tile pitch in bytes
+  constexpr int CPR = BN * (int)sizeof(T) / 16;  // 16-byte chunks per row
+  constexpr int PER = 16 / (int)sizeof(T);
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int mb = (wave >> 1) * 32 * AW, nb = (wave & 1) * 64;
+  const bool vec = (d.n % PER == 0) && (n0 + BN <= d.n);
+#pragma unroll
+  for (int hf = 0; hf < HALVES; ++hf) {
+    if (HALVES == 1 || (wave >> 1) == hf) {
+      char* base = tile + (mb - hf * ROWS + 4 * (lane >> 5)) * TP + (nb + (lane & 31)) * (int)sizeof(T);
+#pragma unroll
+      for (int i = 0; i < AW; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            *reinterpret_cast<T*>(base + (32 * i + 8 * (v >> 2) + (v & 3)) * TP + 32 * j * (int)sizeof(T)) =
+                (T)(0.5f * acc[i][j][v]);
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int c = t; c < ROWS * CPR; c += NT) {
+      const int r = c / CPR, cc = c % CPR;
+      const int m = m0 + hf * ROWS + r;
+      if (m >= d.m) continue;
+      const char* srcp = tile + r * TP + cc * 16;
+      T* dstp = reinterpret_cast<T*>(d.y) + (size_t)m * d.n + n0 + cc * PER;
+      if (vec) {
+        *reinterpret_cast<uint4*>(dstp) = *reinterpret_cast<const uint4*>(srcp);
+      } else {
+        for (int u = 0; u < PER; ++u)
+          if (n0 + cc * PER + u < d.n) dstp[u] = reinterpret_cast<const T*>(srcp)[u];
+      }
+    }
+    if (hf + 1 < HALVES) __syncthreads();
+  }
+}
+
+template <int FMT, int G, int AW, int NP, int H>
+__device__ __forceinline__ void gemm_body(const GemvDesc& d, int m0, int n0, _Float16* xs, _Float16* ws,
+                                          uint8_t* pk, const uint32_t* lut) {
+  constexpr int BM = 64 * AW;               // activation rows per tile
+  constexpr int XCH = BM * BK / 8 / NT;     // 16-byte activation chunks per thread per step
+  constexpr int XBUF = BM * PH, WBUF = BN * PH, PBUF = BN * WP;
+  constexpr int SPG = G / BK;               // steps per group
+  constexpr int SLOTS = 2 * AW * (BK / 16);  // MFMAs per wave and step
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  const int mb = (wave >> 1) * 32 * AW, nb = (wave & 1) * 64;
+  const int nsteps = d.ng * SPG;
 
+  f16v_t acc[AW][2];
+#pragma unroll
+  for (int i = 0; i < AW; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f16v_t{};
+
+  // decoded weight row dr; this thread takes trits [32H, 32H + 32) of each step
+  const int dr = t & (BN - 1);
+  const uint32_t row = (uint32_t)(n0 + dr);
+  Src S;
+  const uint32_t n = (uint32_t)d.n, ng = (uint32_t)d.ng, stride = (uint32_t)d.stride;
+  S.p0 = rsrc(d.plane0, n * stride);
+  S.sc = rsrc(d.scale0, n * ng * 2u);
+  S.offg = rsrc(d.offset, d.offset_mode == 2 ? n * ng * 2u : 0u);
+  S.sc_v = row * ng * 2u;
+  S.offg_v = row * ng * 2u;
+  S.mask_v = row * (uint32_t)d.mwords * 4u;
+  const uint32_t ro = __builtin_amdgcn_raw_buffer_load_b16(rsrc(d.offset, d.offset_mode == 1 ? n * 2u : 0u), row * 2u, 0, 0);
+  Walk<NP> W;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const uint32_t nnz = p == 0 ? d.nnz[0] : d.nnz[1];
+    S.mask[p] = rsrc(p == 0 ? d.mask[0] : d.mask[1], n * (uint32_t)d.mwords * 4u);
+    S.blk[p] = rsrc(p == 0 ? d.blocks[0] : d.blocks[1], nnz * (uint32_t)(G / 4));
+    S.rsc[p] = rsrc(p == 0 ? d.rscale[0] : d.rscale[1], nnz * 2u);
+    W.e[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc(p == 0 ? d.rowptr[0] : d.rowptr[1], n * 4u), row * 4u, 0, 0);
+    W.mwl[p] = __builtin_amdgcn_raw_buffer_load_b32(S.mask[p], S.mask_v, 0, 0);
+    W.mwn[p] = __builtin_amdgcn_raw_buffer_load_b32(S.mask[p], S.mask_v, d.mwords > 1 ? 4 : 0, 0);
+  }
+  // activation chunks (rows past m read as zero) and packed-window chunks
+  const __amdgpu_buffer_rsrc_t xr = rsrc(d.x, (uint32_t)d.m * (uint32_t)d.k * 2u);
+  uint32_t xo[XCH];
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) {
+    const int c = i * NT + t;
+    xo[i] = (uint32_t)(m0 + (c >> 3)) * (uint32_t)d.k * 2u + (uint32_t)(c & 7) * 16u;
+  }
+  // Window chunk i (of WCH) of this thread: row (t >> 2) + 64 i, bytes
+  // 16 (t & 3) .. + 16 of the window.  Every offset that can leave the buffer
+  // sits in the per-lane offset (rows past n read as zero); windows past the
+  // last one reload the last one.
+  const uint32_t wo = (uint32_t)(n0 + (t >> 2)) * stride + (uint32_t)(t & 3) * 16u;
+  const int wlast = (nsteps - 1) / WSTEPS;
+  uint8_t* const wl = pk + (t >> 2) * WP + (t & 3) * 16;
+#define TERN_WLOAD(WV_, W_, I_)                                                                   \
+  WV_ = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(                         \
+      S.p0, wo + (uint32_t)(win_start<FMT>(min((W_), wlast)) + (I_) * 64 * (int)stride), 0, 0))
+#define TERN_WSTORE(WV_, W_, I_) \
+  *reinterpret_cast<uint4*>(wl + ((W_) % NWIN) * PBUF + (I_) * 64 * WP) = WV_
+
+  // two register sets of prefetched operands: step s uses set s & 1
+  uint4 xv0[XCH], xv1[XCH], wv;
+  Pre<NP> P0, P1;
+  // Products of step s from LDS buffers XB_/WB_ with, between the MFMAs:
+  // the loads of step s + 2 (set XL_/PL_, group gl; on even steps one chunk
+  // of the window after next), the decode of step s + 1 (D_, written to WS_)
+  // and the activation chunks of step s + 1 (XN_, to XS_; on odd steps the
+  // window chunk loaded a step ago).  Every step issues the same loads, so
+  // the waits the compiler places for them are exact; each MFMA is followed by
+  // one piece of this work, which runs on the vector ALU, LDS and the memory
+  // pipeline while the matrix core works.  The fragments of the next 16-wide
+  // K slice are read while this slice's MFMAs run.
+#define TERN_PRODUCTS(U_, XB_, WB_, XL_, PL_, AL_, XN_, XS_, D_, WS_, DN_, PNN_)                  \
+  {                                                                                               \
+    h8_t fa[2][AW], fb[2][2];                                                                     \
+    _Pragma("unroll") for (int i = 0; i < AW; ++i)                                                \
+      fa[0][i] = *reinterpret_cast<const h8_t*>(&(XB_)[(mb + 32 * i + (lane & 31)) * PH + 8 * (lane >> 5)]); \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                 \
+      fb[0][j] = *reinterpret_cast<const h8_t*>(&(WB_)[(nb + 32 * j + (lane & 31)) * PH + 8 * (lane >> 5)]); \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    _Pragma("unroll") for (int kk = 0; kk < BK / 16; ++kk) {                                      \
+      _Pragma("unroll") for (int idx = 0; idx < 2 * AW; ++idx) {                                  \
+        acc[idx >> 1][idx & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(                          \
+            fa[kk & 1][idx >> 1], fb[kk & 1][idx & 1], acc[idx >> 1][idx & 1], 0, 0, 0);          \
+        if (idx == 0 && kk + 1 < BK / 16) {                                                       \
+          _Pragma("unroll") for (int i = 0; i < AW; ++i)                                          \
+            fa[(kk + 1) & 1][i] = *reinterpret_cast<const h8_t*>(                                 \
+                &(XB_)[(mb + 32 * i + (lane & 31)) * PH + 16 * (kk + 1) + 8 * (lane >> 5)]);      \
+          _Pragma("unroll") for (int j = 0; j < 2; ++j)                                           \
+            fb[(kk + 1) & 1][j] = *reinterpret_cast<const h8_t*>(                                 \
+                &(WB_)[(nb + 32 * j + (lane & 31)) * PH + 16 * (kk + 1) + 8 * (lane >> 5)]);      \
+        }                                                                                         \
+        const int c = kk * 2 * AW + idx; /* slot */                                               \
+        if (c == 0) load_step<G, NP, AL_>(S, gl, min(gl, d.ng - 1), W, PL_);                     \
+        if (c == 0 && (U_) == 0) {                                                                \
+          _Pragma("unroll") for (int p = 0; p < NP; ++p)                                          \
+            W.mwn[p] = __builtin_amdgcn_raw_buffer_load_b32(S.mask[p], S.mask_v,                    \
+                                                            4 * min((gl >> 5) + 1, d.mwords - 1), 0); \
+        }                                                                                         \
+        if (c < XCH)                                                                              \
+          (XL_)[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(            \
+              xr, xo[c], min(s + 2, nsteps - 1) * BK * 2, 0));                                    \
+        if (c == XCH && (U_) == 0) TERN_WLOAD(wv, (q >> 1) + 2, q & 1);                           \
+        if (c < 16) (D_).pair(c);                                                                 \
+        if (SLOTS > 16) {                                                                         \
+          if (c >= 16 && c < 20) (D_).store(c - 16, WS_);                                         \
+          if (c >= 20 && c < 20 + XCH) {                                                          \
+            const int cx = (c - 20) * NT + t;                                                     \
+            *reinterpret_cast<uint4*>(&(XS_)[(cx >> 3) * PH + (cx & 7) * 8]) = (XN_)[c - 20];     \
+          }                                                                                       \
+          if (c == 20 + XCH && (U_) == 1) TERN_WSTORE(wv, (q >> 1) + 2, q & 1);                   \
+        } else if (c == SLOTS - 1) {                                                              \
+          _Pragma("unroll") for (int q_ = 0; q_ < 4; ++q_) (D_).store(q_, WS_);                   \
+          _Pragma("unroll") for (int i = 0; i < XCH; ++i) {                                       \
+            const int cx = i * NT + t;                                                            \
+            *reinterpret_cast<uint4*>(&(XS_)[(cx >> 3) * PH + (cx & 7) * 8]) = (XN_)[i];          \
+          }                                                                                       \
+          if ((U_) == 1) TERN_WSTORE(wv, (q >> 1) + 2, q & 1);                                    \
+        }                                                                                         \
+        if (c == SLOTS - 1) {                                                                     \
+          const int g2 = (s + 2) / SPG, w2 = (s + 2) / WSTEPS;                                    \
+          (DN_).prep(g2, (s + 2) & (WSTEPS - 1), win_start<FMT>(w2), pk + (w2 % NWIN) * PBUF + dr * WP, \
+                     PNN_, ro, lut);                                                              \
+        }                                                                                         \
+        __builtin_amdgcn_sched_barrier(0);                                                        \
+      }                                                                                           \
+    }                                                                                             \
+  }
+  // Step s = 2q + U_: the products with everything else in their shadow (the
+  // decode of step s + 1 was prepared at the end of step s - 1; the last slot
+  // prepares step s + 2's), then the barrier that publishes step s + 1's LDS
+  // buffers.  Loads past the last step read past the end of
+  // x and of the packed rows, which the buffer resources answer with zeros or
+  // bytes of the next row; nothing reads what they stage.
+#define TERN_STEP(U_, XL_, PL_, XN_, DN_, DL_)                                                    \
+  do {                                                                                            \
+    const int s = 2 * q + (U_);                                                                   \
+    constexpr int AL_ = BK * ((U_) % SPG) + 32 * H;                                               \
+    const int gn = (s + 1) / SPG, gl = (s + 2) / SPG;                                             \
+    if (gl != gn) walk_next<NP>(gn, W);                                                           \
+    TERN_PRODUCTS(U_, xs + (s & 1) * XBUF, ws + (s & 1) * WBUF, XL_, PL_, AL_, XN_,              \
+                  xs + ((s + 1) & 1) * XBUF, DN_, ws + ((s + 1) & 1) * WBUF + dr * PH + 32 * H,   \
+                  DL_, PL_)                                                                       \
+    __syncthreads();                                                                              \
+  } while (0)
+
+  // prologue: windows 0 and 1 and the activation chunks of step 0 to LDS,
+  // loads of steps 0 and 1, decode of step 0
+  {
+    uint4 w00, w01, w10, w11;
+    TERN_WLOAD(w00, 0, 0);
+    TERN_WLOAD(w01, 0, 1);
+    TERN_WLOAD(w10, 1, 0);
+    TERN_WLOAD(w11, 1, 1);
+    TERN_WSTORE(w00, 0, 0);
+    TERN_WSTORE(w01, 0, 1);
+    TERN_WSTORE(w10, 1, 0);
+    TERN_WSTORE(w11, 1, 1);
+  }
+#pragma unroll
+  for (int i = 0; i < XCH; ++i)
+    xv0[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo[i], 0, 0));
+  load_step<G, NP, 32 * H>(S, 0, 0, W, P0);
+  if (SPG == 1) walk_next<NP>(0, W);
+#pragma unroll
+  for (int i = 0; i < XCH; ++i)
+    xv1[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo[i], min(1, nsteps - 1) * BK * 2, 0));
+  load_step<G, NP, (BK % G) + 32 * H>(S, 1 / SPG, min(1 / SPG, d.ng - 1), W, P1);
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) {
+    const int c = i * NT + t;
+    *reinterpret_cast<uint4*>(&xs[(c >> 3) * PH + (c & 7) * 8]) = xv0[i];
+  }
+  __syncthreads();
+  // decoders by step parity (their K offset within the group differs when a
+  // group spans two steps)
+  Dec<FMT, G, NP, 32 * H> De;
+  Dec<FMT, G, NP, (BK % G) + 32 * H> Do;
+  De.prep(0, 0, win_start<FMT>(0), pk + dr * WP, P0, ro, lut);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) De.pair(i);
+#pragma unroll
+  for (int q_ = 0; q_ < 4; ++q_) De.store(q_, &ws[dr * PH + 32 * H]);
+  Do.prep(1 / SPG, 1 & (WSTEPS - 1), win_start<FMT>(0), pk + dr * WP, P1, ro, lut);
+  __syncthreads();
+  int q = 0;
+  for (; 2 * q + 1 < nsteps; ++q) {
+    TERN_STEP(0, xv0, P0, xv1, Do, De);
+    TERN_STEP(1, xv1, P1, xv0, De, Do);
+  }
+  if (nsteps & 1) TERN_STEP(0, xv0, P0, xv1, Do, De);
+#undef TERN_STEP
+#undef TERN_PRODUCTS
+#undef TERN_WSTORE
+#undef TERN_WLOAD
+
+  // ---- epilogue: y = 0.5 * acc (the tile held 2 W~)
+  if (d.y_f32) epilogue<float, AW>(d, m0, n0, acc, reinterpret_cast<char*>(xs));
+  else epilogue<_Float16, AW>(d, m0, n0, acc, reinterpret_cast<char*>(xs));
+}
+
+// Tiles are numbered with the weight tile fastest and dealt to the XCDs in
+// contiguous runs, so the workgroups that run together on one XCD share an
+// activation tile, which then stays in that XCD's L2 (the packed weight tiles
+// are small and stream from HBM).
+template <int FMT, int G, int AW, int NP>
+__global__ __launch_bounds__(NT) void gemm_kernel(GemvDesc d, int mtiles, int ntiles, int per_xcd) {
+  constexpr int BM = 64 * AW;
+  __shared__ _Float16 xs[2 * BM * PH];
+  __shared__ _Float16 ws[2 * BN * PH];
+  __shared__ __attribute__((aligned(16))) uint8_t pk[NWIN * BN * WP];
+  __shared__ uint32_t lut[FMT == 1 ? 256 : 1];
+  const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (tile >= mtiles * ntiles) return;
+  const int m0 = (tile / ntiles) * BM, n0 = (tile % ntiles) * BN;
   if (FMT == 1) {
-    for (int v = t; v < 256; v += NT) lut[v] = v < 243 ? b3_codes(v) : 0u;
+    for (int v = threadIdx.x; v < 256; v += NT) lut[v] = v < 243 ? b3_codes(v) : 0u;
   }
-
-  f4_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
-
-  // decode assignment: thread -> weight row r = t % 128, half h = t / 128 of
-  // the group (h is wave-uniform, so the byte indices below are constants)
-  const int dr = t & (BN - 1), dh = t >> 7;
-  const int wrow = n0 + dr;
-  const bool wrow_ok = wrow < d.n;
-
-  for (int g = 0; g < d.ng; ++g) {
-    __syncthreads();
-    // ---- activation tile: BM x BK halves, 16-byte chunks
-#pragma unroll
-    for (int i = 0; i < BM * BK / 8 / NT; ++i) {
-      const int c = i * NT + t;
-      const int r = c / (BK / 8), c8 = c % (BK / 8);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m0 + r < d.m)
-        v = *reinterpret_cast<const uint4*>(d.x + (size_t)(m0 + r) * d.k + (size_t)g * BK + c8 * 8);
-      *reinterpret_cast<uint4*>(&xs[r * XP + c8 * 8]) = v;
-    }
-    // ---- weight tile: FP16 values of 2*W~ (the 0.5 is applied in the epilogue)
-    if (dh == 0)
-      decode_half<FMT, G, 0>(d, g, wrow, wrow_ok, lut, &wt[dr * XP]);
-    else
-      decode_half<FMT, G, 1>(d, g, wrow, wrow_ok, lut, &wt[dr * XP + G / 2]);
-    __syncthreads();
-    // ---- MFMA over the group
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      h8_t a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + i * 16 + (lane & 15);
-        a[i] = *reinterpret_cast<const h8_t*>(&xs[r * XP + kk + 8 * (lane >> 4)]);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wn * 64 + j * 16 + (lane & 15);
-        b[j] = *reinterpret_cast<const h8_t*>(&wt[r * XP + kk + 8 * (lane >> 4)]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-  }
-
-  // ---- epilogue
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 64 + j * 16 + (lane & 15);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + v;
-        if (m < d.m && n < d.n) {
-          if (d.y_f32)
-            reinterpret_cast<float*>(d.y)[(size_t)m * d.n + n] = 0.5f * acc[i][j][v];
-          else
-            reinterpret_cast<_Float16*>(d.y)[(size_t)m * d.n + n] = (_Float16)(0.5f * acc[i][j][v]);
-        }
-      }
-    }
-  }
+  // half of each step decoded by this thread (wave-uniform)
+  if ((threadIdx.x >> 7) == 0) gemm_body<FMT, G, AW, NP, 0>(d, m0, n0, xs, ws, pk, lut);
+  else gemm_body<FMT, G, AW, NP, 1>(d, m0, n0, xs, ws, pk, lut);
 }
 
 __global__ void zero_fill_kernel(void* y, size_t count, int f32) {
@@ -226,12 +483,29 @@ hipError_t launch_gemm(const GemvDesc& d, int format, hipStream_t s) {
     hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, d.y, count, d.y_f32);
     return hipGetLastError();
   }
-  const dim3 grid((d.n + BN - 1) / BN, (d.m + BM - 1) / BM);
-  if (format == 0 && d.group == 64) hipLaunchKernelGGL((gemm_kernel<0, 64>), grid, dim3(NT), 0, s, d);
-  else if (format == 0 && d.group == 128) hipLaunchKernelGGL((gemm_kernel<0, 128>), grid, dim3(NT), 0, s, d);
-  else if (format == 1 && d.group == 64) hipLaunchKernelGGL((gemm_kernel<1, 64>), grid, dim3(NT), 0, s, d);
-  else if (format == 1 && d.group == 128) hipLaunchKernelGGL((gemm_kernel<1, 128>), grid, dim3(NT), 0, s, d);
-  else return hipErrorInvalidValue;
+  if (!(format == 0 || format == 1) || !(d.group == 64 || d.group == 128)) return hipErrorInvalidValue;
+  // 256-row activation tiles once M fills them; 128-row tiles below
+  const int aw = d.m > 128 ? 4 : 2;
+  const int mtiles = (d.m + 64 * aw - 1) / (64 * aw), ntiles = (d.n + BN - 1) / BN;
+  const int per_xcd = (mtiles * ntiles + 7) / 8;
+  const dim3 grid(8 * per_xcd);
+#define TERN_GEMM_LAUNCH(F, G_, AW_, NP_) \
+  hipLaunchKernelGGL((gemm_kernel<F, G_, AW_, NP_>), grid, dim3(NT), 0, s, d, mtiles, ntiles, per_xcd)
+#define TERN_GEMM_NP(F, G_, AW_)                                          \
+  do {                                                                    \
+    if (d.planes == 1) TERN_GEMM_LAUNCH(F, G_, AW_, 0);                   \
+    else if (d.planes == 2) TERN_GEMM_LAUNCH(F, G_, AW_, 1);              \
+    else TERN_GEMM_LAUNCH(F, G_, AW_, 2);                                 \
+  } while (0)
+  if (format == 0) {
+    if (d.group == 64) { if (aw == 4) TERN_GEMM_NP(0, 64, 4); else TERN_GEMM_NP(0, 64, 2); }
+    else { if (aw == 4) TERN_GEMM_NP(0, 128, 4); else TERN_GEMM_NP(0, 128, 2); }
+  } else {
+    if (d.group == 64) { if (aw == 4) TERN_GEMM_NP(1, 64, 4); else TERN_GEMM_NP(1, 64, 2); }
+    else { if (aw == 4) TERN_GEMM_NP(1, 128, 4); else TERN_GEMM_NP(1, 128, 2); }
+  }
+#undef TERN_GEMM_NP
+#undef TERN_GEMM_LAUNCH
   return hipGetLastError();
 }
 

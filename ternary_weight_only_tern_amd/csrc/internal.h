@@ -20,6 +20,7 @@ struct GemvDesc {
   const uint32_t* rowptr[2];
   const uint8_t* blocks[2];
   const uint16_t* rscale[2];
+  uint32_t nnz[2];        // residual entries of planes 1 and 2
   const uint16_t* offset;
   const uint16_t* x;      // [m][k]
   void* y;                // [m][n]

@@ -174,6 +174,7 @@ void fill_desc(GemvDesc& d, const tern_matrix* w, const uint16_t* x, int m, void
     d.rowptr[p] = on ? w->rowptr[p] : nullptr;
     d.blocks[p] = on ? w->blocks[p] : nullptr;
     d.rscale[p] = on ? w->rscale[p] : nullptr;
+    d.nnz[p] = on ? w->nnz[p] : 0u;
   }
   d.offset = w->offset_mode != TERN_OFF_NONE ? w->offset : nullptr;
   d.x = x;

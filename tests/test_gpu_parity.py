@@ -294,7 +294,7 @@ def _gemm_case(mat, fmt, m, x_law="normal", f32=False, seed=0):
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("shape", SMALL_SHAPES)
-@pytest.mark.parametrize("m", [1, 64, 130])
+@pytest.mark.parametrize("m", [1, 64, 130, 257])
 def test_gemm_small(shape, fmt, m):
     n, k, g, planes, frac, off = shape
     say("gemm small", shape, fmt, m)
