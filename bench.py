@@ -205,7 +205,8 @@ def bench_stack8b(args, stream):
 
 
 def bench_gemm512(args, stream):
-    """Qwen3-8B-class layer at M=512 through the MFMA product (base-3)."""
+    """Qwen3-8B-class layer at M=512 through the matrix-core product (base-3):
+    the seven projections in one grouped launch (a plan)."""
     import torch
     from ternary_weight_only_tern_amd import lib as L
     from ternary_weight_only_tern_amd import synth
@@ -217,9 +218,8 @@ def bench_gemm512(args, stream):
         y = torch.empty((m, pm.n), dtype=torch.float16, device="cuda")
         items.append((pm, xd, y))
     flops = sum(2.0 * m * pm.n * pm.k for pm, _, _ in items)
-    fns = [(lambda pm=pm, xd=xd, y=y: L.tern_gemm(pm, xd, L.TERN_F16, out=y, stream=stream.cuda_stream))
-           for pm, xd, y in items]
-    step = lambda: [f() for f in fns]
+    plan = L.Plan([pm for pm, _, _ in items], [xd for _, xd, _ in items], [y for _, _, y in items])
+    step = lambda: plan.run(stream.cuda_stream)
     steps = max(2, args.steps // 20)
     wall, gpu, _ = time_graph([step], steps, 2, stream)
     step_s = gpu / steps

@@ -161,22 +161,26 @@ tern_status tern_gemv(const tern_matrix *w, const uint16_t *x, int32_t m, void *
 tern_status tern_gemm(const tern_matrix *w, const uint16_t *x, int32_t m, void *y,
                       int32_t y_dtype, void *ws, size_t ws_bytes, void *stream);
 
-/* Grouped decode: count independent products y[i] = x[i] W[i]^T with the same
- * m (1..63), format, group and output dtype, in one launch.
+/* Grouped product: count independent products y[i] = x[i] W[i]^T with the
+ * same m, format, group and output dtype, in one launch (the layer's
+ * projections of one token batch, say).  m <= 63 runs the decode path (as
+ * tern_gemv), m >= 64 the matrix-core path (as tern_gemm) over the output
+ * tiles of every product, products with the longest K first.
  *   w  host array [count] of descriptors
  *   x  host array [count] of device pointers, y likewise
  *   ws device workspace of tern_batch_workspace_bytes(w, count, m) bytes; a
  *      table of one work descriptor per workgroup is copied into it
  *      (hipMemcpyAsync on stream) on every call.  For repeated launches use
  *      tern_plan_create / tern_plan_run.
- * Every product of a batch covers its whole K in one workgroup: 2-bit
- * batches take k <= 16384 (TERN_E_UNSUPPORTED otherwise; use tern_gemv). */
+ * With m <= 63 every product covers its whole K in one workgroup: 2-bit
+ * batches take k <= 12288 (TERN_E_UNSUPPORTED otherwise; use tern_gemv).
+ * Products need k > 0 and group 64 or 128 (TERN_E_UNSUPPORTED otherwise). */
 size_t tern_batch_workspace_bytes(const tern_matrix *w, int32_t count, int32_t m);
 tern_status tern_gemv_batched(const tern_matrix *w, const uint16_t *const *x, void *const *y,
                               int32_t count, int32_t m, int32_t y_dtype, void *ws,
                               size_t ws_bytes, void *stream);
 
-/* A prepared grouped decode.  tern_plan_create copies the work-descriptor
+/* A prepared grouped product.  tern_plan_create copies the work-descriptor
  * table into the caller's device buffer `ws` of tern_batch_workspace_bytes bytes
  * (synchronously) and returns a host
  * handle (malloc'ed; free it with tern_plan_destroy).  tern_plan_run

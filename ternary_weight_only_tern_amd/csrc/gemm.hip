@@ -273,13 +273,18 @@ __device__ __forceinline__ void gemm_body(const GemvDesc& d, int m0, int n0, _Fl
   S.mask_v = row * (uint32_t)d.mwords * 4u;
   const uint32_t ro = __builtin_amdgcn_raw_buffer_load_b16(rsrc(d.offset, d.offset_mode == 1 ? n * 2u : 0u), row * 2u, 0, 0);
   Walk<NP> W;
+  // NP can exceed this matrix's residual planes (a grouped launch takes the
+  // most of its matrices): an absent plane's buffers are NULL and get
+  // zero-size resources, so every load from them reads zero (no residual).
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const uint32_t nnz = p == 0 ? d.nnz[0] : d.nnz[1];
-    S.mask[p] = rsrc(p == 0 ? d.mask[0] : d.mask[1], n * (uint32_t)d.mwords * 4u);
+    const bool on = p < d.planes - 1;
+    const uint32_t nnz = on ? (p == 0 ? d.nnz[0] : d.nnz[1]) : 0u;
+    S.mask[p] = rsrc(p == 0 ? d.mask[0] : d.mask[1], on ? n * (uint32_t)d.mwords * 4u : 0u);
     S.blk[p] = rsrc(p == 0 ? d.blocks[0] : d.blocks[1], nnz * (uint32_t)(G / 4));
     S.rsc[p] = rsrc(p == 0 ? d.rscale[0] : d.rscale[1], nnz * 2u);
-    W.e[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc(p == 0 ? d.rowptr[0] : d.rowptr[1], n * 4u), row * 4u, 0, 0);
+    W.e[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc(p == 0 ? d.rowptr[0] : d.rowptr[1], on ? n * 4u : 0u),
+                                                  row * 4u, 0, 0);
     W.mwl[p] = __builtin_amdgcn_raw_buffer_load_b32(S.mask[p], S.mask_v, 0, 0);
     W.mwn[p] = __builtin_amdgcn_raw_buffer_load_b32(S.mask[p], S.mask_v, d.mwords > 1 ? 4 : 0, 0);
   }
@@ -445,26 +450,39 @@ __device__ __forceinline__ void gemm_body(const GemvDesc& d, int m0, int n0, _Fl
   else epilogue<_Float16, AW>(d, m0, n0, acc, reinterpret_cast<char*>(xs));
 }
 
-// Tiles are numbered with the weight tile fastest and dealt to the XCDs in
-// contiguous runs, so the workgroups that run together on one XCD share an
-// activation tile, which then stays in that XCD's L2 (the packed weight tiles
-// are small and stream from HBM).
+// One BM x 128 output tile at (m0, n0) of the product described by d.
 template <int FMT, int G, int AW, int NP>
-__global__ __launch_bounds__(NT) void gemm_kernel(GemvDesc d, int mtiles, int ntiles, int per_xcd) {
+__device__ __forceinline__ void gemm_tile(const GemvDesc& d, int m0, int n0) {
   constexpr int BM = 64 * AW;
   __shared__ _Float16 xs[2 * BM * PH];
   __shared__ _Float16 ws[2 * BN * PH];
   __shared__ __attribute__((aligned(16))) uint8_t pk[NWIN * BN * WP];
   __shared__ uint32_t lut[FMT == 1 ? 256 : 1];
-  const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (tile >= mtiles * ntiles) return;
-  const int m0 = (tile / ntiles) * BM, n0 = (tile % ntiles) * BN;
   if (FMT == 1) {
     for (int v = threadIdx.x; v < 256; v += NT) lut[v] = v < 243 ? b3_codes(v) : 0u;
   }
   // half of each step decoded by this thread (wave-uniform)
   if ((threadIdx.x >> 7) == 0) gemm_body<FMT, G, AW, NP, 0>(d, m0, n0, xs, ws, pk, lut);
   else gemm_body<FMT, G, AW, NP, 1>(d, m0, n0, xs, ws, pk, lut);
+}
+
+// Tiles are numbered with the weight tile fastest and dealt to the XCDs in
+// contiguous runs, so the workgroups that run together on one XCD share an
+// activation tile, which then stays in that XCD's L2 (the packed weight tiles
+// are small and stream from HBM).
+template <int FMT, int G, int AW, int NP>
+__global__ __launch_bounds__(NT) void gemm_kernel(GemvDesc d, int mtiles, int ntiles, int per_xcd) {
+  const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (tile >= mtiles * ntiles) return;
+  gemm_tile<FMT, G, AW, NP>(d, (tile / ntiles) * (64 * AW), (tile % ntiles) * BN);
+}
+
+// A grouped launch: workgroup b computes the tile at (descs[b].tm0,
+// descs[b].tn0) of the product descs[b] describes.
+template <int FMT, int G, int AW, int NP>
+__global__ __launch_bounds__(NT) void gemm_grouped_kernel(const GemvDesc* __restrict__ descs) {
+  const GemvDesc d = descs[blockIdx.x];
+  gemm_tile<FMT, G, AW, NP>(d, d.tm0, d.tn0);
 }
 
 __global__ void zero_fill_kernel(void* y, size_t count, int f32) {
@@ -485,7 +503,7 @@ hipError_t launch_gemm(const GemvDesc& d, int format, hipStream_t s) {
   }
   if (!(format == 0 || format == 1) || !(d.group == 64 || d.group == 128)) return hipErrorInvalidValue;
   // 256-row activation tiles once M fills them; 128-row tiles below
-  const int aw = d.m > 128 ? 4 : 2;
+  const int aw = gemm_tile_rows(d.m) / 64;
   const int mtiles = (d.m + 64 * aw - 1) / (64 * aw), ntiles = (d.n + BN - 1) / BN;
   const int per_xcd = (mtiles * ntiles + 7) / 8;
   const dim3 grid(8 * per_xcd);
@@ -506,6 +524,31 @@ hipError_t launch_gemm(const GemvDesc& d, int format, hipStream_t s) {
   }
 #undef TERN_GEMM_NP
 #undef TERN_GEMM_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_grouped(const GemvDesc* descs, int count, int format, int group, int aw, int np,
+                               hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  if (!(format == 0 || format == 1) || !(group == 64 || group == 128) || !(aw == 2 || aw == 4) || np < 0 || np > 2)
+    return hipErrorInvalidValue;
+  const dim3 grid(count);
+#define TERN_GG(F, G_, AW_, NP_) hipLaunchKernelGGL((gemm_grouped_kernel<F, G_, AW_, NP_>), grid, dim3(NT), 0, s, descs)
+#define TERN_GG_NP(F, G_, AW_)                        \
+  do {                                                \
+    if (np == 0) TERN_GG(F, G_, AW_, 0);              \
+    else if (np == 1) TERN_GG(F, G_, AW_, 1);         \
+    else TERN_GG(F, G_, AW_, 2);                      \
+  } while (0)
+  if (format == 0) {
+    if (group == 64) { if (aw == 4) TERN_GG_NP(0, 64, 4); else TERN_GG_NP(0, 64, 2); }
+    else { if (aw == 4) TERN_GG_NP(0, 128, 4); else TERN_GG_NP(0, 128, 2); }
+  } else {
+    if (group == 64) { if (aw == 4) TERN_GG_NP(1, 64, 4); else TERN_GG_NP(1, 64, 2); }
+    else { if (aw == 4) TERN_GG_NP(1, 128, 4); else TERN_GG_NP(1, 128, 2); }
+  }
+#undef TERN_GG_NP
+#undef TERN_GG
   return hipGetLastError();
 }
 

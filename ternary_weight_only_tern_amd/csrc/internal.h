@@ -41,6 +41,8 @@ struct GemvDesc {
   // entry index (rowptr value) at each 16-row tile boundary of the item.
   const uint32_t* gidx[2];
   uint32_t tile_e[2][5];
+  // Grouped matrix-core product: origin of this workgroup's output tile.
+  int32_t tm0, tn0;
 };
 
 // ---- decode products (gemv.hip)
@@ -79,6 +81,13 @@ hipError_t launch_tile_bounds(GemvDesc* items, int count, hipStream_t stream);
 
 // ---- MFMA product (gemm.hip)
 hipError_t launch_gemm(const GemvDesc& d, int format, hipStream_t stream);
+// Activation rows per matrix-core tile for m activation rows (256 or 128).
+inline int gemm_tile_rows(int m) { return m > 128 ? 256 : 128; }
+// Grouped matrix-core product: descs (device memory) holds one descriptor per
+// workgroup with its tile origin (tm0, tn0); aw = gemm_tile_rows(m) / 64;
+// np = residual planes of the descriptor with the most (0..2).
+hipError_t launch_gemm_grouped(const GemvDesc* descs, int count, int format, int group, int aw, int np,
+                               hipStream_t stream);
 
 // ---- packing (pack.hip)
 hipError_t launch_pack_plane0(int format, const int8_t* trits, int n, int k, int group,

@@ -231,11 +231,13 @@ tern_status check_xy(const uint16_t* x, void* y, int y_dtype) {
 }  // namespace
 
 struct tern_plan {
-  const GemvDesc* dev;    // one descriptor per work item
+  const GemvDesc* dev;    // one descriptor per work item (or per output tile)
   int total_items;
   int format, group, mt;
   int max_krp;
   bool offsets;
+  bool gemm;              // m >= 64: grouped matrix-core product
+  int aw, np;             // its activation tile (aw * 64 rows) and residual planes
 };
 
 extern "C" {
@@ -421,7 +423,6 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
   if (count < 0) return fail(TERN_E_INVAL, "count=%d is negative", count);
   if (count > 0 && (!w || !x || !y)) return fail(TERN_E_INVAL, "NULL descriptor arrays");
   if (m < 0) return fail(TERN_E_INVAL, "m=%d is negative", m);
-  if (m >= 64) return fail(TERN_E_UNSUPPORTED, "batched decode takes m <= 63 (got %d)", m);
   if (y_dtype != TERN_F16 && y_dtype != TERN_F32) return fail(TERN_E_UNSUPPORTED, "unknown y dtype %d", y_dtype);
   items->clear();
   if (mat) mat->clear();
@@ -468,6 +469,54 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
   return TERN_OK;
 }
 
+// ---- grouped matrix-core products (m >= 64)
+// One descriptor per output tile (tile_rows x 128), matrices with the longest
+// K first so that their tiles start first, and within a matrix the weight
+// tile fastest.  np receives the most residual planes of any matrix.
+static tern_status build_gemm_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y,
+                                    int32_t count, int32_t m, int32_t y_dtype, std::vector<GemvDesc>* tiles,
+                                    int* np) {
+  if (count < 0) return fail(TERN_E_INVAL, "count=%d is negative", count);
+  if (count > 0 && (!w || !x || !y)) return fail(TERN_E_INVAL, "NULL descriptor arrays");
+  if (y_dtype != TERN_F16 && y_dtype != TERN_F32) return fail(TERN_E_UNSUPPORTED, "unknown y dtype %d", y_dtype);
+  tiles->clear();
+  *np = 0;
+  std::vector<int> order;
+  for (int i = 0; i < count; ++i) {
+    TERN_TRY(check_matrix(&w[i]));
+    if (w[i].format != w[0].format || w[i].group != w[0].group)
+      return fail(TERN_E_UNSUPPORTED, "batched products must share format and group");
+    if (!product_group_ok(w[i].group)) return fail(TERN_E_UNSUPPORTED, "products support group 64 or 128");
+    if (w[i].n == 0) continue;
+    if (w[i].k == 0) return fail(TERN_E_UNSUPPORTED, "batched products need k > 0");
+    TERN_TRY(check_xy(x[i], y[i], y_dtype));
+    order.push_back(i);
+    *np = std::max(*np, w[i].planes - 1);
+  }
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return w[a].k > w[b].k; });
+  const int bm = tern::gemm_tile_rows(m);
+  for (int i : order) {
+    GemvDesc d;
+    fill_desc(d, &w[i], x[i], m, y[i], y_dtype == TERN_F32);
+    for (int tm = 0; tm < m; tm += bm)
+      for (int tn = 0; tn < w[i].n; tn += 128) {
+        d.tm0 = tm;
+        d.tn0 = tn;
+        if (tiles->size() >= (size_t)INT32_MAX) return fail(TERN_E_UNSUPPORTED, "batch too large");
+        tiles->push_back(d);
+      }
+  }
+  return TERN_OK;
+}
+
+static size_t gemm_batch_tiles(const tern_matrix* w, int32_t count, int32_t m) {
+  const size_t bm = (size_t)tern::gemm_tile_rows(m);
+  size_t tiles = 0;
+  for (int i = 0; i < count; ++i)
+    if (w[i].n > 0 && w[i].k > 0) tiles += ((size_t)m + bm - 1) / bm * (((size_t)w[i].n + 127) / 128);
+  return tiles;
+}
+
 // Plans of 2-bit products also keep a residual index after the descriptor
 // table: per entry of the first residual plane, its group and scale (u32).
 static bool plan_indexes(const tern_matrix* w) {
@@ -477,6 +526,7 @@ static size_t index_bytes(const tern_matrix* w) { return plan_indexes(w) ? round
 
 size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m) {
   if (count <= 0 || m <= 0 || !w) return 0;
+  if (m >= 64) return round_up(gemm_batch_tiles(w, count, m) * sizeof(GemvDesc), 256);
   int cmax = max_mt(w[0].format, w[0].group), kmax = 0, nblk_min = 1 << 30;
   for (int i = 0; i < count; ++i) {
     if (w[i].n <= 0 || w[i].k <= 0) continue;
@@ -503,6 +553,19 @@ tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, vo
   std::vector<GemvDesc> items;
   int mt = 1, max_krp = 0;
   bool offsets = false;
+  if (m >= 64) {
+    int np = 0;
+    TERN_TRY(build_gemm_batch(w, x, y, count, m, y_dtype, &items, &np));
+    if (items.empty()) return TERN_OK;
+    const size_t need = items.size() * sizeof(GemvDesc);
+    if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "batched product needs %zu workspace bytes", need);
+    TERN_TRY(check_dev(ws, true, "ws"));
+    hipStream_t s = (hipStream_t)stream;
+    TERN_HIP(hipMemcpyAsync(ws, items.data(), need, hipMemcpyHostToDevice, s));
+    TERN_HIP(tern::launch_gemm_grouped(static_cast<const GemvDesc*>(ws), (int)items.size(), w[0].format, w[0].group,
+                                       tern::gemm_tile_rows(m) / 64, np, s));
+    return TERN_OK;
+  }
   TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets));
   if (items.empty()) return TERN_OK;
   const size_t need = items.size() * sizeof(GemvDesc);
@@ -524,6 +587,30 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
   std::vector<int> mat;
   int mt = 1, max_krp = 0;
   bool offsets = false;
+  if (m >= 64) {
+    int np = 0;
+    TERN_TRY(build_gemm_batch(w, x, y, count, m, y_dtype, &items, &np));
+    const size_t need = items.size() * sizeof(GemvDesc);
+    if (!items.empty()) {
+      if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "plan needs %zu workspace bytes", need);
+      TERN_TRY(check_dev(ws, true, "ws"));
+      TERN_HIP(hipMemcpy(ws, items.data(), need, hipMemcpyHostToDevice));
+    }
+    tern_plan* p = static_cast<tern_plan*>(std::malloc(sizeof(tern_plan)));
+    if (!p) return fail(TERN_E_INVAL, "out of host memory");
+    p->dev = static_cast<const GemvDesc*>(ws);
+    p->total_items = (int)items.size();
+    p->format = count > 0 ? w[0].format : 0;
+    p->group = count > 0 ? w[0].group : 128;
+    p->mt = 0;
+    p->max_krp = 0;
+    p->offsets = false;
+    p->gemm = true;
+    p->aw = tern::gemm_tile_rows(m) / 64;
+    p->np = np;
+    *out = p;
+    return TERN_OK;
+  }
   TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets, &mat));
   if (!items.empty()) {
     // workspace: [descriptor per work item][residual index of each matrix]
@@ -557,6 +644,8 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
   p->mt = mt;
   p->max_krp = max_krp;
   p->offsets = offsets;
+  p->gemm = false;
+  p->aw = p->np = 0;
   *out = p;
   return TERN_OK;
 }
@@ -564,6 +653,11 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
 tern_status tern_plan_run(const tern_plan* plan, void* stream) {
   if (!plan) return fail(TERN_E_INVAL, "plan is NULL");
   if (plan->total_items == 0) return TERN_OK;
+  if (plan->gemm) {
+    TERN_HIP(tern::launch_gemm_grouped(plan->dev, plan->total_items, plan->format, plan->group, plan->aw, plan->np,
+                                       (hipStream_t)stream));
+    return TERN_OK;
+  }
   GemvDesc dummy;
   std::memset(&dummy, 0, sizeof(dummy));
   TERN_HIP(launch_decode(plan->format, plan->group, plan->mt, plan->dev, plan->total_items, dummy,
