@@ -262,6 +262,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="direct launches instead of graph replay (profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 8 times (HBM counter calibration)")
+    ap.add_argument("--gemm512-only", action="store_true",
+                    help="only the M=512 matrix-core layer (profiling); prints its result, no JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -284,6 +286,11 @@ def main():
     L.load()
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
+
+    if args.gemm512_only:
+        g = bench_gemm512(args, stream)
+        log(f"bench: M=512 layer {g['step_s']*1e6:.1f} us, {g['tflops']:.1f} TFLOP/s")
+        return
 
     log("bench: packing the 4B-class layer")
     r = bench_layer4b(args, stream)
