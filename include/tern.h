@@ -148,10 +148,13 @@ tern_status tern_pack(const int8_t *trits, const uint16_t *rscale_dense, const t
 tern_status tern_unpack(const tern_matrix *src, int8_t *trits, void *ws, size_t ws_bytes,
                         void *stream);
 
-/* y = x W^T for 1 <= m <= 63 (decode path; the direct ternary product of
+/* y = x W^T for 1 <= m <= 63 (the direct ternary product of
  * "Can ternary LLMs hit 1.58 bits per weight", How It Works, and 2609.09240's
  * direct packed execution).  m == 0 is a no-op; m >= 64 is
- * TERN_E_UNSUPPORTED (use tern_gemm).  ws: tern_workspace_bytes(w, m). */
+ * TERN_E_UNSUPPORTED (use tern_gemm).  ws: tern_workspace_bytes(w, m).
+ * Up to m = 3 (base-3) or 4 (2-bit) the decode kernels run; above that the
+ * 16-row matrix-core product of tern_gemv_batched, which copies a table of
+ * work descriptors into ws (hipMemcpyAsync on stream) on each call. */
 tern_status tern_gemv(const tern_matrix *w, const uint16_t *x, int32_t m, void *y,
                       int32_t y_dtype, void *ws, size_t ws_bytes, void *stream);
 
@@ -163,17 +166,22 @@ tern_status tern_gemm(const tern_matrix *w, const uint16_t *x, int32_t m, void *
 
 /* Grouped product: count independent products y[i] = x[i] W[i]^T with the
  * same m, format, group and output dtype, in one launch (the layer's
- * projections of one token batch, say).  m <= 63 runs the decode path (as
- * tern_gemv), m >= 64 the matrix-core path (as tern_gemm) over the output
- * tiles of every product, products with the longest K first.
+ * projections of one token batch, say), products with the longest K first:
+ *   m <= 3 (base-3) or 4 (2-bit): the decode kernels, one workgroup per
+ *     block of output rows;
+ *   up to m = 63: FP16 MFMA on 16-row tiles decoded into LDS, K split into
+ *     ranges of 4-step multiples with FP32 partials summed in split order
+ *     by a second launch;
+ *   m >= 64: the matrix-core path of tern_gemm over every product's tiles.
  *   w  host array [count] of descriptors
  *   x  host array [count] of device pointers, y likewise
  *   ws device workspace of tern_batch_workspace_bytes(w, count, m) bytes; a
  *      table of one work descriptor per workgroup is copied into it
  *      (hipMemcpyAsync on stream) on every call.  For repeated launches use
  *      tern_plan_create / tern_plan_run.
- * With m <= 63 every product covers its whole K in one workgroup: 2-bit
- * batches take k <= 12288 (TERN_E_UNSUPPORTED otherwise; use tern_gemv).
+ * On the decode kernels every product covers its whole K in one workgroup:
+ * 2-bit batches of m <= 4 take k <= 12288 (TERN_E_UNSUPPORTED otherwise;
+ * use tern_gemv).
  * Products need k > 0 and group 64 or 128 (TERN_E_UNSUPPORTED otherwise). */
 size_t tern_batch_workspace_bytes(const tern_matrix *w, int32_t count, int32_t m);
 tern_status tern_gemv_batched(const tern_matrix *w, const uint16_t *const *x, void *const *y,

@@ -450,6 +450,229 @@ __device__ __forceinline__ void gemm_body(const GemvDesc& d, int m0, int n0, _Fl
   else epilogue<_Float16, AW>(d, m0, n0, acc, reinterpret_cast<char*>(xs));
 }
 
+// ---- small M (1..16 activation rows): 16 x 128 output tiles with
+// v_mfma_f32_16x16x32_f16, K split into step ranges.  Every weight of a range
+// is decoded once; the MFMAs are few, so the decode, not the matrix core,
+// sets the pace, and the step loop needs no interleaving.  The loads, the
+// LDS windows, the decode and the residual walk are those of the large-tile
+// body above.  A workgroup covers steps [s0, s1) (s0 a multiple of WSTEPS);
+// with split >= 0 it writes FP32 partial sums to
+// d.partial[split][m][n], else y.
+typedef float f4v_t __attribute__((ext_vector_type(4)));
+constexpr int BMS = 16;  // activation rows of a small tile
+
+template <int FMT, int G, int NP, int H>
+__device__ __forceinline__ void small_body(const GemvDesc& d, int n0, int s0, int s1, int split, _Float16* xs,
+                                           _Float16* ws, uint8_t* pk, const uint32_t* lut) {
+  constexpr int XBUF = BMS * PH, WBUF = BN * PH, PBUF = BN * WP;
+  constexpr int SPG = G / BK;
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int nsteps = d.ng * SPG;
+
+  f4v_t acc[2] = {f4v_t{0.f, 0.f, 0.f, 0.f}, f4v_t{0.f, 0.f, 0.f, 0.f}};
+
+  const int dr = t & (BN - 1);
+  const uint32_t row = (uint32_t)(n0 + dr);
+  Src S;
+  const uint32_t n = (uint32_t)d.n, ng = (uint32_t)d.ng, stride = (uint32_t)d.stride;
+  S.p0 = rsrc(d.plane0, n * stride);
+  S.sc = rsrc(d.scale0, n * ng * 2u);
+  S.offg = rsrc(d.offset, d.offset_mode == 2 ? n * ng * 2u : 0u);
+  S.sc_v = row * ng * 2u;
+  S.offg_v = row * ng * 2u;
+  S.mask_v = row * (uint32_t)d.mwords * 4u;
+  const uint32_t ro = __builtin_amdgcn_raw_buffer_load_b16(rsrc(d.offset, d.offset_mode == 1 ? n * 2u : 0u), row * 2u, 0, 0);
+  // residual walk at the range's first group: rowptr plus the mask bits before it
+  const int g0 = s0 / SPG;
+  Walk<NP> W;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const bool on = p < d.planes - 1;
+    const uint32_t nnz = on ? (p == 0 ? d.nnz[0] : d.nnz[1]) : 0u;
+    S.mask[p] = rsrc(p == 0 ? d.mask[0] : d.mask[1], on ? n * (uint32_t)d.mwords * 4u : 0u);
+    S.blk[p] = rsrc(p == 0 ? d.blocks[0] : d.blocks[1], nnz * (uint32_t)(G / 4));
+    S.rsc[p] = rsrc(p == 0 ? d.rscale[0] : d.rscale[1], nnz * 2u);
+    uint32_t e = __builtin_amdgcn_raw_buffer_load_b32(rsrc(p == 0 ? d.rowptr[0] : d.rowptr[1], on ? n * 4u : 0u),
+                                                      row * 4u, 0, 0);
+    {
+      // the mask words before the range's word: the first 8 requested together
+      uint32_t mw8[8];
+#pragma unroll
+      for (int w = 0; w < 8; ++w)
+        mw8[w] = __builtin_amdgcn_raw_buffer_load_b32(S.mask[p], w < (g0 >> 5) ? S.mask_v + 4u * w : kOOB, 0, 0);
+#pragma unroll
+      for (int w = 0; w < 8; ++w) e += __popc(mw8[w]);
+      for (int w = 8; w < (g0 >> 5); ++w) e += __popc(__builtin_amdgcn_raw_buffer_load_b32(S.mask[p], S.mask_v, 4 * w, 0));
+    }
+    W.mwl[p] = __builtin_amdgcn_raw_buffer_load_b32(S.mask[p], S.mask_v, 4 * (g0 >> 5), 0);
+    W.mwn[p] = __builtin_amdgcn_raw_buffer_load_b32(S.mask[p], S.mask_v, 4 * min((g0 >> 5) + 1, d.mwords - 1), 0);
+    W.e[p] = e + __popc(W.mwl[p] & ((1u << (g0 & 31)) - 1u));
+  }
+  // activation chunks: threads t < 128 take row t >> 3, chunk t & 7 (rows past m read as zero)
+  const __amdgpu_buffer_rsrc_t xr = rsrc(d.x, (uint32_t)d.m * (uint32_t)d.k * 2u);
+  const uint32_t xo = t < 128 ? (uint32_t)(t >> 3) * (uint32_t)d.k * 2u + (uint32_t)(t & 7) * 16u : kOOB;
+  const uint32_t wo = (uint32_t)(n0 + (t >> 2)) * stride + (uint32_t)(t & 3) * 16u;
+  const int w0 = s0 / WSTEPS, wlast = (nsteps - 1) / WSTEPS;
+  uint8_t* const wl = pk + (t >> 2) * WP + (t & 3) * 16;
+#define TERN_WLOAD(WV_, W_, I_)                                                                   \
+  WV_ = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(                         \
+      S.p0, wo + (uint32_t)(win_start<FMT>(min((W_), wlast)) + (I_) * 64 * (int)stride), 0, 0))
+#define TERN_WSTORE(WV_, W_, I_) \
+  *reinterpret_cast<uint4*>(wl + ((W_) % NWIN) * PBUF + (I_) * 64 * WP) = WV_
+#define TERN_XLOADS(XV_, S_) \
+  XV_ = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo, min((S_), nsteps - 1) * BK * 2, 0))
+#define TERN_XSTORES(XV_, BUF_) \
+  if (t < 128) *reinterpret_cast<uint4*>(&(BUF_)[(t >> 3) * PH + (t & 7) * 8]) = XV_
+
+  uint4 xv0, xv1, wv;
+  Pre<NP> P0, P1;
+  // Step s = s0 + 2q + U_ (buffers by relative parity): the per-step loads
+  // of step s + 3 (into the set step s + 1 used; its decode was prepared a
+  // step ago), the activation tile of step s + 2, the 4 MFMAs of step s, the
+  // decode of step s + 1 and its activation chunks to the other buffers, the
+  // preparation of step s + 2's decode (from loads issued a step ago),
+  // barrier.
+#define TERN_SSTEP(U_, XL_, PL_, PP_, XN_, DN_, DL_)                                              \
+  do {                                                                                            \
+    const int s = s0 + 2 * q + (U_);                                                              \
+    constexpr int AL_ = BK * (((U_) + 1) % SPG) + 32 * H;                                         \
+    const int g2 = (s + 2) / SPG, gl = (s + 3) / SPG;                                             \
+    if (gl != g2) walk_next<NP>(g2, W);                                                           \
+    load_step<G, NP, AL_>(S, gl, min(gl, d.ng - 1), W, PL_);                                      \
+    if ((U_) == 0) {                                                                              \
+      _Pragma("unroll") for (int p = 0; p < NP; ++p)                                              \
+        W.mwn[p] = __builtin_amdgcn_raw_buffer_load_b32(S.mask[p], S.mask_v,                      \
+                                                        4 * min((gl >> 5) + 1, d.mwords - 1), 0); \
+      TERN_WLOAD(wv, w0 + (q >> 1) + 2, q & 1);                                                   \
+    }                                                                                             \
+    TERN_XLOADS(XL_, s + 2);                                                                      \
+    {                                                                                             \
+      const _Float16* xb = xs + ((U_) & 1) * XBUF;                                                \
+      const _Float16* wb = ws + ((U_) & 1) * WBUF;                                                \
+      _Pragma("unroll") for (int kk = 0; kk < BK; kk += 32) {                                     \
+        const h8_t a = *reinterpret_cast<const h8_t*>(&xb[(lane & 15) * PH + kk + 8 * (lane >> 4)]); \
+        _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                           \
+          const h8_t b = *reinterpret_cast<const h8_t*>(                                          \
+              &wb[(32 * wave + 16 * j + (lane & 15)) * PH + kk + 8 * (lane >> 4)]);               \
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);                 \
+        }                                                                                         \
+      }                                                                                           \
+    }                                                                                             \
+    _Pragma("unroll") for (int i = 0; i < 16; ++i) (DN_).pair(i);                                 \
+    _Pragma("unroll") for (int q_ = 0; q_ < 4; ++q_)                                              \
+      (DN_).store(q_, ws + (((U_) + 1) & 1) * WBUF + dr * PH + 32 * H);                           \
+    TERN_XSTORES(XN_, xs + (((U_) + 1) & 1) * XBUF);                                              \
+    if ((U_) == 1) TERN_WSTORE(wv, w0 + (q >> 1) + 2, q & 1);                                     \
+    {                                                                                             \
+      const int wd2 = (s + 2) / WSTEPS;                                                           \
+      (DL_).prep(g2, (s + 2) & (WSTEPS - 1), win_start<FMT>(wd2), pk + (wd2 % NWIN) * PBUF + dr * WP, \
+                 PP_, ro, lut);                                                                   \
+    }                                                                                             \
+    __syncthreads();                                                                              \
+  } while (0)
+
+  // prologue: windows w0 and w0 + 1, loads of steps s0 and s0 + 1, decode of s0
+  {
+    uint4 a0, a1, b0, b1;
+    TERN_WLOAD(a0, w0, 0);
+    TERN_WLOAD(a1, w0, 1);
+    TERN_WLOAD(b0, w0 + 1, 0);
+    TERN_WLOAD(b1, w0 + 1, 1);
+    TERN_WSTORE(a0, w0, 0);
+    TERN_WSTORE(a1, w0, 1);
+    TERN_WSTORE(b0, w0 + 1, 0);
+    TERN_WSTORE(b1, w0 + 1, 1);
+  }
+  TERN_XLOADS(xv0, s0);
+  load_step<G, NP, 32 * H>(S, g0, min(g0, d.ng - 1), W, P0);
+  if (SPG == 1) walk_next<NP>(g0, W);
+  TERN_XLOADS(xv1, s0 + 1);
+  load_step<G, NP, (BK % G) + 32 * H>(S, (s0 + 1) / SPG, min((s0 + 1) / SPG, d.ng - 1), W, P1);
+  TERN_XSTORES(xv0, xs);
+  __syncthreads();
+  Dec<FMT, G, NP, 32 * H> De;
+  Dec<FMT, G, NP, (BK % G) + 32 * H> Do;
+  De.prep(g0, 0, win_start<FMT>(w0), pk + (w0 % NWIN) * PBUF + dr * WP, P0, ro, lut);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) De.pair(i);
+#pragma unroll
+  for (int q_ = 0; q_ < 4; ++q_) De.store(q_, &ws[dr * PH + 32 * H]);
+  Do.prep((s0 + 1) / SPG, 1, win_start<FMT>(w0), pk + (w0 % NWIN) * PBUF + dr * WP, P1, ro, lut);
+  {
+    // step s0 + 2's per-step loads, into the set step s0 used
+    const int g1 = (s0 + 1) / SPG, g2 = (s0 + 2) / SPG;
+    if (g2 != g1) walk_next<NP>(g1, W);
+    load_step<G, NP, 32 * H>(S, g2, min(g2, d.ng - 1), W, P0);
+  }
+  __syncthreads();
+  int q = 0;
+  for (; s0 + 2 * q + 1 < s1; ++q) {
+    TERN_SSTEP(0, xv0, P1, P0, xv1, Do, De);
+    TERN_SSTEP(1, xv1, P0, P1, xv0, De, Do);
+  }
+  if ((s1 - s0) & 1) TERN_SSTEP(0, xv0, P1, P0, xv1, Do, De);
+#undef TERN_SSTEP
+#undef TERN_XSTORES
+#undef TERN_XLOADS
+#undef TERN_WSTORE
+#undef TERN_WLOAD
+
+  // ---- epilogue: lane l holds rows 4 (l / 16) + v of columns l % 16 of its two tiles
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int nn = n0 + 32 * wave + 16 * j + (lane & 15);
+    if (nn >= d.n) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 4 * (lane >> 4) + v;
+      if (m >= d.m) continue;
+      const float val = 0.5f * acc[j][v];
+      if (split >= 0) d.partial[((size_t)split * d.m + m) * d.n + nn] = val;
+      else if (d.y_f32) reinterpret_cast<float*>(d.y)[(size_t)m * d.n + nn] = val;
+      else reinterpret_cast<_Float16*>(d.y)[(size_t)m * d.n + nn] = (_Float16)val;
+    }
+  }
+}
+
+// Grouped small-M launch: workgroup b computes the 16 x 128 tile at column
+// descs[b].tn0 over steps [descs[b].tm0, descs[b].splits) (tm0: first step,
+// splits: end step) into partial slice descs[b].gps (or y when gps < 0).
+template <int FMT, int G, int NP>
+__global__ __launch_bounds__(NT) void gemm_small_kernel(const GemvDesc* __restrict__ descs) {
+  __shared__ __attribute__((aligned(16))) _Float16 smem[2 * BMS * PH + 2 * BN * PH + NWIN * BN * WP / 2];
+  __shared__ uint32_t lut[FMT == 1 ? 256 : 1];
+  const GemvDesc d = descs[blockIdx.x];
+  _Float16* const xs = smem;
+  _Float16* const ws = smem + 2 * BMS * PH;
+  uint8_t* const pk = reinterpret_cast<uint8_t*>(smem + 2 * BMS * PH + 2 * BN * PH);
+  if (FMT == 1) {
+    for (int v = threadIdx.x; v < 256; v += NT) lut[v] = v < 243 ? b3_codes(v) : 0u;
+  }
+  if ((threadIdx.x >> 7) == 0) small_body<FMT, G, NP, 0>(d, d.tn0, d.tm0, d.splits, d.gps, xs, ws, pk, lut);
+  else small_body<FMT, G, NP, 1>(d, d.tn0, d.tm0, d.splits, d.gps, xs, ws, pk, lut);
+}
+
+// y[m][n] = sum_s partial[s][m][n] (in split order) for every product of a
+// grouped launch: block b reduces 256 outputs of product r with
+// r.begin <= b < next product's begin.
+__global__ void reduce_grouped_kernel(const RedDesc* __restrict__ rd, int count) {
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {  // last product whose first block is <= blockIdx.x
+    const int mid = (lo + hi + 1) / 2;
+    if (rd[mid].begin <= (int)blockIdx.x) lo = mid;
+    else hi = mid - 1;
+  }
+  const RedDesc r = rd[lo];
+  const size_t total = (size_t)r.m * r.n;
+  const size_t i = (size_t)(blockIdx.x - r.begin) * 256 + threadIdx.x;
+  if (i >= total) return;
+  float v = 0.f;
+  for (int sp = 0; sp < r.splits; ++sp) v += r.partial[(size_t)sp * total + i];
+  if (r.y_f32) reinterpret_cast<float*>(r.y)[i] = v;
+  else reinterpret_cast<_Float16*>(r.y)[i] = (_Float16)v;
+}
+
 // One BM x 128 output tile at (m0, n0) of the product described by d.
 template <int FMT, int G, int AW, int NP>
 __device__ __forceinline__ void gemm_tile(const GemvDesc& d, int m0, int n0) {
@@ -549,6 +772,30 @@ hipError_t launch_gemm_grouped(const GemvDesc* descs, int count, int format, int
   }
 #undef TERN_GG_NP
 #undef TERN_GG
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_small(const GemvDesc* descs, int count, int format, int group, int np, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  if (!(format == 0 || format == 1) || !(group == 64 || group == 128) || np < 0 || np > 2) return hipErrorInvalidValue;
+  const dim3 grid(count);
+#define TERN_GS(F, G_, NP_) hipLaunchKernelGGL((gemm_small_kernel<F, G_, NP_>), grid, dim3(NT), 0, s, descs)
+#define TERN_GS_NP(F, G_)                     \
+  do {                                        \
+    if (np == 0) TERN_GS(F, G_, 0);           \
+    else if (np == 1) TERN_GS(F, G_, 1);      \
+    else TERN_GS(F, G_, 2);                   \
+  } while (0)
+  if (format == 0) { if (group == 64) TERN_GS_NP(0, 64); else TERN_GS_NP(0, 128); }
+  else { if (group == 64) TERN_GS_NP(1, 64); else TERN_GS_NP(1, 128); }
+#undef TERN_GS_NP
+#undef TERN_GS
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_grouped(const RedDesc* rd, int count, int blocks, hipStream_t s) {
+  if (count <= 0 || blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(reduce_grouped_kernel, dim3(blocks), dim3(256), 0, s, rd, count);
   return hipGetLastError();
 }
 

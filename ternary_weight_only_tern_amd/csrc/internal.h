@@ -88,6 +88,20 @@ inline int gemm_tile_rows(int m) { return m > 128 ? 256 : 128; }
 // np = residual planes of the descriptor with the most (0..2).
 hipError_t launch_gemm_grouped(const GemvDesc* descs, int count, int format, int group, int aw, int np,
                                hipStream_t stream);
+// Small-M (m <= 16) matrix-core product, grouped: one descriptor per
+// workgroup, a 16 x 128 tile at column tn0 over K steps [tm0, splits) of 64;
+// partial slice gps >= 0 writes FP32 sums to partial[gps][m][n], gps < 0
+// writes y.  np as above.
+hipError_t launch_gemm_small(const GemvDesc* descs, int count, int format, int group, int np, hipStream_t stream);
+// Split sums of a grouped small-M launch: product i's blocks start at
+// rd[i].begin (ascending), 256 outputs per block.
+struct RedDesc {
+  const float* partial;  // [splits][m][n]
+  void* y;               // [m][n]
+  int32_t splits, m, n, y_f32;
+  int32_t begin;         // first block of this product
+};
+hipError_t launch_reduce_grouped(const RedDesc* rd, int count, int blocks, hipStream_t stream);
 
 // ---- packing (pack.hip)
 hipError_t launch_pack_plane0(int format, const int8_t* trits, int n, int k, int group,

@@ -237,10 +237,21 @@ struct tern_plan {
   int max_krp;
   bool offsets;
   bool gemm;              // m >= 64: grouped matrix-core product
+  bool small;             // small m on the 16-row matrix-core product
   int aw, np;             // its activation tile (aw * 64 rows) and residual planes
+  const tern::RedDesc* red;  // small: split sums to reduce (device), their count and blocks
+  int nred, red_blocks;
 };
 
 extern "C" {
+
+// Products with 4 (base-3) or 5 (2-bit) to 63 activation rows run the 16-row
+// matrix-core product, whose time is flat in m; below that the decode kernels
+// are faster (crossovers measured on an 8B-class layer on the MI355X).
+static bool small_route(int format, int m) { return m <= 63 && m >= (format == TERN_FMT_B3 ? 4 : 5); }
+
+// Workspace of a small-m product batch (defined with the batch builder).
+static size_t small_batch_ws_bytes(const tern_matrix* w, int32_t count, int32_t m);
 
 size_t tern_row_stride(int32_t k, int32_t group, int32_t format) {
   if (k < 0 || group <= 0 || k % 64 || group % 64 || group > 1024 || k % group) return 0;
@@ -275,7 +286,8 @@ tern_status tern_packed_sizes(int32_t n, int32_t k, int32_t group, int32_t forma
 size_t tern_workspace_bytes(const tern_matrix* w, int32_t m) {
   if (!w || check_shape(w->n, w->k, w->group, w->planes, w->format, w->offset_mode) != TERN_OK) return 0;
   const size_t packing = kFlagBytes + round_up(((size_t)w->n + 1) * 4, 256);
-  return std::max(packing, gemv_ws_bytes(w, m));
+  const size_t product = m > 0 && m <= 63 && small_route(w->format, m) ? small_batch_ws_bytes(w, 1, m) : gemv_ws_bytes(w, m);
+  return std::max(packing, product);
 }
 
 tern_status tern_pack(const int8_t* trits, const uint16_t* rscale_dense, const tern_matrix* dst,
@@ -371,6 +383,10 @@ tern_status tern_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* 
   if (w->k == 0) {
     TERN_HIP(tern::launch_gemm(d, w->format, s));  // ng == 0: zero fill
     return TERN_OK;
+  }
+  if (small_route(w->format, m)) {
+    void* yp = y;
+    return tern_gemv_batched(w, &x, &yp, 1, m, y_dtype, ws, ws_bytes, stream);
   }
   const int cmax = max_mt(w->format, w->group);
   int splits, gps;
@@ -509,6 +525,134 @@ static tern_status build_gemm_batch(const tern_matrix* w, const uint16_t* const*
   return TERN_OK;
 }
 
+// ---- small m on the 16-row matrix-core product
+// Decoded once per 16 activation rows, so the decode-bound small-m products
+// keep the HBM stream; K is split into step ranges (64 trits per step,
+// ranges a multiple of 4 steps) so that the grid holds about 1024 workgroups
+// and no product's K runs long in one workgroup.  Unsplit tiles write y;
+// split ones write FP32 partials that one grouped reduce sums in split order.
+
+struct SmallBatch {
+  std::vector<GemvDesc> tiles;
+  std::vector<tern::RedDesc> red;
+  size_t partial_bytes = 0;
+  int red_blocks = 0, np = 0;
+};
+
+// Step ranges of a product with `steps` steps when the batch holds `total`
+// tile-steps: a multiple of 4 steps each, at least 8, about total / 1024.
+static std::vector<int> small_ranges(int steps, long total) {
+  int u = (int)std::max<long>(8, (total / 1024 + 3) / 4 * 4);
+  const int nr = std::max(1, (steps + u - 1) / u);
+  std::vector<int> b(nr + 1, 0);
+  const int q4 = (steps + 3) / 4;  // ranges in units of 4 steps
+  for (int i = 0; i <= nr; ++i) b[i] = std::min(steps, (int)((long)q4 * i / nr) * 4);
+  b[nr] = steps;
+  std::vector<int> out;
+  for (int i = 0; i <= nr; ++i)
+    if (out.empty() || b[i] > out.back() || i == nr) out.push_back(b[i]);
+  return out;
+}
+
+// Layout of the workspace: [descriptor per tile][partials][reduce table].
+static tern_status build_small_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y, int32_t count,
+                                     int32_t m, int32_t y_dtype, char* ws, SmallBatch* out) {
+  out->tiles.clear();
+  out->red.clear();
+  out->partial_bytes = 0;
+  out->red_blocks = 0;
+  out->np = 0;
+  std::vector<int> order;
+  long total = 0;
+  for (int i = 0; i < count; ++i) {
+    TERN_TRY(check_matrix(&w[i]));
+    if (w[i].format != w[0].format || w[i].group != w[0].group)
+      return fail(TERN_E_UNSUPPORTED, "batched products must share format and group");
+    if (!product_group_ok(w[i].group)) return fail(TERN_E_UNSUPPORTED, "products support group 64 or 128");
+    if (w[i].n == 0) continue;
+    if (w[i].k == 0) return fail(TERN_E_UNSUPPORTED, "batched products need k > 0");
+    TERN_TRY(check_xy(x[i], y[i], y_dtype));
+    order.push_back(i);
+    out->np = std::max(out->np, w[i].planes - 1);
+    total += (long)((w[i].n + 127) / 128) * (w[i].k / 64) * ((m + 15) / 16);
+  }
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return w[a].k > w[b].k; });
+  const size_t esz = y_dtype == TERN_F32 ? 4 : 2;
+  // partials first need their offsets: count them in a first pass
+  size_t poff = 0;
+  std::vector<std::pair<int, std::vector<int>>> plan;  // (matrix, ranges)
+  for (int i : order) plan.push_back({i, small_ranges(w[i].k / 64, total)});
+  const size_t tiles_bytes = [&] {
+    size_t t = 0;
+    for (auto& pr : plan)
+      t += (size_t)((w[pr.first].n + 127) / 128) * (pr.second.size() - 1) * ((m + 15) / 16);
+    return round_up(t * sizeof(GemvDesc), 256);
+  }();
+  for (auto& pr : plan) {
+    const int i = pr.first;
+    const std::vector<int>& rg = pr.second;
+    const int nsplit = (int)rg.size() - 1;
+    for (int c0 = 0; c0 < m; c0 += 16) {
+      const int mc = std::min(16, m - c0);
+      GemvDesc d;
+      fill_desc(d, &w[i], x[i] + (size_t)c0 * w[i].k, mc, static_cast<char*>(y[i]) + (size_t)c0 * w[i].n * esz,
+                y_dtype == TERN_F32);
+      float* part = nullptr;
+      if (nsplit > 1) {
+        part = reinterpret_cast<float*>(ws + tiles_bytes + poff);
+        tern::RedDesc r;
+        r.partial = part;
+        r.y = d.y;
+        r.splits = nsplit;
+        r.m = mc;
+        r.n = w[i].n;
+        r.y_f32 = y_dtype == TERN_F32;
+        r.begin = out->red_blocks;
+        out->red.push_back(r);
+        out->red_blocks += (int)(((size_t)mc * w[i].n + 255) / 256);
+        poff += round_up((size_t)nsplit * mc * w[i].n * 4, 256);
+      }
+      d.partial = part;
+      for (int sp = 0; sp < nsplit; ++sp)
+        for (int tn = 0; tn < w[i].n; tn += 128) {
+          d.tn0 = tn;
+          d.tm0 = rg[sp];
+          d.splits = rg[sp + 1];
+          d.gps = nsplit > 1 ? sp : -1;
+          out->tiles.push_back(d);
+        }
+    }
+  }
+  out->partial_bytes = poff;
+  return TERN_OK;
+}
+
+static size_t small_ws_bytes(const SmallBatch& b) {
+  return round_up(b.tiles.size() * sizeof(GemvDesc), 256) + b.partial_bytes + b.red.size() * sizeof(tern::RedDesc);
+}
+
+// Workspace of a small-m batch: the layout build_small_batch makes, from the
+// shapes alone.
+static size_t small_batch_ws_bytes(const tern_matrix* w, int32_t count, int32_t m) {
+  long total = 0;
+  for (int i = 0; i < count; ++i)
+    if (w[i].n > 0 && w[i].k > 0) total += (long)((w[i].n + 127) / 128) * (w[i].k / 64) * ((m + 15) / 16);
+  size_t tiles = 0, partial = 0, nred = 0;
+  for (int i = 0; i < count; ++i) {
+    if (w[i].n <= 0 || w[i].k <= 0) continue;
+    const int nsplit = (int)small_ranges(w[i].k / 64, total).size() - 1;
+    for (int c0 = 0; c0 < m; c0 += 16) {
+      const int mc = std::min(16, m - c0);
+      tiles += (size_t)nsplit * ((w[i].n + 127) / 128);
+      if (nsplit > 1) {
+        partial += round_up((size_t)nsplit * mc * w[i].n * 4, 256);
+        ++nred;
+      }
+    }
+  }
+  return round_up(tiles * sizeof(GemvDesc), 256) + partial + nred * sizeof(tern::RedDesc);
+}
+
 static size_t gemm_batch_tiles(const tern_matrix* w, int32_t count, int32_t m) {
   const size_t bm = (size_t)tern::gemm_tile_rows(m);
   size_t tiles = 0;
@@ -527,6 +671,7 @@ static size_t index_bytes(const tern_matrix* w) { return plan_indexes(w) ? round
 size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m) {
   if (count <= 0 || m <= 0 || !w) return 0;
   if (m >= 64) return round_up(gemm_batch_tiles(w, count, m) * sizeof(GemvDesc), 256);
+  if (small_route(w[0].format, m)) return small_batch_ws_bytes(w, count, m);
   int cmax = max_mt(w[0].format, w[0].group), kmax = 0, nblk_min = 1 << 30;
   for (int i = 0; i < count; ++i) {
     if (w[i].n <= 0 || w[i].k <= 0) continue;
@@ -564,6 +709,28 @@ tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, vo
     TERN_HIP(hipMemcpyAsync(ws, items.data(), need, hipMemcpyHostToDevice, s));
     TERN_HIP(tern::launch_gemm_grouped(static_cast<const GemvDesc*>(ws), (int)items.size(), w[0].format, w[0].group,
                                        tern::gemm_tile_rows(m) / 64, np, s));
+    return TERN_OK;
+  }
+  if (count > 0 && small_route(w[0].format, m)) {
+    if (!ws) return fail(TERN_E_WORKSPACE, "batched product needs a workspace");
+    TERN_TRY(check_dev(ws, true, "ws"));
+    SmallBatch b;
+    TERN_TRY(build_small_batch(w, x, y, count, m, y_dtype, static_cast<char*>(ws), &b));
+    if (b.tiles.empty()) return TERN_OK;
+    const size_t need = small_ws_bytes(b);
+    if (ws_bytes < need) return fail(TERN_E_WORKSPACE, "batched product needs %zu workspace bytes", need);
+    hipStream_t s = (hipStream_t)stream;
+    char* base = static_cast<char*>(ws);
+    const size_t tb = round_up(b.tiles.size() * sizeof(GemvDesc), 256);
+    TERN_HIP(hipMemcpyAsync(base, b.tiles.data(), b.tiles.size() * sizeof(GemvDesc), hipMemcpyHostToDevice, s));
+    if (!b.red.empty())
+      TERN_HIP(hipMemcpyAsync(base + tb + b.partial_bytes, b.red.data(), b.red.size() * sizeof(tern::RedDesc),
+                              hipMemcpyHostToDevice, s));
+    TERN_HIP(tern::launch_gemm_small(reinterpret_cast<const GemvDesc*>(base), (int)b.tiles.size(), w[0].format,
+                                     w[0].group, b.np, s));
+    if (!b.red.empty())
+      TERN_HIP(tern::launch_reduce_grouped(reinterpret_cast<const tern::RedDesc*>(base + tb + b.partial_bytes),
+                                           (int)b.red.size(), b.red_blocks, s));
     return TERN_OK;
   }
   TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets));
@@ -606,8 +773,45 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
     p->max_krp = 0;
     p->offsets = false;
     p->gemm = true;
+    p->small = false;
     p->aw = tern::gemm_tile_rows(m) / 64;
     p->np = np;
+    p->red = nullptr;
+    p->nred = p->red_blocks = 0;
+    *out = p;
+    return TERN_OK;
+  }
+  if (count > 0 && small_route(w[0].format, m)) {
+    if (!ws) return fail(TERN_E_WORKSPACE, "plan needs a workspace");
+    TERN_TRY(check_dev(ws, true, "ws"));
+    SmallBatch b;
+    TERN_TRY(build_small_batch(w, x, y, count, m, y_dtype, static_cast<char*>(ws), &b));
+    const size_t need = small_ws_bytes(b);
+    if (!b.tiles.empty() && ws_bytes < need) return fail(TERN_E_WORKSPACE, "plan needs %zu workspace bytes", need);
+    char* base = static_cast<char*>(ws);
+    const size_t tb = round_up(b.tiles.size() * sizeof(GemvDesc), 256);
+    if (!b.tiles.empty()) {
+      TERN_HIP(hipMemcpy(base, b.tiles.data(), b.tiles.size() * sizeof(GemvDesc), hipMemcpyHostToDevice));
+      if (!b.red.empty())
+        TERN_HIP(hipMemcpy(base + tb + b.partial_bytes, b.red.data(), b.red.size() * sizeof(tern::RedDesc),
+                           hipMemcpyHostToDevice));
+    }
+    tern_plan* p = static_cast<tern_plan*>(std::malloc(sizeof(tern_plan)));
+    if (!p) return fail(TERN_E_INVAL, "out of host memory");
+    p->dev = reinterpret_cast<const GemvDesc*>(base);
+    p->total_items = (int)b.tiles.size();
+    p->format = w[0].format;
+    p->group = w[0].group;
+    p->mt = 0;
+    p->max_krp = 0;
+    p->offsets = false;
+    p->gemm = false;
+    p->small = true;
+    p->aw = 0;
+    p->np = b.np;
+    p->red = b.red.empty() ? nullptr : reinterpret_cast<const tern::RedDesc*>(base + tb + b.partial_bytes);
+    p->nred = (int)b.red.size();
+    p->red_blocks = b.red_blocks;
     *out = p;
     return TERN_OK;
   }
@@ -645,7 +849,10 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
   p->max_krp = max_krp;
   p->offsets = offsets;
   p->gemm = false;
+  p->small = false;
   p->aw = p->np = 0;
+  p->red = nullptr;
+  p->nred = p->red_blocks = 0;
   *out = p;
   return TERN_OK;
 }
@@ -656,6 +863,13 @@ tern_status tern_plan_run(const tern_plan* plan, void* stream) {
   if (plan->gemm) {
     TERN_HIP(tern::launch_gemm_grouped(plan->dev, plan->total_items, plan->format, plan->group, plan->aw, plan->np,
                                        (hipStream_t)stream));
+    return TERN_OK;
+  }
+  if (plan->small) {
+    TERN_HIP(tern::launch_gemm_small(plan->dev, plan->total_items, plan->format, plan->group, plan->np,
+                                     (hipStream_t)stream));
+    if (plan->nred)
+      TERN_HIP(tern::launch_reduce_grouped(plan->red, plan->nred, plan->red_blocks, (hipStream_t)stream));
     return TERN_OK;
   }
   GemvDesc dummy;

@@ -354,3 +354,52 @@ def test_grouped_gemm_matches_oracle(fmt, m, f32):
         else:
             for y, f in zip(ys, first):
                 assert torch.equal(y, f), "plan runs differ"
+
+
+SMALL_BATCHES = {
+    128: [(130, 1280, 128, 3, 0.2, O.OFF_ROW), (7, 2560, 128, 2, 0.1, O.OFF_NONE),
+          (64, 128, 128, 2, 1.0, O.OFF_NONE), (300, 4096, 128, 1, 0.0, O.OFF_GROUP)],
+    64: [(65, 640, 64, 2, 0.3, O.OFF_GROUP), (128, 64, 64, 1, 0.0, O.OFF_NONE),
+         (33, 3200, 64, 2, 0.5, O.OFF_ROW), (200, 1024, 64, 3, 0.15, O.OFF_NONE)],
+}
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("group", [128, 64])
+@pytest.mark.parametrize("m", [1, 3, 9, 16, 17, 40])
+def test_small_m_batches_match_oracle(fmt, group, m):
+    """Batched calls and plans at m <= 63 (16-row matrix-core product with K
+    split into step ranges and a grouped reduce for base-3 and for 2-bit
+    above 8 rows; the decode kernel below): single-step, odd-step and split
+    products, ragged rows, 1-3 planes, every offset mode, against the oracle."""
+    import torch
+    say("small m batch", fmt, group, m)
+    mats, pms, xs, ys, refs = [], [], [], [], []
+    rng = np.random.default_rng(2000 + 7 * m + group)
+    f32 = m in (9, 40)
+    for i, (n, k, g, planes, frac, off) in enumerate(SMALL_BATCHES[group]):
+        mat, _ = small_matrix(n, k, g, planes, frac, seed=31 * i + m + group, offset_mode=off, scale_law="lognormal")
+        x = synth.draw_x(rng, m, k, "student_t3")
+        mats.append(mat)
+        pms.append(upload_pack(mat, fmt))
+        xs.append(to_dev(x.view(np.uint16)).view(torch.float16))
+        ys.append(torch.empty((m, n), dtype=torch.float32 if f32 else torch.float16, device="cuda"))
+        refs.append(oracle_y(mat, x))
+    L.tern_gemv_batched(pms, xs, ys, _ydt(f32))
+    torch.cuda.synchronize()
+    for y, (y_ref, b) in zip(ys, refs):
+        check_y(y, y_ref, b, f"small batch m={m}")
+    plan = L.Plan(pms, xs, ys, _ydt(f32))
+    first = None
+    for _ in range(2):
+        for y in ys:
+            y.zero_()
+        plan.run()
+        torch.cuda.synchronize()
+        if first is None:
+            first = [y.clone() for y in ys]
+            for y, (y_ref, b) in zip(ys, refs):
+                check_y(y, y_ref, b, f"small plan m={m}")
+        else:
+            for y, f in zip(ys, first):
+                assert torch.equal(y, f), "plan runs differ"
