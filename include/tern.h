@@ -152,9 +152,10 @@ tern_status tern_unpack(const tern_matrix *src, int8_t *trits, void *ws, size_t 
  * "Can ternary LLMs hit 1.58 bits per weight", How It Works, and 2609.09240's
  * direct packed execution).  m == 0 is a no-op; m >= 64 is
  * TERN_E_UNSUPPORTED (use tern_gemm).  ws: tern_workspace_bytes(w, m).
- * Up to m = 3 (base-3) or 4 (2-bit) the decode kernels run; above that the
- * 16-row matrix-core product of tern_gemv_batched, which copies a table of
- * work descriptors into ws (hipMemcpyAsync on stream) on each call. */
+ * Up to m = 3 (base-3) or 4 (2-bit) the decode kernels run; from there to
+ * m = 32 the 16-row matrix-core product of tern_gemv_batched, which copies a
+ * table of work descriptors into ws (hipMemcpyAsync on stream) on each call;
+ * from m = 33 the tiles of tern_gemm. */
 tern_status tern_gemv(const tern_matrix *w, const uint16_t *x, int32_t m, void *y,
                       int32_t y_dtype, void *ws, size_t ws_bytes, void *stream);
 
@@ -169,10 +170,10 @@ tern_status tern_gemm(const tern_matrix *w, const uint16_t *x, int32_t m, void *
  * projections of one token batch, say), products with the longest K first:
  *   m <= 3 (base-3) or 4 (2-bit): the decode kernels, one workgroup per
  *     block of output rows;
- *   up to m = 63: FP16 MFMA on 16-row tiles decoded into LDS, K split into
+ *   up to m = 32: FP16 MFMA on 16-row tiles decoded into LDS, K split into
  *     ranges of 4-step multiples with FP32 partials summed in split order
  *     by a second launch;
- *   m >= 64: the matrix-core path of tern_gemm over every product's tiles.
+ *   m >= 33: the matrix-core path of tern_gemm over every product's tiles.
  *   w  host array [count] of descriptors
  *   x  host array [count] of device pointers, y likewise
  *   ws device workspace of tern_batch_workspace_bytes(w, count, m) bytes; a

@@ -53,7 +53,11 @@ typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;          // wavefronts per workgroup
 constexpr int kRowsWave = 16;      // output rows per wavefront (MFMA N)
 constexpr int kBlockTrits = 256;   // trits per block: 4 lanes x 64 trits of one row
-constexpr int kMaxBlocks = 12;     // blocks per wavefront (all in flight at once)
+constexpr int kMaxBlocks = 12;     // blocks per wavefront
+#ifndef TERN_MFMA_DEPTH
+#define TERN_MFMA_DEPTH 2
+#endif
+constexpr int kDepth = TERN_MFMA_DEPTH;  // weight blocks a wavefront keeps in flight
 constexpr int kZeroBytes = 128;    // zero A operands for inactive slots
 constexpr int kResCap = 64;        // residual entries listed per pass and wavefront
 constexpr int kResStage = 256;     // residual entries a workgroup stages in LDS (plan index)
@@ -71,17 +75,28 @@ __device__ __forceinline__ void wave_sync() {
 
 // B operands of the four MFMAs fed by two 2-bit words w0, w1 (32 trits):
 // b[0] = pairs 0..3 of w0, b[1] = pairs 4..7 of w0, b[2], b[3] likewise of w1.
-// One 64-bit shift serves both words: the high word picks up bits of w0 only
-// below bit 14, which the mask clears.
+// One 64-bit shift serves both words (a full-rate instruction on this GPU;
+// the compiler would otherwise split it into two 32-bit ones): the high word
+// picks up bits of w0 only below bit 14, which the mask clears.
+template <int SH>
+__device__ __forceinline__ uint64_t shl64(uint64_t v) {
+  uint64_t r;
+  asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "n"(SH), "v"(v));
+  return r;
+}
+
 __device__ __forceinline__ void decode_two(uint32_t w0, uint32_t w1, h8_t* b) {
   const uint64_t wd = ((uint64_t)w1 << 32) | w0;
   u4_t lo[2], hi[2];
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const uint64_t s = wd << (14 - 2 * p);
-    lo[p / 4][p % 4] = (uint32_t)s & 0xC000C000u;
-    hi[p / 4][p % 4] = (uint32_t)(s >> 32) & 0xC000C000u;
-  }
+#define TERN_PAIR(P)                                                                          \
+  do {                                                                                        \
+    const uint64_t s_ = (P) == 7 ? wd : shl64<14 - 2 * (P)>(wd);                              \
+    lo[(P) / 4][(P) % 4] = (uint32_t)s_ & 0xC000C000u;                                        \
+    hi[(P) / 4][(P) % 4] = (uint32_t)(s_ >> 32) & 0xC000C000u;                                \
+  } while (0)
+  TERN_PAIR(0); TERN_PAIR(1); TERN_PAIR(2); TERN_PAIR(3);
+  TERN_PAIR(4); TERN_PAIR(5); TERN_PAIR(6); TERN_PAIR(7);
+#undef TERN_PAIR
   b[0] = __builtin_bit_cast(h8_t, lo[0]);
   b[1] = __builtin_bit_cast(h8_t, lo[1]);
   b[2] = __builtin_bit_cast(h8_t, hi[0]);
@@ -162,42 +177,19 @@ __device__ __forceinline__ void decode_quarter(uint32_t v, h8_t* bb) {
   bb[1] = t[1];
 }
 
-// LDS staging of a work item once its small operands have arrived: scales
-// (flat 16-byte chunks, or per row for a K split), activations (zero past
-// the range) and the zero area.
-template <int MP, int KSF>
-__device__ __forceinline__ void stage_lds(uint8_t* lds, uint32_t scoff, uint32_t xoff, bool sflat, int nsch,
-                                          const u4_t (&sv)[KSF], const GLOBAL uint16_t* s0, uintptr_t send,
-                                          uintptr_t sa0, int ngr, int rw, int spitch, int row0, int n, int ng,
-                                          int ga, int nx, int cpr, int krp, int kr, const u4_t (&xv)[8], int tid) {
-  uint16_t* ssm = reinterpret_cast<uint16_t*>(lds + scoff);
-  if (sflat) {
-#pragma unroll
-    for (int u = 0; u < KSF; ++u)
-      if (u * kThreads + tid < nsch) *reinterpret_cast<u4_t*>(lds + scoff + (u * kThreads + tid) * 16) = sv[u];
-    for (int c = KSF * kThreads + tid; c < nsch; c += kThreads)  // long ranges
-      *reinterpret_cast<u4_t*>(lds + scoff + c * 16) = scale_chunk(s0, send, sa0 + (size_t)c * 16);
-  } else {
-    // K split: the item's groups of each row (thread -> groups 32c + sgl, rows srr + 8u)
-    const int sgl = tid % 32, srr = tid / 32;
-    for (int c = 0; c * 32 < ngr; ++c) {
-      const int g = c * 32 + sgl;
-      if (g < ngr)
-        for (int u = 0; u < rw / 8; ++u)
-          ssm[(srr + 8 * u) * spitch + g] = s0[(size_t)min(row0 + srr + 8 * u, n - 1) * ng + ga + g];
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int id = u * kThreads + tid;
-    if (u * kThreads < nx && id < nx) {
-      const int m = xrow_of<MP>(id, cpr);
-      const int kk = (id - m * cpr) * 8;
-      *reinterpret_cast<u4_t*>(lds + xoff + (size_t)m * krp * 2 + kk * 2) = kk < kr ? xv[u] : u4_t{0u, 0u, 0u, 0u};
-    }
-  }
-  if (tid < kZeroBytes / 16) *reinterpret_cast<u4_t*>(lds + tid * 16) = u4_t{0u, 0u, 0u, 0u};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
+
+// 16 bytes per lane from a buffer straight into LDS, without registers: lane
+// l of the wavefront writes dst + 16 l, so dst must be the same in every lane
+// (the chunk of the wavefront's first lane).  Counted by vmcnt like a load.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) alone (expcnt and lgkmcnt left free), n <= 63.
+#define TERN_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
 
 template <int MP>
 struct Win {
@@ -285,29 +277,48 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
   const int cpr = krp / 8;   // 16-byte activation chunks per activation row
   const int nx = dm * cpr;   // at most 2048: MP * krp <= 16384
 
-  // ---- 1. loads of the small operands, then the first weights; only the
-  // small operands are waited for before the main loop
-  // scales, flat: 16-byte chunks covering this item's rows (they are
-  // contiguous), from the 16-byte boundary at or below the first scale
+  // ---- 1. the small operands go straight into LDS (no registers), then
+  // every wavefront requests its weights (below); the workgroup waits for the
+  // small operands only, so the weight stream starts right after the
+  // descriptor.  Scales, flat: 16-byte chunks covering this item's rows
+  // (they are contiguous), from the 16-byte boundary at or below the first
+  // scale; a chunk that reaches past the scale array goes through registers.
   const uintptr_t sfirst = (uintptr_t)(s0 + (size_t)row0 * d.ng);
   const uintptr_t sa0 = sfirst & ~(uintptr_t)15;
   const int sshift = (int)(sfirst - sa0) / 2;  // elements before row0's first scale
   const int nsch = sflat ? (int)(((uintptr_t)(s0 + (size_t)min(row0 + rw, d.n) * d.ng) - sa0 + 15) / 16) : 0;
-  constexpr int kSF = 4;  // chunk rounds loaded ahead (more are staged afterwards)
   const uintptr_t send = (uintptr_t)(s0 + (size_t)d.n * d.ng);  // end of the scale array
-  u4_t sv[kSF];
-#pragma unroll
-  for (int u = 0; u < kSF; ++u)
-    if (u * kThreads < nsch) sv[u] = scale_chunk(s0, send, sa0 + (size_t)min(u * kThreads + tid, nsch - 1) * 16);
-  // activations [dm][krp] (one round always suffices)
-  u4_t xv[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    if (u * kThreads < nx) {
-      const int id = min(u * kThreads + tid, nx - 1);
-      const int m = xrow_of<MP>(id, cpr);
-      const int kk = min((id - m * cpr) * 8, kr - 8);
-      xv[u] = *reinterpret_cast<const GLOBAL u4_t*>(gp(d.x) + (size_t)m * d.k + k0 + kk);
+  const int nsfull = min(nsch, (int)((send - sa0) / 16));       // chunks wholly inside it
+  if (sflat) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(d.scale0, (uint32_t)(send - (uintptr_t)s0));
+    const uint32_t sv0 = (uint32_t)(sa0 - (uintptr_t)s0);
+    for (int u = 0; u * kThreads < nsfull; ++u)
+      if (u * kThreads + tid < nsfull)
+        lds_load16(rs, lds + scoff + (u * kThreads + wave * kWave) * 16, sv0 + (u * kThreads + tid) * 16);
+  } else {
+    // K split: the item's groups of each row (thread -> groups 32c + sgl, rows srr + 8u)
+    uint16_t* ssm = reinterpret_cast<uint16_t*>(lds + scoff);
+    const int sgl = tid % 32, srr = tid / 32;
+    for (int c = 0; c * 32 < ngr; ++c) {
+      const int g = c * 32 + sgl;
+      if (g < ngr)
+        for (int u = 0; u < rw / 8; ++u)
+          ssm[(srr + 8 * u) * spitch + g] = s0[(size_t)min(row0 + srr + 8 * u, d.n - 1) * d.ng + ga + g];
+    }
+  }
+  u4_t sfix = u4_t{0u, 0u, 0u, 0u};
+  if (tid < nsch - nsfull) sfix = scale_chunk(s0, send, sa0 + (size_t)(nsfull + tid) * 16);
+  // activations [dm][krp], row m at m * krp (chunk id at 16 id); zero past the range
+  {
+    const __amdgpu_buffer_rsrc_t rx = rsrc(d.x, (uint32_t)dm * d.k * 2u);
+    for (int u = 0; u * kThreads < nx; ++u) {
+      const int id = u * kThreads + tid;
+      if (id < nx) {
+        const int m = xrow_of<MP>(id, cpr);
+        const int kk = (id - m * cpr) * 8;
+        if (kk < kr) lds_load16(rx, lds + xoff + (u * kThreads + wave * kWave) * 16, ((uint32_t)m * d.k + k0 + kk) * 2u);
+        else *reinterpret_cast<u4_t*>(lds + xoff + id * 16) = u4_t{0u, 0u, 0u, 0u};
+      }
     }
   }
   // first residual plane, when the plan indexed it and the item covers the
@@ -328,17 +339,18 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
   const int gshift = (int)(gfirst - ga0) / 4;
   const int nbch = (int)nres * kBQ;                        // block chunks
   const int ngch = res_idx ? (int)(((uintptr_t)(gix + e1) - ga0 + 15) / 16) : 0;  // index chunks
-  constexpr int kRS = (kResStage * kBQ + kResStage / 4 + 1 + kThreads - 1) / kThreads;
-  u4_t rv[kRS];
-#pragma unroll
-  for (int u = 0; u < kRS; ++u) {
-    if (u * kThreads < nbch + ngch) {
-      const int c = min(u * kThreads + tid, nbch + ngch - 1);
-      if (c < nbch)
-        rv[u] = *reinterpret_cast<const GLOBAL u4_t*>(gp(d.blocks[0]) + ((size_t)e0 * kBQ + c) * 16);
-      else
-        rv[u] = *reinterpret_cast<const GLOBAL u4_t*>(ga0 + (size_t)(c - nbch) * 16);
-    }
+  if (res_idx) {
+    // the index array sits in a 256-byte-rounded allocation of 16-byte aligned start
+    const __amdgpu_buffer_rsrc_t rb = rsrc(d.blocks[0], d.nnz[0] * (uint32_t)(G / 4));
+    const __amdgpu_buffer_rsrc_t rg = rsrc(d.gidx[0], (d.nnz[0] * 4u + 15u) & ~15u);
+    for (int u = 0; u * kThreads < nbch; ++u)
+      if (u * kThreads + tid < nbch)
+        lds_load16(rb, lds + rstoff + (u * kThreads + wave * kWave) * 16, (e0 * kBQ + u * kThreads + tid) * 16u);
+    const uint32_t gv0 = (uint32_t)(ga0 - (uintptr_t)gix);
+    for (int u = 0; u * kThreads < ngch; ++u)
+      if (u * kThreads + tid < ngch)
+        lds_load16(rg, lds + rstoff + kResStage * (G / 4) + (u * kThreads + wave * kWave) * 16,
+                   gv0 + (u * kThreads + tid) * 16u);
   }
   // this row's entries, for the sums
   uint32_t rp0 = 0, rp1 = 0;
@@ -347,6 +359,18 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
     rp1 = gp(d.rowptr[0])[rowc + 1];
   }
 
+  // this wavefront's share of the staged entries (relative to e0): those of
+  // its tile's rows, split evenly over the tile's kw wavefronts; their values
+  // are computed between its plane-0 blocks and summed by this wavefront
+  uint32_t we0 = 0, we1 = 0;
+  if (res_idx) {
+    const uint32_t tb = tile == 0 ? d.tile_e[0][0] : tile == 1 ? d.tile_e[0][1] : tile == 2 ? d.tile_e[0][2] : d.tile_e[0][3];
+    const uint32_t te = tile == 0 ? d.tile_e[0][1] : tile == 1 ? d.tile_e[0][2] : tile == 2 ? d.tile_e[0][3] : d.tile_e[0][4];
+    const uint32_t ps = (te - tb + kw - 1) / kw;
+    we0 = min(te, tb + kp * ps) - e0;
+    we1 = min(te, tb + (kp + 1) * ps) - e0;
+  }
+  const int nrb = (int)((we1 - we0 + 15u) / 16u);  // this wavefront's 16-entry batches
   float* valw = reinterpret_cast<float*>(lds + valoff) + (size_t)wave * kResCap * MP;  // this wave's
   float* valr = reinterpret_cast<float*>(lds + valoff);  // staged entries' values [entry][m]
   uint32_t* ent = reinterpret_cast<uint32_t*>(lds + entoff);
@@ -385,6 +409,15 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
         if (q == r / 4 && ok_) (VAL)[t_ * MP + m] = (RSV) * R_[r % 4];                        \
       }                                                                                       \
     }                                                                                         \
+  } while (0)
+  // batch J of this wavefront's share of the staged entries
+#define TERN_RES_ONE(J)                                                                       \
+  do {                                                                                        \
+    const uint32_t b0_ = we0 + 16u * (uint32_t)(J);                                           \
+    const uint32_t t_ = min(b0_ + r, we1 - 1);                                                \
+    const RB bq_ = *reinterpret_cast<const RB*>(lds + rstoff + t_ * (G / 4) + q * sizeof(RB)); \
+    const uint32_t gi_ = *reinterpret_cast<const uint32_t*>(lds + rstoff + kResStage * (G / 4) + (gshift + t_) * 4); \
+    TERN_RES_BATCH(valr, b0_, we1, bq_, (int)(gi_ & 0xFFFFu), 0.5f * h2f((uint16_t)(gi_ >> 16))); \
   } while (0)
   // each owner adds its row's entries of the window [W0, W0 + WN) in order
 #define TERN_RES_SUM(PRE, CNT, W0, WN)                                                        \
@@ -431,32 +464,27 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
 #define TERN_BODY(NB)                                                                         \
   do {                                                                                        \
     u4_t w_[NB];                                                                              \
-    stage_lds<MP, kSF>(lds, scoff, xoff, sflat, nsch, sv, s0, send, sa0, ngr, rw, spitch, row0,         \
-              d.n, d.ng, ga, nx, cpr, krp, kr, xv, tid);                                      \
-    _Pragma("unroll") for (int u = 0; u < kRS; ++u) {                                         \
-      const int c_ = u * kThreads + tid;                                                      \
-      if (u * kThreads < nbch + ngch && c_ < nbch + ngch)                                     \
-        *reinterpret_cast<u4_t*>(lds + rstoff + (c_ < nbch ? c_ * 16 : kResStage * (G / 4) + (c_ - nbch) * 16)) = rv[u]; \
-    }                                                                                         \
+    /* the weights, behind the small operands in every wavefront's queue */                  \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    constexpr int DP_ = NB < kDepth ? NB : kDepth;                                            \
+    _Pragma("unroll") for (int i = 0; i < DP_; ++i) w_[i] = wload(wr, min(i, max(nblk - 1, 0)), q, rbytes); \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    if (tid < nsch - nsfull) *reinterpret_cast<u4_t*>(lds + scoff + (nsfull + tid) * 16) = sfix; \
+    if (tid < kZeroBytes / 16) *reinterpret_cast<u4_t*>(lds + tid * 16) = u4_t{0u, 0u, 0u, 0u}; \
+    TERN_WAIT_VM(DP_); /* this wavefront's LDS loads have landed */                          \
     __syncthreads();                                                                          \
-    /* the weights, once the small operands have landed (issued earlier they */               \
-    /* would queue the small operands behind every wavefront's weights) */                    \
-    _Pragma("unroll") for (int i = 0; i < NB; ++i) w_[i] = wload(wr, min(i, max(nblk - 1, 0)), q, rbytes); \
-    /* residual batches of the staged entries, spread over the wavefronts */                 \
-    for (uint32_t b0_ = 16u * wave; b0_ < nres; b0_ += 16u * kWaves) {                         \
-      const uint32_t t_ = min(b0_ + r, nres - 1);                                             \
-      const RB bq_ = *reinterpret_cast<const RB*>(lds + rstoff + t_ * (G / 4) + q * sizeof(RB)); \
-      const uint32_t gi_ = *reinterpret_cast<const uint32_t*>(lds + rstoff + kResStage * (G / 4) + (gshift + t_) * 4); \
-      TERN_RES_BATCH(valr, b0_, nres, bq_, (int)(gi_ & 0xFFFFu), 0.5f * h2f((uint16_t)(gi_ >> 16))); \
-    }                                                                                         \
-    /* plane 0 */                                                                             \
+    /* plane 0, with this wavefront's residual batches after its first blocks */            \
     _Pragma("unroll") for (int i = 0; i < NB; ++i) {                                          \
+      /* keep DP_ blocks in flight: request block i + DP_ before block i is used */          \
+      if (i + DP_ < NB) w_[i + DP_] = wload(wr, min(i + DP_, max(nblk - 1, 0)), q, rbytes);     \
       if (i < nblk) {                                                                         \
         TERN_BLOCK(w_[i], i, i);                                                              \
         if (i % BW == BW - 1) TERN_CLOSE(i / BW);                                             \
       }                                                                                       \
+      if (i < nrb) TERN_RES_ONE(i);                                                           \
     }                                                                                         \
     if (nblk > 0 && nblk % BW != 0) TERN_CLOSE((nblk - 1) / BW);                              \
+    for (int j_ = NB; j_ < nrb; ++j_) TERN_RES_ONE(j_);                                       \
   } while (0)
   if (bpp > 8) TERN_BODY(kMaxBlocks);
   else TERN_BODY(8);
@@ -530,6 +558,7 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
       if (cnt) TERN_RES_SUM(pre_r, cnt, w0, wn);
     }
   }
+#undef TERN_RES_ONE
 #undef TERN_RES_BATCH
 #undef TERN_RES_SUM
 
@@ -545,35 +574,20 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
       xsum[id] = s;
     }
   }
-  // ---- the parts of a row tile, summed in part order
-  float* red = reinterpret_cast<float*>(lds + redoff);
-  if (kw > 1) {
-#pragma unroll
-    for (int i = 0; i < NACC; ++i)
-      if (owner && m_of[i] < dm) red[(wave * MP + m_of[i]) * kRowsWave + r] = acc[i];
-  }
-  if (kw > 1 || d.offset_mode != 0 || res_idx) __syncthreads();
-  if (kp != 0) return;
-  if (kw > 1) {
-#pragma unroll
-    for (int i = 0; i < NACC; ++i) {
-      if (owner && m_of[i] < dm) {
-        float v = red[((tile * kw) * MP + m_of[i]) * kRowsWave + r];
-        for (int pp = 1; pp < kw; ++pp) v += red[((tile * kw + pp) * MP + m_of[i]) * kRowsWave + r];
-        acc[i] = v;
-      }
-    }
-  }
-  // staged residual entries of this row: the row's four lanes take every
-  // fourth entry, then the quarters are added (fixed order)
+  // staged residual entries of this row in this wavefront's share: the row's
+  // four lanes take every fourth entry, then the quarters are added (fixed
+  // order); the parts of a tile add their shares with the part sums below
   if (res_idx) {
+    wave_sync();
     float rsum[MP];
 #pragma unroll
     for (int m = 0; m < MP; ++m) rsum[m] = 0.f;
-    if (row_ok)
-      for (uint32_t e = rp0 + q; e < rp1; e += 4)
+    if (row_ok) {
+      const uint32_t lo = max(rp0 - e0, we0), hi = min(rp1 - e0, we1);
+      for (uint32_t e = lo + q; e < hi; e += 4)
 #pragma unroll
-        for (int m = 0; m < MP; ++m) rsum[m] += valr[(e - e0) * MP + m];
+        for (int m = 0; m < MP; ++m) rsum[m] += valr[e * MP + m];
+    }
 #pragma unroll
     for (int m = 0; m < MP; ++m) {
       rsum[m] += __shfl_xor(rsum[m], 16, kWave);
@@ -587,6 +601,25 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
         for (int m = 0; m < MP; ++m) v = m == m_of[i] ? rsum[m] : v;
         acc[i] += v;
       }
+  }
+  // ---- the parts of a row tile, summed in part order
+  float* red = reinterpret_cast<float*>(lds + redoff);
+  if (kw > 1) {
+#pragma unroll
+    for (int i = 0; i < NACC; ++i)
+      if (owner && m_of[i] < dm) red[(wave * MP + m_of[i]) * kRowsWave + r] = acc[i];
+  }
+  if (kw > 1 || d.offset_mode != 0) __syncthreads();
+  if (kp != 0) return;
+  if (kw > 1) {
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) {
+      if (owner && m_of[i] < dm) {
+        float v = red[((tile * kw) * MP + m_of[i]) * kRowsWave + r];
+        for (int pp = 1; pp < kw; ++pp) v += red[((tile * kw + pp) * MP + m_of[i]) * kRowsWave + r];
+        acc[i] = v;
+      }
+    }
   }
   // ---- offsets over the item's range
   if (d.offset_mode != 0) {

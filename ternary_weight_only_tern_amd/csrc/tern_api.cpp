@@ -236,7 +236,7 @@ struct tern_plan {
   int format, group, mt;
   int max_krp;
   bool offsets;
-  bool gemm;              // m >= 64: grouped matrix-core product
+  bool gemm;              // m >= 33: grouped matrix-core product
   bool small;             // small m on the 16-row matrix-core product
   int aw, np;             // its activation tile (aw * 64 rows) and residual planes
   const tern::RedDesc* red;  // small: split sums to reduce (device), their count and blocks
@@ -245,10 +245,12 @@ struct tern_plan {
 
 extern "C" {
 
-// Products with 4 (base-3) or 5 (2-bit) to 63 activation rows run the 16-row
-// matrix-core product, whose time is flat in m; below that the decode kernels
-// are faster (crossovers measured on an 8B-class layer on the MI355X).
-static bool small_route(int format, int m) { return m <= 63 && m >= (format == TERN_FMT_B3 ? 4 : 5); }
+// Routing of products by activation rows (crossovers measured on an
+// 8B-class layer on the MI355X): the decode kernels up to m = 3 (base-3) or
+// 4 (2-bit), the 16-row matrix-core product up to m = 32 (its time grows per
+// 16 rows), the 128/256-row matrix-core tiles from m = 33.
+static bool gemm_route(int m) { return m >= 33; }
+static bool small_route(int format, int m) { return !gemm_route(m) && m >= (format == TERN_FMT_B3 ? 4 : 5); }
 
 // Workspace of a small-m product batch (defined with the batch builder).
 static size_t small_batch_ws_bytes(const tern_matrix* w, int32_t count, int32_t m);
@@ -286,7 +288,7 @@ tern_status tern_packed_sizes(int32_t n, int32_t k, int32_t group, int32_t forma
 size_t tern_workspace_bytes(const tern_matrix* w, int32_t m) {
   if (!w || check_shape(w->n, w->k, w->group, w->planes, w->format, w->offset_mode) != TERN_OK) return 0;
   const size_t packing = kFlagBytes + round_up(((size_t)w->n + 1) * 4, 256);
-  const size_t product = m > 0 && m <= 63 && small_route(w->format, m) ? small_batch_ws_bytes(w, 1, m) : gemv_ws_bytes(w, m);
+  const size_t product = m > 0 && small_route(w->format, m) ? small_batch_ws_bytes(w, 1, m) : gemv_ws_bytes(w, m);
   return std::max(packing, product);
 }
 
@@ -380,8 +382,8 @@ tern_status tern_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* 
   const int y_f32 = y_dtype == TERN_F32;
   GemvDesc d;
   fill_desc(d, w, x, m, y, y_f32);
-  if (w->k == 0) {
-    TERN_HIP(tern::launch_gemm(d, w->format, s));  // ng == 0: zero fill
+  if (w->k == 0 || gemm_route(m)) {
+    TERN_HIP(tern::launch_gemm(d, w->format, s));  // k == 0: zero fill
     return TERN_OK;
   }
   if (small_route(w->format, m)) {
@@ -485,7 +487,7 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
   return TERN_OK;
 }
 
-// ---- grouped matrix-core products (m >= 64)
+// ---- grouped matrix-core products (m >= 33)
 // One descriptor per output tile (tile_rows x 128), matrices with the longest
 // K first so that their tiles start first, and within a matrix the weight
 // tile fastest.  np receives the most residual planes of any matrix.
@@ -670,7 +672,7 @@ static size_t index_bytes(const tern_matrix* w) { return plan_indexes(w) ? round
 
 size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m) {
   if (count <= 0 || m <= 0 || !w) return 0;
-  if (m >= 64) return round_up(gemm_batch_tiles(w, count, m) * sizeof(GemvDesc), 256);
+  if (gemm_route(m)) return round_up(gemm_batch_tiles(w, count, m) * sizeof(GemvDesc), 256);
   if (small_route(w[0].format, m)) return small_batch_ws_bytes(w, count, m);
   int cmax = max_mt(w[0].format, w[0].group), kmax = 0, nblk_min = 1 << 30;
   for (int i = 0; i < count; ++i) {
@@ -698,7 +700,7 @@ tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, vo
   std::vector<GemvDesc> items;
   int mt = 1, max_krp = 0;
   bool offsets = false;
-  if (m >= 64) {
+  if (gemm_route(m)) {
     int np = 0;
     TERN_TRY(build_gemm_batch(w, x, y, count, m, y_dtype, &items, &np));
     if (items.empty()) return TERN_OK;
@@ -754,7 +756,7 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
   std::vector<int> mat;
   int mt = 1, max_krp = 0;
   bool offsets = false;
-  if (m >= 64) {
+  if (gemm_route(m)) {
     int np = 0;
     TERN_TRY(build_gemm_batch(w, x, y, count, m, y_dtype, &items, &np));
     const size_t need = items.size() * sizeof(GemvDesc);
