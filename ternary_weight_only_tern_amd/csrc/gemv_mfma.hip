@@ -209,9 +209,12 @@ constexpr int res_wave_bytes() { return kResCap * 8 + kResCap * MP * 4; }
 // staged residual entries: blocks (G/4 bytes each), then index chunks
 template <int G>
 constexpr int res_stage_bytes() { return kResStage * (G / 4) + (kResStage / 4 + 1) * 16; }
+// Wavefronts per SIMD the kernel's registers are sized for (at least).
+template <int G, int MP>
+constexpr int mfma_waves_per_eu() { return MP == 8 || (G == 64 && MP == 4) ? 2 : 3; }
 
 template <int G, int MP>
-__global__ __launch_bounds__(kWave * kWaves) __attribute__((amdgpu_waves_per_eu(MP == 8 || (G == 64 && MP == 4) ? 2 : 3, 8)))
+__global__ __launch_bounds__(kWave * kWaves) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<G, MP>(), 8)))
 void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc one) {
   constexpr int GW = Win<MP>::GW;
   constexpr int NACC = Win<MP>::NACC;
@@ -237,7 +240,7 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
   const int kw = d.kwaves;
   const int rw = kRowsWave * (kWaves / kw);   // rows per work item
   const int tile = wave / kw, kp = wave % kw;
-  const int row0 = rb * rw;
+  const int row0 = d.row_base + rb * rw;
   const int row = row0 + tile * kRowsWave + r;
   const bool row_ok = row < d.n;
   const int rowc = row_ok ? row : d.n - 1;  // clamped: loads stay in bounds
@@ -656,13 +659,20 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
   }
 }
 
+// Dynamic LDS of a launch (the layout the kernel computes, at its largest).
 template <int G, int MP>
-hipError_t launch_mfma(const GemvDesc* descs, int ndesc, const GemvDesc& one, int items, int max_krp, bool offsets,
-                       hipStream_t s) {
+size_t mfma_lds_bytes(int max_krp, bool offsets) {
   const int ngr = max_krp / G;
   size_t lds = kZeroBytes + (size_t)MP * max_krp * 2 + ((size_t)kGemvRows * ngr * 2 + 32 + 15) / 16 * 16 +
                (size_t)kWaves * res_wave_bytes<MP>() + res_stage_bytes<G>() + (size_t)kWaves * MP * kRowsWave * 4;
   if (offsets) lds += (size_t)MP * (max_krp / G) * 4;
+  return lds;
+}
+
+template <int G, int MP>
+hipError_t launch_mfma(const GemvDesc* descs, int ndesc, const GemvDesc& one, int items, int max_krp, bool offsets,
+                       hipStream_t s) {
+  const size_t lds = mfma_lds_bytes<G, MP>(max_krp, offsets);
   hipLaunchKernelGGL((gemv_mfma_kernel<G, MP>), dim3(items), dim3(kWave * kWaves), lds, s, descs, ndesc, one);
   return hipGetLastError();
 }
@@ -702,7 +712,7 @@ __global__ void tile_bounds_kernel(GemvDesc* items, int count) {
   if (i >= count) return;
   GemvDesc* d = items + i;
   const int item = i - d->tile_begin;
-  const int row0 = (item % d->row_blocks) * kRowsWave * (kWaves / d->kwaves);
+  const int row0 = d->row_base + (item % d->row_blocks) * kRowsWave * (kWaves / d->kwaves);
   for (int p = 0; p < 2; ++p) {
     if (!d->gidx[p]) continue;
     for (int t = 0; t < 5; ++t) d->tile_e[p][t] = d->rowptr[p][min(row0 + kRowsWave * t, d->n)];
@@ -726,6 +736,23 @@ hipError_t launch_tile_bounds(GemvDesc* items, int count, hipStream_t s) {
 }
 
 int gemv_mfma_max_rows(int group) { return group == 128 ? 8 : 4; }
+
+int gemv_mfma_wgs_per_cu(int group, int mp, int max_krp, bool offsets) {
+  // 160 KB of LDS per CU; one wavefront of a workgroup per SIMD
+  size_t lds = 0;
+  int wpe = 3;
+  if (group == 128) {
+    lds = mp == 1 ? mfma_lds_bytes<128, 1>(max_krp, offsets) : mp == 2 ? mfma_lds_bytes<128, 2>(max_krp, offsets)
+        : mp == 4 ? mfma_lds_bytes<128, 4>(max_krp, offsets) : mfma_lds_bytes<128, 8>(max_krp, offsets);
+    wpe = mp == 8 ? mfma_waves_per_eu<128, 8>() : 3;
+  } else {
+    lds = mp == 1 ? mfma_lds_bytes<64, 1>(max_krp, offsets) : mp == 2 ? mfma_lds_bytes<64, 2>(max_krp, offsets)
+        : mfma_lds_bytes<64, 4>(max_krp, offsets);
+    wpe = mp == 4 ? mfma_waves_per_eu<64, 4>() : 3;
+  }
+  const int by_lds = lds ? (int)((160u * 1024u) / lds) : wpe;
+  return std::max(1, std::min(by_lds, wpe));
+}
 
 int gemv_mfma_max_range(int mp) { return std::min(16384 / mp, kMaxBlocks * kBlockTrits * kWaves); }
 

@@ -43,6 +43,9 @@ struct GemvDesc {
   uint32_t tile_e[2][5];
   // Grouped matrix-core product: origin of this workgroup's output tile.
   int32_t tm0, tn0;
+  // Matrix-core decode kernel: first row of this descriptor's row range
+  // (a matrix may be covered by two ranges with different kwaves).
+  int32_t row_base;
 };
 
 // ---- decode products (gemv.hip)
@@ -64,6 +67,9 @@ int gemv_stage_groups(int format, int group);
 // K range (trits) one work item stages, for `mp` padded activation rows.
 int gemv_mfma_max_rows(int group);
 int gemv_mfma_max_range(int mp);
+// Workgroups of the matrix-core decode kernel that one CU holds at once
+// (LDS and register limits) for a launch with these parameters.
+int gemv_mfma_wgs_per_cu(int group, int mp, int max_krp, bool offsets);
 // Same descriptors and work items as launch_gemv; a work item is 64 / kwaves
 // rows; K splits start on 256-trit blocks.  max_krp = the longest range of
 // any descriptor rounded up to 256; offsets = some descriptor has an offset.

@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <queue>
 #include <vector>
 
 #include "internal.h"
@@ -431,6 +432,120 @@ tern_status tern_gemm(const tern_matrix* w, const uint16_t* x, int32_t m, void* 
   return TERN_OK;
 }
 
+// CUs of the current device (256 on the MI355X when the query fails).
+static int tern_cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
+}
+
+// Placement of the matrix-core decode work items.  The hardware hands
+// workgroup j of a launch whose workgroups are all resident at once to the
+// CU of workgroup j mod C (C CUs), so the item table is laid out by CU: the
+// items are packed onto C bins (largest first, each onto the least loaded
+// bin) and bin b's items take positions b, b + C, b + 2C, ...  Before that,
+// while the launch has free slots, 64-row items are split into two 32-row
+// items (twice the wavefronts per 16-row tile) so the bins can be evened
+// out; a matrix keeps its 64-row items first and its 32-row items after
+// them, as two row ranges.  Cost of an item: its 16-row x 256-trit blocks
+// plus a fixed share for its prologue.
+struct PlaceItem {
+  int part, rb;
+  long cost;
+};
+
+static tern_status place_balanced(const std::vector<GemvDesc>& parts, const std::vector<int>& pmat, int slots,
+                                  std::vector<GemvDesc>* items, std::vector<int>* mat) {
+  const int cus = tern_cu_count();
+  // coarse (current kwaves) and fine (twice the kwaves) items per part
+  std::vector<int> coarse(parts.size()), fine(parts.size(), 0);
+  long total = 0;
+  for (size_t t = 0; t < parts.size(); ++t) {
+    coarse[t] = parts[t].row_blocks;
+    total += coarse[t];
+  }
+  auto rows_of = [&](size_t t, bool f) { return rows_per_item(parts[t].kwaves * (f ? 2 : 1)); };
+  auto nblk_of = [&](size_t t) { return (long)((parts[t].k + 255) / 256); };
+  auto fine_count = [&](size_t t, int a) {
+    const int left = std::max(0, parts[t].n - a * rows_of(t, false));
+    return (left + rows_of(t, true) - 1) / rows_of(t, true);
+  };
+  while (total < slots) {
+    // split one 64-row item of the part whose coarse items cost the most
+    long best = -1;
+    size_t bt = 0;
+    for (size_t t = 0; t < parts.size(); ++t) {
+      if (parts[t].kwaves >= 4 || coarse[t] == 0) continue;
+      const long c = (long)(rows_of(t, false) / 16) * nblk_of(t);
+      if (c > best) { best = c; bt = t; }
+    }
+    if (best < 0) break;
+    const int a = coarse[bt] - 1, f = fine_count(bt, a);
+    if (total - (coarse[bt] + fine[bt]) + a + f > slots) break;
+    total += a + f - (coarse[bt] + fine[bt]);
+    coarse[bt] = a;
+    fine[bt] = f;
+  }
+  // descriptors of the row ranges, and the items
+  std::vector<GemvDesc> ranges;
+  std::vector<int> rmat;
+  std::vector<PlaceItem> all;
+  for (size_t t = 0; t < parts.size(); ++t) {
+    for (int f = 0; f < 2; ++f) {
+      const int cnt = f ? fine[t] : coarse[t];
+      if (cnt == 0) continue;
+      GemvDesc d = parts[t];
+      if (f) {
+        set_kwaves(d, d.kwaves * 2);
+        d.row_base = coarse[t] * rows_of(t, false);
+      }
+      d.row_blocks = cnt;
+      const long tiles = rows_of(t, f != 0) / 16;
+      for (int rb = 0; rb < cnt; ++rb) all.push_back(PlaceItem{(int)ranges.size(), rb, tiles * nblk_of(t) + 4});
+      ranges.push_back(d);
+      rmat.push_back(pmat[t]);
+    }
+  }
+  if (all.size() > (size_t)INT32_MAX) return fail(TERN_E_UNSUPPORTED, "batch too large");
+  // largest first onto the least loaded bin
+  std::stable_sort(all.begin(), all.end(), [](const PlaceItem& a, const PlaceItem& b) { return a.cost > b.cost; });
+  std::vector<std::vector<int>> bins(cus);
+  std::vector<long> load(cus, 0);
+  typedef std::pair<long, int> LB;
+  std::priority_queue<LB, std::vector<LB>, std::greater<LB>> heap;
+  for (int b = 0; b < cus; ++b) heap.push(LB(0, b));
+  for (size_t i = 0; i < all.size(); ++i) {
+    const LB top = heap.top();
+    heap.pop();
+    bins[top.second].push_back((int)i);
+    load[top.second] = top.first + all[i].cost;
+    heap.push(LB(load[top.second], top.second));
+  }
+  // bins with more items take the lower CU numbers, so every round of C
+  // positions is filled from its start
+  std::vector<int> border(cus);
+  for (int b = 0; b < cus; ++b) border[b] = b;
+  std::stable_sort(border.begin(), border.end(), [&](int a, int b) { return bins[a].size() > bins[b].size(); });
+  items->clear();
+  if (mat) mat->clear();
+  for (size_t round = 0;; ++round) {
+    bool any = false;
+    for (int r = 0; r < cus; ++r) {
+      const std::vector<int>& bin = bins[border[r]];
+      if (round >= bin.size()) break;
+      const PlaceItem& it = all[bin[round]];
+      GemvDesc d = ranges[it.part];
+      d.tile_begin = (int)items->size() - it.rb;  // the kernel's item index is blockIdx.x - tile_begin
+      items->push_back(d);
+      if (mat) mat->push_back(rmat[it.part]);
+      any = true;
+    }
+    if (!any) break;
+  }
+  return TERN_OK;
+}
+
 // ---- grouped decode
 // A batch launch reads one descriptor per work item: the descriptor of the
 // (matrix, block of activation rows) the item belongs to, longest K first.
@@ -470,19 +585,30 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
   *mt = pick_mt(std::min(std::max(m, 1), cmax));
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return w[a].k > w[b].k; });
   const size_t esz = y_dtype == TERN_F32 ? 4 : 2;
+  std::vector<GemvDesc> parts;
+  std::vector<int> pmat;
   for (int i : order) {
     for (int c0 = 0; c0 < m; c0 += cmax) {
       GemvDesc d;
       fill_desc(d, &w[i], x[i] + (size_t)c0 * w[i].k, std::min(cmax, m - c0),
                 static_cast<char*>(y[i]) + (size_t)c0 * w[i].n * esz, y_dtype == TERN_F32);
       set_kwaves(d, choose_kwaves(w[i].format, w[i].k, nblk_min));
-      d.tile_begin = (int)items->size();
-      if ((size_t)d.tile_begin + d.row_blocks > (size_t)INT32_MAX) return fail(TERN_E_UNSUPPORTED, "batch too large");
-      items->insert(items->end(), (size_t)d.row_blocks, d);
-      if (mat) mat->insert(mat->end(), (size_t)d.row_blocks, i);
+      parts.push_back(d);
+      pmat.push_back(i);
       *max_krp = std::max(*max_krp, round256(w[i].k));
       *offsets = *offsets || w[i].offset_mode != TERN_OFF_NONE;
     }
+  }
+  if (count > 0 && use_mfma(w[0].format)) {
+    const int slots = tern_cu_count() * tern::gemv_mfma_wgs_per_cu(w[0].group, *mt, *max_krp, *offsets);
+    return place_balanced(parts, pmat, slots, items, mat);
+  }
+  for (size_t t = 0; t < parts.size(); ++t) {
+    GemvDesc d = parts[t];
+    d.tile_begin = (int)items->size();
+    if ((size_t)d.tile_begin + d.row_blocks > (size_t)INT32_MAX) return fail(TERN_E_UNSUPPORTED, "batch too large");
+    items->insert(items->end(), (size_t)d.row_blocks, d);
+    if (mat) mat->insert(mat->end(), (size_t)d.row_blocks, pmat[t]);
   }
   return TERN_OK;
 }
@@ -689,6 +815,9 @@ size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m
     const int rpi = rows_per_item(choose_kwaves(w[i].format, w[i].k, nblk_min));
     items += (size_t)((w[i].n + rpi - 1) / rpi) * chunks;
   }
+  // balanced placement may split items up to the launch's resident slots
+  // (at most 3 workgroups per CU)
+  if (use_mfma(w[0].format)) items = std::max(items, (size_t)tern_cu_count() * 3);
   size_t idx = 0;
   for (int i = 0; i < count; ++i) idx += index_bytes(&w[i]);
   return round_up(items * sizeof(GemvDesc), 256) + idx;
