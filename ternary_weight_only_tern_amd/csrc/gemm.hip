@@ -16,6 +16,8 @@
 // Operand layout of the 32x32x16 f16 MFMA: lane l supplies A[l%32][8*(l/32)
 // .. +7] and B[8*(l/32) .. +7][l%32] and receives D[8*(v/4) + 4*(l/32) +
 // v%4][l%32], v = 0..15.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace tern {
@@ -196,10 +198,12 @@ struct Dec {
   }
 };
 
-// y = 0.5 * acc for one tile, staged through LDS (the activation buffers) so
-// that rows leave in 16-byte chunks; FP32 tiles of 256 rows go in two halves.
+// dst = 0.5 * acc for one tile of a [d.m][d.n] array of T, staged through LDS
+// (the activation buffers) so that rows leave in 16-byte chunks; FP32 tiles
+// of 256 rows go in two halves.
 template <typename T, int AW>
-__device__ __forceinline__ void epilogue(const GemvDesc& d, int m0, int n0, const f16v_t (&acc)[AW][2], char* tile) {
+__device__ __forceinline__ void epilogue(const GemvDesc& d, int m0, int n0, const f16v_t (&acc)[AW][2], char* tile,
+                                         void* dst) {
   constexpr int BM = 64 * AW;
   constexpr int HALVES = (sizeof(T) == 4 && AW == 4) ? 2 : 1;
   constexpr int ROWS = BM / HALVES;
@@ -229,7 +233,7 @@ __device__ __forceinline__ void epilogue(const GemvDesc& d, int m0, int n0, cons
       const int m = m0 + hf * ROWS + r;
       if (m >= d.m) continue;
       const char* srcp = tile + r * TP + cc * 16;
-      T* dstp = reinterpret_cast<T*>(d.y) + (size_t)m * d.n + n0 + cc * PER;
+      T* dstp = reinterpret_cast<T*>(dst) + (size_t)m * d.n + n0 + cc * PER;
       if (vec) {
         *reinterpret_cast<uint4*>(dstp) = *reinterpret_cast<const uint4*>(srcp);
       } else {
@@ -253,6 +257,9 @@ __device__ __forceinline__ void gemm_body(const GemvDesc& d, int m0, int n0, _Fl
   const int wave = t >> 6, lane = t & 63;
   const int mb = (wave >> 1) * 32 * AW, nb = (wave & 1) * 64;
   const int nsteps = d.ng * SPG;
+  // this tile's K part: steps [s0, s1), s0 a multiple of WSTEPS
+  const int s0 = d.ks0, s1 = d.ks1;
+  const int g0 = s0 / SPG, w0 = s0 / WSTEPS;
 
   f16v_t acc[AW][2];
 #pragma unroll
@@ -276,6 +283,8 @@ __device__ __forceinline__ void gemm_body(const GemvDesc& d, int m0, int n0, _Fl
   // NP can exceed this matrix's residual planes (a grouped launch takes the
   // most of its matrices): an absent plane's buffers are NULL and get
   // zero-size resources, so every load from them reads zero (no residual).
+  // The walk starts at the part's first group: rowptr plus the mask bits
+  // before it.
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const bool on = p < d.planes - 1;
@@ -283,10 +292,12 @@ __device__ __forceinline__ void gemm_body(const GemvDesc& d, int m0, int n0, _Fl
     S.mask[p] = rsrc(p == 0 ? d.mask[0] : d.mask[1], on ? n * (uint32_t)d.mwords * 4u : 0u);
     S.blk[p] = rsrc(p == 0 ? d.blocks[0] : d.blocks[1], nnz * (uint32_t)(G / 4));
     S.rsc[p] = rsrc(p == 0 ? d.rscale[0] : d.rscale[1], nnz * 2u);
-    W.e[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc(p == 0 ? d.rowptr[0] : d.rowptr[1], on ? n * 4u : 0u),
-                                                  row * 4u, 0, 0);
-    W.mwl[p] = __builtin_amdgcn_raw_buffer_load_b32(S.mask[p], S.mask_v, 0, 0);
-    W.mwn[p] = __builtin_amdgcn_raw_buffer_load_b32(S.mask[p], S.mask_v, d.mwords > 1 ? 4 : 0, 0);
+    uint32_t e = __builtin_amdgcn_raw_buffer_load_b32(rsrc(p == 0 ? d.rowptr[0] : d.rowptr[1], on ? n * 4u : 0u),
+                                                      row * 4u, 0, 0);
+    for (int w = 0; w < (g0 >> 5); ++w) e += __popc(__builtin_amdgcn_raw_buffer_load_b32(S.mask[p], S.mask_v, 4 * w, 0));
+    W.mwl[p] = __builtin_amdgcn_raw_buffer_load_b32(S.mask[p], S.mask_v, 4 * (g0 >> 5), 0);
+    W.mwn[p] = __builtin_amdgcn_raw_buffer_load_b32(S.mask[p], S.mask_v, 4 * min((g0 >> 5) + 1, d.mwords - 1), 0);
+    W.e[p] = e + __popc(W.mwl[p] & ((1u << (g0 & 31)) - 1u));
   }
   // activation chunks (rows past m read as zero) and packed-window chunks
   const __amdgpu_buffer_rsrc_t xr = rsrc(d.x, (uint32_t)d.m * (uint32_t)d.k * 2u);
@@ -351,7 +362,7 @@ __device__ __forceinline__ void gemm_body(const GemvDesc& d, int m0, int n0, _Fl
         if (c < XCH)                                                                              \
           (XL_)[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(            \
               xr, xo[c], min(s + 2, nsteps - 1) * BK * 2, 0));                                    \
-        if (c == XCH && (U_) == 0) TERN_WLOAD(wv, (q >> 1) + 2, q & 1);                           \
+        if (c == XCH && (U_) == 0) TERN_WLOAD(wv, w0 + (q >> 1) + 2, q & 1);                      \
         if (c < 16) (D_).pair(c);                                                                 \
         if (SLOTS > 16) {                                                                         \
           if (c >= 16 && c < 20) (D_).store(c - 16, WS_);                                         \
@@ -359,14 +370,14 @@ __device__ __forceinline__ void gemm_body(const GemvDesc& d, int m0, int n0, _Fl
             const int cx = (c - 20) * NT + t;                                                     \
             *reinterpret_cast<uint4*>(&(XS_)[(cx >> 3) * PH + (cx & 7) * 8]) = (XN_)[c - 20];     \
           }                                                                                       \
-          if (c == 20 + XCH && (U_) == 1) TERN_WSTORE(wv, (q >> 1) + 2, q & 1);                   \
+          if (c == 20 + XCH && (U_) == 1) TERN_WSTORE(wv, w0 + (q >> 1) + 2, q & 1);              \
         } else if (c == SLOTS - 1) {                                                              \
           _Pragma("unroll") for (int q_ = 0; q_ < 4; ++q_) (D_).store(q_, WS_);                   \
           _Pragma("unroll") for (int i = 0; i < XCH; ++i) {                                       \
             const int cx = i * NT + t;                                                            \
             *reinterpret_cast<uint4*>(&(XS_)[(cx >> 3) * PH + (cx & 7) * 8]) = (XN_)[i];          \
           }                                                                                       \
-          if ((U_) == 1) TERN_WSTORE(wv, (q >> 1) + 2, q & 1);                                    \
+          if ((U_) == 1) TERN_WSTORE(wv, w0 + (q >> 1) + 2, q & 1);                               \
         }                                                                                         \
         if (c == SLOTS - 1) {                                                                     \
           const int g2 = (s + 2) / SPG, w2 = (s + 2) / WSTEPS;                                    \
@@ -385,7 +396,7 @@ __device__ __forceinline__ void gemm_body(const GemvDesc& d, int m0, int n0, _Fl
   // bytes of the next row; nothing reads what they stage.
 #define TERN_STEP(U_, XL_, PL_, XN_, DN_, DL_)                                                    \
   do {                                                                                            \
-    const int s = 2 * q + (U_);                                                                   \
+    const int s = s0 + 2 * q + (U_);                                                              \
     constexpr int AL_ = BK * ((U_) % SPG) + 32 * H;                                               \
     const int gn = (s + 1) / SPG, gl = (s + 2) / SPG;                                             \
     if (gl != gn) walk_next<NP>(gn, W);                                                           \
@@ -395,28 +406,28 @@ __device__ __forceinline__ void gemm_body(const GemvDesc& d, int m0, int n0, _Fl
     __syncthreads();                                                                              \
   } while (0)
 
-  // prologue: windows 0 and 1 and the activation chunks of step 0 to LDS,
-  // loads of steps 0 and 1, decode of step 0
+  // prologue: windows w0 and w0 + 1 and the activation chunks of step s0 to
+  // LDS, loads of steps s0 and s0 + 1, decode of step s0
   {
     uint4 w00, w01, w10, w11;
-    TERN_WLOAD(w00, 0, 0);
-    TERN_WLOAD(w01, 0, 1);
-    TERN_WLOAD(w10, 1, 0);
-    TERN_WLOAD(w11, 1, 1);
-    TERN_WSTORE(w00, 0, 0);
-    TERN_WSTORE(w01, 0, 1);
-    TERN_WSTORE(w10, 1, 0);
-    TERN_WSTORE(w11, 1, 1);
+    TERN_WLOAD(w00, w0, 0);
+    TERN_WLOAD(w01, w0, 1);
+    TERN_WLOAD(w10, w0 + 1, 0);
+    TERN_WLOAD(w11, w0 + 1, 1);
+    TERN_WSTORE(w00, w0, 0);
+    TERN_WSTORE(w01, w0, 1);
+    TERN_WSTORE(w10, w0 + 1, 0);
+    TERN_WSTORE(w11, w0 + 1, 1);
   }
 #pragma unroll
   for (int i = 0; i < XCH; ++i)
-    xv0[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo[i], 0, 0));
-  load_step<G, NP, 32 * H>(S, 0, 0, W, P0);
-  if (SPG == 1) walk_next<NP>(0, W);
+    xv0[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo[i], s0 * BK * 2, 0));
+  load_step<G, NP, 32 * H>(S, g0, g0, W, P0);
+  if (SPG == 1) walk_next<NP>(g0, W);
 #pragma unroll
   for (int i = 0; i < XCH; ++i)
-    xv1[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo[i], min(1, nsteps - 1) * BK * 2, 0));
-  load_step<G, NP, (BK % G) + 32 * H>(S, 1 / SPG, min(1 / SPG, d.ng - 1), W, P1);
+    xv1[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo[i], min(s0 + 1, nsteps - 1) * BK * 2, 0));
+  load_step<G, NP, (BK % G) + 32 * H>(S, (s0 + 1) / SPG, min((s0 + 1) / SPG, d.ng - 1), W, P1);
 #pragma unroll
   for (int i = 0; i < XCH; ++i) {
     const int c = i * NT + t;
@@ -427,27 +438,31 @@ __device__ __forceinline__ void gemm_body(const GemvDesc& d, int m0, int n0, _Fl
   // group spans two steps)
   Dec<FMT, G, NP, 32 * H> De;
   Dec<FMT, G, NP, (BK % G) + 32 * H> Do;
-  De.prep(0, 0, win_start<FMT>(0), pk + dr * WP, P0, ro, lut);
+  De.prep(g0, 0, win_start<FMT>(w0), pk + (w0 % NWIN) * PBUF + dr * WP, P0, ro, lut);
 #pragma unroll
   for (int i = 0; i < 16; ++i) De.pair(i);
 #pragma unroll
   for (int q_ = 0; q_ < 4; ++q_) De.store(q_, &ws[dr * PH + 32 * H]);
-  Do.prep(1 / SPG, 1 & (WSTEPS - 1), win_start<FMT>(0), pk + dr * WP, P1, ro, lut);
+  Do.prep((s0 + 1) / SPG, (s0 + 1) & (WSTEPS - 1), win_start<FMT>(w0), pk + (w0 % NWIN) * PBUF + dr * WP, P1, ro,
+          lut);
   __syncthreads();
   int q = 0;
-  for (; 2 * q + 1 < nsteps; ++q) {
+  for (; s0 + 2 * q + 1 < s1; ++q) {
     TERN_STEP(0, xv0, P0, xv1, Do, De);
     TERN_STEP(1, xv1, P1, xv0, De, Do);
   }
-  if (nsteps & 1) TERN_STEP(0, xv0, P0, xv1, Do, De);
+  if ((s1 - s0) & 1) TERN_STEP(0, xv0, P0, xv1, Do, De);
 #undef TERN_STEP
 #undef TERN_PRODUCTS
 #undef TERN_WSTORE
 #undef TERN_WLOAD
 
-  // ---- epilogue: y = 0.5 * acc (the tile held 2 W~)
-  if (d.y_f32) epilogue<float, AW>(d, m0, n0, acc, reinterpret_cast<char*>(xs));
-  else epilogue<_Float16, AW>(d, m0, n0, acc, reinterpret_cast<char*>(xs));
+  // ---- epilogue: y = 0.5 * acc (the tile held 2 W~), or the FP32 partial
+  // sums of this K part
+  if (d.kpart >= 0)
+    epilogue<float, AW>(d, m0, n0, acc, reinterpret_cast<char*>(xs), d.partial + (size_t)d.kpart * d.m * d.n);
+  else if (d.y_f32) epilogue<float, AW>(d, m0, n0, acc, reinterpret_cast<char*>(xs), d.y);
+  else epilogue<_Float16, AW>(d, m0, n0, acc, reinterpret_cast<char*>(xs), d.y);
 }
 
 // ---- small M (1..16 activation rows): 16 x 128 output tiles with
@@ -748,6 +763,14 @@ hipError_t launch_gemm(const GemvDesc& d, int format, hipStream_t s) {
 #undef TERN_GEMM_NP
 #undef TERN_GEMM_LAUNCH
   return hipGetLastError();
+}
+
+int gemm_wgs_per_cu(int format, int aw) {
+  // the static LDS of gemm_tile: activation and decoded-weight double
+  // buffers, packed windows and (base-3) the code table; 160 KB per CU
+  const size_t bm = 64 * (size_t)aw;
+  const size_t lds = 2 * bm * PH * 2 + 2 * (size_t)BN * PH * 2 + (size_t)NWIN * BN * WP + (format == 1 ? 1024 : 4);
+  return std::max(1, (int)((160u * 1024u) / lds));
 }
 
 hipError_t launch_gemm_grouped(const GemvDesc* descs, int count, int format, int group, int aw, int np,

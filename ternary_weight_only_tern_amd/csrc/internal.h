@@ -46,6 +46,9 @@ struct GemvDesc {
   // Matrix-core decode kernel: first row of this descriptor's row range
   // (a matrix may be covered by two ranges with different kwaves).
   int32_t row_base;
+  // Matrix-core tiles: K part [ks0, ks1) in 64-trit steps, and the FP32
+  // partial slice it writes (kpart >= 0) instead of y.
+  int32_t ks0, ks1, kpart;
 };
 
 // ---- decode products (gemv.hip)
@@ -89,9 +92,13 @@ hipError_t launch_tile_bounds(GemvDesc* items, int count, hipStream_t stream);
 hipError_t launch_gemm(const GemvDesc& d, int format, hipStream_t stream);
 // Activation rows per matrix-core tile for m activation rows (256 or 128).
 inline int gemm_tile_rows(int m) { return m > 128 ? 256 : 128; }
+// Workgroups of the large-tile matrix-core kernel one CU holds (LDS limit).
+int gemm_wgs_per_cu(int format, int aw);
 // Grouped matrix-core product: descs (device memory) holds one descriptor per
-// workgroup with its tile origin (tm0, tn0); aw = gemm_tile_rows(m) / 64;
-// np = residual planes of the descriptor with the most (0..2).
+// workgroup with its tile origin (tm0, tn0) and K steps [ks0, ks1) (ks0 a
+// multiple of 4); kpart >= 0 writes FP32 sums to partial[kpart][m][n]
+// instead of y; aw = gemm_tile_rows(m) / 64; np = residual planes of the
+// descriptor with the most (0..2).
 hipError_t launch_gemm_grouped(const GemvDesc* descs, int count, int format, int group, int aw, int np,
                                hipStream_t stream);
 // Small-M (m <= 16) matrix-core product, grouped: one descriptor per

@@ -194,6 +194,9 @@ void fill_desc(GemvDesc& d, const tern_matrix* w, const uint16_t* x, int m, void
   d.row_blocks = (w->n + tern::kGemvRows - 1) / tern::kGemvRows;
   d.y_f32 = y_f32;
   d.kwaves = 1;
+  d.ks0 = 0;
+  d.ks1 = w->k / 64;
+  d.kpart = -1;
 }
 
 void set_kwaves(GemvDesc& d, int kw) {
@@ -613,18 +616,84 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
   return TERN_OK;
 }
 
+// A batch of matrix-core tiles and its workspace layout:
+// [descriptor per tile][FP32 partials of split products][reduce table].
+struct TileBatch {
+  std::vector<GemvDesc> tiles;
+  std::vector<tern::RedDesc> red;
+  size_t partial_bytes = 0;
+  int red_blocks = 0, np = 0;
+};
+
 // ---- grouped matrix-core products (m >= 33)
 // One descriptor per output tile (tile_rows x 128), matrices with the longest
 // K first so that their tiles start first, and within a matrix the weight
 // tile fastest.  np receives the most residual planes of any matrix.
+// Split of each product's K (64-trit steps) for a grouped launch: products
+// whose tiles are at least twice as long as the shortest ones are cut into
+// that many parts (multiples of 4 steps), when that shortens the launch's
+// makespan (largest tiles first onto the least-loaded of the resident slots)
+// by 15 % or more; the parts write FP32 partials that one grouped reduce sums
+// in part order.
+static std::vector<int> split_ranges(int steps, int parts) {
+  std::vector<int> b(parts + 1, 0);
+  const int q4 = (steps + 3) / 4;
+  for (int i = 0; i <= parts; ++i) b[i] = std::min(steps, (int)((long)q4 * i / parts) * 4);
+  b[parts] = steps;
+  return b;
+}
+
+static long lpt_makespan(std::vector<long> len, int slots) {
+  std::sort(len.begin(), len.end(), std::greater<long>());
+  std::priority_queue<long, std::vector<long>, std::greater<long>> heap;
+  for (int i = 0; i < std::max(1, slots); ++i) heap.push(0);
+  long span = 0;
+  for (long l : len) {
+    const long t = heap.top() + l;
+    heap.pop();
+    heap.push(t);
+    span = std::max(span, t);
+  }
+  return span;
+}
+
+static std::vector<int> gemm_splits(const tern_matrix* w, int32_t count, int32_t m) {
+  std::vector<int> parts(count, 1);
+  const int bm = tern::gemm_tile_rows(m);
+  int smin = 1 << 30;
+  for (int i = 0; i < count; ++i)
+    if (w[i].n > 0 && w[i].k > 0) smin = std::min(smin, w[i].k / 64);
+  if (smin == 1 << 30 || count == 0) return parts;
+  const int slots = tern_cu_count() * tern::gemm_wgs_per_cu(w[0].format, bm / 64);
+  std::vector<long> plain, split;
+  std::vector<int> cand(count, 1);
+  for (int i = 0; i < count; ++i) {
+    if (w[i].n <= 0 || w[i].k <= 0) continue;
+    const long tiles = (long)((m + bm - 1) / bm) * ((w[i].n + 127) / 128);
+    const int st = w[i].k / 64;
+    cand[i] = st >= 2 * smin ? std::min(8, st / smin) : 1;
+    if (cand[i] > 1 && st / cand[i] < 8) cand[i] = std::max(1, st / 8);
+    plain.insert(plain.end(), tiles, st);
+    const std::vector<int> r = split_ranges(st, cand[i]);
+    for (int p = 0; p < cand[i]; ++p) split.insert(split.end(), tiles, r[p + 1] - r[p]);
+  }
+  if (lpt_makespan(split, slots) * 100 <= lpt_makespan(plain, slots) * 85) parts = cand;
+  return parts;
+}
+
+// One descriptor per output tile (tile_rows x 128) and K part; tiles of the
+// longest K parts first, and within a product the weight tile fastest.  With
+// ws == nullptr only the layout is computed.
 static tern_status build_gemm_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y,
-                                    int32_t count, int32_t m, int32_t y_dtype, std::vector<GemvDesc>* tiles,
-                                    int* np) {
+                                    int32_t count, int32_t m, int32_t y_dtype, char* ws, TileBatch* out) {
   if (count < 0) return fail(TERN_E_INVAL, "count=%d is negative", count);
   if (count > 0 && (!w || !x || !y)) return fail(TERN_E_INVAL, "NULL descriptor arrays");
   if (y_dtype != TERN_F16 && y_dtype != TERN_F32) return fail(TERN_E_UNSUPPORTED, "unknown y dtype %d", y_dtype);
-  tiles->clear();
-  *np = 0;
+  out->tiles.clear();
+  out->red.clear();
+  out->partial_bytes = 0;
+  out->red_blocks = 0;
+  out->np = 0;
   std::vector<int> order;
   for (int i = 0; i < count; ++i) {
     TERN_TRY(check_matrix(&w[i]));
@@ -635,22 +704,66 @@ static tern_status build_gemm_batch(const tern_matrix* w, const uint16_t* const*
     if (w[i].k == 0) return fail(TERN_E_UNSUPPORTED, "batched products need k > 0");
     TERN_TRY(check_xy(x[i], y[i], y_dtype));
     order.push_back(i);
-    *np = std::max(*np, w[i].planes - 1);
+    out->np = std::max(out->np, w[i].planes - 1);
   }
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return w[a].k > w[b].k; });
+  const std::vector<int> parts = gemm_splits(w, count, m);
   const int bm = tern::gemm_tile_rows(m);
+  size_t ntiles = 0;
+  for (int i : order) ntiles += (size_t)parts[i] * ((m + bm - 1) / bm) * ((w[i].n + 127) / 128);
+  if (ntiles >= (size_t)INT32_MAX) return fail(TERN_E_UNSUPPORTED, "batch too large");
+  const size_t tiles_bytes = round_up(ntiles * sizeof(GemvDesc), 256);
+  size_t poff = 0;
   for (int i : order) {
     GemvDesc d;
     fill_desc(d, &w[i], x[i], m, y[i], y_dtype == TERN_F32);
-    for (int tm = 0; tm < m; tm += bm)
-      for (int tn = 0; tn < w[i].n; tn += 128) {
-        d.tm0 = tm;
-        d.tn0 = tn;
-        if (tiles->size() >= (size_t)INT32_MAX) return fail(TERN_E_UNSUPPORTED, "batch too large");
-        tiles->push_back(d);
-      }
+    const std::vector<int> r = split_ranges(w[i].k / 64, parts[i]);
+    if (parts[i] > 1) {
+      d.partial = ws ? reinterpret_cast<float*>(ws + tiles_bytes + poff) : nullptr;
+      tern::RedDesc rd;
+      rd.partial = d.partial;
+      rd.y = y[i];
+      rd.splits = parts[i];
+      rd.m = m;
+      rd.n = w[i].n;
+      rd.y_f32 = y_dtype == TERN_F32;
+      rd.begin = out->red_blocks;
+      out->red.push_back(rd);
+      out->red_blocks += (int)(((size_t)m * w[i].n + 255) / 256);
+      poff += round_up((size_t)parts[i] * m * w[i].n * 4, 256);
+    }
+    for (int p = 0; p < parts[i]; ++p) {
+      d.ks0 = r[p];
+      d.ks1 = r[p + 1];
+      d.kpart = parts[i] > 1 ? p : -1;
+      for (int tm = 0; tm < m; tm += bm)
+        for (int tn = 0; tn < w[i].n; tn += 128) {
+          d.tm0 = tm;
+          d.tn0 = tn;
+          out->tiles.push_back(d);
+        }
+    }
   }
+  std::stable_sort(out->tiles.begin(), out->tiles.end(),
+                   [](const GemvDesc& a, const GemvDesc& b) { return a.ks1 - a.ks0 > b.ks1 - b.ks0; });
+  out->partial_bytes = poff;
   return TERN_OK;
+}
+
+// Workspace of a grouped matrix-core batch, from the shapes alone.
+static size_t gemm_batch_ws_bytes(const tern_matrix* w, int32_t count, int32_t m) {
+  const std::vector<int> parts = gemm_splits(w, count, m);
+  const int bm = tern::gemm_tile_rows(m);
+  size_t ntiles = 0, partial = 0, nred = 0;
+  for (int i = 0; i < count; ++i) {
+    if (w[i].n <= 0 || w[i].k <= 0) continue;
+    ntiles += (size_t)parts[i] * ((m + bm - 1) / bm) * ((w[i].n + 127) / 128);
+    if (parts[i] > 1) {
+      partial += round_up((size_t)parts[i] * m * w[i].n * 4, 256);
+      ++nred;
+    }
+  }
+  return round_up(ntiles * sizeof(GemvDesc), 256) + partial + nred * sizeof(tern::RedDesc);
 }
 
 // ---- small m on the 16-row matrix-core product
@@ -660,12 +773,6 @@ static tern_status build_gemm_batch(const tern_matrix* w, const uint16_t* const*
 // and no product's K runs long in one workgroup.  Unsplit tiles write y;
 // split ones write FP32 partials that one grouped reduce sums in split order.
 
-struct SmallBatch {
-  std::vector<GemvDesc> tiles;
-  std::vector<tern::RedDesc> red;
-  size_t partial_bytes = 0;
-  int red_blocks = 0, np = 0;
-};
 
 // Step ranges of a product with `steps` steps when the batch holds `total`
 // tile-steps: a multiple of 4 steps each, at least 8, about total / 1024.
@@ -684,7 +791,7 @@ static std::vector<int> small_ranges(int steps, long total) {
 
 // Layout of the workspace: [descriptor per tile][partials][reduce table].
 static tern_status build_small_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y, int32_t count,
-                                     int32_t m, int32_t y_dtype, char* ws, SmallBatch* out) {
+                                     int32_t m, int32_t y_dtype, char* ws, TileBatch* out) {
   out->tiles.clear();
   out->red.clear();
   out->partial_bytes = 0;
@@ -755,7 +862,7 @@ static tern_status build_small_batch(const tern_matrix* w, const uint16_t* const
   return TERN_OK;
 }
 
-static size_t small_ws_bytes(const SmallBatch& b) {
+static size_t tile_ws_bytes(const TileBatch& b) {
   return round_up(b.tiles.size() * sizeof(GemvDesc), 256) + b.partial_bytes + b.red.size() * sizeof(tern::RedDesc);
 }
 
@@ -781,13 +888,6 @@ static size_t small_batch_ws_bytes(const tern_matrix* w, int32_t count, int32_t 
   return round_up(tiles * sizeof(GemvDesc), 256) + partial + nred * sizeof(tern::RedDesc);
 }
 
-static size_t gemm_batch_tiles(const tern_matrix* w, int32_t count, int32_t m) {
-  const size_t bm = (size_t)tern::gemm_tile_rows(m);
-  size_t tiles = 0;
-  for (int i = 0; i < count; ++i)
-    if (w[i].n > 0 && w[i].k > 0) tiles += ((size_t)m + bm - 1) / bm * (((size_t)w[i].n + 127) / 128);
-  return tiles;
-}
 
 // Plans of 2-bit products also keep a residual index after the descriptor
 // table: per entry of the first residual plane, its group and scale (u32).
@@ -798,7 +898,7 @@ static size_t index_bytes(const tern_matrix* w) { return plan_indexes(w) ? round
 
 size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m) {
   if (count <= 0 || m <= 0 || !w) return 0;
-  if (gemm_route(m)) return round_up(gemm_batch_tiles(w, count, m) * sizeof(GemvDesc), 256);
+  if (gemm_route(m)) return gemm_batch_ws_bytes(w, count, m);
   if (small_route(w[0].format, m)) return small_batch_ws_bytes(w, count, m);
   int cmax = max_mt(w[0].format, w[0].group), kmax = 0, nblk_min = 1 << 30;
   for (int i = 0; i < count; ++i) {
@@ -830,25 +930,34 @@ tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, vo
   int mt = 1, max_krp = 0;
   bool offsets = false;
   if (gemm_route(m)) {
-    int np = 0;
-    TERN_TRY(build_gemm_batch(w, x, y, count, m, y_dtype, &items, &np));
-    if (items.empty()) return TERN_OK;
-    const size_t need = items.size() * sizeof(GemvDesc);
-    if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "batched product needs %zu workspace bytes", need);
+    if (!ws) return fail(TERN_E_WORKSPACE, "batched product needs a workspace");
     TERN_TRY(check_dev(ws, true, "ws"));
+    TileBatch b;
+    TERN_TRY(build_gemm_batch(w, x, y, count, m, y_dtype, static_cast<char*>(ws), &b));
+    if (b.tiles.empty()) return TERN_OK;
+    const size_t need = tile_ws_bytes(b);
+    if (ws_bytes < need) return fail(TERN_E_WORKSPACE, "batched product needs %zu workspace bytes", need);
     hipStream_t s = (hipStream_t)stream;
-    TERN_HIP(hipMemcpyAsync(ws, items.data(), need, hipMemcpyHostToDevice, s));
-    TERN_HIP(tern::launch_gemm_grouped(static_cast<const GemvDesc*>(ws), (int)items.size(), w[0].format, w[0].group,
-                                       tern::gemm_tile_rows(m) / 64, np, s));
+    char* base = static_cast<char*>(ws);
+    const size_t tb = round_up(b.tiles.size() * sizeof(GemvDesc), 256);
+    TERN_HIP(hipMemcpyAsync(base, b.tiles.data(), b.tiles.size() * sizeof(GemvDesc), hipMemcpyHostToDevice, s));
+    if (!b.red.empty())
+      TERN_HIP(hipMemcpyAsync(base + tb + b.partial_bytes, b.red.data(), b.red.size() * sizeof(tern::RedDesc),
+                              hipMemcpyHostToDevice, s));
+    TERN_HIP(tern::launch_gemm_grouped(reinterpret_cast<const GemvDesc*>(base), (int)b.tiles.size(), w[0].format,
+                                       w[0].group, tern::gemm_tile_rows(m) / 64, b.np, s));
+    if (!b.red.empty())
+      TERN_HIP(tern::launch_reduce_grouped(reinterpret_cast<const tern::RedDesc*>(base + tb + b.partial_bytes),
+                                           (int)b.red.size(), b.red_blocks, s));
     return TERN_OK;
   }
   if (count > 0 && small_route(w[0].format, m)) {
     if (!ws) return fail(TERN_E_WORKSPACE, "batched product needs a workspace");
     TERN_TRY(check_dev(ws, true, "ws"));
-    SmallBatch b;
+    TileBatch b;
     TERN_TRY(build_small_batch(w, x, y, count, m, y_dtype, static_cast<char*>(ws), &b));
     if (b.tiles.empty()) return TERN_OK;
-    const size_t need = small_ws_bytes(b);
+    const size_t need = tile_ws_bytes(b);
     if (ws_bytes < need) return fail(TERN_E_WORKSPACE, "batched product needs %zu workspace bytes", need);
     hipStream_t s = (hipStream_t)stream;
     char* base = static_cast<char*>(ws);
@@ -886,18 +995,23 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
   int mt = 1, max_krp = 0;
   bool offsets = false;
   if (gemm_route(m)) {
-    int np = 0;
-    TERN_TRY(build_gemm_batch(w, x, y, count, m, y_dtype, &items, &np));
-    const size_t need = items.size() * sizeof(GemvDesc);
-    if (!items.empty()) {
+    TileBatch b;
+    TERN_TRY(build_gemm_batch(w, x, y, count, m, y_dtype, static_cast<char*>(ws), &b));
+    const size_t need = tile_ws_bytes(b);
+    const size_t tb = round_up(b.tiles.size() * sizeof(GemvDesc), 256);
+    char* base = static_cast<char*>(ws);
+    if (!b.tiles.empty()) {
       if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "plan needs %zu workspace bytes", need);
       TERN_TRY(check_dev(ws, true, "ws"));
-      TERN_HIP(hipMemcpy(ws, items.data(), need, hipMemcpyHostToDevice));
+      TERN_HIP(hipMemcpy(base, b.tiles.data(), b.tiles.size() * sizeof(GemvDesc), hipMemcpyHostToDevice));
+      if (!b.red.empty())
+        TERN_HIP(hipMemcpy(base + tb + b.partial_bytes, b.red.data(), b.red.size() * sizeof(tern::RedDesc),
+                           hipMemcpyHostToDevice));
     }
     tern_plan* p = static_cast<tern_plan*>(std::malloc(sizeof(tern_plan)));
     if (!p) return fail(TERN_E_INVAL, "out of host memory");
-    p->dev = static_cast<const GemvDesc*>(ws);
-    p->total_items = (int)items.size();
+    p->dev = reinterpret_cast<const GemvDesc*>(base);
+    p->total_items = (int)b.tiles.size();
     p->format = count > 0 ? w[0].format : 0;
     p->group = count > 0 ? w[0].group : 128;
     p->mt = 0;
@@ -906,18 +1020,19 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
     p->gemm = true;
     p->small = false;
     p->aw = tern::gemm_tile_rows(m) / 64;
-    p->np = np;
-    p->red = nullptr;
-    p->nred = p->red_blocks = 0;
+    p->np = b.np;
+    p->red = b.red.empty() ? nullptr : reinterpret_cast<const tern::RedDesc*>(base + tb + b.partial_bytes);
+    p->nred = (int)b.red.size();
+    p->red_blocks = b.red_blocks;
     *out = p;
     return TERN_OK;
   }
   if (count > 0 && small_route(w[0].format, m)) {
     if (!ws) return fail(TERN_E_WORKSPACE, "plan needs a workspace");
     TERN_TRY(check_dev(ws, true, "ws"));
-    SmallBatch b;
+    TileBatch b;
     TERN_TRY(build_small_batch(w, x, y, count, m, y_dtype, static_cast<char*>(ws), &b));
-    const size_t need = small_ws_bytes(b);
+    const size_t need = tile_ws_bytes(b);
     if (!b.tiles.empty() && ws_bytes < need) return fail(TERN_E_WORKSPACE, "plan needs %zu workspace bytes", need);
     char* base = static_cast<char*>(ws);
     const size_t tb = round_up(b.tiles.size() * sizeof(GemvDesc), 256);
@@ -994,6 +1109,8 @@ tern_status tern_plan_run(const tern_plan* plan, void* stream) {
   if (plan->gemm) {
     TERN_HIP(tern::launch_gemm_grouped(plan->dev, plan->total_items, plan->format, plan->group, plan->aw, plan->np,
                                        (hipStream_t)stream));
+    if (plan->nred)
+      TERN_HIP(tern::launch_reduce_grouped(plan->red, plan->nred, plan->red_blocks, (hipStream_t)stream));
     return TERN_OK;
   }
   if (plan->small) {
