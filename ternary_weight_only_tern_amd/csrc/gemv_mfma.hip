@@ -215,7 +215,7 @@ constexpr int mfma_waves_per_eu() { return MP == 8 || (G == 64 && MP == 4) ? 2 :
 
 template <int G, int MP>
 __global__ __launch_bounds__(kWave * kWaves) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<G, MP>(), 8)))
-void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc one) {
+void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, const WgRec* __restrict__ recs, int ndesc, GemvDesc one) {
   constexpr int GW = Win<MP>::GW;
   constexpr int NACC = Win<MP>::NACC;
   constexpr int GPB = kBlockTrits / G;      // groups per block
@@ -225,11 +225,22 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
   extern __shared__ uint4 smem_all[];
   uint8_t* lds = reinterpret_cast<uint8_t*>(smem_all);
 
-  // one descriptor per work item (grouped launches), or the single one
+  // grouped launches: this workgroup's record names its row range's
+  // descriptor (a few per launch, so they stay in the L2) and its item;
+  // otherwise the single descriptor
   GemvDesc d;
-  if (ndesc > 0) d = descs[blockIdx.x];
-  else d = one;
-  const int item = (int)blockIdx.x - d.tile_begin;
+  int item;
+  uint32_t te[5] = {0u, 0u, 0u, 0u, 0u};
+  if (ndesc > 0) {
+    const WgRec rec = recs[blockIdx.x];
+    d = descs[rec.ri >> 20];
+    item = (int)(rec.ri & 0xFFFFFu);
+#pragma unroll
+    for (int t = 0; t < 5; ++t) te[t] = rec.te[t];
+  } else {
+    d = one;
+    item = (int)blockIdx.x - d.tile_begin;
+  }
   const int rb = item % d.row_blocks;
   const int split = item / d.row_blocks;
   const int tid = threadIdx.x;
@@ -329,10 +340,10 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
   // staged in LDS with the other small operands -- their blocks as raw
   // 16-byte chunks and their index words (group | scale bits << 16)
   uint32_t e0 = 0, e1 = 0;
-  if (d.gidx[0] != nullptr && sflat && d.planes == 2) {
+  if (ndesc > 0 && d.gidx[0] != nullptr && sflat && d.planes == 2) {
     const int nt = rw / kRowsWave;
-    e0 = d.tile_e[0][0];
-    e1 = nt == 1 ? d.tile_e[0][1] : nt == 2 ? d.tile_e[0][2] : d.tile_e[0][4];
+    e0 = te[0];
+    e1 = nt == 1 ? te[1] : nt == 2 ? te[2] : te[4];
   }
   const bool res_idx = e1 > e0 && e1 - e0 <= (uint32_t)kResStage;
   const uint32_t nres = res_idx ? e1 - e0 : 0u;
@@ -367,11 +378,11 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, int ndesc, GemvDesc on
   // are computed between its plane-0 blocks and summed by this wavefront
   uint32_t we0 = 0, we1 = 0;
   if (res_idx) {
-    const uint32_t tb = tile == 0 ? d.tile_e[0][0] : tile == 1 ? d.tile_e[0][1] : tile == 2 ? d.tile_e[0][2] : d.tile_e[0][3];
-    const uint32_t te = tile == 0 ? d.tile_e[0][1] : tile == 1 ? d.tile_e[0][2] : tile == 2 ? d.tile_e[0][3] : d.tile_e[0][4];
-    const uint32_t ps = (te - tb + kw - 1) / kw;
-    we0 = min(te, tb + kp * ps) - e0;
-    we1 = min(te, tb + (kp + 1) * ps) - e0;
+    const uint32_t tb = tile == 0 ? te[0] : tile == 1 ? te[1] : tile == 2 ? te[2] : te[3];
+    const uint32_t tn = tile == 0 ? te[1] : tile == 1 ? te[2] : tile == 2 ? te[3] : te[4];
+    const uint32_t ps = (tn - tb + kw - 1) / kw;
+    we0 = min(tn, tb + kp * ps) - e0;
+    we1 = min(tn, tb + (kp + 1) * ps) - e0;
   }
   const int nrb = (int)((we1 - we0 + 15u) / 16u);  // this wavefront's 16-entry batches
   float* valw = reinterpret_cast<float*>(lds + valoff) + (size_t)wave * kResCap * MP;  // this wave's
@@ -670,22 +681,22 @@ size_t mfma_lds_bytes(int max_krp, bool offsets) {
 }
 
 template <int G, int MP>
-hipError_t launch_mfma(const GemvDesc* descs, int ndesc, const GemvDesc& one, int items, int max_krp, bool offsets,
-                       hipStream_t s) {
+hipError_t launch_mfma(const GemvDesc* descs, const WgRec* recs, int ndesc, const GemvDesc& one, int items, int max_krp,
+                       bool offsets, hipStream_t s) {
   const size_t lds = mfma_lds_bytes<G, MP>(max_krp, offsets);
-  hipLaunchKernelGGL((gemv_mfma_kernel<G, MP>), dim3(items), dim3(kWave * kWaves), lds, s, descs, ndesc, one);
+  hipLaunchKernelGGL((gemv_mfma_kernel<G, MP>), dim3(items), dim3(kWave * kWaves), lds, s, descs, recs, ndesc, one);
   return hipGetLastError();
 }
 
 template <int G>
-hipError_t launch_mfma_g(int mp, const GemvDesc* descs, int ndesc, const GemvDesc& one, int items, int max_krp,
-                         bool offsets, hipStream_t s) {
+hipError_t launch_mfma_g(int mp, const GemvDesc* descs, const WgRec* recs, int ndesc, const GemvDesc& one, int items,
+                         int max_krp, bool offsets, hipStream_t s) {
   switch (mp) {
-    case 1: return launch_mfma<G, 1>(descs, ndesc, one, items, max_krp, offsets, s);
-    case 2: return launch_mfma<G, 2>(descs, ndesc, one, items, max_krp, offsets, s);
-    case 4: return launch_mfma<G, 4>(descs, ndesc, one, items, max_krp, offsets, s);
+    case 1: return launch_mfma<G, 1>(descs, recs, ndesc, one, items, max_krp, offsets, s);
+    case 2: return launch_mfma<G, 2>(descs, recs, ndesc, one, items, max_krp, offsets, s);
+    case 4: return launch_mfma<G, 4>(descs, recs, ndesc, one, items, max_krp, offsets, s);
     case 8:
-      if (G == 128) return launch_mfma<128, 8>(descs, ndesc, one, items, max_krp, offsets, s);
+      if (G == 128) return launch_mfma<128, 8>(descs, recs, ndesc, one, items, max_krp, offsets, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -707,16 +718,15 @@ __global__ void res_index_kernel(const uint32_t* __restrict__ mask, const uint32
   }
 }
 
-__global__ void tile_bounds_kernel(GemvDesc* items, int count) {
+__global__ void tile_bounds_kernel(const GemvDesc* ranges, WgRec* recs, int count) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= count) return;
-  GemvDesc* d = items + i;
-  const int item = i - d->tile_begin;
+  WgRec* rec = recs + i;
+  const GemvDesc* d = ranges + (rec->ri >> 20);
+  const int item = (int)(rec->ri & 0xFFFFFu);
   const int row0 = d->row_base + (item % d->row_blocks) * kRowsWave * (kWaves / d->kwaves);
-  for (int p = 0; p < 2; ++p) {
-    if (!d->gidx[p]) continue;
-    for (int t = 0; t < 5; ++t) d->tile_e[p][t] = d->rowptr[p][min(row0 + kRowsWave * t, d->n)];
-  }
+  if (!d->gidx[0]) return;
+  for (int t = 0; t < 5; ++t) rec->te[t] = d->rowptr[0][min(row0 + kRowsWave * t, d->n)];
 }
 
 }  // namespace
@@ -729,9 +739,9 @@ hipError_t launch_res_index(const uint32_t* mask, const uint32_t* rowptr, const 
   return hipGetLastError();
 }
 
-hipError_t launch_tile_bounds(GemvDesc* items, int count, hipStream_t s) {
+hipError_t launch_tile_bounds(const GemvDesc* ranges, WgRec* recs, int count, hipStream_t s) {
   if (count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(tile_bounds_kernel, dim3((count + 255) / 256), dim3(256), 0, s, items, count);
+  hipLaunchKernelGGL(tile_bounds_kernel, dim3((count + 255) / 256), dim3(256), 0, s, ranges, recs, count);
   return hipGetLastError();
 }
 
@@ -756,11 +766,12 @@ int gemv_mfma_wgs_per_cu(int group, int mp, int max_krp, bool offsets) {
 
 int gemv_mfma_max_range(int mp) { return std::min(16384 / mp, kMaxBlocks * kBlockTrits * kWaves); }
 
-hipError_t launch_gemv_mfma(int group, int mp, const GemvDesc* descs, int ndesc, const GemvDesc& one,
+hipError_t launch_gemv_mfma(int group, int mp, const GemvDesc* descs, const WgRec* recs, int ndesc, const GemvDesc& one,
                             int total_items, int max_krp, bool offsets, hipStream_t s) {
   if (total_items <= 0) return hipSuccess;
-  if (group == 64) return launch_mfma_g<64>(mp, descs, ndesc, one, total_items, max_krp, offsets, s);
-  if (group == 128) return launch_mfma_g<128>(mp, descs, ndesc, one, total_items, max_krp, offsets, s);
+  if (ndesc > 0 && !recs) return hipErrorInvalidValue;
+  if (group == 64) return launch_mfma_g<64>(mp, descs, recs, ndesc, one, total_items, max_krp, offsets, s);
+  if (group == 128) return launch_mfma_g<128>(mp, descs, recs, ndesc, one, total_items, max_krp, offsets, s);
   return hipErrorInvalidValue;
 }
 

@@ -36,11 +36,10 @@ struct GemvDesc {
   int32_t tile_begin;     // first work-item index of this descriptor in the grid
   int32_t y_f32;          // 1: y is fp32, 0: fp16
   int32_t kwaves;         // matrix-core kernel: wavefronts sharing one 16-row tile's K (1, 2, 4)
-  // Residual index prepared with a plan (matrix-core kernel; NULL otherwise):
-  // per residual entry (group | FP16 scale bits << 16), and per work item the
-  // entry index (rowptr value) at each 16-row tile boundary of the item.
+  // Residual index prepared with a plan (matrix-core decode kernel; NULL
+  // otherwise): per entry of the first residual plane, (group | FP16 scale
+  // bits << 16); the entry ranges of the tiles are in the launch's records.
   const uint32_t* gidx[2];
-  uint32_t tile_e[2][5];
   // Grouped matrix-core product: origin of this workgroup's output tile.
   int32_t tm0, tn0;
   // Matrix-core decode kernel: first row of this descriptor's row range
@@ -76,17 +75,30 @@ int gemv_mfma_wgs_per_cu(int group, int mp, int max_krp, bool offsets);
 // Same descriptors and work items as launch_gemv; a work item is 64 / kwaves
 // rows; K splits start on 256-trit blocks.  max_krp = the longest range of
 // any descriptor rounded up to 256; offsets = some descriptor has an offset.
-hipError_t launch_gemv_mfma(int group, int mp, const GemvDesc* descs, int ndesc, const GemvDesc& one,
+// Per-workgroup record of a grouped matrix-core decode launch (32 bytes):
+// ri = range descriptor index << 20 | work item within the range, and the
+// first residual plane's entry index at each 16-row tile boundary of the
+// item (filled by launch_tile_bounds when the range has a residual index).
+struct WgRec {
+  uint32_t ri;
+  uint32_t te[5];
+  uint32_t pad[2];
+};
+// Matrix-core decode launch over total_items workgroups: with ndesc > 0,
+// descs (device memory) holds the launch's row-range descriptors and recs
+// one record per workgroup; with ndesc == 0 every workgroup uses `one`
+// (item = workgroup index).
+hipError_t launch_gemv_mfma(int group, int mp, const GemvDesc* descs, const WgRec* recs, int ndesc, const GemvDesc& one,
                             int total_items, int max_krp, bool offsets, hipStream_t stream);
 
 // Residual index of a plan: for row n's j-th masked group g, entry
 // e = rowptr[n] + j gets gidx[e] = g | rscale[e] << 16 (one thread per row).
 hipError_t launch_res_index(const uint32_t* mask, const uint32_t* rowptr, const uint16_t* rscale, int n,
                             int mwords, uint32_t* gidx, hipStream_t stream);
-// For each of `count` work-item descriptors in device memory whose gidx[p]
-// is set: tile_e[p][t] = rowptr[p][min(row0 + 16 t, n)], t = 0..4, where
+// For each of `count` workgroup records whose range descriptor has a
+// residual index: te[t] = rowptr[0][min(row0 + 16 t, n)], t = 0..4, where
 // row0 is the item's first row.
-hipError_t launch_tile_bounds(GemvDesc* items, int count, hipStream_t stream);
+hipError_t launch_tile_bounds(const GemvDesc* ranges, WgRec* recs, int count, hipStream_t stream);
 
 // ---- MFMA product (gemm.hip)
 hipError_t launch_gemm(const GemvDesc& d, int format, hipStream_t stream);

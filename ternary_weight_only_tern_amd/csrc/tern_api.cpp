@@ -159,9 +159,9 @@ bool product_group_ok(int group) { return group == 64 || group == 128; }
 int round256(int v) { return (v + 255) / 256 * 256; }
 
 // Decode launch over descriptors (device table) or the single descriptor `one`.
-hipError_t launch_decode(int format, int group, int mt, const GemvDesc* descs, int ndesc, const GemvDesc& one,
-                         int items, int max_krp, bool offsets, hipStream_t s) {
-  if (use_mfma(format)) return tern::launch_gemv_mfma(group, mt, descs, ndesc, one, items, max_krp, offsets, s);
+hipError_t launch_decode(int format, int group, int mt, const GemvDesc* descs, const tern::WgRec* recs, int ndesc,
+                         const GemvDesc& one, int items, int max_krp, bool offsets, hipStream_t s) {
+  if (use_mfma(format)) return tern::launch_gemv_mfma(group, mt, descs, recs, ndesc, one, items, max_krp, offsets, s);
   return tern::launch_gemv(format, group, mt, descs, ndesc, one, items, s);
 }
 
@@ -235,7 +235,9 @@ tern_status check_xy(const uint16_t* x, void* y, int y_dtype) {
 }  // namespace
 
 struct tern_plan {
-  const GemvDesc* dev;    // one descriptor per work item (or per output tile)
+  const GemvDesc* dev;    // one descriptor per work item / output tile, or the row ranges
+  const tern::WgRec* recs;  // matrix-core decode: one record per workgroup (else NULL)
+  int ndesc;              // descriptors at dev
   int total_items;
   int format, group, mt;
   int max_krp;
@@ -413,7 +415,7 @@ tern_status tern_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* 
     if (splits > 1) dc.partial = static_cast<float*>(ws);
     dc.tile_begin = 0;
     const int items = splits * dc.row_blocks;
-    TERN_HIP(launch_decode(w->format, w->group, pick_mt(std::min(m, cmax)), nullptr, 0, dc, items,
+    TERN_HIP(launch_decode(w->format, w->group, pick_mt(std::min(m, cmax)), nullptr, nullptr, 0, dc, items,
                            round256(gps * w->group), w->offset_mode != TERN_OFF_NONE, s));
     if (splits > 1) TERN_HIP(tern::launch_splitk_reduce(dc.partial, splits, mc, w->n, dc.y, y_f32, s));
   }
@@ -459,7 +461,7 @@ struct PlaceItem {
 };
 
 static tern_status place_balanced(const std::vector<GemvDesc>& parts, const std::vector<int>& pmat, int slots,
-                                  std::vector<GemvDesc>* items, std::vector<int>* mat) {
+                                  std::vector<GemvDesc>* items, std::vector<int>* mat, std::vector<tern::WgRec>* recs) {
   const int cus = tern_cu_count();
   // coarse (current kwaves) and fine (twice the kwaves) items per part
   std::vector<int> coarse(parts.size()), fine(parts.size(), 0);
@@ -510,7 +512,9 @@ static tern_status place_balanced(const std::vector<GemvDesc>& parts, const std:
       rmat.push_back(pmat[t]);
     }
   }
-  if (all.size() > (size_t)INT32_MAX) return fail(TERN_E_UNSUPPORTED, "batch too large");
+  if (all.size() > (size_t)INT32_MAX || ranges.size() >= (1u << 12)) return fail(TERN_E_UNSUPPORTED, "batch too large");
+  for (const PlaceItem& it : all)
+    if (it.rb >= (1 << 20)) return fail(TERN_E_UNSUPPORTED, "batch too large");
   // largest first onto the least loaded bin
   std::stable_sort(all.begin(), all.end(), [](const PlaceItem& a, const PlaceItem& b) { return a.cost > b.cost; });
   std::vector<std::vector<int>> bins(cus);
@@ -530,18 +534,19 @@ static tern_status place_balanced(const std::vector<GemvDesc>& parts, const std:
   std::vector<int> border(cus);
   for (int b = 0; b < cus; ++b) border[b] = b;
   std::stable_sort(border.begin(), border.end(), [&](int a, int b) { return bins[a].size() > bins[b].size(); });
-  items->clear();
-  if (mat) mat->clear();
+  *items = ranges;
+  if (mat) *mat = rmat;
+  recs->clear();
   for (size_t round = 0;; ++round) {
     bool any = false;
     for (int r = 0; r < cus; ++r) {
       const std::vector<int>& bin = bins[border[r]];
       if (round >= bin.size()) break;
       const PlaceItem& it = all[bin[round]];
-      GemvDesc d = ranges[it.part];
-      d.tile_begin = (int)items->size() - it.rb;  // the kernel's item index is blockIdx.x - tile_begin
-      items->push_back(d);
-      if (mat) mat->push_back(rmat[it.part]);
+      tern::WgRec rec;
+      std::memset(&rec, 0, sizeof(rec));
+      rec.ri = (uint32_t)it.part << 20 | (uint32_t)it.rb;
+      recs->push_back(rec);
       any = true;
     }
     if (!any) break;
@@ -555,13 +560,15 @@ static tern_status place_balanced(const std::vector<GemvDesc>& parts, const std:
 // Every descriptor covers its whole K (no split across workgroups).
 static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y,
                                int32_t count, int32_t m, int32_t y_dtype, std::vector<GemvDesc>* items,
-                               int* mt, int* max_krp, bool* offsets, std::vector<int>* mat = nullptr) {
+                               int* mt, int* max_krp, bool* offsets, std::vector<int>* mat,
+                               std::vector<tern::WgRec>* recs) {
   if (count < 0) return fail(TERN_E_INVAL, "count=%d is negative", count);
   if (count > 0 && (!w || !x || !y)) return fail(TERN_E_INVAL, "NULL descriptor arrays");
   if (m < 0) return fail(TERN_E_INVAL, "m=%d is negative", m);
   if (y_dtype != TERN_F16 && y_dtype != TERN_F32) return fail(TERN_E_UNSUPPORTED, "unknown y dtype %d", y_dtype);
   items->clear();
   if (mat) mat->clear();
+  recs->clear();
   *max_krp = 0;
   *offsets = false;
   std::vector<int> order;
@@ -604,7 +611,7 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
   }
   if (count > 0 && use_mfma(w[0].format)) {
     const int slots = tern_cu_count() * tern::gemv_mfma_wgs_per_cu(w[0].group, *mt, *max_krp, *offsets);
-    return place_balanced(parts, pmat, slots, items, mat);
+    return place_balanced(parts, pmat, slots, items, mat, recs);
   }
   for (size_t t = 0; t < parts.size(); ++t) {
     GemvDesc d = parts[t];
@@ -915,12 +922,17 @@ size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m
     const int rpi = rows_per_item(choose_kwaves(w[i].format, w[i].k, nblk_min));
     items += (size_t)((w[i].n + rpi - 1) / rpi) * chunks;
   }
-  // balanced placement may split items up to the launch's resident slots
-  // (at most 3 workgroups per CU)
-  if (use_mfma(w[0].format)) items = std::max(items, (size_t)tern_cu_count() * 3);
   size_t idx = 0;
   for (int i = 0; i < count; ++i) idx += index_bytes(&w[i]);
-  return round_up(items * sizeof(GemvDesc), 256) + idx;
+  if (!use_mfma(w[0].format)) return round_up(items * sizeof(GemvDesc), 256) + idx;
+  // matrix-core decode: at most two row ranges per (matrix, block of rows)
+  // and one record per workgroup; balanced placement may split items up to
+  // the launch's resident slots (at most 3 workgroups per CU)
+  size_t ranges = 0;
+  for (int i = 0; i < count; ++i)
+    if (w[i].n > 0 && w[i].k > 0) ranges += 2 * chunks;
+  items = std::max(items, (size_t)tern_cu_count() * 3);
+  return round_up(ranges * sizeof(GemvDesc), 256) + round_up(items * sizeof(tern::WgRec), 256) + idx;
 }
 
 tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, void* const* y,
@@ -973,15 +985,23 @@ tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, vo
                                            (int)b.red.size(), b.red_blocks, s));
     return TERN_OK;
   }
-  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets));
+  std::vector<tern::WgRec> recs;
+  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets, nullptr, &recs));
   if (items.empty()) return TERN_OK;
-  const size_t need = items.size() * sizeof(GemvDesc);
+  // workspace: [descriptors][records of the matrix-core decode launch]
+  const size_t dbytes = round_up(items.size() * sizeof(GemvDesc), 256);
+  const size_t need = dbytes + recs.size() * sizeof(tern::WgRec);
   if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "batched decode needs %zu workspace bytes", need);
   TERN_TRY(check_dev(ws, true, "ws"));
   hipStream_t s = (hipStream_t)stream;
-  TERN_HIP(hipMemcpyAsync(ws, items.data(), need, hipMemcpyHostToDevice, s));
-  TERN_HIP(launch_decode(w[0].format, w[0].group, mt, static_cast<const GemvDesc*>(ws), (int)items.size(),
-                         items[0], (int)items.size(), max_krp, offsets, s));
+  char* base = static_cast<char*>(ws);
+  TERN_HIP(hipMemcpyAsync(base, items.data(), items.size() * sizeof(GemvDesc), hipMemcpyHostToDevice, s));
+  if (!recs.empty())
+    TERN_HIP(hipMemcpyAsync(base + dbytes, recs.data(), recs.size() * sizeof(tern::WgRec), hipMemcpyHostToDevice, s));
+  const int nwg = recs.empty() ? (int)items.size() : (int)recs.size();
+  TERN_HIP(launch_decode(w[0].format, w[0].group, mt, reinterpret_cast<const GemvDesc*>(base),
+                         recs.empty() ? nullptr : reinterpret_cast<const tern::WgRec*>(base + dbytes),
+                         (int)items.size(), items[0], nwg, max_krp, offsets, s));
   return TERN_OK;
 }
 
@@ -1011,6 +1031,8 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
     tern_plan* p = static_cast<tern_plan*>(std::malloc(sizeof(tern_plan)));
     if (!p) return fail(TERN_E_INVAL, "out of host memory");
     p->dev = reinterpret_cast<const GemvDesc*>(base);
+    p->recs = nullptr;
+    p->ndesc = (int)b.tiles.size();
     p->total_items = (int)b.tiles.size();
     p->format = count > 0 ? w[0].format : 0;
     p->group = count > 0 ? w[0].group : 128;
@@ -1045,6 +1067,8 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
     tern_plan* p = static_cast<tern_plan*>(std::malloc(sizeof(tern_plan)));
     if (!p) return fail(TERN_E_INVAL, "out of host memory");
     p->dev = reinterpret_cast<const GemvDesc*>(base);
+    p->recs = nullptr;
+    p->ndesc = (int)b.tiles.size();
     p->total_items = (int)b.tiles.size();
     p->format = w[0].format;
     p->group = w[0].group;
@@ -1061,34 +1085,44 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
     *out = p;
     return TERN_OK;
   }
-  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets, &mat));
+  std::vector<tern::WgRec> recs;
+  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets, &mat, &recs));
+  // workspace: [descriptors][workgroup records][residual index of each matrix]
+  const size_t dbytes = round_up(items.size() * sizeof(GemvDesc), 256);
+  const size_t rbytes = round_up(recs.size() * sizeof(tern::WgRec), 256);
+  char* base = static_cast<char*>(ws);
   if (!items.empty()) {
-    // workspace: [descriptor per work item][residual index of each matrix]
-    const size_t dbytes = round_up(items.size() * sizeof(GemvDesc), 256);
     std::vector<size_t> ioff(count, 0);
-    size_t need = dbytes;
+    size_t need = dbytes + rbytes;
     for (int i = 0; i < count; ++i) {
       ioff[i] = need;
       need += index_bytes(&w[i]);
     }
     if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "plan needs %zu workspace bytes", need);
     TERN_TRY(check_dev(ws, true, "ws"));
-    char* base = static_cast<char*>(ws);
-    for (size_t t = 0; t < items.size(); ++t)
-      if (plan_indexes(&w[mat[t]])) items[t].gidx[0] = reinterpret_cast<const uint32_t*>(base + ioff[mat[t]]);
-    TERN_HIP(hipMemcpy(ws, items.data(), items.size() * sizeof(GemvDesc), hipMemcpyHostToDevice));
-    for (int i = 0; i < count; ++i)
-      if (plan_indexes(&w[i]))
-        TERN_HIP(tern::launch_res_index(w[i].mask[0], w[i].rowptr[0], w[i].rscale[0], w[i].n,
-                                        mask_words(w[i].k, w[i].group),
-                                        reinterpret_cast<uint32_t*>(base + ioff[i]), nullptr));
-    TERN_HIP(tern::launch_tile_bounds(static_cast<GemvDesc*>(ws), (int)items.size(), nullptr));
+    // the residual index serves the matrix-core decode launch (records)
+    if (!recs.empty())
+      for (size_t t = 0; t < items.size(); ++t)
+        if (plan_indexes(&w[mat[t]])) items[t].gidx[0] = reinterpret_cast<const uint32_t*>(base + ioff[mat[t]]);
+    TERN_HIP(hipMemcpy(base, items.data(), items.size() * sizeof(GemvDesc), hipMemcpyHostToDevice));
+    if (!recs.empty()) {
+      TERN_HIP(hipMemcpy(base + dbytes, recs.data(), recs.size() * sizeof(tern::WgRec), hipMemcpyHostToDevice));
+      for (int i = 0; i < count; ++i)
+        if (plan_indexes(&w[i]))
+          TERN_HIP(tern::launch_res_index(w[i].mask[0], w[i].rowptr[0], w[i].rscale[0], w[i].n,
+                                          mask_words(w[i].k, w[i].group),
+                                          reinterpret_cast<uint32_t*>(base + ioff[i]), nullptr));
+      TERN_HIP(tern::launch_tile_bounds(reinterpret_cast<const GemvDesc*>(base),
+                                        reinterpret_cast<tern::WgRec*>(base + dbytes), (int)recs.size(), nullptr));
+    }
     TERN_HIP(hipDeviceSynchronize());
   }
   tern_plan* p = static_cast<tern_plan*>(std::malloc(sizeof(tern_plan)));
   if (!p) return fail(TERN_E_INVAL, "out of host memory");
-  p->dev = static_cast<const GemvDesc*>(ws);
-  p->total_items = (int)items.size();
+  p->dev = reinterpret_cast<const GemvDesc*>(base);
+  p->recs = recs.empty() ? nullptr : reinterpret_cast<const tern::WgRec*>(base + dbytes);
+  p->ndesc = (int)items.size();
+  p->total_items = recs.empty() ? (int)items.size() : (int)recs.size();
   p->format = count > 0 ? w[0].format : 0;
   p->group = count > 0 ? w[0].group : 128;
   p->mt = mt;
@@ -1122,7 +1156,7 @@ tern_status tern_plan_run(const tern_plan* plan, void* stream) {
   }
   GemvDesc dummy;
   std::memset(&dummy, 0, sizeof(dummy));
-  TERN_HIP(launch_decode(plan->format, plan->group, plan->mt, plan->dev, plan->total_items, dummy,
+  TERN_HIP(launch_decode(plan->format, plan->group, plan->mt, plan->dev, plan->recs, plan->ndesc, dummy,
                          plan->total_items, plan->max_krp, plan->offsets, (hipStream_t)stream));
   return TERN_OK;
 }
