@@ -558,10 +558,21 @@ static tern_status place_balanced(const std::vector<GemvDesc>& parts, const std:
 // A batch launch reads one descriptor per work item: the descriptor of the
 // (matrix, block of activation rows) the item belongs to, longest K first.
 // Every descriptor covers its whole K (no split across workgroups).
+// Lane-per-row decode kernel (base-3): products whose K is at least twice
+// the shortest are split along K (parts start on stage boundaries) so their
+// work items end with the others; the parts write FP32 partials
+// [splits][m][n] that one grouped reduce sums in split order.  `partial_base`
+// is where the partials start in the workspace (after the item table).
+struct DecodeSplits {
+  std::vector<tern::RedDesc> red;
+  size_t partial_bytes = 0;
+  int red_blocks = 0;
+};
+
 static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y,
                                int32_t count, int32_t m, int32_t y_dtype, std::vector<GemvDesc>* items,
                                int* mt, int* max_krp, bool* offsets, std::vector<int>* mat,
-                               std::vector<tern::WgRec>* recs) {
+                               std::vector<tern::WgRec>* recs, DecodeSplits* sp = nullptr, char* ws = nullptr) {
   if (count < 0) return fail(TERN_E_INVAL, "count=%d is negative", count);
   if (count > 0 && (!w || !x || !y)) return fail(TERN_E_INVAL, "NULL descriptor arrays");
   if (m < 0) return fail(TERN_E_INVAL, "m=%d is negative", m);
@@ -613,13 +624,43 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
     const int slots = tern_cu_count() * tern::gemv_mfma_wgs_per_cu(w[0].group, *mt, *max_krp, *offsets);
     return place_balanced(parts, pmat, slots, items, mat, recs);
   }
+  // K splits of the long products
+  int kmin = 1 << 30;
+  for (const GemvDesc& d : parts) kmin = std::min(kmin, d.k);
+  std::vector<int> nsp(parts.size(), 1), gps(parts.size(), 0);
+  size_t nitems = 0;
+  for (size_t t = 0; t < parts.size(); ++t) {
+    gps[t] = parts[t].ng;
+    if (sp && parts[t].k >= 2 * kmin) split_k(&w[pmat[t]], parts[t].k / kmin, *mt, &nsp[t], &gps[t]);
+    nitems += (size_t)parts[t].row_blocks * nsp[t];
+  }
+  if (nitems > (size_t)INT32_MAX) return fail(TERN_E_UNSUPPORTED, "batch too large");
+  const size_t dbytes = round_up(nitems * sizeof(GemvDesc), 256);
+  size_t poff = 0;
   for (size_t t = 0; t < parts.size(); ++t) {
     GemvDesc d = parts[t];
     d.tile_begin = (int)items->size();
-    if ((size_t)d.tile_begin + d.row_blocks > (size_t)INT32_MAX) return fail(TERN_E_UNSUPPORTED, "batch too large");
-    items->insert(items->end(), (size_t)d.row_blocks, d);
-    if (mat) mat->insert(mat->end(), (size_t)d.row_blocks, pmat[t]);
+    if (nsp[t] > 1) {
+      d.splits = nsp[t];
+      d.gps = gps[t];
+      d.partial = ws ? reinterpret_cast<float*>(ws + dbytes + poff) : nullptr;
+      tern::RedDesc rd;
+      rd.partial = d.partial;
+      rd.y = d.y;
+      rd.splits = nsp[t];
+      rd.m = d.m;
+      rd.n = d.n;
+      rd.y_f32 = d.y_f32;
+      rd.begin = sp->red_blocks;
+      sp->red.push_back(rd);
+      sp->red_blocks += (int)(((size_t)d.m * d.n + 255) / 256);
+      poff += round_up((size_t)nsp[t] * d.m * d.n * 4, 256);
+    }
+    const size_t cnt = (size_t)d.row_blocks * nsp[t];
+    items->insert(items->end(), cnt, d);
+    if (mat) mat->insert(mat->end(), cnt, pmat[t]);
   }
+  if (sp) sp->partial_bytes = poff;
   return TERN_OK;
 }
 
@@ -924,7 +965,30 @@ size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m
   }
   size_t idx = 0;
   for (int i = 0; i < count; ++i) idx += index_bytes(&w[i]);
-  if (!use_mfma(w[0].format)) return round_up(items * sizeof(GemvDesc), 256) + idx;
+  if (!use_mfma(w[0].format)) {
+    // lane-per-row decode: K splits of the long products, their partials and
+    // reduce table (the layout build_batch makes)
+    int kmin = 1 << 30;
+    for (int i = 0; i < count; ++i)
+      if (w[i].n > 0 && w[i].k > 0) kmin = std::min(kmin, w[i].k);
+    const int mtp = pick_mt(std::min(m, cmax));
+    size_t nitems = 0, partial = 0, nred = 0;
+    for (int i = 0; i < count; ++i) {
+      if (w[i].n <= 0 || w[i].k <= 0) continue;
+      int ns = 1, gps = w[i].k / w[i].group;
+      if (w[i].k >= 2 * kmin) split_k(&w[i], w[i].k / kmin, mtp, &ns, &gps);
+      const size_t rb = (size_t)(w[i].n + tern::kGemvRows - 1) / tern::kGemvRows;
+      for (int c0 = 0; c0 < m; c0 += cmax) {
+        const int mc = std::min(cmax, m - c0);
+        nitems += rb * ns;
+        if (ns > 1) {
+          partial += round_up((size_t)ns * mc * w[i].n * 4, 256);
+          ++nred;
+        }
+      }
+    }
+    return round_up(nitems * sizeof(GemvDesc), 256) + round_up(partial + nred * sizeof(tern::RedDesc), 256) + idx;
+  }
   // matrix-core decode: at most two row ranges per (matrix, block of rows)
   // and one record per workgroup; balanced placement may split items up to
   // the launch's resident slots (at most 3 workgroups per CU)
@@ -986,11 +1050,14 @@ tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, vo
     return TERN_OK;
   }
   std::vector<tern::WgRec> recs;
-  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets, nullptr, &recs));
+  DecodeSplits sp;
+  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets, nullptr, &recs, &sp,
+                       static_cast<char*>(ws)));
   if (items.empty()) return TERN_OK;
-  // workspace: [descriptors][records of the matrix-core decode launch]
+  // workspace: [descriptors][records of the matrix-core decode launch, or
+  // the split partials and their reduce table]
   const size_t dbytes = round_up(items.size() * sizeof(GemvDesc), 256);
-  const size_t need = dbytes + recs.size() * sizeof(tern::WgRec);
+  const size_t need = dbytes + recs.size() * sizeof(tern::WgRec) + sp.partial_bytes + sp.red.size() * sizeof(tern::RedDesc);
   if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "batched decode needs %zu workspace bytes", need);
   TERN_TRY(check_dev(ws, true, "ws"));
   hipStream_t s = (hipStream_t)stream;
@@ -998,10 +1065,16 @@ tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, vo
   TERN_HIP(hipMemcpyAsync(base, items.data(), items.size() * sizeof(GemvDesc), hipMemcpyHostToDevice, s));
   if (!recs.empty())
     TERN_HIP(hipMemcpyAsync(base + dbytes, recs.data(), recs.size() * sizeof(tern::WgRec), hipMemcpyHostToDevice, s));
+  if (!sp.red.empty())
+    TERN_HIP(hipMemcpyAsync(base + dbytes + sp.partial_bytes, sp.red.data(), sp.red.size() * sizeof(tern::RedDesc),
+                            hipMemcpyHostToDevice, s));
   const int nwg = recs.empty() ? (int)items.size() : (int)recs.size();
   TERN_HIP(launch_decode(w[0].format, w[0].group, mt, reinterpret_cast<const GemvDesc*>(base),
                          recs.empty() ? nullptr : reinterpret_cast<const tern::WgRec*>(base + dbytes),
                          (int)items.size(), items[0], nwg, max_krp, offsets, s));
+  if (!sp.red.empty())
+    TERN_HIP(tern::launch_reduce_grouped(reinterpret_cast<const tern::RedDesc*>(base + dbytes + sp.partial_bytes),
+                                         (int)sp.red.size(), sp.red_blocks, s));
   return TERN_OK;
 }
 
@@ -1086,10 +1159,14 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
     return TERN_OK;
   }
   std::vector<tern::WgRec> recs;
-  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets, &mat, &recs));
-  // workspace: [descriptors][workgroup records][residual index of each matrix]
+  DecodeSplits sp;
+  TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets, &mat, &recs, &sp,
+                       static_cast<char*>(ws)));
+  // workspace: [descriptors][workgroup records, or split partials and their
+  // reduce table][residual index of each matrix]
   const size_t dbytes = round_up(items.size() * sizeof(GemvDesc), 256);
-  const size_t rbytes = round_up(recs.size() * sizeof(tern::WgRec), 256);
+  const size_t rbytes = round_up(recs.size() * sizeof(tern::WgRec), 256) +
+                        round_up(sp.partial_bytes + sp.red.size() * sizeof(tern::RedDesc), 256);
   char* base = static_cast<char*>(ws);
   if (!items.empty()) {
     std::vector<size_t> ioff(count, 0);
@@ -1105,6 +1182,9 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
       for (size_t t = 0; t < items.size(); ++t)
         if (plan_indexes(&w[mat[t]])) items[t].gidx[0] = reinterpret_cast<const uint32_t*>(base + ioff[mat[t]]);
     TERN_HIP(hipMemcpy(base, items.data(), items.size() * sizeof(GemvDesc), hipMemcpyHostToDevice));
+    if (!sp.red.empty())
+      TERN_HIP(hipMemcpy(base + dbytes + sp.partial_bytes, sp.red.data(), sp.red.size() * sizeof(tern::RedDesc),
+                         hipMemcpyHostToDevice));
     if (!recs.empty()) {
       TERN_HIP(hipMemcpy(base + dbytes, recs.data(), recs.size() * sizeof(tern::WgRec), hipMemcpyHostToDevice));
       for (int i = 0; i < count; ++i)
@@ -1131,8 +1211,9 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
   p->gemm = false;
   p->small = false;
   p->aw = p->np = 0;
-  p->red = nullptr;
-  p->nred = p->red_blocks = 0;
+  p->red = sp.red.empty() ? nullptr : reinterpret_cast<const tern::RedDesc*>(base + dbytes + sp.partial_bytes);
+  p->nred = (int)sp.red.size();
+  p->red_blocks = sp.red_blocks;
   *out = p;
   return TERN_OK;
 }
@@ -1158,6 +1239,8 @@ tern_status tern_plan_run(const tern_plan* plan, void* stream) {
   std::memset(&dummy, 0, sizeof(dummy));
   TERN_HIP(launch_decode(plan->format, plan->group, plan->mt, plan->dev, plan->recs, plan->ndesc, dummy,
                          plan->total_items, plan->max_krp, plan->offsets, (hipStream_t)stream));
+  if (plan->nred)
+    TERN_HIP(tern::launch_reduce_grouped(plan->red, plan->nred, plan->red_blocks, (hipStream_t)stream));
   return TERN_OK;
 }
 
