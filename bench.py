@@ -226,6 +226,43 @@ def bench_gemm512(args, stream):
     return dict(flops=flops, steps=steps, step_s=step_s, tflops=flops / step_s / 1e12)
 
 
+def bench_layer8b(args, stream, m, fmt=1):
+    """One Qwen3-8B-class layer (seven projections, one plan) at m activation
+    rows: the batched variant's sweep points below M=512."""
+    import torch
+    from ternary_weight_only_tern_amd import lib as L
+    from ternary_weight_only_tern_amd import synth
+    pms, xs, ys = [], [], []
+    for proj in range(len(synth.QWEN3_8B_LAYER)):
+        pm, _ = pack_config(4, fmt, proj)
+        xd, _ = x_for(4, proj, m)
+        pms.append(pm)
+        xs.append(xd)
+        ys.append(torch.empty((m, pm.n), dtype=torch.float16, device="cuda"))
+    plan = L.Plan(pms, xs, ys)
+    steps = max(4, args.steps // 20)
+    wall, gpu, _ = time_graph([lambda: plan.run(stream.cuda_stream)], steps, 4, stream)
+    step_s = gpu / steps
+    nbytes = sum(pm.nbytes() for pm in pms)
+    flops = sum(2.0 * m * pm.n * pm.k for pm in pms)
+    return dict(us_per_layer=step_s * 1e6, gbs=nbytes / step_s / 1e9, tflops=flops / step_s / 1e12, steps=steps)
+
+
+def bench_read_probe(stream, nbytes, copies):
+    """Attainable read bandwidth: the library's plain streaming-read probe
+    over `copies` distinct buffers of nbytes each, one launch per buffer."""
+    import torch
+    from ternary_weight_only_tern_amd import lib as L
+    bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device="cuda") for _ in range(copies)]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    fns = [(lambda b=b: L.tern_read_probe(b, sink, stream.cuda_stream)) for b in bufs]
+    steps = copies * max(1, 360 // copies)
+    wall, gpu, _ = time_graph(fns, steps, copies, stream)
+    step_s = gpu / steps
+    del bufs
+    return dict(bytes=nbytes, us=step_s * 1e6, gbs=nbytes / step_s / 1e9)
+
+
 def cpu_baseline(mats, fmt, budget_s=12.0):
     """The oracle's unpack-and-dot on one thread, over whole layers of the
     same workload until about budget_s seconds of CPU work."""
@@ -309,6 +346,20 @@ def main():
         extra["qwen3_8b_layer_m512_b3"] = dict(tflops=g["tflops"], mfma_frac=g["tflops"] / F16_MFMA_PEAK_TFS,
                                                us_per_layer=g["step_s"] * 1e6, steps=g["steps"])
         log(f"bench: M=512 {g['tflops']:.1f} TFLOP/s")
+        sweep = {}
+        for m in (1, 4, 16, 64):
+            q = bench_layer8b(args, stream, m)
+            sweep[f"m{m}"] = dict(us_per_layer=round(q["us_per_layer"], 2), gbs=round(q["gbs"], 1),
+                                  tflops=round(q["tflops"], 2))
+            log(f"bench: 8B-class layer base-3 M={m}: {q['us_per_layer']:.1f} us, {q['gbs']:.1f} GB/s")
+        extra["qwen3_8b_layer_b3_sweep"] = sweep
+        # attainable read bandwidth on this machine: a plain reduction over 1 GiB
+        # buffers, and over 36 buffers of the headline layer's size
+        big = bench_read_probe(stream, 1 << 30, 2)
+        lay = bench_read_probe(stream, r["layer_bytes"] // 256 * 256, LAYERS)
+        extra["read_probe"] = dict(gbs_1gib=round(big["gbs"], 1), gbs_layer_size=round(lay["gbs"], 1),
+                                   us_layer_size=round(lay["us"], 2), kernel="tern_read_probe (plain streaming read)")
+        log(f"bench: read probe {big['gbs']:.1f} GB/s (1 GiB), {lay['gbs']:.1f} GB/s ({lay['bytes']} B per launch)")
     cpu = None
     if not args.skip_cpu:
         log("bench: cpu baseline (oracle)")

@@ -211,6 +211,13 @@ void tern_plan_destroy(tern_plan *plan);
  * Any output pointer may be NULL.  Host-only. */
 tern_status tern_bits(const tern_matrix *w, double *info, double *plane, double *storage);
 
+/* Measurement aid, not part of the product: a plain streaming read of
+ * `bytes` bytes (a multiple of 16) of device memory at `buf` (16-byte
+ * aligned), the attainable-bandwidth reference for the products above.
+ * `sink` is a device u32 that is written only for one improbable input
+ * (it keeps the loads from being dropped).  Async on stream. */
+tern_status tern_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
 const char *tern_status_str(tern_status s);
 const char *tern_last_error(void);
 

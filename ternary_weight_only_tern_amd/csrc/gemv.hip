@@ -36,6 +36,8 @@
 // (a wave prefix sum over the per-row counts places each row's entries), one
 // lane per block decodes it against the group's activations, and each lane
 // then sums the values of its own row's entries in order.
+#include <algorithm>
+
 #include "internal.h"
 
 #define GLOBAL __attribute__((address_space(1)))
@@ -509,6 +511,29 @@ __global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __
   }
 }
 
+// Plain streaming read of `bytes` bytes (a multiple of 16): every wavefront
+// reads 8 KB of consecutive bytes per round (eight 1 KB loads in flight, 16
+// bytes per lane), rounds striding over the grid; the sink is written only
+// if the XOR of everything read equals a value no input here produces, so
+// the loads cannot be dropped.
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ p, size_t n16, uint32_t* sink) {
+  const size_t waves = (size_t)gridDim.x * 4;
+  const size_t wave = (size_t)blockIdx.x * 4 + threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  uint32_t acc = 0;
+  for (size_t base = wave * 512; base < n16; base += waves * 512) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t i = base + (size_t)u * 64 + lane;
+      v[u] = i < n16 ? p[i] : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
 __global__ void splitk_reduce_kernel(const float* __restrict__ partial, int splits, int m, int n,
                                      void* y, int y_f32) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -545,6 +570,15 @@ int gemv_stage_groups(int format, int group) {
   // groups per stage; split boundaries must be multiples of this
   if (format == 0) return group == 64 ? Geo<0, 64>::SG : Geo<0, 128>::SG;
   return group == 64 ? Geo<1, 64>::SG : Geo<1, 128>::SG;
+}
+
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const size_t want = (n16 + 4 * 512 - 1) / (4 * 512);  // one round per wavefront
+  const unsigned blocks = (unsigned)std::min<size_t>(want, 2048);
+  hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const uint4*>(buf), n16, sink);
+  return hipGetLastError();
 }
 
 hipError_t launch_splitk_reduce(const float* partial, int splits, int m, int n, void* y, int y_f32,

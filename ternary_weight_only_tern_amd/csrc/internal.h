@@ -100,6 +100,9 @@ hipError_t launch_res_index(const uint32_t* mask, const uint32_t* rowptr, const 
 // row0 is the item's first row.
 hipError_t launch_tile_bounds(const GemvDesc* ranges, WgRec* recs, int count, hipStream_t stream);
 
+// Plain streaming read of bytes (a multiple of 16) from buf (measurement).
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 // ---- MFMA product (gemm.hip)
 hipError_t launch_gemm(const GemvDesc& d, int format, hipStream_t stream);
 // Activation rows per matrix-core tile for m activation rows (256 or 128).

@@ -1246,6 +1246,15 @@ tern_status tern_plan_run(const tern_plan* plan, void* stream) {
 
 void tern_plan_destroy(tern_plan* plan) { std::free(plan); }
 
+tern_status tern_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes % 16) return fail(TERN_E_INVAL, "bytes=%zu is not a multiple of 16", bytes);
+  if (bytes == 0) return TERN_OK;
+  TERN_TRY(check_dev(buf, true, "buf"));
+  TERN_TRY(check_dev(sink, true, "sink", 4));
+  TERN_HIP(tern::launch_read_probe(buf, bytes, sink, (hipStream_t)stream));
+  return TERN_OK;
+}
+
 tern_status tern_bits(const tern_matrix* w, double* info, double* plane, double* storage) {
   if (!w) return fail(TERN_E_INVAL, "matrix descriptor is NULL");
   TERN_TRY(check_shape(w->n, w->k, w->group, w->planes, w->format, w->offset_mode));

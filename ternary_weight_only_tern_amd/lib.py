@@ -36,7 +36,7 @@ TERN_F32 = 1
 SYMBOLS = ["tern_row_stride", "tern_check", "tern_packed_sizes", "tern_workspace_bytes",
            "tern_pack", "tern_unpack", "tern_gemv", "tern_gemm", "tern_batch_workspace_bytes",
            "tern_gemv_batched", "tern_plan_create", "tern_plan_run", "tern_plan_destroy",
-           "tern_bits", "tern_status_str", "tern_last_error"]
+           "tern_bits", "tern_read_probe", "tern_status_str", "tern_last_error"]
 
 
 class tern_matrix(ctypes.Structure):
@@ -80,6 +80,7 @@ def load() -> ctypes.CDLL:
         "tern_plan_run": (c_int32, [c_void_p, c_void_p]),
         "tern_plan_destroy": (None, [c_void_p]),
         "tern_bits": (c_int32, [P, POINTER(c_double), POINTER(c_double), POINTER(c_double)]),
+        "tern_read_probe": (c_int32, [c_void_p, c_size_t, c_void_p, c_void_p]),
         "tern_status_str": (ctypes.c_char_p, [c_int32]),
         "tern_last_error": (ctypes.c_char_p, []),
     }
@@ -265,6 +266,11 @@ class Plan:
         if getattr(self, "handle", None) and _lib is not None:
             _lib.tern_plan_destroy(self.handle)
             self.handle = None
+
+
+def tern_read_probe(buf, sink, stream=None) -> None:
+    """Plain streaming read of a whole device tensor (measurement aid)."""
+    check(load().tern_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
 
 
 def tern_bits(pm: PackedMatrix) -> dict:

@@ -5,6 +5,8 @@ Packing must be byte-identical to the oracle's encoding; products must meet
 (the tolerance the project fixes for FP32 accumulation on FP16 inputs), with
 y == 0 exactly where that bound is 0.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -404,3 +406,19 @@ def test_small_m_batches_match_oracle(fmt, group, m):
         else:
             for y, f in zip(ys, first):
                 assert torch.equal(y, f), "plan runs differ"
+
+
+def test_read_probe_runs_and_checks_arguments():
+    """The measurement probe reads a buffer without touching the sink (its
+    XOR is not the sentinel for a buffer of ones) and rejects sizes that are
+    not a multiple of 16."""
+    import torch
+    say("read probe")
+    buf = torch.ones(1 << 20, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    L.tern_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.sum().item()) == 0
+    lib = L.load()
+    st = lib.tern_read_probe(ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(24), ctypes.c_void_p(sink.data_ptr()), None)
+    assert st == L.TERN_E_INVAL
