@@ -422,3 +422,55 @@ def test_read_probe_runs_and_checks_arguments():
     lib = L.load()
     st = lib.tern_read_probe(ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(24), ctypes.c_void_p(sink.data_ptr()), None)
     assert st == L.TERN_E_INVAL
+
+
+@pytest.mark.parametrize("m", [64, 512])
+def test_grouped_layer_config4_matches_oracle(m):
+    """The 8B-class layer (base-3, seven projections) through one plan at the
+    sizes the benchmark times: one grouped matrix-core launch whose long-K
+    product may be cut into K parts with FP32 partials and a grouped reduce;
+    every output within the bound."""
+    import torch
+    say("grouped layer config 4", m)
+    mats, pms, xs, ys, refs = [], [], [], [], []
+    for proj in range(7):
+        mat = synth.config_matrix(4, proj)
+        x = synth.config_x(4, m, proj)
+        pms.append(upload_pack(mat, O.FMT_B3))
+        xs.append(to_dev(x.view(np.uint16)).view(torch.float16))
+        ys.append(torch.empty((m, mat["n"]), dtype=torch.float16, device="cuda"))
+        refs.append(oracle_y(mat, x))
+    plan = L.Plan(pms, xs, ys)
+    plan.run()
+    torch.cuda.synchronize()
+    for proj, (y, (y_ref, b)) in enumerate(zip(ys, refs)):
+        check_y(y, y_ref, b, f"grouped layer m={m} proj={proj}")
+
+
+def test_stack_plan_config3_matches_oracle():
+    """The 8B-class stack at M=1 (base-3, 36 layers x 7 projections) through
+    one plan as the benchmark runs it: the layers are byte copies of one
+    packed layer, so every layer's outputs must meet the bound against the
+    oracle's outputs for that layer."""
+    import torch
+    import bench
+    say("stack plan config 3")
+    base, xs, refs = [], [], []
+    for proj in range(7):
+        mat = synth.config_matrix(3, proj)
+        x = synth.config_x(3, 1, proj)
+        base.append(upload_pack(mat, O.FMT_B3))
+        xs.append(to_dev(x.view(np.uint16)).view(torch.float16))
+        refs.append(oracle_y(mat, x))
+    mats, xl, yl = [], [], []
+    for layer in range(36):
+        for proj, pm in enumerate(base):
+            mats.append(pm if layer == 0 else bench.clone_packed(pm))
+            xl.append(xs[proj])
+            yl.append(torch.empty((1, pm.n), dtype=torch.float16, device="cuda"))
+    plan = L.Plan(mats, xl, yl)
+    plan.run()
+    torch.cuda.synchronize()
+    for i, y in enumerate(yl):
+        y_ref, b = refs[i % 7]
+        check_y(y, y_ref, b, f"stack layer {i // 7} proj {i % 7}")
