@@ -729,9 +729,25 @@ static std::vector<int> gemm_splits(const tern_matrix* w, int32_t count, int32_t
   return parts;
 }
 
-// One descriptor per output tile (tile_rows x 128) and K part; tiles of the
-// longest K parts first, and within a product the weight tile fastest.  With
-// ws == nullptr only the layout is computed.
+// Workgroup j of a launch runs on XCD j mod 8, and each XCD has its own L2.
+// Each product's tiles (K part, then activation tile, weight tile fastest)
+// are cut into 8 runs, run x for XCD x, so the workgroups of one XCD share
+// activation tiles in its L2; every XCD takes the products longest K part
+// first.  Positions a short XCD list leaves open hold empty descriptors
+// (n = 0) that exit at once.
+constexpr int kXcds = 8;
+
+static size_t xcd_slots(const std::vector<size_t>& counts) {
+  size_t len[kXcds] = {0};
+  for (size_t t : counts)
+    for (int x = 0; x < kXcds; ++x) len[x] += (x + 1) * t / kXcds - x * t / kXcds;
+  size_t mx = 0;
+  for (int x = 0; x < kXcds; ++x) mx = std::max(mx, len[x]);
+  return mx * kXcds;
+}
+
+// One descriptor per output tile (tile_rows x 128) and K part, laid out by
+// XCD as above.  With ws == nullptr only the layout is computed.
 static tern_status build_gemm_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y,
                                     int32_t count, int32_t m, int32_t y_dtype, char* ws, TileBatch* out) {
   if (count < 0) return fail(TERN_E_INVAL, "count=%d is negative", count);
@@ -757,10 +773,13 @@ static tern_status build_gemm_batch(const tern_matrix* w, const uint16_t* const*
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return w[a].k > w[b].k; });
   const std::vector<int> parts = gemm_splits(w, count, m);
   const int bm = tern::gemm_tile_rows(m);
-  size_t ntiles = 0;
-  for (int i : order) ntiles += (size_t)parts[i] * ((m + bm - 1) / bm) * ((w[i].n + 127) / 128);
+  std::vector<size_t> counts;
+  for (int i : order) counts.push_back((size_t)parts[i] * ((m + bm - 1) / bm) * ((w[i].n + 127) / 128));
+  const size_t ntiles = xcd_slots(counts);
   if (ntiles >= (size_t)INT32_MAX) return fail(TERN_E_UNSUPPORTED, "batch too large");
   const size_t tiles_bytes = round_up(ntiles * sizeof(GemvDesc), 256);
+  std::vector<std::vector<GemvDesc>> ptiles;
+  std::vector<int> plen;
   size_t poff = 0;
   for (int i : order) {
     GemvDesc d;
@@ -780,20 +799,35 @@ static tern_status build_gemm_batch(const tern_matrix* w, const uint16_t* const*
       out->red_blocks += (int)(((size_t)m * w[i].n + 255) / 256);
       poff += round_up((size_t)parts[i] * m * w[i].n * 4, 256);
     }
+    ptiles.emplace_back();
+    plen.push_back(0);
     for (int p = 0; p < parts[i]; ++p) {
       d.ks0 = r[p];
       d.ks1 = r[p + 1];
       d.kpart = parts[i] > 1 ? p : -1;
+      plen.back() = std::max(plen.back(), r[p + 1] - r[p]);
       for (int tm = 0; tm < m; tm += bm)
         for (int tn = 0; tn < w[i].n; tn += 128) {
           d.tm0 = tm;
           d.tn0 = tn;
-          out->tiles.push_back(d);
+          ptiles.back().push_back(d);
         }
     }
   }
-  std::stable_sort(out->tiles.begin(), out->tiles.end(),
-                   [](const GemvDesc& a, const GemvDesc& b) { return a.ks1 - a.ks0 > b.ks1 - b.ks0; });
+  std::vector<int> pord(ptiles.size());
+  for (size_t j = 0; j < pord.size(); ++j) pord[j] = (int)j;
+  std::stable_sort(pord.begin(), pord.end(), [&](int a, int b) { return plen[a] > plen[b]; });
+  std::vector<std::vector<GemvDesc>> lists(kXcds);
+  for (int j : pord) {
+    const size_t t = ptiles[j].size();
+    for (int x = 0; x < kXcds; ++x)
+      lists[x].insert(lists[x].end(), ptiles[j].begin() + x * t / kXcds, ptiles[j].begin() + (x + 1) * t / kXcds);
+  }
+  GemvDesc none;
+  std::memset(&none, 0, sizeof(none));
+  out->tiles.assign(ntiles, none);
+  for (int x = 0; x < kXcds; ++x)
+    for (size_t r2 = 0; r2 < lists[x].size(); ++r2) out->tiles[r2 * kXcds + x] = lists[x][r2];
   out->partial_bytes = poff;
   return TERN_OK;
 }
@@ -802,16 +836,17 @@ static tern_status build_gemm_batch(const tern_matrix* w, const uint16_t* const*
 static size_t gemm_batch_ws_bytes(const tern_matrix* w, int32_t count, int32_t m) {
   const std::vector<int> parts = gemm_splits(w, count, m);
   const int bm = tern::gemm_tile_rows(m);
-  size_t ntiles = 0, partial = 0, nred = 0;
+  size_t partial = 0, nred = 0;
+  std::vector<size_t> counts;
   for (int i = 0; i < count; ++i) {
     if (w[i].n <= 0 || w[i].k <= 0) continue;
-    ntiles += (size_t)parts[i] * ((m + bm - 1) / bm) * ((w[i].n + 127) / 128);
+    counts.push_back((size_t)parts[i] * ((m + bm - 1) / bm) * ((w[i].n + 127) / 128));
     if (parts[i] > 1) {
       partial += round_up((size_t)parts[i] * m * w[i].n * 4, 256);
       ++nred;
     }
   }
-  return round_up(ntiles * sizeof(GemvDesc), 256) + partial + nred * sizeof(tern::RedDesc);
+  return round_up(xcd_slots(counts) * sizeof(GemvDesc), 256) + partial + nred * sizeof(tern::RedDesc);
 }
 
 // ---- small m on the 16-row matrix-core product
