@@ -152,7 +152,7 @@ tern_status tern_unpack(const tern_matrix *src, int8_t *trits, void *ws, size_t 
  * "Can ternary LLMs hit 1.58 bits per weight", How It Works, and 2609.09240's
  * direct packed execution).  m == 0 is a no-op; m >= 64 is
  * TERN_E_UNSUPPORTED (use tern_gemm).  ws: tern_workspace_bytes(w, m).
- * Up to m = 3 (base-3) or 4 (2-bit) the decode kernels run; from there to
+ * Up to m = 2 (base-3) or 3 (2-bit) the decode kernels run; from there to
  * m = 32 the 16-row matrix-core product of tern_gemv_batched, which copies a
  * table of work descriptors into ws (hipMemcpyAsync on stream) on each call;
  * from m = 33 the tiles of tern_gemm. */
@@ -168,7 +168,7 @@ tern_status tern_gemm(const tern_matrix *w, const uint16_t *x, int32_t m, void *
 /* Grouped product: count independent products y[i] = x[i] W[i]^T with the
  * same m, format, group and output dtype, in one launch (the layer's
  * projections of one token batch, say), products with the longest K first:
- *   m <= 3 (base-3) or 4 (2-bit): the decode kernels, one workgroup per
+ *   m <= 2 (base-3) or 3 (2-bit): the decode kernels, one workgroup per
  *     block of output rows;
  *   up to m = 32: FP16 MFMA on 16-row tiles decoded into LDS, K split into
  *     ranges of 4-step multiples with FP32 partials summed in split order
@@ -181,7 +181,7 @@ tern_status tern_gemm(const tern_matrix *w, const uint16_t *x, int32_t m, void *
  *      (hipMemcpyAsync on stream) on every call.  For repeated launches use
  *      tern_plan_create / tern_plan_run.
  * On the decode kernels every product covers its whole K in one workgroup:
- * 2-bit batches of m <= 4 take k <= 12288 (TERN_E_UNSUPPORTED otherwise;
+ * 2-bit batches of m <= 3 take k <= 12288 (TERN_E_UNSUPPORTED otherwise;
  * use tern_gemv).
  * Products need k > 0 and group 64 or 128 (TERN_E_UNSUPPORTED otherwise). */
 size_t tern_batch_workspace_bytes(const tern_matrix *w, int32_t count, int32_t m);

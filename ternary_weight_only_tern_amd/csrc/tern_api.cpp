@@ -252,11 +252,11 @@ struct tern_plan {
 extern "C" {
 
 // Routing of products by activation rows (crossovers measured on an
-// 8B-class layer on the MI355X): the decode kernels up to m = 3 (base-3) or
-// 4 (2-bit), the 16-row matrix-core product up to m = 32 (its time grows per
+// 8B-class layer on the MI355X): the decode kernels up to m = 2 (base-3) or
+// 3 (2-bit), the 16-row matrix-core product up to m = 32 (its time grows per
 // 16 rows), the 128/256-row matrix-core tiles from m = 33.
 static bool gemm_route(int m) { return m >= 33; }
-static bool small_route(int format, int m) { return !gemm_route(m) && m >= (format == TERN_FMT_B3 ? 4 : 5); }
+static bool small_route(int format, int m) { return !gemm_route(m) && m >= (format == TERN_FMT_B3 ? 3 : 4); }
 
 // Workspace of a small-m product batch (defined with the batch builder).
 static size_t small_batch_ws_bytes(const tern_matrix* w, int32_t count, int32_t m);
@@ -852,15 +852,17 @@ static size_t gemm_batch_ws_bytes(const tern_matrix* w, int32_t count, int32_t m
 // ---- small m on the 16-row matrix-core product
 // Decoded once per 16 activation rows, so the decode-bound small-m products
 // keep the HBM stream; K is split into step ranges (64 trits per step,
-// ranges a multiple of 4 steps) so that the grid holds about 1024 workgroups
+// ranges a multiple of 4 steps) so that the grid holds about three workgroups
+// per CU
 // and no product's K runs long in one workgroup.  Unsplit tiles write y;
 // split ones write FP32 partials that one grouped reduce sums in split order.
 
 
 // Step ranges of a product with `steps` steps when the batch holds `total`
-// tile-steps: a multiple of 4 steps each, at least 8, about total / 1024.
+// tile-steps: a multiple of 4 steps each, at least 8, about total / (3 x CUs).
 static std::vector<int> small_ranges(int steps, long total) {
-  int u = (int)std::max<long>(8, (total / 1024 + 3) / 4 * 4);
+  const long target = 3L * tern_cu_count();  // measured best: three workgroups per CU
+  int u = (int)std::max<long>(8, (total / target + 3) / 4 * 4);
   const int nr = std::max(1, (steps + u - 1) / u);
   std::vector<int> b(nr + 1, 0);
   const int q4 = (steps + 3) / 4;  // ranges in units of 4 steps

@@ -136,7 +136,7 @@ def _gemv_case(mat, fmt, m, x_law="normal", f32=False, seed=0, batched=False):
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("shape", SMALL_SHAPES)
-@pytest.mark.parametrize("m", [1, 3, 4, 5, 8])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8])
 def test_gemv_small(shape, fmt, m):
     n, k, g, planes, frac, off = shape
     say("gemv small", shape, fmt, m)
@@ -368,10 +368,10 @@ SMALL_BATCHES = {
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("group", [128, 64])
-@pytest.mark.parametrize("m", [1, 3, 4, 5, 9, 16, 17, 32, 33, 40])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 9, 16, 17, 32, 33, 40])
 def test_small_m_batches_match_oracle(fmt, group, m):
-    """Batched calls and plans at m <= 63 (the decode kernels up to 3 rows
-    for base-3 and 4 for 2-bit; the 16-row matrix-core product with K split
+    """Batched calls and plans at m <= 63 (the decode kernels up to 2 rows
+    for base-3 and 3 for 2-bit; the 16-row matrix-core product with K split
     into step ranges and a grouped reduce up to 32; the 128-row tiles above):
     single-step, odd-step and split products, ragged rows, 1-3 planes, every
     offset mode, against the oracle."""
