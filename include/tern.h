@@ -153,9 +153,9 @@ tern_status tern_unpack(const tern_matrix *src, int8_t *trits, void *ws, size_t 
  * direct packed execution).  m == 0 is a no-op; m >= 64 is
  * TERN_E_UNSUPPORTED (use tern_gemm).  ws: tern_workspace_bytes(w, m).
  * Up to m = 2 (base-3) or 3 (2-bit) the decode kernels run; from there to
- * m = 32 the 16-row matrix-core product of tern_gemv_batched, which copies a
- * table of work descriptors into ws (hipMemcpyAsync on stream) on each call;
- * from m = 33 the tiles of tern_gemm. */
+ * m = 32 the 16-row matrix-core product of tern_gemv_batched, which copies
+ * its work tables into ws (hipMemcpyAsync on stream) on each call; from
+ * m = 33 the tiles of tern_gemm. */
 tern_status tern_gemv(const tern_matrix *w, const uint16_t *x, int32_t m, void *y,
                       int32_t y_dtype, void *ws, size_t ws_bytes, void *stream);
 
@@ -169,29 +169,33 @@ tern_status tern_gemm(const tern_matrix *w, const uint16_t *x, int32_t m, void *
  * same m, format, group and output dtype, in one launch (the layer's
  * projections of one token batch, say), products with the longest K first:
  *   m <= 2 (base-3) or 3 (2-bit): the decode kernels, one workgroup per
- *     block of output rows;
+ *     block of output rows (2-bit: work items packed onto the CUs by size;
+ *     base-3: products of at least twice the shortest K cut into K parts);
  *   up to m = 32: FP16 MFMA on 16-row tiles decoded into LDS, K split into
- *     ranges of 4-step multiples with FP32 partials summed in split order
- *     by a second launch;
- *   m >= 33: the matrix-core path of tern_gemm over every product's tiles.
+ *     ranges of 4-step multiples;
+ *   m >= 33: the matrix-core path of tern_gemm over every product's tiles,
+ *     long-K products cut into K parts when that shortens the launch.
+ *   K parts write FP32 partials to ws that a second launch sums in part
+ *   order (results are bitwise reproducible).
  *   w  host array [count] of descriptors
  *   x  host array [count] of device pointers, y likewise
- *   ws device workspace of tern_batch_workspace_bytes(w, count, m) bytes; a
- *      table of one work descriptor per workgroup is copied into it
- *      (hipMemcpyAsync on stream) on every call.  For repeated launches use
- *      tern_plan_create / tern_plan_run.
- * On the decode kernels every product covers its whole K in one workgroup:
- * 2-bit batches of m <= 3 take k <= 12288 (TERN_E_UNSUPPORTED otherwise;
- * use tern_gemv).
+ *   ws device workspace of tern_batch_workspace_bytes(w, count, m) bytes:
+ *      the work tables (descriptors, per-workgroup records) are copied into
+ *      it (hipMemcpyAsync on stream) on every call, and it holds the
+ *      partials.  For repeated launches use tern_plan_create / tern_plan_run.
+ * On the 2-bit decode kernel every product covers its whole K in one
+ * workgroup: 2-bit batches of m <= 3 take k <= 12288 (TERN_E_UNSUPPORTED
+ * otherwise; use tern_gemv).
  * Products need k > 0 and group 64 or 128 (TERN_E_UNSUPPORTED otherwise). */
 size_t tern_batch_workspace_bytes(const tern_matrix *w, int32_t count, int32_t m);
 tern_status tern_gemv_batched(const tern_matrix *w, const uint16_t *const *x, void *const *y,
                               int32_t count, int32_t m, int32_t y_dtype, void *ws,
                               size_t ws_bytes, void *stream);
 
-/* A prepared grouped product.  tern_plan_create copies the work-descriptor
- * table into the caller's device buffer `ws` of tern_batch_workspace_bytes bytes
- * (synchronously) and returns a host
+/* A prepared grouped product.  tern_plan_create copies the work tables into
+ * the caller's device buffer `ws` of tern_batch_workspace_bytes bytes (which
+ * also holds the plan's partials and residual index; synchronously) and
+ * returns a host
  * handle (malloc'ed; free it with tern_plan_destroy).  tern_plan_run
  * launches the whole batch on stream; it may be called any number of times
  * and captured in a HIP graph.  The buffers named in the plan must stay
