@@ -107,11 +107,19 @@ __device__ __forceinline__ h8_t lds_h8(const uint8_t* lds, uint32_t off) {
   return *reinterpret_cast<const h8_t*>(lds + off);
 }
 
-// 16 bytes (64 trits) of block c of the row at `wrow`; reads past the range
-// are clamped onto its last 16 bytes (their activations are zero).
-__device__ __forceinline__ u4_t wload(const GLOBAL uint8_t* wrow, int c, int q, int rbytes) {
-  const int off = min(c * 64 + q * 16, rbytes - 16);
-  return *reinterpret_cast<const GLOBAL u4_t*>(wrow + off);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes (64 trits) of block c (wave-uniform) of this lane's part of its
+// row: a buffer resource from the item's first row (uniform), the lane's
+// row and quarter as the per-lane offset and the block as the scalar one;
+// bytes past the matrix read as zero.
+__device__ __forceinline__ u4_t wload(__amdgpu_buffer_rsrc_t part, int c, uint32_t lane_off) {
+  // c is the same in every lane (the compiler cannot prove it of values
+  // derived from the wavefront index, and would loop over its values)
+  return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(part, lane_off,
+                                                                        __builtin_amdgcn_readfirstlane(c) * 64, 0));
 }
 
 // 0.5 * scale of this lane's four slots 4q .. 4q+3 in the window whose first
@@ -177,9 +185,6 @@ __device__ __forceinline__ void decode_quarter(uint32_t v, h8_t* bb) {
   bb[1] = t[1];
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
 
 // 16 bytes per lane from a buffer straight into LDS, without registers: lane
 // l of the wavefront writes dst + 16 l, so dst must be the same in every lane
@@ -402,7 +407,14 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, const WgRec* __restric
                           (tile * kRowsWave + r) * spitch + (pga - (sflat ? 0 : ga));
   const int ngp = pgb - pga;
   // an empty part reads, and ignores, the item's first 16 bytes
-  const GLOBAL uint8_t* wr = nblk > 0 ? wrow : wrow - (pb0 * kBlockTrits) / 4;
+  const __amdgpu_buffer_rsrc_t wpart =
+      rsrc(d.plane0 + (size_t)row0 * d.stride, (uint32_t)min((size_t)(d.n - row0) * d.stride, (size_t)0xFFFFFFF0u));
+  const uint32_t wq = (uint32_t)(rowc - row0) * (uint32_t)d.stride + (uint32_t)(k0 + (nblk > 0 ? pb0 * kBlockTrits : 0)) / 4u +
+                      (uint32_t)q * 16u;
+  // the block (within each window) in which this lane's A slot is active:
+  // slot r % GW holds group GPB * (block % BW) + q / (4 / GPB); -1 if never
+  const int rg_ = (r % GW) - q / (4 / GPB);
+  const int wsel = a_row && rg_ >= 0 && rg_ % GPB == 0 && rg_ / GPB < BW ? rg_ / GPB : -1;
 
   // One 16-entry batch: entry t = b0 + r (t < wn) has block quarter BLKQ and
   // group GRR (relative to the item's range); its scaled partial sums go to
@@ -446,10 +458,7 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, const WgRec* __restric
   // unrolled body because BW divides 8.
 #define TERN_BLOCK(V, C, I)                                                                   \
   do {                                                                                        \
-    const int wc_ = (I) % BW;                                                                 \
-    const int grel_ = GPB * wc_ + q / (4 / GPB);                                              \
-    const bool act_ = a_row && (r % GW) == grel_;                                             \
-    const uint32_t aoff_ = act_ ? abase + (uint32_t)(C) * (kBlockTrits * 2) : 0u;             \
+    const uint32_t aoff_ = wsel == (I) % BW ? abase + (uint32_t)(C) * (kBlockTrits * 2) : 0u; \
     h8_t b_[8];                                                                               \
     decode_two((V).x, (V).y, &b_[0]);                                                         \
     decode_two((V).z, (V).w, &b_[4]);                                                         \
@@ -481,7 +490,7 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, const WgRec* __restric
     /* the weights, behind the small operands in every wavefront's queue */                  \
     __builtin_amdgcn_sched_barrier(0);                                                        \
     constexpr int DP_ = NB < kDepth ? NB : kDepth;                                            \
-    _Pragma("unroll") for (int i = 0; i < DP_; ++i) w_[i] = wload(wr, min(i, max(nblk - 1, 0)), q, rbytes); \
+    _Pragma("unroll") for (int i = 0; i < DP_; ++i) w_[i] = wload(wpart, min(i, max(nblk - 1, 0)), wq); \
     __builtin_amdgcn_sched_barrier(0);                                                        \
     if (tid < nsch - nsfull) *reinterpret_cast<u4_t*>(lds + scoff + (nsfull + tid) * 16) = sfix; \
     if (tid < kZeroBytes / 16) *reinterpret_cast<u4_t*>(lds + tid * 16) = u4_t{0u, 0u, 0u, 0u}; \
@@ -490,7 +499,7 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, const WgRec* __restric
     /* plane 0, with this wavefront's residual batches after its first blocks */            \
     _Pragma("unroll") for (int i = 0; i < NB; ++i) {                                          \
       /* keep DP_ blocks in flight: request block i + DP_ before block i is used */          \
-      if (i + DP_ < NB) w_[i + DP_] = wload(wr, min(i + DP_, max(nblk - 1, 0)), q, rbytes);     \
+      if (i + DP_ < NB) w_[i + DP_] = wload(wpart, min(i + DP_, max(nblk - 1, 0)), wq);        \
       if (i < nblk) {                                                                         \
         TERN_BLOCK(w_[i], i, i);                                                              \
         if (i % BW == BW - 1) TERN_CLOSE(i / BW);                                             \
