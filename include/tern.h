@@ -168,9 +168,11 @@ tern_status tern_gemm(const tern_matrix *w, const uint16_t *x, int32_t m, void *
 /* Grouped product: count independent products y[i] = x[i] W[i]^T with the
  * same m, format, group and output dtype, in one launch (the layer's
  * projections of one token batch, say), products with the longest K first:
- *   m <= 2 (base-3) or 3 (2-bit): the decode kernels, one workgroup per
- *     block of output rows (2-bit: work items packed onto the CUs by size;
- *     base-3: products of at least twice the shortest K cut into K parts);
+ *   m <= 2 (base-3), 5 (2-bit, group 128) or 4 (2-bit, group 64): the
+ *     decode kernels, one workgroup per block of output rows (2-bit: work
+ *     items packed onto the CUs by size, products longer than a workgroup's
+ *     activation stage cut into K parts; base-3: products of at least twice
+ *     the shortest K cut into K parts);
  *   up to m = 32: FP16 MFMA on 16-row tiles decoded into LDS, K split into
  *     ranges of 4-step multiples;
  *   m >= 33: the matrix-core path of tern_gemm over every product's tiles,
@@ -183,9 +185,6 @@ tern_status tern_gemm(const tern_matrix *w, const uint16_t *x, int32_t m, void *
  *      the work tables (descriptors, per-workgroup records) are copied into
  *      it (hipMemcpyAsync on stream) on every call, and it holds the
  *      partials.  For repeated launches use tern_plan_create / tern_plan_run.
- * On the 2-bit decode kernel every product covers its whole K in one
- * workgroup: 2-bit batches of m <= 3 take k <= 12288 (TERN_E_UNSUPPORTED
- * otherwise; use tern_gemv).
  * Products need k > 0 and group 64 or 128 (TERN_E_UNSUPPORTED otherwise). */
 size_t tern_batch_workspace_bytes(const tern_matrix *w, int32_t count, int32_t m);
 tern_status tern_gemv_batched(const tern_matrix *w, const uint16_t *const *x, void *const *y,

@@ -253,10 +253,15 @@ extern "C" {
 
 // Routing of products by activation rows (crossovers measured on an
 // 8B-class layer on the MI355X): the decode kernels up to m = 2 (base-3) or
-// 3 (2-bit), the 16-row matrix-core product up to m = 32 (its time grows per
-// 16 rows), the 128/256-row matrix-core tiles from m = 33.
+// one 2-bit decode pass (m = 5 at group 128, where a pass holds 8 rows but
+// the 16-row product wins from 6; m = 4 at group 64), the 16-row
+// matrix-core product up to m = 32 (its time grows per 16 rows), the
+// 128/256-row matrix-core tiles from m = 33.
 static bool gemm_route(int m) { return m >= 33; }
-static bool small_route(int format, int m) { return !gemm_route(m) && m >= (format == TERN_FMT_B3 ? 3 : 4); }
+static bool small_route(int format, int group, int m) {
+  const int decode_max = format == TERN_FMT_B3 ? 2 : (group == 128 ? 5 : 4);
+  return !gemm_route(m) && m > decode_max;
+}
 
 // Workspace of a small-m product batch (defined with the batch builder).
 static size_t small_batch_ws_bytes(const tern_matrix* w, int32_t count, int32_t m);
@@ -294,7 +299,7 @@ tern_status tern_packed_sizes(int32_t n, int32_t k, int32_t group, int32_t forma
 size_t tern_workspace_bytes(const tern_matrix* w, int32_t m) {
   if (!w || check_shape(w->n, w->k, w->group, w->planes, w->format, w->offset_mode) != TERN_OK) return 0;
   const size_t packing = kFlagBytes + round_up(((size_t)w->n + 1) * 4, 256);
-  const size_t product = m > 0 && small_route(w->format, m) ? small_batch_ws_bytes(w, 1, m) : gemv_ws_bytes(w, m);
+  const size_t product = m > 0 && small_route(w->format, w->group, m) ? small_batch_ws_bytes(w, 1, m) : gemv_ws_bytes(w, m);
   return std::max(packing, product);
 }
 
@@ -392,7 +397,7 @@ tern_status tern_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* 
     TERN_HIP(tern::launch_gemm(d, w->format, s));  // k == 0: zero fill
     return TERN_OK;
   }
-  if (small_route(w->format, m)) {
+  if (small_route(w->format, w->group, m)) {
     void* yp = y;
     return tern_gemv_batched(w, &x, &yp, 1, m, y_dtype, ws, ws_bytes, stream);
   }
@@ -466,12 +471,14 @@ static tern_status place_balanced(const std::vector<GemvDesc>& parts, const std:
   // coarse (current kwaves) and fine (twice the kwaves) items per part
   std::vector<int> coarse(parts.size()), fine(parts.size(), 0);
   long total = 0;
+  // (row blocks; a part with K splits has that many items per row block)
+  auto ns_of = [&](size_t t) { return (long)parts[t].splits; };
   for (size_t t = 0; t < parts.size(); ++t) {
     coarse[t] = parts[t].row_blocks;
-    total += coarse[t];
+    total += coarse[t] * ns_of(t);
   }
   auto rows_of = [&](size_t t, bool f) { return rows_per_item(parts[t].kwaves * (f ? 2 : 1)); };
-  auto nblk_of = [&](size_t t) { return (long)((parts[t].k + 255) / 256); };
+  auto nblk_of = [&](size_t t) { return (long)((std::min(parts[t].k, parts[t].gps * parts[t].group) + 255) / 256); };
   auto fine_count = [&](size_t t, int a) {
     const int left = std::max(0, parts[t].n - a * rows_of(t, false));
     return (left + rows_of(t, true) - 1) / rows_of(t, true);
@@ -487,8 +494,9 @@ static tern_status place_balanced(const std::vector<GemvDesc>& parts, const std:
     }
     if (best < 0) break;
     const int a = coarse[bt] - 1, f = fine_count(bt, a);
-    if (total - (coarse[bt] + fine[bt]) + a + f > slots) break;
-    total += a + f - (coarse[bt] + fine[bt]);
+    const long grow = (a + f - (coarse[bt] + fine[bt])) * ns_of(bt);
+    if (total + grow > slots) break;
+    total += grow;
     coarse[bt] = a;
     fine[bt] = f;
   }
@@ -507,7 +515,8 @@ static tern_status place_balanced(const std::vector<GemvDesc>& parts, const std:
       }
       d.row_blocks = cnt;
       const long tiles = rows_of(t, f != 0) / 16;
-      for (int rb = 0; rb < cnt; ++rb) all.push_back(PlaceItem{(int)ranges.size(), rb, tiles * nblk_of(t) + 4});
+      // item = split * row_blocks + row block (the kernel's decomposition)
+      for (int it = 0; it < cnt * d.splits; ++it) all.push_back(PlaceItem{(int)ranges.size(), it, tiles * nblk_of(t) + 4});
       ranges.push_back(d);
       rmat.push_back(pmat[t]);
     }
@@ -567,7 +576,29 @@ struct DecodeSplits {
   std::vector<tern::RedDesc> red;
   size_t partial_bytes = 0;
   int red_blocks = 0;
+  size_t recs_off = 0;  // matrix-core decode: where the workgroup records start
+  size_t part_off = 0;  // where the partials start (the reduce table follows them)
 };
+
+// K parts of a 2-bit product on the matrix-core decode kernel at mp
+// activation rows: a workgroup stages the activations of its K range, so a
+// product longer than the stage holds is cut into parts (split_k), each with
+// kwaves chosen for its own length.
+static void mfma_split(const tern_matrix* w, int mp, int nblk_min, int* ns, int* gps, int* kw) {
+  const int cap = tern::gemv_mfma_max_range(mp);
+  *ns = 1;
+  *gps = w->k / w->group;
+  if (round256(w->k) > cap) split_k(w, (w->k + cap - 1) / cap, mp, ns, gps);
+  *kw = choose_kwaves(w->format, std::min(w->k, *gps * w->group), nblk_min);
+}
+
+// Workspace offsets of a matrix-core decode batch with nparts (matrix, row
+// chunk) parts and at most items_max workgroups: [row ranges (two per part)]
+// [workgroup records][partials][reduce table].
+static void mfma_offsets(size_t nparts, size_t items_max, size_t* recs_off, size_t* part_off) {
+  *recs_off = round_up(2 * nparts * sizeof(GemvDesc), 256);
+  *part_off = *recs_off + round_up(items_max * sizeof(tern::WgRec), 256);
+}
 
 static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y,
                                int32_t count, int32_t m, int32_t y_dtype, std::vector<GemvDesc>* items,
@@ -583,7 +614,7 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
   *max_krp = 0;
   *offsets = false;
   std::vector<int> order;
-  int kmax = 0, nblk_min = 1 << 30;
+  int nblk_min = 1 << 30;
   for (int i = 0; i < count; ++i) {
     TERN_TRY(check_matrix(&w[i]));
     if (w[i].format != w[0].format || w[i].group != w[0].group)
@@ -593,16 +624,9 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
     if (w[i].k == 0) return fail(TERN_E_UNSUPPORTED, "batched decode needs k > 0");
     TERN_TRY(check_xy(x[i], y[i], y_dtype));
     order.push_back(i);
-    kmax = std::max(kmax, w[i].k);
     nblk_min = std::min(nblk_min, (w[i].k + 255) / 256);
   }
-  int cmax = count > 0 ? max_mt(w[0].format, w[0].group) : 1;
-  if (count > 0 && use_mfma(w[0].format)) {
-    // every descriptor covers its whole K, which the activation stage must hold
-    if (round256(kmax) > tern::gemv_mfma_max_range(1))
-      return fail(TERN_E_UNSUPPORTED, "batched 2-bit decode takes k <= %d (got %d)", tern::gemv_mfma_max_range(1), kmax);
-    while (cmax > 1 && round256(kmax) > tern::gemv_mfma_max_range(cmax)) cmax /= 2;
-  }
+  const int cmax = count > 0 ? max_mt(w[0].format, w[0].group) : 1;
   *mt = pick_mt(std::min(std::max(m, 1), cmax));
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return w[a].k > w[b].k; });
   const size_t esz = y_dtype == TERN_F32 ? 4 : 2;
@@ -621,7 +645,45 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
     }
   }
   if (count > 0 && use_mfma(w[0].format)) {
+    // products longer than the activation stage holds at mt rows are cut
+    // into K parts whose FP32 partials a grouped reduce sums in part order
+    *max_krp = 0;
+    size_t coarse_items = 0;
+    for (size_t t = 0; t < parts.size(); ++t) {
+      GemvDesc& d = parts[t];
+      int ns, g, kw;
+      mfma_split(&w[pmat[t]], *mt, nblk_min, &ns, &g, &kw);
+      set_kwaves(d, kw);
+      d.splits = ns;
+      d.gps = g;
+      *max_krp = std::max(*max_krp, round256(std::min(d.k, g * d.group)));
+      coarse_items += (size_t)d.row_blocks * ns;
+    }
     const int slots = tern_cu_count() * tern::gemv_mfma_wgs_per_cu(w[0].group, *mt, *max_krp, *offsets);
+    size_t recs_off, part_off;
+    mfma_offsets(parts.size(), std::max(coarse_items, (size_t)slots), &recs_off, &part_off);
+    size_t poff = 0;
+    for (GemvDesc& d : parts) {
+      if (d.splits <= 1) continue;
+      if (!sp) return fail(TERN_E_UNSUPPORTED, "K parts need the workspace layout");
+      d.partial = ws ? reinterpret_cast<float*>(ws + part_off + poff) : nullptr;
+      tern::RedDesc rd;
+      rd.partial = d.partial;
+      rd.y = d.y;
+      rd.splits = d.splits;
+      rd.m = d.m;
+      rd.n = d.n;
+      rd.y_f32 = d.y_f32;
+      rd.begin = sp->red_blocks;
+      sp->red.push_back(rd);
+      sp->red_blocks += (int)(((size_t)d.m * d.n + 255) / 256);
+      poff += round_up((size_t)d.splits * d.m * d.n * 4, 256);
+    }
+    if (sp) {
+      sp->partial_bytes = poff;
+      sp->recs_off = recs_off;
+      sp->part_off = part_off;
+    }
     return place_balanced(parts, pmat, slots, items, mat, recs);
   }
   // K splits of the long products
@@ -660,7 +722,10 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
     items->insert(items->end(), cnt, d);
     if (mat) mat->insert(mat->end(), cnt, pmat[t]);
   }
-  if (sp) sp->partial_bytes = poff;
+  if (sp) {
+    sp->partial_bytes = poff;
+    sp->part_off = dbytes;
+  }
   return TERN_OK;
 }
 
@@ -984,22 +1049,12 @@ static size_t index_bytes(const tern_matrix* w) { return plan_indexes(w) ? round
 size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m) {
   if (count <= 0 || m <= 0 || !w) return 0;
   if (gemm_route(m)) return gemm_batch_ws_bytes(w, count, m);
-  if (small_route(w[0].format, m)) return small_batch_ws_bytes(w, count, m);
-  int cmax = max_mt(w[0].format, w[0].group), kmax = 0, nblk_min = 1 << 30;
-  for (int i = 0; i < count; ++i) {
-    if (w[i].n <= 0 || w[i].k <= 0) continue;
-    kmax = std::max(kmax, w[i].k);
-    nblk_min = std::min(nblk_min, (w[i].k + 255) / 256);
-  }
-  if (use_mfma(w[0].format))
-    while (cmax > 1 && round256(kmax) > tern::gemv_mfma_max_range(cmax)) cmax /= 2;
-  const size_t chunks = (size_t)(m + cmax - 1) / cmax;
-  size_t items = 0;
-  for (int i = 0; i < count; ++i) {
-    if (w[i].n <= 0 || w[i].k <= 0) continue;
-    const int rpi = rows_per_item(choose_kwaves(w[i].format, w[i].k, nblk_min));
-    items += (size_t)((w[i].n + rpi - 1) / rpi) * chunks;
-  }
+  if (small_route(w[0].format, w[0].group, m)) return small_batch_ws_bytes(w, count, m);
+  const int cmax = max_mt(w[0].format, w[0].group);
+  int nblk_min = 1 << 30;
+  for (int i = 0; i < count; ++i)
+    if (w[i].n > 0 && w[i].k > 0) nblk_min = std::min(nblk_min, (w[i].k + 255) / 256);
+  const int mtp = pick_mt(std::min(m, cmax));
   size_t idx = 0;
   for (int i = 0; i < count; ++i) idx += index_bytes(&w[i]);
   if (!use_mfma(w[0].format)) {
@@ -1008,7 +1063,6 @@ size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m
     int kmin = 1 << 30;
     for (int i = 0; i < count; ++i)
       if (w[i].n > 0 && w[i].k > 0) kmin = std::min(kmin, w[i].k);
-    const int mtp = pick_mt(std::min(m, cmax));
     size_t nitems = 0, partial = 0, nred = 0;
     for (int i = 0; i < count; ++i) {
       if (w[i].n <= 0 || w[i].k <= 0) continue;
@@ -1026,14 +1080,29 @@ size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m
     }
     return round_up(nitems * sizeof(GemvDesc), 256) + round_up(partial + nred * sizeof(tern::RedDesc), 256) + idx;
   }
-  // matrix-core decode: at most two row ranges per (matrix, block of rows)
-  // and one record per workgroup; balanced placement may split items up to
-  // the launch's resident slots (at most 3 workgroups per CU)
-  size_t ranges = 0;
-  for (int i = 0; i < count; ++i)
-    if (w[i].n > 0 && w[i].k > 0) ranges += 2 * chunks;
-  items = std::max(items, (size_t)tern_cu_count() * 3);
-  return round_up(ranges * sizeof(GemvDesc), 256) + round_up(items * sizeof(tern::WgRec), 256) + idx;
+  // matrix-core decode: two row ranges per (matrix, row chunk), one record
+  // per workgroup (balanced placement may split items up to the launch's
+  // resident slots: at most 3 workgroups per CU), the K parts' partials and
+  // their reduce table (the layout build_batch makes)
+  size_t nparts = 0, coarse = 0, partial = 0, nred = 0;
+  for (int i = 0; i < count; ++i) {
+    if (w[i].n <= 0 || w[i].k <= 0) continue;
+    int ns, g, kw;
+    mfma_split(&w[i], mtp, nblk_min, &ns, &g, &kw);
+    const size_t rb = (size_t)(w[i].n + rows_per_item(kw) - 1) / rows_per_item(kw);
+    for (int c0 = 0; c0 < m; c0 += cmax) {
+      const int mc = std::min(cmax, m - c0);
+      ++nparts;
+      coarse += rb * ns;
+      if (ns > 1) {
+        partial += round_up((size_t)ns * mc * w[i].n * 4, 256);
+        ++nred;
+      }
+    }
+  }
+  size_t recs_off, part_off;
+  mfma_offsets(nparts, std::max(coarse, (size_t)tern_cu_count() * 3), &recs_off, &part_off);
+  return round_up(part_off + partial + nred * sizeof(tern::RedDesc), 256) + idx;
 }
 
 tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, void* const* y,
@@ -1064,7 +1133,7 @@ tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, vo
                                            (int)b.red.size(), b.red_blocks, s));
     return TERN_OK;
   }
-  if (count > 0 && small_route(w[0].format, m)) {
+  if (count > 0 && small_route(w[0].format, w[0].group, m)) {
     if (!ws) return fail(TERN_E_WORKSPACE, "batched product needs a workspace");
     TERN_TRY(check_dev(ws, true, "ws"));
     TileBatch b;
@@ -1091,27 +1160,28 @@ tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, vo
   TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets, nullptr, &recs, &sp,
                        static_cast<char*>(ws)));
   if (items.empty()) return TERN_OK;
-  // workspace: [descriptors][records of the matrix-core decode launch, or
-  // the split partials and their reduce table]
-  const size_t dbytes = round_up(items.size() * sizeof(GemvDesc), 256);
-  const size_t need = dbytes + recs.size() * sizeof(tern::WgRec) + sp.partial_bytes + sp.red.size() * sizeof(tern::RedDesc);
+  // workspace: [descriptors][workgroup records (matrix-core decode)]
+  // [partials of the K parts][their reduce table], at the offsets the
+  // builder chose
+  const size_t red_off = sp.part_off + sp.partial_bytes;
+  size_t need = std::max(items.size() * sizeof(GemvDesc), red_off + sp.red.size() * sizeof(tern::RedDesc));
+  if (!recs.empty()) need = std::max(need, sp.recs_off + recs.size() * sizeof(tern::WgRec));
   if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "batched decode needs %zu workspace bytes", need);
   TERN_TRY(check_dev(ws, true, "ws"));
   hipStream_t s = (hipStream_t)stream;
   char* base = static_cast<char*>(ws);
   TERN_HIP(hipMemcpyAsync(base, items.data(), items.size() * sizeof(GemvDesc), hipMemcpyHostToDevice, s));
   if (!recs.empty())
-    TERN_HIP(hipMemcpyAsync(base + dbytes, recs.data(), recs.size() * sizeof(tern::WgRec), hipMemcpyHostToDevice, s));
+    TERN_HIP(hipMemcpyAsync(base + sp.recs_off, recs.data(), recs.size() * sizeof(tern::WgRec), hipMemcpyHostToDevice, s));
   if (!sp.red.empty())
-    TERN_HIP(hipMemcpyAsync(base + dbytes + sp.partial_bytes, sp.red.data(), sp.red.size() * sizeof(tern::RedDesc),
-                            hipMemcpyHostToDevice, s));
+    TERN_HIP(hipMemcpyAsync(base + red_off, sp.red.data(), sp.red.size() * sizeof(tern::RedDesc), hipMemcpyHostToDevice, s));
   const int nwg = recs.empty() ? (int)items.size() : (int)recs.size();
   TERN_HIP(launch_decode(w[0].format, w[0].group, mt, reinterpret_cast<const GemvDesc*>(base),
-                         recs.empty() ? nullptr : reinterpret_cast<const tern::WgRec*>(base + dbytes),
+                         recs.empty() ? nullptr : reinterpret_cast<const tern::WgRec*>(base + sp.recs_off),
                          (int)items.size(), items[0], nwg, max_krp, offsets, s));
   if (!sp.red.empty())
-    TERN_HIP(tern::launch_reduce_grouped(reinterpret_cast<const tern::RedDesc*>(base + dbytes + sp.partial_bytes),
-                                         (int)sp.red.size(), sp.red_blocks, s));
+    TERN_HIP(tern::launch_reduce_grouped(reinterpret_cast<const tern::RedDesc*>(base + red_off), (int)sp.red.size(),
+                                         sp.red_blocks, s));
   return TERN_OK;
 }
 
@@ -1159,7 +1229,7 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
     *out = p;
     return TERN_OK;
   }
-  if (count > 0 && small_route(w[0].format, m)) {
+  if (count > 0 && small_route(w[0].format, w[0].group, m)) {
     if (!ws) return fail(TERN_E_WORKSPACE, "plan needs a workspace");
     TERN_TRY(check_dev(ws, true, "ws"));
     TileBatch b;
@@ -1199,15 +1269,17 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
   DecodeSplits sp;
   TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets, &mat, &recs, &sp,
                        static_cast<char*>(ws)));
-  // workspace: [descriptors][workgroup records, or split partials and their
-  // reduce table][residual index of each matrix]
-  const size_t dbytes = round_up(items.size() * sizeof(GemvDesc), 256);
-  const size_t rbytes = round_up(recs.size() * sizeof(tern::WgRec), 256) +
-                        round_up(sp.partial_bytes + sp.red.size() * sizeof(tern::RedDesc), 256);
+  // workspace: [descriptors][workgroup records (matrix-core decode)]
+  // [partials of the K parts][their reduce table][residual index of each
+  // matrix], at the offsets the builder chose
+  const size_t red_off = sp.part_off + sp.partial_bytes;
+  size_t tables = std::max(items.size() * sizeof(GemvDesc), red_off + sp.red.size() * sizeof(tern::RedDesc));
+  if (!recs.empty()) tables = std::max(tables, sp.recs_off + recs.size() * sizeof(tern::WgRec));
+  tables = round_up(tables, 256);
   char* base = static_cast<char*>(ws);
   if (!items.empty()) {
     std::vector<size_t> ioff(count, 0);
-    size_t need = dbytes + rbytes;
+    size_t need = tables;
     for (int i = 0; i < count; ++i) {
       ioff[i] = need;
       need += index_bytes(&w[i]);
@@ -1220,24 +1292,23 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
         if (plan_indexes(&w[mat[t]])) items[t].gidx[0] = reinterpret_cast<const uint32_t*>(base + ioff[mat[t]]);
     TERN_HIP(hipMemcpy(base, items.data(), items.size() * sizeof(GemvDesc), hipMemcpyHostToDevice));
     if (!sp.red.empty())
-      TERN_HIP(hipMemcpy(base + dbytes + sp.partial_bytes, sp.red.data(), sp.red.size() * sizeof(tern::RedDesc),
-                         hipMemcpyHostToDevice));
+      TERN_HIP(hipMemcpy(base + red_off, sp.red.data(), sp.red.size() * sizeof(tern::RedDesc), hipMemcpyHostToDevice));
     if (!recs.empty()) {
-      TERN_HIP(hipMemcpy(base + dbytes, recs.data(), recs.size() * sizeof(tern::WgRec), hipMemcpyHostToDevice));
+      TERN_HIP(hipMemcpy(base + sp.recs_off, recs.data(), recs.size() * sizeof(tern::WgRec), hipMemcpyHostToDevice));
       for (int i = 0; i < count; ++i)
         if (plan_indexes(&w[i]))
           TERN_HIP(tern::launch_res_index(w[i].mask[0], w[i].rowptr[0], w[i].rscale[0], w[i].n,
                                           mask_words(w[i].k, w[i].group),
                                           reinterpret_cast<uint32_t*>(base + ioff[i]), nullptr));
       TERN_HIP(tern::launch_tile_bounds(reinterpret_cast<const GemvDesc*>(base),
-                                        reinterpret_cast<tern::WgRec*>(base + dbytes), (int)recs.size(), nullptr));
+                                        reinterpret_cast<tern::WgRec*>(base + sp.recs_off), (int)recs.size(), nullptr));
     }
     TERN_HIP(hipDeviceSynchronize());
   }
   tern_plan* p = static_cast<tern_plan*>(std::malloc(sizeof(tern_plan)));
   if (!p) return fail(TERN_E_INVAL, "out of host memory");
   p->dev = reinterpret_cast<const GemvDesc*>(base);
-  p->recs = recs.empty() ? nullptr : reinterpret_cast<const tern::WgRec*>(base + dbytes);
+  p->recs = recs.empty() ? nullptr : reinterpret_cast<const tern::WgRec*>(base + sp.recs_off);
   p->ndesc = (int)items.size();
   p->total_items = recs.empty() ? (int)items.size() : (int)recs.size();
   p->format = count > 0 ? w[0].format : 0;
@@ -1248,7 +1319,7 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
   p->gemm = false;
   p->small = false;
   p->aw = p->np = 0;
-  p->red = sp.red.empty() ? nullptr : reinterpret_cast<const tern::RedDesc*>(base + dbytes + sp.partial_bytes);
+  p->red = sp.red.empty() ? nullptr : reinterpret_cast<const tern::RedDesc*>(base + red_off);
   p->nred = (int)sp.red.size();
   p->red_blocks = sp.red_blocks;
   *out = p;

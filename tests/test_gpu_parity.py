@@ -368,11 +368,12 @@ SMALL_BATCHES = {
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("group", [128, 64])
-@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 9, 16, 17, 32, 33, 40])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 9, 16, 17, 32, 33, 40])
 def test_small_m_batches_match_oracle(fmt, group, m):
     """Batched calls and plans at m <= 63 (the decode kernels up to 2 rows
-    for base-3 and 3 for 2-bit; the 16-row matrix-core product with K split
-    into step ranges and a grouped reduce up to 32; the 128-row tiles above):
+    for base-3 and 5 (group 128) or 4 (group 64) for 2-bit; the 16-row
+    matrix-core product with K split into step ranges and a grouped reduce
+    up to 32; the 128-row tiles above):
     single-step, odd-step and split products, ragged rows, 1-3 planes, every
     offset mode, against the oracle."""
     import torch
@@ -403,6 +404,49 @@ def test_small_m_batches_match_oracle(fmt, group, m):
             first = [y.clone() for y in ys]
             for y, (y_ref, b) in zip(ys, refs):
                 check_y(y, y_ref, b, f"small plan m={m}")
+        else:
+            for y, f in zip(ys, first):
+                assert torch.equal(y, f), "plan runs differ"
+
+
+LONG_K_BATCH = [(96, 9728, 2, 0.2, O.OFF_ROW), (50, 5120, 1, 0.0, O.OFF_GROUP),
+                (130, 12288, 3, 0.1, O.OFF_NONE), (70, 14336, 2, 0.3, O.OFF_ROW), (64, 1024, 2, 0.5, O.OFF_NONE)]
+
+
+@pytest.mark.parametrize("group", [128, 64])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5])
+def test_decode_batch_k_parts_match_oracle(group, m):
+    """2-bit batched calls and plans on the matrix-core decode kernel with
+    products longer than one workgroup stages at m activation rows: those
+    are cut into K parts whose FP32 partials a grouped reduce sums, beside
+    products that are not; ragged rows, 1-3 planes, offsets, against the
+    oracle, and plans bitwise reproducible."""
+    import torch
+    say("decode batch k parts", group, m)
+    mats, pms, xs, ys, refs = [], [], [], [], []
+    rng = np.random.default_rng(4000 + 3 * m + group)
+    for i, (n, k, planes, frac, off) in enumerate(LONG_K_BATCH):
+        mat, _ = small_matrix(n, k, group, planes, frac, seed=53 * i + m + group, offset_mode=off, scale_law="lognormal")
+        x = synth.draw_x(rng, m, k, "student_t3")
+        pms.append(upload_pack(mat, O.FMT_2BIT))
+        xs.append(to_dev(x.view(np.uint16)).view(torch.float16))
+        ys.append(torch.empty((m, n), dtype=torch.float16, device="cuda"))
+        refs.append(oracle_y(mat, x))
+    L.tern_gemv_batched(pms, xs, ys)
+    torch.cuda.synchronize()
+    for i, (y, (y_ref, b)) in enumerate(zip(ys, refs)):
+        check_y(y, y_ref, b, f"k-part batch m={m} i={i}")
+    plan = L.Plan(pms, xs, ys)
+    first = None
+    for _ in range(2):
+        for y in ys:
+            y.zero_()
+        plan.run()
+        torch.cuda.synchronize()
+        if first is None:
+            first = [y.clone() for y in ys]
+            for i, (y, (y_ref, b)) in enumerate(zip(ys, refs)):
+                check_y(y, y_ref, b, f"k-part plan m={m} i={i}")
         else:
             for y, f in zip(ys, first):
                 assert torch.equal(y, f), "plan runs differ"
