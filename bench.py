@@ -248,6 +248,61 @@ def bench_layer8b(args, stream, m, fmt=1):
     return dict(us_per_layer=step_s * 1e6, gbs=nbytes / step_s / 1e9, tflops=flops / step_s / 1e12, steps=steps)
 
 
+def bench_stack8b_launches(args, stream):
+    """The same 8B-class stack as 252 single-product launches (one plan per
+    matrix) replayed from one HIP graph per token, beside the one-launch
+    plan."""
+    import torch
+    from ternary_weight_only_tern_amd import lib as L
+    from ternary_weight_only_tern_amd import synth
+    base, xs = [], []
+    for proj in range(len(synth.QWEN3_8B_LAYER)):
+        pm, _ = pack_config(3, 1, proj)
+        base.append(pm)
+        xd, _ = x_for(3, proj, 1)
+        xs.append(xd)
+    plans, nbytes = [], 0
+    for layer in range(LAYERS):
+        for proj, pm in enumerate(base):
+            c = pm if layer == 0 else clone_packed(pm)
+            y = torch.empty((1, c.n), dtype=torch.float16, device="cuda")
+            plans.append(L.Plan([c], [xs[proj]], [y]))
+            nbytes += c.nbytes()
+    torch.cuda.synchronize()
+    steps = max(2, args.steps // 40)
+
+    def token():
+        for p in plans:
+            p.run(stream.cuda_stream)
+    wall, gpu, _ = time_graph([token], steps, 2, stream)
+    step_s = gpu / steps
+    return dict(stack_bytes=nbytes, steps=steps, step_s=step_s, gbs=nbytes / step_s / 1e9, tok_s=1.0 / step_s)
+
+
+STRESS_COPIES = 57  # 57 x 18.9 MB (2-bit) > 1 GiB: beyond the Infinity Cache
+
+
+def bench_stress(args, stream, fmt, m):
+    """Down-projection stress matrix (K=12288, N=4096; three planes on the
+    same 20 % of groups; per-row offsets; log-normal scales; Student-t x) at
+    m rows: one single-product plan per distinct copy, rotated."""
+    import torch
+    from ternary_weight_only_tern_amd import lib as L
+    pm, _ = pack_config(5, fmt, 0)
+    xd, _ = x_for(5, 0, m)
+    copies = [pm] + [clone_packed(pm) for _ in range(STRESS_COPIES - 1)]
+    y = torch.empty((m, pm.n), dtype=torch.float16, device="cuda")
+    plans = [L.Plan([c], [xd], [y]) for c in copies]
+    fns = [(lambda p=p: p.run(stream.cuda_stream)) for p in plans]
+    steps = STRESS_COPIES * max(1, args.steps // (4 * STRESS_COPIES))
+    wall, gpu, _ = time_graph(fns, steps, STRESS_COPIES, stream)
+    step_s = gpu / steps
+    nbytes = pm.nbytes()
+    del plans, copies
+    return dict(us=round(step_s * 1e6, 2), gbs=round(nbytes / step_s / 1e9, 1),
+                hbm_frac=round(nbytes / step_s / 1e9 / HBM_PEAK_GBS, 4), bytes=nbytes, steps=steps)
+
+
 def bench_read_probe(stream, nbytes, copies):
     """Attainable read bandwidth: the library's plain streaming-read probe
     over `copies` distinct buffers of nbytes each, one launch per buffer."""
@@ -286,6 +341,42 @@ def cpu_baseline(mats, fmt, budget_s=12.0):
     return dict(value=nbytes / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
                 sample=f"{done} pass(es) over the 7 projections of one Qwen3-4B-class layer "
                        f"({'2-bit' if fmt == 0 else 'base-3'}, M=1), fp64 unpack-and-dot, 1 thread, {dt:.1f} s")
+
+
+def cpu_host_dense(mats, budget_s=6.0):
+    """Host baseline beside the strict oracle: the oracle's fp64 dense
+    dequantization and a numpy (BLAS) product on every thread the BLAS pool
+    has, over whole layers of the same workload."""
+    from threadpoolctl import threadpool_info
+    import oracle as O
+    from ternary_weight_only_tern_amd import synth
+    xs = [synth.config_x(2, 1, p) for p in range(len(mats))]
+    layer_bytes = sum(O.bits(O.pack(mt["trits"], mt["scales"], mt["mask_bits"], mt["offset"], mt["group"], 0))["total_bytes"]
+                      for mt in mats)
+    nbytes, done = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        for mt, x in zip(mats, xs):
+            masks = [O.mask_bool(mb, mt["k"] // mt["group"]) for mb in mt["mask_bits"]]
+            w = O.dequant(mt["trits"], mt["scales"], masks, mt["offset"], mt["offset_mode"], mt["group"])
+            _ = np.asarray(x, dtype=np.float64) @ w.T
+        nbytes += layer_bytes
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return dict(value=nbytes / dt / 1e9, unit="GB/s", cores=threads, kind="host dense fp64 dequantize + BLAS",
+                cpu_model=model, cpu_count=os.cpu_count(),
+                sample=f"{done} pass(es) over the 7 projections of one Qwen3-4B-class layer (2-bit bytes), {dt:.1f} s")
 
 
 def main():
@@ -333,7 +424,11 @@ def main():
     r = bench_layer4b(args, stream)
     log(f"bench: layer {r['layer_bytes']} B, {r['step_s']*1e6:.2f} us/step, {r['gbs']:.1f} GB/s; "
         f"single launch {r['launch_s']*1e6:.2f} us = {r['launch_gbs']:.1f} GB/s")
-    extra = {}
+    bits = [L.tern_bits(pm) for pm in r["base"]]
+    wts = [pm.n * pm.k for pm in r["base"]]
+    extra = {"headline_bpw": {key: round(sum(b[key] * w for b, w in zip(bits, wts)) / sum(wts), 4)
+                              for key in ("info", "plane", "storage")},
+             "headline_tokens_per_s_equiv": 1.0 / (LAYERS * r["step_s"])}
     if not args.skip_extra:
         log("bench: 8B-class stack")
         s8 = bench_stack8b(args, stream)
@@ -341,6 +436,11 @@ def main():
                                              gbs=s8["gbs"], hbm_frac=s8["gbs"] / HBM_PEAK_GBS,
                                              tokens_per_s_equiv=s8["tok_s"], steps=s8["steps"])
         log(f"bench: stack {s8['gbs']:.1f} GB/s, {s8['tok_s']:.0f} tok/s-eq")
+        s8l = bench_stack8b_launches(args, stream)
+        extra["qwen3_8b_stack_m1_b3_252_launches"] = dict(us_per_token=s8l["step_s"] * 1e6, gbs=s8l["gbs"],
+                                                          hbm_frac=s8l["gbs"] / HBM_PEAK_GBS,
+                                                          tokens_per_s_equiv=s8l["tok_s"], steps=s8l["steps"])
+        log(f"bench: stack as 252 launches {s8l['gbs']:.1f} GB/s, {s8l['tok_s']:.0f} tok/s-eq")
         log("bench: M=512 MFMA layer")
         g = bench_gemm512(args, stream)
         extra["qwen3_8b_layer_m512_b3"] = dict(tflops=g["tflops"], mfma_frac=g["tflops"] / F16_MFMA_PEAK_TFS,
@@ -353,18 +453,29 @@ def main():
                                   tflops=round(q["tflops"], 2))
             log(f"bench: 8B-class layer base-3 M={m}: {q['us_per_layer']:.1f} us, {q['gbs']:.1f} GB/s")
         extra["qwen3_8b_layer_b3_sweep"] = sweep
+        stress = {}
+        for fmt, fname in ((0, "2bit"), (1, "b3")):
+            for m in (1, 8):
+                q = bench_stress(args, stream, fmt, m)
+                stress[f"{fname}_m{m}"] = q
+                log(f"bench: stress down-projection {fname} M={m}: {q['us']:.2f} us, {q['gbs']:.1f} GB/s")
+        extra["stress_down_proj_k12288"] = stress
         # attainable read bandwidth on this machine: a plain reduction over 1 GiB
         # buffers, and over 36 buffers of the headline layer's size
         big = bench_read_probe(stream, 1 << 30, 2)
         lay = bench_read_probe(stream, r["layer_bytes"] // 256 * 256, LAYERS)
         extra["read_probe"] = dict(gbs_1gib=round(big["gbs"], 1), gbs_layer_size=round(lay["gbs"], 1),
-                                   us_layer_size=round(lay["us"], 2), kernel="tern_read_probe (plain streaming read)")
+                                   us_layer_size=round(lay["us"], 2), kernel="tern_read_probe (plain streaming read)",
+                                   headline_frac_of_layer_size_read=round(r["gbs"] / lay["gbs"], 4))
         log(f"bench: read probe {big['gbs']:.1f} GB/s (1 GiB), {lay['gbs']:.1f} GB/s ({lay['bytes']} B per launch)")
     cpu = None
     if not args.skip_cpu:
         log("bench: cpu baseline (oracle)")
         cpu = cpu_baseline(r["mats"], 0 if args.fmt == "2bit" else 1)
         log(f"bench: cpu {cpu['value']:.4f} GB/s")
+        host = cpu_host_dense(r["mats"])
+        extra["cpu_host_dense"] = host
+        log(f"bench: cpu host dense {host['value']:.4f} GB/s on {host['cores']} threads")
 
     out = {
         "metric": "ternary GEMV packed-weight GB/s (% HBM peak) at M=1; TFLOP/s at M=512",

@@ -152,10 +152,12 @@ tern_status tern_unpack(const tern_matrix *src, int8_t *trits, void *ws, size_t 
  * "Can ternary LLMs hit 1.58 bits per weight", How It Works, and 2609.09240's
  * direct packed execution).  m == 0 is a no-op; m >= 64 is
  * TERN_E_UNSUPPORTED (use tern_gemm).  ws: tern_workspace_bytes(w, m).
- * Up to m = 2 (base-3) or 3 (2-bit) the decode kernels run; from there to
- * m = 32 the 16-row matrix-core product of tern_gemv_batched, which copies
- * its work tables into ws (hipMemcpyAsync on stream) on each call; from
- * m = 33 the tiles of tern_gemm. */
+ * Up to m = 2 (base-3), 5 (2-bit, group 128) or 4 (2-bit, group 64) the
+ * decode kernels run; from there to m = 32 the 16-row matrix-core product
+ * of tern_gemv_batched, which copies its work tables from host memory into
+ * ws (hipMemcpyAsync on stream) on each call, so such calls must not be
+ * captured into a HIP graph (use a plan); from m = 33 the tiles of
+ * tern_gemm. */
 tern_status tern_gemv(const tern_matrix *w, const uint16_t *x, int32_t m, void *y,
                       int32_t y_dtype, void *ws, size_t ws_bytes, void *stream);
 

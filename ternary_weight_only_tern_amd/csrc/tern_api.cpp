@@ -600,6 +600,50 @@ static void mfma_offsets(size_t nparts, size_t items_max, size_t* recs_off, size
   *part_off = *recs_off + round_up(items_max * sizeof(tern::WgRec), 256);
 }
 
+// K parts of every product of a decode batch at mp padded activation rows
+// (vectors indexed like w; products with n == 0 or k == 0 keep one part).
+// Matrix-core kernel: parts no longer than the activation stage holds (with
+// kwaves chosen per part); lane-per-row kernel: products of at least twice
+// the shortest K are cut so that their items end with the others.  A batch
+// whose work items cannot fill the GPU even at their finest (16-row items
+// on the matrix-core kernel, where the placement may go that far; 64-row
+// items otherwise) -- one or two products with few rows -- has every product
+// cut further by the factor that brings it to the target: three workgroups
+// per CU on the matrix-core kernel, kTargetItems on the lane-per-row one.
+static void batch_splits(const tern_matrix* w, int count, int m, int mp, std::vector<int>* ns,
+                         std::vector<int>* gps, std::vector<int>* kw) {
+  ns->assign(count, 1);
+  gps->assign(count, 0);
+  kw->assign(count, 1);
+  if (count <= 0) return;
+  const bool mf = use_mfma(w[0].format);
+  const long chunks = (m + max_mt(w[0].format, w[0].group) - 1) / max_mt(w[0].format, w[0].group);
+  auto live = [&](int i) { return w[i].n > 0 && w[i].k > 0; };
+  int kmin = 1 << 30, nblk_min = 1 << 30;
+  for (int i = 0; i < count; ++i)
+    if (live(i)) {
+      kmin = std::min(kmin, w[i].k);
+      nblk_min = std::min(nblk_min, (w[i].k + 255) / 256);
+    }
+  const int rows = mf ? tern::kGemvRows / 4 : tern::kGemvRows;
+  long items = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!live(i)) continue;
+    (*gps)[i] = w[i].k / w[i].group;
+    if (mf) mfma_split(&w[i], mp, nblk_min, &(*ns)[i], &(*gps)[i], &(*kw)[i]);
+    else if (w[i].k >= 2 * kmin) split_k(&w[i], w[i].k / kmin, mp, &(*ns)[i], &(*gps)[i]);
+    items += (long)((w[i].n + rows - 1) / rows) * (*ns)[i] * chunks;
+  }
+  const long target = mf ? 3L * tern_cu_count() : kTargetItems;
+  if (items == 0 || items >= target) return;
+  const int f = (int)((target + items - 1) / items);
+  for (int i = 0; i < count; ++i) {
+    if (!live(i)) continue;
+    split_k(&w[i], (*ns)[i] * f, mp, &(*ns)[i], &(*gps)[i]);
+    if (mf) (*kw)[i] = choose_kwaves(w[i].format, std::min(w[i].k, (*gps)[i] * w[i].group), nblk_min);
+  }
+}
+
 static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y,
                                int32_t count, int32_t m, int32_t y_dtype, std::vector<GemvDesc>* items,
                                int* mt, int* max_krp, bool* offsets, std::vector<int>* mat,
@@ -644,16 +688,17 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
       *offsets = *offsets || w[i].offset_mode != TERN_OFF_NONE;
     }
   }
+  std::vector<int> bns, bgps, bkw;
+  batch_splits(w, count, m, *mt, &bns, &bgps, &bkw);
   if (count > 0 && use_mfma(w[0].format)) {
-    // products longer than the activation stage holds at mt rows are cut
-    // into K parts whose FP32 partials a grouped reduce sums in part order
+    // products cut into K parts write FP32 partials that a grouped reduce
+    // sums in part order
     *max_krp = 0;
     size_t coarse_items = 0;
     for (size_t t = 0; t < parts.size(); ++t) {
       GemvDesc& d = parts[t];
-      int ns, g, kw;
-      mfma_split(&w[pmat[t]], *mt, nblk_min, &ns, &g, &kw);
-      set_kwaves(d, kw);
+      const int ns = bns[pmat[t]], g = bgps[pmat[t]];
+      set_kwaves(d, bkw[pmat[t]]);
       d.splits = ns;
       d.gps = g;
       *max_krp = std::max(*max_krp, round256(std::min(d.k, g * d.group)));
@@ -686,14 +731,13 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
     }
     return place_balanced(parts, pmat, slots, items, mat, recs);
   }
-  // K splits of the long products
-  int kmin = 1 << 30;
-  for (const GemvDesc& d : parts) kmin = std::min(kmin, d.k);
+  // K parts of the products
   std::vector<int> nsp(parts.size(), 1), gps(parts.size(), 0);
   size_t nitems = 0;
   for (size_t t = 0; t < parts.size(); ++t) {
-    gps[t] = parts[t].ng;
-    if (sp && parts[t].k >= 2 * kmin) split_k(&w[pmat[t]], parts[t].k / kmin, *mt, &nsp[t], &gps[t]);
+    nsp[t] = bns[pmat[t]];
+    gps[t] = bgps[pmat[t]];
+    if (nsp[t] > 1 && !sp) return fail(TERN_E_UNSUPPORTED, "K parts need the workspace layout");
     nitems += (size_t)parts[t].row_blocks * nsp[t];
   }
   if (nitems > (size_t)INT32_MAX) return fail(TERN_E_UNSUPPORTED, "batch too large");
@@ -1051,48 +1095,27 @@ size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m
   if (gemm_route(m)) return gemm_batch_ws_bytes(w, count, m);
   if (small_route(w[0].format, w[0].group, m)) return small_batch_ws_bytes(w, count, m);
   const int cmax = max_mt(w[0].format, w[0].group);
-  int nblk_min = 1 << 30;
-  for (int i = 0; i < count; ++i)
-    if (w[i].n > 0 && w[i].k > 0) nblk_min = std::min(nblk_min, (w[i].k + 255) / 256);
   const int mtp = pick_mt(std::min(m, cmax));
+  std::vector<int> bns, bgps, bkw;
+  batch_splits(w, count, m, mtp, &bns, &bgps, &bkw);
   size_t idx = 0;
   for (int i = 0; i < count; ++i) idx += index_bytes(&w[i]);
-  if (!use_mfma(w[0].format)) {
-    // lane-per-row decode: K splits of the long products, their partials and
-    // reduce table (the layout build_batch makes)
-    int kmin = 1 << 30;
-    for (int i = 0; i < count; ++i)
-      if (w[i].n > 0 && w[i].k > 0) kmin = std::min(kmin, w[i].k);
-    size_t nitems = 0, partial = 0, nred = 0;
-    for (int i = 0; i < count; ++i) {
-      if (w[i].n <= 0 || w[i].k <= 0) continue;
-      int ns = 1, gps = w[i].k / w[i].group;
-      if (w[i].k >= 2 * kmin) split_k(&w[i], w[i].k / kmin, mtp, &ns, &gps);
-      const size_t rb = (size_t)(w[i].n + tern::kGemvRows - 1) / tern::kGemvRows;
-      for (int c0 = 0; c0 < m; c0 += cmax) {
-        const int mc = std::min(cmax, m - c0);
-        nitems += rb * ns;
-        if (ns > 1) {
-          partial += round_up((size_t)ns * mc * w[i].n * 4, 256);
-          ++nred;
-        }
-      }
-    }
-    return round_up(nitems * sizeof(GemvDesc), 256) + round_up(partial + nred * sizeof(tern::RedDesc), 256) + idx;
-  }
-  // matrix-core decode: two row ranges per (matrix, row chunk), one record
-  // per workgroup (balanced placement may split items up to the launch's
-  // resident slots: at most 3 workgroups per CU), the K parts' partials and
-  // their reduce table (the layout build_batch makes)
-  size_t nparts = 0, coarse = 0, partial = 0, nred = 0;
+  const bool mf = use_mfma(w[0].format);
+  // lane-per-row decode: one descriptor per work item, then the partials and
+  // reduce table; matrix-core decode: two row ranges per (matrix, row
+  // chunk), one record per workgroup (balanced placement may split items up
+  // to the launch's resident slots: at most 3 workgroups per CU), then the
+  // partials and reduce table (the layouts build_batch makes)
+  size_t nparts = 0, nitems = 0, coarse = 0, partial = 0, nred = 0;
   for (int i = 0; i < count; ++i) {
     if (w[i].n <= 0 || w[i].k <= 0) continue;
-    int ns, g, kw;
-    mfma_split(&w[i], mtp, nblk_min, &ns, &g, &kw);
-    const size_t rb = (size_t)(w[i].n + rows_per_item(kw) - 1) / rows_per_item(kw);
+    const int ns = bns[i];
+    const int rpi = mf ? rows_per_item(bkw[i]) : tern::kGemvRows;
+    const size_t rb = (size_t)(w[i].n + rpi - 1) / rpi;
     for (int c0 = 0; c0 < m; c0 += cmax) {
       const int mc = std::min(cmax, m - c0);
       ++nparts;
+      nitems += rb * ns;
       coarse += rb * ns;
       if (ns > 1) {
         partial += round_up((size_t)ns * mc * w[i].n * 4, 256);
@@ -1100,6 +1123,8 @@ size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m
       }
     }
   }
+  if (!mf)
+    return round_up(nitems * sizeof(GemvDesc), 256) + round_up(partial + nred * sizeof(tern::RedDesc), 256) + idx;
   size_t recs_off, part_off;
   mfma_offsets(nparts, std::max(coarse, (size_t)tern_cu_count() * 3), &recs_off, &part_off);
   return round_up(part_off + partial + nred * sizeof(tern::RedDesc), 256) + idx;

@@ -452,6 +452,34 @@ def test_decode_batch_k_parts_match_oracle(group, m):
                 assert torch.equal(y, f), "plan runs differ"
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m", [1, 2])
+def test_single_product_batches_fill_the_gpu(fmt, m):
+    """A batch or plan of one product cuts it into enough K parts to fill
+    the GPU (FP32 partials, grouped reduce): the down-projection stress
+    matrix (three planes, row offsets, log-normal scales, Student-t x) and a
+    7-row matrix whose parts are single blocks, against the oracle."""
+    import torch
+    say("single product fill", fmt, m)
+    cases = [(synth.config_matrix(5), "student_t3"),
+             (small_matrix(7, 2560, 128, 2, 0.3, seed=77 + m, offset_mode=O.OFF_GROUP)[0], "normal")]
+    rng = np.random.default_rng(500 + m + 10 * fmt)
+    for ci, (mat, law) in enumerate(cases):
+        x = synth.draw_x(rng, m, mat["k"], law)
+        pm = upload_pack(mat, fmt)
+        xd = to_dev(x.view(np.uint16)).view(torch.float16)
+        y_ref, b = oracle_y(mat, x)
+        y = torch.empty((m, mat["n"]), dtype=torch.float16, device="cuda")
+        L.tern_gemv_batched([pm], [xd], [y])
+        torch.cuda.synchronize()
+        check_y(y, y_ref, b, f"single batched case={ci} m={m}")
+        y.zero_()
+        plan = L.Plan([pm], [xd], [y])
+        plan.run()
+        torch.cuda.synchronize()
+        check_y(y, y_ref, b, f"single plan case={ci} m={m}")
+
+
 def test_read_probe_runs_and_checks_arguments():
     """The measurement probe reads a buffer without touching the sink (its
     XOR is not the sentinel for a buffer of ones) and rejects sizes that are
