@@ -480,6 +480,44 @@ def test_single_product_batches_fill_the_gpu(fmt, m):
         check_y(y, y_ref, b, f"single plan case={ci} m={m}")
 
 
+@pytest.mark.parametrize("group", [128, 64])
+@pytest.mark.parametrize("m", [1, 3, 5])
+def test_dense_residual_lists_in_windows(group, m):
+    """Residual planes listed from the masks (no plan index) with every
+    group masked: a wavefront's rows hold several windows of entries, two
+    residual planes, plus a sparse matrix in the same batch; tern_gemv,
+    batched call and plan, against the oracle."""
+    import torch
+    say("dense residual windows", group, m)
+    rng = np.random.default_rng(900 + m + group)
+    cases = [small_matrix(48, 3072, group, 3, 1.0, seed=91 + m, offset_mode=O.OFF_ROW)[0],
+             small_matrix(100, 2048, group, 2, 0.05, seed=92 + m, offset_mode=O.OFF_NONE)[0]]
+    pms, xs, ys, refs = [], [], [], []
+    for mat in cases:
+        x = synth.draw_x(rng, m, mat["k"], "normal")
+        pm = upload_pack(mat, O.FMT_2BIT)
+        xd = to_dev(x.view(np.uint16)).view(torch.float16)
+        y_ref, b = oracle_y(mat, x)
+        y = L.tern_gemv(pm, xd, L.TERN_F32)
+        torch.cuda.synchronize()
+        check_y(y, y_ref, b, f"gemv dense residual m={m}")
+        pms.append(pm)
+        xs.append(xd)
+        ys.append(torch.empty((m, mat["n"]), dtype=torch.float16, device="cuda"))
+        refs.append((y_ref, b))
+    L.tern_gemv_batched(pms, xs, ys)
+    torch.cuda.synchronize()
+    for i, (y, (y_ref, b)) in enumerate(zip(ys, refs)):
+        check_y(y, y_ref, b, f"batched dense residual m={m} i={i}")
+    plan = L.Plan(pms, xs, ys)
+    for y in ys:
+        y.zero_()
+    plan.run()
+    torch.cuda.synchronize()
+    for i, (y, (y_ref, b)) in enumerate(zip(ys, refs)):
+        check_y(y, y_ref, b, f"plan dense residual m={m} i={i}")
+
+
 def test_read_probe_runs_and_checks_arguments():
     """The measurement probe reads a buffer without touching the sink (its
     XOR is not the sentinel for a buffer of ones) and rejects sizes that are
