@@ -392,6 +392,8 @@ def main():
                     help="only run a plain 256 MiB device copy 8 times (HBM counter calibration)")
     ap.add_argument("--gemm512-only", action="store_true",
                     help="only the M=512 matrix-core layer (profiling); prints its result, no JSON line")
+    ap.add_argument("--stack8b-only", action="store_true",
+                    help="only the 8B-class base-3 stack at M=1 (profiling); prints its result, no JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -418,6 +420,10 @@ def main():
     if args.gemm512_only:
         g = bench_gemm512(args, stream)
         log(f"bench: M=512 layer {g['step_s']*1e6:.1f} us, {g['tflops']:.1f} TFLOP/s")
+        return
+    if args.stack8b_only:
+        s8 = bench_stack8b(args, stream)
+        log(f"bench: 8B-class stack {s8['step_s']*1e6:.1f} us per token, {s8['gbs']:.1f} GB/s")
         return
 
     log("bench: packing the 4B-class layer")

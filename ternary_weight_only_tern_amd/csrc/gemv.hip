@@ -26,8 +26,9 @@
 // the FP16 pair (2*t[2i], 2*t[2i+1]) exactly (bit 15 = sign, bit 14 = the top
 // exponent bit: 0x4000 = 2.0), so one v_dot2_f32_f16 against the natural
 // activation pair (x[2i], x[2i+1]) accumulates 2*(t.x) in FP32.  Base-3 bytes
-// are mapped through two 256-entry LDS tables straight to such pair words
-// (see build_b3_entry); the activations are staged in the matching order.
+// are mapped through a 256-entry LDS table (replicated so that lanes spread
+// over the banks) to such pair words (see b3_entry); the activations are
+// staged in the matching order.
 // Per group the FP32 partial is scaled by 0.5*s (exact) and added to the row
 // accumulator.
 //
@@ -106,39 +107,38 @@ constexpr int wave_lds_bytes() {
   return Geo<FMT, G>::WBYTES + MT * Geo<FMT, G>::XDW * 4 + (FMT == 1 ? MT * Geo<FMT, G>::XNAT * 4 : 0);
 }
 
-// Base-3 byte -> FP16 pair words.  For a byte pair (A, B) holding trits
-// t0..t4 and t5..t9, the decode forms five pair words, each bit 15 / 14 (and
-// 31 / 30) being the 2-bit code of a trit, i.e. the FP16 value 2t:
-//   W0 = lutA[A].x & 0xC000C000 = (t0, t1)    W1 = lutA[A].y = (t2, t3)
-//   W3 = lutB[B].x & 0xC000C000 = (t5, t6)    W4 = lutB[B].y = (t7, t8)
-//   W2 = perm(byte 0 of lutA[A].x, byte 2 of lutB[B].x) = (t4, t9)
-// (t4's code sits at bits 6..7 of lutA.x, t9's at bits 22..23 of lutB.x).
+// Base-3 byte -> FP16 pair words.  One 4-byte table entry per byte value v
+// holds the 2-bit codes c0..c4 of its trits t0..t4 (c = t mod 4, so bits
+// 15:14 of a half word are the FP16 value 2t): c0 at bits 14, c1 at 30,
+// c2 at 12, c3 at 28 and c4 twice, at 6 and 22.  For a byte pair (A, B)
+// holding t0..t4 and t5..t9 the decode forms five pair words:
+//   W0 = eA & 0xC000C000 = (t0, t1)           W1 = (eA << 2) & 0xC000C000 = (t2, t3)
+//   W3 = eB & 0xC000C000 = (t5, t6)           W4 = (eB << 2) & 0xC000C000 = (t7, t8)
+//   W2 = perm(byte 0 of eA, byte 2 of eB) = (t4, t9)
 // The activations of a byte pair are staged in the matching order
 // (x0,x1) (x2,x3) (x4,x9) (x5,x6) (x7,x8).
-__device__ void build_b3_entry(int v, uint2* lutA, uint2* lutB) {
-  uint2 a = make_uint2(0u, 0u), b = make_uint2(0u, 0u);
-  if (v < 243) {
-    int r = v;
-    uint32_t c[5];
-    for (int i = 0; i < 5; ++i) {
-      c[i] = (uint32_t)((r % 3) - 1) & 3u;
-      r /= 3;
-    }
-    a.x = (c[0] << 14) | (c[1] << 30) | (c[4] << 6);
-    a.y = (c[2] << 14) | (c[3] << 30);
-    b.x = (c[0] << 14) | (c[1] << 30) | (c[4] << 22);
-    b.y = (c[2] << 14) | (c[3] << 30);
+// The table is stored kLutCopies times, entry v of copy c at v * kLutCopies
+// + c, and lane l reads copy l % kLutCopies: random byte values then spread
+// over kLutCopies times as many LDS banks.
+#ifndef TERN_B3_LUT_COPIES
+#define TERN_B3_LUT_COPIES 4
+#endif
+constexpr int kLutCopies = TERN_B3_LUT_COPIES;
+__device__ uint32_t b3_entry(int v) {
+  if (v >= 243) return 0u;
+  uint32_t c[5];
+  for (int i = 0; i < 5; ++i) {
+    c[i] = (uint32_t)((v % 3) - 1) & 3u;
+    v /= 3;
   }
-  lutA[v] = a;
-  lutB[v] = b;
+  return (c[0] << 14) | (c[1] << 30) | (c[2] << 12) | (c[3] << 28) | (c[4] << 6) | (c[4] << 22);
 }
 
 // Decode and multiply one LDS stage: groups 0..ngs-1 of the stage, this
 // lane's row at `my`, activations at `xs4` ([MT][XDW] dwords).
 template <int FMT, int G, int MT>
 __device__ __forceinline__ void stage_compute(const uint8_t* my, const u4_t* xs4, int ngs,
-                                              const float* sc, const uint2* lutA,
-                                              const uint2* lutB, float (&acc)[MT]) {
+                                              const float* sc, const uint32_t* lutl, float (&acc)[MT]) {
   using Gm = Geo<FMT, G>;
 #pragma unroll
   for (int j = 0; j < Gm::SG; ++j) {
@@ -194,15 +194,15 @@ __device__ __forceinline__ void stage_compute(const uint8_t* my, const u4_t* xs4
                 if (4 * (5 * bp / 4 + c) < Gm::XGD) xc[m][c] = xs4[(m * Gm::XDW + j * Gm::XGD) / 4 + 5 * bp / 4 + c];
           }
           const int ia = sh + 2 * bp, ib = ia + 1;
-          const uint2 wa = lutA[(dw[ia >> 2] >> ((ia & 3) * 8)) & 0xFFu];
-          uint2 wb = make_uint2(0u, 0u);
-          if (2 * bp + 1 < GB) wb = lutB[(dw[ib >> 2] >> ((ib & 3) * 8)) & 0xFFu];
+          const uint32_t ea = lutl[((dw[ia >> 2] >> ((ia & 3) * 8)) & 0xFFu) * kLutCopies];
+          uint32_t eb = 0u;
+          if (2 * bp + 1 < GB) eb = lutl[((dw[ib >> 2] >> ((ib & 3) * 8)) & 0xFFu) * kLutCopies];
           uint32_t wv[5];
-          wv[0] = wa.x & 0xC000C000u;
-          wv[1] = wa.y;
-          wv[2] = __builtin_amdgcn_perm(wb.x, wa.x, 0x060C000Cu);
-          wv[3] = wb.x & 0xC000C000u;
-          wv[4] = wb.y;
+          wv[0] = ea & 0xC000C000u;
+          wv[1] = (ea << 2) & 0xC000C000u;
+          wv[2] = __builtin_amdgcn_perm(eb, ea, 0x060C000Cu);
+          wv[3] = eb & 0xC000C000u;
+          wv[4] = (eb << 2) & 0xC000C000u;
           // trit positions of the five words: (0,1) (2,3) (4,9) (5,6) (7,8)
           constexpr int first[5] = {0, 2, 4, 5, 7};
 #pragma unroll
@@ -327,8 +327,7 @@ __global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __
   using Gm = Geo<FMT, G>;
   constexpr int WL = wave_lds_bytes<FMT, G, MT>();
   extern __shared__ uint4 stage_all[];  // per wave: [64 rows][PITCH] + activations of a stage
-  __shared__ uint2 lutA[FMT == 1 ? 256 : 1];
-  __shared__ uint2 lutB[FMT == 1 ? 256 : 1];
+  __shared__ uint32_t lut[FMT == 1 ? 256 * kLutCopies : 1];
 
   GemvDesc d;
   if (ndesc > 0) d = descs[blockIdx.x];
@@ -346,7 +345,10 @@ __global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __
   const int nmine = nstages > wave ? (nstages - wave + kWaves - 1) / kWaves : 0;
 
   if (FMT == 1) {
-    for (int v = threadIdx.x; v < 256; v += kWave * kWaves) build_b3_entry(v, lutA, lutB);
+    static_assert(kWave * kWaves == 256, "one byte value per thread");
+    const uint32_t e = b3_entry(threadIdx.x);
+#pragma unroll
+    for (int c = 0; c < kLutCopies; ++c) lut[threadIdx.x * kLutCopies + c] = e;
     __syncthreads();
   }
 
@@ -446,7 +448,7 @@ __global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __
     _Pragma("unroll") for (int j = 0; j < Gm::SG; ++j) sc_[j] = 0.5f * h2f(SP[j]);          \
     wave_sync();                                                                             \
     if ((i_) + kDepth < nmine) TERN_LOAD(P, SP, XP, (i_) + kDepth);                          \
-    stage_compute<FMT, G, MT>(my, xs4, ngs_, sc_, lutA, lutB, acc);                          \
+    stage_compute<FMT, G, MT>(my, xs4, ngs_, sc_, lut + lane % kLutCopies, acc);                          \
   } while (0)
 
   if (nmine > 0) TERN_LOAD(preA, spA, xpA, 0);
