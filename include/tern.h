@@ -179,8 +179,11 @@ tern_status tern_gemm(const tern_matrix *w, const uint16_t *x, int32_t m, void *
  *     ranges of 4-step multiples;
  *   m >= 33: the matrix-core path of tern_gemm over every product's tiles,
  *     long-K products cut into K parts when that shortens the launch.
- *   K parts write FP32 partials to ws that a second launch sums in part
- *   order (results are bitwise reproducible).
+ *   A batch too small to fill the GPU has its decode products cut into
+ *   more K parts.  K parts write FP32 partials to ws; on the decode kernels
+ *   the last workgroup of each row block (arrival counters in ws, cleared
+ *   by this call on stream) adds them in part order, on the matrix-core
+ *   paths a second launch does; results are bitwise reproducible.
  *   w  host array [count] of descriptors
  *   x  host array [count] of device pointers, y likewise
  *   ws device workspace of tern_batch_workspace_bytes(w, count, m) bytes:
@@ -195,7 +198,8 @@ tern_status tern_gemv_batched(const tern_matrix *w, const uint16_t *const *x, vo
 
 /* A prepared grouped product.  tern_plan_create copies the work tables into
  * the caller's device buffer `ws` of tern_batch_workspace_bytes bytes (which
- * also holds the plan's partials and residual index; synchronously) and
+ * also holds the plan's partials, K-part arrival counters -- cleared here,
+ * and left clear by every run -- and residual index; synchronously) and
  * returns a host
  * handle (malloc'ed; free it with tern_plan_destroy).  tern_plan_run
  * launches the whole batch on stream; it may be called any number of times

@@ -40,6 +40,7 @@
 #include <algorithm>
 
 #include "internal.h"
+#include "kparts.h"
 
 #define GLOBAL __attribute__((address_space(1)))
 
@@ -492,20 +493,38 @@ __global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __
 #pragma unroll
   for (int m = 0; m < MT; ++m) red[(wave * MT + m) * kWave + lane] = acc[m];
   __syncthreads();
-  if (wave != 0 || !row_ok) return;
+  const bool writer = wave == 0 && row_ok;
+  if (writer) {
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    float v = red[m * kWave + lane];
+    for (int m = 0; m < MT; ++m) {
+      float v = red[m * kWave + lane];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) v += red[(w * MT + m) * kWave + lane];
-    acc[m] = v;
+      for (int w = 1; w < kWaves; ++w) v += red[(w * MT + m) * kWave + lane];
+      acc[m] = v;
+    }
   }
+  if (d.splits > 1) {
+    if (writer) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        if (m < d.m) part_store(d.partial + ((size_t)split * d.m + m) * d.n + row, acc[m]);
+    }
+    // with a counter, the row block's last part adds the parts in order
+    if (d.ctr == nullptr || !last_part(d.ctr + rb, d.splits) || !writer) return;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m < d.m) {
+        float v = 0.f;
+        for (int sp = 0; sp < d.splits; ++sp) v += part_load(d.partial + ((size_t)sp * d.m + m) * d.n + row);
+        acc[m] = v;
+      }
+    }
+  }
+  if (!writer) return;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     if (m < d.m) {
-      if (d.splits > 1)
-        d.partial[((size_t)split * d.m + m) * d.n + row] = acc[m];
-      else if (d.y_f32)
+      if (d.y_f32)
         reinterpret_cast<float*>(d.y)[(size_t)m * d.n + row] = acc[m];
       else
         reinterpret_cast<_Float16*>(d.y)[(size_t)m * d.n + row] = (_Float16)acc[m];

@@ -38,6 +38,7 @@
 #include <algorithm>
 
 #include "internal.h"
+#include "kparts.h"
 
 #define GLOBAL __attribute__((address_space(1)))
 
@@ -633,8 +634,8 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, const WgRec* __restric
       if (owner && m_of[i] < dm) red[(wave * MP + m_of[i]) * kRowsWave + r] = acc[i];
   }
   if (kw > 1 || d.offset_mode != 0) __syncthreads();
-  if (kp != 0) return;
-  if (kw > 1) {
+  const bool lead = kp == 0;  // the tile's first wavefront finishes its rows
+  if (lead && kw > 1) {
 #pragma unroll
     for (int i = 0; i < NACC; ++i) {
       if (owner && m_of[i] < dm) {
@@ -645,7 +646,7 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, const WgRec* __restric
     }
   }
   // ---- offsets over the item's range
-  if (d.offset_mode != 0) {
+  if (lead && d.offset_mode != 0) {
     const GLOBAL uint16_t* off = gp(d.offset);
 #pragma unroll
     for (int i = 0; i < NACC; ++i) {
@@ -662,16 +663,31 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, const WgRec* __restric
       }
     }
   }
-
   // ---- output
-  if (!owner || !row_ok) return;
+  const bool writer = lead && owner && row_ok;
+  if (d.splits > 1) {
+    if (writer) {
+#pragma unroll
+      for (int i = 0; i < NACC; ++i)
+        if (m_of[i] < dm) part_store(d.partial + ((size_t)split * dm + m_of[i]) * d.n + row, acc[i]);
+    }
+    // with a counter, the row block's last part adds the parts in order
+    if (d.ctr == nullptr || !last_part(d.ctr + rb, d.splits) || !writer) return;
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) {
+      if (m_of[i] < dm) {
+        float v = 0.f;
+        for (int sp = 0; sp < d.splits; ++sp) v += part_load(d.partial + ((size_t)sp * dm + m_of[i]) * d.n + row);
+        acc[i] = v;
+      }
+    }
+  }
+  if (!writer) return;
 #pragma unroll
   for (int i = 0; i < NACC; ++i) {
     const int m = m_of[i];
     if (m < dm) {
-      if (d.splits > 1)
-        d.partial[((size_t)split * dm + m) * d.n + row] = acc[i];
-      else if (d.y_f32)
+      if (d.y_f32)
         reinterpret_cast<float*>(d.y)[(size_t)m * d.n + row] = acc[i];
       else
         reinterpret_cast<_Float16*>(d.y)[(size_t)m * d.n + row] = (_Float16)acc[i];
@@ -686,7 +702,7 @@ size_t mfma_lds_bytes(int max_krp, bool offsets) {
   size_t lds = kZeroBytes + (size_t)MP * max_krp * 2 + ((size_t)kGemvRows * ngr * 2 + 32 + 15) / 16 * 16 +
                (size_t)kWaves * res_wave_bytes<MP>() + res_stage_bytes<G>() + (size_t)kWaves * MP * kRowsWave * 4;
   if (offsets) lds += (size_t)MP * (max_krp / G) * 4;
-  return lds;
+  return lds + 16;  // + the K-part arrival flag (static LDS)
 }
 
 template <int G, int MP>

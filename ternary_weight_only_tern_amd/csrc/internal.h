@@ -48,6 +48,11 @@ struct GemvDesc {
   // Matrix-core tiles: K part [ks0, ks1) in 64-trit steps, and the FP32
   // partial slice it writes (kpart >= 0) instead of y.
   int32_t ks0, ks1, kpart;
+  // Decode kernels with splits > 1: one arrival counter per row block of
+  // this descriptor (zero before the launch; the launch leaves it zero), so
+  // the last workgroup of a row block sums the K parts and writes y; NULL:
+  // only the partials are written (a separate reduce sums them).
+  uint32_t* ctr;
 };
 
 // ---- decode products (gemv.hip)

@@ -564,20 +564,19 @@ static tern_status place_balanced(const std::vector<GemvDesc>& parts, const std:
 }
 
 // ---- grouped decode
-// A batch launch reads one descriptor per work item: the descriptor of the
-// (matrix, block of activation rows) the item belongs to, longest K first.
-// Every descriptor covers its whole K (no split across workgroups).
-// Lane-per-row decode kernel (base-3): products whose K is at least twice
-// the shortest are split along K (parts start on stage boundaries) so their
-// work items end with the others; the parts write FP32 partials
-// [splits][m][n] that one grouped reduce sums in split order.  `partial_base`
-// is where the partials start in the workspace (after the item table).
+// The lane-per-row kernel reads one descriptor per work item (the
+// descriptor of the (matrix, block of activation rows) the item belongs to,
+// longest K first); the matrix-core kernel reads row-range descriptors and
+// one record per workgroup.  Products cut into K parts (batch_splits) write
+// FP32 partials [splits][m][n]; the last workgroup of each row block to
+// finish (arrival counters in the workspace) sums them in part order and
+// writes y, inside the same launch.
 struct DecodeSplits {
-  std::vector<tern::RedDesc> red;
   size_t partial_bytes = 0;
-  int red_blocks = 0;
   size_t recs_off = 0;  // matrix-core decode: where the workgroup records start
-  size_t part_off = 0;  // where the partials start (the reduce table follows them)
+  size_t part_off = 0;  // where the partials start
+  size_t ctr_off = 0;   // where the arrival counters start (after the partials)
+  size_t nctr = 0;      // counters: one per row block of each descriptor with K parts
 };
 
 // K parts of a 2-bit product on the matrix-core decode kernel at mp
@@ -691,8 +690,8 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
   std::vector<int> bns, bgps, bkw;
   batch_splits(w, count, m, *mt, &bns, &bgps, &bkw);
   if (count > 0 && use_mfma(w[0].format)) {
-    // products cut into K parts write FP32 partials that a grouped reduce
-    // sums in part order
+    // products cut into K parts write FP32 partials that the row blocks'
+    // last workgroups sum in part order
     *max_krp = 0;
     size_t coarse_items = 0;
     for (size_t t = 0; t < parts.size(); ++t) {
@@ -712,24 +711,25 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
       if (d.splits <= 1) continue;
       if (!sp) return fail(TERN_E_UNSUPPORTED, "K parts need the workspace layout");
       d.partial = ws ? reinterpret_cast<float*>(ws + part_off + poff) : nullptr;
-      tern::RedDesc rd;
-      rd.partial = d.partial;
-      rd.y = d.y;
-      rd.splits = d.splits;
-      rd.m = d.m;
-      rd.n = d.n;
-      rd.y_f32 = d.y_f32;
-      rd.begin = sp->red_blocks;
-      sp->red.push_back(rd);
-      sp->red_blocks += (int)(((size_t)d.m * d.n + 255) / 256);
       poff += round_up((size_t)d.splits * d.m * d.n * 4, 256);
+    }
+    TERN_TRY(place_balanced(parts, pmat, slots, items, mat, recs));
+    // one arrival counter per row block of every row range with K parts
+    const size_t ctr_off = part_off + poff;
+    size_t nctr = 0;
+    for (GemvDesc& d : *items) {
+      if (d.splits <= 1) continue;
+      d.ctr = ws ? reinterpret_cast<uint32_t*>(ws + ctr_off) + nctr : nullptr;
+      nctr += (size_t)d.row_blocks;
     }
     if (sp) {
       sp->partial_bytes = poff;
       sp->recs_off = recs_off;
       sp->part_off = part_off;
+      sp->ctr_off = ctr_off;
+      sp->nctr = nctr;
     }
-    return place_balanced(parts, pmat, slots, items, mat, recs);
+    return TERN_OK;
   }
   // K parts of the products
   std::vector<int> nsp(parts.size(), 1), gps(parts.size(), 0);
@@ -742,25 +742,22 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
   }
   if (nitems > (size_t)INT32_MAX) return fail(TERN_E_UNSUPPORTED, "batch too large");
   const size_t dbytes = round_up(nitems * sizeof(GemvDesc), 256);
-  size_t poff = 0;
+  size_t ptotal = 0;
+  for (size_t t = 0; t < parts.size(); ++t)
+    if (nsp[t] > 1) ptotal += round_up((size_t)nsp[t] * parts[t].m * parts[t].n * 4, 256);
+  const size_t ctr_off = dbytes + ptotal;
+  size_t poff = 0, nctr = 0;
   for (size_t t = 0; t < parts.size(); ++t) {
     GemvDesc d = parts[t];
     d.tile_begin = (int)items->size();
     if (nsp[t] > 1) {
+      // the row blocks' last K parts sum the partials (arrival counters)
       d.splits = nsp[t];
       d.gps = gps[t];
       d.partial = ws ? reinterpret_cast<float*>(ws + dbytes + poff) : nullptr;
-      tern::RedDesc rd;
-      rd.partial = d.partial;
-      rd.y = d.y;
-      rd.splits = nsp[t];
-      rd.m = d.m;
-      rd.n = d.n;
-      rd.y_f32 = d.y_f32;
-      rd.begin = sp->red_blocks;
-      sp->red.push_back(rd);
-      sp->red_blocks += (int)(((size_t)d.m * d.n + 255) / 256);
+      d.ctr = ws ? reinterpret_cast<uint32_t*>(ws + ctr_off) + nctr : nullptr;
       poff += round_up((size_t)nsp[t] * d.m * d.n * 4, 256);
+      nctr += (size_t)d.row_blocks;
     }
     const size_t cnt = (size_t)d.row_blocks * nsp[t];
     items->insert(items->end(), cnt, d);
@@ -769,6 +766,8 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
   if (sp) {
     sp->partial_bytes = poff;
     sp->part_off = dbytes;
+    sp->ctr_off = ctr_off;
+    sp->nctr = nctr;
   }
   return TERN_OK;
 }
@@ -1106,7 +1105,9 @@ size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m
   // chunk), one record per workgroup (balanced placement may split items up
   // to the launch's resident slots: at most 3 workgroups per CU), then the
   // partials and reduce table (the layouts build_batch makes)
-  size_t nparts = 0, nitems = 0, coarse = 0, partial = 0, nred = 0;
+  // (arrival counters: one per row block of a descriptor with K parts; the
+  // matrix-core placement cuts row blocks down to 16 rows at most)
+  size_t nparts = 0, nitems = 0, coarse = 0, partial = 0, nctr = 0;
   for (int i = 0; i < count; ++i) {
     if (w[i].n <= 0 || w[i].k <= 0) continue;
     const int ns = bns[i];
@@ -1119,15 +1120,14 @@ size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m
       coarse += rb * ns;
       if (ns > 1) {
         partial += round_up((size_t)ns * mc * w[i].n * 4, 256);
-        ++nred;
+        nctr += mf ? (size_t)(w[i].n + tern::kGemvRows / 4 - 1) / (tern::kGemvRows / 4) : rb;
       }
     }
   }
-  if (!mf)
-    return round_up(nitems * sizeof(GemvDesc), 256) + round_up(partial + nred * sizeof(tern::RedDesc), 256) + idx;
+  if (!mf) return round_up(nitems * sizeof(GemvDesc), 256) + round_up(partial + nctr * 4, 256) + idx;
   size_t recs_off, part_off;
   mfma_offsets(nparts, std::max(coarse, (size_t)tern_cu_count() * 3), &recs_off, &part_off);
-  return round_up(part_off + partial + nred * sizeof(tern::RedDesc), 256) + idx;
+  return round_up(part_off + partial + nctr * 4, 256) + idx;
 }
 
 tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, void* const* y,
@@ -1186,10 +1186,9 @@ tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, vo
                        static_cast<char*>(ws)));
   if (items.empty()) return TERN_OK;
   // workspace: [descriptors][workgroup records (matrix-core decode)]
-  // [partials of the K parts][their reduce table], at the offsets the
-  // builder chose
-  const size_t red_off = sp.part_off + sp.partial_bytes;
-  size_t need = std::max(items.size() * sizeof(GemvDesc), red_off + sp.red.size() * sizeof(tern::RedDesc));
+  // [partials of the K parts][arrival counters], at the offsets the builder
+  // chose; the counters are cleared on the stream before the launch
+  size_t need = std::max(items.size() * sizeof(GemvDesc), sp.ctr_off + sp.nctr * 4);
   if (!recs.empty()) need = std::max(need, sp.recs_off + recs.size() * sizeof(tern::WgRec));
   if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "batched decode needs %zu workspace bytes", need);
   TERN_TRY(check_dev(ws, true, "ws"));
@@ -1198,15 +1197,11 @@ tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, vo
   TERN_HIP(hipMemcpyAsync(base, items.data(), items.size() * sizeof(GemvDesc), hipMemcpyHostToDevice, s));
   if (!recs.empty())
     TERN_HIP(hipMemcpyAsync(base + sp.recs_off, recs.data(), recs.size() * sizeof(tern::WgRec), hipMemcpyHostToDevice, s));
-  if (!sp.red.empty())
-    TERN_HIP(hipMemcpyAsync(base + red_off, sp.red.data(), sp.red.size() * sizeof(tern::RedDesc), hipMemcpyHostToDevice, s));
+  if (sp.nctr) TERN_HIP(hipMemsetAsync(base + sp.ctr_off, 0, sp.nctr * 4, s));
   const int nwg = recs.empty() ? (int)items.size() : (int)recs.size();
   TERN_HIP(launch_decode(w[0].format, w[0].group, mt, reinterpret_cast<const GemvDesc*>(base),
                          recs.empty() ? nullptr : reinterpret_cast<const tern::WgRec*>(base + sp.recs_off),
                          (int)items.size(), items[0], nwg, max_krp, offsets, s));
-  if (!sp.red.empty())
-    TERN_HIP(tern::launch_reduce_grouped(reinterpret_cast<const tern::RedDesc*>(base + red_off), (int)sp.red.size(),
-                                         sp.red_blocks, s));
   return TERN_OK;
 }
 
@@ -1295,10 +1290,10 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
   TERN_TRY(build_batch(w, x, y, count, m, y_dtype, &items, &mt, &max_krp, &offsets, &mat, &recs, &sp,
                        static_cast<char*>(ws)));
   // workspace: [descriptors][workgroup records (matrix-core decode)]
-  // [partials of the K parts][their reduce table][residual index of each
-  // matrix], at the offsets the builder chose
-  const size_t red_off = sp.part_off + sp.partial_bytes;
-  size_t tables = std::max(items.size() * sizeof(GemvDesc), red_off + sp.red.size() * sizeof(tern::RedDesc));
+  // [partials of the K parts][arrival counters][residual index of each
+  // matrix], at the offsets the builder chose; the counters are cleared
+  // here and every launch leaves them clear
+  size_t tables = std::max(items.size() * sizeof(GemvDesc), sp.ctr_off + sp.nctr * 4);
   if (!recs.empty()) tables = std::max(tables, sp.recs_off + recs.size() * sizeof(tern::WgRec));
   tables = round_up(tables, 256);
   char* base = static_cast<char*>(ws);
@@ -1316,8 +1311,7 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
       for (size_t t = 0; t < items.size(); ++t)
         if (plan_indexes(&w[mat[t]])) items[t].gidx[0] = reinterpret_cast<const uint32_t*>(base + ioff[mat[t]]);
     TERN_HIP(hipMemcpy(base, items.data(), items.size() * sizeof(GemvDesc), hipMemcpyHostToDevice));
-    if (!sp.red.empty())
-      TERN_HIP(hipMemcpy(base + red_off, sp.red.data(), sp.red.size() * sizeof(tern::RedDesc), hipMemcpyHostToDevice));
+    if (sp.nctr) TERN_HIP(hipMemset(base + sp.ctr_off, 0, sp.nctr * 4));
     if (!recs.empty()) {
       TERN_HIP(hipMemcpy(base + sp.recs_off, recs.data(), recs.size() * sizeof(tern::WgRec), hipMemcpyHostToDevice));
       for (int i = 0; i < count; ++i)
@@ -1344,9 +1338,9 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
   p->gemm = false;
   p->small = false;
   p->aw = p->np = 0;
-  p->red = sp.red.empty() ? nullptr : reinterpret_cast<const tern::RedDesc*>(base + red_off);
-  p->nred = (int)sp.red.size();
-  p->red_blocks = sp.red_blocks;
+  p->red = nullptr;  // K parts are summed inside the decode launch
+  p->nred = 0;
+  p->red_blocks = 0;
   *out = p;
   return TERN_OK;
 }
