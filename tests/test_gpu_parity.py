@@ -518,6 +518,53 @@ def test_dense_residual_lists_in_windows(group, m):
         check_y(y, y_ref, b, f"plan dense residual m={m} i={i}")
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_plan_graph_replays_match_eager(fmt):
+    """A plan captured into a HIP graph: a single product cut into K parts
+    (its row blocks' arrival counters must be left clear by every run) and
+    a seven-product layer, replayed several times with eager launches and
+    synchronizations in between; every replay equals the eager result
+    bitwise and meets the oracle's bound."""
+    import torch
+    say("plan graph replays", fmt)
+    stream = torch.cuda.Stream()
+    cases = []
+    mat = synth.config_matrix(5)
+    x = synth.config_x(5, 1, 0)
+    cases.append(([mat], [x]))
+    mats = [synth.config_matrix(2, proj) for proj in range(7)]
+    xs = [synth.config_x(2, 1, proj) for proj in range(7)]
+    cases.append((mats, xs))
+    for ci, (ms, xh) in enumerate(cases):
+        pms = [upload_pack(mt, fmt) for mt in ms]
+        xd = [to_dev(x_.view(np.uint16)).view(torch.float16) for x_ in xh]
+        ys = [torch.empty((1, mt["n"]), dtype=torch.float16, device="cuda") for mt in ms]
+        plan = L.Plan(pms, xd, ys)
+        with torch.cuda.stream(stream):
+            plan.run(stream.cuda_stream)
+        torch.cuda.synchronize()
+        eager = [y.clone() for y in ys]
+        for mt, x_, y in zip(ms, xh, eager):
+            y_ref, b = oracle_y(mt, x_)
+            check_y(y, y_ref, b, f"eager plan case={ci}")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            plan.run(stream.cuda_stream)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            for y in ys:
+                y.zero_()
+            with torch.cuda.stream(stream):
+                g.replay()
+            torch.cuda.synchronize()
+            for i, (y, e) in enumerate(zip(ys, eager)):
+                assert torch.equal(y, e), f"graph replay {rep} differs (case {ci}, product {i})"
+            plan.run()  # an eager run between replays
+            torch.cuda.synchronize()
+            for y, e in zip(ys, eager):
+                assert torch.equal(y, e), f"eager run after replay {rep} differs (case {ci})"
+
+
 def test_read_probe_runs_and_checks_arguments():
     """The measurement probe reads a buffer without touching the sink (its
     XOR is not the sentinel for a buffer of ones) and rejects sizes that are
