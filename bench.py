@@ -70,11 +70,11 @@ def clone_packed(pm):
     return c
 
 
-def pack_config(cfg: int, fmt: int, proj: int, layer: int = 0):
+def pack_workload(wl: str, fmt: int, proj: int, layer: int = 0):
     import torch
     from ternary_weight_only_tern_amd import lib as L
     from ternary_weight_only_tern_amd import synth
-    mat = synth.config_matrix(cfg, proj, layer)
+    mat = synth.workload_matrix(wl, proj, layer)
     nnz = [int(m.sum()) for m in mat["masks"]]
     pm = L.PackedMatrix(mat["n"], mat["k"], mat["group"], mat["planes"], fmt, mat["offset_mode"], nnz)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -84,10 +84,10 @@ def pack_config(cfg: int, fmt: int, proj: int, layer: int = 0):
     return pm, mat
 
 
-def x_for(cfg, proj, m, layer=0):
+def x_for(wl, proj, m, layer=0):
     import torch
     from ternary_weight_only_tern_amd import synth
-    x = synth.config_x(cfg, m, proj, layer)
+    x = synth.workload_x(wl, m, proj, layer)
     return torch.from_numpy(x.view(np.uint16)).cuda().view(torch.float16), x
 
 
@@ -155,10 +155,10 @@ def bench_layer4b(args, stream):
     fmt = 0 if args.fmt == "2bit" else 1
     base, xs, ys, mats = [], [], [], []
     for proj in range(len(synth.QWEN3_4B_LAYER)):
-        pm, mat = pack_config(2, fmt, proj)
+        pm, mat = pack_workload("qwen3_4b_layer", fmt, proj)
         base.append(pm)
         mats.append(mat)
-        xd, _ = x_for(2, proj, 1)
+        xd, _ = x_for("qwen3_4b_layer", proj, 1)
         xs.append(xd)
         ys.append(torch.empty((1, pm.n), dtype=torch.float16, device="cuda"))
     layer_bytes = sum(pm.nbytes() for pm in base)
@@ -184,9 +184,9 @@ def bench_stack8b(args, stream):
     from ternary_weight_only_tern_amd import synth
     base, xs = [], []
     for proj in range(len(synth.QWEN3_8B_LAYER)):
-        pm, _ = pack_config(3, 1, proj)
+        pm, _ = pack_workload("qwen3_8b_stack", 1, proj)
         base.append(pm)
-        xd, _ = x_for(3, proj, 1)
+        xd, _ = x_for("qwen3_8b_stack", proj, 1)
         xs.append(xd)
     mats, xl, yl = [], [], []
     for layer in range(LAYERS):
@@ -213,8 +213,8 @@ def bench_gemm512(args, stream):
     m = 512
     items = []
     for proj in range(len(synth.QWEN3_8B_LAYER)):
-        pm, _ = pack_config(4, 1, proj)
-        xd, _ = x_for(4, proj, m)
+        pm, _ = pack_workload("qwen3_8b_layer", 1, proj)
+        xd, _ = x_for("qwen3_8b_layer", proj, m)
         y = torch.empty((m, pm.n), dtype=torch.float16, device="cuda")
         items.append((pm, xd, y))
     flops = sum(2.0 * m * pm.n * pm.k for pm, _, _ in items)
@@ -234,8 +234,8 @@ def bench_layer8b(args, stream, m, fmt=1):
     from ternary_weight_only_tern_amd import synth
     pms, xs, ys = [], [], []
     for proj in range(len(synth.QWEN3_8B_LAYER)):
-        pm, _ = pack_config(4, fmt, proj)
-        xd, _ = x_for(4, proj, m)
+        pm, _ = pack_workload("qwen3_8b_layer", fmt, proj)
+        xd, _ = x_for("qwen3_8b_layer", proj, m)
         pms.append(pm)
         xs.append(xd)
         ys.append(torch.empty((m, pm.n), dtype=torch.float16, device="cuda"))
@@ -257,9 +257,9 @@ def bench_stack8b_launches(args, stream):
     from ternary_weight_only_tern_amd import synth
     base, xs = [], []
     for proj in range(len(synth.QWEN3_8B_LAYER)):
-        pm, _ = pack_config(3, 1, proj)
+        pm, _ = pack_workload("qwen3_8b_stack", 1, proj)
         base.append(pm)
-        xd, _ = x_for(3, proj, 1)
+        xd, _ = x_for("qwen3_8b_stack", proj, 1)
         xs.append(xd)
     plans, nbytes = [], 0
     for layer in range(LAYERS):
@@ -288,8 +288,8 @@ def bench_stress(args, stream, fmt, m):
     m rows: one single-product plan per distinct copy, rotated."""
     import torch
     from ternary_weight_only_tern_amd import lib as L
-    pm, _ = pack_config(5, fmt, 0)
-    xd, _ = x_for(5, 0, m)
+    pm, _ = pack_workload("down_proj_stress", fmt, 0)
+    xd, _ = x_for("down_proj_stress", 0, m)
     copies = [pm] + [clone_packed(pm) for _ in range(STRESS_COPIES - 1)]
     y = torch.empty((m, pm.n), dtype=torch.float16, device="cuda")
     plans = [L.Plan([c], [xd], [y]) for c in copies]
@@ -325,7 +325,7 @@ def cpu_baseline(mats, fmt, budget_s=12.0):
     import oracle as O
     from ternary_weight_only_tern_amd import synth
     packed = [O.pack(m["trits"], m["scales"], m["mask_bits"], m["offset"], m["group"], fmt) for m in mats]
-    xs = [synth.config_x(2, 1, p) for p in range(len(mats))]
+    xs = [synth.workload_x("qwen3_4b_layer", 1, p) for p in range(len(mats))]
     nbytes = 0
     done = 0
     t0 = time.perf_counter()
@@ -350,7 +350,7 @@ def cpu_host_dense(mats, budget_s=6.0):
     from threadpoolctl import threadpool_info
     import oracle as O
     from ternary_weight_only_tern_amd import synth
-    xs = [synth.config_x(2, 1, p) for p in range(len(mats))]
+    xs = [synth.workload_x("qwen3_4b_layer", 1, p) for p in range(len(mats))]
     layer_bytes = sum(O.bits(O.pack(mt["trits"], mt["scales"], mt["mask_bits"], mt["offset"], mt["group"], 0))["total_bytes"]
                       for mt in mats)
     nbytes, done = 0, 0
@@ -396,7 +396,7 @@ def main():
                     help="only the 8B-class base-3 stack at M=1 (profiling); prints its result, no JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(the product shards by output rows with no communication; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)

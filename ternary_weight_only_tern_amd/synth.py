@@ -15,8 +15,9 @@ Laws (the pages fix only the group size 128 and FP16 scales/activations):
   x       fp16 ~ N(0, 1), or Student-t(3) clipped to +-65504 for the stress layer
   offset  fp16 ~ N(0, 1) per output row (stress layer only)
 Values are drawn in fp64 and rounded to fp16 (round-to-nearest-even).
-Every matrix has its own stream: PCG64(SeedSequence([seed, cfg, layer, proj]));
-its activations use SeedSequence([seed, cfg, layer, proj, 1]).
+Every matrix has its own stream: PCG64(SeedSequence([seed, stream, layer,
+proj])), where `stream` is the workload's fixed stream id; its activations use
+SeedSequence([seed, stream, layer, proj, 1]).
 """
 from __future__ import annotations
 
@@ -37,27 +38,27 @@ QWEN3_8B_LAYER = [("q", 4096, 4096), ("k", 4096, 1024), ("v", 4096, 1024),
                   ("down", 12288, 4096)]
 NUM_LAYERS = 36
 
-CONFIGS = {
-    1: dict(name="single-gemv K256 N128 G64 2-bit", shapes=[("w", 256, 128)], group=64,
+WORKLOADS = {
+    "single_gemv": dict(stream=1, name="single-gemv K256 N128 G64 2-bit", shapes=[("w", 256, 128)], group=64,
             planes=1, res_frac=0.0, fmt=FMT_2BIT, m=[1], scale_law="uniform",
             x_law="normal", offset_mode=OFF_NONE),
-    2: dict(name="qwen3-4b-class layer M=1", shapes=QWEN3_4B_LAYER, group=128,
+    "qwen3_4b_layer": dict(stream=2, name="qwen3-4b-class layer M=1", shapes=QWEN3_4B_LAYER, group=128,
             planes=2, res_frac=0.10, fmt=FMT_2BIT, m=[1], scale_law="uniform",
             x_law="normal", offset_mode=OFF_NONE),
-    3: dict(name="qwen3-8b-class 36x7 stack M=1 base-3", shapes=QWEN3_8B_LAYER, group=128,
+    "qwen3_8b_stack": dict(stream=3, name="qwen3-8b-class 36x7 stack M=1 base-3", shapes=QWEN3_8B_LAYER, group=128,
             planes=2, res_frac=0.08, fmt=FMT_B3, m=[1], scale_law="uniform",
             x_law="normal", offset_mode=OFF_NONE, layers=NUM_LAYERS),
-    4: dict(name="qwen3-8b-class layer batched base-3", shapes=QWEN3_8B_LAYER, group=128,
+    "qwen3_8b_layer": dict(stream=4, name="qwen3-8b-class layer batched base-3", shapes=QWEN3_8B_LAYER, group=128,
             planes=2, res_frac=0.08, fmt=FMT_B3, m=[1, 4, 16, 64, 512], scale_law="uniform",
             x_law="normal", offset_mode=OFF_NONE),
-    5: dict(name="down-proj stress K12288 N4096", shapes=[("down", 12288, 4096)], group=128,
+    "down_proj_stress": dict(stream=5, name="down-proj stress K12288 N4096", shapes=[("down", 12288, 4096)], group=128,
             planes=3, res_frac=0.20, fmt=FMT_2BIT, m=[1, 8], scale_law="lognormal",
             x_law="student_t3", offset_mode=OFF_ROW, shared_mask=True),
 }
 
 
-def rng_for(seed: int, cfg: int, layer: int, proj: int, extra=None) -> np.random.Generator:
-    key = [seed, cfg, layer, proj] + ([] if extra is None else [extra])
+def rng_for(seed: int, stream: int, layer: int, proj: int, extra=None) -> np.random.Generator:
+    key = [seed, stream, layer, proj] + ([] if extra is None else [extra])
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence(key)))
 
 
@@ -135,19 +136,20 @@ def make_matrix(n: int, k: int, group: int, planes: int, res_frac: float, *,
                 planes=planes)
 
 
-def config_matrix(cfg: int, proj: int = 0, layer: int = 0, seed: int = 0) -> dict:
-    """Matrix `proj` of layer `layer` of a numbered workload configuration."""
-    c = CONFIGS[cfg]
+def workload_matrix(wl: str, proj: int = 0, layer: int = 0, seed: int = 0) -> dict:
+    """Matrix `proj` of layer `layer` of the named workload."""
+    c = WORKLOADS[wl]
     _, k, n = c["shapes"][proj]
     mat = make_matrix(n, k, c["group"], c["planes"], c["res_frac"],
-                      rng=rng_for(seed, cfg, layer, proj), scale_law=c["scale_law"],
+                      rng=rng_for(seed, c["stream"], layer, proj), scale_law=c["scale_law"],
                       offset_mode=c["offset_mode"], shared_mask=c.get("shared_mask", False))
     mat["fmt"] = c["fmt"]
     mat["name"] = c["shapes"][proj][0]
     return mat
 
 
-def config_x(cfg: int, m: int, proj: int = 0, layer: int = 0, seed: int = 0) -> np.ndarray:
-    c = CONFIGS[cfg]
+def workload_x(wl: str, m: int, proj: int = 0, layer: int = 0, seed: int = 0) -> np.ndarray:
+    """Activations [m][k] for matrix `proj` of layer `layer` of the named workload."""
+    c = WORKLOADS[wl]
     _, k, _ = c["shapes"][proj]
-    return draw_x(rng_for(seed, cfg, layer, proj, 1), m, k, c["x_law"])
+    return draw_x(rng_for(seed, c["stream"], layer, proj, 1), m, k, c["x_law"])

@@ -54,12 +54,13 @@ def test_pack_bytes_small(shape, fmt):
     assert_bytes_equal(pm, oracle_pack(mat, fmt))
 
 
-@pytest.mark.parametrize("cfg,proj,fmt", [(1, 0, O.FMT_2BIT), (2, 0, O.FMT_2BIT), (2, 6, O.FMT_B3),
-                                          (3, 4, O.FMT_B3), (3, 6, O.FMT_B3), (5, 0, O.FMT_2BIT),
-                                          (5, 0, O.FMT_B3)])
-def test_pack_bytes_config(cfg, proj, fmt):
-    say("pack config", cfg, proj, fmt)
-    mat = synth.config_matrix(cfg, proj)
+@pytest.mark.parametrize("wl,proj,fmt", [("single_gemv", 0, O.FMT_2BIT), ("qwen3_4b_layer", 0, O.FMT_2BIT),
+                                         ("qwen3_4b_layer", 6, O.FMT_B3), ("qwen3_8b_stack", 4, O.FMT_B3),
+                                         ("qwen3_8b_stack", 6, O.FMT_B3), ("down_proj_stress", 0, O.FMT_2BIT),
+                                         ("down_proj_stress", 0, O.FMT_B3)])
+def test_pack_bytes_workloads(wl, proj, fmt):
+    say("pack workload", wl, proj, fmt)
+    mat = synth.workload_matrix(wl, proj)
     pm = upload_pack(mat, fmt)
     assert_bytes_equal(pm, oracle_pack(mat, fmt))
 
@@ -152,34 +153,34 @@ def test_gemv_m_chunks(m):
     _gemv_case(mat, O.FMT_B3, m, seed=m)
 
 
-def test_gemv_config1():
-    say("gemv config 1")
-    mat = synth.config_matrix(1)
+def test_gemv_single():
+    say("gemv single")
+    mat = synth.workload_matrix("single_gemv")
     _gemv_case(mat, O.FMT_2BIT, 1, seed=0)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_gemv_config2_layer(fmt):
+def test_gemv_qwen3_4b_layer(fmt):
     for proj in range(7):
-        say("gemv config 2", proj, fmt)
-        mat = synth.config_matrix(2, proj)
+        say("gemv qwen3-4b layer", proj, fmt)
+        mat = synth.workload_matrix("qwen3_4b_layer", proj)
         rel = _gemv_case(mat, fmt, 1, seed=proj)
         say("  max |err|/B", rel)
 
 
 @pytest.mark.parametrize("fmt,m,f32", [(O.FMT_2BIT, 1, False), (O.FMT_2BIT, 8, True),
                                        (O.FMT_B3, 1, True), (O.FMT_B3, 8, False)])
-def test_gemv_config5_stress(fmt, m, f32):
-    say("gemv config 5", fmt, m, f32)
-    mat = synth.config_matrix(5)
+def test_gemv_down_proj_stress(fmt, m, f32):
+    say("gemv down-proj stress", fmt, m, f32)
+    mat = synth.workload_matrix("down_proj_stress")
     _gemv_case(mat, fmt, m, x_law="student_t3", f32=f32, seed=5)
 
 
 @pytest.mark.parametrize("m", [1, 4, 16])
-def test_gemv_config4_layer(m):
+def test_gemv_qwen3_8b_layer(m):
     for proj in range(7):
-        say("gemv config 4", proj, m)
-        mat = synth.config_matrix(4, proj)
+        say("gemv qwen3-8b layer", proj, m)
+        mat = synth.workload_matrix("qwen3_8b_layer", proj)
         _gemv_case(mat, O.FMT_B3, m, seed=10 * m + proj)
 
 
@@ -233,8 +234,8 @@ def test_batched_and_plan_match_oracle(fmt):
     say("batched", fmt)
     mats, pms, xs, ys, refs = [], [], [], [], []
     for proj in range(7):
-        mat = synth.config_matrix(2, proj)
-        x = synth.config_x(2, 1, proj)
+        mat = synth.workload_matrix("qwen3_4b_layer", proj)
+        x = synth.workload_x("qwen3_4b_layer", 1, proj)
         mats.append(mat)
         pms.append(upload_pack(mat, fmt))
         xs.append(to_dev(x.view(np.uint16)).view(torch.float16))
@@ -305,16 +306,16 @@ def test_gemm_small(shape, fmt, m):
 
 
 @pytest.mark.parametrize("m", [64, 512])
-def test_gemm_config4_layer(m):
+def test_gemm_qwen3_8b_layer(m):
     for proj in range(7):
-        say("gemm config 4", proj, m)
-        mat = synth.config_matrix(4, proj)
+        say("gemm qwen3-8b layer", proj, m)
+        mat = synth.workload_matrix("qwen3_8b_layer", proj)
         _gemm_case(mat, O.FMT_B3, m, seed=100 * m + proj)
 
 
-def test_gemm_config5():
-    say("gemm config 5")
-    mat = synth.config_matrix(5)
+def test_gemm_down_proj_stress():
+    say("gemm down-proj stress")
+    mat = synth.workload_matrix("down_proj_stress")
     _gemm_case(mat, O.FMT_2BIT, 8, x_law="student_t3", f32=True, seed=55)
 
 
@@ -461,7 +462,7 @@ def test_single_product_batches_fill_the_gpu(fmt, m):
     7-row matrix whose parts are single blocks, against the oracle."""
     import torch
     say("single product fill", fmt, m)
-    cases = [(synth.config_matrix(5), "student_t3"),
+    cases = [(synth.workload_matrix("down_proj_stress"), "student_t3"),
              (small_matrix(7, 2560, 128, 2, 0.3, seed=77 + m, offset_mode=O.OFF_GROUP)[0], "normal")]
     rng = np.random.default_rng(500 + m + 10 * fmt)
     for ci, (mat, law) in enumerate(cases):
@@ -529,11 +530,11 @@ def test_plan_graph_replays_match_eager(fmt):
     say("plan graph replays", fmt)
     stream = torch.cuda.Stream()
     cases = []
-    mat = synth.config_matrix(5)
-    x = synth.config_x(5, 1, 0)
+    mat = synth.workload_matrix("down_proj_stress")
+    x = synth.workload_x("down_proj_stress", 1, 0)
     cases.append(([mat], [x]))
-    mats = [synth.config_matrix(2, proj) for proj in range(7)]
-    xs = [synth.config_x(2, 1, proj) for proj in range(7)]
+    mats = [synth.workload_matrix("qwen3_4b_layer", proj) for proj in range(7)]
+    xs = [synth.workload_x("qwen3_4b_layer", 1, proj) for proj in range(7)]
     cases.append((mats, xs))
     for ci, (ms, xh) in enumerate(cases):
         pms = [upload_pack(mt, fmt) for mt in ms]
@@ -582,17 +583,17 @@ def test_read_probe_runs_and_checks_arguments():
 
 
 @pytest.mark.parametrize("m", [64, 512])
-def test_grouped_layer_config4_matches_oracle(m):
+def test_grouped_qwen3_8b_layer_matches_oracle(m):
     """The 8B-class layer (base-3, seven projections) through one plan at the
     sizes the benchmark times: one grouped matrix-core launch whose long-K
     product may be cut into K parts with FP32 partials and a grouped reduce;
     every output within the bound."""
     import torch
-    say("grouped layer config 4", m)
+    say("grouped qwen3-8b layer", m)
     mats, pms, xs, ys, refs = [], [], [], [], []
     for proj in range(7):
-        mat = synth.config_matrix(4, proj)
-        x = synth.config_x(4, m, proj)
+        mat = synth.workload_matrix("qwen3_8b_layer", proj)
+        x = synth.workload_x("qwen3_8b_layer", m, proj)
         pms.append(upload_pack(mat, O.FMT_B3))
         xs.append(to_dev(x.view(np.uint16)).view(torch.float16))
         ys.append(torch.empty((m, mat["n"]), dtype=torch.float16, device="cuda"))
@@ -604,18 +605,18 @@ def test_grouped_layer_config4_matches_oracle(m):
         check_y(y, y_ref, b, f"grouped layer m={m} proj={proj}")
 
 
-def test_stack_plan_config3_matches_oracle():
+def test_qwen3_8b_stack_plan_matches_oracle():
     """The 8B-class stack at M=1 (base-3, 36 layers x 7 projections) through
     one plan as the benchmark runs it: the layers are byte copies of one
     packed layer, so every layer's outputs must meet the bound against the
     oracle's outputs for that layer."""
     import torch
     import bench
-    say("stack plan config 3")
+    say("qwen3-8b stack plan")
     base, xs, refs = [], [], []
     for proj in range(7):
-        mat = synth.config_matrix(3, proj)
-        x = synth.config_x(3, 1, proj)
+        mat = synth.workload_matrix("qwen3_8b_stack", proj)
+        x = synth.workload_x("qwen3_8b_stack", 1, proj)
         base.append(upload_pack(mat, O.FMT_B3))
         xs.append(to_dev(x.view(np.uint16)).view(torch.float16))
         refs.append(oracle_y(mat, x))

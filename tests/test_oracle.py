@@ -159,11 +159,12 @@ def test_residual_errors():
         O.pack_2bit(np.full((1, 16), 2, dtype=np.int8))
 
 
-def test_full_pack_unpack_roundtrip_all_configs_small():
-    for cfg, fmt in [(1, O.FMT_2BIT), (5, O.FMT_2BIT), (5, O.FMT_B3), (3, O.FMT_B3)]:
-        c = synth.CONFIGS[cfg]
-        rng = np.random.default_rng(cfg)
-        mat = synth.make_matrix(8, 1280 if cfg != 1 else 256, c["group"], c["planes"],
+def test_full_pack_unpack_roundtrip_all_workloads_small():
+    for wl, fmt in [("single_gemv", O.FMT_2BIT), ("down_proj_stress", O.FMT_2BIT), ("down_proj_stress", O.FMT_B3),
+                    ("qwen3_8b_stack", O.FMT_B3)]:
+        c = synth.WORKLOADS[wl]
+        rng = np.random.default_rng(c["stream"])
+        mat = synth.make_matrix(8, 1280 if wl != "single_gemv" else 256, c["group"], c["planes"],
                                 c["res_frac"] or 0.0, rng=rng, scale_law=c["scale_law"],
                                 offset_mode=c["offset_mode"], shared_mask=c.get("shared_mask", False))
         pk = O.pack(mat["trits"], mat["scales"], mat["mask_bits"], mat["offset"], c["group"], fmt)
@@ -308,7 +309,7 @@ def test_bound_dominates_and_zero_case():
 
 
 def test_gemv_packed_equals_gemv():
-    mat = synth.config_matrix(5)
+    mat = synth.workload_matrix("down_proj_stress")
     # shrink the stress layer to a few rows to keep the CPU suite fast
     for key in ("trits",):
         mat[key] = mat[key][:, :6]
@@ -316,7 +317,7 @@ def test_gemv_packed_equals_gemv():
     mat["masks"] = [m[:6] for m in mat["masks"]]
     mat["mask_bits"] = [m[:6] for m in mat["mask_bits"]]
     mat["offset"] = mat["offset"][:6]
-    x = synth.config_x(5, 2)
+    x = synth.workload_x("down_proj_stress", 2)
     for fmt in (O.FMT_2BIT, O.FMT_B3):
         pk = O.pack(mat["trits"], mat["scales"], mat["mask_bits"], mat["offset"], 128, fmt)
         yp = O.gemv_packed(pk, x)
