@@ -92,6 +92,7 @@ def x_for(wl, proj, m, layer=0):
 
 
 EAGER = False  # --eager: launch the steps directly instead of replaying a graph
+LAST_REPLAYS_MS = []  # event times of the last time_graph call's replays (one per rotation)
 
 
 def time_eager(step_fns, steps, warmup, stream):
@@ -143,7 +144,8 @@ def time_graph(step_fns, steps, warmup, stream):
             e.record(stream)
         torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu = sum(s.elapsed_time(e) for s, e in evs) / 1e3
+    LAST_REPLAYS_MS[:] = [s.elapsed_time(e) for s, e in evs]
+    gpu = sum(LAST_REPLAYS_MS) / 1e3
     return wall, gpu, g
 
 
@@ -169,10 +171,12 @@ def bench_layer4b(args, stream):
     fns = [(lambda p=p: p.run(stream.cuda_stream)) for p in plans]
     wall, gpu, _ = time_graph(fns, steps, args.warmup, stream)
     step_s = gpu / steps
+    median_step_s = float(np.median(LAST_REPLAYS_MS)) / 1e3 / len(fns) if LAST_REPLAYS_MS else step_s
     # one kernel launch per step: the average launch duration over the timed
     # region is the step time
     launch_s = step_s
-    return dict(layer_bytes=layer_bytes, steps=steps, wall_s=wall, gpu_s=gpu, step_s=step_s,
+    return dict(layer_bytes=layer_bytes, steps=steps, wall_s=wall, gpu_s=gpu, step_s=step_s, median_step_s=median_step_s,
+                replays=len(LAST_REPLAYS_MS),
                 gbs=layer_bytes / step_s / 1e9, launch_s=launch_s, launch_gbs=layer_bytes / launch_s / 1e9,
                 mats=mats, base=base, xs=xs, weights=sum(pm.n * pm.k for pm in base))
 
@@ -195,13 +199,16 @@ def bench_stack8b(args, stream):
             xl.append(xs[proj])
             yl.append(torch.empty((1, pm.n), dtype=torch.float16, device="cuda"))
     stack_bytes = sum(pm.nbytes() for pm in mats)
+    bits = [L.tern_bits(pm) for pm in base]
+    wts = [pm.n * pm.k for pm in base]
+    bpw = {key: round(sum(b[key] * w for b, w in zip(bits, wts)) / sum(wts), 4) for key in ("info", "plane", "storage")}
     plan = L.Plan(mats, xl, yl)
     torch.cuda.synchronize()
     steps = max(2, args.steps // 20)
     wall, gpu, _ = time_graph([lambda: plan.run(stream.cuda_stream)], steps, max(2, args.warmup // 10), stream)
     step_s = gpu / steps
     return dict(stack_bytes=stack_bytes, steps=steps, step_s=step_s, gbs=stack_bytes / step_s / 1e9,
-                tok_s=1.0 / step_s)
+                tok_s=1.0 / step_s, bpw=bpw)
 
 
 def bench_gemm512(args, stream):
@@ -379,6 +386,31 @@ def cpu_host_dense(mats, budget_s=6.0):
                 sample=f"{done} pass(es) over the 7 projections of one Qwen3-4B-class layer (2-bit bytes), {dt:.1f} s")
 
 
+def cpu_stack_extrapolated(runs=3):
+    """The strict oracle (unpack-and-dot, one thread) on one layer of the
+    8B-class base-3 stack, median of `runs` timings, times 36 layers (the
+    whole stack would take minutes, so this figure is extrapolated)."""
+    from threadpoolctl import threadpool_limits
+    import oracle as O
+    from ternary_weight_only_tern_amd import synth
+    mats = [synth.workload_matrix("qwen3_8b_stack", p) for p in range(len(synth.QWEN3_8B_LAYER))]
+    packed = [O.pack(m["trits"], m["scales"], m["mask_bits"], m["offset"], m["group"], 1) for m in mats]
+    xs = [synth.workload_x("qwen3_8b_stack", 1, p) for p in range(len(mats))]
+    layer_bytes = sum(O.bits(pk)["total_bytes"] for pk in packed)
+    times = []
+    with threadpool_limits(limits=1):
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            for pk, x in zip(packed, xs):
+                O.gemv_packed(pk, x)
+            times.append(time.perf_counter() - t0)
+    layer_s = float(np.median(times))
+    tok_s = LAYERS * layer_s
+    return dict(us_per_token=tok_s * 1e6, tokens_per_s_equiv=1.0 / tok_s, gbs=LAYERS * layer_bytes / tok_s / 1e9,
+                cores=1, kind="oracle", layer_runs_s=[round(t, 3) for t in times],
+                note="one layer timed (median of runs), times 36 layers: extrapolated")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -434,13 +466,15 @@ def main():
     wts = [pm.n * pm.k for pm in r["base"]]
     extra = {"headline_bpw": {key: round(sum(b[key] * w for b, w in zip(bits, wts)) / sum(wts), 4)
                               for key in ("info", "plane", "storage")},
-             "headline_tokens_per_s_equiv": 1.0 / (LAYERS * r["step_s"])}
+             "headline_tokens_per_s_equiv": 1.0 / (LAYERS * r["step_s"]),
+             "headline_median_step_us": round(r["median_step_s"] * 1e6, 3),
+             "headline_timed_replays": r["replays"]}
     if not args.skip_extra:
         log("bench: 8B-class stack")
         s8 = bench_stack8b(args, stream)
         extra["qwen3_8b_stack_m1_b3"] = dict(bytes=s8["stack_bytes"], us_per_token=s8["step_s"] * 1e6,
                                              gbs=s8["gbs"], hbm_frac=s8["gbs"] / HBM_PEAK_GBS,
-                                             tokens_per_s_equiv=s8["tok_s"], steps=s8["steps"])
+                                             tokens_per_s_equiv=s8["tok_s"], steps=s8["steps"], bpw=s8["bpw"])
         log(f"bench: stack {s8['gbs']:.1f} GB/s, {s8['tok_s']:.0f} tok/s-eq")
         s8l = bench_stack8b_launches(args, stream)
         extra["qwen3_8b_stack_m1_b3_252_launches"] = dict(us_per_token=s8l["step_s"] * 1e6, gbs=s8l["gbs"],
@@ -482,6 +516,10 @@ def main():
         host = cpu_host_dense(r["mats"])
         extra["cpu_host_dense"] = host
         log(f"bench: cpu host dense {host['value']:.4f} GB/s on {host['cores']} threads")
+        if not args.skip_extra:
+            cs = cpu_stack_extrapolated()
+            extra["cpu_oracle_qwen3_8b_stack_extrapolated"] = cs
+            log(f"bench: cpu oracle 8B-class stack {cs['tokens_per_s_equiv']:.4f} tok/s-eq (extrapolated)")
 
     out = {
         "metric": "ternary GEMV packed-weight GB/s (% HBM peak) at M=1; TFLOP/s at M=512",
