@@ -220,6 +220,29 @@ void tern_plan_destroy(tern_plan *plan);
  * Any output pointer may be NULL.  Host-only. */
 tern_status tern_bits(const tern_matrix *w, double *info, double *plane, double *storage);
 
+/* Quantizer front-end (the step before tern_pack): FP16 weights w [n][k]
+ * -> trits [2][n][k] (int8, plane 0 then plane 1), scales [2][n][k/group]
+ * (FP16) and per-group offsets [n][k/group] (FP16), so that
+ *   W ~ offset + scales[0] * trits[0] + m * scales[1] * trits[1]
+ * group by group (m: the group's bit in `mask`), ready for tern_pack with
+ * planes = 2 and TERN_OFF_GROUP.  E2M-ATQ, order-2 asymmetric residual
+ * ternarization ("Post-Training Ternarization of Qwen3-4B", §4.3): an offset
+ * and two ternary planes with scales per group, then `iters` refinement
+ * iterations (the pages use 15) with the ternary supports fixed; the second
+ * plane only on the groups set in `mask` (salience-selected, §4.4; u32
+ * bitmap [n][ceil(k/group/32)], bit g % 32 of word g / 32; NULL: none, and
+ * trits[1] and scales[1] are zero).  Initial supports: |w - mean| > 0.7
+ * mean|w - mean| (the ternary-weight-network threshold; the pages give no
+ * rule); an iteration is the least-squares fit of (offset, s0, s1) followed
+ * by the error-minimizing sign of every non-zero trit; a last fit gives the
+ * stored values.  All arithmetic is FP32 in one fixed order, so results are
+ * reproducible bit for bit.  group 64 or 128 and k % group == 0
+ * (TERN_E_UNSUPPORTED otherwise); 0 <= iters <= 1000.  All pointers are
+ * device memory owned by the caller (w, scales, offset 2-byte aligned, mask
+ * 4-byte).  Async on stream. */
+tern_status tern_quantize(const uint16_t *w, int32_t n, int32_t k, int32_t group, const uint32_t *mask,
+                          int32_t iters, int8_t *trits, uint16_t *scales, uint16_t *offset, void *stream);
+
 /* Measurement aid, not part of the product: a plain streaming read of
  * `bytes` bytes (a multiple of 16) of device memory at `buf` (16-byte
  * aligned), the attainable-bandwidth reference for the products above.

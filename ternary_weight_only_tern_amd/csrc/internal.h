@@ -136,6 +136,13 @@ struct RedDesc {
 };
 hipError_t launch_reduce_grouped(const RedDesc* rd, int count, int blocks, hipStream_t stream);
 
+// ---- quantizer front-end (quant.hip)
+// w fp16 [n][k] -> trits int8 [2][n][k], scales fp16 [2][n][k/group],
+// offsets fp16 [n][k/group]; mask: u32 bitmap [n][mwords] of the groups that
+// get the second plane (NULL: none); group 64 or 128.
+hipError_t launch_quantize(const uint16_t* w, int n, int k, int group, const uint32_t* mask, int mwords, int iters,
+                           int8_t* trits, uint16_t* scales, uint16_t* offset, hipStream_t stream);
+
 // ---- packing (pack.hip)
 hipError_t launch_pack_plane0(int format, const int8_t* trits, int n, int k, int group,
                               int stride, uint8_t* plane0, uint32_t* flag, hipStream_t stream);

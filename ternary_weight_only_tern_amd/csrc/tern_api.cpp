@@ -1373,6 +1373,24 @@ tern_status tern_plan_run(const tern_plan* plan, void* stream) {
 
 void tern_plan_destroy(tern_plan* plan) { std::free(plan); }
 
+tern_status tern_quantize(const uint16_t* w, int32_t n, int32_t k, int32_t group, const uint32_t* mask,
+                          int32_t iters, int8_t* trits, uint16_t* scales, uint16_t* offset, void* stream) {
+  if (n < 0 || k < 0) return fail(TERN_E_INVAL, "n=%d, k=%d must not be negative", n, k);
+  if (group != 64 && group != 128) return fail(TERN_E_UNSUPPORTED, "quantize takes group 64 or 128 (got %d)", group);
+  if (k % group) return fail(TERN_E_UNSUPPORTED, "k=%d must be a multiple of group %d", k, group);
+  if (iters < 0 || iters > 1000) return fail(TERN_E_INVAL, "iters=%d must be in [0, 1000]", iters);
+  if ((long long)n * k > (long long)INT32_MAX * 16) return fail(TERN_E_UNSUPPORTED, "matrix too large");
+  if (n == 0 || k == 0) return TERN_OK;
+  TERN_TRY(check_dev(w, true, "w", 2));
+  TERN_TRY(check_dev(trits, true, "trits", 1));
+  TERN_TRY(check_dev(scales, true, "scales", 2));
+  TERN_TRY(check_dev(offset, true, "offset", 2));
+  if (mask) TERN_TRY(check_dev(mask, true, "mask", 4));
+  TERN_HIP(tern::launch_quantize(w, n, k, group, mask, mask_words(k, group), iters, trits, scales, offset,
+                                 (hipStream_t)stream));
+  return TERN_OK;
+}
+
 tern_status tern_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   if (bytes % 16) return fail(TERN_E_INVAL, "bytes=%zu is not a multiple of 16", bytes);
   if (bytes == 0) return TERN_OK;

@@ -36,7 +36,7 @@ TERN_F32 = 1
 SYMBOLS = ["tern_row_stride", "tern_check", "tern_packed_sizes", "tern_workspace_bytes",
            "tern_pack", "tern_unpack", "tern_gemv", "tern_gemm", "tern_batch_workspace_bytes",
            "tern_gemv_batched", "tern_plan_create", "tern_plan_run", "tern_plan_destroy",
-           "tern_bits", "tern_read_probe", "tern_status_str", "tern_last_error"]
+           "tern_bits", "tern_quantize", "tern_read_probe", "tern_status_str", "tern_last_error"]
 
 
 class tern_matrix(ctypes.Structure):
@@ -80,6 +80,8 @@ def load() -> ctypes.CDLL:
         "tern_plan_run": (c_int32, [c_void_p, c_void_p]),
         "tern_plan_destroy": (None, [c_void_p]),
         "tern_bits": (c_int32, [P, POINTER(c_double), POINTER(c_double), POINTER(c_double)]),
+        "tern_quantize": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p,
+                                    c_void_p, c_void_p]),
         "tern_read_probe": (c_int32, [c_void_p, c_size_t, c_void_p, c_void_p]),
         "tern_status_str": (ctypes.c_char_p, [c_int32]),
         "tern_last_error": (ctypes.c_char_p, []),
@@ -266,6 +268,22 @@ class Plan:
         if getattr(self, "handle", None) and _lib is not None:
             _lib.tern_plan_destroy(self.handle)
             self.handle = None
+
+
+def tern_quantize(w, mask_bits=None, group=128, iters=15, stream=None):
+    """Quantize fp16 weights w [n][k] (device tensor; torch.float16 or its
+    uint16 bits) into (trits int8 [2][n][k], scales fp16 [2][n][k/group],
+    offsets fp16 [n][k/group]); mask_bits: int32/uint32 device bitmap
+    [n][ceil(k/group/32)] of the groups that get the second plane, or None."""
+    import torch
+    n, k = w.shape
+    ng = k // group if group else 0
+    trits = torch.empty((2, n, k), dtype=torch.int8, device=w.device)
+    scales = torch.empty((2, n, ng), dtype=torch.float16, device=w.device)
+    offset = torch.empty((n, ng), dtype=torch.float16, device=w.device)
+    check(load().tern_quantize(_ptr(w), n, k, group, _ptr(mask_bits) if mask_bits is not None else None, iters,
+                               _ptr(trits), _ptr(scales), _ptr(offset), _stream(stream)))
+    return trits, scales, offset
 
 
 def tern_read_probe(buf, sink, stream=None) -> None:

@@ -117,3 +117,16 @@ def test_pack_rejects_bad_arguments():
 def test_status_strings():
     for s in range(-6, 1):
         assert L.status_str(s).startswith("TERN_")
+
+
+def test_quantize_rejects_bad_arguments_before_any_launch():
+    lib = L.load()
+    nul = ctypes.c_void_p(0)
+    q = lambda n, k, g, it: lib.tern_quantize(nul, n, k, g, nul, it, nul, nul, nul, nul)
+    assert q(4, 256, 96, 15) == L.TERN_E_UNSUPPORTED
+    assert q(4, 200, 128, 15) == L.TERN_E_UNSUPPORTED
+    assert q(-1, 256, 128, 15) == L.TERN_E_INVAL
+    assert q(4, 256, 128, -1) == L.TERN_E_INVAL
+    assert q(4, 256, 128, 1001) == L.TERN_E_INVAL
+    assert q(0, 256, 128, 15) == L.TERN_OK  # empty: nothing to do, no pointer touched
+    assert q(4, 256, 128, 15) == L.TERN_E_INVAL  # NULL weights

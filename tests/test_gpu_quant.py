@@ -1,0 +1,97 @@
+"""GPU parity of the quantizer front-end (tern_quantize) against the oracle in
+oracle/quant_oracle.py: trits, scales and offsets are compared bit for bit
+(both sides take every decision in FP32 in the same order), then the output
+is packed and multiplied through the library and checked against the
+oracle's product of the oracle's own quantization."""
+import numpy as np
+import pytest
+
+import oracle as O
+import oracle.quant_oracle as Q
+from ternary_weight_only_tern_amd import lib as L
+from ternary_weight_only_tern_amd import synth
+from gpu_util import check_y, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _weights(rng, n, k, group, law):
+    w = synth.draw_x(rng, n, k, law)  # fp16 [n][k]
+    if n >= 3:
+        w[0, :group] = np.float16(0.375)        # a constant group
+        w[1, group:2 * group] = np.float16(0.0)  # an all-zero group (k >= 2 groups)
+        t = rng.integers(-1, 2, size=group)
+        w[2, :group] = (np.float16(0.25) + np.float16(1.5) * t).astype(np.float16)  # representable
+    return w
+
+
+def _run(w, mask_bits, group, iters=15):
+    import torch
+    wd = to_dev(w.view(np.uint16))
+    md = to_dev(mask_bits.view(np.int32)) if mask_bits is not None else None
+    trits, scales, offset = L.tern_quantize(wd, md, group, iters)
+    torch.cuda.synchronize()
+    return trits.cpu().numpy(), scales.cpu().numpy(), offset.cpu().numpy()
+
+
+CASES = [  # n, k, group, mask fraction (None: no mask), weight law, iterations
+    (37, 512, 128, 0.3, "normal", 15),
+    (64, 1024, 128, None, "normal", 15),
+    (5, 256, 64, 1.0, "student_t3", 15),
+    (130, 640, 64, 0.1, "normal", 15),
+    (9, 384, 128, 0.5, "student_t3", 0),
+    (9, 384, 128, 0.5, "normal", 3),
+]
+
+
+@pytest.mark.parametrize("n,k,group,frac,law,iters", CASES)
+def test_quantize_is_bit_exact_with_oracle(n, k, group, frac, law, iters):
+    say("quantize", n, k, group, frac, law, iters)
+    rng = np.random.default_rng(n * 31 + k + group)
+    w = _weights(rng, n, k, group, law)
+    mb = synth.draw_mask(rng, n, k // group, frac)[1] if frac is not None else None
+    trits, scales, offset = _run(w, mb, group, iters)
+    rt, rs, ro = Q.quantize(w, mb, group, iters)
+    assert np.array_equal(trits, rt), f"trits differ at {np.argwhere(trits != rt)[:5].tolist()}"
+    assert np.array_equal(scales.view(np.uint16), rs.view(np.uint16)), "scales differ"
+    assert np.array_equal(offset.view(np.uint16), ro.view(np.uint16)), "offsets differ"
+
+
+def test_quantize_empty_and_degenerate_shapes():
+    import torch
+    say("quantize empty")
+    w = torch.zeros((0, 256), dtype=torch.float16, device="cuda")
+    trits, scales, offset = L.tern_quantize(w, None, 128)
+    assert trits.shape == (2, 0, 256) and scales.shape == (2, 0, 2) and offset.shape == (0, 2)
+    # one row, one group, every weight equal: no trits, offset = the weight
+    w1 = np.full((1, 128), np.float16(-2.5))
+    t, s, o = _run(w1, None, 128)
+    assert not t.any() and not s.any() and o[0, 0] == np.float16(-2.5)
+
+
+@pytest.mark.parametrize("fmt", [O.FMT_2BIT, O.FMT_B3])
+def test_quantized_layer_packs_and_multiplies(fmt):
+    """Quantize a 4B-class projection's shape (q, 2560 -> 4096) with a 10 %
+    salience mask, pack the result (two planes, per-group offsets) and run the
+    product: within the bound of the oracle's product of the oracle's own
+    quantization (which the kernel's output equals bit for bit)."""
+    import torch
+    say("quantize -> pack -> gemv", fmt)
+    rng = np.random.default_rng(11 + fmt)
+    n, k, group = 4096, 2560, 128
+    w = synth.draw_x(rng, n, k, "normal")
+    sel, mb = synth.draw_mask(rng, n, k // group, 0.10)
+    wd = to_dev(w.view(np.uint16))
+    trits, scales, offset = L.tern_quantize(wd, to_dev(mb.view(np.int32)), group)
+    nnz = [int(sel.sum())]
+    pm = L.PackedMatrix(n, k, group, 2, fmt, O.OFF_GROUP, nnz)
+    L.tern_pack(pm, trits, scales, to_dev(mb[None].view(np.int32)), offset)
+    x = synth.draw_x(rng, 1, k, "normal")
+    xd = to_dev(x.view(np.uint16)).view(torch.float16)
+    y = L.tern_gemv(pm, xd, L.TERN_F32)
+    torch.cuda.synchronize()
+    rt, rs, ro = Q.quantize(w, mb, group)
+    assert np.array_equal(trits.cpu().numpy(), rt)
+    y_ref = O.gemv(rt, [rs[0], rs[1]], [sel], ro, O.OFF_GROUP, x, group)
+    b = O.bound(rt, [rs[0], rs[1]], [sel], ro, O.OFF_GROUP, x, group)
+    check_y(y, y_ref, b, "quantized layer")
