@@ -310,6 +310,63 @@ def bench_stress(args, stream, fmt, m):
                 hbm_frac=round(nbytes / step_s / 1e9 / HBM_PEAK_GBS, 4), bytes=nbytes, steps=steps)
 
 
+def bench_quantize(args, stream):
+    """The quantizer front-end on a 4B-class layer: FP16 weights of the seven
+    projections (unit normal; the method is scale-equivariant) with a 10 %
+    salience mask -> trit planes, scales and offsets, one launch per
+    projection, 15 refinement iterations."""
+    import torch
+    from ternary_weight_only_tern_amd import lib as L
+    from ternary_weight_only_tern_amd import synth
+    rng = np.random.default_rng(2024)
+    items, nw = [], 0
+    for _, k, n in synth.QWEN3_4B_LAYER:
+        w = synth.draw_x(rng, n, k, "normal")
+        _, mb = synth.draw_mask(rng, n, k // 128, 0.10)
+        wd = torch.from_numpy(w.view(np.uint16)).cuda()
+        md = torch.from_numpy(mb.view(np.int32)).cuda()
+        t = torch.empty((2, n, k), dtype=torch.int8, device="cuda")
+        sc = torch.empty((2, n, k // 128), dtype=torch.float16, device="cuda")
+        of = torch.empty((n, k // 128), dtype=torch.float16, device="cuda")
+        items.append((wd, md, t, sc, of, n, k))
+        nw += n * k
+    lib = L.load()
+
+    def step():
+        for wd, md, t, sc, of, n, k in items:
+            L.check(lib.tern_quantize(wd.data_ptr(), n, k, 128, md.data_ptr(), 15, t.data_ptr(), sc.data_ptr(),
+                                      of.data_ptr(), stream.cuda_stream))
+    steps = max(4, args.steps // 100)
+    wall, gpu, _ = time_graph([step], steps, 2, stream)
+    step_s = gpu / steps
+    io_bytes = nw * 2 + nw * 2 + sum(n * (k // 128) * 2 * 3 + n * ((k // 128 + 31) // 32) * 4 for _, _, _, _, _, n, k in items)
+    return dict(ms_per_layer=step_s * 1e3, weights_per_s=nw / step_s, gbs=io_bytes / step_s / 1e9, steps=steps,
+                weights=nw, io_bytes=io_bytes)
+
+
+def cpu_quantize_baseline(budget_s=6.0):
+    """The quantizer oracle (vectorized numpy FP32, one thread) on the 4B-class
+    k projection's shape (1024 x 2560), repeated for about budget_s seconds."""
+    from threadpoolctl import threadpool_limits
+    import oracle.quant_oracle as Q
+    from ternary_weight_only_tern_amd import synth
+    rng = np.random.default_rng(2024)
+    _, k, n = synth.QWEN3_4B_LAYER[1]
+    w = synth.draw_x(rng, n, k, "normal")
+    _, mb = synth.draw_mask(rng, n, k // 128, 0.10)
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            Q.quantize(w, mb, 128)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return dict(weights_per_s=done * n * k / dt, cores=1, kind="oracle",
+                sample=f"{done} quantization(s) of a {n} x {k} projection, 1 thread, {dt:.1f} s")
+
+
 def bench_read_probe(stream, nbytes, copies):
     """Attainable read bandwidth: the library's plain streaming-read probe
     over `copies` distinct buffers of nbytes each, one launch per buffer."""
@@ -500,6 +557,12 @@ def main():
                 stress[f"{fname}_m{m}"] = q
                 log(f"bench: stress down-projection {fname} M={m}: {q['us']:.2f} us, {q['gbs']:.1f} GB/s")
         extra["stress_down_proj_k12288"] = stress
+        qz = bench_quantize(args, stream)
+        extra["quantize_qwen3_4b_layer"] = dict(ms_per_layer=round(qz["ms_per_layer"], 4),
+                                                weights_per_s=qz["weights_per_s"], gbs=round(qz["gbs"], 1),
+                                                hbm_frac=round(qz["gbs"] / HBM_PEAK_GBS, 4), steps=qz["steps"],
+                                                kernel="quantize_kernel<128>: one wavefront per (row, group)")
+        log(f"bench: quantize 4B-class layer {qz['ms_per_layer']:.3f} ms, {qz['weights_per_s']/1e9:.2f} G weights/s")
         # attainable read bandwidth on this machine: a plain reduction over 1 GiB
         # buffers, and over 36 buffers of the headline layer's size
         big = bench_read_probe(stream, 1 << 30, 2)
@@ -517,6 +580,9 @@ def main():
         extra["cpu_host_dense"] = host
         log(f"bench: cpu host dense {host['value']:.4f} GB/s on {host['cores']} threads")
         if not args.skip_extra:
+            cq = cpu_quantize_baseline()
+            extra["cpu_oracle_quantize"] = cq
+            log(f"bench: cpu quantize {cq['weights_per_s']/1e6:.2f} M weights/s")
             cs = cpu_stack_extrapolated()
             extra["cpu_oracle_qwen3_8b_stack_extrapolated"] = cs
             log(f"bench: cpu oracle 8B-class stack {cs['tokens_per_s_equiv']:.4f} tok/s-eq (extrapolated)")

@@ -20,9 +20,12 @@
 //
 // Decisions depend on floating-point sums, so every quantity is computed in
 // FP32 with one fixed order: a group sum pairs element i with i + G/2, then
-// halves again (lane l holds elements l and l + 64; the butterfly of xor
-// shuffles gives every lane the same, bitwise, total), and no multiply-add
-// is contracted.  Results are therefore reproducible bit for bit.
+// halves again, and no multiply-add is contracted.  Results are therefore
+// reproducible bit for bit.  Sixteen lanes share a group: lane l holds
+// elements l + 16 j, so the first halvings (i + 64, i + 32, i + 16) are adds
+// inside the lane and the last four are xor shuffles 8, 4, 2, 1, which give
+// the group's sixteen lanes the same total bit for bit; a wavefront
+// quantizes four groups.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -35,13 +38,21 @@ namespace tern {
 namespace {
 
 constexpr int kWave = 64;
+constexpr int kLanes = 16;  // lanes per group
 
+// Sum over the group's E * 16 elements in the fixed halving order.
 template <int E>
 __device__ __forceinline__ float group_sum(const float (&v)[E]) {
-  float x = v[0];
-  if (E == 2) x = v[0] + v[1];
+  float t[E];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = x + __shfl_xor(x, o, kWave);
+  for (int j = 0; j < E; ++j) t[j] = v[j];
+#pragma unroll
+  for (int h = E / 2; h >= 1; h /= 2)
+#pragma unroll
+    for (int j = 0; j < h; ++j) t[j] = t[j] + t[j + h];
+  float x = t[0];
+#pragma unroll
+  for (int o = kLanes / 2; o > 0; o >>= 1) x = x + __shfl_xor(x, o, kWave);
   return x;
 }
 
@@ -92,22 +103,25 @@ __device__ __forceinline__ Fit fit(const float (&w)[E], const int8_t (&t0)[E], c
   return f;
 }
 
-// One wavefront per (row, group): groups grp = row * ng + g.
+// Sixteen lanes per (row, group): groups grp = row * ng + g, four per
+// wavefront.
 template <int G>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ wt, int n, int k,
                                                        const uint32_t* __restrict__ mask, int mwords, int iters,
                                                        int8_t* __restrict__ trits, uint16_t* __restrict__ scales,
                                                        uint16_t* __restrict__ offset) {
-  constexpr int E = G / kWave;
+  constexpr int E = G / kLanes;
   const int ng = k / G;
-  const long grp = (long)blockIdx.x * 4 + threadIdx.x / kWave;
-  if (grp >= (long)n * ng) return;  // whole wavefront
-  const int lane = threadIdx.x % kWave;
+  const long total = (long)n * ng;
+  const long gq = (long)blockIdx.x * (256 / kLanes) + threadIdx.x / kLanes;
+  const bool live = gq < total;  // the last wavefront may hold fewer groups
+  const long grp = live ? gq : total - 1;
+  const int lane = threadIdx.x % kLanes;
   const int row = (int)(grp / ng), g = (int)(grp % ng);
   const size_t base = (size_t)row * k + (size_t)g * G;
   float w[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) w[e] = (float)__builtin_bit_cast(_Float16, wt[base + lane + kWave * e]);
+  for (int e = 0; e < E; ++e) w[e] = (float)__builtin_bit_cast(_Float16, wt[base + lane + kLanes * e]);
   const bool masked = mask != nullptr && ((mask[(size_t)row * mwords + g / 32] >> (g % 32)) & 1u);
   const float inv = 1.0f / (float)G, gf = (float)G;
 
@@ -164,10 +178,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   }
   const Fit f = fit<E>(w, t0, t1, masked, sw, n0, n1, gf);
 
+  if (!live) return;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    trits[base + lane + kWave * e] = t0[e];
-    trits[(size_t)n * k + base + lane + kWave * e] = t1[e];
+    trits[base + lane + kLanes * e] = t0[e];
+    trits[(size_t)n * k + base + lane + kLanes * e] = t1[e];
   }
   if (lane == 0) {
     const size_t sg = (size_t)row * ng + g;
@@ -183,7 +198,7 @@ hipError_t launch_quantize(const uint16_t* w, int n, int k, int group, const uin
                            int8_t* trits, uint16_t* scales, uint16_t* offset, hipStream_t s) {
   const long groups = (long)n * (k / group);
   if (groups <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((groups + 3) / 4));
+  const dim3 grid((unsigned)((groups + 15) / 16));
   if (group == 128)
     hipLaunchKernelGGL((quantize_kernel<128>), grid, dim3(256), 0, s, w, n, k, mask, mwords, iters, trits, scales,
                        offset);
