@@ -483,6 +483,8 @@ def main():
                     help="only the M=512 matrix-core layer (profiling); prints its result, no JSON line")
     ap.add_argument("--stack8b-only", action="store_true",
                     help="only the 8B-class base-3 stack at M=1 (profiling); prints its result, no JSON line")
+    ap.add_argument("--quantize-only", action="store_true",
+                    help="only the quantizer on a 4B-class layer (profiling); prints its result, no JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -509,6 +511,10 @@ def main():
     if args.gemm512_only:
         g = bench_gemm512(args, stream)
         log(f"bench: M=512 layer {g['step_s']*1e6:.1f} us, {g['tflops']:.1f} TFLOP/s")
+        return
+    if args.quantize_only:
+        qz = bench_quantize(args, stream)
+        log(f"bench: quantize 4B-class layer {qz['ms_per_layer']:.3f} ms, {qz['weights_per_s']/1e9:.2f} G weights/s")
         return
     if args.stack8b_only:
         s8 = bench_stack8b(args, stream)
