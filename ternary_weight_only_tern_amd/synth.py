@@ -153,3 +153,14 @@ def workload_x(wl: str, m: int, proj: int = 0, layer: int = 0, seed: int = 0) ->
     c = WORKLOADS[wl]
     _, k, _ = c["shapes"][proj]
     return draw_x(rng_for(seed, c["stream"], layer, proj, 1), m, k, c["x_law"])
+
+
+def draw_rotation(rng: np.random.Generator, nb: int, block: int) -> np.ndarray:
+    """nb random orthogonal block x block matrices (QR of a Gaussian draw, the
+    usual Haar construction), rounded to fp16: [nb][block][block]."""
+    out = np.empty((nb, block, block), dtype=np.float16)
+    for b in range(nb):
+        q, r = np.linalg.qr(rng.standard_normal((block, block)))
+        q = q * np.sign(np.diag(r))[None, :]
+        out[b] = q.astype(np.float16)
+    return out
