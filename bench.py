@@ -344,6 +344,33 @@ def bench_quantize(args, stream):
                 weights=nw, io_bytes=io_bytes)
 
 
+def bench_rotate(args, stream):
+    """The activation rotation at M=1 for the three inputs of a 4B-class
+    layer (hidden 2560 for q/k/v and gate/up, attention output 4096 for o,
+    MLP intermediate 9728 for down), 128 x 128 blocks, three launches per
+    step."""
+    import torch
+    from ternary_weight_only_tern_amd import lib as L
+    from ternary_weight_only_tern_amd import synth
+    rng = np.random.default_rng(7)
+    items, nbytes = [], 0
+    for k in (2560, 4096, 9728):
+        R = torch.from_numpy(synth.draw_rotation(rng, k // 128, 128).view(np.uint16)).cuda()
+        x = torch.from_numpy(synth.draw_x(rng, 1, k, "normal").view(np.uint16)).cuda()
+        o = torch.empty_like(x)
+        items.append((R, x, o, k))
+        nbytes += k * 128 * 2 + 2 * k * 2
+    lib = L.load()
+
+    def step():
+        for R, x, o, k in items:
+            L.check(lib.tern_rotate(R.data_ptr(), 128, x.data_ptr(), 1, k, o.data_ptr(), stream.cuda_stream))
+    steps = max(20, args.steps // 10)
+    wall, gpu, _ = time_graph([step], steps, 4, stream)
+    step_s = gpu / steps
+    return dict(us_per_layer=step_s * 1e6, gbs=nbytes / step_s / 1e9, bytes=nbytes, steps=steps)
+
+
 def cpu_quantize_baseline(budget_s=6.0):
     """The quantizer oracle (vectorized numpy FP32, one thread) on the 4B-class
     k projection's shape (1024 x 2560), repeated for about budget_s seconds."""
@@ -567,8 +594,13 @@ def main():
         extra["quantize_qwen3_4b_layer"] = dict(ms_per_layer=round(qz["ms_per_layer"], 4),
                                                 weights_per_s=qz["weights_per_s"], gbs=round(qz["gbs"], 1),
                                                 hbm_frac=round(qz["gbs"] / HBM_PEAK_GBS, 4), steps=qz["steps"],
-                                                kernel="quantize_kernel<128>: one wavefront per (row, group)")
+                                                kernel="quantize_kernel<128>: sixteen lanes per (row, group)")
         log(f"bench: quantize 4B-class layer {qz['ms_per_layer']:.3f} ms, {qz['weights_per_s']/1e9:.2f} G weights/s")
+        rt = bench_rotate(args, stream)
+        extra["rotate_m1_qwen3_4b_inputs"] = dict(us_per_layer=round(rt["us_per_layer"], 3), gbs=round(rt["gbs"], 1),
+                                                  bytes=rt["bytes"], steps=rt["steps"],
+                                                  note="three launches: K = 2560, 4096, 9728; 128 x 128 blocks")
+        log(f"bench: rotate M=1 inputs of a 4B-class layer {rt['us_per_layer']:.2f} us")
         # attainable read bandwidth on this machine: a plain reduction over 1 GiB
         # buffers, and over 36 buffers of the headline layer's size
         big = bench_read_probe(stream, 1 << 30, 2)

@@ -243,6 +243,18 @@ tern_status tern_bits(const tern_matrix *w, double *info, double *plane, double 
 tern_status tern_quantize(const uint16_t *w, int32_t n, int32_t k, int32_t group, const uint32_t *mask,
                           int32_t iters, int8_t *trits, uint16_t *scales, uint16_t *offset, void *stream);
 
+/* Activation-side rotation before the packed product ("Post-Training
+ * Ternarization of Qwen3-4B", §4.2: the weights are quantized in a rotated
+ * basis and inference rotates the activations to match; the pages do not
+ * give the rotation's structure): out = x blockdiag(R)^T, i.e.
+ *   out[m][b*block + i] = sum_j R[b][i][j] * x[m][b*block + j],
+ * R fp16 [k/block][block][block] (16-byte aligned), x and out fp16 [m][k]
+ * (4-byte aligned; out may equal x).  FP32 accumulation, FP16 output
+ * (round to nearest even).  block 64 or 128 and k % block == 0
+ * (TERN_E_UNSUPPORTED otherwise).  Async on stream. */
+tern_status tern_rotate(const uint16_t *R, int32_t block, const uint16_t *x, int32_t m, int32_t k, uint16_t *out,
+                        void *stream);
+
 /* Measurement aid, not part of the product: a plain streaming read of
  * `bytes` bytes (a multiple of 16) of device memory at `buf` (16-byte
  * aligned), the attainable-bandwidth reference for the products above.

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtern.so")
 
-SOURCES = ["tern_api.cpp", "pack.hip", "gemv.hip", "gemv_mfma.hip", "gemm.hip", "quant.hip"]
+SOURCES = ["tern_api.cpp", "pack.hip", "gemv.hip", "gemv_mfma.hip", "gemm.hip", "quant.hip", "rotate.hip"]
 ARCH = os.environ.get("TERN_OFFLOAD_ARCH", "gfx950")
 
 

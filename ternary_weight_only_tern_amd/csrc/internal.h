@@ -143,6 +143,11 @@ hipError_t launch_reduce_grouped(const RedDesc* rd, int count, int blocks, hipSt
 hipError_t launch_quantize(const uint16_t* w, int n, int k, int group, const uint32_t* mask, int mwords, int iters,
                            int8_t* trits, uint16_t* scales, uint16_t* offset, hipStream_t stream);
 
+// ---- activation rotation (rotate.hip)
+// out[m][k] = blockdiag(R) x: R fp16 [k/block][block][block], block 64 or 128.
+hipError_t launch_rotate(const uint16_t* R, int block, const uint16_t* x, int m, int k, uint16_t* out,
+                         hipStream_t stream);
+
 // ---- packing (pack.hip)
 hipError_t launch_pack_plane0(int format, const int8_t* trits, int n, int k, int group,
                               int stride, uint8_t* plane0, uint32_t* flag, hipStream_t stream);

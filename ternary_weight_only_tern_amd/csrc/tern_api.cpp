@@ -1391,6 +1391,19 @@ tern_status tern_quantize(const uint16_t* w, int32_t n, int32_t k, int32_t group
   return TERN_OK;
 }
 
+tern_status tern_rotate(const uint16_t* R, int32_t block, const uint16_t* x, int32_t m, int32_t k, uint16_t* out,
+                        void* stream) {
+  if (m < 0 || k < 0) return fail(TERN_E_INVAL, "m=%d, k=%d must not be negative", m, k);
+  if (block != 64 && block != 128) return fail(TERN_E_UNSUPPORTED, "rotate takes block 64 or 128 (got %d)", block);
+  if (k % block) return fail(TERN_E_UNSUPPORTED, "k=%d must be a multiple of block %d", k, block);
+  if (m == 0 || k == 0) return TERN_OK;
+  TERN_TRY(check_dev(R, true, "R", 16));
+  TERN_TRY(check_dev(x, true, "x", 4));
+  TERN_TRY(check_dev(out, true, "out", 4));
+  TERN_HIP(tern::launch_rotate(R, block, x, m, k, out, (hipStream_t)stream));
+  return TERN_OK;
+}
+
 tern_status tern_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   if (bytes % 16) return fail(TERN_E_INVAL, "bytes=%zu is not a multiple of 16", bytes);
   if (bytes == 0) return TERN_OK;

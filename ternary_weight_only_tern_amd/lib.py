@@ -36,7 +36,7 @@ TERN_F32 = 1
 SYMBOLS = ["tern_row_stride", "tern_check", "tern_packed_sizes", "tern_workspace_bytes",
            "tern_pack", "tern_unpack", "tern_gemv", "tern_gemm", "tern_batch_workspace_bytes",
            "tern_gemv_batched", "tern_plan_create", "tern_plan_run", "tern_plan_destroy",
-           "tern_bits", "tern_quantize", "tern_read_probe", "tern_status_str", "tern_last_error"]
+           "tern_bits", "tern_quantize", "tern_rotate", "tern_read_probe", "tern_status_str", "tern_last_error"]
 
 
 class tern_matrix(ctypes.Structure):
@@ -82,6 +82,7 @@ def load() -> ctypes.CDLL:
         "tern_bits": (c_int32, [P, POINTER(c_double), POINTER(c_double), POINTER(c_double)]),
         "tern_quantize": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p,
                                     c_void_p, c_void_p]),
+        "tern_rotate": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
         "tern_read_probe": (c_int32, [c_void_p, c_size_t, c_void_p, c_void_p]),
         "tern_status_str": (ctypes.c_char_p, [c_int32]),
         "tern_last_error": (ctypes.c_char_p, []),
@@ -284,6 +285,18 @@ def tern_quantize(w, mask_bits=None, group=128, iters=15, stream=None):
     check(load().tern_quantize(_ptr(w), n, k, group, _ptr(mask_bits) if mask_bits is not None else None, iters,
                                _ptr(trits), _ptr(scales), _ptr(offset), _stream(stream)))
     return trits, scales, offset
+
+
+def tern_rotate(R, x, out=None, stream=None):
+    """out = x rotated by the block-diagonal R (device tensors: R fp16
+    [k/block][block][block], x fp16 [m][k]); returns out (fp16 [m][k])."""
+    import torch
+    m, k = x.shape
+    block = R.shape[-1]
+    if out is None:
+        out = torch.empty((m, k), dtype=torch.float16, device=x.device)
+    check(load().tern_rotate(_ptr(R), block, _ptr(x), m, k, _ptr(out), _stream(stream)))
+    return out
 
 
 def tern_read_probe(buf, sink, stream=None) -> None:

@@ -130,3 +130,14 @@ def test_quantize_rejects_bad_arguments_before_any_launch():
     assert q(4, 256, 128, 1001) == L.TERN_E_INVAL
     assert q(0, 256, 128, 15) == L.TERN_OK  # empty: nothing to do, no pointer touched
     assert q(4, 256, 128, 15) == L.TERN_E_INVAL  # NULL weights
+
+
+def test_rotate_rejects_bad_arguments_before_any_launch():
+    lib = L.load()
+    nul = ctypes.c_void_p(0)
+    r = lambda block, m, k: lib.tern_rotate(nul, block, nul, m, k, nul, nul)
+    assert r(96, 1, 384) == L.TERN_E_UNSUPPORTED
+    assert r(128, 1, 200) == L.TERN_E_UNSUPPORTED
+    assert r(128, -1, 256) == L.TERN_E_INVAL
+    assert r(128, 0, 256) == L.TERN_OK
+    assert r(128, 2, 256) == L.TERN_E_INVAL  # NULL pointers
