@@ -204,8 +204,9 @@ def bench_stack8b(args, stream):
     bpw = {key: round(sum(b[key] * w for b, w in zip(bits, wts)) / sum(wts), 4) for key in ("info", "plane", "storage")}
     plan = L.Plan(mats, xl, yl)
     torch.cuda.synchronize()
-    steps = max(2, args.steps // 20)
-    wall, gpu, _ = time_graph([lambda: plan.run(stream.cuda_stream)], steps, max(2, args.warmup // 10), stream)
+    per = 3  # steps captured per graph replay
+    steps = max(per, args.steps // 20 // per * per)
+    wall, gpu, _ = time_graph([lambda: plan.run(stream.cuda_stream)] * per, steps, per, stream)
     step_s = gpu / steps
     return dict(stack_bytes=stack_bytes, steps=steps, step_s=step_s, gbs=stack_bytes / step_s / 1e9,
                 tok_s=1.0 / step_s, bpw=bpw)
@@ -227,8 +228,9 @@ def bench_gemm512(args, stream):
     flops = sum(2.0 * m * pm.n * pm.k for pm, _, _ in items)
     plan = L.Plan([pm for pm, _, _ in items], [xd for _, xd, _ in items], [y for _, _, y in items])
     step = lambda: plan.run(stream.cuda_stream)
-    steps = max(2, args.steps // 20)
-    wall, gpu, _ = time_graph([step], steps, 2, stream)
+    per = 6  # steps captured per graph replay
+    steps = max(per, args.steps // 20 // per * per)
+    wall, gpu, _ = time_graph([step] * per, steps, per, stream)
     step_s = gpu / steps
     return dict(flops=flops, steps=steps, step_s=step_s, tflops=flops / step_s / 1e12)
 
@@ -247,8 +249,9 @@ def bench_layer8b(args, stream, m, fmt=1):
         xs.append(xd)
         ys.append(torch.empty((m, pm.n), dtype=torch.float16, device="cuda"))
     plan = L.Plan(pms, xs, ys)
-    steps = max(4, args.steps // 20)
-    wall, gpu, _ = time_graph([lambda: plan.run(stream.cuda_stream)], steps, 4, stream)
+    per = 6  # steps captured per graph replay (a replay's own launch cost is then shared)
+    steps = max(per, args.steps // 20 // per * per)
+    wall, gpu, _ = time_graph([lambda: plan.run(stream.cuda_stream)] * per, steps, per, stream)
     step_s = gpu / steps
     nbytes = sum(pm.nbytes() for pm in pms)
     flops = sum(2.0 * m * pm.n * pm.k for pm in pms)
@@ -336,8 +339,9 @@ def bench_quantize(args, stream):
         for wd, md, t, sc, of, n, k in items:
             L.check(lib.tern_quantize(wd.data_ptr(), n, k, 128, md.data_ptr(), 15, t.data_ptr(), sc.data_ptr(),
                                       of.data_ptr(), stream.cuda_stream))
-    steps = max(4, args.steps // 100)
-    wall, gpu, _ = time_graph([step], steps, 2, stream)
+    per = 2  # steps captured per graph replay
+    steps = max(per, args.steps // 100 // per * per)
+    wall, gpu, _ = time_graph([step] * per, steps, per, stream)
     step_s = gpu / steps
     io_bytes = nw * 2 + nw * 2 + sum(n * (k // 128) * 2 * 3 + n * ((k // 128 + 31) // 32) * 4 for _, _, _, _, _, n, k in items)
     return dict(ms_per_layer=step_s * 1e3, weights_per_s=nw / step_s, gbs=io_bytes / step_s / 1e9, steps=steps,
@@ -347,8 +351,8 @@ def bench_quantize(args, stream):
 def bench_rotate(args, stream):
     """The activation rotation at M=1 for the three inputs of a 4B-class
     layer (hidden 2560 for q/k/v and gate/up, attention output 4096 for o,
-    MLP intermediate 9728 for down), 128 x 128 blocks, three launches per
-    step."""
+    MLP intermediate 9728 for down), 128 x 128 blocks, one batched launch
+    per step."""
     import torch
     from ternary_weight_only_tern_amd import lib as L
     from ternary_weight_only_tern_amd import synth
@@ -361,12 +365,17 @@ def bench_rotate(args, stream):
         items.append((R, x, o, k))
         nbytes += k * 128 * 2 + 2 * k * 2
     lib = L.load()
+    import ctypes
+    rp = (ctypes.c_void_p * 3)(*[it[0].data_ptr() for it in items])
+    xp = (ctypes.c_void_p * 3)(*[it[1].data_ptr() for it in items])
+    op = (ctypes.c_void_p * 3)(*[it[2].data_ptr() for it in items])
+    kk = (ctypes.c_int32 * 3)(*[it[3] for it in items])
 
     def step():
-        for R, x, o, k in items:
-            L.check(lib.tern_rotate(R.data_ptr(), 128, x.data_ptr(), 1, k, o.data_ptr(), stream.cuda_stream))
-    steps = max(20, args.steps // 10)
-    wall, gpu, _ = time_graph([step], steps, 4, stream)
+        L.check(lib.tern_rotate_batched(3, rp, 128, xp, kk, 1, op, stream.cuda_stream))
+    per = 12  # steps captured per graph replay (a replay's own launch cost is then shared)
+    steps = max(per, args.steps // 10 // per * per)
+    wall, gpu, _ = time_graph([step] * per, steps, per, stream)
     step_s = gpu / steps
     return dict(us_per_layer=step_s * 1e6, gbs=nbytes / step_s / 1e9, bytes=nbytes, steps=steps)
 
@@ -599,7 +608,7 @@ def main():
         rt = bench_rotate(args, stream)
         extra["rotate_m1_qwen3_4b_inputs"] = dict(us_per_layer=round(rt["us_per_layer"], 3), gbs=round(rt["gbs"], 1),
                                                   bytes=rt["bytes"], steps=rt["steps"],
-                                                  note="three launches: K = 2560, 4096, 9728; 128 x 128 blocks")
+                                                  note="one launch for K = 2560, 4096, 9728; 128 x 128 blocks")
         log(f"bench: rotate M=1 inputs of a 4B-class layer {rt['us_per_layer']:.2f} us")
         # attainable read bandwidth on this machine: a plain reduction over 1 GiB
         # buffers, and over 36 buffers of the headline layer's size
