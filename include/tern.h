@@ -255,6 +255,15 @@ tern_status tern_quantize(const uint16_t *w, int32_t n, int32_t k, int32_t group
 tern_status tern_rotate(const uint16_t *R, int32_t block, const uint16_t *x, int32_t m, int32_t k, uint16_t *out,
                         void *stream);
 
+/* Several rotations in one launch (a layer's inputs, say): for i < count
+ * (0..8; TERN_E_UNSUPPORTED above), out[i] = x[i] rotated by R[i] as in
+ * tern_rotate, all with the same block and m; R, x, out are host arrays
+ * of device pointers and k a host array of sizes (each a multiple of
+ * block).  No workspace: the pointers travel in the kernel's arguments,
+ * so the call may be captured into a HIP graph.  Async on stream. */
+tern_status tern_rotate_batched(int32_t count, const uint16_t *const *R, int32_t block, const uint16_t *const *x,
+                                const int32_t *k, int32_t m, uint16_t *const *out, void *stream);
+
 /* Measurement aid, not part of the product: a plain streaming read of
  * `bytes` bytes (a multiple of 16) of device memory at `buf` (16-byte
  * aligned), the attainable-bandwidth reference for the products above.

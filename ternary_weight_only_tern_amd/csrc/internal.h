@@ -144,9 +144,19 @@ hipError_t launch_quantize(const uint16_t* w, int n, int k, int group, const uin
                            int8_t* trits, uint16_t* scales, uint16_t* offset, hipStream_t stream);
 
 // ---- activation rotation (rotate.hip)
-// out[m][k] = blockdiag(R) x: R fp16 [k/block][block][block], block 64 or 128.
-hipError_t launch_rotate(const uint16_t* R, int block, const uint16_t* x, int m, int k, uint16_t* out,
-                         hipStream_t stream);
+// out_i[m][k_i] = blockdiag(R_i) x_i for up to kMaxRotations inputs in one
+// launch: R_i fp16 [k_i/block][block][block], block 64 or 128; begin[i] =
+// first workgroup (block) of input i, begin[count] = total blocks.
+constexpr int kMaxRotations = 8;
+struct RotBatch {
+  const uint16_t* R[kMaxRotations];
+  const uint16_t* x[kMaxRotations];
+  uint16_t* out[kMaxRotations];
+  int32_t k[kMaxRotations];
+  int32_t begin[kMaxRotations + 1];
+  int32_t count, m;
+};
+hipError_t launch_rotate(const RotBatch& a, int block, hipStream_t stream);
 
 // ---- packing (pack.hip)
 hipError_t launch_pack_plane0(int format, const int8_t* trits, int n, int k, int group,

@@ -14,7 +14,10 @@
 // over the FP16 pairs of its row (FP16 products are exact in FP32);
 // outputs are FP16 (round to nearest even).  A workgroup reads its
 // activations before writing any output, and no other workgroup touches
-// them, so out may equal x.
+// them, so out may equal x.  Up to kMaxRotations inputs (a layer's q/k/v and
+// gate/up input, attention output and MLP intermediate, say) share one
+// launch: their pointers travel in the kernel arguments and workgroup j
+// belongs to the input whose block range holds j.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -30,25 +33,35 @@ typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 constexpr int kRows = 16;  // activation rows per workgroup
 
 template <int B>
-__global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* __restrict__ R, const uint16_t* x, int m, int k,
-                                                     uint16_t* out) {
+__global__ __launch_bounds__(256) void rotate_kernel(RotBatch a) {
   constexpr int P = B / 2 + 1;  // padded row pitch of R in LDS (FP16 pairs)
   __shared__ uint32_t rs[B * P];
   __shared__ uint32_t xs[kRows * B / 2];  // [row][B/2] FP16 pairs
-  const int b = blockIdx.x;
+  int in = 0;
+  while (in + 1 < a.count && (int)blockIdx.x >= a.begin[in + 1]) ++in;
+  const uint16_t* __restrict__ R = a.R[in];
+  const uint16_t* x = a.x[in];
+  uint16_t* out = a.out[in];
+  const int k = a.k[in], m = a.m;
+  const int b = (int)blockIdx.x - a.begin[in];
   const int m0 = blockIdx.y * kRows;
   const int rows = min(kRows, m - m0);
   const int t = threadIdx.x;
-  // R_b: B rows of B / 8 16-byte chunks
+  // R_b: B rows of B / 8 16-byte chunks, every chunk of the thread requested
+  // before any is stored
+  constexpr int NC = B * (B / 8) / 256;
   const u4_t* rg = reinterpret_cast<const u4_t*>(R + (size_t)b * B * B);
-  for (int c = t; c < B * (B / 8); c += 256) {
-    const int row = c / (B / 8), q = c % (B / 8);
-    const u4_t v = rg[c];
+  u4_t v[NC];
+#pragma unroll
+  for (int u = 0; u < NC; ++u) v[u] = rg[t + 256 * u];
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    const int c = t + 256 * u, row = c / (B / 8), q = c % (B / 8);
     uint32_t* d = rs + row * P + 4 * q;
-    d[0] = v.x;
-    d[1] = v.y;
-    d[2] = v.z;
-    d[3] = v.w;
+    d[0] = v[u].x;
+    d[1] = v[u].y;
+    d[2] = v[u].z;
+    d[3] = v[u].w;
   }
   for (int e = t; e < rows * (B / 2); e += 256) {
     const int r = e / (B / 2), j = e % (B / 2);
@@ -69,14 +82,14 @@ __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* __restrict_
 
 }  // namespace
 
-hipError_t launch_rotate(const uint16_t* R, int block, const uint16_t* x, int m, int k, uint16_t* out,
-                         hipStream_t s) {
-  if (m <= 0 || k <= 0) return hipSuccess;
-  const dim3 grid((unsigned)(k / block), (unsigned)((m + kRows - 1) / kRows));
+hipError_t launch_rotate(const RotBatch& a, int block, hipStream_t s) {
+  const int blocks = a.begin[a.count];
+  if (a.m <= 0 || blocks <= 0) return hipSuccess;
+  const dim3 grid((unsigned)blocks, (unsigned)((a.m + kRows - 1) / kRows));
   if (block == 128)
-    hipLaunchKernelGGL((rotate_kernel<128>), grid, dim3(256), 0, s, R, x, m, k, out);
+    hipLaunchKernelGGL((rotate_kernel<128>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((rotate_kernel<64>), grid, dim3(256), 0, s, R, x, m, k, out);
+    hipLaunchKernelGGL((rotate_kernel<64>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1393,17 +1393,46 @@ tern_status tern_quantize(const uint16_t* w, int32_t n, int32_t k, int32_t group
   return TERN_OK;
 }
 
+tern_status tern_rotate_batched(int32_t count, const uint16_t* const* R, int32_t block, const uint16_t* const* x,
+                                const int32_t* k, int32_t m, uint16_t* const* out, void* stream) {
+  if (count < 0 || count > tern::kMaxRotations)
+    return fail(TERN_E_UNSUPPORTED, "count=%d: one launch rotates 0..%d inputs", count, tern::kMaxRotations);
+  if (m < 0) return fail(TERN_E_INVAL, "m=%d must not be negative", m);
+  if (block != 64 && block != 128) return fail(TERN_E_UNSUPPORTED, "rotate takes block 64 or 128 (got %d)", block);
+  if (count > 0 && (!R || !x || !k || !out)) return fail(TERN_E_INVAL, "NULL argument arrays");
+  tern::RotBatch a;
+  std::memset(&a, 0, sizeof(a));
+  a.m = m;
+  int blocks = 0;
+  for (int i = 0; i < count; ++i) {
+    if (k[i] < 0) return fail(TERN_E_INVAL, "k[%d]=%d must not be negative", i, k[i]);
+    if (k[i] % block) return fail(TERN_E_UNSUPPORTED, "k[%d]=%d must be a multiple of block %d", i, k[i], block);
+  }
+  if (m == 0) return TERN_OK;
+  for (int i = 0; i < count; ++i) {
+    if (k[i] == 0) continue;
+    TERN_TRY(check_dev(R[i], true, "R", 16));
+    TERN_TRY(check_dev(x[i], true, "x", 4));
+    TERN_TRY(check_dev(out[i], true, "out", 4));
+    a.R[a.count] = R[i];
+    a.x[a.count] = x[i];
+    a.out[a.count] = out[i];
+    a.k[a.count] = k[i];
+    a.begin[a.count] = blocks;
+    blocks += k[i] / block;
+    ++a.count;
+  }
+  a.begin[a.count] = blocks;
+  if (a.count == 0) return TERN_OK;
+  TERN_HIP(tern::launch_rotate(a, block, (hipStream_t)stream));
+  return TERN_OK;
+}
+
 tern_status tern_rotate(const uint16_t* R, int32_t block, const uint16_t* x, int32_t m, int32_t k, uint16_t* out,
                         void* stream) {
   if (m < 0 || k < 0) return fail(TERN_E_INVAL, "m=%d, k=%d must not be negative", m, k);
-  if (block != 64 && block != 128) return fail(TERN_E_UNSUPPORTED, "rotate takes block 64 or 128 (got %d)", block);
-  if (k % block) return fail(TERN_E_UNSUPPORTED, "k=%d must be a multiple of block %d", k, block);
-  if (m == 0 || k == 0) return TERN_OK;
-  TERN_TRY(check_dev(R, true, "R", 16));
-  TERN_TRY(check_dev(x, true, "x", 4));
-  TERN_TRY(check_dev(out, true, "out", 4));
-  TERN_HIP(tern::launch_rotate(R, block, x, m, k, out, (hipStream_t)stream));
-  return TERN_OK;
+  uint16_t* o = out;
+  return tern_rotate_batched(1, &R, block, &x, &k, m, &o, stream);
 }
 
 tern_status tern_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

@@ -36,7 +36,7 @@ TERN_F32 = 1
 SYMBOLS = ["tern_row_stride", "tern_check", "tern_packed_sizes", "tern_workspace_bytes",
            "tern_pack", "tern_unpack", "tern_gemv", "tern_gemm", "tern_batch_workspace_bytes",
            "tern_gemv_batched", "tern_plan_create", "tern_plan_run", "tern_plan_destroy",
-           "tern_bits", "tern_quantize", "tern_rotate", "tern_read_probe", "tern_status_str", "tern_last_error"]
+           "tern_bits", "tern_quantize", "tern_rotate", "tern_rotate_batched", "tern_read_probe", "tern_status_str", "tern_last_error"]
 
 
 class tern_matrix(ctypes.Structure):
@@ -83,6 +83,8 @@ def load() -> ctypes.CDLL:
         "tern_quantize": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p,
                                     c_void_p, c_void_p]),
         "tern_rotate": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+        "tern_rotate_batched": (c_int32, [c_int32, POINTER(c_void_p), c_int32, POINTER(c_void_p), POINTER(c_int32),
+                                          c_int32, POINTER(c_void_p), c_void_p]),
         "tern_read_probe": (c_int32, [c_void_p, c_size_t, c_void_p, c_void_p]),
         "tern_status_str": (ctypes.c_char_p, [c_int32]),
         "tern_last_error": (ctypes.c_char_p, []),
@@ -297,6 +299,23 @@ def tern_rotate(R, x, out=None, stream=None):
         out = torch.empty((m, k), dtype=torch.float16, device=x.device)
     check(load().tern_rotate(_ptr(R), block, _ptr(x), m, k, _ptr(out), _stream(stream)))
     return out
+
+
+def tern_rotate_batched(Rs, xs, outs=None, stream=None):
+    """Rotate several activation tensors in one launch (same block size and
+    number of rows); returns the outputs."""
+    import torch
+    n = len(xs)
+    m = xs[0].shape[0] if n else 0
+    block = Rs[0].shape[-1] if n else 128
+    if outs is None:
+        outs = [torch.empty_like(x) for x in xs]
+    rp = (c_void_p * max(n, 1))(*[r.data_ptr() for r in Rs])
+    xp = (c_void_p * max(n, 1))(*[x.data_ptr() for x in xs])
+    op = (c_void_p * max(n, 1))(*[o.data_ptr() for o in outs])
+    kk = (c_int32 * max(n, 1))(*[x.shape[1] for x in xs])
+    check(load().tern_rotate_batched(n, rp, block, xp, kk, m, op, _stream(stream)))
+    return outs
 
 
 def tern_read_probe(buf, sink, stream=None) -> None:

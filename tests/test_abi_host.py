@@ -141,3 +141,15 @@ def test_rotate_rejects_bad_arguments_before_any_launch():
     assert r(128, -1, 256) == L.TERN_E_INVAL
     assert r(128, 0, 256) == L.TERN_OK
     assert r(128, 2, 256) == L.TERN_E_INVAL  # NULL pointers
+
+
+def test_rotate_batched_rejects_bad_arguments_before_any_launch():
+    lib = L.load()
+    ks = (ctypes.c_int32 * 2)(256, 200)
+    ptrs = (ctypes.c_void_p * 2)(None, None)
+    assert lib.tern_rotate_batched(9, ptrs, 128, ptrs, ks, 1, ptrs, None) == L.TERN_E_UNSUPPORTED
+    assert lib.tern_rotate_batched(2, ptrs, 128, ptrs, ks, 1, ptrs, None) == L.TERN_E_UNSUPPORTED  # 200 % 128
+    assert lib.tern_rotate_batched(1, ptrs, 96, ptrs, ks, 1, ptrs, None) == L.TERN_E_UNSUPPORTED
+    assert lib.tern_rotate_batched(1, ptrs, 128, ptrs, ks, -1, ptrs, None) == L.TERN_E_INVAL
+    assert lib.tern_rotate_batched(0, None, 128, None, None, 1, None, None) == L.TERN_OK
+    assert lib.tern_rotate_batched(1, ptrs, 128, ptrs, ks, 1, ptrs, None) == L.TERN_E_INVAL  # NULL device pointers

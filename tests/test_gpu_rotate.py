@@ -54,3 +54,21 @@ def test_rotate_identity_and_in_place():
     L.tern_rotate(Rd, xd, out=xd)
     torch.cuda.synchronize()
     assert torch.equal(out, xd)
+
+
+def test_rotate_batched_equals_single_launches():
+    """A layer's three inputs (K = 2560, 4096, 9728) and a ragged fourth in one
+    launch equal separate tern_rotate calls bit for bit, at M = 1 and 20."""
+    import torch
+    say("rotate batched")
+    rng = np.random.default_rng(21)
+    for m in (1, 20):
+        Rs, xs = [], []
+        for k in (2560, 4096, 9728, 384):
+            Rs.append(_dev16(synth.draw_rotation(rng, k // 128, 128)))
+            xs.append(_dev16(synth.draw_x(rng, m, k, "normal")))
+        outs = L.tern_rotate_batched(Rs, xs)
+        singles = [L.tern_rotate(R, x) for R, x in zip(Rs, xs)]
+        torch.cuda.synchronize()
+        for o, s_ in zip(outs, singles):
+            assert torch.equal(o, s_)
