@@ -9,13 +9,16 @@
 // are summed in wave order through LDS at the end (deterministic, and no
 // global memory fence: on this multi-XCD part a device-scope fence writes
 // back and invalidates the L2).  When a row block is also split along K
-// across workgroups, each split writes FP32 partials and a second kernel sums
-// them in split order.
+// across workgroups, each split writes FP32 partials that are summed in split
+// order: by the row block's last workgroup in batches and plans, by a second
+// kernel in the single-product call.
 //
 // Stage.  A stage is 128 (2-bit) or 208 (base-3) bytes of each of the 64
 // rows, i.e. whole groups.  Its packed rows are loaded with coalesced 16-byte
 // loads (8 or 13 lanes per row), two (2-bit) or one (base-3) stages ahead,
-// and written to the wave's
+// marked non-temporal (every weight byte is read once per product, so it
+// should not displace the activations and tables from the caches; plain
+// streams of this kind run ~10 % faster so marked), and written to the wave's
 // LDS area together with the stage's activations; each lane then decodes its
 // own row.  All lanes sit at the same K position, so activations are read
 // with wave-uniform (broadcast) LDS reads.
@@ -292,7 +295,7 @@ __device__ __forceinline__ void residual_compact(const GemvDesc& d, int p, int r
       for (int m = 0; m < MT; ++m) part[m] = 0.f;
 #pragma unroll
       for (int q = 0; q < G / 64; ++q) {
-        const u4_t v = blk[q];
+        const u4_t v = __builtin_nontemporal_load(blk + q);
         const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -390,7 +393,7 @@ __global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __
       const int c = i * kWave + lane;                                                        \
       const int r = c / Gm::CPR, col = c % Gm::CPR;                                          \
       if (r < rows_here && col * 16 < bytes_)                                                \
-        P[i] = *reinterpret_cast<const GLOBAL u4_t*>(base_ + (size_t)r * d.stride + col * 16); \
+        P[i] = __builtin_nontemporal_load(reinterpret_cast<const GLOBAL u4_t*>(base_ + (size_t)r * d.stride + col * 16)); \
     }                                                                                        \
     _Pragma("unroll") for (int j = 0; j < Gm::SG; ++j)                                       \
       SP[j] = (row_ok && gs_ + j < gb) ? srow[gs_ + j] : (uint16_t)0;                        \
@@ -533,8 +536,8 @@ __global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __
 }
 
 // Plain streaming read of `bytes` bytes (a multiple of 16): every wavefront
-// reads 8 KB of consecutive bytes per round (eight 1 KB loads in flight, 16
-// bytes per lane), rounds striding over the grid; the sink is written only
+// reads 8 KB of consecutive bytes per round (eight 1 KB non-temporal loads in
+// flight, 16 bytes per lane), rounds striding over the grid; the sink is written only
 // if the XOR of everything read equals a value no input here produces, so
 // the loads cannot be dropped.
 __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ p, size_t n16, uint32_t* sink) {
@@ -547,7 +550,8 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const size_t i = base + (size_t)u * 64 + lane;
-      v[u] = i < n16 ? p[i] : uint4{0u, 0u, 0u, 0u};
+      v[u] = i < n16 ? __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u4_t*>(p) + i))
+                      : uint4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
