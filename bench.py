@@ -521,6 +521,10 @@ def main():
                     help="only the 8B-class base-3 stack at M=1 (profiling); prints its result, no JSON line")
     ap.add_argument("--quantize-only", action="store_true",
                     help="only the quantizer on a 4B-class layer (profiling); prints its result, no JSON line")
+    ap.add_argument("--rotate-only", action="store_true",
+                    help="only the activation rotation of a 4B-class layer's M=1 inputs (profiling); no JSON line")
+    ap.add_argument("--layer8b-only", type=int, metavar="M", default=0,
+                    help="only the base-3 8B-class layer at M activation rows (profiling); no JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -551,6 +555,15 @@ def main():
     if args.quantize_only:
         qz = bench_quantize(args, stream)
         log(f"bench: quantize 4B-class layer {qz['ms_per_layer']:.3f} ms, {qz['weights_per_s']/1e9:.2f} G weights/s")
+        return
+    if args.rotate_only:
+        ro = bench_rotate(args, stream)
+        log(f"bench: rotation of a 4B-class layer's M=1 inputs {ro['us_per_layer']:.2f} us, {ro['gbs']:.1f} GB/s")
+        return
+    if args.layer8b_only > 0:
+        q = bench_layer8b(args, stream, args.layer8b_only)
+        log(f"bench: 8B-class layer base-3 M={args.layer8b_only}: {q['us_per_layer']:.1f} us, {q['gbs']:.1f} GB/s, "
+            f"{q['tflops']:.1f} TFLOP/s")
         return
     if args.stack8b_only:
         s8 = bench_stack8b(args, stream)
