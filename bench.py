@@ -364,15 +364,10 @@ def bench_rotate(args, stream):
         o = torch.empty_like(x)
         items.append((R, x, o, k))
         nbytes += k * 128 * 2 + 2 * k * 2
-    lib = L.load()
-    import ctypes
-    rp = (ctypes.c_void_p * 3)(*[it[0].data_ptr() for it in items])
-    xp = (ctypes.c_void_p * 3)(*[it[1].data_ptr() for it in items])
-    op = (ctypes.c_void_p * 3)(*[it[2].data_ptr() for it in items])
-    kk = (ctypes.c_int32 * 3)(*[it[3] for it in items])
+    Rs, xs, outs = [it[0] for it in items], [it[1] for it in items], [it[2] for it in items]
 
     def step():
-        L.check(lib.tern_rotate_batched(3, rp, 128, xp, kk, 1, op, stream.cuda_stream))
+        L.tern_rotate_batched(Rs, xs, outs, stream.cuda_stream)
     per = 12  # steps captured per graph replay (a replay's own launch cost is then shared)
     steps = max(per, args.steps // 10 // per * per)
     wall, gpu, _ = time_graph([step] * per, steps, per, stream)
