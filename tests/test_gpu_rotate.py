@@ -72,3 +72,52 @@ def test_rotate_batched_equals_single_launches():
         torch.cuda.synchronize()
         for o, s_ in zip(outs, singles):
             assert torch.equal(o, s_)
+
+
+def test_rotate_batched_eight_inputs_empty_input_and_graph_replays():
+    """The most inputs one launch takes (8, block 64, one of them with K = 0,
+    which the call skips) at a ragged M = 19 equals separate launches bit for
+    bit; the same call captured into a graph and replayed after the inputs
+    change (eager work and synchronisations between replays) equals the eager
+    call on every replay."""
+    import torch
+    say("rotate batched: 8 inputs, K = 0, graph replays")
+    rng = np.random.default_rng(33)
+    m, block = 19, 64
+    ks = (64, 128, 320, 0, 1024, 2560, 192, 4096)
+    Rs = [_dev16(synth.draw_rotation(rng, k // block, block)) if k else
+          torch.empty((0, block, block), dtype=torch.float16, device="cuda") for k in ks]
+    xs = [_dev16(synth.draw_x(rng, m, k, "student_t3")) if k else
+          torch.empty((m, 0), dtype=torch.float16, device="cuda") for k in ks]
+    outs = L.tern_rotate_batched(Rs, xs)
+    singles = [L.tern_rotate(R, x) if x.shape[1] else torch.empty_like(x) for R, x in zip(Rs, xs)]
+    torch.cuda.synchronize()
+    for o, s_ in zip(outs, singles):
+        assert torch.equal(o, s_)
+    for o, R, x in zip(outs, Rs, xs):  # one of them against the oracle as well
+        if x.shape[1] == 2560:
+            got = o.cpu().numpy().astype(np.float64)
+            Rh, xh = R.cpu().numpy(), x.cpu().numpy()
+            assert (np.abs(got - Rt.rotate(Rh, xh)) <= 2e-3 * Rt.rotate_bound(Rh, xh)).all()
+
+    gouts = [torch.empty_like(x) for x in xs]
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        L.tern_rotate_batched(Rs, xs, gouts, stream.cuda_stream)  # warm the call once outside the capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            L.tern_rotate_batched(Rs, xs, gouts, stream.cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in xs:
+            if x.shape[1]:
+                x.copy_(_dev16(synth.draw_x(rng, m, x.shape[1], "normal")))
+        want = L.tern_rotate_batched(Rs, xs)
+        torch.cuda.synchronize()
+        for o in gouts:
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for g, w_ in zip(gouts, want):
+            assert torch.equal(g, w_), f"replay {rep} differs from the eager call"
