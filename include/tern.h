@@ -204,7 +204,9 @@ tern_status tern_gemv_batched(const tern_matrix *w, const uint16_t *const *x, vo
  * handle (malloc'ed; free it with tern_plan_destroy).  tern_plan_run
  * launches the whole batch on stream; it may be called any number of times
  * and captured in a HIP graph.  The buffers named in the plan must stay
- * valid while the plan is used. */
+ * valid while the plan is used.  Runs of one plan (or of plans, or batched
+ * calls, that share a workspace) use the same partials and K-part counters,
+ * so runs that overlap in time race: order them on one stream. */
 typedef struct tern_plan tern_plan;
 tern_status tern_plan_create(const tern_matrix *w, const uint16_t *const *x, void *const *y,
                              int32_t count, int32_t m, int32_t y_dtype, void *ws,
