@@ -261,8 +261,11 @@ tern_status tern_rotate(const uint16_t *R, int32_t block, const uint16_t *x, int
  * (0..8; TERN_E_UNSUPPORTED above), out[i] = x[i] rotated by R[i] as in
  * tern_rotate, all with the same block and m; R, x, out are host arrays
  * of device pointers and k a host array of sizes (each a multiple of
- * block).  No workspace: the pointers travel in the kernel's arguments,
- * so the call may be captured into a HIP graph.  Async on stream. */
+ * block).  Inputs with k[i] == 0 are skipped (their pointers are not
+ * read) and m == 0 launches nothing.  out[i] may equal x[i], but the
+ * buffers of different inputs must not overlap.  No workspace: the
+ * pointers travel in the kernel's arguments, so the call may be captured
+ * into a HIP graph.  Async on stream. */
 tern_status tern_rotate_batched(int32_t count, const uint16_t *const *R, int32_t block, const uint16_t *const *x,
                                 const int32_t *k, int32_t m, uint16_t *const *out, void *stream);
 

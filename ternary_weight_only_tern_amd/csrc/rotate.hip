@@ -7,9 +7,10 @@
 // block-diagonal matrix aligned with the weight groups.
 //
 // One workgroup of 256 threads per (block, chunk of up to kRows activation
-// rows): R_b and the block's activations are copied to LDS with contiguous
-// 16-byte loads (R's rows padded by one 4-byte word, so that the threads'
-// row reads below fall in distinct banks); thread t computes output row
+// rows): R_b is copied to LDS with contiguous 16-byte loads (its rows padded
+// by one 4-byte word, so that the threads' row reads below fall in distinct
+// banks) and the block's activations with contiguous 4-byte loads (x and out
+// need only 4-byte alignment); thread t computes output row
 // t % B of activation rows t / B, t / B + 256 / B, ... with v_dot2_f32_f16
 // over the FP16 pairs of its row (FP16 products are exact in FP32);
 // outputs are FP16 (round to nearest even).  A workgroup reads its
