@@ -76,6 +76,9 @@ int gemv_mfma_max_rows(int group);
 int gemv_mfma_max_range(int mp);
 // Workgroups of the matrix-core decode kernel that one CU holds at once
 // (LDS and register limits) for a launch with these parameters.
+// Most workgroups per CU that a matrix-core decode launch is placed for
+// (the workspace layout reserves one record per such slot).
+constexpr int kMfmaMaxWgsPerCu = 3;
 int gemv_mfma_wgs_per_cu(int group, int mp, int max_krp, bool offsets);
 // Same descriptors and work items as launch_gemv; a work item is 64 / kwaves
 // rows; K splits start on 256-trit blocks.  max_krp = the longest range of

@@ -705,7 +705,8 @@ static tern_status build_batch(const tern_matrix* w, const uint16_t* const* x, v
       *max_krp = std::max(*max_krp, round256(std::min(d.k, g * d.group)));
       coarse_items += (size_t)d.row_blocks * ns;
     }
-    const int slots = tern_cu_count() * tern::gemv_mfma_wgs_per_cu(w[0].group, *mt, *max_krp, *offsets);
+    const int slots = tern_cu_count() * std::min(tern::gemv_mfma_wgs_per_cu(w[0].group, *mt, *max_krp, *offsets),
+                                                 tern::kMfmaMaxWgsPerCu);
     size_t recs_off, part_off;
     mfma_offsets(parts.size(), std::max(coarse_items, (size_t)slots), &recs_off, &part_off);
     size_t poff = 0;
@@ -1105,7 +1106,7 @@ size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m
   // lane-per-row decode: one descriptor per work item, then the partials and
   // reduce table; matrix-core decode: two row ranges per (matrix, row
   // chunk), one record per workgroup (balanced placement may split items up
-  // to the launch's resident slots: at most 3 workgroups per CU), then the
+  // to the launch's resident slots: at most kMfmaMaxWgsPerCu per CU), then the
   // partials and reduce table (the layouts build_batch makes)
   // (arrival counters: one per row block of a descriptor with K parts; the
   // matrix-core placement cuts row blocks down to 16 rows at most)
@@ -1128,7 +1129,7 @@ size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m
   }
   if (!mf) return round_up(nitems * sizeof(GemvDesc), 256) + round_up(partial + nctr * 4, 256) + idx;
   size_t recs_off, part_off;
-  mfma_offsets(nparts, std::max(coarse, (size_t)tern_cu_count() * 3), &recs_off, &part_off);
+  mfma_offsets(nparts, std::max(coarse, (size_t)tern_cu_count() * tern::kMfmaMaxWgsPerCu), &recs_off, &part_off);
   return round_up(part_off + partial + nctr * 4, 256) + idx;
 }
 
