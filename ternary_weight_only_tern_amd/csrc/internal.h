@@ -53,6 +53,12 @@ struct GemvDesc {
   // the last workgroup of a row block sums the K parts and writes y; NULL:
   // only the partials are written (a separate reduce sums them).
   uint32_t* ctr;
+  // Base-3 matrix-core decode: the activations in its slot order
+  // ([m][ng][b3_chunks_per_group][4] FP16) and, with an offset, the FP32
+  // group sums of x ([m][ng]); both prepared by launch_b3_prep.  There,
+  // splits counts K parts and gps is the 208-byte stages per part.
+  const uint16_t* x5;
+  const float* xs;
 };
 
 // ---- decode products (gemv.hip)
@@ -110,6 +116,36 @@ hipError_t launch_tile_bounds(const GemvDesc* ranges, WgRec* recs, int count, hi
 
 // Plain streaming read of bytes (a multiple of 16) from buf (measurement).
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
+// ---- base-3 matrix-core decode (gemv_b3.hip), up to 4 activation rows
+constexpr int kB3Waves = 8;          // wavefronts per workgroup; one workgroup per CU
+// Work item of a grouped launch: descriptor index << 16 | K part, and the
+// 64-row block.  Wavefront w of the launch (workgroup * kB3Waves + wave)
+// takes items [wbeg[w], wbeg[w + 1]).
+struct B3Item {
+  uint32_t dp;
+  uint32_t rb;
+};
+// Activation preparation of one product: x [m][k] FP16 -> x5 (slot order)
+// and, if xs is not NULL, FP32 group sums xs [m][k/group]; m <= 4.
+struct B3Prep {
+  const uint16_t* x;
+  uint16_t* x5;
+  float* xs;
+  int32_t k, m;
+};
+// Instructions (4-slot chunks) per group: 33 at group 128, 16 at group 64;
+// groups per 208-byte stage: 8 and 16.
+int b3_chunks_per_group(int group);
+int b3_stage_groups(int group);
+// preps (device) holds count preparations; with preps == NULL, `one` alone.
+hipError_t launch_b3_prep(int group, const B3Prep* preps, int count, const B3Prep& one, hipStream_t stream);
+// nwg workgroups.  With descs (device) the items and wbeg tables drive the
+// wavefronts; with descs == NULL every wavefront w takes items w, w + W, ...
+// (W = nwg * kB3Waves) below one_items of the single descriptor `one`
+// (item = K part * row_blocks + row block).  mt: 1, 2 or 4 rows per pass.
+hipError_t launch_gemv_b3(int group, int mt, const GemvDesc* descs, const B3Item* items, const uint32_t* wbeg, int nwg,
+                          const GemvDesc& one, int one_items, hipStream_t stream);
 
 // ---- MFMA product (gemm.hip)
 hipError_t launch_gemm(const GemvDesc& d, int format, hipStream_t stream);

@@ -45,4 +45,16 @@ __device__ __forceinline__ bool last_part(uint32_t* ctr, int splits) {
   return last_flag != 0u;
 }
 
+// The same for a single wavefront that owns a whole work item (no workgroup
+// barrier): true in every lane of the wavefront that adds the parts.
+__device__ __forceinline__ bool last_part_wave(uint32_t* ctr, int splits, int lane) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // this wavefront's part stores are acknowledged
+  uint32_t before = 0u;
+  if (lane == 0) before = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  before = __shfl(before, 0, 64);
+  const bool last = before + 1u == (uint32_t)splits;
+  if (last && lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last;
+}
+
 }  // namespace tern

@@ -247,6 +247,12 @@ struct tern_plan {
   int aw, np;             // its activation tile (aw * 64 rows) and residual planes
   const tern::RedDesc* red;  // small: split sums to reduce (device), their count and blocks
   int nred, red_blocks;
+  bool b3;                // base-3 matrix-core decode: preparations, item lists and workgroups
+  const tern::B3Prep* preps;
+  int nprep;
+  const tern::B3Item* b3items;
+  const uint32_t* wbeg;
+  int nwg;
 };
 
 extern "C" {
@@ -259,12 +265,22 @@ extern "C" {
 // 128/256-row matrix-core tiles from m = 33.
 static bool gemm_route(int m) { return m >= 33; }
 static bool small_route(int format, int group, int m) {
-  const int decode_max = format == TERN_FMT_B3 ? 2 : (group == 128 ? 5 : 4);
+  const int decode_max = format == TERN_FMT_B3 ? 4 : (group == 128 ? 5 : 4);
   return !gemm_route(m) && m > decode_max;
+}
+// Base-3 products with up to 4 activation rows run on the base-3 matrix-core
+// decode (one pass covers 4 rows at the cost of one).
+static bool b3_route(int format, int group, int m) {
+  return format == TERN_FMT_B3 && product_group_ok(group) && m >= 1 && m <= 4;
 }
 
 // Workspace of a small-m product batch (defined with the batch builder).
 static size_t small_batch_ws_bytes(const tern_matrix* w, int32_t count, int32_t m);
+// Single base-3 product at m <= 4 (defined with the base-3 batch builder).
+static void b3_single_layout(const tern_matrix* w, int m, int* parts, int* sps, size_t* x5_off, size_t* xs_off,
+                             size_t* total);
+static tern_status b3_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* y, int32_t y_dtype, void* ws,
+                           size_t ws_bytes, hipStream_t s);
 
 size_t tern_row_stride(int32_t k, int32_t group, int32_t format) {
   if (k < 0 || group <= 0 || k % 64 || group % 64 || group > 1024 || k % group) return 0;
@@ -299,7 +315,12 @@ tern_status tern_packed_sizes(int32_t n, int32_t k, int32_t group, int32_t forma
 size_t tern_workspace_bytes(const tern_matrix* w, int32_t m) {
   if (!w || check_shape(w->n, w->k, w->group, w->planes, w->format, w->offset_mode) != TERN_OK) return 0;
   const size_t packing = kFlagBytes + round_up(((size_t)w->n + 1) * 4, 256);
-  const size_t product = m > 0 && small_route(w->format, w->group, m) ? small_batch_ws_bytes(w, 1, m) : gemv_ws_bytes(w, m);
+  size_t product = m > 0 && small_route(w->format, w->group, m) ? small_batch_ws_bytes(w, 1, m) : gemv_ws_bytes(w, m);
+  if (b3_route(w->format, w->group, m) && w->n > 0 && w->k > 0) {
+    int parts, sps;
+    size_t x5_off, xs_off;
+    b3_single_layout(w, m, &parts, &sps, &x5_off, &xs_off, &product);
+  }
   return std::max(packing, product);
 }
 
@@ -401,6 +422,7 @@ tern_status tern_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* 
     void* yp = y;
     return tern_gemv_batched(w, &x, &yp, 1, m, y_dtype, ws, ws_bytes, stream);
   }
+  if (b3_route(w->format, w->group, m)) return b3_gemv(w, x, m, y, y_dtype, ws, ws_bytes, s);
   const int cmax = max_mt(w->format, w->group);
   int splits, gps;
   choose_splits(w, pick_mt(std::min(m, cmax)), &splits, &gps);
@@ -1092,9 +1114,254 @@ static bool plan_indexes(const tern_matrix* w) {
 }
 static size_t index_bytes(const tern_matrix* w) { return plan_indexes(w) ? round_up((size_t)w->nnz[0] * 4, 256) : 0; }
 
+// ---- base-3 matrix-core decode batches (m <= 4)
+// Workspace layout: [descriptors][activation preparations][wavefront item
+// ranges][items][partials of K-split products][arrival counters][x5 of each
+// product][group sums of x for products with an offset].  Every wavefront of
+// the persistent launch (kB3Waves per CU) gets a list of (product, 64-row
+// block, K part) items, packed largest first onto the least loaded
+// wavefront; a product is cut into K parts of whole 208-byte stages only
+// when the launch would otherwise hold under two stages per wavefront.
+struct B3Batch {
+  std::vector<GemvDesc> descs;
+  std::vector<tern::B3Prep> preps;
+  std::vector<tern::B3Item> items;
+  std::vector<uint32_t> wbeg;
+  size_t descs_off = 0, preps_off = 0, wbeg_off = 0, items_off = 0, part_off = 0, ctr_off = 0, total = 0;
+  size_t nctr = 0;
+  int mt = 1, nwg = 0;
+};
+
+static size_t b3_x5_bytes(const tern_matrix* w, int m) {
+  return round_up((size_t)m * (w->k / w->group) * tern::b3_chunks_per_group(w->group) * 8, 256);
+}
+static size_t b3_xs_bytes(const tern_matrix* w, int m) {
+  return w->offset_mode != TERN_OFF_NONE ? round_up((size_t)m * (w->k / w->group) * 4, 256) : 0;
+}
+// 208-byte stages of a row and the stages per K part of every product.
+static int b3_stages(const tern_matrix* w) {
+  const int sg = tern::b3_stage_groups(w->group);
+  return (w->k / w->group + sg - 1) / sg;
+}
+
+// Builds the batch (items only when `items` is true); ws may be NULL (sizes only).
+static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y, int32_t count,
+                                  int32_t m, int32_t y_dtype, char* ws, bool items, B3Batch* b) {
+  if (count < 0) return fail(TERN_E_INVAL, "count=%d is negative", count);
+  if (count > 0 && !w) return fail(TERN_E_INVAL, "NULL descriptor array");
+  if (items && count > 0 && (!x || !y)) return fail(TERN_E_INVAL, "NULL activation or output arrays");
+  if (m < 1 || m > 4) return fail(TERN_E_UNSUPPORTED, "the base-3 decode takes 1..4 activation rows (m=%d)", m);
+  if (y_dtype != TERN_F16 && y_dtype != TERN_F32) return fail(TERN_E_UNSUPPORTED, "unknown y dtype %d", y_dtype);
+  b->mt = pick_mt(m);
+  std::vector<int> order;
+  for (int i = 0; i < count; ++i) {
+    TERN_TRY(check_matrix(&w[i]));
+    if (w[i].format != TERN_FMT_B3 || w[i].group != w[0].group)
+      return fail(TERN_E_UNSUPPORTED, "batched products must share format and group");
+    if (!product_group_ok(w[i].group)) return fail(TERN_E_UNSUPPORTED, "products support group 64 or 128");
+    if (w[i].n == 0) continue;
+    if (w[i].k == 0) return fail(TERN_E_UNSUPPORTED, "batched products need k > 0");
+    if (items) TERN_TRY(check_xy(x[i], y[i], y_dtype));
+    order.push_back(i);
+  }
+  const int cus = tern_cu_count();
+  const long waves = (long)cus * tern::kB3Waves;
+  // stages per K part: at most half the average stages per wavefront
+  long units = 0;
+  for (int i : order) units += (long)((w[i].n + tern::kGemvRows - 1) / tern::kGemvRows) * b3_stages(&w[i]);
+  const int target = (int)std::max(1L, units / (2 * waves));
+  std::vector<int> sps(count, 1), parts(count, 1);
+  for (int i : order) {
+    const int nst = b3_stages(&w[i]);
+    sps[i] = std::min(nst, target);
+    parts[i] = (nst + sps[i] - 1) / sps[i];
+  }
+  // layout
+  const size_t nd = order.size();
+  b->descs_off = 0;
+  b->preps_off = round_up(nd * sizeof(GemvDesc), 256);
+  b->wbeg_off = b->preps_off + round_up(nd * sizeof(tern::B3Prep), 256);
+  b->nwg = nd ? cus : 0;
+  b->items_off = b->wbeg_off + round_up(((size_t)waves + 1) * 4, 256);
+  size_t nitems = 0, partial = 0, nctr = 0;
+  for (int i : order) {
+    const size_t rb = (size_t)(w[i].n + tern::kGemvRows - 1) / tern::kGemvRows;
+    nitems += rb * parts[i];
+    if (parts[i] > 1) {
+      partial += round_up((size_t)parts[i] * m * w[i].n * 4, 256);
+      nctr += rb;
+    }
+  }
+  b->part_off = b->items_off + round_up(nitems * sizeof(tern::B3Item), 256);
+  b->ctr_off = b->part_off + partial;
+  b->nctr = nctr;
+  size_t off = b->ctr_off + round_up(nctr * 4, 256);
+  std::vector<size_t> x5_off(count, 0), xs_off(count, 0);
+  for (int i : order) {
+    x5_off[i] = off;
+    off += b3_x5_bytes(&w[i], m);
+  }
+  for (int i : order) {
+    xs_off[i] = off;
+    off += b3_xs_bytes(&w[i], m);
+  }
+  b->total = off;
+  b->descs.clear();
+  b->preps.clear();
+  b->items.clear();
+  b->wbeg.clear();
+  if (!items) return TERN_OK;
+
+  // descriptors and preparations
+  const size_t esz = y_dtype == TERN_F32 ? 4 : 2;
+  (void)esz;
+  size_t poff = 0, coff = 0;
+  for (int i : order) {
+    GemvDesc d;
+    fill_desc(d, &w[i], x[i], m, y[i], y_dtype == TERN_F32);
+    d.splits = parts[i];
+    d.gps = sps[i];
+    d.x5 = ws ? reinterpret_cast<const uint16_t*>(ws + x5_off[i]) : nullptr;
+    d.xs = ws && w[i].offset_mode != TERN_OFF_NONE ? reinterpret_cast<const float*>(ws + xs_off[i]) : nullptr;
+    if (parts[i] > 1) {
+      d.partial = ws ? reinterpret_cast<float*>(ws + b->part_off + poff) : nullptr;
+      d.ctr = ws ? reinterpret_cast<uint32_t*>(ws + b->ctr_off) + coff : nullptr;
+      poff += round_up((size_t)parts[i] * m * w[i].n * 4, 256);
+      coff += (size_t)d.row_blocks;
+    }
+    b->descs.push_back(d);
+    tern::B3Prep pr;
+    pr.x = x[i];
+    pr.x5 = const_cast<uint16_t*>(d.x5);
+    pr.xs = const_cast<float*>(d.xs);
+    pr.k = w[i].k;
+    pr.m = m;
+    b->preps.push_back(pr);
+  }
+  // items, largest first onto the least loaded wavefront
+  struct It {
+    uint32_t dp, rb;
+    int cost;
+  };
+  std::vector<It> all;
+  all.reserve(nitems);
+  for (size_t di = 0; di < nd; ++di) {
+    const GemvDesc& d = b->descs[di];
+    const int nst = (d.ng + tern::b3_stage_groups(d.group) - 1) / tern::b3_stage_groups(d.group);
+    for (int pt = 0; pt < d.splits; ++pt) {
+      const int st = std::min(nst, (pt + 1) * d.gps) - pt * d.gps;
+      for (int rb = 0; rb < d.row_blocks; ++rb) {
+        const int rows = std::min(tern::kGemvRows, d.n - rb * tern::kGemvRows);
+        all.push_back({(uint32_t)(di << 16 | (uint32_t)pt), (uint32_t)rb, st * 64 + rows});
+      }
+    }
+  }
+  if (nd > 65535) return fail(TERN_E_UNSUPPORTED, "a batch takes at most 65535 products");
+  std::stable_sort(all.begin(), all.end(), [](const It& a, const It& c) { return a.cost > c.cost; });
+  typedef std::pair<long, int> Load;
+  std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+  for (int wv = 0; wv < (int)waves; ++wv) heap.push({0L, wv});
+  std::vector<std::vector<uint32_t>> lists(waves);
+  for (size_t t = 0; t < all.size(); ++t) {
+    Load l = heap.top();
+    heap.pop();
+    lists[l.second].push_back((uint32_t)t);
+    l.first += all[t].cost;
+    heap.push(l);
+  }
+  b->wbeg.assign((size_t)waves + 1, 0u);
+  b->items.reserve(all.size());
+  for (long wv = 0; wv < waves; ++wv) {
+    b->wbeg[wv] = (uint32_t)b->items.size();
+    for (uint32_t t : lists[wv]) b->items.push_back({all[t].dp, all[t].rb});
+  }
+  b->wbeg[waves] = (uint32_t)b->items.size();
+  return TERN_OK;
+}
+
+// Copies a built batch's tables into ws (asynchronously on s, or synchronously
+// when s is NULL and sync is true) and clears its counters.
+static tern_status upload_b3_batch(const B3Batch& b, char* ws, hipStream_t s, bool sync) {
+  auto cp = [&](size_t off, const void* src, size_t bytes) -> hipError_t {
+    if (!bytes) return hipSuccess;
+    return sync ? hipMemcpy(ws + off, src, bytes, hipMemcpyHostToDevice)
+                : hipMemcpyAsync(ws + off, src, bytes, hipMemcpyHostToDevice, s);
+  };
+  TERN_HIP(cp(b.descs_off, b.descs.data(), b.descs.size() * sizeof(GemvDesc)));
+  TERN_HIP(cp(b.preps_off, b.preps.data(), b.preps.size() * sizeof(tern::B3Prep)));
+  TERN_HIP(cp(b.wbeg_off, b.wbeg.data(), b.wbeg.size() * 4));
+  TERN_HIP(cp(b.items_off, b.items.data(), b.items.size() * sizeof(tern::B3Item)));
+  if (b.nctr) TERN_HIP(sync ? hipMemset(ws + b.ctr_off, 0, b.nctr * 4) : hipMemsetAsync(ws + b.ctr_off, 0, b.nctr * 4, s));
+  return TERN_OK;
+}
+
+static tern_status run_b3_batch(const B3Batch& b, int group, char* ws, hipStream_t s) {
+  if (b.descs.empty()) return TERN_OK;
+  tern::B3Prep none;
+  std::memset(&none, 0, sizeof(none));
+  GemvDesc dummy;
+  std::memset(&dummy, 0, sizeof(dummy));
+  TERN_HIP(tern::launch_b3_prep(group, reinterpret_cast<const tern::B3Prep*>(ws + b.preps_off), (int)b.preps.size(),
+                                none, s));
+  TERN_HIP(tern::launch_gemv_b3(group, b.mt, reinterpret_cast<const GemvDesc*>(ws + b.descs_off),
+                                reinterpret_cast<const tern::B3Item*>(ws + b.items_off),
+                                reinterpret_cast<const uint32_t*>(ws + b.wbeg_off), b.nwg, dummy, 0, s));
+  return TERN_OK;
+}
+
+// Single base-3 product at m <= 4 without host tables: every wavefront takes
+// items w, w + W, ... of the one descriptor; K parts (when the product is too
+// small to fill the GPU) write FP32 partials that a second kernel sums.
+// Workspace: [partials][x5][group sums].
+static void b3_single_layout(const tern_matrix* w, int m, int* parts, int* sps, size_t* x5_off, size_t* xs_off,
+                             size_t* total) {
+  const long waves = (long)tern_cu_count() * tern::kB3Waves;
+  const int rb = (w->n + tern::kGemvRows - 1) / tern::kGemvRows;
+  const int nst = b3_stages(w);
+  const int target = (int)std::max(1L, (long)rb * nst / (2 * waves));
+  *sps = std::min(nst, target);
+  *parts = (nst + *sps - 1) / *sps;
+  *x5_off = split_ws_bytes(*parts, m, w->n);
+  *xs_off = *x5_off + b3_x5_bytes(w, m);
+  *total = *xs_off + b3_xs_bytes(w, m);
+}
+
+static tern_status b3_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* y, int32_t y_dtype, void* ws,
+                           size_t ws_bytes, hipStream_t s) {
+  int parts, sps;
+  size_t x5_off, xs_off, total;
+  b3_single_layout(w, m, &parts, &sps, &x5_off, &xs_off, &total);
+  if (!ws || ws_bytes < total) return fail(TERN_E_WORKSPACE, "tern_gemv needs %zu workspace bytes", total);
+  TERN_TRY(check_dev(ws, true, "ws"));
+  char* base = static_cast<char*>(ws);
+  GemvDesc d;
+  fill_desc(d, w, x, m, y, y_dtype == TERN_F32);
+  d.splits = parts;
+  d.gps = sps;
+  d.x5 = reinterpret_cast<const uint16_t*>(base + x5_off);
+  d.xs = w->offset_mode != TERN_OFF_NONE ? reinterpret_cast<const float*>(base + xs_off) : nullptr;
+  if (parts > 1) d.partial = reinterpret_cast<float*>(base);
+  tern::B3Prep pr;
+  pr.x = x;
+  pr.x5 = const_cast<uint16_t*>(d.x5);
+  pr.xs = const_cast<float*>(d.xs);
+  pr.k = w->k;
+  pr.m = m;
+  TERN_HIP(tern::launch_b3_prep(w->group, nullptr, 1, pr, s));
+  const int items = d.row_blocks * parts;
+  const int nwg = std::min(tern_cu_count(), (items + tern::kB3Waves - 1) / tern::kB3Waves);
+  TERN_HIP(tern::launch_gemv_b3(w->group, pick_mt(m), nullptr, nullptr, nullptr, nwg, d, items, s));
+  if (parts > 1) TERN_HIP(tern::launch_splitk_reduce(d.partial, parts, m, w->n, y, y_dtype == TERN_F32, s));
+  return TERN_OK;
+}
+
 size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m) {
   if (count <= 0 || m <= 0 || !w) return 0;
   if (gemm_route(m)) return gemm_batch_ws_bytes(w, count, m);
+  if (b3_route(w[0].format, w[0].group, m)) {
+    B3Batch b;
+    return build_b3_batch(w, nullptr, nullptr, count, m, TERN_F16, nullptr, false, &b) == TERN_OK ? b.total : 0;
+  }
   if (small_route(w[0].format, w[0].group, m)) return small_batch_ws_bytes(w, count, m);
   const int cmax = max_mt(w[0].format, w[0].group);
   const int mtp = pick_mt(std::min(m, cmax));
@@ -1160,6 +1427,16 @@ tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, vo
       TERN_HIP(tern::launch_reduce_grouped(reinterpret_cast<const tern::RedDesc*>(base + tb + b.partial_bytes),
                                            (int)b.red.size(), b.red_blocks, s));
     return TERN_OK;
+  }
+  if (count > 0 && b3_route(w[0].format, w[0].group, m)) {
+    B3Batch b;
+    TERN_TRY(build_b3_batch(w, x, y, count, m, y_dtype, static_cast<char*>(ws), true, &b));
+    if (b.descs.empty()) return TERN_OK;
+    if (!ws || ws_bytes < b.total) return fail(TERN_E_WORKSPACE, "batched product needs %zu workspace bytes", b.total);
+    TERN_TRY(check_dev(ws, true, "ws"));
+    hipStream_t s = (hipStream_t)stream;
+    TERN_TRY(upload_b3_batch(b, static_cast<char*>(ws), s, false));
+    return run_b3_batch(b, w[0].group, static_cast<char*>(ws), s);
   }
   if (count > 0 && small_route(w[0].format, w[0].group, m)) {
     if (!ws) return fail(TERN_E_WORKSPACE, "batched product needs a workspace");
@@ -1233,6 +1510,7 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
     }
     tern_plan* p = static_cast<tern_plan*>(std::malloc(sizeof(tern_plan)));
     if (!p) return fail(TERN_E_INVAL, "out of host memory");
+  std::memset(p, 0, sizeof(*p));
     p->dev = reinterpret_cast<const GemvDesc*>(base);
     p->recs = nullptr;
     p->ndesc = (int)b.tiles.size();
@@ -1249,6 +1527,33 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
     p->red = b.red.empty() ? nullptr : reinterpret_cast<const tern::RedDesc*>(base + tb + b.partial_bytes);
     p->nred = (int)b.red.size();
     p->red_blocks = b.red_blocks;
+    *out = p;
+    return TERN_OK;
+  }
+  if (count > 0 && b3_route(w[0].format, w[0].group, m)) {
+    B3Batch b;
+    TERN_TRY(build_b3_batch(w, x, y, count, m, y_dtype, static_cast<char*>(ws), true, &b));
+    char* base = static_cast<char*>(ws);
+    if (!b.descs.empty()) {
+      if (!ws || ws_bytes < b.total) return fail(TERN_E_WORKSPACE, "plan needs %zu workspace bytes", b.total);
+      TERN_TRY(check_dev(ws, true, "ws"));
+      TERN_TRY(upload_b3_batch(b, base, nullptr, true));
+    }
+    tern_plan* p = static_cast<tern_plan*>(std::malloc(sizeof(tern_plan)));
+    if (!p) return fail(TERN_E_INVAL, "out of host memory");
+    std::memset(p, 0, sizeof(*p));
+    p->format = w[0].format;
+    p->group = w[0].group;
+    p->mt = b.mt;
+    p->total_items = (int)b.items.size();
+    p->b3 = true;
+    p->dev = reinterpret_cast<const GemvDesc*>(base + b.descs_off);
+    p->ndesc = (int)b.descs.size();
+    p->preps = reinterpret_cast<const tern::B3Prep*>(base + b.preps_off);
+    p->nprep = (int)b.preps.size();
+    p->b3items = reinterpret_cast<const tern::B3Item*>(base + b.items_off);
+    p->wbeg = reinterpret_cast<const uint32_t*>(base + b.wbeg_off);
+    p->nwg = b.nwg;
     *out = p;
     return TERN_OK;
   }
@@ -1269,6 +1574,7 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
     }
     tern_plan* p = static_cast<tern_plan*>(std::malloc(sizeof(tern_plan)));
     if (!p) return fail(TERN_E_INVAL, "out of host memory");
+  std::memset(p, 0, sizeof(*p));
     p->dev = reinterpret_cast<const GemvDesc*>(base);
     p->recs = nullptr;
     p->ndesc = (int)b.tiles.size();
@@ -1325,10 +1631,12 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
       TERN_HIP(tern::launch_tile_bounds(reinterpret_cast<const GemvDesc*>(base),
                                         reinterpret_cast<tern::WgRec*>(base + sp.recs_off), (int)recs.size(), nullptr));
     }
-    TERN_HIP(hipDeviceSynchronize());
+    // the index kernels ran on the null stream; wait for them only
+    TERN_HIP(hipStreamSynchronize(nullptr));
   }
   tern_plan* p = static_cast<tern_plan*>(std::malloc(sizeof(tern_plan)));
   if (!p) return fail(TERN_E_INVAL, "out of host memory");
+  std::memset(p, 0, sizeof(*p));
   p->dev = reinterpret_cast<const GemvDesc*>(base);
   p->recs = recs.empty() ? nullptr : reinterpret_cast<const tern::WgRec*>(base + sp.recs_off);
   p->ndesc = (int)items.size();
@@ -1351,6 +1659,16 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
 tern_status tern_plan_run(const tern_plan* plan, void* stream) {
   if (!plan) return fail(TERN_E_INVAL, "plan is NULL");
   if (plan->total_items == 0) return TERN_OK;
+  if (plan->b3) {
+    tern::B3Prep none;
+    std::memset(&none, 0, sizeof(none));
+    GemvDesc dummy;
+    std::memset(&dummy, 0, sizeof(dummy));
+    TERN_HIP(tern::launch_b3_prep(plan->group, plan->preps, plan->nprep, none, (hipStream_t)stream));
+    TERN_HIP(tern::launch_gemv_b3(plan->group, plan->mt, plan->dev, plan->b3items, plan->wbeg, plan->nwg, dummy, 0,
+                                  (hipStream_t)stream));
+    return TERN_OK;
+  }
   if (plan->gemm) {
     TERN_HIP(tern::launch_gemm_grouped(plan->dev, plan->total_items, plan->format, plan->group, plan->aw, plan->np,
                                        (hipStream_t)stream));

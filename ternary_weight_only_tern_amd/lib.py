@@ -257,7 +257,12 @@ class Plan:
         self.m = xs[0].shape[0] if xs else 0
         descs, xp, yp = _arrays(mats, xs, ys)
         nbytes = load().tern_batch_workspace_bytes(descs, len(mats), self.m)
-        self.ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=xs[0].device)
+        # tern_plan_create writes every table and clears its counters itself
+        # (synchronously, on the null stream): no fill is queued here, and the
+        # caller's queued work on its inputs is finished first
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=xs[0].device)
+        if xs:
+            torch.cuda.current_stream(xs[0].device).synchronize()
         self._keep = (mats, xs, ys)
         handle = c_void_p()
         check(load().tern_plan_create(descs, xp, yp, len(mats), self.m, y_dtype, _ptr(self.ws),
