@@ -13,7 +13,8 @@ check_quantization(w, mask_bits, group, trits, scales, offset) verifies:
         output's own trits, to half an FP16 unit in the last place plus an
         FP32 solve margin;
   (iii) signs: every non-zero trit has the error-minimizing sign given that
-        fit, except at near-ties;
+        fit, except at near-ties (with no refinement iteration: the sign the
+        threshold rule gives);
   (iv)  error: the per-group squared error of the output is at most
         (1 + 1e-3) times that of the fp64 oracle's own quantization (both with
         FP16-rounded values), plus a tiny absolute term.
@@ -79,16 +80,23 @@ def check_quantization(w, mask_bits, group, trits, scales, offset, iters=15):
         bad = np.abs(got - ref) > tol
         assert not bad.any(), f"{name} off the least-squares fit at groups {np.argwhere(bad)[:5].ravel().tolist()}"
 
-    # (iii) signs given that fit (plane 0, then plane 1 with plane 0 as output)
+    # (iii) signs: with no refinement (iters == 0) they are the threshold
+    # rule's (the sign of r, then of the residual); otherwise error-minimizing
+    # given that fit (plane 0, then plane 1 with plane 0 as output)
+    if iters == 0:
+        i0, i1 = Q.initial_supports(W, masked)
+        assert np.array_equal(np.where(sup0, t0, 0), np.where(sup0, i0, 0)), "plane-0 signs off the threshold rule"
+        on1 = sup1 & (i1 != 0)
+        assert np.array_equal(np.where(on1, t1, 0), np.where(on1, i1, 0)), "plane-1 signs off the threshold rule"
     e0 = W - fm[:, None] - f1[:, None] * t1
     g0 = f0[:, None] * e0
     tie0 = np.abs(g0) <= TIE_MARGIN * (f0[:, None] ** 2 + np.abs(g0).max(axis=1, keepdims=True) * 1e-3) + 1e-30
-    bad_s0 = sup0 & (t0 != np.where(g0 < 0, -1, 1)) & ~tie0
+    bad_s0 = sup0 & (t0 != np.where(g0 < 0, -1, 1)) & ~tie0 & (iters > 0)
     assert not bad_s0.any(), f"plane-0 sign not error-minimizing at {np.argwhere(bad_s0)[:5].tolist()}"
     e1 = W - fm[:, None] - f0[:, None] * t0
     g1 = f1[:, None] * e1
     tie1 = np.abs(g1) <= TIE_MARGIN * (f1[:, None] ** 2 + np.abs(g1).max(axis=1, keepdims=True) * 1e-3) + 1e-30
-    bad_s1 = sup1 & (t1 != np.where(g1 < 0, -1, 1)) & ~tie1
+    bad_s1 = sup1 & (t1 != np.where(g1 < 0, -1, 1)) & ~tie1 & (iters > 0)
     assert not bad_s1.any(), f"plane-1 sign not error-minimizing at {np.argwhere(bad_s1)[:5].tolist()}"
 
     # (iv) error against the fp64 oracle's own quantization (both FP16-rounded)
