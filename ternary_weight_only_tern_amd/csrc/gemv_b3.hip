@@ -60,10 +60,10 @@ constexpr int kStageLds = kGemvRows * kStageBytes;
 #ifndef TERN_B3_AUX
 #define TERN_B3_AUX 0   // cache policy of the weight stream loads
 #endif
-#ifndef TERN_B3_LUT_COPIES
-#define TERN_B3_LUT_COPIES 8
-#endif
-constexpr int kLutCopies = TERN_B3_LUT_COPIES;
+// 16 copies of each 16-byte entry fill a 256-byte table row: the 16 lanes an
+// LDS cycle serves read distinct banks whatever their byte values, and the
+// entry address is the byte value in bits 8..15 (one byte permute).
+constexpr int kLutCopies = 16;
 constexpr int kLutStride = 16 * kLutCopies;
 constexpr int kLutBytes = 256 * kLutStride;
 constexpr int kB3Lds = kLutBytes + kB3Waves * kStageLds;
@@ -121,31 +121,44 @@ __device__ __forceinline__ int x5_pos(int c, int h) {
   return pos >= 0 && pos < G ? pos : -1;
 }
 
-// One block per (product, activation row): x5 chunks of the row and, when
-// asked for, the FP32 sums of every group (in position order).
+// x5 chunks and, when asked for, FP32 group sums of one activation row of
+// one product: blockIdx.y = product * 4 + activation row, blockIdx.x = a
+// block of 256 chunks (one per thread; group sums by the threads of block 0,
+// one group each, in position order).
 template <int G>
 __global__ __launch_bounds__(256) void b3_prep_kernel(const B3Prep* __restrict__ preps, B3Prep one) {
   using Gm = B3Geo<G>;
-  const B3Prep p = preps ? preps[blockIdx.x / 4] : one;
-  const int m = blockIdx.x % 4;
+  const B3Prep p = preps ? preps[blockIdx.y / 4] : one;
+  const int m = blockIdx.y % 4;
   if (m >= p.m) return;
   const int ng = p.k / G;
   const uint16_t* xr = p.x + (size_t)m * p.k;
-  uint16_t* o = p.x5 + (size_t)m * ng * Gm::CPG * 4;
-  for (int c = threadIdx.x; c < ng * Gm::CPG; c += 256) {
+  const int c = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  if (c < ng * Gm::CPG) {
     const int g = c / Gm::CPG, cc = c % Gm::CPG;
     uint32_t v[2];
+#pragma unroll
     for (int hp = 0; hp < 2; ++hp) {
       const int p0 = x5_pos<G>(cc, 2 * hp), p1 = x5_pos<G>(cc, 2 * hp + 1);
       const uint32_t a = p0 >= 0 ? xr[g * G + p0] : 0u, b = p1 >= 0 ? xr[g * G + p1] : 0u;
       v[hp] = a | (b << 16);
     }
-    *reinterpret_cast<u2_t*>(o + (size_t)c * 4) = u2_t{v[0], v[1]};
+    *reinterpret_cast<u2_t*>(p.x5 + ((size_t)m * ng * Gm::CPG + c) * 4) = u2_t{v[0], v[1]};
   }
-  if (p.xs) {
+  if (p.xs && blockIdx.x == 0) {
     for (int g = threadIdx.x; g < ng; g += 256) {
+      const u4_t* xg = reinterpret_cast<const u4_t*>(xr + (size_t)g * G);
+      u4_t w[G / 8];
+#pragma unroll
+      for (int i = 0; i < G / 8; ++i) w[i] = xg[i];
       float s = 0.f;
-      for (int i = 0; i < G; ++i) s += h2f(xr[g * G + i]);
+#pragma unroll
+      for (int i = 0; i < G / 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s += h2f((uint16_t)(w[i][j] & 0xFFFFu));
+          s += h2f((uint16_t)(w[i][j] >> 16));
+        }
       p.xs[(size_t)m * ng + g] = s;
     }
   }
@@ -158,19 +171,35 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint8_t* ds
 }
 
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }      // vmcnt(0)
+template <int N>
+__device__ __forceinline__ void wait_vm() {  // vmcnt(N), N <= 63
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }    // lgkmcnt(0)
 
-// The table entry of byte o (0..207) of this lane's stage row W.
-__device__ __forceinline__ u4_t lut_at(const uint8_t* lut_lane, const uint32_t (&W)[kStageBytes / 4], int o) {
-  const uint32_t v = (W[o >> 2] >> (8 * (o & 3))) & 0xFFu;
-  return *reinterpret_cast<const u4_t*>(lut_lane + v * kLutStride);
+// The table entry of byte o (0..207) of this lane's stage row W; coff is
+// the lane's copy offset (16 * (lane % 16)) and the table starts at LDS 0.
+__device__ __forceinline__ u4_t lut_at(const uint8_t* lds, uint32_t coff, const uint32_t (&W)[kStageBytes / 4], int o) {
+  // address = coff | byte << 8: byte 0 from coff, byte 1 from W's byte o % 4
+  const uint32_t a = __builtin_amdgcn_perm(W[o >> 2], coff, 0x0C0C0000u | ((4u + (uint32_t)(o & 3)) << 8));
+  return *reinterpret_cast<const u4_t*>(lds + a);
 }
 
+// Activation chunks of a stage (A operands) and where the next stage's come
+// from: register u holds chunks 16u .. 16u+15 and is refilled with the next
+// stage's register u right after its last instruction of this stage.
 template <int G>
 struct StageRegs {
-  u2_t a[B3Geo<G>::AREG];   // activation chunks (A operands)
-  u4_t sc[B3Geo<G>::SCW];   // FP16 group scales of the lane's row
+  u2_t a[B3Geo<G>::AREG];
+  __amdgpu_buffer_rsrc_t rx;   // the product's x5
+  uint32_t next;               // byte offset of the lane's next-stage register 0
 };
+
+template <int G>
+__device__ __forceinline__ u2_t load_areg(const StageRegs<G>& R, uint32_t off) {
+  return __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(R.rx, off, 0, 0));
+}
 
 // Compile-time loop: f(integral_constant<int, I>) for I in [I0, N).
 template <int I, int N, typename F>
@@ -190,8 +219,8 @@ __device__ __forceinline__ f4_t mfma_chunk(const u2_t* a, u2_t b, f4_t acc) {
 // Group Gi of the stage: its 26 (13) bytes through the table and the matrix
 // cores, then the row's group scale onto the FP32 accumulators.
 template <int G, int MT, int Gi>
-__device__ __forceinline__ void b3_group(const uint8_t* lut_lane, const uint32_t (&W)[kStageBytes / 4],
-                                         const StageRegs<G>& R, float (&acc)[MT]) {
+__device__ __forceinline__ void b3_group(const uint8_t* lds, uint32_t coff, const uint32_t (&W)[kStageBytes / 4],
+                                         const StageRegs<G>& R, const u4_t (&SC)[B3Geo<G>::SCW], float (&acc)[MT]) {
   using Gm = B3Geo<G>;
   constexpr int o0 = Gi * Gm::GB;    // first byte of the group in the stage
   constexpr int t0 = Gi * Gm::CPG;   // first chunk of the group in the stage
@@ -200,7 +229,7 @@ __device__ __forceinline__ void b3_group(const uint8_t* lut_lane, const uint32_t
     constexpr int q = decltype(qc)::value;
     u4_t e[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) e[b] = lut_at(lut_lane, W, o0 + 4 * q + b);
+    for (int b = 0; b < 4; ++b) e[b] = lut_at(lds, coff, W, o0 + 4 * q + b);
     D0 = mfma_chunk<t0 + 5 * q + 0>(R.a, u2_t{e[0].x, e[0].y}, D0);
     D1 = mfma_chunk<t0 + 5 * q + 1>(R.a, u2_t{e[1].x, e[1].y}, D1);
     D0 = mfma_chunk<t0 + 5 * q + 2>(R.a, u2_t{e[2].x, e[2].y}, D0);
@@ -209,10 +238,10 @@ __device__ __forceinline__ void b3_group(const uint8_t* lut_lane, const uint32_t
   });
   if constexpr (Gm::T > 0) {
     constexpr int tt = t0 + 5 * Gm::Q;
-    const u4_t e0 = lut_at(lut_lane, W, o0 + 4 * Gm::Q);
+    const u4_t e0 = lut_at(lds, coff, W, o0 + 4 * Gm::Q);
     D1 = mfma_chunk<tt>(R.a, u2_t{e0.x, e0.y}, D1);
     if constexpr (Gm::T == 2) {
-      const u4_t e1 = lut_at(lut_lane, W, o0 + 4 * Gm::Q + 1);
+      const u4_t e1 = lut_at(lds, coff, W, o0 + 4 * Gm::Q + 1);
       D0 = mfma_chunk<tt + 1>(R.a, u2_t{e1.x, e1.y}, D0);
       if constexpr (Gm::T4) D1 = mfma_chunk<tt + 2>(R.a, u2_t{e0.z | e1.w, 0u}, D1);
     } else {
@@ -220,13 +249,258 @@ __device__ __forceinline__ void b3_group(const uint8_t* lut_lane, const uint32_t
       if constexpr (Gm::T4) D0 = mfma_chunk<tt + 1>(R.a, u2_t{e0.z, 0u}, D0);
     }
   }
-  const uint32_t sw = R.sc[Gi / 8][(Gi % 8) / 2];
+  const uint32_t sw = SC[Gi / 8][(Gi % 8) / 2];
   const float s = h2f((uint16_t)(Gi % 2 ? sw >> 16 : sw & 0xFFFFu));
 #pragma unroll
   for (int i = 0; i < MT; ++i) acc[i] = fmaf(s, D0[i] + D1[i], acc[i]);
 }
 
+// A whole stage as one software pipeline of steps (a quad of bytes, or a
+// group's tail bytes): the table entries of step i + P are requested before
+// the instructions of step i, so P steps of LDS latency are in flight.
+#ifndef TERN_B3_DEPTH
+#define TERN_B3_DEPTH 2
+#endif
+template <int G>
+struct B3Steps {
+  using Gm = B3Geo<G>;
+  static constexpr int SPG = Gm::Q + (Gm::T > 0 ? 1 : 0);   // steps per group
+  static constexpr int NS = Gm::SG * SPG;                     // steps per stage
+};
+
+template <int G, int I>
+__device__ __forceinline__ void b3_load_step(const uint8_t* lds, uint32_t coff, const uint32_t (&W)[kStageBytes / 4], u4_t (&e)[4]) {
+  using Gm = B3Geo<G>;
+  constexpr int g = I / B3Steps<G>::SPG, r = I % B3Steps<G>::SPG;
+  constexpr int nb = r < Gm::Q ? 4 : Gm::T;
+  constexpr int o = g * Gm::GB + 4 * r;
+#pragma unroll
+  for (int b = 0; b < nb; ++b) e[b] = lut_at(lds, coff, W, o + b);
+}
+
+template <int G, int I>
+__device__ __forceinline__ void b3_mfma_step(const StageRegs<G>& R, const u4_t (&e)[4], f4_t& D0, f4_t& D1) {
+  using Gm = B3Geo<G>;
+  constexpr int g = I / B3Steps<G>::SPG, r = I % B3Steps<G>::SPG;
+  constexpr int t = g * Gm::CPG + 5 * r;   // first chunk of the step
+  if constexpr (r < Gm::Q) {
+    D0 = mfma_chunk<t + 0>(R.a, u2_t{e[0].x, e[0].y}, D0);
+    D1 = mfma_chunk<t + 1>(R.a, u2_t{e[1].x, e[1].y}, D1);
+    D0 = mfma_chunk<t + 2>(R.a, u2_t{e[2].x, e[2].y}, D0);
+    D1 = mfma_chunk<t + 3>(R.a, u2_t{e[3].x, e[3].y}, D1);
+    D0 = mfma_chunk<t + 4>(R.a, u2_t{e[0].z | e[1].w, e[2].z | e[3].w}, D0);
+  } else if constexpr (Gm::T == 2) {
+    D1 = mfma_chunk<t + 0>(R.a, u2_t{e[0].x, e[0].y}, D1);
+    D0 = mfma_chunk<t + 1>(R.a, u2_t{e[1].x, e[1].y}, D0);
+    if constexpr (Gm::T4) D1 = mfma_chunk<t + 2>(R.a, u2_t{e[0].z | e[1].w, 0u}, D1);
+  } else {
+    static_assert(Gm::T == 1, "tails of one or two bytes");
+    D1 = mfma_chunk<t + 0>(R.a, u2_t{e[0].x, e[0].y}, D1);
+    if constexpr (Gm::T4) D0 = mfma_chunk<t + 1>(R.a, u2_t{e[0].z, 0u}, D0);
+  }
+}
+
 template <int G, int MT>
+__device__ __forceinline__ void b3_stage_full(const uint8_t* lds, uint32_t coff, const uint32_t (&W)[kStageBytes / 4],
+                                              StageRegs<G>& R, const u4_t (&SC)[B3Geo<G>::SCW], float (&acc)[MT]) {
+  using Gm = B3Geo<G>;
+  constexpr int P = TERN_B3_DEPTH;
+  constexpr int NS = B3Steps<G>::NS, SPG = B3Steps<G>::SPG;
+  u4_t E[P + 1][4];
+  f4_t D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
+  sfor<0, P>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i < NS) b3_load_step<G, i>(lds, coff, W, E[i % (P + 1)]);
+  });
+  sfor<0, NS>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i + P < NS) b3_load_step<G, i + P>(lds, coff, W, E[(i + P) % (P + 1)]);
+    b3_mfma_step<G, i>(R, E[i % (P + 1)], D0, D1);
+    // chunks [tf, tl] of this step; refill the registers whose last chunk is among them
+    constexpr int g = i / SPG, r = i % SPG;
+    constexpr int tf = g * Gm::CPG + 5 * r;
+    constexpr int tl = r < Gm::Q ? tf + 4 : g * Gm::CPG + Gm::CPG - 1;
+    sfor<0, Gm::AREG>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      constexpr int last = 16 * u + 15 < Gm::CPS ? 16 * u + 15 : Gm::CPS - 1;
+      if constexpr (last >= tf && last <= tl) R.a[u] = load_areg(R, R.next + 128u * u);
+    });
+    if constexpr (r == SPG - 1) {
+      const uint32_t sw = SC[g / 8][(g % 8) / 2];
+      const float sc = h2f((uint16_t)(g % 2 ? sw >> 16 : sw & 0xFFFFu));
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[m] = fmaf(sc, D0[m] + D1[m], acc[m]);
+      D0 = f4_t{0.f, 0.f, 0.f, 0.f};
+      D1 = f4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  });
+}
+
+// Residual pass: the residual planes and the offset of kB3ResRows rows of
+// one product, summed in FP32 into its rsum before the plane-0 product runs
+// (which adds them when it writes y).  The activations are staged in LDS a
+// window of groups at a time, each group padded by 16 bytes (lanes that read
+// different groups then use different banks); entries (one per thread) are
+// decoded from their 2-bit blocks and multiplied against them; each row's
+// thread then adds its entries' values in entry order, window by window, so
+// the sum is in (row, group) order.  Offsets use FP32 group sums of x taken
+// from the staged windows.  Runs with several workgroups per CU, so the
+// latency of its gathers hides behind other workgroups.
+constexpr int kResThreads = kB3ResRows;
+constexpr int kResMaxWindow = 32768;  // activation window bytes, at most
+constexpr int kResPer = 4;            // entries per thread and chunk
+constexpr int kResChunk = kResPer * kResThreads;
+
+// Window of a launch whose longest product has max_k inputs: all of it when
+// it fits, else the most whole groups that do.
+template <int G, int MT>
+constexpr int res_window(int max_k) {
+  return (max_k / G) * MT * (2 * G + 16) <= kResMaxWindow ? (max_k / G) * MT * (2 * G + 16)
+                                                           : kResMaxWindow / (MT * (2 * G + 16)) * MT * (2 * G + 16);
+}
+template <int G, int MT>
+constexpr int res_lds_bytes(int max_k) { return res_window<G, MT>(max_k) + kResChunk * MT * 4 + MT * (max_k / G) * 4; }
+
+// TABLE: units and descriptors from device tables; else the row blocks of
+// `one` (a compile-time choice: a descriptor chosen at run time between a
+// table and the argument would be copied to scratch memory)
+template <int G, int MT, bool TABLE>
+__global__ __launch_bounds__(kResThreads) void b3_res_kernel(const GemvDesc* __restrict__ descs,
+                                                             const B3ResItem* __restrict__ units, GemvDesc one,
+                                                             int window) {
+  constexpr int GP = 2 * G + 16;
+  constexpr int CPGX = 2 * G / 16;
+  extern __shared__ uint4 res_smem[];
+  uint8_t* xw = reinterpret_cast<uint8_t*>(res_smem);
+  float* vals = reinterpret_cast<float*>(xw + window);
+  GemvDesc d;
+  int rb;
+  if constexpr (TABLE) {
+    const B3ResItem u = units[blockIdx.x];
+    d = descs[u.desc];
+    rb = (int)u.rb;
+  } else {
+    d = one;
+    rb = (int)blockIdx.x;
+  }
+  float* xsum = vals + kResChunk * MT;
+  const int tid = threadIdx.x;
+  const int r0 = rb * kB3ResRows;
+  const int rlast = min(r0 + kB3ResRows, d.n);
+  const int row = r0 + tid;
+  const bool row_ok = row < rlast;
+  float acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = 0.f;
+  const int wgn = min(d.ng, window / (MT * GP));
+  for (int wg0 = 0; wg0 < d.ng; wg0 += wgn) {
+    const int wg1 = min(d.ng, wg0 + wgn), wn = wg1 - wg0;
+    __syncthreads();  // the previous window is no longer read
+    for (int c = tid; c < MT * wn * CPGX; c += kResThreads) {
+      const int m = c / (wn * CPGX), rem = c % (wn * CPGX);
+      const int gl = rem / CPGX, j = rem % CPGX;
+      *reinterpret_cast<u4_t*>(xw + (m * wgn + gl) * GP + 16 * j) =
+          *reinterpret_cast<const GLOBAL u4_t*>(gp(d.x) + (size_t)min(m, d.m - 1) * d.k + (size_t)(wg0 + gl) * G + j * 8);
+    }
+    __syncthreads();
+    if (d.offset_mode != 0) {  // group sums of x, in position order
+      for (int c = tid; c < MT * wn; c += kResThreads) {
+        const int m = c / wn, gl = c % wn;
+        const uint32_t* xg = reinterpret_cast<const uint32_t*>(xw + (m * wgn + gl) * GP);
+        float sx = 0.f;
+        for (int i = 0; i < G / 2; ++i) {
+          sx += h2f((uint16_t)(xg[i] & 0xFFFFu));
+          sx += h2f((uint16_t)(xg[i] >> 16));
+        }
+        xsum[m * d.ng + wg0 + gl] = sx;
+      }
+    }
+    for (int p = 0; p + 1 < d.planes; ++p) {
+      // (selects, not indexing with p: the descriptor stays in registers)
+      const GLOBAL uint32_t* rowptr = gp(p == 0 ? d.rowptr[0] : d.rowptr[1]);
+      const uint32_t E0 = rowptr[r0], E1 = rowptr[rlast];
+      const uint32_t rp_lo = row_ok ? rowptr[row] : 0u, rp_hi = row_ok ? rowptr[row + 1] : 0u;
+      const GLOBAL uint32_t* gidx = gp(p == 0 ? d.gidx[0] : d.gidx[1]);
+      const GLOBAL u4_t* blocks = reinterpret_cast<const GLOBAL u4_t*>(gp(p == 0 ? d.blocks[0] : d.blocks[1]));
+      for (uint32_t c0 = E0; c0 < E1; c0 += kResChunk) {
+        const uint32_t c1 = min(E1, c0 + (uint32_t)kResChunk);
+        // every load of the thread's entries first, then the arithmetic
+        uint32_t gi[kResPer];
+        u4_t bv[kResPer][G / 64];
+#pragma unroll
+        for (int r = 0; r < kResPer; ++r) {
+          const uint32_t e = c0 + (uint32_t)(tid + r * kResThreads);
+          gi[r] = e < c1 ? gidx[e] : 0xFFFFu;
+#pragma unroll
+          for (int q = 0; q < G / 64; ++q)
+            bv[r][q] = e < c1 ? __builtin_nontemporal_load(blocks + (size_t)e * (G / 64) + q) : u4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int r = 0; r < kResPer; ++r) {
+          const int g = (int)(gi[r] & 0xFFFFu);
+          float part[MT];
+#pragma unroll
+          for (int m = 0; m < MT; ++m) part[m] = 0.f;
+          if (g >= wg0 && g < wg1) {
+#pragma unroll
+            for (int q = 0; q < G / 64; ++q) {
+              const uint32_t ws[4] = {bv[r][q].x, bv[r][q].y, bv[r][q].z, bv[r][q].w};
+#pragma unroll
+              for (int m = 0; m < MT; ++m) {
+                const uint8_t* xg = xw + (m * wgn + (g - wg0)) * GP + q * 128;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                  const u4_t x0 = *reinterpret_cast<const u4_t*>(xg + 32 * u);
+                  const u4_t x1 = *reinterpret_cast<const u4_t*>(xg + 32 * u + 16);
+                  const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+                  for (int i = 0; i < 8; ++i) part[m] = dot2(pair_of(ws[u], 14 - 2 * i), xs[i], part[m]);
+                }
+              }
+            }
+            const float rs = 0.5f * h2f((uint16_t)(gi[r] >> 16));
+#pragma unroll
+            for (int m = 0; m < MT; ++m) part[m] *= rs;
+          }
+          const uint32_t e = c0 + (uint32_t)(tid + r * kResThreads);
+          if (e < c1) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) vals[(e - c0) * MT + m] = part[m];
+          }
+        }
+        __syncthreads();
+        // this row's entries of the chunk, in entry order (entries outside
+        // the window add an exact zero)
+        const uint32_t lo = max(rp_lo, c0), hi = min(rp_hi, c1);
+        for (uint32_t e = lo; e < hi; ++e)
+#pragma unroll
+          for (int m = 0; m < MT; ++m) acc[m] += vals[(e - c0) * MT + m];
+        __syncthreads();
+      }
+    }
+  }
+  __syncthreads();  // the group sums are complete
+  if (!row_ok) return;
+  if (d.offset_mode != 0) {
+    const GLOBAL uint16_t* off = gp(d.offset);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (d.offset_mode == 1) {
+        float sx = 0.f;
+        for (int g = 0; g < d.ng; ++g) sx += xsum[m * d.ng + g];
+        acc[m] = fmaf(h2f(off[row]), sx, acc[m]);
+      } else {
+        for (int g = 0; g < d.ng; ++g) acc[m] = fmaf(h2f(off[(size_t)row * d.ng + g]), xsum[m * d.ng + g], acc[m]);
+      }
+    }
+  }
+  float* rs = const_cast<float*>(d.rsum);
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+    if (m < d.m) rs[(size_t)m * d.n + row] = acc[m];
+}
+
+template <int G, int MT, bool TABLE>
 __global__ __launch_bounds__(kB3Threads) void gemv_b3_kernel(const GemvDesc* __restrict__ descs,
                                                              const B3Item* __restrict__ items,
                                                              const uint32_t* __restrict__ wbeg, GemvDesc one,
@@ -243,10 +517,10 @@ __global__ __launch_bounds__(kB3Threads) void gemv_b3_kernel(const GemvDesc* __r
   __syncthreads();
 
   uint8_t* buf = lds + kLutBytes + wave * kStageLds;
-  const uint8_t* lut_lane = lds + (lane % kLutCopies) * 16;
+  const uint32_t coff = (uint32_t)(lane % kLutCopies) * 16u;
   const int gw = (int)blockIdx.x * kB3Waves + wave;
   int it = gw, it_end = one_items, it_step = (int)gridDim.x * kB3Waves;
-  if (descs) {
+  if constexpr (TABLE) {
     it = (int)wbeg[gw];
     it_end = (int)wbeg[gw + 1];
     it_step = 1;
@@ -255,7 +529,7 @@ __global__ __launch_bounds__(kB3Threads) void gemv_b3_kernel(const GemvDesc* __r
   for (; it < it_end; it += it_step) {
     GemvDesc d;
     int rb, part;
-    if (descs) {
+    if constexpr (TABLE) {
       const B3Item e = items[it];
       d = descs[e.dp >> 16];
       part = (int)(e.dp & 0xFFFFu);
@@ -270,23 +544,34 @@ __global__ __launch_bounds__(kB3Threads) void gemv_b3_kernel(const GemvDesc* __r
     const bool row_ok = row < d.n;
     const int nst = (d.ng + Gm::SG - 1) / Gm::SG;
     const int s0 = part * d.gps, s1 = min(nst, s0 + d.gps);
-    const int ga = s0 * Gm::SG, gb = min(d.ng, s1 * Gm::SG);
+    const int gb = min(d.ng, s1 * Gm::SG);
+    // the residual planes' and offset's sums of the lane's row (residual
+    // pass), requested before the stream so that no later wait holds on it
+    float rres[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      rres[m] = d.rsum && row_ok ? d.rsum[(size_t)min(m, d.m - 1) * d.n + row] : 0.f;
 
     const __amdgpu_buffer_rsrc_t rw = rsrc(d.plane0 + (size_t)row0 * d.stride, (size_t)(d.n - row0) * d.stride);
     const __amdgpu_buffer_rsrc_t rs = rsrc(d.scale0 + (size_t)row0 * d.ng, (size_t)(d.n - row0) * d.ng * 2);
     const size_t x5row = (size_t)d.ng * Gm::CPG * 8;   // bytes per activation row of x5
     const __amdgpu_buffer_rsrc_t rx = rsrc(d.x5, x5row * d.m);
-    // the lane's share of a stage's loads: chunk 64 u + lane = (row, 16-byte column)
-    uint32_t voff[kStageChunks];
-#pragma unroll
-    for (int u = 0; u < kStageChunks; ++u) {
-      const int c = 64 * u + lane;
-      voff[u] = (uint32_t)(c / kStageChunks) * (uint32_t)d.stride + (uint32_t)(c % kStageChunks) * 16u;
-    }
     const uint32_t svoff = (uint32_t)lane * (uint32_t)d.ng * 2u;
     const uint32_t avoff = (uint32_t)min(lane % 4, d.m - 1) * (uint32_t)x5row + (uint32_t)(lane / 4) * 8u;
 
-    auto issue = [&](int s, StageRegs<G>& R) {
+    // the lane's share of a stage's loads: chunk 64 u + lane = (row, 16-byte
+    // column), computed per item (the opaque copy of the lane index keeps the
+    // compiler from holding the lane-only parts for the whole launch)
+    int lq = lane;
+    asm volatile("" : "+v"(lq));
+    uint32_t voff[kStageChunks];
+#pragma unroll
+    for (int u = 0; u < kStageChunks; ++u) {
+      const int c = 64 * u + lq;
+      voff[u] = (uint32_t)(c / kStageChunks) * (uint32_t)d.stride + (uint32_t)(c % kStageChunks) * 16u;
+    }
+    // stage s into the LDS buffer and its scales into SC
+    auto issue = [&](int s, u4_t (&SC)[Gm::SCW]) {
 #pragma unroll
       for (int u = 0; u < kStageChunks; ++u) lds_load16(rw, buf + 1024 * u, voff[u] + (uint32_t)s * kStageBytes);
       // scales: 16-byte loads when every row's scales start on a dword (an
@@ -295,7 +580,7 @@ __global__ __launch_bounds__(kB3Threads) void gemv_b3_kernel(const GemvDesc* __r
       if ((d.ng & 1) == 0) {
 #pragma unroll
         for (int w = 0; w < Gm::SCW; ++w)
-          R.sc[w] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, svoff + (uint32_t)(s * Gm::SG) * 2u + 16u * w, 0, 0));
+          SC[w] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, svoff + (uint32_t)(s * Gm::SG) * 2u + 16u * w, 0, 0));
       } else {
 #pragma unroll
         for (int w = 0; w < Gm::SCW; ++w) {
@@ -303,20 +588,22 @@ __global__ __launch_bounds__(kB3Threads) void gemv_b3_kernel(const GemvDesc* __r
 #pragma unroll
           for (int j = 0; j < 8; ++j)
             h[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, svoff + (uint32_t)(s * Gm::SG + 8 * w + j) * 2u, 0, 0);
-          R.sc[w] = u4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+          SC[w] = u4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
         }
       }
-#pragma unroll
-      for (int u = 0; u < Gm::AREG; ++u)
-        R.a[u] = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(rx, avoff + (uint32_t)(s * Gm::CPS) * 8u + 128u * u, 0, 0));
     };
 
     float acc[MT];
 #pragma unroll
     for (int i = 0; i < MT; ++i) acc[i] = 0.f;
 
-    auto body = [&](int s, StageRegs<G>& Rc, StageRegs<G>& Rn) {
-      wait_vm0();    // stage s is in LDS; its scales and activations are in Rc
+    StageRegs<G> R;
+    R.rx = rx;
+    auto body = [&](int s, const u4_t (&SCc)[Gm::SCW], u4_t (&SCn)[Gm::SCW]) {
+      // stage s is in LDS and its scales have arrived: everything but the
+      // AREG activation loads issued after them (this stage's registers,
+      // which the compiler waits for at their first use)
+      wait_vm<Gm::AREG>();
       wave_sync();
       uint32_t W[kStageBytes / 4];
 #pragma unroll
@@ -326,55 +613,40 @@ __global__ __launch_bounds__(kB3Threads) void gemv_b3_kernel(const GemvDesc* __r
       }
       wait_lgkm0();  // the buffer is free for the next stage
       wave_sync();
-      if (s + 1 < s1) issue(s + 1, Rn);
+      if (s + 1 < s1) issue(s + 1, SCn);
+      R.next = avoff + (uint32_t)((s + 1) * Gm::CPS) * 8u;
       const int gs = s * Gm::SG;
-      sfor<0, Gm::SG>([&](auto gc) {
-        constexpr int g = decltype(gc)::value;
-        if (gs + g < gb) b3_group<G, MT, g>(lut_lane, W, Rc, acc);
-      });
+      if (gs + Gm::SG <= gb) {
+        b3_stage_full<G, MT>(lds, coff, W, R, SCc, acc);
+      } else {  // the row's last, partial stage (no next stage)
+        sfor<0, Gm::SG>([&](auto gc) {
+          constexpr int g = decltype(gc)::value;
+          if (gs + g < gb) b3_group<G, MT, g>(lds, coff, W, R, SCc, acc);
+        });
+      }
     };
 
     if (s0 < s1) {
-      StageRegs<G> RA, RB;
+      u4_t SA[Gm::SCW], SB[Gm::SCW];
       wait_lgkm0();
       wave_sync();
-      issue(s0, RA);
+      issue(s0, SA);
+#pragma unroll
+      for (int u = 0; u < Gm::AREG; ++u) R.a[u] = load_areg(R, avoff + (uint32_t)(s0 * Gm::CPS) * 8u + 128u * u);
       int s = s0;
       for (; s + 1 < s1; s += 2) {
-        body(s, RA, RB);
-        body(s + 1, RB, RA);
+        body(s, SA, SB);
+        body(s + 1, SB, SA);
       }
-      if (s < s1) body(s, RA, RB);
+      if (s < s1) body(s, SA, SB);
     }
 
-    // ---- residual planes and offsets over the item's groups [ga, gb)
-    const GLOBAL uint32_t* xr[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) xr[m] = reinterpret_cast<const GLOBAL uint32_t*>(gp(d.x) + (size_t)min(m, d.m - 1) * d.k);
-    if (gb > ga) {
-      if (d.planes > 1) residual_compact<G, MT>(d, 0, row, row_ok, ga, gb, xr, buf, kStageLds, acc);
-      if (d.planes > 2) residual_compact<G, MT>(d, 1, row, row_ok, ga, gb, xr, buf, kStageLds, acc);
-      if (d.offset_mode != 0 && row_ok) {
-        const GLOBAL uint16_t* off = gp(d.offset);
-        const GLOBAL float* xs = gp(d.xs);
-        if (d.offset_mode == 1) {
-          const float o = h2f(off[row]);
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            float sx = 0.f;
-            for (int g = ga; g < gb; ++g) sx += xs[(size_t)min(m, d.m - 1) * d.ng + g];
-            acc[m] = fmaf(o, sx, acc[m]);
-          }
-        } else {
-          for (int g = ga; g < gb; ++g) {
-            const float o = h2f(off[(size_t)row * d.ng + g]);
-#pragma unroll
-            for (int m = 0; m < MT; ++m) acc[m] = fmaf(o, xs[(size_t)min(m, d.m - 1) * d.ng + g], acc[m]);
-          }
-        }
-      }
-    }
     wave_sync();
+    // the residual sums join the first K part (or the whole row)
+    if (part == 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[m] += rres[m];
+    }
 
     // ---- output, or this part's partial sums (summed by the row block's last part)
     if (d.splits > 1) {
@@ -408,8 +680,12 @@ __global__ __launch_bounds__(kB3Threads) void gemv_b3_kernel(const GemvDesc* __r
 template <int G, int MT>
 hipError_t launch_b3_mt(const GemvDesc* descs, const B3Item* items, const uint32_t* wbeg, int nwg, const GemvDesc& one,
                         int one_items, hipStream_t s) {
-  hipLaunchKernelGGL((gemv_b3_kernel<G, MT>), dim3(nwg), dim3(kB3Threads), 0, s, descs, items, wbeg, one,
-                     one_items);
+  if (descs)
+    hipLaunchKernelGGL((gemv_b3_kernel<G, MT, true>), dim3(nwg), dim3(kB3Threads), 0, s, descs, items, wbeg, one,
+                       one_items);
+  else
+    hipLaunchKernelGGL((gemv_b3_kernel<G, MT, false>), dim3(nwg), dim3(kB3Threads), 0, s, descs, items, wbeg, one,
+                       one_items);
   return hipGetLastError();
 }
 
@@ -424,16 +700,50 @@ hipError_t launch_b3_g(int mt, const GemvDesc* descs, const B3Item* items, const
   }
 }
 
+template <int G, int MT>
+hipError_t launch_res_mt(const GemvDesc* descs, const B3ResItem* units, int nunits, const GemvDesc& one, int max_k,
+                         hipStream_t s) {
+  const size_t lds = (size_t)res_lds_bytes<G, MT>(max_k);
+  if (units)
+    hipLaunchKernelGGL((b3_res_kernel<G, MT, true>), dim3(nunits), dim3(kResThreads), lds, s, descs, units, one,
+                       res_window<G, MT>(max_k));
+  else
+    hipLaunchKernelGGL((b3_res_kernel<G, MT, false>), dim3(nunits), dim3(kResThreads), lds, s, descs, units, one,
+                       res_window<G, MT>(max_k));
+  return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_res_g(int mt, const GemvDesc* descs, const B3ResItem* units, int nunits, const GemvDesc& one,
+                        int max_k, hipStream_t s) {
+  switch (mt) {
+    case 1: return launch_res_mt<G, 1>(descs, units, nunits, one, max_k, s);
+    case 2: return launch_res_mt<G, 2>(descs, units, nunits, one, max_k, s);
+    case 4: return launch_res_mt<G, 4>(descs, units, nunits, one, max_k, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_b3_res(int group, int mt, const GemvDesc* descs, const B3ResItem* units, int nunits,
+                         const GemvDesc& one, int max_k, hipStream_t s) {
+  if (nunits <= 0) return hipSuccess;
+  if (group == 64) return launch_res_g<64>(mt, descs, units, nunits, one, max_k, s);
+  if (group == 128) return launch_res_g<128>(mt, descs, units, nunits, one, max_k, s);
+  return hipErrorInvalidValue;
+}
 
 int b3_chunks_per_group(int group) { return group == 64 ? B3Geo<64>::CPG : B3Geo<128>::CPG; }
 int b3_stage_groups(int group) { return group == 64 ? B3Geo<64>::SG : B3Geo<128>::SG; }
 
-hipError_t launch_b3_prep(int group, const B3Prep* preps, int count, const B3Prep& one, hipStream_t s) {
-  const int blocks = (preps ? count : 1) * 4;
-  if (blocks <= 0) return hipSuccess;
-  if (group == 64) hipLaunchKernelGGL(b3_prep_kernel<64>, dim3(blocks), dim3(256), 0, s, preps, one);
-  else if (group == 128) hipLaunchKernelGGL(b3_prep_kernel<128>, dim3(blocks), dim3(256), 0, s, preps, one);
+hipError_t launch_b3_prep(int group, const B3Prep* preps, int count, const B3Prep& one, int max_k, hipStream_t s) {
+  const int rows = (preps ? count : 1) * 4;
+  if (rows <= 0 || max_k <= 0) return hipSuccess;
+  const int chunks = max_k / group * b3_chunks_per_group(group);
+  const dim3 grid((unsigned)((chunks + 255) / 256), (unsigned)rows);
+  if (group == 64) hipLaunchKernelGGL(b3_prep_kernel<64>, grid, dim3(256), 0, s, preps, one);
+  else if (group == 128) hipLaunchKernelGGL(b3_prep_kernel<128>, grid, dim3(256), 0, s, preps, one);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

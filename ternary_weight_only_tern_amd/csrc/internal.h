@@ -56,9 +56,16 @@ struct GemvDesc {
   // Base-3 matrix-core decode: the activations in its slot order
   // ([m][ng][b3_chunks_per_group][4] FP16) and, with an offset, the FP32
   // group sums of x ([m][ng]); both prepared by launch_b3_prep.  There,
-  // splits counts K parts and gps is the 208-byte stages per part.
+  // the first p0 parts are K parts of plane 0 (gps 208-byte stages each)
+  // and, when splits > p0, part p0 adds the residual planes and the offset
+  // over the whole row; splits parts in all are summed in part order.
   const uint16_t* x5;
   const float* xs;
+  int32_t p0;
+  // Base-3 matrix-core decode: FP32 sums of the residual planes and the
+  // offset per output ([m][n]), written by launch_b3_res before the product
+  // and added to y by it; NULL when the matrix has neither.
+  const float* rsum;
 };
 
 // ---- decode products (gemv.hip)
@@ -118,7 +125,7 @@ hipError_t launch_tile_bounds(const GemvDesc* ranges, WgRec* recs, int count, hi
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 // ---- base-3 matrix-core decode (gemv_b3.hip), up to 4 activation rows
-constexpr int kB3Waves = 8;          // wavefronts per workgroup; one workgroup per CU
+constexpr int kB3Waves = 7;          // wavefronts per workgroup; one workgroup per CU (LDS)
 // Work item of a grouped launch: descriptor index << 16 | K part, and the
 // 64-row block.  Wavefront w of the launch (workgroup * kB3Waves + wave)
 // takes items [wbeg[w], wbeg[w + 1]).
@@ -138,8 +145,21 @@ struct B3Prep {
 // groups per 208-byte stage: 8 and 16.
 int b3_chunks_per_group(int group);
 int b3_stage_groups(int group);
-// preps (device) holds count preparations; with preps == NULL, `one` alone.
-hipError_t launch_b3_prep(int group, const B3Prep* preps, int count, const B3Prep& one, hipStream_t stream);
+// Residual pass work unit: descriptor index and block of kB3ResRows output
+// rows.  One workgroup per unit sums the residual planes and the offset of its
+// rows into the descriptor's rsum.
+constexpr int kB3ResRows = 256;
+struct B3ResItem {
+  uint32_t desc;
+  uint32_t rb;
+};
+// nunits workgroups over units (device), or with units == NULL the row blocks
+// of the single descriptor `one`.  max_k: the longest k.
+hipError_t launch_b3_res(int group, int mt, const GemvDesc* descs, const B3ResItem* units, int nunits,
+                         const GemvDesc& one, int max_k, hipStream_t stream);
+// preps (device) holds count preparations; with preps == NULL, `one` alone;
+// max_k: the longest k among them.
+hipError_t launch_b3_prep(int group, const B3Prep* preps, int count, const B3Prep& one, int max_k, hipStream_t stream);
 // nwg workgroups.  With descs (device) the items and wbeg tables drive the
 // wavefronts; with descs == NULL every wavefront w takes items w, w + W, ...
 // (W = nwg * kB3Waves) below one_items of the single descriptor `one`

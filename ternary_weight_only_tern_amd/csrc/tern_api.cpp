@@ -252,7 +252,9 @@ struct tern_plan {
   int nprep;
   const tern::B3Item* b3items;
   const uint32_t* wbeg;
-  int nwg;
+  int nwg, b3_maxk;
+  const tern::B3ResItem* b3res;  // residual pass units and their count
+  int nres;
 };
 
 extern "C" {
@@ -1122,27 +1124,39 @@ static size_t index_bytes(const tern_matrix* w) { return plan_indexes(w) ? round
 // block, K part) items, packed largest first onto the least loaded
 // wavefront; a product is cut into K parts of whole 208-byte stages only
 // when the launch would otherwise hold under two stages per wavefront.
+struct B3Index {  // residual index of one plane of one product (launch_res_index)
+  const uint32_t* mask;
+  const uint32_t* rowptr;
+  const uint16_t* rscale;
+  int n, mwords;
+  uint32_t* gidx;
+};
 struct B3Batch {
   std::vector<GemvDesc> descs;
+  std::vector<B3Index> index;
   std::vector<tern::B3Prep> preps;
   std::vector<tern::B3Item> items;
   std::vector<uint32_t> wbeg;
-  size_t descs_off = 0, preps_off = 0, wbeg_off = 0, items_off = 0, part_off = 0, ctr_off = 0, total = 0;
+  std::vector<tern::B3ResItem> res;  // residual pass units
+  size_t descs_off = 0, preps_off = 0, wbeg_off = 0, items_off = 0, part_off = 0, ctr_off = 0, res_off = 0, total = 0;
   size_t nctr = 0;
-  int mt = 1, nwg = 0;
+  int mt = 1, nwg = 0, max_k = 0;
 };
 
 static size_t b3_x5_bytes(const tern_matrix* w, int m) {
   return round_up((size_t)m * (w->k / w->group) * tern::b3_chunks_per_group(w->group) * 8, 256);
 }
-static size_t b3_xs_bytes(const tern_matrix* w, int m) {
-  return w->offset_mode != TERN_OFF_NONE ? round_up((size_t)m * (w->k / w->group) * 4, 256) : 0;
-}
-// 208-byte stages of a row and the stages per K part of every product.
+// 208-byte stages of a row.
 static int b3_stages(const tern_matrix* w) {
   const int sg = tern::b3_stage_groups(w->group);
   return (w->k / w->group + sg - 1) / sg;
 }
+// A product with residual planes or an offset goes through the residual pass.
+static bool b3_has_res(const tern_matrix* w) { return w->planes > 1 || w->offset_mode != TERN_OFF_NONE; }
+static size_t b3_rsum_bytes(const tern_matrix* w, int m) {
+  return b3_has_res(w) ? round_up((size_t)m * w->n * 4, 256) : 0;
+}
+static int b3_res_units(const tern_matrix* w) { return (w->n + tern::kB3ResRows - 1) / tern::kB3ResRows; }
 
 // Builds the batch (items only when `items` is true); ws may be NULL (sizes only).
 static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y, int32_t count,
@@ -1171,10 +1185,13 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
   for (int i : order) units += (long)((w[i].n + tern::kGemvRows - 1) / tern::kGemvRows) * b3_stages(&w[i]);
   const int target = (int)std::max(1L, units / (2 * waves));
   std::vector<int> sps(count, 1), parts(count, 1);
+  size_t nres = 0;
   for (int i : order) {
     const int nst = b3_stages(&w[i]);
     sps[i] = std::min(nst, target);
     parts[i] = (nst + sps[i] - 1) / sps[i];
+    b->max_k = std::max(b->max_k, w[i].k);
+    if (b3_has_res(&w[i])) nres += (size_t)b3_res_units(&w[i]);
   }
   // layout
   const size_t nd = order.size();
@@ -1192,7 +1209,8 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
       nctr += rb;
     }
   }
-  b->part_off = b->items_off + round_up(nitems * sizeof(tern::B3Item), 256);
+  b->res_off = b->items_off + round_up(nitems * sizeof(tern::B3Item), 256);
+  b->part_off = b->res_off + round_up(nres * sizeof(tern::B3ResItem), 256);
   b->ctr_off = b->part_off + partial;
   b->nctr = nctr;
   size_t off = b->ctr_off + round_up(nctr * 4, 256);
@@ -1202,11 +1220,20 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
     off += b3_x5_bytes(&w[i], m);
   }
   for (int i : order) {
-    xs_off[i] = off;
-    off += b3_xs_bytes(&w[i], m);
+    xs_off[i] = off;  // residual sums
+    off += b3_rsum_bytes(&w[i], m);
   }
+  // residual index per plane (entry -> group and scale)
+  std::vector<size_t> gi_off(2 * (size_t)count, 0);
+  for (int i : order)
+    for (int p = 0; p + 1 < w[i].planes; ++p) {
+      gi_off[2 * i + p] = off;
+      off += round_up((size_t)w[i].nnz[p] * 4, 256);
+    }
   b->total = off;
   b->descs.clear();
+  b->res.clear();
+  b->index.clear();
   b->preps.clear();
   b->items.clear();
   b->wbeg.clear();
@@ -1220,9 +1247,18 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
     GemvDesc d;
     fill_desc(d, &w[i], x[i], m, y[i], y_dtype == TERN_F32);
     d.splits = parts[i];
+    d.p0 = parts[i];
     d.gps = sps[i];
     d.x5 = ws ? reinterpret_cast<const uint16_t*>(ws + x5_off[i]) : nullptr;
-    d.xs = ws && w[i].offset_mode != TERN_OFF_NONE ? reinterpret_cast<const float*>(ws + xs_off[i]) : nullptr;
+    d.rsum = ws && b3_has_res(&w[i]) ? reinterpret_cast<const float*>(ws + xs_off[i]) : nullptr;
+    if (b3_has_res(&w[i]))
+      for (int u = 0; u < b3_res_units(&w[i]); ++u) b->res.push_back({(uint32_t)b->descs.size(), (uint32_t)u});
+    for (int p = 0; p + 1 < w[i].planes; ++p) {
+      uint32_t* gidx = ws ? reinterpret_cast<uint32_t*>(ws + gi_off[2 * i + p]) : nullptr;
+      d.gidx[p] = gidx;
+      if (w[i].nnz[p] > 0)
+        b->index.push_back({w[i].mask[p], w[i].rowptr[p], w[i].rscale[p], w[i].n, mask_words(w[i].k, w[i].group), gidx});
+    }
     if (parts[i] > 1) {
       d.partial = ws ? reinterpret_cast<float*>(ws + b->part_off + poff) : nullptr;
       d.ctr = ws ? reinterpret_cast<uint32_t*>(ws + b->ctr_off) + coff : nullptr;
@@ -1233,7 +1269,7 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
     tern::B3Prep pr;
     pr.x = x[i];
     pr.x5 = const_cast<uint16_t*>(d.x5);
-    pr.xs = const_cast<float*>(d.xs);
+    pr.xs = nullptr;
     pr.k = w[i].k;
     pr.m = m;
     b->preps.push_back(pr);
@@ -1252,7 +1288,8 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
       const int st = std::min(nst, (pt + 1) * d.gps) - pt * d.gps;
       for (int rb = 0; rb < d.row_blocks; ++rb) {
         const int rows = std::min(tern::kGemvRows, d.n - rb * tern::kGemvRows);
-        all.push_back({(uint32_t)(di << 16 | (uint32_t)pt), (uint32_t)rb, st * 64 + rows});
+        const int cost = st * 64 + rows;
+        all.push_back({(uint32_t)(di << 16 | (uint32_t)pt), (uint32_t)rb, cost});
       }
     }
   }
@@ -1291,7 +1328,11 @@ static tern_status upload_b3_batch(const B3Batch& b, char* ws, hipStream_t s, bo
   TERN_HIP(cp(b.preps_off, b.preps.data(), b.preps.size() * sizeof(tern::B3Prep)));
   TERN_HIP(cp(b.wbeg_off, b.wbeg.data(), b.wbeg.size() * 4));
   TERN_HIP(cp(b.items_off, b.items.data(), b.items.size() * sizeof(tern::B3Item)));
+  TERN_HIP(cp(b.res_off, b.res.data(), b.res.size() * sizeof(tern::B3ResItem)));
   if (b.nctr) TERN_HIP(sync ? hipMemset(ws + b.ctr_off, 0, b.nctr * 4) : hipMemsetAsync(ws + b.ctr_off, 0, b.nctr * 4, s));
+  for (const B3Index& ix : b.index)
+    TERN_HIP(tern::launch_res_index(ix.mask, ix.rowptr, ix.rscale, ix.n, ix.mwords, ix.gidx, sync ? nullptr : s));
+  if (sync && !b.index.empty()) TERN_HIP(hipStreamSynchronize(nullptr));
   return TERN_OK;
 }
 
@@ -1302,7 +1343,10 @@ static tern_status run_b3_batch(const B3Batch& b, int group, char* ws, hipStream
   GemvDesc dummy;
   std::memset(&dummy, 0, sizeof(dummy));
   TERN_HIP(tern::launch_b3_prep(group, reinterpret_cast<const tern::B3Prep*>(ws + b.preps_off), (int)b.preps.size(),
-                                none, s));
+                                none, b.max_k, s));
+  TERN_HIP(tern::launch_b3_res(group, b.mt, reinterpret_cast<const GemvDesc*>(ws + b.descs_off),
+                               reinterpret_cast<const tern::B3ResItem*>(ws + b.res_off), (int)b.res.size(), dummy,
+                               b.max_k, s));
   TERN_HIP(tern::launch_gemv_b3(group, b.mt, reinterpret_cast<const GemvDesc*>(ws + b.descs_off),
                                 reinterpret_cast<const tern::B3Item*>(ws + b.items_off),
                                 reinterpret_cast<const uint32_t*>(ws + b.wbeg_off), b.nwg, dummy, 0, s));
@@ -1322,8 +1366,9 @@ static void b3_single_layout(const tern_matrix* w, int m, int* parts, int* sps, 
   *sps = std::min(nst, target);
   *parts = (nst + *sps - 1) / *sps;
   *x5_off = split_ws_bytes(*parts, m, w->n);
-  *xs_off = *x5_off + b3_x5_bytes(w, m);
-  *total = *xs_off + b3_xs_bytes(w, m);
+  *xs_off = *x5_off + b3_x5_bytes(w, m);  // residual sums
+  *total = *xs_off + b3_rsum_bytes(w, m);
+  for (int p = 0; p + 1 < w->planes; ++p) *total += round_up((size_t)w->nnz[p] * 4, 256);  // residual index
 }
 
 static tern_status b3_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* y, int32_t y_dtype, void* ws,
@@ -1337,17 +1382,27 @@ static tern_status b3_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, v
   GemvDesc d;
   fill_desc(d, w, x, m, y, y_dtype == TERN_F32);
   d.splits = parts;
+  d.p0 = parts;
   d.gps = sps;
   d.x5 = reinterpret_cast<const uint16_t*>(base + x5_off);
-  d.xs = w->offset_mode != TERN_OFF_NONE ? reinterpret_cast<const float*>(base + xs_off) : nullptr;
+  d.rsum = b3_has_res(w) ? reinterpret_cast<const float*>(base + xs_off) : nullptr;
   if (parts > 1) d.partial = reinterpret_cast<float*>(base);
+  size_t gi = xs_off + b3_rsum_bytes(w, m);
+  for (int p = 0; p + 1 < w->planes; ++p) {
+    d.gidx[p] = reinterpret_cast<const uint32_t*>(base + gi);
+    if (w->nnz[p] > 0)
+      TERN_HIP(tern::launch_res_index(w->mask[p], w->rowptr[p], w->rscale[p], w->n, mask_words(w->k, w->group),
+                                      reinterpret_cast<uint32_t*>(base + gi), s));
+    gi += round_up((size_t)w->nnz[p] * 4, 256);
+  }
   tern::B3Prep pr;
   pr.x = x;
   pr.x5 = const_cast<uint16_t*>(d.x5);
-  pr.xs = const_cast<float*>(d.xs);
+  pr.xs = nullptr;
   pr.k = w->k;
   pr.m = m;
-  TERN_HIP(tern::launch_b3_prep(w->group, nullptr, 1, pr, s));
+  TERN_HIP(tern::launch_b3_prep(w->group, nullptr, 1, pr, w->k, s));
+  if (d.rsum) TERN_HIP(tern::launch_b3_res(w->group, pick_mt(m), nullptr, nullptr, b3_res_units(w), d, w->k, s));
   const int items = d.row_blocks * parts;
   const int nwg = std::min(tern_cu_count(), (items + tern::kB3Waves - 1) / tern::kB3Waves);
   TERN_HIP(tern::launch_gemv_b3(w->group, pick_mt(m), nullptr, nullptr, nullptr, nwg, d, items, s));
@@ -1552,6 +1607,9 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
     p->preps = reinterpret_cast<const tern::B3Prep*>(base + b.preps_off);
     p->nprep = (int)b.preps.size();
     p->b3items = reinterpret_cast<const tern::B3Item*>(base + b.items_off);
+    p->b3_maxk = b.max_k;
+    p->b3res = reinterpret_cast<const tern::B3ResItem*>(base + b.res_off);
+    p->nres = (int)b.res.size();
     p->wbeg = reinterpret_cast<const uint32_t*>(base + b.wbeg_off);
     p->nwg = b.nwg;
     *out = p;
@@ -1664,7 +1722,9 @@ tern_status tern_plan_run(const tern_plan* plan, void* stream) {
     std::memset(&none, 0, sizeof(none));
     GemvDesc dummy;
     std::memset(&dummy, 0, sizeof(dummy));
-    TERN_HIP(tern::launch_b3_prep(plan->group, plan->preps, plan->nprep, none, (hipStream_t)stream));
+    TERN_HIP(tern::launch_b3_prep(plan->group, plan->preps, plan->nprep, none, plan->b3_maxk, (hipStream_t)stream));
+    TERN_HIP(tern::launch_b3_res(plan->group, plan->mt, plan->dev, plan->b3res, plan->nres, dummy, plan->b3_maxk,
+                                 (hipStream_t)stream));
     TERN_HIP(tern::launch_gemv_b3(plan->group, plan->mt, plan->dev, plan->b3items, plan->wbeg, plan->nwg, dummy, 0,
                                   (hipStream_t)stream));
     return TERN_OK;
