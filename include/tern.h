@@ -212,6 +212,14 @@ tern_status tern_plan_create(const tern_matrix *w, const uint16_t *const *x, voi
                              int32_t count, int32_t m, int32_t y_dtype, void *ws,
                              size_t ws_bytes, tern_plan **out);
 tern_status tern_plan_run(const tern_plan *plan, void *stream);
+/* tern_plan_run that also records two caller-created HIP events (hipEvent_t;
+ * either may be NULL) on stream.  Base-3 plans at m <= 4: `before` behind
+ * the launches that prepare the main decode's inputs (the activation layout
+ * and the residual pass), `after` behind the main decode; the time between
+ * them is that kernel's duration.  Other plans: the two bracket the whole
+ * run.  A measurement hook; a run with events must not be captured in a
+ * graph. */
+tern_status tern_plan_run_events(const tern_plan *plan, void *stream, void *before, void *after);
 void tern_plan_destroy(tern_plan *plan);
 
 /* Bits per weight of a packed matrix (2609.01962 §3.2, §7.1: effective bits

@@ -350,6 +350,7 @@ constexpr int kResThreads = kB3ResRows;
 constexpr int kResMaxWindow = 32768;  // activation window bytes, at most
 constexpr int kResPer = 4;            // entries per thread and chunk
 constexpr int kResChunk = kResPer * kResThreads;
+constexpr int kResBatch = 4;          // activation loads per thread in flight while staging
 
 // Window of a launch whose longest product has max_k inputs: all of it when
 // it fits, else the most whole groups that do.
@@ -393,14 +394,56 @@ __global__ __launch_bounds__(kResThreads) void b3_res_kernel(const GemvDesc* __r
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0.f;
   const int wgn = min(d.ng, window / (MT * GP));
+
+  // a chunk of entries [c0, c1) of a plane: every load first (thread tid
+  // takes entries c0 + tid + r * kResThreads)
+  uint32_t gi[kResPer];
+  u4_t bv[kResPer][G / 64];
+  auto load_chunk = [&](const GLOBAL uint32_t* gidx, const GLOBAL u4_t* blocks, uint32_t c0, uint32_t c1) {
+#pragma unroll
+    for (int r = 0; r < kResPer; ++r) {
+      const uint32_t e = c0 + (uint32_t)(tid + r * kResThreads);
+      gi[r] = e < c1 ? gidx[e] : 0xFFFFu;
+#pragma unroll
+      for (int q = 0; q < G / 64; ++q)
+        bv[r][q] = e < c1 ? __builtin_nontemporal_load(blocks + (size_t)e * (G / 64) + q) : u4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  // the first chunk of the first plane is requested before the activations
+  // are staged, so that the two latencies overlap
+  bool prefetched = false;
+  if (d.planes > 1) {
+    const GLOBAL uint32_t* rowptr = gp(d.rowptr[0]);
+    const uint32_t E0 = rowptr[r0], E1 = rowptr[rlast];
+    if (E0 < E1) {
+      load_chunk(gp(d.gidx[0]), reinterpret_cast<const GLOBAL u4_t*>(gp(d.blocks[0])), E0,
+                 min(E1, E0 + (uint32_t)kResChunk));
+      prefetched = true;
+    }
+  }
+
   for (int wg0 = 0; wg0 < d.ng; wg0 += wgn) {
     const int wg1 = min(d.ng, wg0 + wgn), wn = wg1 - wg0;
     __syncthreads();  // the previous window is no longer read
-    for (int c = tid; c < MT * wn * CPGX; c += kResThreads) {
-      const int m = c / (wn * CPGX), rem = c % (wn * CPGX);
-      const int gl = rem / CPGX, j = rem % CPGX;
-      *reinterpret_cast<u4_t*>(xw + (m * wgn + gl) * GP + 16 * j) =
-          *reinterpret_cast<const GLOBAL u4_t*>(gp(d.x) + (size_t)min(m, d.m - 1) * d.k + (size_t)(wg0 + gl) * G + j * 8);
+    // stage the window: kResBatch loads per thread in flight, then the stores
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const GLOBAL uint8_t* xsrc =
+          reinterpret_cast<const GLOBAL uint8_t*>(gp(d.x)) + ((size_t)min(m, d.m - 1) * d.k + (size_t)wg0 * G) * 2;
+      const int total = wn * CPGX;
+      for (int cb = 0; cb < total; cb += kResThreads * kResBatch) {
+        u4_t v[kResBatch];
+#pragma unroll
+        for (int j = 0; j < kResBatch; ++j) {
+          const int c = cb + tid + j * kResThreads;
+          if (c < total) v[j] = *reinterpret_cast<const GLOBAL u4_t*>(xsrc + (size_t)c * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < kResBatch; ++j) {
+          const int c = cb + tid + j * kResThreads;
+          if (c < total) *reinterpret_cast<u4_t*>(xw + (m * wgn + c / CPGX) * GP + 16 * (c % CPGX)) = v[j];
+        }
+      }
     }
     __syncthreads();
     if (d.offset_mode != 0) {  // group sums of x, in position order
@@ -424,17 +467,8 @@ __global__ __launch_bounds__(kResThreads) void b3_res_kernel(const GemvDesc* __r
       const GLOBAL u4_t* blocks = reinterpret_cast<const GLOBAL u4_t*>(gp(p == 0 ? d.blocks[0] : d.blocks[1]));
       for (uint32_t c0 = E0; c0 < E1; c0 += kResChunk) {
         const uint32_t c1 = min(E1, c0 + (uint32_t)kResChunk);
-        // every load of the thread's entries first, then the arithmetic
-        uint32_t gi[kResPer];
-        u4_t bv[kResPer][G / 64];
-#pragma unroll
-        for (int r = 0; r < kResPer; ++r) {
-          const uint32_t e = c0 + (uint32_t)(tid + r * kResThreads);
-          gi[r] = e < c1 ? gidx[e] : 0xFFFFu;
-#pragma unroll
-          for (int q = 0; q < G / 64; ++q)
-            bv[r][q] = e < c1 ? __builtin_nontemporal_load(blocks + (size_t)e * (G / 64) + q) : u4_t{0u, 0u, 0u, 0u};
-        }
+        if (prefetched) prefetched = false;  // (the first chunk of plane 0 in the first window)
+        else load_chunk(gidx, blocks, c0, c1);
 #pragma unroll
         for (int r = 0; r < kResPer; ++r) {
           const int g = (int)(gi[r] & 0xFFFFu);
@@ -503,8 +537,8 @@ __global__ __launch_bounds__(kResThreads) void b3_res_kernel(const GemvDesc* __r
 template <int G, int MT, bool TABLE>
 __global__ __launch_bounds__(kB3Threads) void gemv_b3_kernel(const GemvDesc* __restrict__ descs,
                                                              const B3Item* __restrict__ items,
-                                                             const uint32_t* __restrict__ wbeg, GemvDesc one,
-                                                             int one_items) {
+                                                             uint32_t* __restrict__ queue, GemvDesc one,
+                                                             int nitems) {
   using Gm = B3Geo<G>;
   __shared__ uint4 b3_smem[kB3Lds / 16];
   uint8_t* lds = reinterpret_cast<uint8_t*>(b3_smem);
@@ -518,15 +552,27 @@ __global__ __launch_bounds__(kB3Threads) void gemv_b3_kernel(const GemvDesc* __r
 
   uint8_t* buf = lds + kLutBytes + wave * kStageLds;
   const uint32_t coff = (uint32_t)(lane % kLutCopies) * 16u;
-  const int gw = (int)blockIdx.x * kB3Waves + wave;
-  int it = gw, it_end = one_items, it_step = (int)gridDim.x * kB3Waves;
+  // Items.  With a table: one queue per XCD (workgroups are dealt to the
+  // XCDs in turn), each a list of items in decreasing cost; wavefront w of
+  // the queue's workgroups starts with its item w and takes further ones from
+  // the queue's counter, so that wavefronts that run faster (the older wave of
+  // a SIMD wins issue, CUs differ in speed) take more items.  Without a table
+  // wavefront w takes items w, w + W, ... of the one descriptor.
+  int gw = (int)blockIdx.x * kB3Waves + wave;
+  int nw = (int)gridDim.x * kB3Waves;
+  int ibeg = 0, iend = nitems;
+  uint32_t* qc = queue;
   if constexpr (TABLE) {
-    it = (int)wbeg[gw];
-    it_end = (int)wbeg[gw + 1];
-    it_step = 1;
+    const int q = (int)blockIdx.x % kB3Queues;
+    qc = queue + q * kB3QueueWords;
+    ibeg = (int)qc[2];
+    iend = (int)qc[3];
+    gw = ((int)blockIdx.x / kB3Queues) * kB3Waves + wave;
+    nw = (((int)gridDim.x - q + kB3Queues - 1) / kB3Queues) * kB3Waves;
   }
-
-  for (; it < it_end; it += it_step) {
+  int next = 0;
+  for (int it = ibeg + gw; it < iend; it = next) {
+    uint32_t qv = 0;
     GemvDesc d;
     int rb, part;
     if constexpr (TABLE) {
@@ -613,7 +659,14 @@ __global__ __launch_bounds__(kB3Threads) void gemv_b3_kernel(const GemvDesc* __r
       }
       wait_lgkm0();  // the buffer is free for the next stage
       wave_sync();
-      if (s + 1 < s1) issue(s + 1, SCn);
+      if (s + 1 < s1) {
+        issue(s + 1, SCn);
+      } else if constexpr (TABLE) {
+        // the next item, requested during the last stage: vector memory
+        // operations complete in order, so a request issued before a
+        // stage's loads would hold up the wait for them
+        if (lane == 0) qv = __hip_atomic_fetch_add(qc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       R.next = avoff + (uint32_t)((s + 1) * Gm::CPS) * 8u;
       const int gs = s * Gm::SG;
       if (gs + Gm::SG <= gb) {
@@ -639,9 +692,13 @@ __global__ __launch_bounds__(kB3Threads) void gemv_b3_kernel(const GemvDesc* __r
         body(s + 1, SB, SA);
       }
       if (s < s1) body(s, SA, SB);
+    } else if constexpr (TABLE) {
+      if (lane == 0) qv = __hip_atomic_fetch_add(qc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     wave_sync();
+    if constexpr (TABLE) next = ibeg + nw + (int)__builtin_amdgcn_readfirstlane(qv);
+    else next = it + nw;
     // the residual sums join the first K part (or the whole row)
     if (part == 0) {
 #pragma unroll
@@ -675,27 +732,38 @@ __global__ __launch_bounds__(kB3Threads) void gemv_b3_kernel(const GemvDesc* __r
       }
     }
   }
+  if constexpr (TABLE) {
+    // the last wavefront to finish (every fetch from the queue has returned
+    // by then) clears the queue for the next launch
+    if (lane == 0) {
+      const uint32_t done = __hip_atomic_fetch_add(qc + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (done == (uint32_t)nw - 1u) {
+        __hip_atomic_store(qc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(qc + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
 }
 
 template <int G, int MT>
-hipError_t launch_b3_mt(const GemvDesc* descs, const B3Item* items, const uint32_t* wbeg, int nwg, const GemvDesc& one,
-                        int one_items, hipStream_t s) {
+hipError_t launch_b3_mt(const GemvDesc* descs, const B3Item* items, uint32_t* queue, int nwg, const GemvDesc& one,
+                        int nitems, hipStream_t s) {
   if (descs)
-    hipLaunchKernelGGL((gemv_b3_kernel<G, MT, true>), dim3(nwg), dim3(kB3Threads), 0, s, descs, items, wbeg, one,
-                       one_items);
+    hipLaunchKernelGGL((gemv_b3_kernel<G, MT, true>), dim3(nwg), dim3(kB3Threads), 0, s, descs, items, queue, one,
+                       nitems);
   else
-    hipLaunchKernelGGL((gemv_b3_kernel<G, MT, false>), dim3(nwg), dim3(kB3Threads), 0, s, descs, items, wbeg, one,
-                       one_items);
+    hipLaunchKernelGGL((gemv_b3_kernel<G, MT, false>), dim3(nwg), dim3(kB3Threads), 0, s, descs, items, queue, one,
+                       nitems);
   return hipGetLastError();
 }
 
 template <int G>
-hipError_t launch_b3_g(int mt, const GemvDesc* descs, const B3Item* items, const uint32_t* wbeg, int nwg,
-                       const GemvDesc& one, int one_items, hipStream_t s) {
+hipError_t launch_b3_g(int mt, const GemvDesc* descs, const B3Item* items, uint32_t* queue, int nwg,
+                       const GemvDesc& one, int nitems, hipStream_t s) {
   switch (mt) {
-    case 1: return launch_b3_mt<G, 1>(descs, items, wbeg, nwg, one, one_items, s);
-    case 2: return launch_b3_mt<G, 2>(descs, items, wbeg, nwg, one, one_items, s);
-    case 4: return launch_b3_mt<G, 4>(descs, items, wbeg, nwg, one, one_items, s);
+    case 1: return launch_b3_mt<G, 1>(descs, items, queue, nwg, one, nitems, s);
+    case 2: return launch_b3_mt<G, 2>(descs, items, queue, nwg, one, nitems, s);
+    case 4: return launch_b3_mt<G, 4>(descs, items, queue, nwg, one, nitems, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -748,11 +816,11 @@ hipError_t launch_b3_prep(int group, const B3Prep* preps, int count, const B3Pre
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_b3(int group, int mt, const GemvDesc* descs, const B3Item* items, const uint32_t* wbeg, int nwg,
-                          const GemvDesc& one, int one_items, hipStream_t s) {
+hipError_t launch_gemv_b3(int group, int mt, const GemvDesc* descs, const B3Item* items, uint32_t* queue, int nwg,
+                          const GemvDesc& one, int nitems, hipStream_t s) {
   if (nwg <= 0) return hipSuccess;
-  if (group == 64) return launch_b3_g<64>(mt, descs, items, wbeg, nwg, one, one_items, s);
-  if (group == 128) return launch_b3_g<128>(mt, descs, items, wbeg, nwg, one, one_items, s);
+  if (group == 64) return launch_b3_g<64>(mt, descs, items, queue, nwg, one, nitems, s);
+  if (group == 128) return launch_b3_g<128>(mt, descs, items, queue, nwg, one, nitems, s);
   return hipErrorInvalidValue;
 }
 

@@ -127,8 +127,13 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipS
 // ---- base-3 matrix-core decode (gemv_b3.hip), up to 4 activation rows
 constexpr int kB3Waves = 7;          // wavefronts per workgroup; one workgroup per CU (LDS)
 // Work item of a grouped launch: descriptor index << 16 | K part, and the
-// 64-row block.  Wavefront w of the launch (workgroup * kB3Waves + wave)
-// takes items [wbeg[w], wbeg[w + 1]).
+// 64-row block.  The items are split into kB3Queues lists of about equal
+// cost, one per XCD (workgroup b serves list b % kB3Queues), each in
+// decreasing cost.  Queue q is the words [q * kB3QueueWords, + 4): the next
+// item beyond the first (taken from a counter), the finished wavefronts
+// (both zero between launches), and the list's first and end item.
+constexpr int kB3Queues = 8;
+constexpr int kB3QueueWords = 1024;  // 4 KB apart
 struct B3Item {
   uint32_t dp;
   uint32_t rb;
@@ -160,12 +165,14 @@ hipError_t launch_b3_res(int group, int mt, const GemvDesc* descs, const B3ResIt
 // preps (device) holds count preparations; with preps == NULL, `one` alone;
 // max_k: the longest k among them.
 hipError_t launch_b3_prep(int group, const B3Prep* preps, int count, const B3Prep& one, int max_k, hipStream_t stream);
-// nwg workgroups.  With descs (device) the items and wbeg tables drive the
-// wavefronts; with descs == NULL every wavefront w takes items w, w + W, ...
-// (W = nwg * kB3Waves) below one_items of the single descriptor `one`
-// (item = K part * row_blocks + row block).  mt: 1, 2 or 4 rows per pass.
-hipError_t launch_gemv_b3(int group, int mt, const GemvDesc* descs, const B3Item* items, const uint32_t* wbeg, int nwg,
-                          const GemvDesc& one, int one_items, hipStream_t stream);
+// nwg workgroups.  With descs (device), the items table and the queues
+// (kB3Queues * kB3QueueWords device words; the launch leaves the counters
+// zero) drive the wavefronts; with descs == NULL every wavefront w takes
+// items w, w + W, ... (W = nwg * kB3Waves) below nitems of the single
+// descriptor `one` (item = K part * row_blocks + row block).  mt: 1, 2 or 4
+// rows per pass.  Launches that share queues must not overlap.
+hipError_t launch_gemv_b3(int group, int mt, const GemvDesc* descs, const B3Item* items, uint32_t* queue, int nwg,
+                          const GemvDesc& one, int nitems, hipStream_t stream);
 
 // ---- MFMA product (gemm.hip)
 hipError_t launch_gemm(const GemvDesc& d, int format, hipStream_t stream);

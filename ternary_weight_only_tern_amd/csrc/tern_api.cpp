@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <queue>
+#include <map>
 #include <vector>
 
 #include "internal.h"
@@ -251,7 +252,7 @@ struct tern_plan {
   const tern::B3Prep* preps;
   int nprep;
   const tern::B3Item* b3items;
-  const uint32_t* wbeg;
+  uint32_t* queue;
   int nwg, b3_maxk;
   const tern::B3ResItem* b3res;  // residual pass units and their count
   int nres;
@@ -1117,13 +1118,14 @@ static bool plan_indexes(const tern_matrix* w) {
 static size_t index_bytes(const tern_matrix* w) { return plan_indexes(w) ? round_up((size_t)w->nnz[0] * 4, 256) : 0; }
 
 // ---- base-3 matrix-core decode batches (m <= 4)
-// Workspace layout: [descriptors][activation preparations][wavefront item
-// ranges][items][partials of K-split products][arrival counters][x5 of each
-// product][group sums of x for products with an offset].  Every wavefront of
-// the persistent launch (kB3Waves per CU) gets a list of (product, 64-row
-// block, K part) items, packed largest first onto the least loaded
-// wavefront; a product is cut into K parts of whole 208-byte stages only
-// when the launch would otherwise hold under two stages per wavefront.
+// Workspace layout: [descriptors][activation preparations][queue counters]
+// [items][residual pass units][partials of K-split products][arrival
+// counters][x5 of each distinct activation][residual sums][residual index].
+// The persistent launch (kB3Waves per CU) takes (product, 64-row block, K
+// part) items, largest first, from a queue; a product is cut into K parts of
+// whole 208-byte stages only when the launch would otherwise hold under two
+// stages per wavefront.  Products that read the same activations (the same
+// x pointer and k, as q/k/v or gate/up of a layer) share one x5.
 struct B3Index {  // residual index of one plane of one product (launch_res_index)
   const uint32_t* mask;
   const uint32_t* rowptr;
@@ -1136,9 +1138,9 @@ struct B3Batch {
   std::vector<B3Index> index;
   std::vector<tern::B3Prep> preps;
   std::vector<tern::B3Item> items;
-  std::vector<uint32_t> wbeg;
   std::vector<tern::B3ResItem> res;  // residual pass units
-  size_t descs_off = 0, preps_off = 0, wbeg_off = 0, items_off = 0, part_off = 0, ctr_off = 0, res_off = 0, total = 0;
+  std::vector<uint32_t> queues;      // kB3Queues * kB3QueueWords words
+  size_t descs_off = 0, preps_off = 0, queue_off = 0, items_off = 0, part_off = 0, ctr_off = 0, res_off = 0, total = 0;
   size_t nctr = 0;
   int mt = 1, nwg = 0, max_k = 0;
 };
@@ -1197,9 +1199,9 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
   const size_t nd = order.size();
   b->descs_off = 0;
   b->preps_off = round_up(nd * sizeof(GemvDesc), 256);
-  b->wbeg_off = b->preps_off + round_up(nd * sizeof(tern::B3Prep), 256);
-  b->nwg = nd ? cus : 0;
-  b->items_off = b->wbeg_off + round_up(((size_t)waves + 1) * 4, 256);
+  b->queue_off = b->preps_off + round_up(nd * sizeof(tern::B3Prep), 256);
+  b->nwg = nd ? std::max(cus, tern::kB3Queues) : 0;
+  b->items_off = b->queue_off + (size_t)tern::kB3Queues * tern::kB3QueueWords * 4;
   size_t nitems = 0, partial = 0, nctr = 0;
   for (int i : order) {
     const size_t rb = (size_t)(w[i].n + tern::kGemvRows - 1) / tern::kGemvRows;
@@ -1214,8 +1216,19 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
   b->ctr_off = b->part_off + partial;
   b->nctr = nctr;
   size_t off = b->ctr_off + round_up(nctr * 4, 256);
+  // x5 per distinct activation (without x, as for sizing, one per product)
   std::vector<size_t> x5_off(count, 0), xs_off(count, 0);
+  std::vector<bool> x5_own(count, true);
+  std::map<std::pair<const uint16_t*, int>, int> x5_first;
   for (int i : order) {
+    if (x) {
+      auto ins = x5_first.insert({{x[i], w[i].k}, i});
+      if (!ins.second) {
+        x5_off[i] = x5_off[ins.first->second];
+        x5_own[i] = false;
+        continue;
+      }
+    }
     x5_off[i] = off;
     off += b3_x5_bytes(&w[i], m);
   }
@@ -1236,7 +1249,6 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
   b->index.clear();
   b->preps.clear();
   b->items.clear();
-  b->wbeg.clear();
   if (!items) return TERN_OK;
 
   // descriptors and preparations
@@ -1266,6 +1278,7 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
       coff += (size_t)d.row_blocks;
     }
     b->descs.push_back(d);
+    if (!x5_own[i]) continue;
     tern::B3Prep pr;
     pr.x = x[i];
     pr.x5 = const_cast<uint16_t*>(d.x5);
@@ -1294,25 +1307,23 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
     }
   }
   if (nd > 65535) return fail(TERN_E_UNSUPPORTED, "a batch takes at most 65535 products");
+  // largest first onto the queue (XCD) of least cost; each list stays in
+  // decreasing cost, the order its wavefronts take them in
   std::stable_sort(all.begin(), all.end(), [](const It& a, const It& c) { return a.cost > c.cost; });
-  typedef std::pair<long, int> Load;
-  std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
-  for (int wv = 0; wv < (int)waves; ++wv) heap.push({0L, wv});
-  std::vector<std::vector<uint32_t>> lists(waves);
+  std::vector<std::vector<uint32_t>> lists(tern::kB3Queues);
+  std::vector<long> load(tern::kB3Queues, 0L);
   for (size_t t = 0; t < all.size(); ++t) {
-    Load l = heap.top();
-    heap.pop();
-    lists[l.second].push_back((uint32_t)t);
-    l.first += all[t].cost;
-    heap.push(l);
+    const int q = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    lists[q].push_back((uint32_t)t);
+    load[q] += all[t].cost;
   }
-  b->wbeg.assign((size_t)waves + 1, 0u);
   b->items.reserve(all.size());
-  for (long wv = 0; wv < waves; ++wv) {
-    b->wbeg[wv] = (uint32_t)b->items.size();
-    for (uint32_t t : lists[wv]) b->items.push_back({all[t].dp, all[t].rb});
+  b->queues.assign((size_t)tern::kB3Queues * tern::kB3QueueWords, 0u);
+  for (int q = 0; q < tern::kB3Queues; ++q) {
+    b->queues[(size_t)q * tern::kB3QueueWords + 2] = (uint32_t)b->items.size();
+    for (uint32_t t : lists[q]) b->items.push_back({all[t].dp, all[t].rb});
+    b->queues[(size_t)q * tern::kB3QueueWords + 3] = (uint32_t)b->items.size();
   }
-  b->wbeg[waves] = (uint32_t)b->items.size();
   return TERN_OK;
 }
 
@@ -1326,9 +1337,9 @@ static tern_status upload_b3_batch(const B3Batch& b, char* ws, hipStream_t s, bo
   };
   TERN_HIP(cp(b.descs_off, b.descs.data(), b.descs.size() * sizeof(GemvDesc)));
   TERN_HIP(cp(b.preps_off, b.preps.data(), b.preps.size() * sizeof(tern::B3Prep)));
-  TERN_HIP(cp(b.wbeg_off, b.wbeg.data(), b.wbeg.size() * 4));
   TERN_HIP(cp(b.items_off, b.items.data(), b.items.size() * sizeof(tern::B3Item)));
   TERN_HIP(cp(b.res_off, b.res.data(), b.res.size() * sizeof(tern::B3ResItem)));
+  TERN_HIP(cp(b.queue_off, b.queues.data(), b.queues.size() * 4));
   if (b.nctr) TERN_HIP(sync ? hipMemset(ws + b.ctr_off, 0, b.nctr * 4) : hipMemsetAsync(ws + b.ctr_off, 0, b.nctr * 4, s));
   for (const B3Index& ix : b.index)
     TERN_HIP(tern::launch_res_index(ix.mask, ix.rowptr, ix.rscale, ix.n, ix.mwords, ix.gidx, sync ? nullptr : s));
@@ -1349,7 +1360,8 @@ static tern_status run_b3_batch(const B3Batch& b, int group, char* ws, hipStream
                                b.max_k, s));
   TERN_HIP(tern::launch_gemv_b3(group, b.mt, reinterpret_cast<const GemvDesc*>(ws + b.descs_off),
                                 reinterpret_cast<const tern::B3Item*>(ws + b.items_off),
-                                reinterpret_cast<const uint32_t*>(ws + b.wbeg_off), b.nwg, dummy, 0, s));
+                                reinterpret_cast<uint32_t*>(ws + b.queue_off), b.nwg, dummy,
+                                (int)b.items.size(), s));
   return TERN_OK;
 }
 
@@ -1610,7 +1622,7 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
     p->b3_maxk = b.max_k;
     p->b3res = reinterpret_cast<const tern::B3ResItem*>(base + b.res_off);
     p->nres = (int)b.res.size();
-    p->wbeg = reinterpret_cast<const uint32_t*>(base + b.wbeg_off);
+    p->queue = reinterpret_cast<uint32_t*>(base + b.queue_off);
     p->nwg = b.nwg;
     *out = p;
     return TERN_OK;
@@ -1714,42 +1726,46 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
   return TERN_OK;
 }
 
-tern_status tern_plan_run(const tern_plan* plan, void* stream) {
+static tern_status plan_launch(const tern_plan* plan, hipStream_t s, hipEvent_t before, hipEvent_t after) {
   if (!plan) return fail(TERN_E_INVAL, "plan is NULL");
-  if (plan->total_items == 0) return TERN_OK;
-  if (plan->b3) {
+  if (plan->b3 && plan->total_items > 0) {
     tern::B3Prep none;
     std::memset(&none, 0, sizeof(none));
     GemvDesc dummy;
     std::memset(&dummy, 0, sizeof(dummy));
-    TERN_HIP(tern::launch_b3_prep(plan->group, plan->preps, plan->nprep, none, plan->b3_maxk, (hipStream_t)stream));
-    TERN_HIP(tern::launch_b3_res(plan->group, plan->mt, plan->dev, plan->b3res, plan->nres, dummy, plan->b3_maxk,
-                                 (hipStream_t)stream));
-    TERN_HIP(tern::launch_gemv_b3(plan->group, plan->mt, plan->dev, plan->b3items, plan->wbeg, plan->nwg, dummy, 0,
-                                  (hipStream_t)stream));
+    TERN_HIP(tern::launch_b3_prep(plan->group, plan->preps, plan->nprep, none, plan->b3_maxk, s));
+    TERN_HIP(tern::launch_b3_res(plan->group, plan->mt, plan->dev, plan->b3res, plan->nres, dummy, plan->b3_maxk, s));
+    if (before) TERN_HIP(hipEventRecord(before, s));
+    TERN_HIP(tern::launch_gemv_b3(plan->group, plan->mt, plan->dev, plan->b3items, plan->queue, plan->nwg, dummy,
+                                  plan->total_items, s));
+    if (after) TERN_HIP(hipEventRecord(after, s));
     return TERN_OK;
   }
-  if (plan->gemm) {
-    TERN_HIP(tern::launch_gemm_grouped(plan->dev, plan->total_items, plan->format, plan->group, plan->aw, plan->np,
-                                       (hipStream_t)stream));
-    if (plan->nred)
-      TERN_HIP(tern::launch_reduce_grouped(plan->red, plan->nred, plan->red_blocks, (hipStream_t)stream));
-    return TERN_OK;
+  if (before) TERN_HIP(hipEventRecord(before, s));
+  if (plan->total_items == 0) {
+  } else if (plan->gemm) {
+    TERN_HIP(tern::launch_gemm_grouped(plan->dev, plan->total_items, plan->format, plan->group, plan->aw, plan->np, s));
+    if (plan->nred) TERN_HIP(tern::launch_reduce_grouped(plan->red, plan->nred, plan->red_blocks, s));
+  } else if (plan->small) {
+    TERN_HIP(tern::launch_gemm_small(plan->dev, plan->total_items, plan->format, plan->group, plan->np, s));
+    if (plan->nred) TERN_HIP(tern::launch_reduce_grouped(plan->red, plan->nred, plan->red_blocks, s));
+  } else {
+    GemvDesc dummy;
+    std::memset(&dummy, 0, sizeof(dummy));
+    TERN_HIP(launch_decode(plan->format, plan->group, plan->mt, plan->dev, plan->recs, plan->ndesc, dummy,
+                           plan->total_items, plan->max_krp, plan->offsets, s));
+    if (plan->nred) TERN_HIP(tern::launch_reduce_grouped(plan->red, plan->nred, plan->red_blocks, s));
   }
-  if (plan->small) {
-    TERN_HIP(tern::launch_gemm_small(plan->dev, plan->total_items, plan->format, plan->group, plan->np,
-                                     (hipStream_t)stream));
-    if (plan->nred)
-      TERN_HIP(tern::launch_reduce_grouped(plan->red, plan->nred, plan->red_blocks, (hipStream_t)stream));
-    return TERN_OK;
-  }
-  GemvDesc dummy;
-  std::memset(&dummy, 0, sizeof(dummy));
-  TERN_HIP(launch_decode(plan->format, plan->group, plan->mt, plan->dev, plan->recs, plan->ndesc, dummy,
-                         plan->total_items, plan->max_krp, plan->offsets, (hipStream_t)stream));
-  if (plan->nred)
-    TERN_HIP(tern::launch_reduce_grouped(plan->red, plan->nred, plan->red_blocks, (hipStream_t)stream));
+  if (after) TERN_HIP(hipEventRecord(after, s));
   return TERN_OK;
+}
+
+tern_status tern_plan_run(const tern_plan* plan, void* stream) {
+  return plan_launch(plan, (hipStream_t)stream, nullptr, nullptr);
+}
+
+tern_status tern_plan_run_events(const tern_plan* plan, void* stream, void* before, void* after) {
+  return plan_launch(plan, (hipStream_t)stream, (hipEvent_t)before, (hipEvent_t)after);
 }
 
 void tern_plan_destroy(tern_plan* plan) { std::free(plan); }

@@ -35,7 +35,7 @@ TERN_F32 = 1
 
 SYMBOLS = ["tern_row_stride", "tern_check", "tern_packed_sizes", "tern_workspace_bytes",
            "tern_pack", "tern_unpack", "tern_gemv", "tern_gemm", "tern_batch_workspace_bytes",
-           "tern_gemv_batched", "tern_plan_create", "tern_plan_run", "tern_plan_destroy",
+           "tern_gemv_batched", "tern_plan_create", "tern_plan_run", "tern_plan_run_events", "tern_plan_destroy",
            "tern_bits", "tern_quantize", "tern_rotate", "tern_rotate_batched", "tern_read_probe", "tern_status_str", "tern_last_error"]
 
 
@@ -78,6 +78,7 @@ def load() -> ctypes.CDLL:
         "tern_gemv_batched": (c_int32, [P, POINTER(c_void_p), POINTER(c_void_p), c_int32, c_int32, c_int32, c_void_p, c_size_t, c_void_p]),
         "tern_plan_create": (c_int32, [P, POINTER(c_void_p), POINTER(c_void_p), c_int32, c_int32, c_int32, c_void_p, c_size_t, POINTER(c_void_p)]),
         "tern_plan_run": (c_int32, [c_void_p, c_void_p]),
+        "tern_plan_run_events": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p]),
         "tern_plan_destroy": (None, [c_void_p]),
         "tern_bits": (c_int32, [P, POINTER(c_double), POINTER(c_double), POINTER(c_double)]),
         "tern_quantize": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p,
@@ -249,6 +250,15 @@ def tern_gemv_batched(mats, xs, ys, y_dtype=TERN_F16, stream=None, ws=None):
     return ys
 
 
+def _event(e):
+    """The HIP event handle of a torch.cuda.Event (created on first record)."""
+    if e is None:
+        return None
+    if not e.cuda_event:
+        e.record()
+    return e.cuda_event
+
+
 class Plan:
     """tern_plan_create / tern_plan_run / tern_plan_destroy."""
 
@@ -271,6 +281,11 @@ class Plan:
 
     def run(self, stream=None):
         check(load().tern_plan_run(self.handle, _stream(stream)))
+
+    def run_events(self, before, after, stream=None):
+        """run() recording two torch.cuda.Event objects (created with
+        enable_timing=True) around the main decode launch."""
+        check(load().tern_plan_run_events(self.handle, _stream(stream), _event(before), _event(after)))
 
     def __del__(self):
         if getattr(self, "handle", None) and _lib is not None:

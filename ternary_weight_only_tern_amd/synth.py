@@ -37,6 +37,10 @@ QWEN3_8B_LAYER = [("q", 4096, 4096), ("k", 4096, 1024), ("v", 4096, 1024),
                   ("o", 4096, 4096), ("gate", 4096, 12288), ("up", 4096, 12288),
                   ("down", 12288, 4096)]
 NUM_LAYERS = 36
+# For each projection of a decoder layer, the projection whose input it
+# reads: q/k/v take the same normed hidden state, gate/up the same normed
+# post-attention state (one activation vector each per layer and token).
+LAYER_INPUT = (0, 0, 0, 3, 4, 4, 6)
 
 WORKLOADS = {
     "single_gemv": dict(stream=1, name="single-gemv K256 N128 G64 2-bit", shapes=[("w", 256, 128)], group=64,
