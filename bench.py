@@ -573,6 +573,8 @@ def main():
                     help="only the activation rotation of a 4B-class layer's M=1 inputs (profiling); no JSON line")
     ap.add_argument("--layer8b-only", type=int, metavar="M", default=0,
                     help="only the base-3 8B-class layer at M activation rows (profiling); no JSON line")
+    ap.add_argument("--stress-only", metavar="FMT:M", default="",
+                    help="only the stress down-projection, FMT 2bit or b3, at M rows (profiling); no JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -604,6 +606,11 @@ def main():
         q = bench_layer8b(args, stream, m)
         log(f"bench: 8B-class layer base-3 M={m}: {q['us_per_layer']:.1f} us, {q['gbs']:.1f} GB/s, "
             f"{q['tflops']:.1f} TFLOP/s ({q['copies']} copies rotated)")
+        return
+    if args.stress_only:
+        fname, m = args.stress_only.split(":")
+        q = bench_stress(args, stream, {"2bit": 0, "b3": 1}[fname], int(m))
+        log(f"bench: stress down-projection {fname} M={m}: {q['us']:.2f} us, {q['gbs']:.1f} GB/s")
         return
     if args.layer4b_only:
         r = bench_layer4b(args, stream)

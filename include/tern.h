@@ -222,6 +222,20 @@ tern_status tern_plan_run(const tern_plan *plan, void *stream);
 tern_status tern_plan_run_events(const tern_plan *plan, void *stream, void *before, void *after);
 void tern_plan_destroy(tern_plan *plan);
 
+/* Routing of base-3 products at m <= 4 (tern_gemv, tern_gemv_batched,
+ * tern_plan_create and their workspace sizes).  A launch whose products
+ * hold at least this many 64-row stages of plane 0 (ceil(n / 64) *
+ * ceil(k / (8 * 128)) per product at group 128, ceil(k / (16 * 64)) at group
+ * 64) runs the persistent matrix-core stream kernel with a separate residual
+ * pass; smaller launches run the lane-per-row decode, whose work items are
+ * finer.  Default: four stages per wavefront of the stream kernel (7168 on
+ * 256 CUs).  stages >= 0 sets the threshold (0: every such launch takes the
+ * stream kernel), -1 restores the default, any other negative value only
+ * queries.  Returns the threshold in effect before the call.  Process-wide;
+ * workspace sizes and plans follow the threshold in effect when they are
+ * computed or created.  Host-only. */
+int64_t tern_b3_min_stages(int64_t stages);
+
 /* Bits per weight of a packed matrix (2609.01962 §3.2, §7.1: effective bits
  * count log2(3) per stored trit over the planes actually present):
  *   info    = log2(3) * (n*k + group * sum nnz) / (n*k)

@@ -130,6 +130,8 @@ __global__ __launch_bounds__(256) void b3_prep_kernel(const B3Prep* __restrict__
   using Gm = B3Geo<G>;
   const B3Prep p = preps ? preps[blockIdx.y / 4] : one;
   const int m = blockIdx.y % 4;
+  if (p.zero && blockIdx.x == 0 && m == 0)
+    for (int i = threadIdx.x; i < p.nzero; i += 256) p.zero[i] = 0u;
   if (m >= p.m) return;
   const int ng = p.k / G;
   const uint16_t* xr = p.x + (size_t)m * p.k;
@@ -347,20 +349,23 @@ __device__ __forceinline__ void b3_stage_full(const uint8_t* lds, uint32_t coff,
 // from the staged windows.  Runs with several workgroups per CU, so the
 // latency of its gathers hides behind other workgroups.
 constexpr int kResThreads = kB3ResRows;
-constexpr int kResMaxWindow = 32768;  // activation window bytes, at most
 constexpr int kResPer = 4;            // entries per thread and chunk
 constexpr int kResChunk = kResPer * kResThreads;
 constexpr int kResBatch = 4;          // activation loads per thread in flight while staging
 
-// Window of a launch whose longest product has max_k inputs: all of it when
-// it fits, else the most whole groups that do.
+// Activation window of a launch whose longest product has max_k inputs,
+// within lds_cap bytes of LDS in all: every group when they fit, else the
+// most whole groups that do.
 template <int G, int MT>
-constexpr int res_window(int max_k) {
-  return (max_k / G) * MT * (2 * G + 16) <= kResMaxWindow ? (max_k / G) * MT * (2 * G + 16)
-                                                           : kResMaxWindow / (MT * (2 * G + 16)) * MT * (2 * G + 16);
+constexpr int res_window(int max_k, int lds_cap) {
+  const int per = MT * (2 * G + 16);
+  const int room = lds_cap - kResChunk * MT * 4 - MT * (max_k / G) * 4;
+  return (max_k / G) * per <= room ? (max_k / G) * per : room / per * per;
 }
 template <int G, int MT>
-constexpr int res_lds_bytes(int max_k) { return res_window<G, MT>(max_k) + kResChunk * MT * 4 + MT * (max_k / G) * 4; }
+constexpr int res_lds_bytes(int max_k, int lds_cap) {
+  return res_window<G, MT>(max_k, lds_cap) + kResChunk * MT * 4 + MT * (max_k / G) * 4;
+}
 
 // TABLE: units and descriptors from device tables; else the row blocks of
 // `one` (a compile-time choice: a descriptor chosen at run time between a
@@ -375,15 +380,22 @@ __global__ __launch_bounds__(kResThreads) void b3_res_kernel(const GemvDesc* __r
   uint8_t* xw = reinterpret_cast<uint8_t*>(res_smem);
   float* vals = reinterpret_cast<float*>(xw + window);
   GemvDesc d;
-  int rb;
+  int rb, slot;
   if constexpr (TABLE) {
     const B3ResItem u = units[blockIdx.x];
     d = descs[u.desc];
     rb = (int)u.rb;
+    slot = (int)u.slot;
   } else {
     d = one;
-    rb = (int)blockIdx.x;
+    rb = (int)blockIdx.x / d.rslots;
+    slot = (int)blockIdx.x % d.rslots;
   }
+  // this unit's residual plane (-1: none, the offset alone) and entry range
+  // of the row block; slot 0 also adds the offset
+  const int rplane = d.planes > 1 ? slot / d.rsplit : -1;
+  const int rpart_ix = d.planes > 1 ? slot % d.rsplit : 0;
+  const bool with_off = d.offset_mode != 0 && slot == 0;
   float* xsum = vals + kResChunk * MT;
   const int tid = threadIdx.x;
   const int r0 = rb * kB3ResRows;
@@ -409,20 +421,31 @@ __global__ __launch_bounds__(kResThreads) void b3_res_kernel(const GemvDesc* __r
         bv[r][q] = e < c1 ? __builtin_nontemporal_load(blocks + (size_t)e * (G / 64) + q) : u4_t{0u, 0u, 0u, 0u};
     }
   };
-  // the first chunk of the first plane is requested before the activations
-  // are staged, so that the two latencies overlap
-  bool prefetched = false;
-  if (d.planes > 1) {
-    const GLOBAL uint32_t* rowptr = gp(d.rowptr[0]);
+  // the plane's entries of the row block, [E0, E1), and this unit's part
+  // [A0, A1) of them; (selects, not indexing with the plane: the descriptor
+  // stays in registers)
+  const GLOBAL uint32_t* rowptr = gp(rplane == 1 ? d.rowptr[1] : d.rowptr[0]);
+  const GLOBAL uint32_t* gidx = gp(rplane == 1 ? d.gidx[1] : d.gidx[0]);
+  const GLOBAL u4_t* blocks = reinterpret_cast<const GLOBAL u4_t*>(gp(rplane == 1 ? d.blocks[1] : d.blocks[0]));
+  uint32_t A0 = 0, A1 = 0, rp_lo = 0, rp_hi = 0;
+  if (rplane >= 0) {
     const uint32_t E0 = rowptr[r0], E1 = rowptr[rlast];
-    if (E0 < E1) {
-      load_chunk(gp(d.gidx[0]), reinterpret_cast<const GLOBAL u4_t*>(gp(d.blocks[0])), E0,
-                 min(E1, E0 + (uint32_t)kResChunk));
-      prefetched = true;
-    }
+    const uint64_t len = E1 - E0;
+    A0 = E0 + (uint32_t)(len * (uint64_t)rpart_ix / (uint64_t)d.rsplit);
+    A1 = E0 + (uint32_t)(len * (uint64_t)(rpart_ix + 1) / (uint64_t)d.rsplit);
+    rp_lo = row_ok ? rowptr[row] : 0u;
+    rp_hi = row_ok ? rowptr[row + 1] : 0u;
+  }
+  // the first chunk is requested before the activations are staged, so that
+  // the two latencies overlap
+  bool prefetched = false;
+  if (A0 < A1) {
+    load_chunk(gidx, blocks, A0, min(A1, A0 + (uint32_t)kResChunk));
+    prefetched = true;
   }
 
-  for (int wg0 = 0; wg0 < d.ng; wg0 += wgn) {
+  // (a unit with neither entries nor the offset stages nothing)
+  for (int wg0 = 0; wg0 < (with_off || A0 < A1 ? d.ng : 0); wg0 += wgn) {
     const int wg1 = min(d.ng, wg0 + wgn), wn = wg1 - wg0;
     __syncthreads();  // the previous window is no longer read
     // stage the window: kResBatch loads per thread in flight, then the stores
@@ -446,7 +469,7 @@ __global__ __launch_bounds__(kResThreads) void b3_res_kernel(const GemvDesc* __r
       }
     }
     __syncthreads();
-    if (d.offset_mode != 0) {  // group sums of x, in position order
+    if (with_off) {  // group sums of x, in position order
       for (int c = tid; c < MT * wn; c += kResThreads) {
         const int m = c / wn, gl = c % wn;
         const uint32_t* xg = reinterpret_cast<const uint32_t*>(xw + (m * wgn + gl) * GP);
@@ -458,16 +481,10 @@ __global__ __launch_bounds__(kResThreads) void b3_res_kernel(const GemvDesc* __r
         xsum[m * d.ng + wg0 + gl] = sx;
       }
     }
-    for (int p = 0; p + 1 < d.planes; ++p) {
-      // (selects, not indexing with p: the descriptor stays in registers)
-      const GLOBAL uint32_t* rowptr = gp(p == 0 ? d.rowptr[0] : d.rowptr[1]);
-      const uint32_t E0 = rowptr[r0], E1 = rowptr[rlast];
-      const uint32_t rp_lo = row_ok ? rowptr[row] : 0u, rp_hi = row_ok ? rowptr[row + 1] : 0u;
-      const GLOBAL uint32_t* gidx = gp(p == 0 ? d.gidx[0] : d.gidx[1]);
-      const GLOBAL u4_t* blocks = reinterpret_cast<const GLOBAL u4_t*>(gp(p == 0 ? d.blocks[0] : d.blocks[1]));
-      for (uint32_t c0 = E0; c0 < E1; c0 += kResChunk) {
-        const uint32_t c1 = min(E1, c0 + (uint32_t)kResChunk);
-        if (prefetched) prefetched = false;  // (the first chunk of plane 0 in the first window)
+    {
+      for (uint32_t c0 = A0; c0 < A1; c0 += kResChunk) {
+        const uint32_t c1 = min(A1, c0 + (uint32_t)kResChunk);
+        if (prefetched) prefetched = false;  // (the first chunk, in the first window)
         else load_chunk(gidx, blocks, c0, c1);
 #pragma unroll
         for (int r = 0; r < kResPer; ++r) {
@@ -514,8 +531,7 @@ __global__ __launch_bounds__(kResThreads) void b3_res_kernel(const GemvDesc* __r
     }
   }
   __syncthreads();  // the group sums are complete
-  if (!row_ok) return;
-  if (d.offset_mode != 0) {
+  if (with_off && row_ok) {
     const GLOBAL uint16_t* off = gp(d.offset);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -529,9 +545,26 @@ __global__ __launch_bounds__(kResThreads) void b3_res_kernel(const GemvDesc* __r
     }
   }
   float* rs = const_cast<float*>(d.rsum);
+  if (d.rslots > 1) {
+    // this unit's sums; the row block's last unit adds them in slot order
+    if (row_ok) {
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
-    if (m < d.m) rs[(size_t)m * d.n + row] = acc[m];
+      for (int m = 0; m < MT; ++m)
+        if (m < d.m) part_store(d.rpart + ((size_t)slot * d.m + m) * d.n + row, acc[m]);
+    }
+    if (!last_part(d.rctr + rb, d.rslots)) return;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      acc[m] = 0.f;
+      if (m < d.m && row_ok)
+        for (int sl = 0; sl < d.rslots; ++sl) acc[m] += part_load(d.rpart + ((size_t)sl * d.m + m) * d.n + row);
+    }
+  }
+  if (row_ok) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      if (m < d.m) rs[(size_t)m * d.n + row] = acc[m];
+  }
 }
 
 template <int G, int MT, bool TABLE>
@@ -770,24 +803,26 @@ hipError_t launch_b3_g(int mt, const GemvDesc* descs, const B3Item* items, uint3
 
 template <int G, int MT>
 hipError_t launch_res_mt(const GemvDesc* descs, const B3ResItem* units, int nunits, const GemvDesc& one, int max_k,
-                         hipStream_t s) {
-  const size_t lds = (size_t)res_lds_bytes<G, MT>(max_k);
+                         int lds_cap, hipStream_t s) {
+  const int window = res_window<G, MT>(max_k, lds_cap);
+  if (window < MT * (2 * G + 16)) return hipErrorInvalidValue;  // not one group fits
+  const size_t lds = (size_t)res_lds_bytes<G, MT>(max_k, lds_cap);
   if (units)
     hipLaunchKernelGGL((b3_res_kernel<G, MT, true>), dim3(nunits), dim3(kResThreads), lds, s, descs, units, one,
-                       res_window<G, MT>(max_k));
+                       window);
   else
     hipLaunchKernelGGL((b3_res_kernel<G, MT, false>), dim3(nunits), dim3(kResThreads), lds, s, descs, units, one,
-                       res_window<G, MT>(max_k));
+                       window);
   return hipGetLastError();
 }
 
 template <int G>
 hipError_t launch_res_g(int mt, const GemvDesc* descs, const B3ResItem* units, int nunits, const GemvDesc& one,
-                        int max_k, hipStream_t s) {
+                        int max_k, int lds_cap, hipStream_t s) {
   switch (mt) {
-    case 1: return launch_res_mt<G, 1>(descs, units, nunits, one, max_k, s);
-    case 2: return launch_res_mt<G, 2>(descs, units, nunits, one, max_k, s);
-    case 4: return launch_res_mt<G, 4>(descs, units, nunits, one, max_k, s);
+    case 1: return launch_res_mt<G, 1>(descs, units, nunits, one, max_k, lds_cap, s);
+    case 2: return launch_res_mt<G, 2>(descs, units, nunits, one, max_k, lds_cap, s);
+    case 4: return launch_res_mt<G, 4>(descs, units, nunits, one, max_k, lds_cap, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -795,10 +830,10 @@ hipError_t launch_res_g(int mt, const GemvDesc* descs, const B3ResItem* units, i
 }  // namespace
 
 hipError_t launch_b3_res(int group, int mt, const GemvDesc* descs, const B3ResItem* units, int nunits,
-                         const GemvDesc& one, int max_k, hipStream_t s) {
+                         const GemvDesc& one, int max_k, int lds_cap, hipStream_t s) {
   if (nunits <= 0) return hipSuccess;
-  if (group == 64) return launch_res_g<64>(mt, descs, units, nunits, one, max_k, s);
-  if (group == 128) return launch_res_g<128>(mt, descs, units, nunits, one, max_k, s);
+  if (group == 64) return launch_res_g<64>(mt, descs, units, nunits, one, max_k, lds_cap, s);
+  if (group == 128) return launch_res_g<128>(mt, descs, units, nunits, one, max_k, lds_cap, s);
   return hipErrorInvalidValue;
 }
 

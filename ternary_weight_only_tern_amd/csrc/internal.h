@@ -66,6 +66,16 @@ struct GemvDesc {
   // offset per output ([m][n]), written by launch_b3_res before the product
   // and added to y by it; NULL when the matrix has neither.
   const float* rsum;
+  // Residual pass: each residual plane's entries of a row block are cut into
+  // rsplit ranges; rslots = max(1, (planes - 1) * rsplit) units per row
+  // block (slot = plane * rsplit + range; slot 0 also adds the offset).
+  // With rslots > 1 every unit stores its rows' sums in rpart
+  // ([rslots][m][n] FP32) and the row block's last unit (arrival counter
+  // rctr[row block], zero between launches) adds them in slot order into
+  // rsum.
+  int32_t rsplit, rslots;
+  float* rpart;
+  uint32_t* rctr;
 };
 
 // ---- decode products (gemv.hip)
@@ -145,23 +155,27 @@ struct B3Prep {
   uint16_t* x5;
   float* xs;
   int32_t k, m;
+  uint32_t* zero;  // if not NULL: nzero words cleared (counters of the passes that follow)
+  int32_t nzero;
 };
 // Instructions (4-slot chunks) per group: 33 at group 128, 16 at group 64;
 // groups per 208-byte stage: 8 and 16.
 int b3_chunks_per_group(int group);
 int b3_stage_groups(int group);
-// Residual pass work unit: descriptor index and block of kB3ResRows output
-// rows.  One workgroup per unit sums the residual planes and the offset of its
-// rows into the descriptor's rsum.
+// Residual pass work unit: descriptor index, block of kB3ResRows output
+// rows and slot (see GemvDesc::rslots).  One workgroup per unit.
 constexpr int kB3ResRows = 256;
 struct B3ResItem {
   uint32_t desc;
   uint32_t rb;
+  uint32_t slot;
 };
-// nunits workgroups over units (device), or with units == NULL the row blocks
-// of the single descriptor `one`.  max_k: the longest k.
+// nunits workgroups over units (device), or with units == NULL the units
+// (row block * rslots + slot) of the single descriptor `one`.  max_k: the
+// longest k; lds_cap: the most LDS bytes a workgroup may take (a large
+// activation window for launches of few units, smaller ones for occupancy).
 hipError_t launch_b3_res(int group, int mt, const GemvDesc* descs, const B3ResItem* units, int nunits,
-                         const GemvDesc& one, int max_k, hipStream_t stream);
+                         const GemvDesc& one, int max_k, int lds_cap, hipStream_t stream);
 // preps (device) holds count preparations; with preps == NULL, `one` alone;
 // max_k: the longest k among them.
 hipError_t launch_b3_prep(int group, const B3Prep* preps, int count, const B3Prep& one, int max_k, hipStream_t stream);

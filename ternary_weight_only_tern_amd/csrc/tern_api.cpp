@@ -276,12 +276,16 @@ static bool small_route(int format, int group, int m) {
 static bool b3_route(int format, int group, int m) {
   return format == TERN_FMT_B3 && product_group_ok(group) && m >= 1 && m <= 4;
 }
+// The same for a launch of count products: only launches with enough
+// 64-row stages for the persistent stream kernel take it (defined with the
+// base-3 batch builder).
+static bool b3_route_n(const tern_matrix* w, int count, int m);
 
 // Workspace of a small-m product batch (defined with the batch builder).
 static size_t small_batch_ws_bytes(const tern_matrix* w, int32_t count, int32_t m);
 // Single base-3 product at m <= 4 (defined with the base-3 batch builder).
-static void b3_single_layout(const tern_matrix* w, int m, int* parts, int* sps, size_t* x5_off, size_t* xs_off,
-                             size_t* total);
+static void b3_single_layout(const tern_matrix* w, int m, int* parts, int* sps, int* rsplit, size_t* x5_off,
+                             size_t* xs_off, size_t* rp_off, size_t* rc_off, size_t* total);
 static tern_status b3_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* y, int32_t y_dtype, void* ws,
                            size_t ws_bytes, hipStream_t s);
 
@@ -319,10 +323,10 @@ size_t tern_workspace_bytes(const tern_matrix* w, int32_t m) {
   if (!w || check_shape(w->n, w->k, w->group, w->planes, w->format, w->offset_mode) != TERN_OK) return 0;
   const size_t packing = kFlagBytes + round_up(((size_t)w->n + 1) * 4, 256);
   size_t product = m > 0 && small_route(w->format, w->group, m) ? small_batch_ws_bytes(w, 1, m) : gemv_ws_bytes(w, m);
-  if (b3_route(w->format, w->group, m) && w->n > 0 && w->k > 0) {
-    int parts, sps;
-    size_t x5_off, xs_off;
-    b3_single_layout(w, m, &parts, &sps, &x5_off, &xs_off, &product);
+  if (b3_route_n(w, 1, m) && w->n > 0 && w->k > 0) {
+    int parts, sps, rsplit;
+    size_t x5_off, xs_off, rp_off, rc_off;
+    b3_single_layout(w, m, &parts, &sps, &rsplit, &x5_off, &xs_off, &rp_off, &rc_off, &product);
   }
   return std::max(packing, product);
 }
@@ -425,7 +429,7 @@ tern_status tern_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* 
     void* yp = y;
     return tern_gemv_batched(w, &x, &yp, 1, m, y_dtype, ws, ws_bytes, stream);
   }
-  if (b3_route(w->format, w->group, m)) return b3_gemv(w, x, m, y, y_dtype, ws, ws_bytes, s);
+  if (b3_route_n(w, 1, m)) return b3_gemv(w, x, m, y, y_dtype, ws, ws_bytes, s);
   const int cmax = max_mt(w->format, w->group);
   int splits, gps;
   choose_splits(w, pick_mt(std::min(m, cmax)), &splits, &gps);
@@ -1140,6 +1144,8 @@ struct B3Batch {
   std::vector<tern::B3Item> items;
   std::vector<tern::B3ResItem> res;  // residual pass units
   std::vector<uint32_t> queues;      // kB3Queues * kB3QueueWords words
+  std::vector<std::pair<size_t, size_t>> zero;  // (offset, bytes) cleared at upload: residual-pass counters
+  size_t rctr_off = 0, rctr_bytes = 0;
   size_t descs_off = 0, preps_off = 0, queue_off = 0, items_off = 0, part_off = 0, ctr_off = 0, res_off = 0, total = 0;
   size_t nctr = 0;
   int mt = 1, nwg = 0, max_k = 0;
@@ -1153,12 +1159,63 @@ static int b3_stages(const tern_matrix* w) {
   const int sg = tern::b3_stage_groups(w->group);
   return (w->k / w->group + sg - 1) / sg;
 }
+// Launches of fewer 64-row stages than this (default: four per wavefront of
+// the persistent launch) use the lane-per-row decode, whose work items are
+// finer; tern_b3_min_stages changes it.
+static int64_t g_b3_min_stages = -1;
+static int64_t b3_min_stages() {
+  return g_b3_min_stages >= 0 ? g_b3_min_stages : 4L * tern_cu_count() * tern::kB3Waves;
+}
+static bool b3_route_n(const tern_matrix* w, int count, int m) {
+  if (count <= 0 || !w || !b3_route(w[0].format, w[0].group, m)) return false;
+  int64_t stages = 0;
+  for (int i = 0; i < count; ++i)
+    if (w[i].group == w[0].group && w[i].n > 0 && w[i].k > 0)
+      stages += (int64_t)((w[i].n + tern::kGemvRows - 1) / tern::kGemvRows) * b3_stages(&w[i]);
+  return stages >= b3_min_stages();
+}
 // A product with residual planes or an offset goes through the residual pass.
 static bool b3_has_res(const tern_matrix* w) { return w->planes > 1 || w->offset_mode != TERN_OFF_NONE; }
 static size_t b3_rsum_bytes(const tern_matrix* w, int m) {
   return b3_has_res(w) ? round_up((size_t)m * w->n * 4, 256) : 0;
 }
 static int b3_res_units(const tern_matrix* w) { return (w->n + tern::kB3ResRows - 1) / tern::kB3ResRows; }
+// Residual pass: entry ranges per plane and row block (GemvDesc::rsplit) for
+// the products `order` of w: up to about 2048 entries per unit, then more
+// ranges (down to about 256 entries, one per thread) while the launch would
+// hold fewer than two units per CU.
+static std::vector<int> b3_res_splits(const tern_matrix* w, const std::vector<int>& order, int count) {
+  std::vector<int> sp(count, 1);
+  std::vector<double> avg(count, 0.0);
+  long units = 0;
+  for (int i : order) {
+    if (!b3_has_res(&w[i])) continue;
+    const int nrb = b3_res_units(&w[i]);
+    for (int p = 0; p + 1 < w[i].planes; ++p) avg[i] = std::max(avg[i], (double)w[i].nnz[p] / nrb);
+    sp[i] = std::max(1, (int)std::ceil(avg[i] / 2048.0));
+    units += (long)nrb * std::max(1, w[i].planes - 1) * sp[i];
+  }
+  const long want = 2L * tern_cu_count();
+  if (units > 0 && units < want) {
+    const long f = (want + units - 1) / units;
+    for (int i : order)
+      if (b3_has_res(&w[i]) && w[i].planes > 1)
+        sp[i] = (int)std::max<long>(sp[i], std::min<long>({(long)sp[i] * f, (long)(avg[i] / 256.0), 64L}));
+  }
+  return sp;
+}
+static int b3_res_slots(const tern_matrix* w, int split) { return w->planes > 1 ? (w->planes - 1) * split : 1; }
+// Partial sums and arrival counters of a product whose residual pass has
+// several units per row block.
+static size_t b3_rpart_bytes(const tern_matrix* w, int m, int split) {
+  return b3_has_res(w) && b3_res_slots(w, split) > 1 ? round_up((size_t)b3_res_slots(w, split) * m * w->n * 4, 256) : 0;
+}
+static size_t b3_rctr_bytes(const tern_matrix* w, int split) {
+  return b3_has_res(w) && b3_res_slots(w, split) > 1 ? round_up((size_t)b3_res_units(w) * 4, 256) : 0;
+}
+// LDS a residual-pass workgroup may take: a large activation window when the
+// launch has few units, a smaller one (more workgroups per CU) otherwise.
+static int b3_res_lds_cap(long nunits) { return nunits <= 4L * tern_cu_count() ? 65536 : 36864; }
 
 // Builds the batch (items only when `items` is true); ws may be NULL (sizes only).
 static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y, int32_t count,
@@ -1188,12 +1245,13 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
   const int target = (int)std::max(1L, units / (2 * waves));
   std::vector<int> sps(count, 1), parts(count, 1);
   size_t nres = 0;
+  const std::vector<int> rsp = b3_res_splits(w, order, count);
   for (int i : order) {
     const int nst = b3_stages(&w[i]);
     sps[i] = std::min(nst, target);
     parts[i] = (nst + sps[i] - 1) / sps[i];
     b->max_k = std::max(b->max_k, w[i].k);
-    if (b3_has_res(&w[i])) nres += (size_t)b3_res_units(&w[i]);
+    if (b3_has_res(&w[i])) nres += (size_t)b3_res_units(&w[i]) * b3_res_slots(&w[i], rsp[i]);
   }
   // layout
   const size_t nd = order.size();
@@ -1232,10 +1290,16 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
     x5_off[i] = off;
     off += b3_x5_bytes(&w[i], m);
   }
+  std::vector<size_t> rp_off(count, 0), rc_off(count, 0);
   for (int i : order) {
     xs_off[i] = off;  // residual sums
     off += b3_rsum_bytes(&w[i], m);
+    rp_off[i] = off;  // residual pass partials and arrival counters
+    off += b3_rpart_bytes(&w[i], m, rsp[i]);
+    rc_off[i] = off;
+    off += b3_rctr_bytes(&w[i], rsp[i]);
   }
+
   // residual index per plane (entry -> group and scale)
   std::vector<size_t> gi_off(2 * (size_t)count, 0);
   for (int i : order)
@@ -1246,6 +1310,7 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
   b->total = off;
   b->descs.clear();
   b->res.clear();
+  b->zero.clear();
   b->index.clear();
   b->preps.clear();
   b->items.clear();
@@ -1263,8 +1328,17 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
     d.gps = sps[i];
     d.x5 = ws ? reinterpret_cast<const uint16_t*>(ws + x5_off[i]) : nullptr;
     d.rsum = ws && b3_has_res(&w[i]) ? reinterpret_cast<const float*>(ws + xs_off[i]) : nullptr;
+    d.rsplit = rsp[i];
+    d.rslots = b3_res_slots(&w[i], rsp[i]);
+    if (b3_has_res(&w[i]) && d.rslots > 1) {
+      d.rpart = ws ? reinterpret_cast<float*>(ws + rp_off[i]) : nullptr;
+      d.rctr = ws ? reinterpret_cast<uint32_t*>(ws + rc_off[i]) : nullptr;
+      b->zero.push_back({rc_off[i], b3_rctr_bytes(&w[i], rsp[i])});
+    }
     if (b3_has_res(&w[i]))
-      for (int u = 0; u < b3_res_units(&w[i]); ++u) b->res.push_back({(uint32_t)b->descs.size(), (uint32_t)u});
+      for (int u = 0; u < b3_res_units(&w[i]); ++u)
+        for (int sl = 0; sl < d.rslots; ++sl)
+          b->res.push_back({(uint32_t)b->descs.size(), (uint32_t)u, (uint32_t)sl});
     for (int p = 0; p + 1 < w[i].planes; ++p) {
       uint32_t* gidx = ws ? reinterpret_cast<uint32_t*>(ws + gi_off[2 * i + p]) : nullptr;
       d.gidx[p] = gidx;
@@ -1280,9 +1354,9 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
     b->descs.push_back(d);
     if (!x5_own[i]) continue;
     tern::B3Prep pr;
+    std::memset(&pr, 0, sizeof(pr));
     pr.x = x[i];
     pr.x5 = const_cast<uint16_t*>(d.x5);
-    pr.xs = nullptr;
     pr.k = w[i].k;
     pr.m = m;
     b->preps.push_back(pr);
@@ -1340,6 +1414,8 @@ static tern_status upload_b3_batch(const B3Batch& b, char* ws, hipStream_t s, bo
   TERN_HIP(cp(b.items_off, b.items.data(), b.items.size() * sizeof(tern::B3Item)));
   TERN_HIP(cp(b.res_off, b.res.data(), b.res.size() * sizeof(tern::B3ResItem)));
   TERN_HIP(cp(b.queue_off, b.queues.data(), b.queues.size() * 4));
+  for (const auto& z : b.zero)
+    TERN_HIP(sync ? hipMemset(ws + z.first, 0, z.second) : hipMemsetAsync(ws + z.first, 0, z.second, s));
   if (b.nctr) TERN_HIP(sync ? hipMemset(ws + b.ctr_off, 0, b.nctr * 4) : hipMemsetAsync(ws + b.ctr_off, 0, b.nctr * 4, s));
   for (const B3Index& ix : b.index)
     TERN_HIP(tern::launch_res_index(ix.mask, ix.rowptr, ix.rscale, ix.n, ix.mwords, ix.gidx, sync ? nullptr : s));
@@ -1357,7 +1433,7 @@ static tern_status run_b3_batch(const B3Batch& b, int group, char* ws, hipStream
                                 none, b.max_k, s));
   TERN_HIP(tern::launch_b3_res(group, b.mt, reinterpret_cast<const GemvDesc*>(ws + b.descs_off),
                                reinterpret_cast<const tern::B3ResItem*>(ws + b.res_off), (int)b.res.size(), dummy,
-                               b.max_k, s));
+                               b.max_k, b3_res_lds_cap((long)b.res.size()), s));
   TERN_HIP(tern::launch_gemv_b3(group, b.mt, reinterpret_cast<const GemvDesc*>(ws + b.descs_off),
                                 reinterpret_cast<const tern::B3Item*>(ws + b.items_off),
                                 reinterpret_cast<uint32_t*>(ws + b.queue_off), b.nwg, dummy,
@@ -1369,25 +1445,28 @@ static tern_status run_b3_batch(const B3Batch& b, int group, char* ws, hipStream
 // items w, w + W, ... of the one descriptor; K parts (when the product is too
 // small to fill the GPU) write FP32 partials that a second kernel sums.
 // Workspace: [partials][x5][group sums].
-static void b3_single_layout(const tern_matrix* w, int m, int* parts, int* sps, size_t* x5_off, size_t* xs_off,
-                             size_t* total) {
+static void b3_single_layout(const tern_matrix* w, int m, int* parts, int* sps, int* rsplit, size_t* x5_off,
+                             size_t* xs_off, size_t* rp_off, size_t* rc_off, size_t* total) {
   const long waves = (long)tern_cu_count() * tern::kB3Waves;
   const int rb = (w->n + tern::kGemvRows - 1) / tern::kGemvRows;
   const int nst = b3_stages(w);
   const int target = (int)std::max(1L, (long)rb * nst / (2 * waves));
   *sps = std::min(nst, target);
   *parts = (nst + *sps - 1) / *sps;
+  *rsplit = b3_res_splits(w, std::vector<int>{0}, 1)[0];
   *x5_off = split_ws_bytes(*parts, m, w->n);
   *xs_off = *x5_off + b3_x5_bytes(w, m);  // residual sums
-  *total = *xs_off + b3_rsum_bytes(w, m);
+  *rp_off = *xs_off + b3_rsum_bytes(w, m);  // residual pass partials, arrival counters
+  *rc_off = *rp_off + b3_rpart_bytes(w, m, *rsplit);
+  *total = *rc_off + b3_rctr_bytes(w, *rsplit);
   for (int p = 0; p + 1 < w->planes; ++p) *total += round_up((size_t)w->nnz[p] * 4, 256);  // residual index
 }
 
 static tern_status b3_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* y, int32_t y_dtype, void* ws,
                            size_t ws_bytes, hipStream_t s) {
-  int parts, sps;
-  size_t x5_off, xs_off, total;
-  b3_single_layout(w, m, &parts, &sps, &x5_off, &xs_off, &total);
+  int parts, sps, rsplit;
+  size_t x5_off, xs_off, rp_off, rc_off, total;
+  b3_single_layout(w, m, &parts, &sps, &rsplit, &x5_off, &xs_off, &rp_off, &rc_off, &total);
   if (!ws || ws_bytes < total) return fail(TERN_E_WORKSPACE, "tern_gemv needs %zu workspace bytes", total);
   TERN_TRY(check_dev(ws, true, "ws"));
   char* base = static_cast<char*>(ws);
@@ -1398,8 +1477,14 @@ static tern_status b3_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, v
   d.gps = sps;
   d.x5 = reinterpret_cast<const uint16_t*>(base + x5_off);
   d.rsum = b3_has_res(w) ? reinterpret_cast<const float*>(base + xs_off) : nullptr;
+  d.rsplit = rsplit;
+  d.rslots = b3_res_slots(w, rsplit);
+  if (d.rsum && d.rslots > 1) {
+    d.rpart = reinterpret_cast<float*>(base + rp_off);
+    d.rctr = reinterpret_cast<uint32_t*>(base + rc_off);
+  }
   if (parts > 1) d.partial = reinterpret_cast<float*>(base);
-  size_t gi = xs_off + b3_rsum_bytes(w, m);
+  size_t gi = rc_off + b3_rctr_bytes(w, rsplit);
   for (int p = 0; p + 1 < w->planes; ++p) {
     d.gidx[p] = reinterpret_cast<const uint32_t*>(base + gi);
     if (w->nnz[p] > 0)
@@ -1408,13 +1493,17 @@ static tern_status b3_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, v
     gi += round_up((size_t)w->nnz[p] * 4, 256);
   }
   tern::B3Prep pr;
+  std::memset(&pr, 0, sizeof(pr));
   pr.x = x;
   pr.x5 = const_cast<uint16_t*>(d.x5);
-  pr.xs = nullptr;
   pr.k = w->k;
   pr.m = m;
+  pr.zero = d.rctr;  // the residual pass's counters start at zero (cleared in the launch: no memset node)
+  pr.nzero = d.rctr ? b3_res_units(w) : 0;
   TERN_HIP(tern::launch_b3_prep(w->group, nullptr, 1, pr, w->k, s));
-  if (d.rsum) TERN_HIP(tern::launch_b3_res(w->group, pick_mt(m), nullptr, nullptr, b3_res_units(w), d, w->k, s));
+  const long nres = (long)b3_res_units(w) * d.rslots;
+  if (d.rsum)
+    TERN_HIP(tern::launch_b3_res(w->group, pick_mt(m), nullptr, nullptr, (int)nres, d, w->k, b3_res_lds_cap(nres), s));
   const int items = d.row_blocks * parts;
   const int nwg = std::min(tern_cu_count(), (items + tern::kB3Waves - 1) / tern::kB3Waves);
   TERN_HIP(tern::launch_gemv_b3(w->group, pick_mt(m), nullptr, nullptr, nullptr, nwg, d, items, s));
@@ -1425,7 +1514,7 @@ static tern_status b3_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, v
 size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m) {
   if (count <= 0 || m <= 0 || !w) return 0;
   if (gemm_route(m)) return gemm_batch_ws_bytes(w, count, m);
-  if (b3_route(w[0].format, w[0].group, m)) {
+  if (b3_route_n(w, count, m)) {
     B3Batch b;
     return build_b3_batch(w, nullptr, nullptr, count, m, TERN_F16, nullptr, false, &b) == TERN_OK ? b.total : 0;
   }
@@ -1495,7 +1584,7 @@ tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, vo
                                            (int)b.red.size(), b.red_blocks, s));
     return TERN_OK;
   }
-  if (count > 0 && b3_route(w[0].format, w[0].group, m)) {
+  if (count > 0 && b3_route_n(w, count, m)) {
     B3Batch b;
     TERN_TRY(build_b3_batch(w, x, y, count, m, y_dtype, static_cast<char*>(ws), true, &b));
     if (b.descs.empty()) return TERN_OK;
@@ -1597,7 +1686,7 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
     *out = p;
     return TERN_OK;
   }
-  if (count > 0 && b3_route(w[0].format, w[0].group, m)) {
+  if (count > 0 && b3_route_n(w, count, m)) {
     B3Batch b;
     TERN_TRY(build_b3_batch(w, x, y, count, m, y_dtype, static_cast<char*>(ws), true, &b));
     char* base = static_cast<char*>(ws);
@@ -1734,7 +1823,8 @@ static tern_status plan_launch(const tern_plan* plan, hipStream_t s, hipEvent_t 
     GemvDesc dummy;
     std::memset(&dummy, 0, sizeof(dummy));
     TERN_HIP(tern::launch_b3_prep(plan->group, plan->preps, plan->nprep, none, plan->b3_maxk, s));
-    TERN_HIP(tern::launch_b3_res(plan->group, plan->mt, plan->dev, plan->b3res, plan->nres, dummy, plan->b3_maxk, s));
+    TERN_HIP(tern::launch_b3_res(plan->group, plan->mt, plan->dev, plan->b3res, plan->nres, dummy, plan->b3_maxk,
+                                 b3_res_lds_cap(plan->nres), s));
     if (before) TERN_HIP(hipEventRecord(before, s));
     TERN_HIP(tern::launch_gemv_b3(plan->group, plan->mt, plan->dev, plan->b3items, plan->queue, plan->nwg, dummy,
                                   plan->total_items, s));
@@ -1758,6 +1848,13 @@ static tern_status plan_launch(const tern_plan* plan, hipStream_t s, hipEvent_t 
   }
   if (after) TERN_HIP(hipEventRecord(after, s));
   return TERN_OK;
+}
+
+int64_t tern_b3_min_stages(int64_t stages) {
+  const int64_t before = b3_min_stages();
+  if (stages >= 0) g_b3_min_stages = stages;
+  else if (stages == -1) g_b3_min_stages = -1;
+  return before;
 }
 
 tern_status tern_plan_run(const tern_plan* plan, void* stream) {

@@ -35,7 +35,7 @@ TERN_F32 = 1
 
 SYMBOLS = ["tern_row_stride", "tern_check", "tern_packed_sizes", "tern_workspace_bytes",
            "tern_pack", "tern_unpack", "tern_gemv", "tern_gemm", "tern_batch_workspace_bytes",
-           "tern_gemv_batched", "tern_plan_create", "tern_plan_run", "tern_plan_run_events", "tern_plan_destroy",
+           "tern_gemv_batched", "tern_plan_create", "tern_plan_run", "tern_plan_run_events", "tern_plan_destroy", "tern_b3_min_stages",
            "tern_bits", "tern_quantize", "tern_rotate", "tern_rotate_batched", "tern_read_probe", "tern_status_str", "tern_last_error"]
 
 
@@ -79,6 +79,7 @@ def load() -> ctypes.CDLL:
         "tern_plan_create": (c_int32, [P, POINTER(c_void_p), POINTER(c_void_p), c_int32, c_int32, c_int32, c_void_p, c_size_t, POINTER(c_void_p)]),
         "tern_plan_run": (c_int32, [c_void_p, c_void_p]),
         "tern_plan_run_events": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p]),
+        "tern_b3_min_stages": (ctypes.c_int64, [ctypes.c_int64]),
         "tern_plan_destroy": (None, [c_void_p]),
         "tern_bits": (c_int32, [P, POINTER(c_double), POINTER(c_double), POINTER(c_double)]),
         "tern_quantize": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p,
@@ -341,6 +342,13 @@ def tern_rotate_batched(Rs, xs, outs=None, stream=None):
 def tern_read_probe(buf, sink, stream=None) -> None:
     """Plain streaming read of a whole device tensor (measurement aid)."""
     check(load().tern_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
+
+
+def tern_b3_min_stages(stages: int = -2) -> int:
+    """Threshold (in 64-row stages per launch) from which base-3 products at
+    m <= 4 take the matrix-core stream kernel: stages >= 0 sets it, -1
+    restores the default, -2 queries; returns the value in effect before."""
+    return int(load().tern_b3_min_stages(stages))
 
 
 def tern_bits(pm: PackedMatrix) -> dict:

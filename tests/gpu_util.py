@@ -2,6 +2,7 @@
 ABI, and compare against the CPU oracle."""
 from __future__ import annotations
 
+import contextlib
 import sys
 
 import numpy as np
@@ -9,6 +10,19 @@ import numpy as np
 import oracle as O
 from ternary_weight_only_tern_amd import lib as L
 from ternary_weight_only_tern_amd import synth
+
+
+@contextlib.contextmanager
+def b3_route(route: str):
+    """route "stream": every base-3 launch at m <= 4 takes the matrix-core
+    stream kernel (threshold 0); "auto": the library's default threshold
+    (small launches take the lane-per-row decode)."""
+    if route == "stream":
+        L.tern_b3_min_stages(0)
+    try:
+        yield
+    finally:
+        L.tern_b3_min_stages(-1)
 
 
 def say(*a):

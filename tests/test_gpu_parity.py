@@ -14,12 +14,15 @@ import oracle as O
 from ternary_weight_only_tern_amd import lib as L
 from ternary_weight_only_tern_amd import synth
 
-from gpu_util import (assert_bytes_equal, check_y, oracle_pack, oracle_y, say, small_matrix,
+from gpu_util import (assert_bytes_equal, b3_route, check_y, oracle_pack, oracle_y, say, small_matrix,
                        to_dev, upload_pack)
 
 pytestmark = pytest.mark.gpu
 
 FMTS = [O.FMT_2BIT, O.FMT_B3]
+# formats with the base-3 route forced onto the matrix-core stream kernel as
+# well as the default routing (small launches take the lane-per-row decode)
+FMT_ROUTES = [(O.FMT_2BIT, "auto"), (O.FMT_B3, "auto"), (O.FMT_B3, "stream")]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -145,6 +148,67 @@ def test_gemv_small(shape, fmt, m):
     _gemv_case(mat, fmt, m, x_law="student_t3", seed=m)
 
 
+@pytest.mark.parametrize("shape", SMALL_SHAPES)
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+def test_gemv_small_b3_stream(shape, m):
+    """The small shapes through the base-3 matrix-core stream kernel (the
+    default routing sends launches this small to the lane-per-row decode)."""
+    n, k, g, planes, frac, off = shape
+    say("gemv small b3 stream", shape, m)
+    mat, _ = small_matrix(n, k, g, planes, frac, seed=7 * n + k, offset_mode=off, scale_law="lognormal")
+    with b3_route("stream"):
+        _gemv_case(mat, O.FMT_B3, m, x_law="student_t3", seed=m)
+
+
+@pytest.mark.parametrize("route", ["stream", "auto"])
+@pytest.mark.parametrize("m", [1, 3, 4])
+@pytest.mark.parametrize("planes,off", [(3, O.OFF_ROW), (2, O.OFF_GROUP), (3, O.OFF_NONE)])
+def test_b3_residual_split_units(planes, off, m, route):
+    """Base-3 at m <= 4 with dense residual planes on few rows: the residual
+    pass cuts each plane's entries of a row block into many ranges (units
+    that sum their own rows, the block's last unit adding them in slot
+    order).  Single products (tern_gemv: counters cleared inside the launch
+    sequence) and a plan of both (counters cleared at creation), each run
+    twice (the counters are left clear by the first run); runs are
+    bit-identical."""
+    import torch
+    say("b3 residual split units", planes, off, m, route)
+    with b3_route(route):
+        _residual_split_case(planes, off, m)
+
+
+def _residual_split_case(planes, off, m):
+    import torch
+    mats = [small_matrix(300, 2560, 128, planes, 1.0, seed=90 + planes, offset_mode=off)[0],
+            small_matrix(130, 1280, 128, planes, 0.6, seed=91 + planes, offset_mode=off)[0]]
+    rng = np.random.default_rng(m)
+    xs = [synth.draw_x(rng, m, mat["k"], "student_t3") for mat in mats]
+    pms = [upload_pack(mat, O.FMT_B3) for mat in mats]
+    xds = [to_dev(x.view(np.uint16)).view(torch.float16) for x in xs]
+    refs = [oracle_y(mat, x) for mat, x in zip(mats, xs)]
+    first = []
+    for rep in range(2):
+        for i, (pm, xd) in enumerate(zip(pms, xds)):
+            y = L.tern_gemv(pm, xd, L.TERN_F32)
+            torch.cuda.synchronize()
+            check_y(y, *refs[i], f"single product {i} run {rep}")
+            if rep == 0:
+                first.append(y.clone())
+            else:
+                assert torch.equal(y, first[i]), "runs differ"
+    ys = [torch.empty((m, pm.n), dtype=torch.float32, device="cuda") for pm in pms]
+    plan = L.Plan(pms, xds, ys, y_dtype=L.TERN_F32)
+    prev = None
+    for rep in range(2):
+        plan.run()
+        torch.cuda.synchronize()
+        for i, y in enumerate(ys):
+            check_y(y, *refs[i], f"plan product {i} run {rep}")
+        if prev is not None:
+            assert all(torch.equal(a, b) for a, b in zip(prev, ys)), "plan runs differ"
+        prev = [y.clone() for y in ys]
+
+
 @pytest.mark.parametrize("m", [9, 17, 32, 33, 63])
 def test_gemv_m_chunks(m):
     say("gemv chunks", m)
@@ -184,7 +248,13 @@ def test_gemv_qwen3_8b_layer(m):
         _gemv_case(mat, O.FMT_B3, m, seed=10 * m + proj)
 
 
-def test_gemv_zero_and_sign_invariants():
+@pytest.mark.parametrize("route", ["auto", "stream"])
+def test_gemv_zero_and_sign_invariants(route):
+    with b3_route(route):
+        _invariants_case()
+
+
+def _invariants_case():
     import torch
     say("gemv invariants")
     mat, rng = small_matrix(200, 1280, 128, 3, 0.2, seed=12, offset_mode=O.OFF_ROW)
@@ -224,8 +294,13 @@ def test_gemv_degenerate_shapes():
             check_y(y, y_ref, b, "n=1")
 
 
-@pytest.mark.parametrize("fmt", FMTS)
-def test_batched_and_plan_match_oracle(fmt):
+@pytest.mark.parametrize("fmt,route", FMT_ROUTES)
+def test_batched_and_plan_match_oracle(fmt, route):
+    with b3_route(route):
+        _batched_and_plan_case(fmt)
+
+
+def _batched_and_plan_case(fmt):
     """The 4B-class layer through one grouped launch and through a plan (whose
     2-bit residual entries come from a plan-time index and are added in entry
     order after the K parts are combined, so its rounding may differ from the
@@ -519,8 +594,13 @@ def test_dense_residual_lists_in_windows(group, m):
         check_y(y, y_ref, b, f"plan dense residual m={m} i={i}")
 
 
-@pytest.mark.parametrize("fmt", FMTS)
-def test_plan_graph_replays_match_eager(fmt):
+@pytest.mark.parametrize("fmt,route", FMT_ROUTES)
+def test_plan_graph_replays_match_eager(fmt, route):
+    with b3_route(route):
+        _graph_replays_case(fmt)
+
+
+def _graph_replays_case(fmt):
     """A plan captured into a HIP graph: a single product cut into K parts
     (its row blocks' arrival counters must be left clear by every run) and
     a seven-product layer, replayed several times with eager launches and
@@ -633,8 +713,13 @@ def test_qwen3_8b_stack_plan_matches_oracle():
             del mat
 
 
-@pytest.mark.parametrize("fmt", FMTS)
-def test_plan_recreated_after_repack(fmt):
+@pytest.mark.parametrize("fmt,route", FMT_ROUTES)
+def test_plan_recreated_after_repack(fmt, route):
+    with b3_route(route):
+        _recreate_case(fmt)
+
+
+def _recreate_case(fmt):
     """A plan keeps tables derived from the packed matrices (the residual
     index built from masks, row pointers and residual scales), so after the
     buffers are packed again with other contents a new plan is created: it
