@@ -161,6 +161,22 @@ tern_status tern_unpack(const tern_matrix *src, int8_t *trits, void *ws, size_t 
 tern_status tern_gemv(const tern_matrix *w, const uint16_t *x, int32_t m, void *y,
                       int32_t y_dtype, void *ws, size_t ws_bytes, void *stream);
 
+/* tern_gemv for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same product, with the workspace in a fixed device array inside the
+ * library of TERN_NOALLOC_WORKSPACE_BYTES (16 MiB) per GPU, held by each GPU
+ * the library runs on until the process ends.  Calls no hipMalloc or hipFree.
+ * A product whose tern_workspace_bytes(w, m) exceeds that size returns
+ * TERN_E_WORKSPACE (use tern_gemv with a workspace); 16 MiB covers every
+ * m <= 63 product of the Qwen3-4B and -8B shapes.  Every call on a GPU uses
+ * that GPU's one array: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and must be ordered by the caller.  The
+ * remaining rules are tern_gemv's (up to m = 32 it copies work tables from
+ * host memory, so those calls are not for graph capture). */
+#define TERN_NOALLOC_WORKSPACE_BYTES ((size_t)16 << 20)
+tern_status tern_gemv_noalloc(const tern_matrix *w, const uint16_t *x, int32_t m, void *y,
+                              int32_t y_dtype, void *stream);
+
 /* y = x W^T for any m >= 0 through FP16 MFMA on tiles decoded into LDS
  * (tuned for m >= 64).  Supports group in {64, 128}; other groups return
  * TERN_E_UNSUPPORTED.  ws: tern_workspace_bytes(w, m). */

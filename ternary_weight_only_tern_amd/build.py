@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtern.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["tern_api.cpp", "pack.hip", "gemv.hip", "gemv_mfma.hip", "gemv_b3.hip", "gemm.hip", "quant.hip",
+SOURCES = ["tern_api.cpp", "pack.hip", "gemv.hip", "gemv_mfma.hip", "gemv_b3.hip", "gemm.hip", "quant.hip", "noalloc.hip",
            "rotate.hip"]
 ARCH = os.environ.get("TERN_OFFLOAD_ARCH", "gfx950")
 

@@ -6,7 +6,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "tern.h"
+
 namespace tern {
+
+// Records msg as the calling thread's last error (tern_last_error) and
+// returns s (host code).
+tern_status record_failure(tern_status s, const char* msg);
 
 constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kGemvRows = 64;      // rows per decode work item: one row per lane

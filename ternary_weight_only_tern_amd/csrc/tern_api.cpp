@@ -34,6 +34,12 @@ tern_status hip_fail(hipError_t e, const char* what) {
   return fail(TERN_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+}  // namespace
+
+tern_status tern::record_failure(tern_status s, const char* msg) { return fail(s, "%s", msg); }
+
+namespace {
+
 #define TERN_HIP(call)                                  \
   do {                                                  \
     hipError_t e_ = (call);                             \

@@ -35,7 +35,7 @@ TERN_F32 = 1
 
 SYMBOLS = ["tern_row_stride", "tern_check", "tern_packed_sizes", "tern_workspace_bytes",
            "tern_pack", "tern_unpack", "tern_gemv", "tern_gemm", "tern_batch_workspace_bytes",
-           "tern_gemv_batched", "tern_plan_create", "tern_plan_run", "tern_plan_run_events", "tern_plan_destroy", "tern_b3_min_stages",
+           "tern_gemv_batched", "tern_plan_create", "tern_plan_run", "tern_plan_run_events", "tern_plan_destroy", "tern_b3_min_stages", "tern_gemv_noalloc",
            "tern_bits", "tern_quantize", "tern_rotate", "tern_rotate_batched", "tern_read_probe", "tern_status_str", "tern_last_error"]
 
 
@@ -80,6 +80,7 @@ def load() -> ctypes.CDLL:
         "tern_plan_run": (c_int32, [c_void_p, c_void_p]),
         "tern_plan_run_events": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p]),
         "tern_b3_min_stages": (ctypes.c_int64, [ctypes.c_int64]),
+        "tern_gemv_noalloc": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p]),
         "tern_plan_destroy": (None, [c_void_p]),
         "tern_bits": (c_int32, [P, POINTER(c_double), POINTER(c_double), POINTER(c_double)]),
         "tern_quantize": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p,
@@ -226,6 +227,15 @@ def _product(fn, pm, x, y_dtype, out, stream, ws):
 
 def tern_gemv(pm, x, y_dtype=TERN_F16, out=None, stream=None, ws=None):
     return _product(load().tern_gemv, pm, x, y_dtype, out, stream, ws)
+
+
+def tern_gemv_noalloc(pm, x, out, y_dtype=TERN_F16, stream=None):
+    """tern_gemv with the library's fixed per-GPU workspace: the caller
+    passes the output tensor `out` ([m][n], fp16 or fp32 per y_dtype); no
+    device memory is allocated."""
+    d = pm.desc()
+    check(load().tern_gemv_noalloc(ctypes.byref(d), _ptr(x), x.shape[0], _ptr(out), y_dtype, _stream(stream)))
+    return out
 
 
 def tern_gemm(pm, x, y_dtype=TERN_F16, out=None, stream=None, ws=None):
