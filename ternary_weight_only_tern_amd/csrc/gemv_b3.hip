@@ -126,16 +126,16 @@ __device__ __forceinline__ int x5_pos(int c, int h) {
 // block of 256 chunks (one per thread; group sums by the threads of block 0,
 // one group each, in position order).
 template <int G>
-__global__ __launch_bounds__(256) void b3_prep_kernel(const B3Prep* __restrict__ preps, B3Prep one) {
+__device__ __forceinline__ void b3_prep_block(const B3Prep* __restrict__ preps, const B3Prep& one, int bx, int by) {
   using Gm = B3Geo<G>;
-  const B3Prep p = preps ? preps[blockIdx.y / 4] : one;
-  const int m = blockIdx.y % 4;
-  if (p.zero && blockIdx.x == 0 && m == 0)
+  const B3Prep p = preps ? preps[by / 4] : one;
+  const int m = by % 4;
+  if (p.zero && bx == 0 && m == 0)
     for (int i = threadIdx.x; i < p.nzero; i += 256) p.zero[i] = 0u;
   if (m >= p.m) return;
   const int ng = p.k / G;
   const uint16_t* xr = p.x + (size_t)m * p.k;
-  const int c = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  const int c = bx * 256 + (int)threadIdx.x;
   if (c < ng * Gm::CPG) {
     const int g = c / Gm::CPG, cc = c % Gm::CPG;
     uint32_t v[2];
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void b3_prep_kernel(const B3Prep* __restrict__
     }
     *reinterpret_cast<u2_t*>(p.x5 + ((size_t)m * ng * Gm::CPG + c) * 4) = u2_t{v[0], v[1]};
   }
-  if (p.xs && blockIdx.x == 0) {
+  if (p.xs && bx == 0) {
     for (int g = threadIdx.x; g < ng; g += 256) {
       const u4_t* xg = reinterpret_cast<const u4_t*>(xr + (size_t)g * G);
       u4_t w[G / 8];
@@ -164,6 +164,11 @@ __global__ __launch_bounds__(256) void b3_prep_kernel(const B3Prep* __restrict__
       p.xs[(size_t)m * ng + g] = s;
     }
   }
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void b3_prep_kernel(const B3Prep* __restrict__ preps, B3Prep one) {
+  b3_prep_block<G>(preps, one, (int)blockIdx.x, (int)blockIdx.y);
 }
 
 // 16 bytes per lane from a buffer straight into LDS: lane l writes dst + 16 l
@@ -373,19 +378,33 @@ constexpr int res_lds_bytes(int max_k, int lds_cap) {
 template <int G, int MT, bool TABLE>
 __global__ __launch_bounds__(kResThreads) void b3_res_kernel(const GemvDesc* __restrict__ descs,
                                                              const B3ResItem* __restrict__ units, GemvDesc one,
-                                                             int window) {
+                                                             int window, int nunits,
+                                                             const B3Prep* __restrict__ preps, int prep_bx) {
   constexpr int GP = 2 * G + 16;
   constexpr int CPGX = 2 * G / 16;
+  if constexpr (TABLE) {
+    // workgroups past the units prepare the activation layouts of the
+    // product launch that follows (one launch less)
+    if ((int)blockIdx.x >= nunits) {
+      const int pb = (int)blockIdx.x - nunits;
+      B3Prep none{};
+      b3_prep_block<G>(preps, none, pb % prep_bx, pb / prep_bx);
+      return;
+    }
+  }
   extern __shared__ uint4 res_smem[];
   uint8_t* xw = reinterpret_cast<uint8_t*>(res_smem);
   float* vals = reinterpret_cast<float*>(xw + window);
   GemvDesc d;
   int rb, slot;
+  uint32_t ua0 = 0, ua1 = 0;
   if constexpr (TABLE) {
     const B3ResItem u = units[blockIdx.x];
     d = descs[u.desc];
     rb = (int)u.rb;
     slot = (int)u.slot;
+    ua0 = u.a0;
+    ua1 = u.a1;
   } else {
     d = one;
     rb = (int)blockIdx.x / d.rslots;
@@ -429,10 +448,15 @@ __global__ __launch_bounds__(kResThreads) void b3_res_kernel(const GemvDesc* __r
   const GLOBAL u4_t* blocks = reinterpret_cast<const GLOBAL u4_t*>(gp(rplane == 1 ? d.blocks[1] : d.blocks[0]));
   uint32_t A0 = 0, A1 = 0, rp_lo = 0, rp_hi = 0;
   if (rplane >= 0) {
-    const uint32_t E0 = rowptr[r0], E1 = rowptr[rlast];
-    const uint64_t len = E1 - E0;
-    A0 = E0 + (uint32_t)(len * (uint64_t)rpart_ix / (uint64_t)d.rsplit);
-    A1 = E0 + (uint32_t)(len * (uint64_t)(rpart_ix + 1) / (uint64_t)d.rsplit);
+    if constexpr (TABLE) {  // prepared with the table (launch_b3_res_ranges)
+      A0 = ua0;
+      A1 = ua1;
+    } else {
+      const uint32_t E0 = rowptr[r0], E1 = rowptr[rlast];
+      const uint64_t len = E1 - E0;
+      A0 = E0 + (uint32_t)(len * (uint64_t)rpart_ix / (uint64_t)d.rsplit);
+      A1 = E0 + (uint32_t)(len * (uint64_t)(rpart_ix + 1) / (uint64_t)d.rsplit);
+    }
     rp_lo = row_ok ? rowptr[row] : 0u;
     rp_hi = row_ok ? rowptr[row + 1] : 0u;
   }
@@ -803,26 +827,29 @@ hipError_t launch_b3_g(int mt, const GemvDesc* descs, const B3Item* items, uint3
 
 template <int G, int MT>
 hipError_t launch_res_mt(const GemvDesc* descs, const B3ResItem* units, int nunits, const GemvDesc& one, int max_k,
-                         int lds_cap, hipStream_t s) {
+                         int lds_cap, const B3Prep* preps, int nprep, int prep_max_k, hipStream_t s) {
   const int window = res_window<G, MT>(max_k, lds_cap);
   if (window < MT * (2 * G + 16)) return hipErrorInvalidValue;  // not one group fits
   const size_t lds = (size_t)res_lds_bytes<G, MT>(max_k, lds_cap);
-  if (units)
-    hipLaunchKernelGGL((b3_res_kernel<G, MT, true>), dim3(nunits), dim3(kResThreads), lds, s, descs, units, one,
-                       window);
-  else
+  if (units) {
+    const int prep_bx = std::max(1, (prep_max_k / G * B3Geo<G>::CPG + 255) / 256);
+    const int prep_blocks = preps ? prep_bx * nprep * 4 : 0;
+    hipLaunchKernelGGL((b3_res_kernel<G, MT, true>), dim3(nunits + prep_blocks), dim3(kResThreads), lds, s, descs,
+                       units, one, window, nunits, preps, prep_bx);
+  } else {
     hipLaunchKernelGGL((b3_res_kernel<G, MT, false>), dim3(nunits), dim3(kResThreads), lds, s, descs, units, one,
-                       window);
+                       window, nunits, preps, 1);
+  }
   return hipGetLastError();
 }
 
 template <int G>
 hipError_t launch_res_g(int mt, const GemvDesc* descs, const B3ResItem* units, int nunits, const GemvDesc& one,
-                        int max_k, int lds_cap, hipStream_t s) {
+                        int max_k, int lds_cap, const B3Prep* preps, int nprep, int prep_max_k, hipStream_t s) {
   switch (mt) {
-    case 1: return launch_res_mt<G, 1>(descs, units, nunits, one, max_k, lds_cap, s);
-    case 2: return launch_res_mt<G, 2>(descs, units, nunits, one, max_k, lds_cap, s);
-    case 4: return launch_res_mt<G, 4>(descs, units, nunits, one, max_k, lds_cap, s);
+    case 1: return launch_res_mt<G, 1>(descs, units, nunits, one, max_k, lds_cap, preps, nprep, prep_max_k, s);
+    case 2: return launch_res_mt<G, 2>(descs, units, nunits, one, max_k, lds_cap, preps, nprep, prep_max_k, s);
+    case 4: return launch_res_mt<G, 4>(descs, units, nunits, one, max_k, lds_cap, preps, nprep, prep_max_k, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -830,11 +857,41 @@ hipError_t launch_res_g(int mt, const GemvDesc* descs, const B3ResItem* units, i
 }  // namespace
 
 hipError_t launch_b3_res(int group, int mt, const GemvDesc* descs, const B3ResItem* units, int nunits,
-                         const GemvDesc& one, int max_k, int lds_cap, hipStream_t s) {
+                         const GemvDesc& one, int max_k, int lds_cap, const B3Prep* preps, int nprep, int prep_max_k,
+                         hipStream_t s) {
   if (nunits <= 0) return hipSuccess;
-  if (group == 64) return launch_res_g<64>(mt, descs, units, nunits, one, max_k, lds_cap, s);
-  if (group == 128) return launch_res_g<128>(mt, descs, units, nunits, one, max_k, lds_cap, s);
+  if (group == 64) return launch_res_g<64>(mt, descs, units, nunits, one, max_k, lds_cap, preps, nprep, prep_max_k, s);
+  if (group == 128) return launch_res_g<128>(mt, descs, units, nunits, one, max_k, lds_cap, preps, nprep, prep_max_k, s);
   return hipErrorInvalidValue;
+}
+
+namespace {
+// The entry range [a0, a1) of every residual-pass unit of a table: its part
+// of its plane's entries of its row block.
+__global__ __launch_bounds__(256) void b3_res_ranges_kernel(const GemvDesc* __restrict__ descs,
+                                                            B3ResItem* __restrict__ units, int nunits) {
+  const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  if (i >= nunits) return;
+  B3ResItem u = units[i];
+  const GemvDesc& d = descs[u.desc];
+  u.a0 = u.a1 = 0u;
+  if (d.planes > 1) {
+    const int rplane = (int)u.slot / d.rsplit, part = (int)u.slot % d.rsplit;
+    const uint32_t* rowptr = rplane == 1 ? d.rowptr[1] : d.rowptr[0];
+    const int r0 = (int)u.rb * kB3ResRows, rlast = min(r0 + kB3ResRows, d.n);
+    const uint32_t E0 = rowptr[r0], E1 = rowptr[rlast];
+    const uint64_t len = E1 - E0;
+    u.a0 = E0 + (uint32_t)(len * (uint64_t)part / (uint64_t)d.rsplit);
+    u.a1 = E0 + (uint32_t)(len * (uint64_t)(part + 1) / (uint64_t)d.rsplit);
+  }
+  units[i] = u;
+}
+}  // namespace
+
+hipError_t launch_b3_res_ranges(const GemvDesc* descs, B3ResItem* units, int nunits, hipStream_t s) {
+  if (nunits <= 0) return hipSuccess;
+  hipLaunchKernelGGL(b3_res_ranges_kernel, dim3((nunits + 255) / 256), dim3(256), 0, s, descs, units, nunits);
+  return hipGetLastError();
 }
 
 int b3_chunks_per_group(int group) { return group == 64 ? B3Geo<64>::CPG : B3Geo<128>::CPG; }

@@ -175,13 +175,22 @@ struct B3ResItem {
   uint32_t desc;
   uint32_t rb;
   uint32_t slot;
+  uint32_t a0, a1;  // the unit's entries (launch_b3_res_ranges)
 };
+// Fills a0 and a1 of every unit of a table from the row pointers (after the
+// descriptors and units are in device memory; again whenever rowptr changes).
+hipError_t launch_b3_res_ranges(const GemvDesc* descs, B3ResItem* units, int nunits, hipStream_t stream);
 // nunits workgroups over units (device), or with units == NULL the units
 // (row block * rslots + slot) of the single descriptor `one`.  max_k: the
 // longest k; lds_cap: the most LDS bytes a workgroup may take (a large
 // activation window for launches of few units, smaller ones for occupancy).
+// With units, the nprep activation preparations in preps (device; longest
+// k prep_max_k; none when preps is NULL) run in the same launch, as
+// launch_b3_prep would (their zero fields must be NULL: the units do not
+// wait for them).  Nothing is launched when nunits is 0.
 hipError_t launch_b3_res(int group, int mt, const GemvDesc* descs, const B3ResItem* units, int nunits,
-                         const GemvDesc& one, int max_k, int lds_cap, hipStream_t stream);
+                         const GemvDesc& one, int max_k, int lds_cap, const B3Prep* preps, int nprep,
+                         int prep_max_k, hipStream_t stream);
 // preps (device) holds count preparations; with preps == NULL, `one` alone;
 // max_k: the longest k among them.
 hipError_t launch_b3_prep(int group, const B3Prep* preps, int count, const B3Prep& one, int max_k, hipStream_t stream);

@@ -1344,7 +1344,7 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
     if (b3_has_res(&w[i]))
       for (int u = 0; u < b3_res_units(&w[i]); ++u)
         for (int sl = 0; sl < d.rslots; ++sl)
-          b->res.push_back({(uint32_t)b->descs.size(), (uint32_t)u, (uint32_t)sl});
+          b->res.push_back({(uint32_t)b->descs.size(), (uint32_t)u, (uint32_t)sl, 0u, 0u});
     for (int p = 0; p + 1 < w[i].planes; ++p) {
       uint32_t* gidx = ws ? reinterpret_cast<uint32_t*>(ws + gi_off[2 * i + p]) : nullptr;
       d.gidx[p] = gidx;
@@ -1425,7 +1425,10 @@ static tern_status upload_b3_batch(const B3Batch& b, char* ws, hipStream_t s, bo
   if (b.nctr) TERN_HIP(sync ? hipMemset(ws + b.ctr_off, 0, b.nctr * 4) : hipMemsetAsync(ws + b.ctr_off, 0, b.nctr * 4, s));
   for (const B3Index& ix : b.index)
     TERN_HIP(tern::launch_res_index(ix.mask, ix.rowptr, ix.rscale, ix.n, ix.mwords, ix.gidx, sync ? nullptr : s));
-  if (sync && !b.index.empty()) TERN_HIP(hipStreamSynchronize(nullptr));
+  TERN_HIP(tern::launch_b3_res_ranges(reinterpret_cast<const GemvDesc*>(ws + b.descs_off),
+                                      reinterpret_cast<tern::B3ResItem*>(ws + b.res_off), (int)b.res.size(),
+                                      sync ? nullptr : s));
+  if (sync && (!b.index.empty() || !b.res.empty())) TERN_HIP(hipStreamSynchronize(nullptr));
   return TERN_OK;
 }
 
@@ -1435,11 +1438,13 @@ static tern_status run_b3_batch(const B3Batch& b, int group, char* ws, hipStream
   std::memset(&none, 0, sizeof(none));
   GemvDesc dummy;
   std::memset(&dummy, 0, sizeof(dummy));
-  TERN_HIP(tern::launch_b3_prep(group, reinterpret_cast<const tern::B3Prep*>(ws + b.preps_off), (int)b.preps.size(),
-                                none, b.max_k, s));
-  TERN_HIP(tern::launch_b3_res(group, b.mt, reinterpret_cast<const GemvDesc*>(ws + b.descs_off),
-                               reinterpret_cast<const tern::B3ResItem*>(ws + b.res_off), (int)b.res.size(), dummy,
-                               b.max_k, b3_res_lds_cap((long)b.res.size()), s));
+  const tern::B3Prep* preps = reinterpret_cast<const tern::B3Prep*>(ws + b.preps_off);
+  if (b.res.empty())
+    TERN_HIP(tern::launch_b3_prep(group, preps, (int)b.preps.size(), none, b.max_k, s));
+  else  // the preparations ride along in the residual pass's launch
+    TERN_HIP(tern::launch_b3_res(group, b.mt, reinterpret_cast<const GemvDesc*>(ws + b.descs_off),
+                                 reinterpret_cast<const tern::B3ResItem*>(ws + b.res_off), (int)b.res.size(), dummy,
+                                 b.max_k, b3_res_lds_cap((long)b.res.size()), preps, (int)b.preps.size(), b.max_k, s));
   TERN_HIP(tern::launch_gemv_b3(group, b.mt, reinterpret_cast<const GemvDesc*>(ws + b.descs_off),
                                 reinterpret_cast<const tern::B3Item*>(ws + b.items_off),
                                 reinterpret_cast<uint32_t*>(ws + b.queue_off), b.nwg, dummy,
@@ -1509,7 +1514,8 @@ static tern_status b3_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, v
   TERN_HIP(tern::launch_b3_prep(w->group, nullptr, 1, pr, w->k, s));
   const long nres = (long)b3_res_units(w) * d.rslots;
   if (d.rsum)
-    TERN_HIP(tern::launch_b3_res(w->group, pick_mt(m), nullptr, nullptr, (int)nres, d, w->k, b3_res_lds_cap(nres), s));
+    TERN_HIP(tern::launch_b3_res(w->group, pick_mt(m), nullptr, nullptr, (int)nres, d, w->k, b3_res_lds_cap(nres),
+                                 nullptr, 0, 0, s));
   const int items = d.row_blocks * parts;
   const int nwg = std::min(tern_cu_count(), (items + tern::kB3Waves - 1) / tern::kB3Waves);
   TERN_HIP(tern::launch_gemv_b3(w->group, pick_mt(m), nullptr, nullptr, nullptr, nwg, d, items, s));
@@ -1828,9 +1834,11 @@ static tern_status plan_launch(const tern_plan* plan, hipStream_t s, hipEvent_t 
     std::memset(&none, 0, sizeof(none));
     GemvDesc dummy;
     std::memset(&dummy, 0, sizeof(dummy));
-    TERN_HIP(tern::launch_b3_prep(plan->group, plan->preps, plan->nprep, none, plan->b3_maxk, s));
-    TERN_HIP(tern::launch_b3_res(plan->group, plan->mt, plan->dev, plan->b3res, plan->nres, dummy, plan->b3_maxk,
-                                 b3_res_lds_cap(plan->nres), s));
+    if (plan->nres == 0)
+      TERN_HIP(tern::launch_b3_prep(plan->group, plan->preps, plan->nprep, none, plan->b3_maxk, s));
+    else  // the preparations ride along in the residual pass's launch
+      TERN_HIP(tern::launch_b3_res(plan->group, plan->mt, plan->dev, plan->b3res, plan->nres, dummy, plan->b3_maxk,
+                                   b3_res_lds_cap(plan->nres), plan->preps, plan->nprep, plan->b3_maxk, s));
     if (before) TERN_HIP(hipEventRecord(before, s));
     TERN_HIP(tern::launch_gemv_b3(plan->group, plan->mt, plan->dev, plan->b3items, plan->queue, plan->nwg, dummy,
                                   plan->total_items, s));
