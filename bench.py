@@ -633,7 +633,8 @@ def main():
     med = float(np.median(r["step_ms"]))
     kern_s = float(np.mean(r["kern_ms"])) / 1e3
     log(f"bench: stack {r['stack_bytes']} B, {r['step_s']*1e6:.1f} us/token (median {med*1e3:.1f}), "
-        f"{r['stack_bytes'] / r['step_s'] / 1e9:.1f} GB/s; stream kernel {kern_s*1e6:.1f} us = "
+        f"{r['stack_bytes'] / r['step_s'] / 1e9:.1f} GB/s; stream kernel {kern_s*1e6:.1f} us "
+        f"(event mean over {r['steps']} launches) for {r['kern_bytes']} algorithmic bytes = "
         f"{r['kern_bytes'] / kern_s / 1e9:.1f} GB/s")
     if args.stack8b_only:
         return
