@@ -485,9 +485,9 @@ def cpu_baseline(budget_s=12.0):
                 break
     dt = time.perf_counter() - t0
     return dict(value=round(nbytes / dt / 1e9, 6), unit="GB/s", cores=1, kind="oracle",
-                sample=f"{done} pass(es) over the 7 projections of layer 0 of the Qwen3-8B-class stack "
-                       f"(base-3, M=1; {nmat} products, {nbytes} packed bytes), fp64 unpack-and-dot, 1 thread, "
-                       f"{dt:.1f} s",
+                sample=f"{done} pass(es) over the {len(packed)} projections of layer 0 of the Qwen3-8B-class stack "
+                       f"(base-3, M=1; {nmat} products and {nbytes} packed bytes in all), fp64 unpack-and-dot, "
+                       f"1 thread, {dt:.1f} s",
                 tokens_per_s_equiv=round(nbytes / dt / (LAYERS * sum(O.bits(pk)["total_bytes"] for pk in packed)), 8))
 
 

@@ -142,7 +142,10 @@ tern_status tern_pack(const int8_t *trits, const uint16_t *rscale_dense, const t
                       void *ws, size_t ws_bytes, void *stream);
 
 /* Unpack to device int8 [planes][n][k] (zeros outside the residual masks) and
- * validate the artifact.  Synchronises stream.  TERN_E_CORRUPT on a 2-bit
+ * validate the artifact (the pages check an artifact before trusting it:
+ * "Post-Training Ternarization of Qwen3-4B" §11.3, a checkpoint that was not
+ * ternary was rejected by verification, and §9.2, a lossy packing that had
+ * dropped a plane).  ws: tern_workspace_bytes(src, 1).  Synchronises stream.  TERN_E_CORRUPT on a 2-bit
  * code 10, a base-3 byte above 242, a non-zero base-3 padding trit or a
  * rowptr that disagrees with the mask popcounts. */
 tern_status tern_unpack(const tern_matrix *src, int8_t *trits, void *ws, size_t ws_bytes,
@@ -152,8 +155,12 @@ tern_status tern_unpack(const tern_matrix *src, int8_t *trits, void *ws, size_t 
  * "Can ternary LLMs hit 1.58 bits per weight", How It Works, and 2609.09240's
  * direct packed execution).  m == 0 is a no-op; m >= 64 is
  * TERN_E_UNSUPPORTED (use tern_gemm).  ws: tern_workspace_bytes(w, m).
- * Up to m = 2 (base-3), 5 (2-bit, group 128) or 4 (2-bit, group 64) the
- * decode kernels run; from there to m = 32 the 16-row matrix-core product
+ * Up to m = 4 (base-3), 5 (2-bit, group 128) or 4 (2-bit, group 64) the
+ * decode kernels run (base-3: the matrix-core stream kernel with a separate
+ * residual pass when the product holds at least tern_b3_min_stages stages,
+ * the lane-per-row decode below that; K parts, when the product is too
+ * small to fill the GPU, are summed by a second kernel); from there to
+ * m = 32 the 16-row matrix-core product
  * of tern_gemv_batched, which copies its work tables from host memory into
  * ws (hipMemcpyAsync on stream) on each call, so such calls must not be
  * captured into a HIP graph (use a plan); from m = 33 the tiles of
@@ -178,19 +185,31 @@ tern_status tern_gemv_noalloc(const tern_matrix *w, const uint16_t *x, int32_t m
                               int32_t y_dtype, void *stream);
 
 /* y = x W^T for any m >= 0 through FP16 MFMA on tiles decoded into LDS
- * (tuned for m >= 64).  Supports group in {64, 128}; other groups return
- * TERN_E_UNSUPPORTED.  ws: tern_workspace_bytes(w, m). */
+ * (tuned for m >= 64): the same direct product from the packed planes as
+ * tern_gemv ("Post-Training Ternarization of Qwen3-4B" §10.2, a packed
+ * kernel reading the encoded planes; 2609.09240's direct packed execution),
+ * for many activation rows at once (prefill, batched decode; the pages
+ * measure one row).  Supports group in {64, 128}; other groups return
+ * TERN_E_UNSUPPORTED.  ws: tern_workspace_bytes(w, m) (unused today). */
 tern_status tern_gemm(const tern_matrix *w, const uint16_t *x, int32_t m, void *y,
                       int32_t y_dtype, void *ws, size_t ws_bytes, void *stream);
 
 /* Grouped product: count independent products y[i] = x[i] W[i]^T with the
  * same m, format, group and output dtype, in one launch (the layer's
- * projections of one token batch, say), products with the longest K first:
- *   m <= 2 (base-3), 5 (2-bit, group 128) or 4 (2-bit, group 64): the
- *     decode kernels, one workgroup per block of output rows (2-bit: work
+ * projections of one token batch, say; the direct packed runtime of
+ * 2609.09240 runs every linear layer of the model from its packed planes,
+ * and this call runs a layer's, or a whole stack's, in one go), products
+ * with the longest K first:
+ *   m <= 4 (base-3), 5 (2-bit, group 128) or 4 (2-bit, group 64): the
+ *     decode kernels.  2-bit: one workgroup per block of output rows, work
  *     items packed onto the CUs by size, products longer than a workgroup's
- *     activation stage cut into K parts; base-3: products of at least twice
- *     the shortest K cut into K parts);
+ *     activation stage cut into K parts.  Base-3, launches of at least
+ *     tern_b3_min_stages stages: the activation layout and the residual pass
+ *     (residual planes and offsets, FP32 row sums), then the persistent
+ *     matrix-core stream kernel over 64-row items taken from per-XCD queues;
+ *     products that read the same x (pointer and k) share its staged layout.
+ *     Smaller base-3 launches: the lane-per-row decode, products of at least
+ *     twice the shortest K cut into K parts;
  *   up to m = 32: FP16 MFMA on 16-row tiles decoded into LDS, K split into
  *     ranges of 4-step multiples;
  *   m >= 33: the matrix-core path of tern_gemm over every product's tiles,
@@ -214,15 +233,20 @@ tern_status tern_gemv_batched(const tern_matrix *w, const uint16_t *const *x, vo
 
 /* A prepared grouped product.  tern_plan_create copies the work tables into
  * the caller's device buffer `ws` of tern_batch_workspace_bytes bytes (which
- * also holds the plan's partials, K-part arrival counters -- cleared here,
- * and left clear by every run -- and residual index; synchronously) and
- * returns a host
- * handle (malloc'ed; free it with tern_plan_destroy).  tern_plan_run
- * launches the whole batch on stream; it may be called any number of times
- * and captured in a HIP graph.  The buffers named in the plan must stay
- * valid while the plan is used.  Runs of one plan (or of plans, or batched
- * calls, that share a workspace) use the same partials and K-part counters,
- * so runs that overlap in time race: order them on one stream. */
+ * also holds the plan's partials, arrival and queue counters -- cleared
+ * here, and left clear by every run -- and the tables it derives from the
+ * matrices; synchronously) and returns a host handle (malloc'ed; free it
+ * with tern_plan_destroy).  tern_plan_run launches the whole batch on
+ * stream; it may be called any number of times and captured in a HIP graph.
+ * The buffers named in the plan must stay valid while the plan is used, and
+ * their contents must not change in ways the plan has read: the plan keeps
+ * tables derived from the masks, row pointers and residual scales (the
+ * residual index, the residual pass's entry ranges, tile entry bounds), so
+ * after a matrix is packed again (or those arrays change) the plan must be
+ * created again; plane-0 bytes, scales, offsets and x may change between
+ * runs.  Runs of one plan (or of plans, or batched calls, that share a
+ * workspace) use the same partials and counters, so runs that overlap in
+ * time race: order them on one stream. */
 typedef struct tern_plan tern_plan;
 tern_status tern_plan_create(const tern_matrix *w, const uint16_t *const *x, void *const *y,
                              int32_t count, int32_t m, int32_t y_dtype, void *ws,
