@@ -46,6 +46,7 @@ __device__ __forceinline__ uint32_t pk_add(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, a) + __builtin_bit_cast(h2_t, b));
 }
 __device__ __forceinline__ uint32_t splat(uint32_t h) { return (h & 0xFFFFu) * 0x10001u; }
+__device__ __forceinline__ float h2f_bits(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
 
 // Base-3 byte -> five 2-bit codes at bits 0..9 (trit i at bits 2i..2i+1).
 __device__ __forceinline__ uint32_t b3_codes(uint32_t v) {
@@ -134,16 +135,24 @@ __device__ __forceinline__ void walk_next(int g, Walk<NP>& W) {
   }
 }
 
-// 2*W~ for the thread's 32 trits as 16 FP16 pairs in K order:
-// 2*(s0*t0 + m1*s1*t1 + m2*s2*t2 + off) with FP16 fused multiply-adds.  prep()
-// reads the packed bytes from the LDS window and takes the scales, pair(i)
-// forms pair i, store() writes four pairs to LDS; the product loop calls them
-// one piece at a time between its MFMAs.
-template <int FMT, int G, int NP, int A>
+// The decoded weights of the thread's 32 trits as 16 FP16 pairs in K order.
+// Narrow (WIDE false): 2*W~ = 2*(s0*t0 + m1*s1*t1 + m2*s2*t2 + off) with FP16
+// fused multiply-adds, for products whose chain rounds at most once (no
+// offset and at most one residual plane, or an offset and no residual plane:
+// the first multiply-add of (2t) * s is exact).  Wide: W~ formed in FP32 from
+// exact products (2t) * (s/2) and rounded once to FP16, for products with an
+// offset and residual planes, or two residual planes, whose FP16 chain
+// would round two or three times; the tile then holds W~ instead of 2*W~ (the
+// epilogue scales by 1 instead of 0.5).  prep() reads the packed bytes from
+// the LDS window and takes the scales, pair(i) forms pair i, store() writes
+// four pairs to LDS; the product loop calls them one piece at a time between
+// its MFMAs.
+template <int FMT, int G, int NP, int A, bool WIDE>
 struct Dec {
   static constexpr int B0 = A / 5, NB = (A + 31) / 5 - B0 + 1;
   uint32_t out[16];
-  uint32_t s0, o2, s1[NP > 0 ? NP : 1];
+  uint32_t s0, o2, s1[NP > 0 ? NP : 1];  // narrow: FP16 pairs
+  float s0h, of, s1h[NP > 0 ? NP : 1];   // wide: s0 / 2, off, s_p / 2 in FP32
   uint32_t w[FMT == 0 ? 2 : NB];  // 2-bit words, or base-3 code words
   uint32_t rw[NP > 0 ? NP : 1][2];
 
@@ -152,9 +161,14 @@ struct Dec {
   // offset (FP16 bits; 0 unless per-row offsets)
   __device__ __forceinline__ void prep(int g, int u, int wstart, const uint8_t* win, const Pre<NP>& P,
                                        uint32_t ro, const uint32_t* lut) {
-    s0 = splat(P.s0);
-    const uint32_t o = splat(ro | P.off);  // at most one of them is non-zero
-    o2 = pk_add(o, o);
+    if constexpr (WIDE) {
+      s0h = 0.5f * h2f_bits(P.s0);
+      of = h2f_bits(ro | P.off);  // at most one of them is non-zero
+    } else {
+      s0 = splat(P.s0);
+      const uint32_t o = splat(ro | P.off);  // at most one of them is non-zero
+      o2 = pk_add(o, o);
+    }
     if constexpr (FMT == 0) {
       const uint2 v = *reinterpret_cast<const uint2*>(win + 16 * u + 8 * ((A / 32) & 1));
       w[0] = v.x;
@@ -172,25 +186,40 @@ struct Dec {
     }
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      s1[p] = ((P.has >> p) & 1u) ? splat(P.rs[p]) : 0u;
+      if constexpr (WIDE) s1h[p] = ((P.has >> p) & 1u) ? 0.5f * h2f_bits(P.rs[p]) : 0.f;
+      else s1[p] = ((P.has >> p) & 1u) ? splat(P.rs[p]) : 0u;
       rw[p][0] = P.rw[p][0];
       rw[p][1] = P.rw[p][1];
     }
   }
 
   __device__ __forceinline__ void pair(int i) {
-    uint32_t v;
+    uint32_t t2;  // FP16 pair (2 t, 2 t') of plane 0
     if constexpr (FMT == 0) {
-      v = pk_fma(pair_of(w[i >> 3], 14 - 2 * (i & 7)), s0, o2);
+      t2 = pair_of(w[i >> 3], 14 - 2 * (i & 7));
     } else {
       const int ta = A + 2 * i, tb = ta + 1;
       const uint32_t ca = (w[ta / 5 - B0] >> (2 * (ta % 5))) & 3u;
       const uint32_t cb = (w[tb / 5 - B0] >> (2 * (tb % 5))) & 3u;
-      v = pk_fma((ca << 14) | (cb << 30), s0, o2);
+      t2 = (ca << 14) | (cb << 30);
     }
+    if constexpr (WIDE) {
+      h2_t h = __builtin_bit_cast(h2_t, t2);
+      float a = fmaf((float)h.x, s0h, of), b = fmaf((float)h.y, s0h, of);
 #pragma unroll
-    for (int p = 0; p < NP; ++p) v = pk_fma(pair_of(rw[p][i >> 3], 14 - 2 * (i & 7)), s1[p], v);
-    out[i] = v;
+      for (int p = 0; p < NP; ++p) {
+        h = __builtin_bit_cast(h2_t, pair_of(rw[p][i >> 3], 14 - 2 * (i & 7)));
+        a = fmaf((float)h.x, s1h[p], a);
+        b = fmaf((float)h.y, s1h[p], b);
+      }
+      const h2_t r = {(_Float16)a, (_Float16)b};
+      out[i] = __builtin_bit_cast(uint32_t, r);
+    } else {
+      uint32_t v = pk_fma(t2, s0, o2);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) v = pk_fma(pair_of(rw[p][i >> 3], 14 - 2 * (i & 7)), s1[p], v);
+      out[i] = v;
+    }
   }
 
   __device__ __forceinline__ void store(int q, _Float16* dst_h) const {
@@ -198,12 +227,12 @@ struct Dec {
   }
 };
 
-// dst = 0.5 * acc for one tile of a [d.m][d.n] array of T, staged through LDS
+// dst = esc * acc for one tile of a [d.m][d.n] array of T, staged through LDS
 // (the activation buffers) so that rows leave in 16-byte chunks; FP32 tiles
 // of 256 rows go in two halves.
 template <typename T, int AW>
 __device__ __forceinline__ void epilogue(const GemvDesc& d, int m0, int n0, const f16v_t (&acc)[AW][2], char* tile,
-                                         void* dst) {
+                                         void* dst, float esc) {
   constexpr int BM = 64 * AW;
   constexpr int HALVES = (sizeof(T) == 4 && AW == 4) ? 2 : 1;
   constexpr int ROWS = BM / HALVES;
@@ -224,7 +253,7 @@ __device__ __forceinline__ void epilogue(const GemvDesc& d, int m0, int n0, cons
 #pragma unroll
           for (int v = 0; v < 16; ++v)
             *reinterpret_cast<T*>(base + (32 * i + 8 * (v >> 2) + (v & 3)) * TP + 32 * j * (int)sizeof(T)) =
-                (T)(0.5f * acc[i][j][v]);
+                (T)(esc * acc[i][j][v]);
     }
     __syncthreads();
 #pragma unroll 4
@@ -245,7 +274,7 @@ __device__ __forceinline__ void epilogue(const GemvDesc& d, int m0, int n0, cons
   }
 }
 
-template <int FMT, int G, int AW, int NP, int H>
+template <int FMT, int G, int AW, int NP, int H, bool WIDE>
 __device__ __forceinline__ void gemm_body(const GemvDesc& d, int m0, int n0, _Float16* xs, _Float16* ws,
                                           uint8_t* pk, const uint32_t* lut) {
   constexpr int BM = 64 * AW;               // activation rows per tile
@@ -436,8 +465,8 @@ __device__ __forceinline__ void gemm_body(const GemvDesc& d, int m0, int n0, _Fl
   __syncthreads();
   // decoders by step parity (their K offset within the group differs when a
   // group spans two steps)
-  Dec<FMT, G, NP, 32 * H> De;
-  Dec<FMT, G, NP, (BK % G) + 32 * H> Do;
+  Dec<FMT, G, NP, 32 * H, WIDE> De;
+  Dec<FMT, G, NP, (BK % G) + 32 * H, WIDE> Do;
   De.prep(g0, 0, win_start<FMT>(w0), pk + (w0 % NWIN) * PBUF + dr * WP, P0, ro, lut);
 #pragma unroll
   for (int i = 0; i < 16; ++i) De.pair(i);
@@ -457,12 +486,13 @@ __device__ __forceinline__ void gemm_body(const GemvDesc& d, int m0, int n0, _Fl
 #undef TERN_WSTORE
 #undef TERN_WLOAD
 
-  // ---- epilogue: y = 0.5 * acc (the tile held 2 W~), or the FP32 partial
-  // sums of this K part
+  // ---- epilogue: y = 0.5 * acc (the narrow tile held 2 W~; the wide one W~),
+  // or the FP32 partial sums of this K part
+  constexpr float esc = WIDE ? 1.f : 0.5f;
   if (d.kpart >= 0)
-    epilogue<float, AW>(d, m0, n0, acc, reinterpret_cast<char*>(xs), d.partial + (size_t)d.kpart * d.m * d.n);
-  else if (d.y_f32) epilogue<float, AW>(d, m0, n0, acc, reinterpret_cast<char*>(xs), d.y);
-  else epilogue<_Float16, AW>(d, m0, n0, acc, reinterpret_cast<char*>(xs), d.y);
+    epilogue<float, AW>(d, m0, n0, acc, reinterpret_cast<char*>(xs), d.partial + (size_t)d.kpart * d.m * d.n, esc);
+  else if (d.y_f32) epilogue<float, AW>(d, m0, n0, acc, reinterpret_cast<char*>(xs), d.y, esc);
+  else epilogue<_Float16, AW>(d, m0, n0, acc, reinterpret_cast<char*>(xs), d.y, esc);
 }
 
 // ---- small M (1..16 activation rows): 16 x 128 output tiles with
@@ -476,7 +506,7 @@ __device__ __forceinline__ void gemm_body(const GemvDesc& d, int m0, int n0, _Fl
 typedef float f4v_t __attribute__((ext_vector_type(4)));
 constexpr int BMS = 16;  // activation rows of a small tile
 
-template <int FMT, int G, int NP, int H>
+template <int FMT, int G, int NP, int H, bool WIDE>
 __device__ __forceinline__ void small_body(const GemvDesc& d, int n0, int s0, int s1, int split, _Float16* xs,
                                            _Float16* ws, uint8_t* pk, const uint32_t* lut) {
   constexpr int XBUF = BMS * PH, WBUF = BN * PH, PBUF = BN * WP;
@@ -606,8 +636,8 @@ __device__ __forceinline__ void small_body(const GemvDesc& d, int n0, int s0, in
   load_step<G, NP, (BK % G) + 32 * H>(S, (s0 + 1) / SPG, min((s0 + 1) / SPG, d.ng - 1), W, P1);
   TERN_XSTORES(xv0, xs);
   __syncthreads();
-  Dec<FMT, G, NP, 32 * H> De;
-  Dec<FMT, G, NP, (BK % G) + 32 * H> Do;
+  Dec<FMT, G, NP, 32 * H, WIDE> De;
+  Dec<FMT, G, NP, (BK % G) + 32 * H, WIDE> Do;
   De.prep(g0, 0, win_start<FMT>(w0), pk + (w0 % NWIN) * PBUF + dr * WP, P0, ro, lut);
 #pragma unroll
   for (int i = 0; i < 16; ++i) De.pair(i);
@@ -642,7 +672,7 @@ __device__ __forceinline__ void small_body(const GemvDesc& d, int n0, int s0, in
     for (int v = 0; v < 4; ++v) {
       const int m = 4 * (lane >> 4) + v;
       if (m >= d.m) continue;
-      const float val = 0.5f * acc[j][v];
+      const float val = (WIDE ? 1.f : 0.5f) * acc[j][v];  // the narrow tile held 2 W~
       if (split >= 0) d.partial[((size_t)split * d.m + m) * d.n + nn] = val;
       else if (d.y_f32) reinterpret_cast<float*>(d.y)[(size_t)m * d.n + nn] = val;
       else reinterpret_cast<_Float16*>(d.y)[(size_t)m * d.n + nn] = (_Float16)val;
@@ -653,7 +683,7 @@ __device__ __forceinline__ void small_body(const GemvDesc& d, int n0, int s0, in
 // Grouped small-M launch: workgroup b computes the 16 x 128 tile at column
 // descs[b].tn0 over steps [descs[b].tm0, descs[b].splits) (tm0: first step,
 // splits: end step) into partial slice descs[b].gps (or y when gps < 0).
-template <int FMT, int G, int NP>
+template <int FMT, int G, int NP, bool WIDE>
 __global__ __launch_bounds__(NT) void gemm_small_kernel(const GemvDesc* __restrict__ descs) {
   __shared__ __attribute__((aligned(16))) _Float16 smem[2 * BMS * PH + 2 * BN * PH + NWIN * BN * WP / 2];
   __shared__ uint32_t lut[FMT == 1 ? 256 : 1];
@@ -664,8 +694,8 @@ __global__ __launch_bounds__(NT) void gemm_small_kernel(const GemvDesc* __restri
   if (FMT == 1) {
     for (int v = threadIdx.x; v < 256; v += NT) lut[v] = v < 243 ? b3_codes(v) : 0u;
   }
-  if ((threadIdx.x >> 7) == 0) small_body<FMT, G, NP, 0>(d, d.tn0, d.tm0, d.splits, d.gps, xs, ws, pk, lut);
-  else small_body<FMT, G, NP, 1>(d, d.tn0, d.tm0, d.splits, d.gps, xs, ws, pk, lut);
+  if ((threadIdx.x >> 7) == 0) small_body<FMT, G, NP, 0, WIDE>(d, d.tn0, d.tm0, d.splits, d.gps, xs, ws, pk, lut);
+  else small_body<FMT, G, NP, 1, WIDE>(d, d.tn0, d.tm0, d.splits, d.gps, xs, ws, pk, lut);
 }
 
 // y[m][n] = sum_s partial[s][m][n] (in split order) for every product of a
@@ -689,7 +719,7 @@ __global__ void reduce_grouped_kernel(const RedDesc* __restrict__ rd, int count)
 }
 
 // One BM x 128 output tile at (m0, n0) of the product described by d.
-template <int FMT, int G, int AW, int NP>
+template <int FMT, int G, int AW, int NP, bool WIDE>
 __device__ __forceinline__ void gemm_tile(const GemvDesc& d, int m0, int n0) {
   constexpr int BM = 64 * AW;
   __shared__ _Float16 xs[2 * BM * PH];
@@ -700,28 +730,28 @@ __device__ __forceinline__ void gemm_tile(const GemvDesc& d, int m0, int n0) {
     for (int v = threadIdx.x; v < 256; v += NT) lut[v] = v < 243 ? b3_codes(v) : 0u;
   }
   // half of each step decoded by this thread (wave-uniform)
-  if ((threadIdx.x >> 7) == 0) gemm_body<FMT, G, AW, NP, 0>(d, m0, n0, xs, ws, pk, lut);
-  else gemm_body<FMT, G, AW, NP, 1>(d, m0, n0, xs, ws, pk, lut);
+  if ((threadIdx.x >> 7) == 0) gemm_body<FMT, G, AW, NP, 0, WIDE>(d, m0, n0, xs, ws, pk, lut);
+  else gemm_body<FMT, G, AW, NP, 1, WIDE>(d, m0, n0, xs, ws, pk, lut);
 }
 
 // Tiles are numbered with the weight tile fastest and dealt to the XCDs in
 // contiguous runs, so the workgroups that run together on one XCD share an
 // activation tile, which then stays in that XCD's L2 (the packed weight tiles
 // are small and stream from HBM).
-template <int FMT, int G, int AW, int NP>
+template <int FMT, int G, int AW, int NP, bool WIDE>
 __global__ __launch_bounds__(NT) void gemm_kernel(GemvDesc d, int mtiles, int ntiles, int per_xcd) {
   const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (tile >= mtiles * ntiles) return;
-  gemm_tile<FMT, G, AW, NP>(d, (tile / ntiles) * (64 * AW), (tile % ntiles) * BN);
+  gemm_tile<FMT, G, AW, NP, WIDE>(d, (tile / ntiles) * (64 * AW), (tile % ntiles) * BN);
 }
 
 // A grouped launch: workgroup b computes the tile at (descs[b].tm0,
 // descs[b].tn0) of the product descs[b] describes (none if its n is 0).
-template <int FMT, int G, int AW, int NP>
+template <int FMT, int G, int AW, int NP, bool WIDE>
 __global__ __launch_bounds__(NT) void gemm_grouped_kernel(const GemvDesc* __restrict__ descs) {
   const GemvDesc d = descs[blockIdx.x];
   if (d.n <= 0) return;  // a position left open by the XCD layout
-  gemm_tile<FMT, G, AW, NP>(d, d.tm0, d.tn0);
+  gemm_tile<FMT, G, AW, NP, WIDE>(d, d.tm0, d.tn0);
 }
 
 __global__ void zero_fill_kernel(void* y, size_t count, int f32) {
@@ -732,6 +762,8 @@ __global__ void zero_fill_kernel(void* y, size_t count, int f32) {
 }
 
 }  // namespace
+
+bool gemm_wide(int np, bool offsets) { return np >= 2 || (np == 1 && offsets); }
 
 hipError_t launch_gemm(const GemvDesc& d, int format, hipStream_t s) {
   if (d.m <= 0 || d.n <= 0) return hipSuccess;
@@ -746,13 +778,15 @@ hipError_t launch_gemm(const GemvDesc& d, int format, hipStream_t s) {
   const int mtiles = (d.m + 64 * aw - 1) / (64 * aw), ntiles = (d.n + BN - 1) / BN;
   const int per_xcd = (mtiles * ntiles + 7) / 8;
   const dim3 grid(8 * per_xcd);
-#define TERN_GEMM_LAUNCH(F, G_, AW_, NP_) \
-  hipLaunchKernelGGL((gemm_kernel<F, G_, AW_, NP_>), grid, dim3(NT), 0, s, d, mtiles, ntiles, per_xcd)
+  const bool wide = gemm_wide(d.planes - 1, d.offset_mode != 0);
+#define TERN_GEMM_LAUNCH(F, G_, AW_, NP_, W_) \
+  hipLaunchKernelGGL((gemm_kernel<F, G_, AW_, NP_, W_>), grid, dim3(NT), 0, s, d, mtiles, ntiles, per_xcd)
 #define TERN_GEMM_NP(F, G_, AW_)                                          \
   do {                                                                    \
-    if (d.planes == 1) TERN_GEMM_LAUNCH(F, G_, AW_, 0);                   \
-    else if (d.planes == 2) TERN_GEMM_LAUNCH(F, G_, AW_, 1);              \
-    else TERN_GEMM_LAUNCH(F, G_, AW_, 2);                                 \
+    if (d.planes == 1) TERN_GEMM_LAUNCH(F, G_, AW_, 0, false);            \
+    else if (d.planes == 2 && !wide) TERN_GEMM_LAUNCH(F, G_, AW_, 1, false); \
+    else if (d.planes == 2) TERN_GEMM_LAUNCH(F, G_, AW_, 1, true);        \
+    else TERN_GEMM_LAUNCH(F, G_, AW_, 2, true);                           \
   } while (0)
   if (format == 0) {
     if (d.group == 64) { if (aw == 4) TERN_GEMM_NP(0, 64, 4); else TERN_GEMM_NP(0, 64, 2); }
@@ -775,17 +809,20 @@ int gemm_wgs_per_cu(int format, int aw) {
 }
 
 hipError_t launch_gemm_grouped(const GemvDesc* descs, int count, int format, int group, int aw, int np,
-                               hipStream_t s) {
+                               bool offsets, hipStream_t s) {
   if (count <= 0) return hipSuccess;
   if (!(format == 0 || format == 1) || !(group == 64 || group == 128) || !(aw == 2 || aw == 4) || np < 0 || np > 2)
     return hipErrorInvalidValue;
   const dim3 grid(count);
-#define TERN_GG(F, G_, AW_, NP_) hipLaunchKernelGGL((gemm_grouped_kernel<F, G_, AW_, NP_>), grid, dim3(NT), 0, s, descs)
-#define TERN_GG_NP(F, G_, AW_)                        \
-  do {                                                \
-    if (np == 0) TERN_GG(F, G_, AW_, 0);              \
-    else if (np == 1) TERN_GG(F, G_, AW_, 1);         \
-    else TERN_GG(F, G_, AW_, 2);                      \
+  const bool wide = gemm_wide(np, offsets);
+#define TERN_GG(F, G_, AW_, NP_, W_) \
+  hipLaunchKernelGGL((gemm_grouped_kernel<F, G_, AW_, NP_, W_>), grid, dim3(NT), 0, s, descs)
+#define TERN_GG_NP(F, G_, AW_)                              \
+  do {                                                      \
+    if (np == 0) TERN_GG(F, G_, AW_, 0, false);             \
+    else if (np == 1 && !wide) TERN_GG(F, G_, AW_, 1, false); \
+    else if (np == 1) TERN_GG(F, G_, AW_, 1, true);         \
+    else TERN_GG(F, G_, AW_, 2, true);                      \
   } while (0)
   if (format == 0) {
     if (group == 64) { if (aw == 4) TERN_GG_NP(0, 64, 4); else TERN_GG_NP(0, 64, 2); }
@@ -799,16 +836,19 @@ hipError_t launch_gemm_grouped(const GemvDesc* descs, int count, int format, int
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_small(const GemvDesc* descs, int count, int format, int group, int np, hipStream_t s) {
+hipError_t launch_gemm_small(const GemvDesc* descs, int count, int format, int group, int np, bool offsets,
+                             hipStream_t s) {
   if (count <= 0) return hipSuccess;
   if (!(format == 0 || format == 1) || !(group == 64 || group == 128) || np < 0 || np > 2) return hipErrorInvalidValue;
   const dim3 grid(count);
-#define TERN_GS(F, G_, NP_) hipLaunchKernelGGL((gemm_small_kernel<F, G_, NP_>), grid, dim3(NT), 0, s, descs)
-#define TERN_GS_NP(F, G_)                     \
-  do {                                        \
-    if (np == 0) TERN_GS(F, G_, 0);           \
-    else if (np == 1) TERN_GS(F, G_, 1);      \
-    else TERN_GS(F, G_, 2);                   \
+  const bool wide = gemm_wide(np, offsets);
+#define TERN_GS(F, G_, NP_, W_) hipLaunchKernelGGL((gemm_small_kernel<F, G_, NP_, W_>), grid, dim3(NT), 0, s, descs)
+#define TERN_GS_NP(F, G_)                             \
+  do {                                                \
+    if (np == 0) TERN_GS(F, G_, 0, false);            \
+    else if (np == 1 && !wide) TERN_GS(F, G_, 1, false); \
+    else if (np == 1) TERN_GS(F, G_, 1, true);        \
+    else TERN_GS(F, G_, 2, true);                     \
   } while (0)
   if (format == 0) { if (group == 64) TERN_GS_NP(0, 64); else TERN_GS_NP(0, 128); }
   else { if (group == 64) TERN_GS_NP(1, 64); else TERN_GS_NP(1, 128); }

@@ -213,14 +213,20 @@ int gemm_wgs_per_cu(int format, int aw);
 // workgroup with its tile origin (tm0, tn0) and K steps [ks0, ks1) (ks0 a
 // multiple of 4); kpart >= 0 writes FP32 sums to partial[kpart][m][n]
 // instead of y; aw = gemm_tile_rows(m) / 64; np = residual planes of the
-// descriptor with the most (0..2).
+// descriptor with the most (0..2); offsets: some descriptor has an offset.
+// np and offsets pick the decode's precision (gemm_wide).
 hipError_t launch_gemm_grouped(const GemvDesc* descs, int count, int format, int group, int aw, int np,
-                               hipStream_t stream);
+                               bool offsets, hipStream_t stream);
 // Small-M (m <= 16) matrix-core product, grouped: one descriptor per
 // workgroup, a 16 x 128 tile at column tn0 over K steps [tm0, splits) of 64;
 // partial slice gps >= 0 writes FP32 sums to partial[gps][m][n], gps < 0
-// writes y.  np as above.
-hipError_t launch_gemm_small(const GemvDesc* descs, int count, int format, int group, int np, hipStream_t stream);
+// writes y.  np and offsets as above.
+hipError_t launch_gemm_small(const GemvDesc* descs, int count, int format, int group, int np, bool offsets,
+                             hipStream_t stream);
+// Whether the tile decode forms W~ in FP32 and rounds it once (products
+// whose FP16 multiply-add chain would round more than once: an offset with
+// residual planes, or two residual planes) instead of FP16 multiply-adds.
+bool gemm_wide(int np, bool offsets);
 // Split sums of a grouped small-M launch: product i's blocks start at
 // rd[i].begin (ascending), 256 outputs per block.
 struct RedDesc {

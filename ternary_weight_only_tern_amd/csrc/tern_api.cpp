@@ -252,6 +252,7 @@ struct tern_plan {
   bool gemm;              // m >= 33: grouped matrix-core product
   bool small;             // small m on the 16-row matrix-core product
   int aw, np;             // its activation tile (aw * 64 rows) and residual planes
+  bool offs;              // some product has an offset
   const tern::RedDesc* red;  // small: split sums to reduce (device), their count and blocks
   int nred, red_blocks;
   bool b3;                // base-3 matrix-core decode: preparations, item lists and workgroups
@@ -817,6 +818,7 @@ struct TileBatch {
   std::vector<tern::RedDesc> red;
   size_t partial_bytes = 0;
   int red_blocks = 0, np = 0;
+  bool offs = false;  // some product has an offset (with np, picks the tile decode's precision)
 };
 
 // ---- grouped matrix-core products (m >= 33)
@@ -904,6 +906,7 @@ static tern_status build_gemm_batch(const tern_matrix* w, const uint16_t* const*
   out->partial_bytes = 0;
   out->red_blocks = 0;
   out->np = 0;
+  out->offs = false;
   std::vector<int> order;
   for (int i = 0; i < count; ++i) {
     TERN_TRY(check_matrix(&w[i]));
@@ -915,6 +918,7 @@ static tern_status build_gemm_batch(const tern_matrix* w, const uint16_t* const*
     TERN_TRY(check_xy(x[i], y[i], y_dtype));
     order.push_back(i);
     out->np = std::max(out->np, w[i].planes - 1);
+    out->offs = out->offs || w[i].offset_mode != TERN_OFF_NONE;
   }
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return w[a].k > w[b].k; });
   const std::vector<int> parts = gemm_splits(w, count, m);
@@ -1028,6 +1032,7 @@ static tern_status build_small_batch(const tern_matrix* w, const uint16_t* const
   out->partial_bytes = 0;
   out->red_blocks = 0;
   out->np = 0;
+  out->offs = false;
   std::vector<int> order;
   long total = 0;
   for (int i = 0; i < count; ++i) {
@@ -1040,6 +1045,7 @@ static tern_status build_small_batch(const tern_matrix* w, const uint16_t* const
     TERN_TRY(check_xy(x[i], y[i], y_dtype));
     order.push_back(i);
     out->np = std::max(out->np, w[i].planes - 1);
+    out->offs = out->offs || w[i].offset_mode != TERN_OFF_NONE;
     total += (long)((w[i].n + 127) / 128) * (w[i].k / 64) * ((m + 15) / 16);
   }
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return w[a].k > w[b].k; });
@@ -1590,7 +1596,7 @@ tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, vo
       TERN_HIP(hipMemcpyAsync(base + tb + b.partial_bytes, b.red.data(), b.red.size() * sizeof(tern::RedDesc),
                               hipMemcpyHostToDevice, s));
     TERN_HIP(tern::launch_gemm_grouped(reinterpret_cast<const GemvDesc*>(base), (int)b.tiles.size(), w[0].format,
-                                       w[0].group, tern::gemm_tile_rows(m) / 64, b.np, s));
+                                       w[0].group, tern::gemm_tile_rows(m) / 64, b.np, b.offs, s));
     if (!b.red.empty())
       TERN_HIP(tern::launch_reduce_grouped(reinterpret_cast<const tern::RedDesc*>(base + tb + b.partial_bytes),
                                            (int)b.red.size(), b.red_blocks, s));
@@ -1622,7 +1628,7 @@ tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, vo
       TERN_HIP(hipMemcpyAsync(base + tb + b.partial_bytes, b.red.data(), b.red.size() * sizeof(tern::RedDesc),
                               hipMemcpyHostToDevice, s));
     TERN_HIP(tern::launch_gemm_small(reinterpret_cast<const GemvDesc*>(base), (int)b.tiles.size(), w[0].format,
-                                     w[0].group, b.np, s));
+                                     w[0].group, b.np, b.offs, s));
     if (!b.red.empty())
       TERN_HIP(tern::launch_reduce_grouped(reinterpret_cast<const tern::RedDesc*>(base + tb + b.partial_bytes),
                                            (int)b.red.size(), b.red_blocks, s));
@@ -1692,6 +1698,7 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
     p->small = false;
     p->aw = tern::gemm_tile_rows(m) / 64;
     p->np = b.np;
+    p->offs = b.offs;
     p->red = b.red.empty() ? nullptr : reinterpret_cast<const tern::RedDesc*>(base + tb + b.partial_bytes);
     p->nred = (int)b.red.size();
     p->red_blocks = b.red_blocks;
@@ -1759,6 +1766,7 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
     p->small = true;
     p->aw = 0;
     p->np = b.np;
+    p->offs = b.offs;
     p->red = b.red.empty() ? nullptr : reinterpret_cast<const tern::RedDesc*>(base + tb + b.partial_bytes);
     p->nred = (int)b.red.size();
     p->red_blocks = b.red_blocks;
@@ -1848,10 +1856,11 @@ static tern_status plan_launch(const tern_plan* plan, hipStream_t s, hipEvent_t 
   if (before) TERN_HIP(hipEventRecord(before, s));
   if (plan->total_items == 0) {
   } else if (plan->gemm) {
-    TERN_HIP(tern::launch_gemm_grouped(plan->dev, plan->total_items, plan->format, plan->group, plan->aw, plan->np, s));
+    TERN_HIP(tern::launch_gemm_grouped(plan->dev, plan->total_items, plan->format, plan->group, plan->aw, plan->np,
+                                       plan->offs, s));
     if (plan->nred) TERN_HIP(tern::launch_reduce_grouped(plan->red, plan->nred, plan->red_blocks, s));
   } else if (plan->small) {
-    TERN_HIP(tern::launch_gemm_small(plan->dev, plan->total_items, plan->format, plan->group, plan->np, s));
+    TERN_HIP(tern::launch_gemm_small(plan->dev, plan->total_items, plan->format, plan->group, plan->np, plan->offs, s));
     if (plan->nred) TERN_HIP(tern::launch_reduce_grouped(plan->red, plan->nred, plan->red_blocks, s));
   } else {
     GemvDesc dummy;
