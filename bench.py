@@ -277,6 +277,82 @@ def bench_stack8b(args, stream, mats, xs, ys):
                 weights=sum(wts), plan=plan)
 
 
+def time_plan(plan, steps, warmup, stream):
+    """Mean step time of a plan launched directly on `stream`, events around
+    the timed steps."""
+    import torch
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            plan.run(stream.cuda_stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            plan.run(stream.cuda_stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+    return a.elapsed_time(b) / 1e3 / steps
+
+
+def bench_stack8b_rotated(stream, mats, xs, ys, steps=200):
+    """The headline stack with a rotation on every distinct input of every
+    layer (one seeded 128 x 128 block-diagonal R per layer and input: 216 MB
+    of rotation blocks per token), folded into the activation preparation of
+    one rotated plan; beside the same plan without rotations."""
+    import torch
+    from ternary_weight_only_tern_amd import lib as L
+    from ternary_weight_only_tern_amd import synth
+    rng = np.random.default_rng(4242)
+    rot_of, rots = {}, []
+    for x, pm in zip(xs, mats):
+        if x.data_ptr() not in rot_of:
+            R = synth.draw_rotation(rng, pm.k // 128, 128)
+            rot_of[x.data_ptr()] = torch.from_numpy(R.view(np.uint16)).cuda().view(torch.float16)
+        rots.append(rot_of[x.data_ptr()])
+    rbytes = sum(r.numel() * 2 for r in rot_of.values())
+    plan_r = L.Plan(mats, xs, ys, rots=rots, rot_block=128)
+    plan_p = L.Plan(mats, xs, ys)
+    torch.cuda.synchronize()
+    t_r = time_plan(plan_r, steps, 10, stream)
+    t_p = time_plan(plan_p, steps, 10, stream)
+    del plan_r, plan_p, rot_of, rots
+    return dict(us_per_token=round(t_r * 1e6, 2), us_per_token_unrotated=round(t_p * 1e6, 2),
+                rotation_bytes=rbytes, steps=steps)
+
+
+def bench_layer4b_rotated(stream, steps=720):
+    """The 4B-class layer (2-bit, M=1) with its three distinct inputs rotated
+    (128 x 128 blocks; the decode route runs one rotation launch before the
+    product), beside the same layer unrotated; 36 byte copies rotated."""
+    import torch
+    from ternary_weight_only_tern_amd import lib as L
+    from ternary_weight_only_tern_amd import synth
+    base, xs, ys = [], [], []
+    for proj in range(len(synth.QWEN3_4B_LAYER)):
+        pm, _ = pack_workload("qwen3_4b_layer", 0, proj)
+        base.append(pm)
+        xs.append(x_for("qwen3_4b_layer", synth.LAYER_INPUT[proj], 1)[0])
+        ys.append(torch.empty((1, pm.n), dtype=torch.float16, device="cuda"))
+    rng = np.random.default_rng(4243)
+    rot_of = {}
+    for x, pm in zip(xs, base):
+        if x.data_ptr() not in rot_of:
+            R = synth.draw_rotation(rng, pm.k // 128, 128)
+            rot_of[x.data_ptr()] = torch.from_numpy(R.view(np.uint16)).cuda().view(torch.float16)
+    rots = [rot_of[x.data_ptr()] for x in xs]
+    layers = [base] + [[clone_packed(pm) for pm in base] for _ in range(LAYERS - 1)]
+    out = {}
+    for name, kw in (("rotated", dict(rots=rots, rot_block=128)), ("unrotated", {})):
+        plans = [L.Plan(layer, xs, ys, **kw) for layer in layers]
+        fns = [(lambda p=p: p.run(stream.cuda_stream)) for p in plans]
+        wall, gpu, _ = time_graph(fns, steps, LAYERS, stream)
+        out[name] = round(gpu / steps * 1e6, 3)
+        del plans, fns
+    del layers
+    return dict(us_per_layer=out["rotated"], us_per_layer_unrotated=out["unrotated"],
+                rotation_bytes=sum(r.numel() * 2 for r in rot_of.values()), steps=steps)
+
+
 def bench_stack8b_graph(stream, plan):
     """The same plan replayed from a HIP graph (three tokens per replay)."""
     per = 3
@@ -653,6 +729,11 @@ def main():
                                                    gbs=round(r["stack_bytes"] / gr["step_s"] / 1e9, 1),
                                                    replays=gr["replays"], tokens_per_replay=3)
         log(f"bench: stack from a graph {gr['step_s']*1e6:.1f} us/token")
+        rot = bench_stack8b_rotated(stream, mats, xs, ys)
+        extra["qwen3_8b_stack_m1_b3_rotated"] = dict(rot, note="rotation folded into the activation preparation "
+                                                     "(tern_plan_create_rotated), one 128x128 block-diagonal R per "
+                                                     "layer and distinct input")
+        log(f"bench: stack with rotations {rot['us_per_token']:.1f} us/token (without {rot['us_per_token_unrotated']:.1f})")
         s8l = bench_stack8b_launches(stream, mats, xs, ys)
         extra["qwen3_8b_stack_m1_b3_252_launches"] = dict(us_per_token=round(s8l["step_s"] * 1e6, 2),
                                                           gbs=round(s8l["gbs"], 1),
@@ -678,6 +759,10 @@ def main():
                  for key in ("info", "plane", "storage")},
             note="one grouped launch per layer; 36 byte copies of the layer rotated")
         log(f"bench: 4B-class layer {l4['step_s']*1e6:.2f} us/step, {l4['gbs']:.1f} GB/s")
+        r4 = bench_layer4b_rotated(stream)
+        extra["qwen3_4b_layer_m1_2bit_rotated"] = dict(r4, note="one rotation launch for the layer's three inputs "
+                                                       "before the decode launch, both in one plan")
+        log(f"bench: 4B-class layer with rotations {r4['us_per_layer']:.2f} us (without {r4['us_per_layer_unrotated']:.2f})")
         sweep = {}
         for m in (1, 4, 16, 64, 512):
             q = bench_layer8b(args, stream, m)

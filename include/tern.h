@@ -262,6 +262,30 @@ tern_status tern_plan_run(const tern_plan *plan, void *stream);
 tern_status tern_plan_run_events(const tern_plan *plan, void *stream, void *before, void *after);
 void tern_plan_destroy(tern_plan *plan);
 
+/* A plan whose products take rotated activations: y[i] = x[i]
+ * blockdiag(R_i)^T W[i]^T, the rotation applied to the activations before
+ * the packed product ("Post-Training Ternarization of Qwen3-4B", §4.2: the
+ * weights are quantized in a rotated basis and inference rotates the
+ * activations to match), with R_i = rot[i] (device fp16
+ * [k/rot_block][rot_block][rot_block], 16-byte aligned; NULL: product i
+ * takes x[i] as it is), rot_block 64 or 128, each rotated k a multiple of
+ * it; the rotation is that of tern_rotate (FP32 sums, FP16 values).
+ * Products that read the same x must share its rotation (TERN_E_INVAL).
+ * ws: tern_rotated_workspace_bytes(w, count, m) bytes; it holds one rotated
+ * copy of each distinct rotated x, then the plan's own tables.  Base-3 plans
+ * at m <= 4 on the stream kernel rotate inside their activation preparation
+ * (the rotation costs no launch of its own beyond that preparation, which
+ * then runs before the residual pass instead of alongside it); other plans
+ * launch the rotations (tern_rotate_batched's kernel, up to 8 inputs per
+ * launch) before the product.  rot == NULL is tern_plan_create.  The rest is
+ * as for tern_plan_create (run with tern_plan_run, free with
+ * tern_plan_destroy). */
+size_t tern_rotated_workspace_bytes(const tern_matrix *w, int32_t count, int32_t m);
+tern_status tern_plan_create_rotated(const tern_matrix *w, const uint16_t *const *x,
+                                     const uint16_t *const *rot, int32_t rot_block, void *const *y,
+                                     int32_t count, int32_t m, int32_t y_dtype, void *ws,
+                                     size_t ws_bytes, tern_plan **out);
+
 /* Routing of base-3 products at m <= 4 (tern_gemv, tern_gemv_batched,
  * tern_plan_create and their workspace sizes).  A launch whose products
  * hold at least this many 64-row stages of plane 0 (ceil(n / 64) *

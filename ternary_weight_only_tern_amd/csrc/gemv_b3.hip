@@ -138,14 +138,33 @@ __device__ __forceinline__ void b3_prep_block(const B3Prep* __restrict__ preps, 
   const int c = bx * 256 + (int)threadIdx.x;
   if (c < ng * Gm::CPG) {
     const int g = c / Gm::CPG, cc = c % Gm::CPG;
-    uint32_t v[2];
+    uint32_t h[4];
 #pragma unroll
-    for (int hp = 0; hp < 2; ++hp) {
-      const int p0 = x5_pos<G>(cc, 2 * hp), p1 = x5_pos<G>(cc, 2 * hp + 1);
-      const uint32_t a = p0 >= 0 ? xr[g * G + p0] : 0u, b = p1 >= 0 ? xr[g * G + p1] : 0u;
-      v[hp] = a | (b << 16);
+    for (int q = 0; q < 4; ++q) {
+      const int pos = x5_pos<G>(cc, q);
+      if (pos < 0) {
+        h[q] = 0u;
+      } else if (p.R == nullptr) {
+        h[q] = xr[g * G + pos];
+      } else {
+        // the rotated activation at this position: row i of block b of R
+        // times block b of x, FP32 sums in position order, one FP16 rounding
+        const int P = g * G + pos, B = p.rblock, b = P / B, i = P % B;
+        const u4_t* rrow = reinterpret_cast<const u4_t*>(p.R + ((size_t)b * B + i) * B);
+        const u4_t* xb = reinterpret_cast<const u4_t*>(xr + (size_t)b * B);
+        float acc = 0.f;
+        for (int j = 0; j < B / 8; ++j) {
+          const u4_t rv = rrow[j], xv = xb[j];
+          acc = dot2(rv.x, xv.x, acc);
+          acc = dot2(rv.y, xv.y, acc);
+          acc = dot2(rv.z, xv.z, acc);
+          acc = dot2(rv.w, xv.w, acc);
+        }
+        h[q] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)acc);
+        p.xr[(size_t)m * p.k + P] = (uint16_t)h[q];
+      }
     }
-    *reinterpret_cast<u2_t*>(p.x5 + ((size_t)m * ng * Gm::CPG + c) * 4) = u2_t{v[0], v[1]};
+    *reinterpret_cast<u2_t*>(p.x5 + ((size_t)m * ng * Gm::CPG + c) * 4) = u2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
   }
   if (p.xs && bx == 0) {
     for (int g = threadIdx.x; g < ng; g += 256) {

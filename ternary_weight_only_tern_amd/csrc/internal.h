@@ -163,6 +163,12 @@ struct B3Prep {
   int32_t k, m;
   uint32_t* zero;  // if not NULL: nzero words cleared (counters of the passes that follow)
   int32_t nzero;
+  // if R is not NULL: the activations are rotated first, blockdiag(R) x with
+  // R fp16 [k/rblock][rblock][rblock] (FP32 sums, FP16 values), x5 holds the
+  // rotated values and xr [m][k] a copy of them in position order
+  const uint16_t* R;
+  uint16_t* xr;
+  int32_t rblock;
 };
 // Instructions (4-slot chunks) per group: 33 at group 128, 16 at group 64;
 // groups per 208-byte stage: 8 and 16.

@@ -263,6 +263,9 @@ struct tern_plan {
   int nwg, b3_maxk;
   const tern::B3ResItem* b3res;  // residual pass units and their count
   int nres;
+  bool prep_first;        // base-3: the preparations rotate, so they run before the residual pass
+  tern::RotBatch* rots;   // rotations launched before the product (malloc'ed; NULL: none)
+  int nrots, rot_block;
 };
 
 extern "C" {
@@ -1158,6 +1161,7 @@ struct B3Batch {
   std::vector<uint32_t> queues;      // kB3Queues * kB3QueueWords words
   std::vector<std::pair<size_t, size_t>> zero;  // (offset, bytes) cleared at upload: residual-pass counters
   size_t rctr_off = 0, rctr_bytes = 0;
+  bool prep_first = false;  // the preparations rotate (launched before the residual pass)
   size_t descs_off = 0, preps_off = 0, queue_off = 0, items_off = 0, part_off = 0, ctr_off = 0, res_off = 0, total = 0;
   size_t nctr = 0;
   int mt = 1, nwg = 0, max_k = 0;
@@ -1231,7 +1235,9 @@ static int b3_res_lds_cap(long nunits) { return nunits <= 4L * tern_cu_count() ?
 
 // Builds the batch (items only when `items` is true); ws may be NULL (sizes only).
 static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y, int32_t count,
-                                  int32_t m, int32_t y_dtype, char* ws, bool items, B3Batch* b) {
+                                  int32_t m, int32_t y_dtype, char* ws, bool items, B3Batch* b,
+                                  const uint16_t* const* rot = nullptr, uint16_t* const* xr = nullptr,
+                                  int rot_block = 0) {
   if (count < 0) return fail(TERN_E_INVAL, "count=%d is negative", count);
   if (count > 0 && !w) return fail(TERN_E_INVAL, "NULL descriptor array");
   if (items && count > 0 && (!x || !y)) return fail(TERN_E_INVAL, "NULL activation or output arrays");
@@ -1294,7 +1300,10 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
     if (x) {
       auto ins = x5_first.insert({{x[i], w[i].k}, i});
       if (!ins.second) {
-        x5_off[i] = x5_off[ins.first->second];
+        const int f = ins.first->second;
+        if (rot && rot[f] != rot[i])
+          return fail(TERN_E_INVAL, "products %d and %d read the same x with different rotations", f, i);
+        x5_off[i] = x5_off[f];
         x5_own[i] = false;
         continue;
       }
@@ -1323,6 +1332,7 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
   b->descs.clear();
   b->res.clear();
   b->zero.clear();
+  b->prep_first = false;
   b->index.clear();
   b->preps.clear();
   b->items.clear();
@@ -1334,7 +1344,7 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
   size_t poff = 0, coff = 0;
   for (int i : order) {
     GemvDesc d;
-    fill_desc(d, &w[i], x[i], m, y[i], y_dtype == TERN_F32);
+    fill_desc(d, &w[i], rot && rot[i] ? xr[i] : x[i], m, y[i], y_dtype == TERN_F32);
     d.splits = parts[i];
     d.p0 = parts[i];
     d.gps = sps[i];
@@ -1371,6 +1381,12 @@ static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x
     pr.x5 = const_cast<uint16_t*>(d.x5);
     pr.k = w[i].k;
     pr.m = m;
+    if (rot && rot[i]) {  // rotated in the preparation; the residual pass reads the rotated copy
+      pr.R = rot[i];
+      pr.xr = xr[i];
+      pr.rblock = rot_block;
+      b->prep_first = true;
+    }
     b->preps.push_back(pr);
   }
   // items, largest first onto the least loaded wavefront
@@ -1659,6 +1675,43 @@ tern_status tern_gemv_batched(const tern_matrix* w, const uint16_t* const* x, vo
   return TERN_OK;
 }
 
+// A plan on the base-3 stream kernel (optionally with rotations folded into
+// its activation preparation: rot[i] / xr[i] per product, or NULL).
+static tern_status b3_plan_create(const tern_matrix* w, const uint16_t* const* x, void* const* y, int32_t count,
+                                  int32_t m, int32_t y_dtype, void* ws, size_t ws_bytes,
+                                  const uint16_t* const* rot, uint16_t* const* xr, int rot_block,
+                                  tern_plan** out) {
+  B3Batch b;
+  TERN_TRY(build_b3_batch(w, x, y, count, m, y_dtype, static_cast<char*>(ws), true, &b, rot, xr, rot_block));
+  char* base = static_cast<char*>(ws);
+  if (!b.descs.empty()) {
+    if (!ws || ws_bytes < b.total) return fail(TERN_E_WORKSPACE, "plan needs %zu workspace bytes", b.total);
+    TERN_TRY(check_dev(ws, true, "ws"));
+    TERN_TRY(upload_b3_batch(b, base, nullptr, true));
+  }
+  tern_plan* p = static_cast<tern_plan*>(std::malloc(sizeof(tern_plan)));
+  if (!p) return fail(TERN_E_INVAL, "out of host memory");
+  std::memset(p, 0, sizeof(*p));
+  p->format = w[0].format;
+  p->group = w[0].group;
+  p->mt = b.mt;
+  p->total_items = (int)b.items.size();
+  p->b3 = true;
+  p->dev = reinterpret_cast<const GemvDesc*>(base + b.descs_off);
+  p->ndesc = (int)b.descs.size();
+  p->preps = reinterpret_cast<const tern::B3Prep*>(base + b.preps_off);
+  p->nprep = (int)b.preps.size();
+  p->b3items = reinterpret_cast<const tern::B3Item*>(base + b.items_off);
+  p->b3_maxk = b.max_k;
+  p->b3res = reinterpret_cast<const tern::B3ResItem*>(base + b.res_off);
+  p->nres = (int)b.res.size();
+  p->queue = reinterpret_cast<uint32_t*>(base + b.queue_off);
+  p->nwg = b.nwg;
+  p->prep_first = b.prep_first;
+  *out = p;
+  return TERN_OK;
+}
+
 tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, void* const* y,
                              int32_t count, int32_t m, int32_t y_dtype, void* ws, size_t ws_bytes,
                              tern_plan** out) {
@@ -1705,36 +1758,8 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
     *out = p;
     return TERN_OK;
   }
-  if (count > 0 && b3_route_n(w, count, m)) {
-    B3Batch b;
-    TERN_TRY(build_b3_batch(w, x, y, count, m, y_dtype, static_cast<char*>(ws), true, &b));
-    char* base = static_cast<char*>(ws);
-    if (!b.descs.empty()) {
-      if (!ws || ws_bytes < b.total) return fail(TERN_E_WORKSPACE, "plan needs %zu workspace bytes", b.total);
-      TERN_TRY(check_dev(ws, true, "ws"));
-      TERN_TRY(upload_b3_batch(b, base, nullptr, true));
-    }
-    tern_plan* p = static_cast<tern_plan*>(std::malloc(sizeof(tern_plan)));
-    if (!p) return fail(TERN_E_INVAL, "out of host memory");
-    std::memset(p, 0, sizeof(*p));
-    p->format = w[0].format;
-    p->group = w[0].group;
-    p->mt = b.mt;
-    p->total_items = (int)b.items.size();
-    p->b3 = true;
-    p->dev = reinterpret_cast<const GemvDesc*>(base + b.descs_off);
-    p->ndesc = (int)b.descs.size();
-    p->preps = reinterpret_cast<const tern::B3Prep*>(base + b.preps_off);
-    p->nprep = (int)b.preps.size();
-    p->b3items = reinterpret_cast<const tern::B3Item*>(base + b.items_off);
-    p->b3_maxk = b.max_k;
-    p->b3res = reinterpret_cast<const tern::B3ResItem*>(base + b.res_off);
-    p->nres = (int)b.res.size();
-    p->queue = reinterpret_cast<uint32_t*>(base + b.queue_off);
-    p->nwg = b.nwg;
-    *out = p;
-    return TERN_OK;
-  }
+  if (count > 0 && b3_route_n(w, count, m))
+    return b3_plan_create(w, x, y, count, m, y_dtype, ws, ws_bytes, nullptr, nullptr, 0, out);
   if (count > 0 && small_route(w[0].format, w[0].group, m)) {
     if (!ws) return fail(TERN_E_WORKSPACE, "plan needs a workspace");
     TERN_TRY(check_dev(ws, true, "ws"));
@@ -1837,16 +1862,21 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
 
 static tern_status plan_launch(const tern_plan* plan, hipStream_t s, hipEvent_t before, hipEvent_t after) {
   if (!plan) return fail(TERN_E_INVAL, "plan is NULL");
+  for (int r = 0; r < plan->nrots; ++r) TERN_HIP(tern::launch_rotate(plan->rots[r], plan->rot_block, s));
   if (plan->b3 && plan->total_items > 0) {
     tern::B3Prep none;
     std::memset(&none, 0, sizeof(none));
     GemvDesc dummy;
     std::memset(&dummy, 0, sizeof(dummy));
-    if (plan->nres == 0)
+    if (plan->nres == 0 || plan->prep_first) {
+      // rotating preparations write what the residual pass reads: a launch of their own
       TERN_HIP(tern::launch_b3_prep(plan->group, plan->preps, plan->nprep, none, plan->b3_maxk, s));
-    else  // the preparations ride along in the residual pass's launch
+      TERN_HIP(tern::launch_b3_res(plan->group, plan->mt, plan->dev, plan->b3res, plan->nres, dummy, plan->b3_maxk,
+                                   b3_res_lds_cap(plan->nres), nullptr, 0, 0, s));
+    } else {  // the preparations ride along in the residual pass's launch
       TERN_HIP(tern::launch_b3_res(plan->group, plan->mt, plan->dev, plan->b3res, plan->nres, dummy, plan->b3_maxk,
                                    b3_res_lds_cap(plan->nres), plan->preps, plan->nprep, plan->b3_maxk, s));
+    }
     if (before) TERN_HIP(hipEventRecord(before, s));
     TERN_HIP(tern::launch_gemv_b3(plan->group, plan->mt, plan->dev, plan->b3items, plan->queue, plan->nwg, dummy,
                                   plan->total_items, s));
@@ -1888,7 +1918,90 @@ tern_status tern_plan_run_events(const tern_plan* plan, void* stream, void* befo
   return plan_launch(plan, (hipStream_t)stream, (hipEvent_t)before, (hipEvent_t)after);
 }
 
-void tern_plan_destroy(tern_plan* plan) { std::free(plan); }
+void tern_plan_destroy(tern_plan* plan) {
+  if (plan) std::free(plan->rots);
+  std::free(plan);
+}
+
+size_t tern_rotated_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m) {
+  if (count <= 0 || m <= 0 || !w) return 0;
+  size_t bytes = tern_batch_workspace_bytes(w, count, m);
+  for (int i = 0; i < count; ++i)
+    if (w[i].k > 0) bytes += round_up((size_t)2 * m * w[i].k, 256);  // a rotated copy per product at most
+  return bytes;
+}
+
+tern_status tern_plan_create_rotated(const tern_matrix* w, const uint16_t* const* x, const uint16_t* const* rot,
+                                     int32_t rot_block, void* const* y, int32_t count, int32_t m, int32_t y_dtype,
+                                     void* ws, size_t ws_bytes, tern_plan** out) {
+  if (!out) return fail(TERN_E_INVAL, "out is NULL");
+  *out = nullptr;
+  if (!rot) return tern_plan_create(w, x, y, count, m, y_dtype, ws, ws_bytes, out);
+  if (rot_block != 64 && rot_block != 128) return fail(TERN_E_UNSUPPORTED, "rotation blocks of 64 or 128 (got %d)", rot_block);
+  if (count < 0 || m < 0) return fail(TERN_E_INVAL, "count=%d, m=%d must not be negative", count, m);
+  if (count > 0 && (!w || !x || !y)) return fail(TERN_E_INVAL, "NULL descriptor, activation or output arrays");
+  // one rotated copy per distinct (x, R) at the start of ws, the plan's own
+  // workspace after them
+  std::map<const uint16_t*, std::pair<const uint16_t*, size_t>> seen;  // x -> (R, offset of its copy)
+  std::vector<const uint16_t*> xin(count > 0 ? count : 1);
+  std::vector<uint16_t*> xr(count > 0 ? count : 1, nullptr);
+  size_t off = 0;
+  for (int i = 0; i < count; ++i) {
+    xin[i] = x[i];
+    if (!rot[i] || w[i].n <= 0 || w[i].k <= 0 || m == 0) continue;
+    if (w[i].k % rot_block) return fail(TERN_E_UNSUPPORTED, "product %d: k=%d is not a multiple of the rotation block", i, w[i].k);
+    TERN_TRY(check_dev(rot[i], true, "rotation", 16));
+    TERN_TRY(check_dev(x[i], true, "x", 16));
+    auto it = seen.find(x[i]);
+    if (it == seen.end()) {
+      it = seen.insert({x[i], {rot[i], off}}).first;
+      off += round_up((size_t)2 * m * w[i].k, 256);
+    } else if (it->second.first != rot[i]) {
+      return fail(TERN_E_INVAL, "product %d reads an x that another product rotates differently", i);
+    }
+    if (!ws) return fail(TERN_E_WORKSPACE, "a rotated plan needs a workspace");
+    xr[i] = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + it->second.second);
+    xin[i] = xr[i];
+  }
+  if (off > ws_bytes) return fail(TERN_E_WORKSPACE, "rotated plan needs more workspace");
+  char* inner = static_cast<char*>(ws) + off;
+  const size_t inner_bytes = ws_bytes - off;
+  if (count > 0 && b3_route_n(w, count, m))  // folded into the activation preparation
+    return b3_plan_create(w, x, y, count, m, y_dtype, inner, inner_bytes, rot, xr.data(), rot_block, out);
+  TERN_TRY(tern_plan_create(w, xin.data(), y, count, m, y_dtype, inner, inner_bytes, out));
+  // other routes: rotation launches (up to kMaxRotations inputs each) into the copies
+  std::vector<tern::RotBatch> rb;
+  std::map<const uint16_t*, bool> done;
+  for (int i = 0; i < count; ++i) {
+    if (!xr[i] || done[x[i]]) continue;
+    done[x[i]] = true;
+    if (rb.empty() || rb.back().count == tern::kMaxRotations) {
+      tern::RotBatch a;
+      std::memset(&a, 0, sizeof(a));
+      a.m = m;
+      rb.push_back(a);
+    }
+    tern::RotBatch& a = rb.back();
+    a.R[a.count] = rot[i];
+    a.x[a.count] = x[i];
+    a.out[a.count] = xr[i];
+    a.k[a.count] = w[i].k;
+    a.begin[a.count + 1] = a.begin[a.count] + w[i].k / rot_block;
+    ++a.count;
+  }
+  if (!rb.empty()) {
+    (*out)->rots = static_cast<tern::RotBatch*>(std::malloc(rb.size() * sizeof(tern::RotBatch)));
+    if (!(*out)->rots) {
+      tern_plan_destroy(*out);
+      *out = nullptr;
+      return fail(TERN_E_INVAL, "out of host memory");
+    }
+    std::memcpy((*out)->rots, rb.data(), rb.size() * sizeof(tern::RotBatch));
+    (*out)->nrots = (int)rb.size();
+    (*out)->rot_block = rot_block;
+  }
+  return TERN_OK;
+}
 
 tern_status tern_quantize(const uint16_t* w, int32_t n, int32_t k, int32_t group, const uint32_t* mask,
                           int32_t iters, int8_t* trits, uint16_t* scales, uint16_t* offset, void* stream) {

@@ -36,6 +36,7 @@ TERN_F32 = 1
 SYMBOLS = ["tern_row_stride", "tern_check", "tern_packed_sizes", "tern_workspace_bytes",
            "tern_pack", "tern_unpack", "tern_gemv", "tern_gemm", "tern_batch_workspace_bytes",
            "tern_gemv_batched", "tern_plan_create", "tern_plan_run", "tern_plan_run_events", "tern_plan_destroy", "tern_b3_min_stages", "tern_gemv_noalloc",
+           "tern_rotated_workspace_bytes", "tern_plan_create_rotated",
            "tern_bits", "tern_quantize", "tern_rotate", "tern_rotate_batched", "tern_read_probe", "tern_status_str", "tern_last_error"]
 
 
@@ -80,6 +81,9 @@ def load() -> ctypes.CDLL:
         "tern_plan_run": (c_int32, [c_void_p, c_void_p]),
         "tern_plan_run_events": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p]),
         "tern_b3_min_stages": (ctypes.c_int64, [ctypes.c_int64]),
+        "tern_rotated_workspace_bytes": (c_size_t, [c_void_p, c_int32, c_int32]),
+        "tern_plan_create_rotated": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32,
+                                              c_int32, c_void_p, c_size_t, c_void_p]),
         "tern_gemv_noalloc": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p]),
         "tern_plan_destroy": (None, [c_void_p]),
         "tern_bits": (c_int32, [P, POINTER(c_double), POINTER(c_double), POINTER(c_double)]),
@@ -271,23 +275,33 @@ def _event(e):
 
 
 class Plan:
-    """tern_plan_create / tern_plan_run / tern_plan_destroy."""
+    """tern_plan_create / tern_plan_run / tern_plan_destroy; with `rots` (a
+    list of fp16 rotation-block tensors or None per product) and rot_block,
+    tern_plan_create_rotated."""
 
-    def __init__(self, mats, xs, ys, y_dtype=TERN_F16):
+    def __init__(self, mats, xs, ys, y_dtype=TERN_F16, rots=None, rot_block=128):
         import torch
         self.m = xs[0].shape[0] if xs else 0
         descs, xp, yp = _arrays(mats, xs, ys)
-        nbytes = load().tern_batch_workspace_bytes(descs, len(mats), self.m)
+        if rots is not None:
+            nbytes = load().tern_rotated_workspace_bytes(descs, len(mats), self.m)
+        else:
+            nbytes = load().tern_batch_workspace_bytes(descs, len(mats), self.m)
         # tern_plan_create writes every table and clears its counters itself
         # (synchronously, on the null stream): no fill is queued here, and the
         # caller's queued work on its inputs is finished first
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=xs[0].device)
         if xs:
             torch.cuda.current_stream(xs[0].device).synchronize()
-        self._keep = (mats, xs, ys)
+        self._keep = (mats, xs, ys, rots)
         handle = c_void_p()
-        check(load().tern_plan_create(descs, xp, yp, len(mats), self.m, y_dtype, _ptr(self.ws),
-                                      self.ws.numel(), ctypes.byref(handle)))
+        if rots is not None:
+            rp = (c_void_p * max(len(rots), 1))(*[None if r is None else r.data_ptr() for r in rots])
+            check(load().tern_plan_create_rotated(descs, xp, rp, rot_block, yp, len(mats), self.m, y_dtype,
+                                                  _ptr(self.ws), self.ws.numel(), ctypes.byref(handle)))
+        else:
+            check(load().tern_plan_create(descs, xp, yp, len(mats), self.m, y_dtype, _ptr(self.ws),
+                                          self.ws.numel(), ctypes.byref(handle)))
         self.handle = handle
 
     def run(self, stream=None):

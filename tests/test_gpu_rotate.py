@@ -121,3 +121,70 @@ def test_rotate_batched_eight_inputs_empty_input_and_graph_replays():
         torch.cuda.synchronize()
         for g, w_ in zip(gouts, want):
             assert torch.equal(g, w_), f"replay {rep} differs from the eager call"
+
+
+@pytest.mark.parametrize("fmt,m,route,block", [(O.FMT_B3, 1, "stream", 128), (O.FMT_B3, 4, "stream", 64),
+                                               (O.FMT_B3, 1, "auto", 128), (O.FMT_2BIT, 1, "auto", 128),
+                                               (O.FMT_2BIT, 8, "auto", 64), (O.FMT_B3, 64, "auto", 128)])
+def test_rotated_plan_matches_oracle(fmt, m, route, block):
+    """Rotate-then-product through one plan (tern_plan_create_rotated): on the
+    base-3 stream kernel the rotation runs inside the activation preparation;
+    on the other routes rotation launches precede the product.  Two products
+    share one x and its rotation, one takes another rotation, one takes its x
+    unrotated.  Checked against the oracle's rotation followed by its product:
+    |y - y_ref| <= 2e-3 * B(|xr|) + 2.004e-3 * B(sum_j |R||x|), the product's
+    bound on the exact rotated x plus the rotation's own bound carried through
+    the weights; run twice, bit-identical."""
+    import torch
+    from gpu_util import b3_route, check_y, oracle_y, small_matrix, upload_pack
+    say("rotated plan", fmt, m, route, block)
+    rng = np.random.default_rng(m + block)
+    mats = [small_matrix(300, 2560, 128, 2, 0.3, seed=41, offset_mode=O.OFF_GROUP)[0],
+            small_matrix(130, 2560, 128, 2, 0.1, seed=42)[0],
+            small_matrix(200, 1280, 128, 3, 0.2, seed=43, offset_mode=O.OFF_ROW)[0],
+            small_matrix(64, 1024, 128, 1, 0.0, seed=44)[0]]
+    xa = synth.draw_x(rng, m, 2560, "normal")
+    xc = synth.draw_x(rng, m, 1280, "student_t3")
+    xd = synth.draw_x(rng, m, 1024, "normal")
+    R1 = synth.draw_rotation(rng, 2560 // block, block)
+    R2 = synth.draw_rotation(rng, 1280 // block, block)
+    xs_h = [xa, xa, xc, xd]
+    rots_h = [R1, R1, R2, None]
+    with b3_route(route):
+        pms = [upload_pack(mt, fmt) for mt in mats]
+        xa_d, xc_d, xd_d = _dev16(xa), _dev16(xc), _dev16(xd)
+        xs = [xa_d, xa_d, xc_d, xd_d]
+        R1d, R2d = _dev16(R1), _dev16(R2)
+        rots = [R1d, R1d, R2d, None]
+        ys = [torch.empty((m, mt["n"]), dtype=torch.float32, device="cuda") for mt in mats]
+        plan = L.Plan(pms, xs, ys, y_dtype=L.TERN_F32, rots=rots, rot_block=block)
+        plan.run()
+        torch.cuda.synchronize()
+        first = [y.clone() for y in ys]
+        plan.run()
+        torch.cuda.synchronize()
+    for i, (mt, x, R) in enumerate(zip(mats, xs_h, rots_h)):
+        assert torch.equal(ys[i], first[i]), "runs differ"
+        if R is None:
+            y_ref, b = oracle_y(mt, x)
+        else:
+            xr = Rt.rotate(R, x)
+            y_ref, b1 = oracle_y(mt, xr)
+            _, b2 = oracle_y(mt, Rt.rotate_bound(R, x))
+            b = b1 + 1.002 * b2
+        check_y(ys[i], y_ref, b, f"rotated plan product {i}")
+
+
+def test_rotated_plan_rejects_mixed_rotations():
+    """Products that read one x with different rotations are refused."""
+    import torch
+    from gpu_util import small_matrix, upload_pack
+    say("rotated plan: mixed rotations")
+    rng = np.random.default_rng(3)
+    mats = [small_matrix(64, 1024, 128, 1, 0.0, seed=s)[0] for s in (1, 2)]
+    pms = [upload_pack(mt, O.FMT_2BIT) for mt in mats]
+    x = _dev16(synth.draw_x(rng, 1, 1024, "normal"))
+    R1, R2 = (_dev16(synth.draw_rotation(rng, 8, 128)) for _ in range(2))
+    ys = [torch.empty((1, 64), dtype=torch.float16, device="cuda") for _ in range(2)]
+    with pytest.raises(L.TernError):
+        L.Plan(pms, [x, x], ys, rots=[R1, R2])
