@@ -321,17 +321,21 @@ def bench_stack8b_rotated(stream, mats, xs, ys, steps=200):
 
 
 def bench_layer4b_rotated(stream, steps=720):
-    """The 4B-class layer (2-bit, M=1) with its three distinct inputs rotated
-    (128 x 128 blocks; the decode route runs one rotation launch before the
-    product), beside the same layer unrotated; 36 byte copies rotated."""
+    """The 4B-class layer (2-bit, M=1) with its four distinct inputs (q/k/v
+    and gate/up share one each) rotated by 128 x 128 blocks inside the
+    decode launch (its first workgroups rotate; tern_plan_launches is 1),
+    beside the same layer unrotated; 36 byte copies rotated."""
     import torch
     from ternary_weight_only_tern_amd import lib as L
     from ternary_weight_only_tern_amd import synth
-    base, xs, ys = [], [], []
+    base, xs, ys, xin = [], [], [], {}
     for proj in range(len(synth.QWEN3_4B_LAYER)):
         pm, _ = pack_workload("qwen3_4b_layer", 0, proj)
         base.append(pm)
-        xs.append(x_for("qwen3_4b_layer", synth.LAYER_INPUT[proj], 1)[0])
+        src = synth.LAYER_INPUT[proj]
+        if src not in xin:
+            xin[src] = x_for("qwen3_4b_layer", src, 1)[0]
+        xs.append(xin[src])
         ys.append(torch.empty((1, pm.n), dtype=torch.float16, device="cuda"))
     rng = np.random.default_rng(4243)
     rot_of = {}
@@ -342,14 +346,17 @@ def bench_layer4b_rotated(stream, steps=720):
     rots = [rot_of[x.data_ptr()] for x in xs]
     layers = [base] + [[clone_packed(pm) for pm in base] for _ in range(LAYERS - 1)]
     out = {}
+    launches = {}
     for name, kw in (("rotated", dict(rots=rots, rot_block=128)), ("unrotated", {})):
         plans = [L.Plan(layer, xs, ys, **kw) for layer in layers]
+        launches[name] = plans[0].launches()
         fns = [(lambda p=p: p.run(stream.cuda_stream)) for p in plans]
         wall, gpu, _ = time_graph(fns, steps, LAYERS, stream)
         out[name] = round(gpu / steps * 1e6, 3)
         del plans, fns
     del layers
     return dict(us_per_layer=out["rotated"], us_per_layer_unrotated=out["unrotated"],
+                launches=launches["rotated"], launches_unrotated=launches["unrotated"],
                 rotation_bytes=sum(r.numel() * 2 for r in rot_of.values()), steps=steps)
 
 
@@ -760,8 +767,8 @@ def main():
             note="one grouped launch per layer; 36 byte copies of the layer rotated")
         log(f"bench: 4B-class layer {l4['step_s']*1e6:.2f} us/step, {l4['gbs']:.1f} GB/s")
         r4 = bench_layer4b_rotated(stream)
-        extra["qwen3_4b_layer_m1_2bit_rotated"] = dict(r4, note="one rotation launch for the layer's three inputs "
-                                                       "before the decode launch, both in one plan")
+        extra["qwen3_4b_layer_m1_2bit_rotated"] = dict(r4, note="the layer's four distinct inputs rotated inside "
+                                                       "the decode launch (one plan, one launch)")
         log(f"bench: 4B-class layer with rotations {r4['us_per_layer']:.2f} us (without {r4['us_per_layer_unrotated']:.2f})")
         sweep = {}
         for m in (1, 4, 16, 64, 512):

@@ -261,6 +261,10 @@ tern_status tern_plan_run(const tern_plan *plan, void *stream);
  * graph. */
 tern_status tern_plan_run_events(const tern_plan *plan, void *stream, void *before, void *after);
 void tern_plan_destroy(tern_plan *plan);
+/* Kernel launches one tern_plan_run of this plan makes (rotation launches
+ * included), for sizing graphs and reading traces; -1 for NULL.  Host-only,
+ * no GPU call. */
+int32_t tern_plan_launches(const tern_plan *plan);
 
 /* A plan whose products take rotated activations: y[i] = x[i]
  * blockdiag(R_i)^T W[i]^T, the rotation applied to the activations before
@@ -271,14 +275,24 @@ void tern_plan_destroy(tern_plan *plan);
  * takes x[i] as it is), rot_block 64 or 128, each rotated k a multiple of
  * it; the rotation is that of tern_rotate (FP32 sums, FP16 values).
  * Products that read the same x must share its rotation (TERN_E_INVAL).
- * ws: tern_rotated_workspace_bytes(w, count, m) bytes; it holds one rotated
- * copy of each distinct rotated x, then the plan's own tables.  Base-3 plans
- * at m <= 4 on the stream kernel rotate inside their activation preparation
- * (the rotation costs no launch of its own beyond that preparation, which
- * then runs before the residual pass instead of alongside it); other plans
- * launch the rotations (tern_rotate_batched's kernel, up to 8 inputs per
- * launch) before the product.  rot == NULL is tern_plan_create.  The rest is
- * as for tern_plan_create (run with tern_plan_run, free with
+ * ws: tern_rotated_workspace_bytes(w, count, m) bytes; it holds the
+ * counters of a rotation inside the product's launch (below), one rotated
+ * copy of each distinct rotated x, then the plan's own tables.  Where the
+ * rotation runs:
+ *  - base-3 plans at m <= 4 on the stream kernel: inside their activation
+ *    preparation (no launch of its own; the preparation then runs before the
+ *    residual pass instead of alongside it);
+ *  - 2-bit plans on the decode route (m <= 5 at group 128, m <= 4 at group
+ *    64) with at most 8 distinct rotated inputs: inside the product's own
+ *    launch, whose first workgroups rotate while the others request their
+ *    first weights and then wait for the rotated activations (the FP32 sum
+ *    of a rotated value is taken in an order of its own, so a value may
+ *    differ from tern_rotate's in the last FP16 place);
+ *  - other plans: rotation launches (tern_rotate_batched's kernel, up to 8
+ *    inputs per launch) before the product.
+ * tern_plan_launches tells which.  The counters make overlapping runs of one
+ * plan race (as do its partial sums).  rot == NULL is tern_plan_create.  The
+ * rest is as for tern_plan_create (run with tern_plan_run, free with
  * tern_plan_destroy). */
 size_t tern_rotated_workspace_bytes(const tern_matrix *w, int32_t count, int32_t m);
 tern_status tern_plan_create_rotated(const tern_matrix *w, const uint16_t *const *x,

@@ -36,6 +36,7 @@
 // per-group activation sums computed once per workgroup.  All sums are in a
 // fixed order, so results are bitwise reproducible.
 #include <algorithm>
+#include <cstring>
 
 #include "internal.h"
 #include "kparts.h"
@@ -219,9 +220,146 @@ constexpr int res_stage_bytes() { return kResStage * (G / 4) + (kResStage / 4 + 
 template <int G, int MP>
 constexpr int mfma_waves_per_eu() { return MP == 8 || (G == 64 && MP == 4) ? 2 : 3; }
 
-template <int G, int MP>
-__global__ __launch_bounds__(kWave * kWaves) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<G, MP>(), 8)))
-void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, const WgRec* __restrict__ recs, int ndesc, GemvDesc one) {
+// ---- the rotation folded into the launch (RotFold): xr = blockdiag(R) x
+// ("Post-Training Ternarization of Qwen3-4B", §4.2: inference rotates the
+// activations into the basis the weights were quantized in).  Share s of
+// an input covers kRotShareRows consecutive positions: LPR adjacent lanes
+// form one position's row of R times x (each a 1/LPR part of the row, B /
+// (2 LPR) FP16 pairs with v_dot2_f32_f16 in order), add their parts (lane
+// distance 1, 2, ...: a fixed order, so runs are reproducible), and each
+// even position stores itself and the next as one word.
+template <int RBLK>
+__device__ __forceinline__ void rot_share(const RotFold& f, int share) {
+  constexpr int LPR = kThreads / kRotShareRows;  // lanes per position
+  constexpr int CPT = RBLK / 8 / LPR;            // 16-byte chunks of a row per lane
+  static_assert(LPR >= 1 && LPR <= 32 && CPT >= 1 && kThreads == LPR * kRotShareRows, "share shape");
+  const RotBatch& a = f.a;
+  // this share's input, picked with uniform selects (an indexed read would
+  // copy the argument block to scratch memory)
+  const uint16_t* R = a.R[0];
+  const uint16_t* x = a.x[0];
+  uint16_t* out = a.out[0];
+  int k = a.k[0], first = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxRotations; ++q)
+    if (q < a.count && share >= a.begin[q]) {
+      R = a.R[q];
+      x = a.x[q];
+      out = a.out[q];
+      k = a.k[q];
+      first = a.begin[q];
+    }
+  const int t = threadIdx.x, i = t / LPR, j = t % LPR;
+  const int pos = (share - first) * kRotShareRows + i;  // the last share of an input may pass k
+  const bool live = pos < k;
+  const int pc = live ? pos : k - 1;
+  const int b = pc / RBLK, ib = pc % RBLK;
+  const GLOBAL u4_t* rr = reinterpret_cast<const GLOBAL u4_t*>(gp(R) + ((size_t)b * RBLK + ib) * RBLK) + j * CPT;
+  u4_t rv[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) rv[c] = rr[c];
+  for (int m = 0; m < a.m; ++m) {
+    const GLOBAL u4_t* xp = reinterpret_cast<const GLOBAL u4_t*>(gp(x) + (size_t)m * k + (size_t)b * RBLK) + j * CPT;
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const u4_t xv = xp[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // through plain words: a bit cast of a vector element itself reads
+        // element 0 with this compiler
+        const uint32_t rw = rv[c][e], xw = xv[e];
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, rw), __builtin_bit_cast(h2_t, xw), acc, false);
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) acc += __shfl_xor(acc, o, kWave);
+    const float next = __shfl_down(acc, LPR, kWave);  // position pos + 1
+    if (live && t % (2 * LPR) == 0) {
+      const uint32_t word = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)acc) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)next) << 16);
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(out + (size_t)m * k + pos), word, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // the stores are acknowledged by the device-coherent level, in every
+  // wavefront, before the share counts itself in; the last share raises
+  // the ready flag copy of every group that has members (one per lane of
+  // wavefront 0; a group with none would never lower it)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  if (t < kWave) {
+    uint32_t before = 0u;
+    if (t == 0) before = __hip_atomic_fetch_add(f.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    before = __shfl(before, 0, kWave);
+    if (before + 1u == (uint32_t)f.shares && t < (int)gridDim.x - f.shares)
+      __hip_atomic_store(f.sync + kRotLineWords * (1 + t), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The counters of a folded rotation, one 256-byte line each (RotFold.sync):
+// line 0 holds the shares counted [0], the waiter groups done [1] and the
+// give-up word [2]; line 1 + c holds copy c of the ready flag [0] and the
+// count of group c's workgroups through the wait [1].  A product workgroup
+// belongs to group (its index) % kRotFlags, so every address is polled by a
+// few workgroups only (accesses to one address are served one at a time).
+static_assert(kRotFlags == kWave, "one flag copy per lane");
+
+// Product side: wait until this group's flag copy is raised (bounded; a wait
+// that gives up records it and goes on), then count the workgroup in at its
+// group.  Returns that count's old value (thread 0; used by rot_release).
+// Shares are the launch's lowest workgroups, so each is placed before any
+// workgroup that waits for it, and shares never wait.
+constexpr uint64_t kRotWaitTicks = 2000000;  // 20 ms of the 100 MHz clock
+__device__ __forceinline__ uint32_t rot_wait(const RotFold& f, int wg) {
+  uint32_t* line = f.sync + kRotLineWords * (1 + wg % kRotFlags);
+  uint32_t mine = 0u;
+  if (threadIdx.x == 0) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+      __builtin_amdgcn_s_sleep(2);
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kRotWaitTicks) {
+        __hip_atomic_store(f.sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    mine = __hip_atomic_fetch_add(line + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return mine;
+}
+
+// Thread 0 of a product workgroup, late in its run (the count returned by
+// rot_wait has arrived by then): the group's last workgroup lowers the
+// group's flag copy and clears its count, then counts the group in; the
+// last group clears line 0 for the next launch.
+__device__ __forceinline__ void rot_release(const RotFold& f, int wg, uint32_t mine) {
+  const int items = (int)gridDim.x - f.shares;
+  const int c = wg % kRotFlags;
+  const uint32_t members = (uint32_t)(items / kRotFlags + (c < items % kRotFlags ? 1 : 0));
+  if (mine + 1u != members) return;
+  uint32_t* line = f.sync + kRotLineWords * (1 + c);
+  __hip_atomic_store(line, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(line + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t groups = (uint32_t)min(items, kRotFlags);
+  if (__hip_atomic_fetch_add(f.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u == groups) {
+    __hip_atomic_store(f.sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(f.sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The product; with RBLK > 0 the launch's first f.shares workgroups rotate
+// (rot_share) and the activations are staged after rot_wait.
+template <int G, int MP, int RBLK>
+__device__ __forceinline__ void mfma_body(const GemvDesc* __restrict__ descs, const WgRec* __restrict__ recs,
+                                          int ndesc, const GemvDesc& one, const RotFold& f) {
+  if constexpr (RBLK > 0) {
+    if ((int)blockIdx.x < f.shares) {
+      rot_share<RBLK>(f, (int)blockIdx.x);
+      return;
+    }
+  }
+  const int wg = (int)blockIdx.x - (RBLK > 0 ? f.shares : 0);
   constexpr int GW = Win<MP>::GW;
   constexpr int NACC = Win<MP>::NACC;
   constexpr int GPB = kBlockTrits / G;      // groups per block
@@ -237,15 +375,15 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, const WgRec* __restric
   GemvDesc d;
   int item;
   uint32_t te[5] = {0u, 0u, 0u, 0u, 0u};
-  if (ndesc > 0) {
-    const WgRec rec = recs[blockIdx.x];
+  if (RBLK > 0 || ndesc > 0) {  // rotating launches are always grouped
+    const WgRec rec = recs[wg];
     d = descs[rec.ri >> 20];
     item = (int)(rec.ri & 0xFFFFFu);
 #pragma unroll
     for (int t = 0; t < 5; ++t) te[t] = rec.te[t];
   } else {
     d = one;
-    item = (int)blockIdx.x - d.tile_begin;
+    item = wg - d.tile_begin;
   }
   const int rb = item % d.row_blocks;
   const int split = item / d.row_blocks;
@@ -328,19 +466,26 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, const WgRec* __restric
   }
   u4_t sfix = u4_t{0u, 0u, 0u, 0u};
   if (tid < nsch - nsfull) sfix = scale_chunk(s0, send, sa0 + (size_t)(nsfull + tid) * 16);
-  // activations [dm][krp], row m at m * krp (chunk id at 16 id); zero past the range
-  {
-    const __amdgpu_buffer_rsrc_t rx = rsrc(d.x, (uint32_t)dm * d.k * 2u);
-    for (int u = 0; u * kThreads < nx; ++u) {
-      const int id = u * kThreads + tid;
-      if (id < nx) {
-        const int m = xrow_of<MP>(id, cpr);
-        const int kk = (id - m * cpr) * 8;
-        if (kk < kr) lds_load16(rx, lds + xoff + (u * kThreads + wave * kWave) * 16, ((uint32_t)m * d.k + k0 + kk) * 2u);
-        else *reinterpret_cast<u4_t*>(lds + xoff + id * 16) = u4_t{0u, 0u, 0u, 0u};
-      }
-    }
-  }
+  // activations [dm][krp], row m at m * krp (chunk id at 16 id); zero past
+  // the range.  Rotated activations are written during the launch, so they
+  // are staged after rot_wait, with ordinary loads: the shares' stores went
+  // through to the device-coherent level, and no workgroup reads the rotated
+  // copy before the flag rises, so no L2 holds a line of it from before this
+  // launch's stores (the L2s start each launch invalidated).
+#define TERN_STAGE_X()                                                                        \
+  do {                                                                                        \
+    const __amdgpu_buffer_rsrc_t rx_ = rsrc(d.x, (uint32_t)dm * d.k * 2u);                    \
+    for (int u = 0; u * kThreads < nx; ++u) {                                                 \
+      const int id = u * kThreads + tid;                                                      \
+      if (id < nx) {                                                                          \
+        const int m = xrow_of<MP>(id, cpr);                                                   \
+        const int kk = (id - m * cpr) * 8;                                                    \
+        if (kk < kr) lds_load16(rx_, lds + xoff + (u * kThreads + wave * kWave) * 16, ((uint32_t)m * d.k + k0 + kk) * 2u); \
+        else *reinterpret_cast<u4_t*>(lds + xoff + id * 16) = u4_t{0u, 0u, 0u, 0u};           \
+      }                                                                                       \
+    }                                                                                         \
+  } while (0)
+  if (RBLK == 0) TERN_STAGE_X();
   // first residual plane, when the plan indexed it and the item covers the
   // whole row: the workgroup's entries [e0, e1) (its rows are contiguous) are
   // staged in LDS with the other small operands -- their blocks as raw
@@ -495,7 +640,15 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, const WgRec* __restric
     __builtin_amdgcn_sched_barrier(0);                                                        \
     if (tid < nsch - nsfull) *reinterpret_cast<u4_t*>(lds + scoff + (nsfull + tid) * 16) = sfix; \
     if (tid < kZeroBytes / 16) *reinterpret_cast<u4_t*>(lds + tid * 16) = u4_t{0u, 0u, 0u, 0u}; \
-    TERN_WAIT_VM(DP_); /* this wavefront's LDS loads have landed */                          \
+    if (RBLK > 0) {                                                                           \
+      /* the poll returns behind this wavefront's first DP_ blocks (loads */                  \
+      /* complete in order), which arrive early; the rest stream after it */                  \
+      rot_mine = rot_wait(f, wg);                                                             \
+      TERN_STAGE_X();                                                                         \
+      TERN_WAIT_VM(0);                                                                        \
+    } else {                                                                                  \
+      TERN_WAIT_VM(DP_); /* this wavefront's LDS loads have landed */                        \
+    }                                                                                         \
     __syncthreads();                                                                          \
     /* plane 0, with this wavefront's residual batches after its first blocks */            \
     _Pragma("unroll") for (int i = 0; i < NB; ++i) {                                          \
@@ -510,11 +663,13 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, const WgRec* __restric
     if (nblk > 0 && nblk % BW != 0) TERN_CLOSE((nblk - 1) / BW);                              \
     for (int j_ = NB; j_ < nrb; ++j_) TERN_RES_ONE(j_);                                       \
   } while (0)
+  uint32_t rot_mine = 0u;
   if (bpp > 8) TERN_BODY(kMaxBlocks);
   else TERN_BODY(8);
 #undef TERN_BODY
 #undef TERN_BLOCK
 #undef TERN_CLOSE
+#undef TERN_STAGE_X
 
   // sum the lanes that hold other groups of the same (row, activation row)
   if (GW >= 8) acc[0] += __shfl_xor(acc[0], 16, kWave);
@@ -663,6 +818,7 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, const WgRec* __restric
       }
     }
   }
+  if (RBLK > 0 && tid == 0) rot_release(f, wg, rot_mine);
   // ---- output
   const bool writer = lead && owner && row_ok;
   if (d.splits > 1) {
@@ -695,6 +851,22 @@ void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, const WgRec* __restric
   }
 }
 
+template <int G, int MP>
+__global__ __launch_bounds__(kWave * kWaves) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<G, MP>(), 8)))
+void gemv_mfma_kernel(const GemvDesc* __restrict__ descs, const WgRec* __restrict__ recs, int ndesc, GemvDesc one) {
+  RotFold none;
+  none.shares = 0;
+  mfma_body<G, MP, 0>(descs, recs, ndesc, one, none);
+}
+
+template <int G, int MP, int RBLK>
+__global__ __launch_bounds__(kWave * kWaves) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<G, MP>(), 8)))
+void gemv_mfma_rot_kernel(const GemvDesc* __restrict__ descs, const WgRec* __restrict__ recs, int ndesc, RotFold f) {
+  GemvDesc none;
+  none.tile_begin = 0;
+  mfma_body<G, MP, RBLK>(descs, recs, ndesc, none, f);
+}
+
 // Dynamic LDS of a launch (the layout the kernel computes, at its largest).
 template <int G, int MP>
 size_t mfma_lds_bytes(int max_krp, bool offsets) {
@@ -710,6 +882,18 @@ hipError_t launch_mfma(const GemvDesc* descs, const WgRec* recs, int ndesc, cons
                        bool offsets, hipStream_t s) {
   const size_t lds = mfma_lds_bytes<G, MP>(max_krp, offsets);
   hipLaunchKernelGGL((gemv_mfma_kernel<G, MP>), dim3(items), dim3(kWave * kWaves), lds, s, descs, recs, ndesc, one);
+  return hipGetLastError();
+}
+
+template <int G, int MP>
+hipError_t launch_mfma_rot(const GemvDesc* descs, const WgRec* recs, int ndesc, int items, int max_krp, bool offsets,
+                           const RotFold& f, hipStream_t s) {
+  const size_t lds = mfma_lds_bytes<G, MP>(max_krp, offsets);
+  const dim3 grid((unsigned)(f.shares + items));
+  if (f.block == 128)
+    hipLaunchKernelGGL((gemv_mfma_rot_kernel<G, MP, 128>), grid, dim3(kWave * kWaves), lds, s, descs, recs, ndesc, f);
+  else
+    hipLaunchKernelGGL((gemv_mfma_rot_kernel<G, MP, 64>), grid, dim3(kWave * kWaves), lds, s, descs, recs, ndesc, f);
   return hipGetLastError();
 }
 
@@ -798,6 +982,28 @@ hipError_t launch_gemv_mfma(int group, int mp, const GemvDesc* descs, const WgRe
   if (group == 64) return launch_mfma_g<64>(mp, descs, recs, ndesc, one, total_items, max_krp, offsets, s);
   if (group == 128) return launch_mfma_g<128>(mp, descs, recs, ndesc, one, total_items, max_krp, offsets, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv_mfma_rot(int group, int mp, const GemvDesc* descs, const WgRec* recs, int ndesc,
+                                int total_items, int max_krp, bool offsets, const RotFold& f, hipStream_t s) {
+  if (total_items <= 0) return hipSuccess;
+  if (ndesc <= 0 || !recs || !f.sync || f.shares < 0 || f.a.m > mp || !(f.block == 64 || f.block == 128))
+    return hipErrorInvalidValue;
+  if (f.shares == 0) {
+    GemvDesc unused;
+    std::memset(&unused, 0, sizeof(unused));
+    return launch_gemv_mfma(group, mp, descs, recs, ndesc, unused, total_items, max_krp, offsets, s);
+  }
+  switch (group * 16 + mp) {
+    case 128 * 16 + 1: return launch_mfma_rot<128, 1>(descs, recs, ndesc, total_items, max_krp, offsets, f, s);
+    case 128 * 16 + 2: return launch_mfma_rot<128, 2>(descs, recs, ndesc, total_items, max_krp, offsets, f, s);
+    case 128 * 16 + 4: return launch_mfma_rot<128, 4>(descs, recs, ndesc, total_items, max_krp, offsets, f, s);
+    case 128 * 16 + 8: return launch_mfma_rot<128, 8>(descs, recs, ndesc, total_items, max_krp, offsets, f, s);
+    case 64 * 16 + 1: return launch_mfma_rot<64, 1>(descs, recs, ndesc, total_items, max_krp, offsets, f, s);
+    case 64 * 16 + 2: return launch_mfma_rot<64, 2>(descs, recs, ndesc, total_items, max_krp, offsets, f, s);
+    case 64 * 16 + 4: return launch_mfma_rot<64, 4>(descs, recs, ndesc, total_items, max_krp, offsets, f, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace tern

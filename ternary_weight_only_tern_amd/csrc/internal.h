@@ -265,6 +265,29 @@ struct RotBatch {
 };
 hipError_t launch_rotate(const RotBatch& a, int block, hipStream_t stream);
 
+// The rotation folded into a matrix-core decode launch (plans only).  The
+// launch's first `shares` workgroups each rotate kRotShareRows consecutive
+// positions of one input into a.out (a.begin counts shares: ceil(k_i /
+// kRotShareRows) per input) with write-through stores and count themselves
+// in; the last raises kRotFlags copies of a ready flag.  Every later
+// workgroup requests its first weight blocks, waits for its group's flag
+// copy, and then stages its activations (the descriptors' x, which point
+// into a.out).  The counters clear themselves by the end of each launch
+// (sync: kRotSyncBytes, zero before the first launch; layout in
+// gemv_mfma.hip).  The wait is bounded; a wait that gives up sets word 2.
+// Launches of one plan must not overlap.
+constexpr int kRotShareRows = 128;
+constexpr int kRotFlags = 64;
+constexpr int kRotLineWords = 64;  // 256 bytes
+constexpr size_t kRotSyncBytes = (size_t)(kRotFlags + 1) * kRotLineWords * 4;
+struct RotFold {
+  RotBatch a;
+  int32_t block, shares;
+  uint32_t* sync;  // kRotSyncBytes, zero before the first launch
+};
+hipError_t launch_gemv_mfma_rot(int group, int mp, const GemvDesc* descs, const WgRec* recs, int ndesc,
+                                int total_items, int max_krp, bool offsets, const RotFold& rot, hipStream_t stream);
+
 // ---- packing (pack.hip)
 hipError_t launch_pack_plane0(int format, const int8_t* trits, int n, int k, int group,
                               int stride, uint8_t* plane0, uint32_t* flag, hipStream_t stream);

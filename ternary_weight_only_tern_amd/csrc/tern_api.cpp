@@ -266,6 +266,8 @@ struct tern_plan {
   bool prep_first;        // base-3: the preparations rotate, so they run before the residual pass
   tern::RotBatch* rots;   // rotations launched before the product (malloc'ed; NULL: none)
   int nrots, rot_block;
+  bool folded;            // matrix-core decode: the rotations run inside its launch (fold)
+  tern::RotFold fold;
 };
 
 extern "C" {
@@ -1892,6 +1894,10 @@ static tern_status plan_launch(const tern_plan* plan, hipStream_t s, hipEvent_t 
   } else if (plan->small) {
     TERN_HIP(tern::launch_gemm_small(plan->dev, plan->total_items, plan->format, plan->group, plan->np, plan->offs, s));
     if (plan->nred) TERN_HIP(tern::launch_reduce_grouped(plan->red, plan->nred, plan->red_blocks, s));
+  } else if (plan->folded) {
+    TERN_HIP(tern::launch_gemv_mfma_rot(plan->group, plan->mt, plan->dev, plan->recs, plan->ndesc, plan->total_items,
+                                        plan->max_krp, plan->offsets, plan->fold, s));
+    if (plan->nred) TERN_HIP(tern::launch_reduce_grouped(plan->red, plan->nred, plan->red_blocks, s));
   } else {
     GemvDesc dummy;
     std::memset(&dummy, 0, sizeof(dummy));
@@ -1918,14 +1924,30 @@ tern_status tern_plan_run_events(const tern_plan* plan, void* stream, void* befo
   return plan_launch(plan, (hipStream_t)stream, (hipEvent_t)before, (hipEvent_t)after);
 }
 
+int32_t tern_plan_launches(const tern_plan* plan) {
+  if (!plan) return -1;
+  int32_t n = plan->nrots;
+  if (plan->total_items == 0) return n;
+  if (plan->b3) {
+    const bool own_prep = plan->nres == 0 || plan->prep_first;
+    return n + (own_prep && plan->nprep > 0 ? 1 : 0) + (plan->nres > 0 ? 1 : 0) + (plan->nwg > 0 ? 1 : 0);
+  }
+  return n + 1 + (plan->nred > 0 ? 1 : 0);
+}
+
 void tern_plan_destroy(tern_plan* plan) {
   if (plan) std::free(plan->rots);
   std::free(plan);
 }
 
+// A rotated plan's workspace: the counters of a folded rotation
+// (tern::kRotSyncBytes), one rotated copy per distinct x, then the plan's
+// own tables.
+using tern::kRotSyncBytes;
+
 size_t tern_rotated_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m) {
   if (count <= 0 || m <= 0 || !w) return 0;
-  size_t bytes = tern_batch_workspace_bytes(w, count, m);
+  size_t bytes = tern_batch_workspace_bytes(w, count, m) + kRotSyncBytes;
   for (int i = 0; i < count; ++i)
     if (w[i].k > 0) bytes += round_up((size_t)2 * m * w[i].k, 256);  // a rotated copy per product at most
   return bytes;
@@ -1940,12 +1962,12 @@ tern_status tern_plan_create_rotated(const tern_matrix* w, const uint16_t* const
   if (rot_block != 64 && rot_block != 128) return fail(TERN_E_UNSUPPORTED, "rotation blocks of 64 or 128 (got %d)", rot_block);
   if (count < 0 || m < 0) return fail(TERN_E_INVAL, "count=%d, m=%d must not be negative", count, m);
   if (count > 0 && (!w || !x || !y)) return fail(TERN_E_INVAL, "NULL descriptor, activation or output arrays");
-  // one rotated copy per distinct (x, R) at the start of ws, the plan's own
-  // workspace after them
+  // the fold's counters, then one rotated copy per distinct (x, R), then the
+  // plan's own workspace
   std::map<const uint16_t*, std::pair<const uint16_t*, size_t>> seen;  // x -> (R, offset of its copy)
   std::vector<const uint16_t*> xin(count > 0 ? count : 1);
   std::vector<uint16_t*> xr(count > 0 ? count : 1, nullptr);
-  size_t off = 0;
+  size_t off = kRotSyncBytes;
   for (int i = 0; i < count; ++i) {
     xin[i] = x[i];
     if (!rot[i] || w[i].n <= 0 || w[i].k <= 0 || m == 0) continue;
@@ -1988,6 +2010,29 @@ tern_status tern_plan_create_rotated(const tern_matrix* w, const uint16_t* const
     a.k[a.count] = w[i].k;
     a.begin[a.count + 1] = a.begin[a.count] + w[i].k / rot_block;
     ++a.count;
+  }
+  tern_plan* p = *out;
+  // the matrix-core decode takes up to kMaxRotations inputs inside its own
+  // launch: the shares first, then the product's workgroups
+  if (rb.size() == 1 && !p->gemm && !p->small && !p->b3 && p->recs && p->total_items > 0 && use_mfma(p->format) &&
+      m <= p->mt) {
+    tern::RotFold& f = p->fold;
+    f.a = rb[0];
+    for (int i = 0; i <= f.a.count; ++i) f.a.begin[i] = 0;
+    for (int i = 0; i < f.a.count; ++i)
+      f.a.begin[i + 1] = f.a.begin[i] + (f.a.k[i] + tern::kRotShareRows - 1) / tern::kRotShareRows;
+    f.block = rot_block;
+    f.shares = f.a.begin[f.a.count];
+    f.sync = static_cast<uint32_t*>(ws);
+    hipError_t e = hipMemset(ws, 0, kRotSyncBytes);
+    if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+    if (e != hipSuccess) {
+      tern_plan_destroy(p);
+      *out = nullptr;
+      return fail(TERN_E_HIP, "hipMemset: %s", hipGetErrorString(e));
+    }
+    p->folded = true;
+    return TERN_OK;
   }
   if (!rb.empty()) {
     (*out)->rots = static_cast<tern::RotBatch*>(std::malloc(rb.size() * sizeof(tern::RotBatch)));

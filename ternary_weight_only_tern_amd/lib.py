@@ -35,7 +35,7 @@ TERN_F32 = 1
 
 SYMBOLS = ["tern_row_stride", "tern_check", "tern_packed_sizes", "tern_workspace_bytes",
            "tern_pack", "tern_unpack", "tern_gemv", "tern_gemm", "tern_batch_workspace_bytes",
-           "tern_gemv_batched", "tern_plan_create", "tern_plan_run", "tern_plan_run_events", "tern_plan_destroy", "tern_b3_min_stages", "tern_gemv_noalloc",
+           "tern_gemv_batched", "tern_plan_create", "tern_plan_run", "tern_plan_run_events", "tern_plan_launches", "tern_plan_destroy", "tern_b3_min_stages", "tern_gemv_noalloc",
            "tern_rotated_workspace_bytes", "tern_plan_create_rotated",
            "tern_bits", "tern_quantize", "tern_rotate", "tern_rotate_batched", "tern_read_probe", "tern_status_str", "tern_last_error"]
 
@@ -80,6 +80,7 @@ def load() -> ctypes.CDLL:
         "tern_plan_create": (c_int32, [P, POINTER(c_void_p), POINTER(c_void_p), c_int32, c_int32, c_int32, c_void_p, c_size_t, POINTER(c_void_p)]),
         "tern_plan_run": (c_int32, [c_void_p, c_void_p]),
         "tern_plan_run_events": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p]),
+        "tern_plan_launches": (c_int32, [c_void_p]),
         "tern_b3_min_stages": (ctypes.c_int64, [ctypes.c_int64]),
         "tern_rotated_workspace_bytes": (c_size_t, [c_void_p, c_int32, c_int32]),
         "tern_plan_create_rotated": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32,
@@ -311,6 +312,10 @@ class Plan:
         """run() recording two torch.cuda.Event objects (created with
         enable_timing=True) around the main decode launch."""
         check(load().tern_plan_run_events(self.handle, _stream(stream), _event(before), _event(after)))
+
+    def launches(self):
+        """Kernel launches one run() makes (tern_plan_launches)."""
+        return int(load().tern_plan_launches(self.handle))
 
     def __del__(self):
         if getattr(self, "handle", None) and _lib is not None:

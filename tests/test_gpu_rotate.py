@@ -158,6 +158,7 @@ def test_rotated_plan_matches_oracle(fmt, m, route, block):
         rots = [R1d, R1d, R2d, None]
         ys = [torch.empty((m, mt["n"]), dtype=torch.float32, device="cuda") for mt in mats]
         plan = L.Plan(pms, xs, ys, y_dtype=L.TERN_F32, rots=rots, rot_block=block)
+        say("launches per run:", plan.launches())
         plan.run()
         torch.cuda.synchronize()
         first = [y.clone() for y in ys]
@@ -188,3 +189,108 @@ def test_rotated_plan_rejects_mixed_rotations():
     ys = [torch.empty((1, 64), dtype=torch.float16, device="cuda") for _ in range(2)]
     with pytest.raises(L.TernError):
         L.Plan(pms, [x, x], ys, rots=[R1, R2])
+
+
+# the folded rotation's counters at the start of a rotated plan's workspace:
+# 65 lines of 256 bytes (shares and groups counted, give-up word; 64 copies
+# of the ready flag with their groups' counts)
+ROT_SYNC_BYTES = 65 * 256
+
+
+def _rotated_layer(rng, group, block, ks, m, fmt):
+    """Products with rotated inputs: for each k in ks a product of that depth
+    (some with residual planes and offsets), one distinct x and R per k,
+    plus a product that shares the first x and R and one unrotated
+    product."""
+    from gpu_util import small_matrix, upload_pack
+    mats, xs_h, rots_h = [], [], []
+    for i, k in enumerate(ks):
+        mt = small_matrix(96 + 40 * i, k, group, 1 + i % 3, 0.2, seed=60 + i,
+                          offset_mode=(O.OFF_NONE, O.OFF_ROW, O.OFF_GROUP)[i % 3])[0]
+        mats.append(mt)
+        xs_h.append(synth.draw_x(rng, m, k, ("normal", "student_t3")[i % 2]))
+        rots_h.append(synth.draw_rotation(rng, k // block, block))
+    mats.append(small_matrix(70, ks[0], group, 2, 0.1, seed=70)[0])
+    xs_h.append(xs_h[0])
+    rots_h.append(rots_h[0])
+    mats.append(small_matrix(64, ks[-1], group, 1, 0.0, seed=71)[0])
+    xs_h.append(synth.draw_x(rng, m, ks[-1], "normal"))
+    rots_h.append(None)
+    pms = [upload_pack(mt, fmt) for mt in mats]
+    return mats, xs_h, rots_h, pms
+
+
+def _check_rotated(ys, mats, xs_h, rots_h, what):
+    from gpu_util import check_y, oracle_y
+    for i, (mt, x, R) in enumerate(zip(mats, xs_h, rots_h)):
+        if R is None:
+            y_ref, b = oracle_y(mt, x)
+        else:
+            y_ref, b1 = oracle_y(mt, Rt.rotate(R, x))
+            _, b2 = oracle_y(mt, Rt.rotate_bound(R, x))
+            b = b1 + 1.002 * b2
+        check_y(ys[i], y_ref, b, f"{what}: product {i}")
+
+
+@pytest.mark.parametrize("group,m,block,ks", [(128, 1, 128, (2560, 4096, 9728)), (128, 2, 64, (1408, 2560)),
+                                              (128, 5, 128, (1024, 3072)), (64, 4, 64, (1344, 640, 2048)),
+                                              (64, 1, 128, (512, 1536))])
+def test_rotated_plan_folded_into_decode_launch(group, m, block, ks):
+    """2-bit plans on the decode route rotate inside the product's own launch
+    (tern_plan_launches == 1): the launch's first workgroups rotate, the
+    others wait for the rotated activations.  Against the oracle's rotation
+    followed by its product (bound as above), with a ragged last share (k =
+    1344 = 21 * 64 at block 64), several inputs, one x shared by two
+    products and one unrotated product; five eager runs bit-identical; the
+    plan captured in a graph and replayed after the inputs change (eager
+    work between replays) equals the eager run every time; the wait never
+    gave up (the workspace's give-up word stays zero)."""
+    import torch
+    say("folded rotation", group, m, block, ks)
+    rng = np.random.default_rng(group + m + block + len(ks))
+    mats, xs_h, rots_h, pms = _rotated_layer(rng, group, block, ks, m, O.FMT_2BIT)
+    xd = {}
+    xs = [xd.setdefault(id(x), _dev16(x)) for x in xs_h]
+    rd = {}
+    rots = [None if R is None else rd.setdefault(id(R), _dev16(R)) for R in rots_h]
+    ys = [torch.empty((m, mt["n"]), dtype=torch.float32, device="cuda") for mt in mats]
+    plan = L.Plan(pms, xs, ys, y_dtype=L.TERN_F32, rots=rots, rot_block=block)
+    assert plan.launches() == 1, f"{plan.launches()} launches: the rotation is not folded"
+    first = None
+    for rep in range(5):
+        plan.run()
+        torch.cuda.synchronize()
+        if first is None:
+            first = [y.clone() for y in ys]
+        for y, f in zip(ys, first):
+            assert torch.equal(y, f), f"run {rep} differs"
+    _check_rotated(ys, mats, xs_h, rots_h, "folded rotation")
+    sync = plan.ws[:ROT_SYNC_BYTES].cpu().numpy().view(np.uint32)
+    assert not sync.any(), f"rotation counters left set at words {np.flatnonzero(sync)[:8].tolist()}"
+
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        plan.run(stream.cuda_stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            plan.run(stream.cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        new_h = {}
+        for key, x in xd.items():
+            fresh = synth.draw_x(rng, m, x.shape[1], "normal")
+            x.copy_(_dev16(fresh))
+            new_h[key] = fresh
+        plan.run()
+        torch.cuda.synchronize()
+        want = [y.clone() for y in ys]
+        for y in ys:
+            y.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (y, w_) in enumerate(zip(ys, want)):
+            assert torch.equal(y, w_), f"replay {rep}: product {i} differs from the eager run"
+    _check_rotated(ys, mats, [new_h[id(x)] for x in xs_h], rots_h, "folded rotation after replays")
+    sync = plan.ws[:ROT_SYNC_BYTES].cpu().numpy().view(np.uint32)
+    assert not sync.any(), f"rotation counters left set at words {np.flatnonzero(sync)[:8].tolist()}"
