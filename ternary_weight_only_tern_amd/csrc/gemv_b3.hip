@@ -142,27 +142,7 @@ __device__ __forceinline__ void b3_prep_block(const B3Prep* __restrict__ preps, 
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int pos = x5_pos<G>(cc, q);
-      if (pos < 0) {
-        h[q] = 0u;
-      } else if (p.R == nullptr) {
-        h[q] = xr[g * G + pos];
-      } else {
-        // the rotated activation at this position: row i of block b of R
-        // times block b of x, FP32 sums in position order, one FP16 rounding
-        const int P = g * G + pos, B = p.rblock, b = P / B, i = P % B;
-        const u4_t* rrow = reinterpret_cast<const u4_t*>(p.R + ((size_t)b * B + i) * B);
-        const u4_t* xb = reinterpret_cast<const u4_t*>(xr + (size_t)b * B);
-        float acc = 0.f;
-        for (int j = 0; j < B / 8; ++j) {
-          const u4_t rv = rrow[j], xv = xb[j];
-          acc = dot2(rv.x, xv.x, acc);
-          acc = dot2(rv.y, xv.y, acc);
-          acc = dot2(rv.z, xv.z, acc);
-          acc = dot2(rv.w, xv.w, acc);
-        }
-        h[q] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)acc);
-        p.xr[(size_t)m * p.k + P] = (uint16_t)h[q];
-      }
+      h[q] = pos < 0 ? 0u : xr[g * G + pos];
     }
     *reinterpret_cast<u2_t*>(p.x5 + ((size_t)m * ng * Gm::CPG + c) * 4) = u2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
   }
@@ -188,6 +168,96 @@ __device__ __forceinline__ void b3_prep_block(const B3Prep* __restrict__ preps, 
 template <int G>
 __global__ __launch_bounds__(256) void b3_prep_kernel(const B3Prep* __restrict__ preps, B3Prep one) {
   b3_prep_block<G>(preps, one, (int)blockIdx.x, (int)blockIdx.y);
+}
+
+// The preparation of a rotated plan: blockIdx.y = product, blockIdx.x = a
+// span of S = max(B, G) positions (whole R blocks and whole groups) for every
+// activation row.  With R: the span's R blocks are copied to LDS with
+// contiguous 16-byte loads (rows padded by a word, so that threads reading
+// consecutive rows use distinct banks), and each value is row i of its block
+// times the block of x, v_dot2_f32_f16 over the FP16 pairs in position order
+// (FP32), one FP16 rounding; the values go to xr in position order (the
+// residual pass reads them) and to x5 in slot order.  Without R the span is
+// copied to x5.  The first span of each product also clears its zero list.
+template <int G, int B>
+__global__ __launch_bounds__(256) void b3_prep_rot_kernel(const B3Prep* __restrict__ preps) {
+  using Gm = B3Geo<G>;
+  constexpr int S = B > G ? B : G;
+  constexpr int P = B / 2 + 1;  // padded R row pitch in LDS (FP16 pairs)
+  constexpr int NC = S * (B / 8) / 256;
+  static_assert(NC >= 1 && S * (B / 8) % 256 == 0, "R chunks spread over the threads");
+  __shared__ uint32_t rs[S * P];
+  __shared__ uint32_t xs2[4 * S / 2];  // [row][S/2] FP16 pairs
+  __shared__ uint16_t val[4 * S];      // [row][S]
+  const B3Prep p = preps[blockIdx.y];
+  const int t = threadIdx.x;
+  if (p.zero && blockIdx.x == 0)
+    for (int i = t; i < p.nzero; i += 256) p.zero[i] = 0u;
+  const int p0 = (int)blockIdx.x * S;
+  if (p0 >= p.k) return;
+  const int m = p.m;
+  // positions of the span inside x: all of them for a rotated product (k is
+  // a multiple of B and of G); an unrotated one may end inside the span
+  const int len = min(S, p.k - p0);
+  for (int e = t; e < m * (S / 8); e += 256) {
+    const int r = e / (S / 8), j = e % (S / 8);
+    if (8 * j >= len) continue;
+    const u4_t v = *reinterpret_cast<const u4_t*>(p.x + (size_t)r * p.k + p0 + 8 * j);
+    uint32_t* d = xs2 + r * (S / 2) + 4 * j;
+    d[0] = v.x;
+    d[1] = v.y;
+    d[2] = v.z;
+    d[3] = v.w;
+  }
+  if (p.R) {
+    // the span's rows of R are contiguous: S rows of B / 8 chunks
+    const u4_t* rg = reinterpret_cast<const u4_t*>(p.R + (size_t)p0 * B);
+    u4_t v[NC];
+#pragma unroll
+    for (int u = 0; u < NC; ++u) v[u] = rg[t + 256 * u];
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const int c = t + 256 * u, row = c / (B / 8), q = c % (B / 8);
+      uint32_t* d = rs + row * P + 4 * q;
+      d[0] = v[u].x;
+      d[1] = v[u].y;
+      d[2] = v[u].z;
+      d[3] = v[u].w;
+    }
+  }
+  __syncthreads();
+  for (int e = t; e < m * S; e += 256) {
+    const int r = e / S, i = e % S;
+    if (i >= len) continue;
+    uint16_t h;
+    if (p.R) {
+      const uint32_t* ri = rs + i * P;
+      const uint32_t* xb = xs2 + r * (S / 2) + (i / B) * (B / 2);
+      float acc = 0.f;
+#pragma unroll 16
+      for (int j = 0; j < B / 2; ++j) acc = dot2(ri[j], xb[j], acc);
+      h = __builtin_bit_cast(uint16_t, (_Float16)acc);
+      p.xr[(size_t)r * p.k + p0 + i] = h;
+    } else {
+      h = reinterpret_cast<const uint16_t*>(xs2)[r * S + i];
+    }
+    val[r * S + i] = h;
+  }
+  __syncthreads();
+  const int ng = p.k / G, g0 = p0 / G;
+  constexpr int CS = (S / G) * Gm::CPG;  // chunks of the span per activation row
+  for (int e = t; e < m * CS; e += 256) {
+    const int r = e / CS, c = e % CS, gl = c / Gm::CPG, cc = c % Gm::CPG;
+    if (g0 + gl >= ng) continue;
+    uint32_t h[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pos = x5_pos<G>(cc, q);
+      h[q] = pos < 0 ? 0u : val[r * S + gl * G + pos];
+    }
+    *reinterpret_cast<u2_t*>(p.x5 + ((size_t)(r * ng + g0 + gl) * Gm::CPG + cc) * 4) =
+        u2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  }
 }
 
 // 16 bytes per lane from a buffer straight into LDS: lane l writes dst + 16 l
@@ -923,6 +993,18 @@ hipError_t launch_b3_prep(int group, const B3Prep* preps, int count, const B3Pre
   const dim3 grid((unsigned)((chunks + 255) / 256), (unsigned)rows);
   if (group == 64) hipLaunchKernelGGL(b3_prep_kernel<64>, grid, dim3(256), 0, s, preps, one);
   else if (group == 128) hipLaunchKernelGGL(b3_prep_kernel<128>, grid, dim3(256), 0, s, preps, one);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_b3_prep_rot(int group, int block, const B3Prep* preps, int count, int max_k, hipStream_t s) {
+  if (count <= 0 || max_k <= 0) return hipSuccess;
+  const int span = std::max(group, block);
+  const dim3 grid((unsigned)((max_k + span - 1) / span), (unsigned)count);
+  if (group == 128 && block == 128) hipLaunchKernelGGL((b3_prep_rot_kernel<128, 128>), grid, dim3(256), 0, s, preps);
+  else if (group == 128 && block == 64) hipLaunchKernelGGL((b3_prep_rot_kernel<128, 64>), grid, dim3(256), 0, s, preps);
+  else if (group == 64 && block == 128) hipLaunchKernelGGL((b3_prep_rot_kernel<64, 128>), grid, dim3(256), 0, s, preps);
+  else if (group == 64 && block == 64) hipLaunchKernelGGL((b3_prep_rot_kernel<64, 64>), grid, dim3(256), 0, s, preps);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

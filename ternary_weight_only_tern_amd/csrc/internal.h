@@ -163,9 +163,10 @@ struct B3Prep {
   int32_t k, m;
   uint32_t* zero;  // if not NULL: nzero words cleared (counters of the passes that follow)
   int32_t nzero;
-  // if R is not NULL: the activations are rotated first, blockdiag(R) x with
-  // R fp16 [k/rblock][rblock][rblock] (FP32 sums, FP16 values), x5 holds the
-  // rotated values and xr [m][k] a copy of them in position order
+  // rotated plans (launch_b3_prep_rot): if R is not NULL, the activations
+  // are rotated first, blockdiag(R) x with R fp16 [k/rblock][rblock][rblock]
+  // (FP32 sums, FP16 values); x5 holds the rotated values and xr [m][k] a
+  // copy of them in position order
   const uint16_t* R;
   uint16_t* xr;
   int32_t rblock;
@@ -200,6 +201,10 @@ hipError_t launch_b3_res(int group, int mt, const GemvDesc* descs, const B3ResIt
 // preps (device) holds count preparations; with preps == NULL, `one` alone;
 // max_k: the longest k among them.
 hipError_t launch_b3_prep(int group, const B3Prep* preps, int count, const B3Prep& one, int max_k, hipStream_t stream);
+// The preparation of a rotated plan's count products (device table; block =
+// the plan's rotation block, 64 or 128): rotates the products with R, copies
+// the others, and clears every zero list; one launch.
+hipError_t launch_b3_prep_rot(int group, int block, const B3Prep* preps, int count, int max_k, hipStream_t stream);
 // nwg workgroups.  With descs (device), the items table and the queues
 // (kB3Queues * kB3QueueWords device words; the launch leaves the counters
 // zero) drive the wavefronts; with descs == NULL every wavefront w takes

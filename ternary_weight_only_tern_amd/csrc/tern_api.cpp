@@ -1710,6 +1710,7 @@ static tern_status b3_plan_create(const tern_matrix* w, const uint16_t* const* x
   p->queue = reinterpret_cast<uint32_t*>(base + b.queue_off);
   p->nwg = b.nwg;
   p->prep_first = b.prep_first;
+  p->rot_block = rot_block;
   *out = p;
   return TERN_OK;
 }
@@ -1872,7 +1873,10 @@ static tern_status plan_launch(const tern_plan* plan, hipStream_t s, hipEvent_t 
     std::memset(&dummy, 0, sizeof(dummy));
     if (plan->nres == 0 || plan->prep_first) {
       // rotating preparations write what the residual pass reads: a launch of their own
-      TERN_HIP(tern::launch_b3_prep(plan->group, plan->preps, plan->nprep, none, plan->b3_maxk, s));
+      if (plan->prep_first)
+        TERN_HIP(tern::launch_b3_prep_rot(plan->group, plan->rot_block, plan->preps, plan->nprep, plan->b3_maxk, s));
+      else
+        TERN_HIP(tern::launch_b3_prep(plan->group, plan->preps, plan->nprep, none, plan->b3_maxk, s));
       TERN_HIP(tern::launch_b3_res(plan->group, plan->mt, plan->dev, plan->b3res, plan->nres, dummy, plan->b3_maxk,
                                    b3_res_lds_cap(plan->nres), nullptr, 0, 0, s));
     } else {  // the preparations ride along in the residual pass's launch

@@ -176,6 +176,37 @@ def test_rotated_plan_matches_oracle(fmt, m, route, block):
         check_y(ys[i], y_ref, b, f"rotated plan product {i}")
 
 
+@pytest.mark.parametrize("m", [1, 3])
+def test_rotated_stream_plan_group64_block128(m):
+    """Base-3 stream route at group 64 with 128 x 128 rotation blocks: the
+    preparation works in spans of 128 positions, so an unrotated product with
+    k = 960 (7.5 spans) ends inside its last span; two rotated products (k =
+    1024 and 1536) and the unrotated one, against the oracle as above."""
+    import torch
+    from gpu_util import b3_route, small_matrix, upload_pack
+    say("rotated stream plan, group 64, block 128, m =", m)
+    rng = np.random.default_rng(90 + m)
+    mats = [small_matrix(130, 1024, 64, 2, 0.2, seed=91, offset_mode=O.OFF_GROUP)[0],
+            small_matrix(100, 960, 64, 1, 0.0, seed=92, offset_mode=O.OFF_ROW)[0],
+            small_matrix(70, 1536, 64, 3, 0.1, seed=93)[0]]
+    xs_h = [synth.draw_x(rng, m, mt["k"], "student_t3") for mt in mats]
+    rots_h = [synth.draw_rotation(rng, 1024 // 128, 128), None, synth.draw_rotation(rng, 1536 // 128, 128)]
+    with b3_route("stream"):
+        pms = [upload_pack(mt, O.FMT_B3) for mt in mats]
+        xs = [_dev16(x) for x in xs_h]
+        rots = [None if R is None else _dev16(R) for R in rots_h]
+        ys = [torch.empty((m, mt["n"]), dtype=torch.float32, device="cuda") for mt in mats]
+        plan = L.Plan(pms, xs, ys, y_dtype=L.TERN_F32, rots=rots, rot_block=128)
+        plan.run()
+        torch.cuda.synchronize()
+        first = [y.clone() for y in ys]
+        plan.run()
+        torch.cuda.synchronize()
+    for y, f in zip(ys, first):
+        assert torch.equal(y, f), "runs differ"
+    _check_rotated(ys, mats, xs_h, rots_h, "rotated stream plan")
+
+
 def test_rotated_plan_rejects_mixed_rotations():
     """Products that read one x with different rotations are refused."""
     import torch
