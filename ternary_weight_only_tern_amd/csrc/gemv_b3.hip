@@ -121,15 +121,12 @@ __device__ __forceinline__ int x5_pos(int c, int h) {
   return pos >= 0 && pos < G ? pos : -1;
 }
 
-// x5 chunks and, when asked for, FP32 group sums of one activation row of
-// one product: blockIdx.y = product * 4 + activation row, blockIdx.x = a
-// block of 256 chunks (one per thread; group sums by the threads of block 0,
-// one group each, in position order).
+// x5 chunks and, when asked for, FP32 group sums of activation row m of the
+// product p: bx = a block of 256 chunks (one per thread; group sums by the
+// threads of block 0, one group each, in position order).
 template <int G>
-__device__ __forceinline__ void b3_prep_block(const B3Prep* __restrict__ preps, const B3Prep& one, int bx, int by) {
+__device__ __forceinline__ void b3_prep_rows(const B3Prep& p, int bx, int m) {
   using Gm = B3Geo<G>;
-  const B3Prep p = preps ? preps[by / 4] : one;
-  const int m = by % 4;
   if (p.zero && bx == 0 && m == 0)
     for (int i = threadIdx.x; i < p.nzero; i += 256) p.zero[i] = 0u;
   if (m >= p.m) return;
@@ -165,9 +162,17 @@ __device__ __forceinline__ void b3_prep_block(const B3Prep* __restrict__ preps, 
   }
 }
 
+// (each caller passes a struct it has loaded: choosing between a table
+// entry and another struct at run time would copy them to scratch memory)
 template <int G>
 __global__ __launch_bounds__(256) void b3_prep_kernel(const B3Prep* __restrict__ preps, B3Prep one) {
-  b3_prep_block<G>(preps, one, (int)blockIdx.x, (int)blockIdx.y);
+  const int by = (int)blockIdx.y;
+  if (preps) {
+    const B3Prep p = preps[by / 4];
+    b3_prep_rows<G>(p, (int)blockIdx.x, by % 4);
+  } else {
+    b3_prep_rows<G>(one, (int)blockIdx.x, by % 4);
+  }
 }
 
 // The preparation of a rotated plan: blockIdx.y = product, blockIdx.x = a
@@ -475,9 +480,9 @@ __global__ __launch_bounds__(kResThreads) void b3_res_kernel(const GemvDesc* __r
     // workgroups past the units prepare the activation layouts of the
     // product launch that follows (one launch less)
     if ((int)blockIdx.x >= nunits) {
-      const int pb = (int)blockIdx.x - nunits;
-      B3Prep none{};
-      b3_prep_block<G>(preps, none, pb % prep_bx, pb / prep_bx);
+      const int pb = (int)blockIdx.x - nunits, by = pb / prep_bx;
+      const B3Prep p = preps[by / 4];
+      b3_prep_rows<G>(p, pb % prep_bx, by % 4);
       return;
     }
   }
