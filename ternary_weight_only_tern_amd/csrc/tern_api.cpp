@@ -676,7 +676,10 @@ static void batch_splits(const tern_matrix* w, int count, int m, int mp, std::ve
   }
   // (measured: half as many lane-per-row items as a lone product's split
   // rule aims for finishes the small base-3 batches 2-3 % sooner)
-  const long target = mf ? 3L * tern_cu_count() : kTargetItems / 2;
+#ifndef TERN_MFMA_TARGET  // workgroups per CU that a small matrix-core decode batch is cut to fill
+#define TERN_MFMA_TARGET 3
+#endif
+  const long target = mf ? (long)TERN_MFMA_TARGET * tern_cu_count() : kTargetItems / 2;
   if (items == 0 || items >= target) return;
   const int f = (int)((target + items - 1) / items);
   for (int i = 0; i < count; ++i) {
