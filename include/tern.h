@@ -160,11 +160,13 @@ tern_status tern_unpack(const tern_matrix *src, int8_t *trits, void *ws, size_t 
  * residual pass when the product holds at least tern_b3_min_stages stages,
  * the lane-per-row decode below that; K parts, when the product is too
  * small to fill the GPU, are summed by a second kernel); from there to
- * m = 32 the 16-row matrix-core product
- * of tern_gemv_batched, which copies its work tables from host memory into
- * ws (hipMemcpyAsync on stream) on each call, so such calls must not be
- * captured into a HIP graph (use a plan); from m = 33 the tiles of
- * tern_gemm. */
+ * m = 32 the 16-row matrix-core product, whose tile table and reduce table
+ * a small kernel writes into ws from a description passed by value; from
+ * m = 33 the tiles of tern_gemm.  No route takes a table from host memory
+ * (the one exception: a base-3 product large enough for the stream kernel,
+ * whose item lists are copied from host memory like tern_gemv_batched's),
+ * so a call can be captured into a HIP graph and replayed while x changes,
+ * as long as ws stays the call's own. */
 tern_status tern_gemv(const tern_matrix *w, const uint16_t *x, int32_t m, void *y,
                       int32_t y_dtype, void *ws, size_t ws_bytes, void *stream);
 
@@ -178,8 +180,7 @@ tern_status tern_gemv(const tern_matrix *w, const uint16_t *x, int32_t m, void *
  * m <= 63 product of the Qwen3-4B and -8B shapes.  Every call on a GPU uses
  * that GPU's one array: calls that overlap in time on one GPU (other
  * streams, other host threads) race and must be ordered by the caller.  The
- * remaining rules are tern_gemv's (up to m = 32 it copies work tables from
- * host memory, so those calls are not for graph capture). */
+ * remaining rules are tern_gemv's, graph capture included. */
 #define TERN_NOALLOC_WORKSPACE_BYTES ((size_t)16 << 20)
 tern_status tern_gemv_noalloc(const tern_matrix *w, const uint16_t *x, int32_t m, void *y,
                               int32_t y_dtype, void *stream);

@@ -857,6 +857,29 @@ hipError_t launch_gemm_small(const GemvDesc* descs, int count, int format, int g
   return hipGetLastError();
 }
 
+// One thread per tile (plus the reduce entries): the table that a batch
+// would copy from host memory, written on the device from SmallSpec.
+__global__ void small_tiles_kernel(SmallSpec sp, GemvDesc* __restrict__ tiles, RedDesc* __restrict__ red) {
+  const int t = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  const int per_chunk = sp.nsplit * sp.ntn;
+  if (t < sp.nred) red[t] = t == 0 ? sp.red[0] : sp.red[1];
+  if (t >= sp.nchunk * per_chunk) return;
+  const int c = t / per_chunk, r = t % per_chunk, split = r / sp.ntn;
+  GemvDesc d = c == 0 ? sp.base[0] : sp.base[1];
+  d.tn0 = (r % sp.ntn) * 128;
+  d.tm0 = sp.rg[split];
+  d.splits = sp.rg[split + 1];
+  d.gps = sp.nsplit > 1 ? split : -1;
+  tiles[t] = d;
+}
+
+hipError_t launch_small_tiles(const SmallSpec& sp, GemvDesc* tiles, RedDesc* red, hipStream_t s) {
+  const int n = std::max(sp.nchunk * sp.nsplit * sp.ntn, sp.nred);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(small_tiles_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, sp, tiles, red);
+  return hipGetLastError();
+}
+
 hipError_t launch_reduce_grouped(const RedDesc* rd, int count, int blocks, hipStream_t s) {
   if (count <= 0 || blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(reduce_grouped_kernel, dim3(blocks), dim3(256), 0, s, rd, count);

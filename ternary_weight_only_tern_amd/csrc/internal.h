@@ -248,6 +248,21 @@ struct RedDesc {
 };
 hipError_t launch_reduce_grouped(const RedDesc* rd, int count, int blocks, hipStream_t stream);
 
+// One product's 16-row matrix-core tiles described compactly, for the tiles
+// and reduce table to be written on the device (tern_gemv: no table comes
+// from host memory, so the call can be captured).  Tile t is chunk t /
+// (nsplit * ntn), split (t / ntn) % nsplit, columns 128 * (t % ntn): the
+// chunk's base descriptor with tn0, tm0 = rg[split], splits = rg[split + 1]
+// and gps = split (or -1 with one split).
+constexpr int kSmallMaxRanges = 64;
+struct SmallSpec {
+  GemvDesc base[2];                   // per 16-row activation chunk
+  RedDesc red[2];                     // the chunks' reduce entries (nsplit > 1)
+  int32_t nchunk, nsplit, ntn, nred;
+  int32_t rg[kSmallMaxRanges + 1];    // step ranges of the splits
+};
+hipError_t launch_small_tiles(const SmallSpec& spec, GemvDesc* tiles, RedDesc* red, hipStream_t stream);
+
 // ---- quantizer front-end (quant.hip)
 // w fp16 [n][k] -> trits int8 [2][n][k], scales fp16 [2][n][k/group],
 // offsets fp16 [n][k/group]; mask: u32 bitmap [n][mwords] of the groups that

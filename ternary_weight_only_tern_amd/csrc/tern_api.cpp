@@ -295,6 +295,10 @@ static bool b3_route_n(const tern_matrix* w, int count, int m);
 
 // Workspace of a small-m product batch (defined with the batch builder).
 static size_t small_batch_ws_bytes(const tern_matrix* w, int32_t count, int32_t m);
+// One small-m product whose tile table is written on the device (defined
+// with the batch builder).
+static tern_status small_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* y, int32_t y_dtype,
+                              void* ws, size_t ws_bytes, hipStream_t s);
 // Single base-3 product at m <= 4 (defined with the base-3 batch builder).
 static void b3_single_layout(const tern_matrix* w, int m, int* parts, int* sps, int* rsplit, size_t* x5_off,
                              size_t* xs_off, size_t* rp_off, size_t* rc_off, size_t* total);
@@ -437,10 +441,7 @@ tern_status tern_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* 
     TERN_HIP(tern::launch_gemm(d, w->format, s));  // k == 0: zero fill
     return TERN_OK;
   }
-  if (small_route(w->format, w->group, m)) {
-    void* yp = y;
-    return tern_gemv_batched(w, &x, &yp, 1, m, y_dtype, ws, ws_bytes, stream);
-  }
+  if (small_route(w->format, w->group, m)) return small_gemv(w, x, m, y, y_dtype, ws, ws_bytes, s);
   if (b3_route_n(w, 1, m)) return b3_gemv(w, x, m, y, y_dtype, ws, ws_bytes, s);
   const int cmax = max_mt(w->format, w->group);
   int splits, gps;
@@ -1109,6 +1110,57 @@ static tern_status build_small_batch(const tern_matrix* w, const uint16_t* const
 
 static size_t tile_ws_bytes(const TileBatch& b) {
   return round_up(b.tiles.size() * sizeof(GemvDesc), 256) + b.partial_bytes + b.red.size() * sizeof(tern::RedDesc);
+}
+
+// The same batch for one product, with the tiles and the reduce table
+// written by a kernel from a compact description (launch_small_tiles), so
+// that no table comes from host memory; a product with more K ranges than
+// the description holds goes through tern_gemv_batched.
+static tern_status small_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, void* y, int32_t y_dtype,
+                              void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!ws) return fail(TERN_E_WORKSPACE, "tern_gemv needs a workspace at m=%d", m);
+  TERN_TRY(check_dev(ws, true, "ws"));
+  TileBatch b;
+  TERN_TRY(build_small_batch(w, &x, &y, 1, m, y_dtype, static_cast<char*>(ws), &b));
+  if (b.tiles.empty()) return TERN_OK;
+  const size_t need = tile_ws_bytes(b);
+  if (ws_bytes < need) return fail(TERN_E_WORKSPACE, "tern_gemv needs %zu workspace bytes", need);
+  tern::SmallSpec sp;
+  std::memset(&sp, 0, sizeof(sp));
+  sp.nchunk = (m + 15) / 16;
+  sp.ntn = (w->n + 127) / 128;
+  sp.nsplit = (int)(b.tiles.size() / ((size_t)sp.nchunk * sp.ntn));
+  bool fits = sp.nchunk <= 2 && b.red.size() <= 2 && sp.nsplit >= 1 && sp.nsplit <= tern::kSmallMaxRanges &&
+              b.tiles.size() == (size_t)sp.nchunk * sp.nsplit * sp.ntn;
+  if (fits) {
+    for (int c = 0; c < sp.nchunk; ++c) sp.base[c] = b.tiles[(size_t)c * sp.nsplit * sp.ntn];
+    for (int k = 0; k < sp.nsplit; ++k) {
+      sp.rg[k] = b.tiles[(size_t)k * sp.ntn].tm0;
+      sp.rg[k + 1] = b.tiles[(size_t)k * sp.ntn].splits;
+    }
+    sp.nred = (int)b.red.size();
+    for (int r = 0; r < sp.nred; ++r) sp.red[r] = b.red[r];
+    // the description reproduces the builder's table exactly
+    for (size_t t = 0; t < b.tiles.size() && fits; ++t) {
+      const int per = sp.nsplit * sp.ntn, c = (int)t / per, r = (int)t % per, k = r / sp.ntn;
+      const GemvDesc& d = b.tiles[t];
+      fits = d.tn0 == (r % sp.ntn) * 128 && d.tm0 == sp.rg[k] && d.splits == sp.rg[k + 1] &&
+             d.gps == (sp.nsplit > 1 ? k : -1) && d.x == sp.base[c].x && d.y == sp.base[c].y &&
+             d.partial == sp.base[c].partial && d.m == sp.base[c].m;
+    }
+  }
+  if (!fits) {
+    void* yp = y;
+    return tern_gemv_batched(w, &x, &yp, 1, m, y_dtype, ws, ws_bytes, s);
+  }
+  char* base = static_cast<char*>(ws);
+  const size_t tb = round_up(b.tiles.size() * sizeof(GemvDesc), 256);
+  tern::RedDesc* red = reinterpret_cast<tern::RedDesc*>(base + tb + b.partial_bytes);
+  TERN_HIP(tern::launch_small_tiles(sp, reinterpret_cast<GemvDesc*>(base), red, s));
+  TERN_HIP(tern::launch_gemm_small(reinterpret_cast<const GemvDesc*>(base), (int)b.tiles.size(), w->format, w->group,
+                                   b.np, b.offs, s));
+  if (!b.red.empty()) TERN_HIP(tern::launch_reduce_grouped(red, (int)b.red.size(), b.red_blocks, s));
+  return TERN_OK;
 }
 
 // Workspace of a small-m batch: the layout build_small_batch makes, from the
