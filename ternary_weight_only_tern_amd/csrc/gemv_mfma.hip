@@ -490,8 +490,11 @@ __device__ __forceinline__ void mfma_body(const GemvDesc* __restrict__ descs, co
   // whole row: the workgroup's entries [e0, e1) (its rows are contiguous) are
   // staged in LDS with the other small operands -- their blocks as raw
   // 16-byte chunks and their index words (group | scale bits << 16)
+  // (or, with an index per K part, the item's entries of every residual
+  // plane in its K part)
+  const bool part_idx = (RBLK > 0 || ndesc > 0) && d.pidx != nullptr;
   uint32_t e0 = 0, e1 = 0;
-  if (ndesc > 0 && d.gidx[0] != nullptr && sflat && d.planes == 2) {
+  if ((RBLK > 0 || ndesc > 0) && (part_idx || (d.gidx[0] != nullptr && sflat && d.planes == 2))) {
     const int nt = rw / kRowsWave;
     e0 = te[0];
     e1 = nt == 1 ? te[1] : nt == 2 ? te[2] : te[4];
@@ -499,15 +502,16 @@ __device__ __forceinline__ void mfma_body(const GemvDesc* __restrict__ descs, co
   const bool res_idx = e1 > e0 && e1 - e0 <= (uint32_t)kResStage;
   const uint32_t nres = res_idx ? e1 - e0 : 0u;
   constexpr int kBQ = G / 4 / 16;                          // 16-byte chunks per block
-  const GLOBAL uint32_t* gix = gp(d.gidx[0]);
+  const GLOBAL uint32_t* gix = gp(part_idx ? d.pidx : d.gidx[0]);
   const uintptr_t gfirst = (uintptr_t)(gix + e0), ga0 = gfirst & ~(uintptr_t)15;
   const int gshift = (int)(gfirst - ga0) / 4;
   const int nbch = (int)nres * kBQ;                        // block chunks
   const int ngch = res_idx ? (int)(((uintptr_t)(gix + e1) - ga0 + 15) / 16) : 0;  // index chunks
   if (res_idx) {
     // the index array sits in a 256-byte-rounded allocation of 16-byte aligned start
-    const __amdgpu_buffer_rsrc_t rb = rsrc(d.blocks[0], d.nnz[0] * (uint32_t)(G / 4));
-    const __amdgpu_buffer_rsrc_t rg = rsrc(d.gidx[0], (d.nnz[0] * 4u + 15u) & ~15u);
+    const uint32_t nnz_ = part_idx ? d.pnnz : d.nnz[0];
+    const __amdgpu_buffer_rsrc_t rb = rsrc(part_idx ? d.pblocks : d.blocks[0], nnz_ * (uint32_t)(G / 4));
+    const __amdgpu_buffer_rsrc_t rg = rsrc(part_idx ? d.pidx : d.gidx[0], (nnz_ * 4u + 15u) & ~15u);
     for (int u = 0; u * kThreads < nbch; ++u)
       if (u * kThreads + tid < nbch)
         lds_load16(rb, lds + rstoff + (u * kThreads + wave * kWave) * 16, (e0 * kBQ + u * kThreads + tid) * 16u);
@@ -520,8 +524,9 @@ __device__ __forceinline__ void mfma_body(const GemvDesc* __restrict__ descs, co
   // this row's entries, for the sums
   uint32_t rp0 = 0, rp1 = 0;
   if (res_idx) {
-    rp0 = gp(d.rowptr[0])[rowc];
-    rp1 = gp(d.rowptr[0])[rowc + 1];
+    const GLOBAL uint32_t* rp_ = part_idx ? gp(d.prowptr) + (size_t)split * d.n : gp(d.rowptr[0]);
+    rp0 = rp_[rowc];
+    rp1 = rp_[rowc + 1];
   }
 
   // this wavefront's share of the staged entries (relative to e0): those of
@@ -687,7 +692,7 @@ __device__ __forceinline__ void mfma_body(const GemvDesc* __restrict__ descs, co
     const GLOBAL uint8_t* blocks = gp(p == 0 ? d.blocks[0] : d.blocks[1]);
     const GLOBAL uint16_t* rscale = gp(p == 0 ? d.rscale[0] : d.rscale[1]);
     const uint32_t w_begin = 0;
-    if (p == 0 && res_idx) continue;  // done before plane 0
+    if (res_idx && (p == 0 || part_idx)) continue;  // staged: done with plane 0
     // general path: list from the mask in global memory, window by window
     const int wlo = pga >> 5, whi = (pgb - 1) >> 5;
     const GLOBAL uint32_t* mrow = gp(p == 0 ? d.mask[0] : d.mask[1]) + (size_t)rowc * d.mwords;
@@ -934,8 +939,74 @@ __global__ void tile_bounds_kernel(const GemvDesc* ranges, WgRec* recs, int coun
   const GemvDesc* d = ranges + (rec->ri >> 20);
   const int item = (int)(rec->ri & 0xFFFFFu);
   const int row0 = d->row_base + (item % d->row_blocks) * kRowsWave * (kWaves / d->kwaves);
+  if (d->pidx) {  // the item's K part in the index per K part
+    const uint32_t* base = d->prowptr + (size_t)(item / d->row_blocks) * d->n;
+    for (int t = 0; t < 5; ++t) rec->te[t] = base[min(row0 + kRowsWave * t, d->n)];
+    return;
+  }
   if (!d->gidx[0]) return;
   for (int t = 0; t < 5; ++t) rec->te[t] = d->rowptr[0][min(row0 + kRowsWave * t, d->n)];
+}
+
+// Index per K part: one thread per (part, row).  Residual planes are at
+// most two; their masks, row pointers, blocks and scales come by value.
+struct PartPlanes {
+  const uint32_t* mask[2];
+  const uint32_t* rowptr[2];
+  const uint8_t* blocks[2];
+  const uint16_t* rscale[2];
+};
+
+// The entries of (part s, row r) over planes p < nres, in plane then group
+// order: group g of the part's range [ga, gb) with its mask bit set.
+__device__ __forceinline__ uint32_t part_row_count(const PartPlanes& pp, int p, int r, int mwords, int ga, int gb) {
+  const uint32_t* mrow = (p == 0 ? pp.mask[0] : pp.mask[1]) + (size_t)r * mwords;
+  uint32_t c = 0;
+  for (int w = ga >> 5; w <= (gb - 1) >> 5; ++w) c += __popc(mrow[w] & range_bits(ga - (w << 5), gb - (w << 5)));
+  return c;
+}
+
+__global__ void part_count_kernel(PartPlanes pp, int nres, int n, int ng, int mwords, int parts, int gps,
+                                  uint32_t* __restrict__ prowptr) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i == 0) prowptr[0] = 0u;
+  if (i >= parts * n) return;
+  const int s = i / n, r = i % n, ga = s * gps, gb = min(ng, ga + gps);
+  uint32_t c = 0;
+  for (int p = 0; p < nres; ++p) c += part_row_count(pp, p, r, mwords, ga, gb);
+  prowptr[1 + i] = c;  // scanned in place next
+}
+
+template <int G>
+__global__ void part_fill_kernel(PartPlanes pp, int nres, int n, int ng, int mwords, int gps,
+                                 const uint32_t* __restrict__ prowptr, int parts, uint8_t* __restrict__ pblocks,
+                                 uint32_t* __restrict__ pidx) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i >= parts * n) return;
+  const int s = i / n, r = i % n, ga = s * gps, gb = min(ng, ga + gps);
+  uint32_t e = prowptr[i];
+  for (int p = 0; p < nres; ++p) {
+    const uint32_t* mrow = (p == 0 ? pp.mask[0] : pp.mask[1]) + (size_t)r * mwords;
+    const uint8_t* blocks = p == 0 ? pp.blocks[0] : pp.blocks[1];
+    const uint16_t* rscale = p == 0 ? pp.rscale[0] : pp.rscale[1];
+    // the row's entry number of group g: its row pointer plus the set bits before g
+    uint32_t eo = (p == 0 ? pp.rowptr[0] : pp.rowptr[1])[r];
+    for (int w = 0; w < (ga >> 5); ++w) eo += __popc(mrow[w]);
+    if (ga & 31) eo += __popc(mrow[ga >> 5] & ((1u << (ga & 31)) - 1u));
+    for (int w = ga >> 5; w <= (gb - 1) >> 5; ++w) {
+      uint32_t bits = mrow[w] & range_bits(ga - (w << 5), gb - (w << 5));
+      while (bits) {
+        const int g = (w << 5) + __builtin_ctz(bits);
+        bits &= bits - 1u;
+        const uint4* src = reinterpret_cast<const uint4*>(blocks + (size_t)eo * (G / 4));
+        uint4* dst = reinterpret_cast<uint4*>(pblocks + (size_t)e * (G / 4));
+        for (int c = 0; c < G / 64; ++c) dst[c] = src[c];
+        pidx[e] = (uint32_t)(g - ga) | ((uint32_t)rscale[eo] << 16);
+        ++eo;
+        ++e;
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -945,6 +1016,36 @@ hipError_t launch_res_index(const uint32_t* mask, const uint32_t* rowptr, const 
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(res_index_kernel, dim3((n + 255) / 256), dim3(256), 0, s, mask, rowptr, rscale, n, mwords,
                      gidx);
+  return hipGetLastError();
+}
+
+hipError_t launch_part_index(const uint32_t* const* mask, const uint32_t* const* rowptr, const uint8_t* const* blocks,
+                             const uint16_t* const* rscale, int nres, int n, int ng, int mwords, int group, int parts,
+                             int gps, uint32_t* prowptr, uint8_t* pblocks, uint32_t* pidx, hipStream_t s) {
+  if (n <= 0 || parts <= 0 || nres < 1 || nres > 2 || gps <= 0) return hipErrorInvalidValue;
+  PartPlanes pp;
+  for (int p = 0; p < 2; ++p) {
+    const int q = p < nres ? p : 0;
+    pp.mask[p] = mask[q];
+    pp.rowptr[p] = rowptr[q];
+    pp.blocks[p] = blocks[q];
+    pp.rscale[p] = rscale[q];
+  }
+  const int total = parts * n;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  hipLaunchKernelGGL(part_count_kernel, grid, dim3(256), 0, s, pp, nres, n, ng, mwords, parts, gps, prowptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_rowptr_scan(prowptr, total, s);
+  if (e != hipSuccess) return e;
+  if (group == 128)
+    hipLaunchKernelGGL(part_fill_kernel<128>, grid, dim3(256), 0, s, pp, nres, n, ng, mwords, gps, prowptr, parts,
+                       pblocks, pidx);
+  else if (group == 64)
+    hipLaunchKernelGGL(part_fill_kernel<64>, grid, dim3(256), 0, s, pp, nres, n, ng, mwords, gps, prowptr, parts,
+                       pblocks, pidx);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -46,6 +46,17 @@ struct GemvDesc {
   // otherwise): per entry of the first residual plane, (group | FP16 scale
   // bits << 16); the entry ranges of the tiles are in the launch's records.
   const uint32_t* gidx[2];
+  // Residual index per K part prepared with a plan (matrix-core decode
+  // kernel, products cut into K parts or with two residual planes; NULL
+  // otherwise): the entries of every residual plane ordered by (K part,
+  // row, plane, group), with their blocks copied in that order (pblocks,
+  // group/4 bytes each) and (group relative to the part | FP16 scale bits
+  // << 16) in pidx; part s's row r starts at prowptr[s * n + r]
+  // (prowptr[splits * n] = pnnz, the total).
+  const uint32_t* pidx;
+  const uint8_t* pblocks;
+  const uint32_t* prowptr;
+  uint32_t pnnz;
   // Grouped matrix-core product: origin of this workgroup's output tile.
   int32_t tm0, tn0;
   // Matrix-core decode kernel: first row of this descriptor's row range
@@ -136,6 +147,12 @@ hipError_t launch_res_index(const uint32_t* mask, const uint32_t* rowptr, const 
 // residual index: te[t] = rowptr[0][min(row0 + 16 t, n)], t = 0..4, where
 // row0 is the item's first row.
 hipError_t launch_tile_bounds(const GemvDesc* ranges, WgRec* recs, int count, hipStream_t stream);
+// Residual index per K part of one product (see GemvDesc::pidx): nres
+// residual planes (1 or 2), K parts of gps groups.  Counts into prowptr,
+// scans it, then fills pblocks and pidx (three launches).
+hipError_t launch_part_index(const uint32_t* const* mask, const uint32_t* const* rowptr, const uint8_t* const* blocks,
+                             const uint16_t* const* rscale, int nres, int n, int ng, int mwords, int group, int parts,
+                             int gps, uint32_t* prowptr, uint8_t* pblocks, uint32_t* pidx, hipStream_t stream);
 
 // Plain streaming read of bytes (a multiple of 16) from buf (measurement).
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);

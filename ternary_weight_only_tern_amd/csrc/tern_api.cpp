@@ -1192,6 +1192,20 @@ static bool plan_indexes(const tern_matrix* w) {
   return use_mfma(w->format) && w->planes == 2 && w->nnz[0] > 0 && w->n > 0 && w->k > 0;
 }
 static size_t index_bytes(const tern_matrix* w) { return plan_indexes(w) ? round_up((size_t)w->nnz[0] * 4, 256) : 0; }
+// A plan also indexes per K part the residual planes of a matrix-core decode
+// product cut into K parts or with two residual planes (GemvDesc::pidx), so
+// that its items stage their entries as whole-row items do: the part row
+// pointers, then the entries' blocks and index words.
+static bool plan_part_indexes(const tern_matrix* w, int parts) {
+  return use_mfma(w->format) && w->n > 0 && w->k > 0 && w->planes >= 2 && (parts > 1 || w->planes == 3) &&
+         w->nnz[0] + (w->planes == 3 ? w->nnz[1] : 0u) > 0;
+}
+static size_t part_entries(const tern_matrix* w) { return (size_t)w->nnz[0] + (w->planes == 3 ? w->nnz[1] : 0u); }
+static size_t part_index_bytes(const tern_matrix* w, int parts) {
+  if (!plan_part_indexes(w, parts)) return 0;
+  const size_t e = part_entries(w);
+  return round_up(((size_t)parts * w->n + 1) * 4, 256) + round_up(e * (w->group / 4), 256) + round_up(e * 4, 256);
+}
 
 // ---- base-3 matrix-core decode batches (m <= 4)
 // Workspace layout: [descriptors][activation preparations][queue counters]
@@ -1615,7 +1629,7 @@ size_t tern_batch_workspace_bytes(const tern_matrix* w, int32_t count, int32_t m
   std::vector<int> bns, bgps, bkw;
   batch_splits(w, count, m, mtp, &bns, &bgps, &bkw);
   size_t idx = 0;
-  for (int i = 0; i < count; ++i) idx += index_bytes(&w[i]);
+  for (int i = 0; i < count; ++i) idx += index_bytes(&w[i]) + part_index_bytes(&w[i], bns[i]);
   const bool mf = use_mfma(w[0].format);
   // lane-per-row decode: one descriptor per work item, then the partials and
   // reduce table; matrix-core decode: two row ranges per (matrix, row
@@ -1869,27 +1883,68 @@ tern_status tern_plan_create(const tern_matrix* w, const uint16_t* const* x, voi
   tables = round_up(tables, 256);
   char* base = static_cast<char*>(ws);
   if (!items.empty()) {
-    std::vector<size_t> ioff(count, 0);
+    // K parts of each product (all of its descriptors share them)
+    std::vector<int> parts(count, 1), pgps(count, 0);
+    for (size_t t = 0; t < items.size(); ++t) {
+      parts[mat[t]] = items[t].splits;
+      pgps[mat[t]] = items[t].gps;
+    }
+    std::vector<size_t> ioff(count, 0), poff(count, 0);
     size_t need = tables;
     for (int i = 0; i < count; ++i) {
       ioff[i] = need;
       need += index_bytes(&w[i]);
+      poff[i] = need;
+      need += recs.empty() ? 0 : part_index_bytes(&w[i], parts[i]);
     }
     if (!ws || ws_bytes < need) return fail(TERN_E_WORKSPACE, "plan needs %zu workspace bytes", need);
     TERN_TRY(check_dev(ws, true, "ws"));
-    // the residual index serves the matrix-core decode launch (records)
+    // the residual indexes serve the matrix-core decode launch (records)
+    auto part_ptrs = [&](int i, uint32_t** prow, uint8_t** pblk, uint32_t** pix) {
+      char* q = base + poff[i];
+      *prow = reinterpret_cast<uint32_t*>(q);
+      q += round_up(((size_t)parts[i] * w[i].n + 1) * 4, 256);
+      *pblk = reinterpret_cast<uint8_t*>(q);
+      q += round_up(part_entries(&w[i]) * (w[i].group / 4), 256);
+      *pix = reinterpret_cast<uint32_t*>(q);
+    };
     if (!recs.empty())
-      for (size_t t = 0; t < items.size(); ++t)
-        if (plan_indexes(&w[mat[t]])) items[t].gidx[0] = reinterpret_cast<const uint32_t*>(base + ioff[mat[t]]);
+      for (size_t t = 0; t < items.size(); ++t) {
+        const int i = mat[t];
+        if (plan_part_indexes(&w[i], parts[i])) {
+          uint32_t *prow, *pix;
+          uint8_t* pblk;
+          part_ptrs(i, &prow, &pblk, &pix);
+          items[t].prowptr = prow;
+          items[t].pblocks = pblk;
+          items[t].pidx = pix;
+          items[t].pnnz = (uint32_t)part_entries(&w[i]);
+        } else if (plan_indexes(&w[i])) {
+          items[t].gidx[0] = reinterpret_cast<const uint32_t*>(base + ioff[i]);
+        }
+      }
     TERN_HIP(hipMemcpy(base, items.data(), items.size() * sizeof(GemvDesc), hipMemcpyHostToDevice));
     if (sp.nctr) TERN_HIP(hipMemset(base + sp.ctr_off, 0, sp.nctr * 4));
     if (!recs.empty()) {
       TERN_HIP(hipMemcpy(base + sp.recs_off, recs.data(), recs.size() * sizeof(tern::WgRec), hipMemcpyHostToDevice));
-      for (int i = 0; i < count; ++i)
-        if (plan_indexes(&w[i]))
+      for (int i = 0; i < count; ++i) {
+        if (plan_part_indexes(&w[i], parts[i])) {
+          uint32_t *prow, *pix;
+          uint8_t* pblk;
+          part_ptrs(i, &prow, &pblk, &pix);
+          const uint32_t* msk[2] = {w[i].mask[0], w[i].mask[1]};
+          const uint32_t* rpt[2] = {w[i].rowptr[0], w[i].rowptr[1]};
+          const uint8_t* blk[2] = {w[i].blocks[0], w[i].blocks[1]};
+          const uint16_t* rsc[2] = {w[i].rscale[0], w[i].rscale[1]};
+          TERN_HIP(tern::launch_part_index(msk, rpt, blk, rsc, w[i].planes - 1, w[i].n, w[i].k / w[i].group,
+                                           mask_words(w[i].k, w[i].group), w[i].group, parts[i], pgps[i], prow, pblk,
+                                           pix, nullptr));
+        } else if (plan_indexes(&w[i])) {
           TERN_HIP(tern::launch_res_index(w[i].mask[0], w[i].rowptr[0], w[i].rscale[0], w[i].n,
                                           mask_words(w[i].k, w[i].group),
                                           reinterpret_cast<uint32_t*>(base + ioff[i]), nullptr));
+        }
+      }
       TERN_HIP(tern::launch_tile_bounds(reinterpret_cast<const GemvDesc*>(base),
                                         reinterpret_cast<tern::WgRec*>(base + sp.recs_off), (int)recs.size(), nullptr));
     }
