@@ -242,10 +242,11 @@ tern_status tern_gemv_batched(const tern_matrix *w, const uint16_t *const *x, vo
  * The buffers named in the plan must stay valid while the plan is used, and
  * their contents must not change in ways the plan has read: the plan keeps
  * tables derived from the masks, row pointers and residual scales (the
- * residual index, the residual pass's entry ranges, tile entry bounds), so
- * after a matrix is packed again (or those arrays change) the plan must be
- * created again; plane-0 bytes, scales, offsets and x may change between
- * runs.  Runs of one plan (or of plans, or batched calls, that share a
+ * residual index, the residual pass's entry ranges, tile entry bounds) and,
+ * for 2-bit products cut into K parts or with two residual planes, a copy
+ * of the residual blocks in K-part order, so after a matrix is packed again
+ * (or those arrays change) the plan must be created again; plane-0 bytes,
+ * plane-0 scales, offsets and x may change between runs.  Runs of one plan (or of plans, or batched calls, that share a
  * workspace) use the same partials and counters, so runs that overlap in
  * time race: order them on one stream. */
 typedef struct tern_plan tern_plan;
