@@ -340,7 +340,22 @@ __global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __
   if (rz > ra) {
     if (d.planes > 1) residual_compact<G, MT>(d, 0, row, row_ok, ra, rz, xr, lds, WL, acc);
     if (d.planes > 2) residual_compact<G, MT>(d, 1, row, row_ok, ra, rz, xr, lds, WL, acc);
-    if (d.offset_mode != 0) {
+    if (d.offset_mode == 1) {
+      // one offset per row: it multiplies the sum of x over the whole
+      // range, so the range is summed at once (one cross-lane sum)
+      float xs[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        float v = 0.f;
+        for (int pi = ra * (G / 2) + lane; pi < rz * (G / 2); pi += kWave) v = dot2(xr[m][pi], 0x3C003C00u, v);
+        xs[m] = wave_sum(v);
+      }
+      if (row_ok) {
+        const float o = h2f(gp(d.offset)[row]);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m] = fmaf(o, xs[m], acc[m]);
+      }
+    } else if (d.offset_mode != 0) {
       const GLOBAL uint16_t* off = gp(d.offset);
       for (int g = ra; g < rz; ++g) {
         float xs[MT];
@@ -351,7 +366,7 @@ __global__ __launch_bounds__(kWave * kWaves) void gemv_kernel(const GemvDesc* __
           xs[m] = wave_sum(v);
         }
         if (row_ok) {
-          const float o = h2f(d.offset_mode == 1 ? off[row] : off[(size_t)row * d.ng + g]);
+          const float o = h2f(off[(size_t)row * d.ng + g]);
 #pragma unroll
           for (int m = 0; m < MT; ++m) acc[m] = fmaf(o, xs[m], acc[m]);
         }
