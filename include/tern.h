@@ -308,10 +308,12 @@ tern_status tern_plan_create_rotated(const tern_matrix *w, const uint16_t *const
  * ceil(k / (8 * 128)) per product at group 128, ceil(k / (16 * 64)) at group
  * 64) runs the persistent matrix-core stream kernel with a separate residual
  * pass; smaller launches run the lane-per-row decode, whose work items are
- * finer.  Default: four stages per wavefront of the stream kernel (7168 on
- * 256 CUs).  stages >= 0 sets the threshold (0: every such launch takes the
- * stream kernel), -1 restores the default, any other negative value only
- * queries.  Returns the threshold in effect before the call.  Process-wide;
+ * finer.  Default: four stages per wavefront of the stream kernel at m = 1
+ * (7168 on 256 CUs), four stages per CU at m = 2..4 (1024).  stages >= 0
+ * sets one threshold for every m (0: every such launch takes the stream
+ * kernel), -1 restores the defaults, any other negative value only queries.
+ * Returns the threshold in effect before the call (the m = 1 one while the
+ * defaults are in effect).  Process-wide;
  * workspace sizes and plans follow the threshold in effect when they are
  * computed or created.  Host-only. */
 int64_t tern_b3_min_stages(int64_t stages);

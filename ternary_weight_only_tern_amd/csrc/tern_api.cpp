@@ -1246,12 +1246,18 @@ static int b3_stages(const tern_matrix* w) {
   const int sg = tern::b3_stage_groups(w->group);
   return (w->k / w->group + sg - 1) / sg;
 }
-// Launches of fewer 64-row stages than this (default: four per wavefront of
-// the persistent launch) use the lane-per-row decode, whose work items are
-// finer; tern_b3_min_stages changes it.
+// Launches of fewer 64-row stages than this use the lane-per-row decode,
+// whose work items are finer; tern_b3_min_stages changes it.  Default
+// (measured on the MI355X): four per wavefront of the persistent launch at
+// m = 1; four per CU at m = 2..4, where the lane-per-row decode holds more
+// activation rows per lane (fewer wavefronts per SIMD) while the stream
+// kernel covers up to four rows in one pass (4B- and 8B-class layers at m =
+// 2..4: 7-30 % less time; single products of 256-768 stages stay faster
+// on the lane-per-row decode).
 static int64_t g_b3_min_stages = -1;
-static int64_t b3_min_stages() {
-  return g_b3_min_stages >= 0 ? g_b3_min_stages : 4L * tern_cu_count() * tern::kB3Waves;
+static int64_t b3_min_stages(int m = 1) {
+  if (g_b3_min_stages >= 0) return g_b3_min_stages;
+  return m >= 2 ? 4L * tern_cu_count() : 4L * tern_cu_count() * tern::kB3Waves;
 }
 static bool b3_route_n(const tern_matrix* w, int count, int m) {
   if (count <= 0 || !w || !b3_route(w[0].format, w[0].group, m)) return false;
@@ -1259,7 +1265,7 @@ static bool b3_route_n(const tern_matrix* w, int count, int m) {
   for (int i = 0; i < count; ++i)
     if (w[i].group == w[0].group && w[i].n > 0 && w[i].k > 0)
       stages += (int64_t)((w[i].n + tern::kGemvRows - 1) / tern::kGemvRows) * b3_stages(&w[i]);
-  return stages >= b3_min_stages();
+  return stages >= b3_min_stages(m);
 }
 // A product with residual planes or an offset goes through the residual pass.
 static bool b3_has_res(const tern_matrix* w) { return w->planes > 1 || w->offset_mode != TERN_OFF_NONE; }
