@@ -650,6 +650,9 @@ def main():
                     help="only the M=512 matrix-core layer (profiling); no JSON line")
     ap.add_argument("--layer4b-only", action="store_true",
                     help="only the 4B-class 2-bit layer at M=1 (profiling); no JSON line")
+    ap.add_argument("--layer4b-rotated-only", action="store_true",
+                    help="only the 4B-class 2-bit layer at M=1 with and without its inputs rotated inside the "
+                         "decode launch (profiling); no JSON line")
     ap.add_argument("--quantize-only", action="store_true",
                     help="only the quantizer on a 4B-class layer (profiling); no JSON line")
     ap.add_argument("--rotate-only", action="store_true",
@@ -698,6 +701,11 @@ def main():
     if args.layer4b_only:
         r = bench_layer4b(args, stream)
         log(f"bench: 4B-class layer {r['step_s']*1e6:.2f} us/step, {r['gbs']:.1f} GB/s")
+        return
+    if args.layer4b_rotated_only:
+        r4 = bench_layer4b_rotated(stream, steps=max(LAYERS, args.steps // LAYERS * LAYERS))
+        log(f"bench: 4B-class layer with rotations {r4['us_per_layer']:.2f} us (without "
+            f"{r4['us_per_layer_unrotated']:.2f}), {r4['launches']} launch(es) per layer")
         return
     if args.quantize_only:
         qz = bench_quantize(args, stream)
