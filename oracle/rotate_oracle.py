@@ -7,10 +7,10 @@ with the HIP library.
 What is computed, and where the pages define it
 ------------------------------------------------
 "Post-Training Ternarization of Qwen3-4B" (arXiv 2609.01962v1 summary) §4.2:
-KOTMS moves the weights into a ternary-friendly basis with structured
-orthogonal matrices, and inference applies the equivalent rotation to the
-activations before the quantized linear product; the rotation preserves norms
-in exact arithmetic.  The pages do not give the structure, so the reading
+the weights are quantized after an orthogonal change of basis, so at run
+time the activations are rotated by the matching transform before they meet
+the ternary product (an orthogonal map leaves norms unchanged in exact
+arithmetic).  The pages do not give the structure, so the reading
 here is the plainest one that fits: a block-diagonal R with B x B blocks
 (B = 64 or 128, aligned with the weight groups), given by the caller:
     xr[m, b*B + i] = sum_j R[b][i][j] * x[m, b*B + j].
