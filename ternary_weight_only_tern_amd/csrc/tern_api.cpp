@@ -834,12 +834,16 @@ struct TileBatch {
 // One descriptor per output tile (tile_rows x 128), matrices with the longest
 // K first so that their tiles start first, and within a matrix the weight
 // tile fastest.  np receives the most residual planes of any matrix.
-// Split of each product's K (64-trit steps) for a grouped launch: products
-// whose tiles are at least twice as long as the shortest ones are cut into
-// that many parts (multiples of 4 steps), when that shortens the launch's
-// makespan (largest tiles first onto the least-loaded of the resident slots)
-// by 15 % or more; the parts write FP32 partials that one grouped reduce sums
-// in part order.
+// Split of each product's K (64-trit steps) for a grouped launch.  Three
+// candidates: products whose tiles are at least twice as long as the
+// shortest ones cut into that many parts; every product cut into parts of
+// about 32 steps; and parts of about 16 steps (parts are multiples of 4 steps
+// and at least 8).  Each candidate is scored by its makespan (largest tiles
+// first onto the least-loaded of the resident slots, in steps) plus the time
+// of its FP32 partials (written by the tiles, read by the grouped reduce)
+// expressed in steps.  The best one is taken when it scores 15 % or more
+// below the uncut launch.  The parts write FP32 partials that one grouped
+// reduce sums in part order.
 static std::vector<int> split_ranges(int steps, int parts) {
   std::vector<int> b(parts + 1, 0);
   const int q4 = (steps + 3) / 4;
@@ -862,6 +866,13 @@ static long lpt_makespan(std::vector<long> len, int slots) {
   return span;
 }
 
+// Measured time of one 64-trit step of a tile with one workgroup per CU
+// (8B-class layer: 128-row tiles ~1.0 us, 256-row tiles ~1.7 us), and the
+// rate at which partial sums are written and read back (~4 TB/s): together
+// they turn a candidate's partial traffic into steps of launch time.
+static double gemm_step_us(int bm) { return bm >= 256 ? 1.7 : 1.0; }
+constexpr double kPartialBytesPerUs = 4.0e6;
+
 static std::vector<int> gemm_splits(const tern_matrix* w, int32_t count, int32_t m) {
   std::vector<int> parts(count, 1);
   const int bm = tern::gemm_tile_rows(m);
@@ -870,19 +881,45 @@ static std::vector<int> gemm_splits(const tern_matrix* w, int32_t count, int32_t
     if (w[i].n > 0 && w[i].k > 0) smin = std::min(smin, w[i].k / 64);
   if (smin == 1 << 30 || count == 0) return parts;
   const int slots = tern_cu_count() * tern::gemm_wgs_per_cu(w[0].format, bm / 64);
-  std::vector<long> plain, split;
-  std::vector<int> cand(count, 1);
+  // score of a split: makespan in steps plus the partial traffic in steps
+  auto score = [&](const std::vector<int>& cut) {
+    std::vector<long> len;
+    double bytes = 0;
+    for (int i = 0; i < count; ++i) {
+      if (w[i].n <= 0 || w[i].k <= 0) continue;
+      const long tiles = (long)((m + bm - 1) / bm) * ((w[i].n + 127) / 128);
+      const std::vector<int> r = split_ranges(w[i].k / 64, cut[i]);
+      for (int p = 0; p < cut[i]; ++p) len.insert(len.end(), tiles, r[p + 1] - r[p]);
+      if (cut[i] > 1) bytes += 2.0 * cut[i] * (double)m * w[i].n * 4;
+    }
+    return (double)lpt_makespan(len, slots) + bytes / kPartialBytesPerUs / gemm_step_us(bm);
+  };
+  // parts of about `len` steps each (at least 8 steps, at most 8 parts)
+  auto cut_to = [&](int len) {
+    std::vector<int> c(count, 1);
+    for (int i = 0; i < count; ++i) {
+      if (w[i].n <= 0 || w[i].k <= 0) continue;
+      const int st = w[i].k / 64;
+      c[i] = std::max(1, std::min({8, st / 8, (st + len - 1) / len}));
+    }
+    return c;
+  };
+  std::vector<int> longc(count, 1);
   for (int i = 0; i < count; ++i) {
     if (w[i].n <= 0 || w[i].k <= 0) continue;
-    const long tiles = (long)((m + bm - 1) / bm) * ((w[i].n + 127) / 128);
     const int st = w[i].k / 64;
-    cand[i] = st >= 2 * smin ? std::min(8, st / smin) : 1;
-    if (cand[i] > 1 && st / cand[i] < 8) cand[i] = std::max(1, st / 8);
-    plain.insert(plain.end(), tiles, st);
-    const std::vector<int> r = split_ranges(st, cand[i]);
-    for (int p = 0; p < cand[i]; ++p) split.insert(split.end(), tiles, r[p + 1] - r[p]);
+    longc[i] = st >= 2 * smin ? std::min(8, st / smin) : 1;
+    if (longc[i] > 1 && st / longc[i] < 8) longc[i] = std::max(1, st / 8);
   }
-  if (lpt_makespan(split, slots) * 100 <= lpt_makespan(plain, slots) * 85) parts = cand;
+  const double plain = score(parts);
+  double best = plain * 0.85;
+  for (const std::vector<int>& cand : {longc, cut_to(32), cut_to(16)}) {
+    const double sc = score(cand);
+    if (sc <= best) {
+      best = sc;
+      parts = cand;
+    }
+  }
   return parts;
 }
 
