@@ -160,6 +160,7 @@ LAST_REPLAYS_MS = []  # event times of the last time_graph call's replays (one p
 def time_eager(step_fns, steps, warmup, stream):
     import torch
     per = len(step_fns)
+    LAST_REPLAYS_MS[:] = []  # no replays: callers fall back to the mean
     with torch.cuda.stream(stream):
         for i in range(max(warmup, per)):
             step_fns[i % per]()
@@ -211,6 +212,20 @@ def time_graph(step_fns, steps, warmup, stream):
     return wall, gpu, g
 
 
+MIN_REPLAYS = 30  # every graph-timed figure is the median of at least this many replays
+SETTLE_S = 0.5    # untimed headline runs after the warm-up, in seconds (clocks reach their steady state)
+
+
+def replay_stats(per):
+    """Per-step seconds from the last time_graph call's replays (each of `per`
+    steps): median, min and max over the replays, and their count."""
+    ms = sorted(LAST_REPLAYS_MS)
+    if not ms:
+        return dict(median_s=None, min_s=None, max_s=None, replays=0)
+    return dict(median_s=float(np.median(ms)) / 1e3 / per, min_s=ms[0] / 1e3 / per, max_s=ms[-1] / 1e3 / per,
+                replays=len(ms))
+
+
 def bench_layer4b(args, stream, fmt=0):
     """Qwen3-4B-class layer, M=1, 2-bit: 36 byte copies of the layer rotated
     (1.07 GB), one grouped launch per step, replayed from a HIP graph."""
@@ -229,7 +244,7 @@ def bench_layer4b(args, stream, fmt=0):
     layers = [base] + [[clone_packed(pm) for pm in base] for _ in range(LAYERS - 1)]
     plans = [L.Plan(layer, xs, ys) for layer in layers]
     torch.cuda.synchronize()
-    steps = max(LAYERS, (args.steps + LAYERS - 1) // LAYERS * LAYERS)
+    steps = LAYERS * max(MIN_REPLAYS, (args.steps + LAYERS - 1) // LAYERS)
     fns = [(lambda p=p: p.run(stream.cuda_stream)) for p in plans]
     wall, gpu, _ = time_graph(fns, steps, LAYERS, stream)
     step_s = gpu / steps
@@ -254,6 +269,17 @@ def bench_stack8b(args, stream, mats, xs, ys):
         for _ in range(max(args.warmup, 1)):
             plan.run(cs)
         torch.cuda.synchronize()
+        # settle: after the stack's CPU-side build the GPU has idled for
+        # seconds and its clocks are down; untimed runs continue until
+        # SETTLE_S of work has passed since the warm-up began, so that the
+        # timed steps see the steady state whatever --warmup is (measured:
+        # 485 us/token over 20 steps after 5 warm-up runs, 417 once settled)
+        settle_runs, t_w = 0, time.perf_counter()
+        while time.perf_counter() - t_w < SETTLE_S:
+            for _ in range(20):
+                plan.run(cs)
+            settle_runs += 20
+            torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         before = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         after = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -273,6 +299,7 @@ def bench_stack8b(args, stream, mats, xs, ys):
     wts = [pm.n * pm.k for pm in mats]
     bpw = {key: round(sum(b[key] * w for b, w in zip(bits, wts)) / sum(wts), 4) for key in ("info", "plane", "storage")}
     return dict(stack_bytes=stack_bytes, steps=steps, wall_s=wall, total_s=total_s, step_s=total_s / steps,
+                settle_runs=settle_runs,
                 step_ms=step_ms, kern_ms=kern_ms, kern_bytes=stream_kernel_bytes(mats, xs), bpw=bpw,
                 weights=sum(wts), plan=plan)
 
@@ -391,13 +418,15 @@ def bench_layer8b(args, stream, m, fmt=1):
     plans = [L.Plan(layer, xs, ys) for layer in layers]
     torch.cuda.synchronize()
     fns = [(lambda p=p: p.run(stream.cuda_stream)) for p in plans]
-    steps = copies * max(1, args.steps // (20 * copies))
+    steps = copies * max(MIN_REPLAYS, args.steps // (20 * copies))
     wall, gpu, _ = time_graph(fns, steps, copies, stream)
-    step_s = gpu / steps
+    rs = replay_stats(copies)
+    step_s = rs["median_s"] or gpu / steps
     flops = sum(2.0 * m * pm.n * pm.k for pm in base)
     del plans, layers
     return dict(us_per_layer=step_s * 1e6, gbs=nbytes / step_s / 1e9, tflops=flops / step_s / 1e12, steps=steps,
-                copies=copies, rotated_bytes=copies * nbytes)
+                copies=copies, rotated_bytes=copies * nbytes, replays=rs["replays"],
+                us_min=(rs["min_s"] or step_s) * 1e6, us_max=(rs["max_s"] or step_s) * 1e6)
 
 
 def bench_stack8b_launches(stream, mats, xs, ys):
@@ -435,13 +464,16 @@ def bench_stress(args, stream, fmt, m):
     y = torch.empty((m, pm.n), dtype=torch.float16, device="cuda")
     plans = [L.Plan([c], [xd], [y]) for c in copies]
     fns = [(lambda p=p: p.run(stream.cuda_stream)) for p in plans]
-    steps = STRESS_COPIES * max(1, args.steps // (4 * STRESS_COPIES))
+    steps = STRESS_COPIES * max(MIN_REPLAYS, args.steps // (4 * STRESS_COPIES))
     wall, gpu, _ = time_graph(fns, steps, STRESS_COPIES, stream)
-    step_s = gpu / steps
+    rs = replay_stats(STRESS_COPIES)
+    step_s = rs["median_s"] or gpu / steps
     nbytes = pm.nbytes()
     del plans, copies
     return dict(us=round(step_s * 1e6, 2), gbs=round(nbytes / step_s / 1e9, 1),
-                hbm_frac=round(nbytes / step_s / 1e9 / HBM_PEAK_GBS, 4), bytes=nbytes, steps=steps)
+                hbm_frac=round(nbytes / step_s / 1e9 / HBM_PEAK_GBS, 4), bytes=nbytes, steps=steps,
+                replays=rs["replays"], us_min=round((rs["min_s"] or step_s) * 1e6, 2),
+                us_max=round((rs["max_s"] or step_s) * 1e6, 2))
 
 
 def bench_quantize(args, stream):
@@ -471,12 +503,13 @@ def bench_quantize(args, stream):
             L.check(lib.tern_quantize(wd.data_ptr(), n, k, 128, md.data_ptr(), 15, t.data_ptr(), sc.data_ptr(),
                                       of.data_ptr(), stream.cuda_stream))
     per = 2  # steps captured per graph replay
-    steps = max(per, args.steps // 100 // per * per)
+    steps = per * max(MIN_REPLAYS, args.steps // 100 // per)
     wall, gpu, _ = time_graph([step] * per, steps, per, stream)
-    step_s = gpu / steps
+    rs = replay_stats(per)
+    step_s = rs["median_s"] or gpu / steps
     io_bytes = nw * 2 + nw * 2 + sum(n * (k // 128) * 2 * 3 + n * ((k // 128 + 31) // 32) * 4 for _, _, _, _, _, n, k in items)
     return dict(ms_per_layer=step_s * 1e3, weights_per_s=nw / step_s, gbs=io_bytes / step_s / 1e9, steps=steps,
-                weights=nw, io_bytes=io_bytes)
+                weights=nw, io_bytes=io_bytes, replays=rs["replays"])
 
 
 def bench_rotate(args, stream):
@@ -500,10 +533,12 @@ def bench_rotate(args, stream):
     def step():
         L.tern_rotate_batched(Rs, xs, outs, stream.cuda_stream)
     per = 12  # steps captured per graph replay (a replay's own launch cost is then shared)
-    steps = max(per, args.steps // 10 // per * per)
+    steps = per * max(MIN_REPLAYS, args.steps // 10 // per)
     wall, gpu, _ = time_graph([step] * per, steps, per, stream)
-    step_s = gpu / steps
-    return dict(us_per_layer=step_s * 1e6, gbs=nbytes / step_s / 1e9, bytes=nbytes, steps=steps)
+    rs = replay_stats(per)
+    step_s = rs["median_s"] or gpu / steps
+    return dict(us_per_layer=step_s * 1e6, gbs=nbytes / step_s / 1e9, bytes=nbytes, steps=steps,
+                replays=rs["replays"])
 
 
 def cpu_quantize_baseline(budget_s=6.0):
@@ -734,6 +769,8 @@ def main():
              "headline_step_us": {"median": round(med * 1e3, 2), "min": round(min(r["step_ms"]) * 1e3, 2),
                                   "max": round(max(r["step_ms"]) * 1e3, 2), "timed_steps": r["steps"]},
              "headline_wall_s": round(r["wall_s"], 4),
+             "headline_settle": {"untimed_runs_after_warmup": r["settle_runs"], "seconds": SETTLE_S,
+                                 "why": "steady clocks before the timed steps (the stack is built on the CPU first)"},
              "headline_stream_kernel_us": {"mean": round(kern_s * 1e6, 2),
                                            "median": round(float(np.median(r["kern_ms"])) * 1e3, 2),
                                            "min": round(min(r["kern_ms"]) * 1e3, 2),
@@ -767,7 +804,7 @@ def main():
         wts = [pm.n * pm.k for pm in l4["base"]]
         extra["qwen3_4b_layer_m1_2bit"] = dict(
             bytes=l4["layer_bytes"], us_per_step=round(l4["step_s"] * 1e6, 3),
-            median_us_per_step=round(l4["median_step_s"] * 1e6, 3), gbs=round(l4["gbs"], 1),
+            median_us_per_step=round(l4["median_step_s"] * 1e6, 3), gbs=round(l4["gbs"], 1), replays=l4["replays"],
             hbm_frac=round(l4["gbs"] / HBM_PEAK_GBS, 4), steps=l4["steps"],
             tokens_per_s_equiv=round(1.0 / (LAYERS * l4["step_s"]), 1),
             bpw={key: round(sum(b[key] * w for b, w in zip(bits, wts)) / sum(wts), 4)
@@ -782,7 +819,8 @@ def main():
         for m in (1, 4, 16, 64, 512):
             q = bench_layer8b(args, stream, m)
             sweep[f"m{m}"] = dict(us_per_layer=round(q["us_per_layer"], 2), gbs=round(q["gbs"], 1),
-                                  tflops=round(q["tflops"], 2), copies_rotated=q["copies"])
+                                  tflops=round(q["tflops"], 2), copies_rotated=q["copies"], replays=q["replays"],
+                                  us_min=round(q["us_min"], 2), us_max=round(q["us_max"], 2))
             if m == 512:
                 sweep[f"m{m}"]["mfma_frac"] = round(q["tflops"] / F16_MFMA_PEAK_TFS, 4)
             log(f"bench: 8B-class layer base-3 M={m}: {q['us_per_layer']:.1f} us, {q['gbs']:.1f} GB/s, "
@@ -799,11 +837,12 @@ def main():
         extra["quantize_qwen3_4b_layer"] = dict(ms_per_layer=round(qz["ms_per_layer"], 4),
                                                 weights_per_s=qz["weights_per_s"], gbs=round(qz["gbs"], 1),
                                                 hbm_frac=round(qz["gbs"] / HBM_PEAK_GBS, 4), steps=qz["steps"],
+                                                replays=qz["replays"],
                                                 kernel="quantize_kernel<128>: sixteen lanes per (row, group)")
         log(f"bench: quantize 4B-class layer {qz['ms_per_layer']:.3f} ms")
         rt = bench_rotate(args, stream)
         extra["rotate_m1_qwen3_4b_inputs"] = dict(us_per_layer=round(rt["us_per_layer"], 3), gbs=round(rt["gbs"], 1),
-                                                  bytes=rt["bytes"], steps=rt["steps"],
+                                                  bytes=rt["bytes"], steps=rt["steps"], replays=rt["replays"],
                                                   note="one launch for K = 2560, 4096, 9728; 128 x 128 blocks")
         log(f"bench: rotate M=1 inputs of a 4B-class layer {rt['us_per_layer']:.2f} us")
         big = bench_read_probe(stream, 1 << 30, 2)
