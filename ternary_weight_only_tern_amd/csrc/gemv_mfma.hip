@@ -283,24 +283,40 @@ __device__ __forceinline__ void rot_share(const RotFold& f, int share) {
     }
   }
   // the stores are acknowledged by the device-coherent level, in every
-  // wavefront, before the share counts itself in; the last share raises
-  // the ready flag copy of every group that has members (one per lane of
-  // wavefront 0; a group with none would never lower it)
+  // wavefront, before the share counts itself in.  Two levels: share s
+  // counts itself in at sub-count s % kRotSubs; the share that completes a
+  // sub-count clears it (no other share of this launch touches it again)
+  // and counts the sub-count in at the top count; the share that completes
+  // the top count raises the ready flag copy of every group that has members
+  // (one per lane of wavefront 0; a group with none would never lower it).
+  // Returning atomics on one word are served one at a time, so this keeps
+  // each chain short (about shares / kRotSubs, then kRotSubs) instead of
+  // one chain of every share.
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   if (t < kWave) {
-    uint32_t before = 0u;
-    if (t == 0) before = __hip_atomic_fetch_add(f.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    before = __shfl(before, 0, kWave);
-    if (before + 1u == (uint32_t)f.shares && t < (int)gridDim.x - f.shares)
+    uint32_t last = 0u;
+    if (t == 0) {
+      const int c = share % kRotSubs;
+      const uint32_t members = (uint32_t)(f.shares / kRotSubs + (c < f.shares % kRotSubs ? 1 : 0));
+      uint32_t* sub = f.sync + kRotLineWords * (1 + kRotFlags + c);
+      if (__hip_atomic_fetch_add(sub, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u == members) {
+        __hip_atomic_store(sub, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t subs = (uint32_t)min(f.shares, kRotSubs);
+        last = __hip_atomic_fetch_add(f.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u == subs ? 1u : 0u;
+      }
+    }
+    last = __shfl(last, 0, kWave);
+    if (last && t < (int)gridDim.x - f.shares)
       __hip_atomic_store(f.sync + kRotLineWords * (1 + t), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 // The counters of a folded rotation, one 256-byte line each (RotFold.sync):
-// line 0 holds the shares counted [0], the waiter groups done [1] and the
-// give-up word [2]; line 1 + c holds copy c of the ready flag [0] and the
-// count of group c's workgroups through the wait [1].  A product workgroup
+// line 0 holds the share sub-counts completed [0], the waiter groups done
+// [1] and the give-up word [2]; line 1 + c holds copy c of the ready flag [0]
+// and the count of group c's workgroups through the wait [1]; line
+// 1 + kRotFlags + c holds share sub-count c [0].  A product workgroup
 // belongs to group (its index) % kRotFlags, so every address is polled by a
 // few workgroups only (accesses to one address are served one at a time).
 static_assert(kRotFlags == kWave, "one flag copy per lane");

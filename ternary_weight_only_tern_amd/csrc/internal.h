@@ -315,8 +315,9 @@ hipError_t launch_rotate(const RotBatch& a, int block, hipStream_t stream);
 // Launches of one plan must not overlap.
 constexpr int kRotShareRows = 128;
 constexpr int kRotFlags = 64;
+constexpr int kRotSubs = 16;       // share sub-counts (the shares' count-in has two levels)
 constexpr int kRotLineWords = 64;  // 256 bytes
-constexpr size_t kRotSyncBytes = (size_t)(kRotFlags + 1) * kRotLineWords * 4;
+constexpr size_t kRotSyncBytes = (size_t)(kRotFlags + 1 + kRotSubs) * kRotLineWords * 4;
 struct RotFold {
   RotBatch a;
   int32_t block, shares;

@@ -225,7 +225,7 @@ def test_rotated_plan_rejects_mixed_rotations():
 # the folded rotation's counters at the start of a rotated plan's workspace:
 # 65 lines of 256 bytes (shares and groups counted, give-up word; 64 copies
 # of the ready flag with their groups' counts)
-ROT_SYNC_BYTES = 65 * 256
+ROT_SYNC_BYTES = (65 + 16) * 256  # flag lines and the share sub-counts
 
 
 def _rotated_layer(rng, group, block, ks, m, fmt):
