@@ -532,7 +532,7 @@ def bench_rotate(args, stream):
 
     def step():
         L.tern_rotate_batched(Rs, xs, outs, stream.cuda_stream)
-    per = 12  # steps captured per graph replay (a replay's own launch cost is then shared)
+    per = 48  # steps captured per graph replay (a replay's own submission cost is then shared by 48 short launches)
     steps = per * max(MIN_REPLAYS, args.steps // 10 // per)
     wall, gpu, _ = time_graph([step] * per, steps, per, stream)
     rs = replay_stats(per)
