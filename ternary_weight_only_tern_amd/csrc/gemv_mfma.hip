@@ -368,7 +368,7 @@ __device__ __forceinline__ void rot_release(const RotFold& f, int wg, uint32_t m
 // (rot_share) and the activations are staged after rot_wait.
 template <int G, int MP, int RBLK>
 __device__ __forceinline__ void mfma_body(const GemvDesc* __restrict__ descs, const WgRec* __restrict__ recs,
-                                          int ndesc, const GemvDesc& one, const RotFold& f) {
+                                          int ndesc, GemvDesc one, const RotFold& f) {
   if constexpr (RBLK > 0) {
     if ((int)blockIdx.x < f.shares) {
       rot_share<RBLK>(f, (int)blockIdx.x);
