@@ -685,6 +685,44 @@ def test_grouped_qwen3_8b_layer_matches_oracle(m):
         check_y(y, y_ref, b, f"grouped layer m={m} proj={proj}")
 
 
+@pytest.mark.parametrize("m", [2, 4])
+def test_b3_layer_plan_two_stage_parts_match_oracle(m):
+    """The 8B-class layer (base-3, seven projections) through one plan at
+    m = 2 and 4, as the benchmark runs it: the matrix-core stream kernel
+    after the residual pass.  The layer holds more 64-row stages than the
+    launch has wavefronts, so its products are cut into K parts of two
+    stages whose FP32 partials the row block's last part sums; every output
+    within the bound, and two runs bitwise equal."""
+    import torch
+    say("b3 layer plan, two-stage K parts", m)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    mats, pms, xs, ys, refs = [], [], [], [], []
+    stages = 0
+    for proj in range(7):
+        mat = synth.workload_matrix("qwen3_8b_layer", proj)
+        x = synth.workload_x("qwen3_8b_layer", m, proj)
+        stages += -(-mat["n"] // 64) * -(-mat["k"] // 1024)
+        pms.append(upload_pack(mat, O.FMT_B3))
+        xs.append(to_dev(x.view(np.uint16)).view(torch.float16))
+        ys.append(torch.empty((m, mat["n"]), dtype=torch.float16, device="cuda"))
+        refs.append(oracle_y(mat, x))
+    assert stages > 7 * cus, (stages, cus)
+    plan = L.Plan(pms, xs, ys)
+    first = None
+    for _ in range(2):
+        for y in ys:
+            y.zero_()
+        plan.run()
+        torch.cuda.synchronize()
+        if first is None:
+            first = [y.clone() for y in ys]
+            for proj, (y, (y_ref, b)) in enumerate(zip(ys, refs)):
+                check_y(y, y_ref, b, f"b3 layer plan m={m} proj={proj}")
+        else:
+            for y, f in zip(ys, first):
+                assert torch.equal(y, f), "plan runs differ"
+
+
 @pytest.mark.timeout(600)
 def test_qwen3_8b_stack_plan_matches_oracle():
     """The 8B-class stack at M=1 as the benchmark builds and runs it: 36
