@@ -186,10 +186,24 @@ class PackedMatrix:
         return sum(sz) + extra
 
 
-def _workspace(desc: tern_matrix, m: int, device="cuda"):
+def _zeroed(nbytes: int, device, stream):
+    """A zero-filled workspace for a call on `stream`.  The fill is queued on
+    torch's current stream.  When the call goes to a stream of the caller's,
+    which may be another one, that stream waits for the fill, and the
+    allocator is told that the stream uses the buffer, so that it does not
+    hand the memory out again (and fill it on torch's stream) before the
+    call has finished there."""
     import torch
-    nbytes = load().tern_workspace_bytes(ctypes.byref(desc), m)
-    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+    ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if stream is not None:
+        ext = torch.cuda.ExternalStream(stream, device=ws.device)
+        ext.wait_stream(torch.cuda.current_stream(ws.device))
+        ws.record_stream(ext)
+    return ws
+
+
+def _workspace(desc: tern_matrix, m: int, device="cuda", stream=None):
+    return _zeroed(load().tern_workspace_bytes(ctypes.byref(desc), m), device, stream)
 
 
 def tern_pack(pm: PackedMatrix, trits, scales, mask_bits, offset=None, stream=None, ws=None):
@@ -202,7 +216,7 @@ def tern_pack(pm: PackedMatrix, trits, scales, mask_bits, offset=None, stream=No
     if pm.offset is not None:
         pm.offset.copy_(offset)
     d = pm.desc()
-    ws = ws if ws is not None else _workspace(d, 1, pm.plane0.device)
+    ws = ws if ws is not None else _workspace(d, 1, pm.plane0.device, stream)
     rs = scales[1:].contiguous() if pm.planes > 1 else None
     check(load().tern_pack(_ptr(trits), _ptr(rs), ctypes.byref(d), _ptr(ws), ws.numel(), _stream(stream)))
     return pm
@@ -213,7 +227,7 @@ def tern_unpack(pm: PackedMatrix, out=None, stream=None, ws=None):
     d = pm.desc()
     if out is None:
         out = torch.empty((pm.planes, pm.n, pm.k), dtype=torch.int8, device=pm.plane0.device)
-    ws = ws if ws is not None else _workspace(d, 1, pm.plane0.device)
+    ws = ws if ws is not None else _workspace(d, 1, pm.plane0.device, stream)
     check(load().tern_unpack(ctypes.byref(d), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
@@ -225,7 +239,7 @@ def _product(fn, pm, x, y_dtype, out, stream, ws):
         dt = torch.float32 if y_dtype == TERN_F32 else torch.float16
         out = torch.empty((m, pm.n), dtype=dt, device=x.device)
     d = pm.desc()
-    ws = ws if ws is not None else _workspace(d, m, x.device)
+    ws = ws if ws is not None else _workspace(d, m, x.device, stream)
     check(fn(ctypes.byref(d), _ptr(x), m, _ptr(out), y_dtype, _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
@@ -256,12 +270,10 @@ def _arrays(mats, xs, ys):
 
 
 def tern_gemv_batched(mats, xs, ys, y_dtype=TERN_F16, stream=None, ws=None):
-    import torch
     m = xs[0].shape[0] if xs else 0
     descs, xp, yp = _arrays(mats, xs, ys)
     if ws is None:
-        nbytes = load().tern_batch_workspace_bytes(descs, len(mats), m)
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=xs[0].device)
+        ws = _zeroed(load().tern_batch_workspace_bytes(descs, len(mats), m), xs[0].device, stream)
     check(load().tern_gemv_batched(descs, xp, yp, len(mats), m, y_dtype, _ptr(ws), ws.numel(), _stream(stream)))
     return ys
 

@@ -685,6 +685,38 @@ def test_grouped_qwen3_8b_layer_matches_oracle(m):
         check_y(y, y_ref, b, f"grouped layer m={m} proj={proj}")
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_calls_on_a_caller_stream_match_current_stream(fmt):
+    """tern_gemv, tern_gemv_batched and tern_unpack through the binding on a
+    stream of the caller's, with the workspaces the binding allocates: the
+    same bits as on torch's current stream (the zero fill of such a
+    workspace is queued on torch's stream and finished before a call on
+    another stream starts), and the product within the oracle's bound."""
+    import torch
+    say("calls on a caller stream", fmt)
+    mat, rng = small_matrix(300, 2560, 128, 2, 0.2, seed=77, offset_mode=O.OFF_ROW)
+    x = synth.draw_x(rng, 3, 2560, "normal")
+    pm = upload_pack(mat, fmt)
+    xd = to_dev(x.view(np.uint16)).view(torch.float16)
+    y0 = L.tern_gemv(pm, xd)
+    yb0 = [torch.empty_like(y0)]
+    L.tern_gemv_batched([pm], [xd], yb0)
+    t0 = L.tern_unpack(pm)
+    y1, yb1, t1 = torch.empty_like(y0), [torch.empty_like(y0)], torch.empty_like(t0)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    L.tern_gemv(pm, xd, out=y1, stream=s.cuda_stream)
+    L.tern_gemv_batched([pm], [xd], yb1, stream=s.cuda_stream)
+    L.tern_unpack(pm, out=t1, stream=s.cuda_stream)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1), "tern_gemv differs on the caller's stream"
+    assert torch.equal(yb0[0], yb1[0]), "tern_gemv_batched differs on the caller's stream"
+    assert torch.equal(t0, t1), "tern_unpack differs on the caller's stream"
+    y_ref, b = oracle_y(mat, x)
+    check_y(y1, y_ref, b, f"caller stream fmt={fmt}")
+
+
 @pytest.mark.parametrize("m", [2, 4])
 def test_b3_layer_plan_two_stage_parts_match_oracle(m):
     """The 8B-class layer (base-3, seven projections) through one plan at
