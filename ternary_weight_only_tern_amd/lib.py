@@ -290,7 +290,10 @@ def _event(e):
 class Plan:
     """tern_plan_create / tern_plan_run / tern_plan_destroy; with `rots` (a
     list of fp16 rotation-block tensors or None per product) and rot_block,
-    tern_plan_create_rotated."""
+    tern_plan_create_rotated.  The plan's workspace is a torch tensor that
+    lives as long as the Plan: keep the Plan until runs queued on a stream
+    other than torch's current one have finished (torch's allocator may hand
+    the memory out again as soon as the Plan is gone)."""
 
     def __init__(self, mats, xs, ys, y_dtype=TERN_F16, rots=None, rot_block=128):
         import torch
