@@ -273,8 +273,9 @@ struct tern_plan {
 extern "C" {
 
 // Routing of products by activation rows (crossovers measured on an
-// 8B-class layer on the MI355X): the decode kernels up to m = 2 (base-3) or
-// one 2-bit decode pass (m = 5 at group 128, where a pass holds 8 rows but
+// 8B-class layer on the MI355X): the decode kernels up to m = 4 (base-3,
+// whose matrix-core decode covers four rows in one pass) or one 2-bit
+// decode pass (m = 5 at group 128, where a pass holds 8 rows but
 // the 16-row product wins from 6; m = 4 at group 64), the 16-row
 // matrix-core product up to m = 32 (its time grows per 16 rows), the
 // 128/256-row matrix-core tiles from m = 33.
