@@ -481,8 +481,8 @@ __global__ __launch_bounds__(kResThreads) void b3_res_kernel(const GemvDesc* __r
     // product launch that follows (one launch less)
     if ((int)blockIdx.x >= nunits) {
       const int pb = (int)blockIdx.x - nunits, by = pb / prep_bx;
-      const B3Prep p = preps[by / 4];
-      b3_prep_rows<G>(p, pb % prep_bx, by % 4);
+      const B3Prep p = preps[by / MT];
+      b3_prep_rows<G>(p, pb % prep_bx, by % MT);
       return;
     }
   }
@@ -927,7 +927,10 @@ hipError_t launch_res_mt(const GemvDesc* descs, const B3ResItem* units, int nuni
   const size_t lds = (size_t)res_lds_bytes<G, MT>(max_k, lds_cap);
   if (units) {
     const int prep_bx = std::max(1, (prep_max_k / G * B3Geo<G>::CPG + 255) / 256);
-    const int prep_blocks = preps ? prep_bx * nprep * 4 : 0;
+    // one block row per activation row of the launch (MT >= m): at m = 1 the
+    // 8B-class stack's launch held 6,480 empty workgroups with four
+    // (stack 406.3-406.5 against 407.9-408.1 us per token)
+    const int prep_blocks = preps ? prep_bx * nprep * MT : 0;
     hipLaunchKernelGGL((b3_res_kernel<G, MT, true>), dim3(nunits + prep_blocks), dim3(kResThreads), lds, s, descs,
                        units, one, window, nunits, preps, prep_bx);
   } else {
