@@ -953,6 +953,12 @@ hipError_t launch_res_g(int mt, const GemvDesc* descs, const B3ResItem* units, i
 
 }  // namespace
 
+int b3_res_window_groups(int group, int mt, int max_k, int lds_cap) {
+  const int ng = max_k / group, per = mt * (2 * group + 16);
+  const int room = lds_cap - kResChunk * mt * 4 - mt * ng * 4;
+  return room <= 0 ? 0 : std::min(ng, room / per);
+}
+
 hipError_t launch_b3_res(int group, int mt, const GemvDesc* descs, const B3ResItem* units, int nunits,
                          const GemvDesc& one, int max_k, int lds_cap, const B3Prep* preps, int nprep, int prep_max_k,
                          hipStream_t s) {

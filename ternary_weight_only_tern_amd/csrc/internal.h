@@ -212,6 +212,10 @@ hipError_t launch_b3_res_ranges(const GemvDesc* descs, B3ResItem* units, int nun
 // k prep_max_k; none when preps is NULL) run in the same launch, as
 // launch_b3_prep would (their zero fields must be NULL: the units do not
 // wait for them).  Nothing is launched when nunits is 0.
+// Whole groups of activations (of mt rows) in a residual-pass window whose
+// workgroup takes at most lds_cap bytes of LDS, for a launch whose longest
+// product has max_k inputs (every group when they fit).
+int b3_res_window_groups(int group, int mt, int max_k, int lds_cap);
 hipError_t launch_b3_res(int group, int mt, const GemvDesc* descs, const B3ResItem* units, int nunits,
                          const GemvDesc& one, int max_k, int lds_cap, const B3Prep* preps, int nprep,
                          int prep_max_k, hipStream_t stream);

@@ -1345,9 +1345,19 @@ static size_t b3_rpart_bytes(const tern_matrix* w, int m, int split) {
 static size_t b3_rctr_bytes(const tern_matrix* w, int split) {
   return b3_has_res(w) && b3_res_slots(w, split) > 1 ? round_up((size_t)b3_res_units(w) * 4, 256) : 0;
 }
-// LDS a residual-pass workgroup may take: a large activation window when the
-// launch has few units, a smaller one (more workgroups per CU) otherwise.
-static int b3_res_lds_cap(long nunits) { return nunits <= 4L * tern_cu_count() ? 65536 : 36864; }
+// LDS a residual-pass workgroup may take.  Many units: a smaller window
+// (more workgroups per CU).  Few units: 64 KB when that holds every group of
+// the longest product in one window; when it cannot (the long product takes
+// several windows either way), 52 KB for a third workgroup per CU as long as
+// that window still holds 8 groups (8B-class layer at m = 4: 60.4 against
+// 61.7 us; at m = 2, where 64 KB holds the whole down projection, 52 KB took
+// 42.2 against 38.3 us).
+static int b3_res_lds_cap(long nunits, int group, int mt, int max_k) {
+  if (nunits > 4L * tern_cu_count()) return 36864;
+  const int ng = group > 0 ? max_k / group : 0;
+  if (ng <= 0 || tern::b3_res_window_groups(group, mt, max_k, 65536) >= ng) return 65536;
+  return tern::b3_res_window_groups(group, mt, max_k, 53248) >= 8 ? 53248 : 65536;
+}
 
 // Builds the batch (items only when `items` is true); ws may be NULL (sizes only).
 static tern_status build_b3_batch(const tern_matrix* w, const uint16_t* const* x, void* const* y, int32_t count,
@@ -1592,7 +1602,8 @@ static tern_status run_b3_batch(const B3Batch& b, int group, char* ws, hipStream
   else  // the preparations ride along in the residual pass's launch
     TERN_HIP(tern::launch_b3_res(group, b.mt, reinterpret_cast<const GemvDesc*>(ws + b.descs_off),
                                  reinterpret_cast<const tern::B3ResItem*>(ws + b.res_off), (int)b.res.size(), dummy,
-                                 b.max_k, b3_res_lds_cap((long)b.res.size()), preps, (int)b.preps.size(), b.max_k, s));
+                                 b.max_k, b3_res_lds_cap((long)b.res.size(), group, b.mt, b.max_k), preps,
+                                 (int)b.preps.size(), b.max_k, s));
   TERN_HIP(tern::launch_gemv_b3(group, b.mt, reinterpret_cast<const GemvDesc*>(ws + b.descs_off),
                                 reinterpret_cast<const tern::B3Item*>(ws + b.items_off),
                                 reinterpret_cast<uint32_t*>(ws + b.queue_off), b.nwg, dummy,
@@ -1662,7 +1673,8 @@ static tern_status b3_gemv(const tern_matrix* w, const uint16_t* x, int32_t m, v
   TERN_HIP(tern::launch_b3_prep(w->group, nullptr, 1, pr, w->k, s));
   const long nres = (long)b3_res_units(w) * d.rslots;
   if (d.rsum)
-    TERN_HIP(tern::launch_b3_res(w->group, pick_mt(m), nullptr, nullptr, (int)nres, d, w->k, b3_res_lds_cap(nres),
+    TERN_HIP(tern::launch_b3_res(w->group, pick_mt(m), nullptr, nullptr, (int)nres, d, w->k,
+                                 b3_res_lds_cap(nres, w->group, pick_mt(m), w->k),
                                  nullptr, 0, 0, s));
   const int items = d.row_blocks * parts;
   const int nwg = std::min(tern_cu_count(), (items + tern::kB3Waves - 1) / tern::kB3Waves);
@@ -2043,10 +2055,10 @@ static tern_status plan_launch(const tern_plan* plan, hipStream_t s, hipEvent_t 
       else
         TERN_HIP(tern::launch_b3_prep(plan->group, plan->preps, plan->nprep, none, plan->b3_maxk, s));
       TERN_HIP(tern::launch_b3_res(plan->group, plan->mt, plan->dev, plan->b3res, plan->nres, dummy, plan->b3_maxk,
-                                   b3_res_lds_cap(plan->nres), nullptr, 0, 0, s));
+                                   b3_res_lds_cap(plan->nres, plan->group, plan->mt, plan->b3_maxk), nullptr, 0, 0, s));
     } else {  // the preparations ride along in the residual pass's launch
       TERN_HIP(tern::launch_b3_res(plan->group, plan->mt, plan->dev, plan->b3res, plan->nres, dummy, plan->b3_maxk,
-                                   b3_res_lds_cap(plan->nres), plan->preps, plan->nprep, plan->b3_maxk, s));
+                                   b3_res_lds_cap(plan->nres, plan->group, plan->mt, plan->b3_maxk), plan->preps, plan->nprep, plan->b3_maxk, s));
     }
     if (before) TERN_HIP(hipEventRecord(before, s));
     TERN_HIP(tern::launch_gemv_b3(plan->group, plan->mt, plan->dev, plan->b3items, plan->queue, plan->nwg, dummy,
